@@ -1,0 +1,124 @@
+"""Drive a ``workloads.Workload`` through the oracle.  Test infrastructure.
+
+Order of one decode step ([KVX §01]: the new token's K/V are appended before
+its query reads the history): copy-on-write block copies, then the slot-scatter
+write of the new tokens, then attention over every sequence's whole history.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .block_manager import BlockManager
+from .cache_ops import copy_blocks, write
+
+
+class OracleState:
+    """Pools, manager and the decode step's tables, as the oracle computes them."""
+
+    def __init__(self, wl, keep_values=True):
+        self.wl = wl
+        dt = np.float32 if wl.dtype == "f32" else np.uint16
+        shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim)
+        self.k_pool = np.zeros(shape, dtype=dt)
+        self.v_pool = np.zeros(shape, dtype=dt)
+        self.bm = BlockManager(wl.num_blocks, wl.block_size, wl.free_order)
+        self.ctx_slots = []
+        # Token-order histories of every sequence (for the contiguous check).
+        self.keep_values = keep_values
+        self.hist_k: dict[int, list] = {}
+        self.hist_v: dict[int, list] = {}
+
+    # context build --------------------------------------------------------
+    def build_context(self):
+        wl, bm = self.wl, self.bm
+        cursor = 0
+        for op in wl.ops:
+            kind = op[0]
+            if kind == "add":
+                bm.add_seq(op[1])
+                self._hist_init(op[1])
+            elif kind == "append":
+                s, n = op[1], op[2]
+                slots, cow = bm.append_slots([s], n)
+                assert not cow, "context appends never write into shared blocks"
+                write(wl.ctx_k[cursor:cursor + n], wl.ctx_v[cursor:cursor + n],
+                      slots, self.k_pool, self.v_pool)
+                self.ctx_slots.extend(slots)
+                if self.keep_values:
+                    self.hist_k[s].extend(range(cursor, cursor + n))
+                    self.hist_v[s].extend(range(cursor, cursor + n))
+                cursor += n
+            elif kind == "share_prefix":
+                dst, src, n = op[1], op[2], op[3]
+                bm.share_prefix(dst, src, n)
+                if self.keep_values:
+                    self.hist_k[dst] = list(self.hist_k[src][:n])
+                    self.hist_v[dst] = list(self.hist_v[src][:n])
+            elif kind == "fork":
+                p, c = op[1], op[2]
+                bm.fork(p, c)
+                if self.keep_values:
+                    self.hist_k[c] = list(self.hist_k[p])
+                    self.hist_v[c] = list(self.hist_v[p])
+            else:
+                raise ValueError(f"unknown op {kind}")
+            bm.check()
+        assert cursor == wl.ctx_tokens
+
+    def _hist_init(self, s):
+        if self.keep_values:
+            self.hist_k[s] = []
+            self.hist_v[s] = []
+
+    # decode step ----------------------------------------------------------
+    def decode_tables(self):
+        """Host part of the step: one appended slot per sequence, the CoW pairs,
+        then the exported tables and lengths."""
+        wl = self.wl
+        slots, cow = self.bm.append_slots([int(s) for s in wl.decode_seqs], 1)
+        self.bm.check()
+        rows, lens = self.bm.export([int(s) for s in wl.decode_seqs], wl.max_blocks_per_seq)
+        self.slot_mapping = np.asarray(slots, dtype=np.int32)
+        self.cow_pairs = np.asarray(cow, dtype=np.int32).reshape(-1, 2)
+        self.block_tables = np.asarray(rows, dtype=np.int32)
+        self.seq_lens = np.asarray(lens, dtype=np.int32)
+        assert np.array_equal(self.seq_lens, wl.seq_lens)
+        if self.keep_values:
+            for i, s in enumerate(wl.decode_seqs):
+                self.hist_k[int(s)].append(("new", i))
+                self.hist_v[int(s)].append(("new", i))
+
+    def decode_device_part(self):
+        """copy -> write on the oracle pools."""
+        copy_blocks(self.cow_pairs.tolist(), self.k_pool, self.v_pool)
+        write(self.wl.new_k, self.wl.new_v, self.slot_mapping, self.k_pool, self.v_pool)
+
+    def attention(self, seqs=None):
+        from .attention import attention_decode
+        wl = self.wl
+        return attention_decode(wl.q, self.k_pool, self.v_pool, self.block_tables,
+                                self.seq_lens, wl.scale, seqs=seqs)
+
+    def history(self, s):
+        """Token-order K/V of sequence ``s`` rebuilt from the drawn values
+        (no pool involved)."""
+        wl = self.wl
+
+        def rows(idx, ctx, new):
+            out = []
+            for r in idx:
+                out.append(new[r[1]] if isinstance(r, tuple) else ctx[r])
+            if not out:
+                return np.zeros((0,) + ctx.shape[1:], dtype=ctx.dtype)
+            return np.stack(out)
+        return rows(self.hist_k[s], wl.ctx_k, wl.new_k), rows(self.hist_v[s], wl.ctx_v, wl.new_v)
+
+
+def run_step(wl, keep_values=True):
+    """Full oracle decode step.  Returns the ``OracleState`` after copy and write
+    (attention is computed on demand with ``.attention()``)."""
+    st = OracleState(wl, keep_values=keep_values)
+    st.build_context()
+    st.decode_tables()
+    st.decode_device_part()
+    return st
