@@ -1,0 +1,247 @@
+/*
+ * pkv.h -- C ABI of libpkv: the data-parallel hot path of PagedAttention on
+ * AMD Instinct MI355X (gfx950), plus the host block manager that produces its
+ * block tables and slot lists.
+ *
+ * Pages cited (titles as they appear on each page):
+ *   [KVM]  "19.2 KV Cache 系统化管理" -- book chapter, sections 19.2.1-19.2.6,
+ *          figures 19-5..19-8; section 19.2.3 holds a simplified implementation
+ *          (block pool, block table, block-wise online-softmax attention).
+ *   [KVX]  "KV Cache：长上下文为什么吃显存，PagedAttention 怎么救" -- explainer,
+ *          numbered sections 00-07 (01: new-token attention equation;
+ *          02: memory formula, GQA ratio; 03: MHA/MQA/GQA table).
+ *   [SLOT] "推理与 KV Cache 02:分页、共享与回收如何协作" -- blog post; sections
+ *          "从一个位置找到缓存块" (locate), "按整块分配,会多占多少空间"
+ *          (whole-block), "请求结束后,缓存会立刻消失吗" (release).
+ *   [PFX]  "学习大模型推理的显存优化：PagedAttention 与前缀缓存" -- blog post;
+ *          sections "PagedAttention 原理" (principle), "前缀缓存" (prefix).
+ *   [ENG]  the PagedAttention engineering article served under the page title
+ *          "企业官网建设流程全解析"; numbered sections 1.1-8.3.
+ *
+ * Conventions shared by every device entry point
+ * ----------------------------------------------
+ *  - Cache pools: ``k_cache`` and ``v_cache`` are device buffers laid out as
+ *    [num_blocks][block_size][num_kv_heads][head_dim] (row-major), the pool
+ *    shape of [KVM §19.2.3].  Token slot ``s`` is row ``s`` of the pool viewed
+ *    as [num_blocks * block_size][num_kv_heads][head_dim]: slot = physical
+ *    block id * block_size + offset in block ([SLOT §locate], token-slot
+ *    equation).
+ *  - Element type: ``pkv_geom.dtype`` (fp32 or bf16) for the pools and for every
+ *    K/V/Q/output buffer; no conversion is ever made.
+ *  - Ownership: the caller allocates and owns every buffer (pools, tokens,
+ *    index arrays, query, output, workspace).  The library keeps no pointer
+ *    after a call returns and allocates no device memory on these paths.
+ *  - Streams: ``stream`` is a ``hipStream_t`` passed as ``void*`` (NULL = the
+ *    null stream).  Calls only enqueue work; they never synchronise.  A device
+ *    fault surfaces at the caller's next synchronisation.
+ *  - Errors: every entry point returns a ``pkv_status``; on any non-OK status
+ *    nothing was enqueued and ``pkv_last_error()`` (per host thread) says why.
+ *    Argument checks are made on the host from sizes and pointers only; no
+ *    device data is read on the host.
+ *  - Index safety: kernels skip (do not dereference) slots, block ids and pairs
+ *    outside the pool, so bad indices never touch memory outside the pools;
+ *    the *values* produced for such entries are unspecified.
+ *  - Alignment: every device pointer must be 16-byte aligned and one token row
+ *    (num_kv_heads * head_dim * element size) a multiple of 16 bytes.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pkv_status;
+#define PKV_OK 0
+#define PKV_ERR_INVALID_ARG 1    /* bad shape, pointer, alignment or size     */
+#define PKV_ERR_UNSUPPORTED 2    /* valid but not built (e.g. head_dim 96)    */
+#define PKV_ERR_NO_FREE_BLOCKS 3 /* block manager: pool exhausted             */
+#define PKV_ERR_HIP 4            /* the HIP runtime refused a launch          */
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/* Geometry of one cache pool pair.  block_size must be a power of two;
+ * num_blocks * block_size < 2^31. */
+typedef struct pkv_geom {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype; /* pkv_dtype */
+} pkv_geom;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int32_t pkv_version(void);
+
+/* Message of the last non-OK status returned on this host thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* ------------------------------------------------------------------------- */
+/* Device entry points                                                        */
+/* ------------------------------------------------------------------------- */
+
+/* pkv_write -- slot-scatter KV append ([KVM §19.2.3] writing one token's K and
+ * V into its block slot; [KVX §01] the new token's K/V are appended to the
+ * layer cache before its query reads the history).
+ *   k, v          device [num_tokens][num_kv_heads][head_dim], pool dtype.
+ *   slot_mapping  device int32 [num_tokens]; token i goes to slot
+ *                 slot_mapping[i]; a negative slot means "skip this token".
+ *   k_cache/v_cache  the pools (modified in place).
+ * Bit copy: the stored bits equal the input bits.  Slots must be distinct
+ * (repeated slots race: which token wins is unspecified).  num_tokens == 0 is a
+ * no-op.  Errors: INVALID_ARG (null/misaligned pointer, bad geometry,
+ * num_tokens < 0), HIP. */
+pkv_status pkv_write(const void* k, const void* v, const int32_t* slot_mapping,
+                     int32_t num_tokens, void* k_cache, void* v_cache,
+                     const pkv_geom* geom, void* stream);
+
+/* pkv_copy_blocks -- copy-on-write block copy ([KVM §19.2.2], Fig. 19-8: when a
+ * block with reference count > 1 is written, a new block receives a copy of the
+ * original contents; [ENG §4.2]).
+ *   src_dst_pairs device int32 [num_pairs][2]; for each pair the whole dst block
+ *                 (all block_size slots, K and V, stale slots included) becomes
+ *                 a bit copy of the src block.
+ * A dst must not repeat nor be any pair's src (those races are unspecified).
+ * num_pairs == 0 is a no-op.  Errors: INVALID_ARG, HIP. */
+pkv_status pkv_copy_blocks(const int32_t* src_dst_pairs, int32_t num_pairs,
+                           void* k_cache, void* v_cache, const pkv_geom* geom,
+                           void* stream);
+
+/* Split-KV partition length (tokens) that pkv_attention_decode uses when its
+ * partition_tokens argument is 0.  Returns max_seq_len rounded up to a whole
+ * tile (no split) when one partition per sequence is enough, else a multiple
+ * of both block_size and 16.  Returns 0 on invalid arguments. */
+int32_t pkv_attention_partition_tokens(int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t max_seq_len, const pkv_geom* geom);
+
+/* Workspace bytes pkv_attention_decode needs for these sizes (0 when no split
+ * happens).  partition_tokens as for pkv_attention_decode (0 = automatic).
+ * Returns (size_t)-1 on invalid arguments. */
+size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t max_seq_len, int32_t partition_tokens,
+                                     const pkv_geom* geom);
+
+/* pkv_attention_decode -- block-table-driven decode attention with grouped
+ * query heads ([KVM §19.2.3] paged attention with block-wise online softmax,
+ * Fig. 19-5; [KVX §01] new-token attention equation; [KVX §02]/[KVX §03] GQA).
+ * For every sequence s and query head h (group g = h / (num_q_heads /
+ * num_kv_heads)):
+ *     out[s][h] = sum_{t < L_s} softmax_t(scale * q[s][h] . K_s[t]) * V_s[t]
+ * with K_s[t]/V_s[t] at block block_tables[s][t / block_size], offset
+ * t % block_size ([SLOT §locate]) and L_s = seq_lens[s]; L_s == 0 gives zeros.
+ *   q, out        device [num_seqs][num_q_heads][head_dim], pool dtype; out is
+ *                 rounded to nearest-even from fp32 for bf16.
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; entries past
+ *                 ceil(L_s / block_size) are never read.
+ *   seq_lens      device int32 [num_seqs].
+ *   max_seq_len   host-side upper bound of seq_lens; tokens beyond
+ *                 min(max_seq_len, max_blocks_per_seq * block_size) are ignored.
+ *   partition_tokens  0 = automatic, else the split-KV partition length (a
+ *                 multiple of block_size and of 16).  With more than one
+ *                 partition per sequence each partition's (max, sum, weighted
+ *                 sum) goes to the workspace and a log-sum-exp merge kernel
+ *                 produces out.
+ *   workspace     device buffer of at least pkv_attention_workspace_bytes(...)
+ *                 bytes (may be NULL when that is 0); contents on entry are
+ *                 ignored.
+ * Supported: head_dim 64 or 128; block_size a power of two >= 8;
+ * num_q_heads a multiple of num_kv_heads with at most 64 heads per group.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+pkv_status pkv_attention_decode(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* seq_lens, float scale, void* out,
+                                int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
+                                int32_t partition_tokens, void* workspace,
+                                size_t workspace_bytes, const pkv_geom* geom, void* stream);
+
+/* pkv_attention_decode_phase -- the same computation in two enqueued phases,
+ * for callers that time, overlap or order them separately.  phases: 1 = the
+ * per-partition kernel only (writes out directly when one partition covers
+ * every sequence, else the workspace), 2 = the log-sum-exp merge only (reads
+ * the workspace a previous phase-1 call with identical arguments filled;
+ * nothing is enqueued when there is a single partition), 3 = both, which is
+ * exactly pkv_attention_decode.  Arguments and errors as for
+ * pkv_attention_decode; INVALID_ARG for any other phases value. */
+pkv_status pkv_attention_decode_phase(int32_t phases, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                      float scale, void* out, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t max_seq_len,
+                                      int32_t partition_tokens, void* workspace,
+                                      size_t workspace_bytes, const pkv_geom* geom,
+                                      void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Host block manager (host memory only; one handle must not be used from two */
+/* threads at once).                                                          */
+/* ------------------------------------------------------------------------- */
+
+/* Pool of num_blocks blocks of block_size slots ([KVM §19.2.2], [KVM §19.2.3]).
+ * free_order (host int32 [num_blocks], a permutation of 0..num_blocks-1, or
+ * NULL for 0..num_blocks-1) is the initial free list; blocks are taken from its
+ * end and returned to its end (most recently freed first, [ENG §3.2]).
+ * Returns NULL on invalid arguments. */
+typedef struct pkv_bm pkv_bm;
+pkv_bm* pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order);
+void pkv_bm_destroy(pkv_bm* bm);
+
+/* New empty sequence.  INVALID_ARG if the id exists. */
+pkv_status pkv_bm_add_seq(pkv_bm* bm, int64_t seq);
+
+/* Empty sequence dst takes src's first num_tokens tokens by reference: the
+ * blocks holding them get one more reference each ([KVM §19.2.5], [PFX
+ * §prefix]).  INVALID_ARG if dst is not empty or src is shorter. */
+pkv_status pkv_bm_share_prefix(pkv_bm* bm, int64_t dst, int64_t src, int32_t num_tokens);
+
+/* New sequence child as a copy of parent: same table and length, one more
+ * reference on every block ([ENG §5.1], [KVM §19.2.2] parallel sampling). */
+pkv_status pkv_bm_fork(pkv_bm* bm, int64_t parent, int64_t child);
+
+/* Append tokens_each tokens to each of the n sequences seqs[0..n) in order
+ * (sequence-major).  For each token: logical block = filled / block_size,
+ * offset = filled % block_size ([SLOT §locate]); a new block is allocated when
+ * the logical block does not exist yet ([KVM §19.2.2] step 2); if it exists but
+ * is shared (reference count > 1) it is replaced by a fresh block and the pair
+ * (old, new) is emitted for pkv_copy_blocks while the old block loses one
+ * reference ([KVM §19.2.2], Fig. 19-8).  slots_out (host int32
+ * [n * tokens_each]) receives slot = block * block_size + offset.
+ * cow_pairs_out (host int32 [n][2], at most one pair per sequence per call) and
+ * *num_cow_out receive the copy pairs in order; cow_pairs_out may be NULL only
+ * if no copy is needed.  All-or-nothing: on NO_FREE_BLOCKS (or any error) the
+ * manager is left exactly as before ([KVM §19.2.6]; [ENG §3.2]). */
+pkv_status pkv_bm_append_slots(pkv_bm* bm, const int64_t* seqs, int32_t n,
+                               int32_t tokens_each, int32_t* slots_out,
+                               int32_t* cow_pairs_out, int32_t* num_cow_out);
+
+/* Release every block of the sequence, the partly filled last one included
+ * ([KVM §19.2.3]; [ENG §7.1]); blocks reaching zero references go back to the
+ * free list, their data untouched ([ENG §3.2]). */
+pkv_status pkv_bm_free_seq(pkv_bm* bm, int64_t seq);
+
+/* Block tables of seqs[0..n) as host int32 [n][max_blocks] padded with -1, and
+ * their token counts (host int32 [n]).  INVALID_ARG if a table is longer than
+ * max_blocks or a sequence is unknown. */
+pkv_status pkv_bm_export(const pkv_bm* bm, const int64_t* seqs, int32_t n, int32_t max_blocks,
+                         int32_t* block_tables_out, int32_t* seq_lens_out);
+
+int32_t pkv_bm_num_free(const pkv_bm* bm);
+/* Reference count of a block (-1 if out of range). */
+int32_t pkv_bm_refcount(const pkv_bm* bm, int32_t block);
+/* Tokens in a sequence (-1 if unknown). */
+int32_t pkv_bm_num_tokens(const pkv_bm* bm, int64_t seq);
+/* Copy the free list (bottom to top) into out[0..cap); *n_out = its length. */
+pkv_status pkv_bm_free_list(const pkv_bm* bm, int32_t* out, int32_t cap, int32_t* n_out);
+/* Invariants ([ENG §7.1], [ENG §7.2]): free list without duplicates; free and
+ * referenced blocks partition the pool; every reference count equals the
+ * number of table entries naming that block; every table holds
+ * ceil(tokens / block_size) blocks.  INVALID_ARG (with a message) on violation. */
+pkv_status pkv_bm_check(const pkv_bm* bm);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,141 @@
+"""Torch-facing binding of the device entry points of ``libpkv``.
+
+Marshalling only: tensors are checked for device, dtype, shape and layout,
+then their data pointers, sizes and the current HIP stream go to the C ABI.
+Every step of the path runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import PKV_BF16, PKV_F32, PkvGeom, check, lib
+
+_DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
+
+
+def geom_of(k_cache: torch.Tensor) -> PkvGeom:
+    """Geometry of a pool tensor [num_blocks, block_size, num_kv_heads, head_dim]."""
+    if k_cache.dim() != 4:
+        raise ValueError("cache must be [num_blocks, block_size, num_kv_heads, head_dim]")
+    if k_cache.dtype not in _DTYPES:
+        raise TypeError(f"unsupported cache dtype {k_cache.dtype}")
+    nb, B, H, D = k_cache.shape
+    return PkvGeom(nb, B, H, D, _DTYPES[k_cache.dtype])
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, device=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def write(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None:
+    """Scatter token rows k/v [T, H_kv, D] into the pools at ``slot_mapping``
+    (int32 [T], negative = skip)."""
+    g = geom_of(k_cache)
+    dev = k_cache.device
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (k, "k"), (v, "v")):
+        _need(t, n, k_cache.dtype, dev)
+    _need(slot_mapping, "slot_mapping", torch.int32, dev)
+    T = slot_mapping.numel()
+    if k.shape != (T, g.num_kv_heads, g.head_dim) or v.shape != k.shape:
+        raise ValueError("k/v must be [T, num_kv_heads, head_dim]")
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("pool shapes differ")
+    check(lib().pkv_write(_ptr(k), _ptr(v), _ptr(slot_mapping), T, _ptr(k_cache), _ptr(v_cache),
+                          ctypes.byref(g), _stream(stream)), "pkv_write")
+
+
+def copy_blocks(pairs, k_cache, v_cache, stream=None) -> None:
+    """Whole-block copies for int32 [P, 2] (src, dst) pairs."""
+    g = geom_of(k_cache)
+    dev = k_cache.device
+    _need(k_cache, "k_cache", None, dev)
+    _need(v_cache, "v_cache", k_cache.dtype, dev)
+    _need(pairs, "pairs", torch.int32, dev)
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [P, 2]")
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("pool shapes differ")
+    check(lib().pkv_copy_blocks(_ptr(pairs), pairs.shape[0], _ptr(k_cache), _ptr(v_cache),
+                                ctypes.byref(g), _stream(stream)), "pkv_copy_blocks")
+
+
+def partition_tokens(num_seqs: int, num_q_heads: int, max_seq_len: int, k_cache) -> int:
+    """The library's automatic split-KV partition length for these sizes."""
+    g = geom_of(k_cache)
+    return int(lib().pkv_attention_partition_tokens(num_seqs, num_q_heads, max_seq_len,
+                                                    ctypes.byref(g)))
+
+
+def workspace_bytes(num_seqs: int, num_q_heads: int, max_seq_len: int, k_cache,
+                    partition_tokens: int = 0) -> int:
+    g = geom_of(k_cache)
+    n = lib().pkv_attention_workspace_bytes(num_seqs, num_q_heads, max_seq_len,
+                                            partition_tokens, ctypes.byref(g))
+    if n == ctypes.c_size_t(-1).value:
+        check(1, "pkv_attention_workspace_bytes")
+    return int(n)
+
+
+def attention_decode(q, k_cache, v_cache, block_tables, seq_lens, scale, out=None,
+                     max_seq_len=None, partition_tokens=0, workspace=None, stream=None,
+                     phases=3):
+    """Decode attention; returns ``out`` [N, H_q, D] (allocated if None).
+
+    ``max_seq_len`` is the host-known bound of ``seq_lens`` (default: the
+    capacity of the block tables).  A workspace is allocated here only when the
+    caller passes none and the split needs one; callers that must not
+    allocate pass their own (size from ``workspace_bytes``).  ``phases``: 1 =
+    partition kernel only, 2 = merge only, 3 = both (see include/pkv.h)."""
+    g = geom_of(k_cache)
+    dev = k_cache.device
+    _need(k_cache, "k_cache", None, dev)
+    _need(v_cache, "v_cache", k_cache.dtype, dev)
+    _need(q, "q", k_cache.dtype, dev)
+    _need(block_tables, "block_tables", torch.int32, dev)
+    _need(seq_lens, "seq_lens", torch.int32, dev)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("pool shapes differ")
+    N, Hq, D = q.shape
+    if D != g.head_dim or block_tables.dim() != 2 or block_tables.shape[0] != N or \
+            seq_lens.shape != (N,):
+        raise ValueError("shape mismatch between q, block_tables, seq_lens and the pools")
+    max_blocks = block_tables.shape[1]
+    if max_seq_len is None:
+        max_seq_len = max_blocks * g.block_size
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", q.dtype, dev)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    need = workspace_bytes(N, Hq, max_seq_len, k_cache, partition_tokens)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need(workspace, "workspace", None, dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().pkv_attention_decode_phase(int(phases), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                           _ptr(block_tables), max_blocks, _ptr(seq_lens),
+                                           float(scale), _ptr(out), N, Hq, int(max_seq_len),
+                                           int(partition_tokens), _ptr(workspace), ws_bytes,
+                                           ctypes.byref(g), _stream(stream)),
+          "pkv_attention_decode")
+    return out

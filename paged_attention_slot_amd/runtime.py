@@ -1,0 +1,156 @@
+"""One decode step of a workload on the GPU, driven through ``libpkv``.
+
+The library's host block manager replays the workload's operation trace
+(sequence creation, context appends, prefix sharing, forks), the context K/V
+are placed with one bulk ``pkv_write``, then the decode step is, in stream
+order ([KVX §01]: the new token is appended before its query reads the
+history; page keys in include/pkv.h):
+
+    pkv_copy_blocks (copy-on-write pairs, if any)
+    pkv_write       (one new token per sequence)
+    pkv_attention_decode (+ split-KV merge)
+
+``layers`` > 1 keeps that many independent pool pairs with identical block
+tables (one per transformer layer); ``step(layer)`` runs the step on one of
+them, so consecutive steps read different memory as a model's layers do.
+"""
+from __future__ import annotations
+
+import time
+
+import numpy as np
+import torch
+
+from . import ops
+from .block_manager import BlockManager
+
+
+def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Host values (float32, or bf16 bit patterns as uint16) -> device tensor."""
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+    return t.to(device).view(torch.bfloat16)
+
+
+def to_host_bits(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> host array of its stored values (uint16 bits for bf16)."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+class DecodeStep:
+    def __init__(self, wl, device=None, layers: int = 1, partition_tokens: int | None = None,
+                 keep_context: bool = False):
+        self.wl = wl
+        self.device = torch.device(device or "cuda")
+        self.torch_dtype = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+        self.layers = int(layers)
+
+        # -- host: block manager replays the trace --------------------------
+        bm = BlockManager(wl.num_blocks, wl.block_size, wl.free_order)
+        ctx_slots = np.empty(wl.ctx_tokens, dtype=np.int32)
+        cur = 0
+        for op in wl.ops:
+            kind = op[0]
+            if kind == "add":
+                bm.add_seq(op[1])
+            elif kind == "append":
+                slots, cow = bm.append_slots([op[1]], op[2])
+                if len(cow):
+                    raise RuntimeError("context append wrote into a shared block")
+                ctx_slots[cur:cur + op[2]] = slots
+                cur += op[2]
+            elif kind == "share_prefix":
+                bm.share_prefix(op[1], op[2], op[3])
+            elif kind == "fork":
+                bm.fork(op[1], op[2])
+            else:
+                raise ValueError(f"unknown op {kind}")
+        assert cur == wl.ctx_tokens
+        self.ctx_slots = ctx_slots
+
+        # decode step, host part: one slot per sequence, CoW pairs, tables
+        t0 = time.perf_counter()
+        slots, cow = bm.append_slots(wl.decode_seqs, 1)
+        tables, lens = bm.export(wl.decode_seqs, wl.max_blocks_per_seq)
+        self.host_tables_s = time.perf_counter() - t0
+        self.bm = bm
+        self.slot_mapping_h, self.cow_pairs_h = slots, cow
+        self.block_tables_h, self.seq_lens_h = tables, lens
+        if not np.array_equal(lens, wl.seq_lens):
+            raise RuntimeError("block manager lengths differ from the workload's")
+
+        # -- device ------------------------------------------------------------
+        dev = self.device
+        shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim)
+        self.k_caches = [torch.zeros(shape, dtype=self.torch_dtype, device=dev)]
+        self.v_caches = [torch.zeros(shape, dtype=self.torch_dtype, device=dev)]
+        if wl.ctx_tokens:
+            ck = to_device(wl.ctx_k, wl.dtype, dev)
+            cv = to_device(wl.ctx_v, wl.dtype, dev)
+            cs = torch.from_numpy(ctx_slots).to(dev)
+            ops.write(ck, cv, cs, self.k_caches[0], self.v_caches[0])
+            if keep_context:
+                self.ctx_k_dev, self.ctx_v_dev, self.ctx_slots_dev = ck, cv, cs
+            else:
+                del ck, cv, cs
+        for _ in range(1, self.layers):
+            self.k_caches.append(self.k_caches[0].clone())
+            self.v_caches.append(self.v_caches[0].clone())
+        self.q = to_device(wl.q, wl.dtype, dev)
+        self.new_k = to_device(wl.new_k, wl.dtype, dev)
+        self.new_v = to_device(wl.new_v, wl.dtype, dev)
+        self.slot_mapping = torch.from_numpy(slots).to(dev)
+        self.cow_pairs = torch.from_numpy(np.ascontiguousarray(cow).reshape(-1, 2)).to(dev)
+        self.block_tables = torch.from_numpy(tables).to(dev)
+        self.seq_lens = torch.from_numpy(lens).to(dev)
+        self.max_seq_len = int(lens.max()) if lens.size else 0
+        pt = wl.partition_tokens if partition_tokens is None else partition_tokens
+        self.partition_tokens = int(pt or 0)
+        self.out = torch.empty_like(self.q)
+        n = ops.workspace_bytes(wl.num_seqs, wl.num_q_heads, self.max_seq_len, self.k_caches[0],
+                                self.partition_tokens)
+        self.workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=dev) if n else None
+        torch.cuda.synchronize(dev)
+
+    @property
+    def k_cache(self):
+        return self.k_caches[0]
+
+    @property
+    def v_cache(self):
+        return self.v_caches[0]
+
+    def copy(self, layer=0, stream=None):
+        if self.cow_pairs.shape[0]:
+            ops.copy_blocks(self.cow_pairs, self.k_caches[layer], self.v_caches[layer],
+                            stream=stream)
+
+    def write(self, layer=0, stream=None):
+        ops.write(self.new_k, self.new_v, self.slot_mapping, self.k_caches[layer],
+                  self.v_caches[layer], stream=stream)
+
+    def attention(self, layer=0, stream=None, out=None, partition_tokens=None, phases=3):
+        pt = self.partition_tokens if partition_tokens is None else partition_tokens
+        ws = self.workspace
+        if pt != self.partition_tokens:
+            ws = None  # let the binding size a workspace for this split
+        return ops.attention_decode(self.q, self.k_caches[layer], self.v_caches[layer],
+                                    self.block_tables, self.seq_lens, self.wl.scale,
+                                    out=self.out if out is None else out,
+                                    max_seq_len=self.max_seq_len, partition_tokens=pt,
+                                    workspace=ws, stream=stream, phases=phases)
+
+    @property
+    def num_parts(self) -> int:
+        pt = self.partition_tokens or ops.partition_tokens(
+            self.wl.num_seqs, self.wl.num_q_heads, self.max_seq_len, self.k_caches[0])
+        return max(1, -(-self.max_seq_len // pt))
+
+    def step(self, layer=0, stream=None):
+        """copy -> write -> attention on one layer's pools (enqueue only)."""
+        self.copy(layer, stream)
+        self.write(layer, stream)
+        return self.attention(layer, stream)

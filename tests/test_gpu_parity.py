@@ -1,0 +1,204 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Write and copy: bit-exact full pools.  Attention: the gate of tests/parity.py
+against the fp64 oracle, plus exact special cases (a single position returns
+its value; a different physical placement gives bit-identical output; an empty
+history gives zeros).  Small cases span several tiles with ragged tails; the
+full-size configurations run in the launch configuration the bench times.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle.attention import attention_decode as oracle_attention  # noqa: E402
+from oracle.attention import attention_split as oracle_split  # noqa: E402
+from oracle.attention import to_f64  # noqa: E402
+from oracle.replay import run_step  # noqa: E402
+from tests.parity import assert_gate  # noqa: E402
+from workloads import config_workload, independent_workload, shared_prefix_workload  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from paged_attention_slot_amd import lib
+    lib()  # fail loudly if the library is missing
+    return torch.device("cuda:0")
+
+
+def run_both(wl, partition_tokens=None, attention=True):
+    from paged_attention_slot_amd.runtime import DecodeStep
+    say(f"  case {wl.name}: N={wl.num_seqs} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} "
+        f"D={wl.head_dim} B={wl.block_size} {wl.dtype} maxlen={wl.max_seq_len} "
+        f"pt={partition_tokens} seed={wl.seed}")
+    step = DecodeStep(wl, partition_tokens=partition_tokens)
+    step.copy()
+    step.write()
+    if attention:
+        step.attention()
+    torch.cuda.synchronize()
+    ost = run_step(wl, keep_values=False)
+    # the two block managers agree on the step's host part
+    assert np.array_equal(step.slot_mapping_h, ost.slot_mapping)
+    assert np.array_equal(step.cow_pairs_h.reshape(-1, 2), ost.cow_pairs.reshape(-1, 2))
+    assert np.array_equal(step.block_tables_h, ost.block_tables)
+    return step, ost
+
+
+def host_bits(t):
+    from paged_attention_slot_amd.runtime import to_host_bits
+    return to_host_bits(t)
+
+
+def check_pools(step, ost):
+    assert np.array_equal(host_bits(step.k_cache), ost.k_pool), "K pool differs"
+    assert np.array_equal(host_bits(step.v_cache), ost.v_pool), "V pool differs"
+
+
+def gpu_out(step):
+    return to_f64(host_bits(step.out))
+
+
+LENS = [1, 7, 16, 17, 33, 100, 255, 300]
+SMALL = [
+    # dtype, B, D, Hq, Hkv
+    ("bf16", 16, 128, 16, 8),
+    ("bf16", 16, 128, 32, 8),
+    ("bf16", 32, 128, 64, 8),
+    ("bf16", 8, 64, 8, 8),
+    ("bf16", 64, 64, 12, 4),
+    ("bf16", 16, 128, 16, 1),
+    ("f32", 16, 64, 8, 2),
+    ("f32", 32, 128, 4, 4),
+    ("f32", 8, 128, 6, 2),
+]
+
+
+@pytest.mark.parametrize("dtype,B,D,Hq,Hkv", SMALL, ids=lambda v: str(v))
+def test_small_write_and_attention(dtype, B, D, Hq, Hkv):
+    wl = independent_workload(LENS, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=B,
+                              dtype=dtype, seed=100 + B + D + Hq)
+    step, ost = run_both(wl)
+    check_pools(step, ost)
+    ref = oracle_attention(wl.q, ost.k_pool, ost.v_pool, ost.block_tables, ost.seq_lens,
+                           wl.scale)
+    out = gpu_out(step)
+    r = assert_gate(out, ref, dtype, wl.name)
+    say("  gate", r)
+    G = Hq // Hkv
+    for i, L in enumerate(wl.seq_lens):
+        if L == 1:  # a single position: the output is that position's value, exactly
+            for h in range(Hq):
+                assert np.array_equal(out[i, h], to_f64(wl.new_v[i, h // G]))
+
+
+@pytest.mark.parametrize("pt", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("dtype,B", [("bf16", 16), ("f32", 16), ("bf16", 32)])
+def test_split_kv_matches_oracle_and_unsplit(pt, dtype, B):
+    if pt % B:
+        pytest.skip("partition must be a multiple of the block size")
+    wl = independent_workload([1, 15, 16, 17, 64, 200, 333, 513], num_q_heads=16,
+                              num_kv_heads=4, head_dim=128, block_size=B, dtype=dtype, seed=7)
+    step, ost = run_both(wl, partition_tokens=pt)
+    split = gpu_out(step)
+    ref = oracle_split(wl.q, ost.k_pool, ost.v_pool, ost.block_tables, ost.seq_lens, wl.scale,
+                       pt)
+    assert_gate(split, ref, dtype, f"split {pt}")
+    whole = to_f64(host_bits(step.attention(partition_tokens=10**6 // B * B)))
+    torch.cuda.synchronize()
+    assert_gate(split, whole, dtype, "split vs unsplit")
+
+
+def test_physical_placement_gives_bit_identical_output():
+    a = independent_workload([5, 40, 97, 160], num_q_heads=32, num_kv_heads=8, head_dim=128,
+                             block_size=16, dtype="bf16", seed=3)
+    b = independent_workload([5, 40, 97, 160], num_q_heads=32, num_kv_heads=8, head_dim=128,
+                             block_size=16, dtype="bf16", seed=3)
+    b.free_order = np.random.default_rng(1234).permutation(b.num_blocks).astype(np.int32)
+    sa, oa = run_both(a)
+    sb, ob = run_both(b)
+    assert not np.array_equal(oa.block_tables, ob.block_tables)
+    assert np.array_equal(host_bits(sa.out), host_bits(sb.out))
+
+
+def test_zero_length_sequences_give_zeros():
+    from paged_attention_slot_amd import ops
+    wl = independent_workload([3, 50, 20], num_q_heads=8, num_kv_heads=2, head_dim=64,
+                              block_size=16, dtype="bf16", seed=9)
+    step, ost = run_both(wl, attention=False)
+    lens = step.seq_lens.clone()
+    lens[1] = 0
+    for pt in (0, 16):
+        out = torch.full_like(step.q, 7.0)
+        ops.attention_decode(step.q, step.k_cache, step.v_cache, step.block_tables, lens,
+                             wl.scale, out=out, max_seq_len=50, partition_tokens=pt)
+        torch.cuda.synchronize()
+        o = to_f64(host_bits(out))
+        assert not o[1].any()
+        ref = oracle_attention(wl.q, ost.k_pool, ost.v_pool, ost.block_tables,
+                               lens.cpu().numpy(), wl.scale)
+        assert_gate(o, ref, "bf16", f"zero-length pt={pt}")
+
+
+def test_copy_on_write_family_small():
+    wl = shared_prefix_workload(prefix_tokens=64, suffix_lens=[3, 16, 7, 1, 12, 30, 9],
+                                forking_parents=4, samples_per_fork=4, num_q_heads=16,
+                                num_kv_heads=4, head_dim=128, block_size=16, dtype="bf16", seed=5)
+    step, ost = run_both(wl)
+    assert len(ost.cow_pairs) == 12
+    check_pools(step, ost)
+    ref = oracle_attention(wl.q, ost.k_pool, ost.v_pool, ost.block_tables, ost.seq_lens,
+                           wl.scale)
+    assert_gate(gpu_out(step), ref, "bf16", "cow family")
+
+
+# -- full-size configurations, in the bench's launch configuration -----------
+
+def sampled_pairs(wl, rng, n_seqs, heads_per_seq):
+    seqs = np.sort(rng.choice(wl.num_seqs, size=min(n_seqs, wl.num_seqs), replace=False))
+    heads = {int(s): np.sort(rng.choice(wl.num_q_heads, size=heads_per_seq, replace=False))
+             for s in seqs}
+    return seqs, heads
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3-0.6b-layer", "shared-prefix-cow"])
+def test_config_full(name):
+    wl = config_workload(name)
+    step, ost = run_both(wl)
+    check_pools(step, ost)
+    ref = oracle_attention(wl.q, ost.k_pool, ost.v_pool, ost.block_tables, ost.seq_lens,
+                           wl.scale)
+    out = gpu_out(step)
+    r = assert_gate(out, ref, wl.dtype, name)
+    say("  gate", r)
+    if name == "tiny":
+        # the page's self-check bound, fp32 end to end
+        assert r["max_abs"] < 1e-5
+
+
+@pytest.mark.parametrize("name", ["llama3-8b-layer", "llama3.1-70b-longctx"])
+def test_config_full_sampled(name):
+    wl = config_workload(name)
+    step, ost = run_both(wl)
+    check_pools(step, ost)
+    out = gpu_out(step)
+    rng = np.random.default_rng(17)
+    seqs, heads = sampled_pairs(wl, rng, 12 if wl.num_seqs > 4 else 4, 8)
+    ref = oracle_attention(wl.q, ost.k_pool, ost.v_pool, ost.block_tables, ost.seq_lens,
+                           wl.scale, seqs=[int(s) for s in seqs])
+    for s in seqs:
+        hs = heads[int(s)]
+        r = assert_gate(out[s, hs], ref[s, hs], wl.dtype, f"{name} seq {s}")
+    say("  last gate", r)
+    assert np.isfinite(out).all()

@@ -1,0 +1,122 @@
+"""The C-ABI library loads, exports every symbol ``include/pkv.h`` declares,
+and rejects bad arguments on the host with the documented status codes
+(no GPU: none of these calls reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+pkv = pytest.importorskip("paged_attention_slot_amd")
+from paged_attention_slot_amd import _lib  # noqa: E402
+from paged_attention_slot_amd._lib import PkvGeom  # noqa: E402
+
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_\w+)\s*\(", text)))
+
+
+def test_library_loads():
+    lib = pkv.lib()
+    assert lib.pkv_version() >= 100
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    lib = pkv.lib()
+    names = declared_symbols()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), set(names) ^ set(_lib.SIGNATURES)
+
+
+def g(nb=16, B=16, H=2, D=64, dt=0):
+    return PkvGeom(nb, B, H, D, dt)
+
+
+def last_error():
+    return pkv.lib().pkv_last_error().decode()
+
+
+def test_write_validation():
+    lib = pkv.lib()
+    x = ctypes.c_void_p(0x1000)
+    assert lib.pkv_write(x, x, x, 1, x, x, None, None) == _lib.PKV_ERR_INVALID_ARG
+    assert "geometry" in last_error()
+    assert lib.pkv_write(x, x, x, 1, x, x, ctypes.byref(g(B=12)), None) == _lib.PKV_ERR_INVALID_ARG
+    assert "power of two" in last_error()
+    assert lib.pkv_write(x, x, x, -1, x, x, ctypes.byref(g()), None) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_write(x, x, x, 0, x, x, ctypes.byref(g()), None) == _lib.PKV_OK
+    bad = ctypes.c_void_p(0x1004)
+    assert lib.pkv_write(bad, x, x, 1, x, x, ctypes.byref(g()), None) == _lib.PKV_ERR_INVALID_ARG
+    assert "misaligned" in last_error()
+    assert lib.pkv_write(None, x, x, 1, x, x, ctypes.byref(g()), None) == _lib.PKV_ERR_INVALID_ARG
+    big = g(nb=1 << 27, B=16)
+    assert lib.pkv_write(x, x, x, 1, x, x, ctypes.byref(big), None) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_write(x, x, x, 1, x, x, ctypes.byref(g(H=1, D=2, dt=1)), None) == \
+        _lib.PKV_ERR_INVALID_ARG     # 4-byte rows are not a multiple of 16
+
+
+def test_copy_validation():
+    lib = pkv.lib()
+    x = ctypes.c_void_p(0x1000)
+    assert lib.pkv_copy_blocks(x, 0, x, x, ctypes.byref(g()), None) == _lib.PKV_OK
+    assert lib.pkv_copy_blocks(x, -2, x, x, ctypes.byref(g()), None) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_copy_blocks(None, 3, x, x, ctypes.byref(g()), None) == _lib.PKV_ERR_INVALID_ARG
+
+
+def test_attention_validation_and_workspace_size():
+    lib = pkv.lib()
+    x = ctypes.c_void_p(0x1000)
+
+    def call(geom, N=2, Hq=8, maxlen=100, pt=0, ws=None, wsb=0, scale=0.1, mb=7):
+        return lib.pkv_attention_decode(x, x, x, x, mb, x, scale, x, N, Hq, maxlen, pt, ws, wsb,
+                                        ctypes.byref(geom), None)
+
+    assert call(g(D=96)) == _lib.PKV_ERR_UNSUPPORTED
+    assert call(g(B=4)) == _lib.PKV_ERR_UNSUPPORTED
+    assert call(g(), Hq=7) == _lib.PKV_ERR_INVALID_ARG
+    assert call(g(), pt=24) == _lib.PKV_ERR_INVALID_ARG
+    assert call(g(), scale=float("nan")) == _lib.PKV_ERR_INVALID_ARG
+    assert call(g(), N=0) == _lib.PKV_OK
+    # split needs a workspace
+    assert call(g(), maxlen=100, pt=32) == _lib.PKV_ERR_INVALID_ARG
+    assert "workspace" in last_error()
+    # workspace size: N * Hq * P * (D + 2) floats
+    n = lib.pkv_attention_workspace_bytes(2, 8, 100, 32, ctypes.byref(g()))
+    assert n == 2 * 8 * 4 * (64 + 2) * 4
+    assert lib.pkv_attention_workspace_bytes(2, 8, 100, 0, ctypes.byref(g())) == 0
+    assert lib.pkv_attention_workspace_bytes(2, 8, 100, 24, ctypes.byref(g())) == \
+        ctypes.c_size_t(-1).value
+
+
+@pytest.mark.parametrize("maxlen,B,expect", [(100, 16, 112), (4096, 16, 256), (8192, 16, 512),
+                                             (131072, 32, 512), (10, 64, 64), (300, 8, 256)])
+def test_automatic_partition(maxlen, B, expect):
+    lib = pkv.lib()
+    got = lib.pkv_attention_partition_tokens(4, 8, maxlen, ctypes.byref(g(nb=8192, B=B)))
+    assert got == expect
+    assert got % 16 == 0 and got % B == 0
+
+
+def test_block_manager_errors():
+    bm = pkv.BlockManager(2, 4)
+    bm.add_seq(1)
+    with pytest.raises(pkv.PkvError):
+        bm.add_seq(1)
+    with pytest.raises(pkv.PkvError):
+        bm.fork(9, 10)
+    with pytest.raises(pkv.NoFreeBlocks):
+        bm.append_slots([1], 9)
+    assert bm.num_tokens(1) == 0 and bm.num_free() == 2
+    with pytest.raises(pkv.PkvError):
+        bm.export([1, 2], 4)
+    assert pkv.lib().pkv_bm_create(0, 4, None) is None
+    bad = (ctypes.c_int32 * 3)(0, 0, 1)
+    assert pkv.lib().pkv_bm_create(3, 4, bad) is None

@@ -269,7 +269,10 @@ def _slack_pool(need: int) -> int:
     return _ceil_div(need * 11, 10)
 
 
-def _draw_values(ss_kids, n_seqs, n_ctx, hq, hkv, d, dtype):
+def _draw_values(ss_kids, n_seqs, n_ctx, hq, hkv, d, dtype, values=True):
+    if not values:
+        z = np.zeros(0, dtype=np.float32 if dtype == "f32" else np.uint16)
+        return z, z, z, z, z
     q = normal_array(ss_kids[_S_Q], (n_seqs, hq, d), dtype)
     ck = normal_array(ss_kids[_S_CTXK], (n_ctx, hkv, d), dtype)
     cv = normal_array(ss_kids[_S_CTXV], (n_ctx, hkv, d), dtype)
@@ -280,7 +283,7 @@ def _draw_values(ss_kids, n_seqs, n_ctx, hq, hkv, d, dtype):
 
 def independent_workload(lens, *, num_q_heads, num_kv_heads, head_dim, block_size,
                          dtype, seed, pool_blocks=0, partition_tokens=0, name="custom",
-                         scale=None, kids=None) -> Workload:
+                         scale=None, kids=None, values=True) -> Workload:
     """Independent sequences with the given final lengths (context = len - 1
     tokens, then one decode append each).  Physical ids come from a seeded
     random permutation of the pool."""
@@ -301,7 +304,7 @@ def independent_workload(lens, *, num_q_heads, num_kv_heads, head_dim, block_siz
             ops.append(("append", s, int(L - 1)))
     n_ctx = int(np.sum(lens - 1))
     q, ck, cv, nk, nv = _draw_values(kids, lens.size, n_ctx, num_q_heads, num_kv_heads,
-                                     head_dim, dtype)
+                                     head_dim, dtype, values)
     return Workload(name=name, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
                     head_dim=head_dim, block_size=block_size, dtype=dtype, num_blocks=nb,
                     free_order=perm, ops=ops, ctx_tokens=n_ctx,
@@ -313,7 +316,8 @@ def independent_workload(lens, *, num_q_heads, num_kv_heads, head_dim, block_siz
 
 def shared_prefix_workload(*, prefix_tokens, suffix_lens, forking_parents, samples_per_fork,
                            num_q_heads, num_kv_heads, head_dim, block_size, dtype, seed,
-                           partition_tokens=0, name="shared-prefix", kids=None) -> Workload:
+                           partition_tokens=0, name="shared-prefix", kids=None,
+                           values=True) -> Workload:
     """Base sequences 0..n-1 share one prefix (sequence 0 writes it, the others
     take it by reference), then each appends its own suffix.  The first
     ``forking_parents`` base sequences whose last block is partially filled fork
@@ -358,7 +362,7 @@ def shared_prefix_workload(*, prefix_tokens, suffix_lens, forking_parents, sampl
     perm = np.random.Generator(np.random.PCG64(kids[_S_PERM])).permutation(nb).astype(np.int32)
     n_ctx = int(prefix_tokens + np.sum(suffix))
     q, ck, cv, nk, nv = _draw_values(kids, nseq, n_ctx, num_q_heads, num_kv_heads, head_dim,
-                                     dtype)
+                                     dtype, values)
     return Workload(name=name, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
                     head_dim=head_dim, block_size=block_size, dtype=dtype, num_blocks=nb,
                     free_order=perm, ops=ops, ctx_tokens=n_ctx,
@@ -368,14 +372,15 @@ def shared_prefix_workload(*, prefix_tokens, suffix_lens, forking_parents, sampl
                     seed=seed, meta={"parents": parents, "children": child_of})
 
 
-def config_workload(name: str, seed: int | None = None) -> Workload:
-    """The named configuration's workload (seed defaults to the config's)."""
+def config_workload(name: str, seed: int | None = None, values: bool = True) -> Workload:
+    """The named configuration's workload (seed defaults to the config's).
+    ``values=False`` skips drawing q/K/V (trace and sizes only)."""
     c = CONFIGS[name]
     seed = c.seed if seed is None else seed
     kids = np.random.SeedSequence(seed).spawn(8)
     common = dict(num_q_heads=c.num_q_heads, num_kv_heads=c.num_kv_heads,
                   head_dim=c.head_dim, block_size=c.block_size, dtype=c.dtype, seed=seed,
-                  partition_tokens=c.partition_tokens, name=c.name, kids=kids)
+                  partition_tokens=c.partition_tokens, name=c.name, kids=kids, values=values)
     if c.prefix_tokens:
         g = np.random.Generator(np.random.PCG64(kids[_S_SUFFIX]))
         suffix = g.integers(c.suffix_range[0], c.suffix_range[1] + 1, size=c.base_seqs)
