@@ -65,6 +65,58 @@ def cpu_baseline(wl, budget_s: float) -> dict:
             "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
+def kernel_source_sha256() -> str:
+    """Hash of the attention kernel's sources (matches profile records)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("paged_attention_slot_amd/csrc/attn_decode.hip",
+              "paged_attention_slot_amd/csrc/pkv_device.h"):
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the counter record under profiles/ for this
+    kernel and workload, if the kernel sources are unchanged since; else None."""
+    import glob
+    import re
+    sha = kernel_source_sha256()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as fh:
+            for m in re.finditer(r"<!-- pkv-traffic (\{.*?\}) -->", fh.read()):
+                rec = json.loads(m.group(1))
+                if rec["kernel"] == kernel and rec["workload"] == workload and \
+                        rec["source_sha256"] == sha:
+                    return (rec["fetch_kib"] * rec["fetch_scale"] +
+                            rec["write_kib"] * rec["write_scale"]) * 1024.0
+    return None
+
+
+def stream_read_gbps(nbytes: int = 4 << 30, iters: int = 10, workgroups: int = 8192) -> float:
+    """Achievable read rate on this device: libpkv's plain coalesced stream
+    kernel over ``nbytes`` (median of ``iters`` runs, HIP events)."""
+    import numpy as np
+    import torch
+
+    from paged_attention_slot_amd import ops
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(workgroups, dtype=torch.int32, device="cuda")
+    ops.stream_read(buf, sink, workgroups)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        ops.stream_read(buf, sink, workgroups)
+        b.record()
+    torch.cuda.synchronize()
+    t = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    del buf
+    torch.cuda.empty_cache()
+    return nbytes / t / 1e9
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -75,6 +127,8 @@ def main() -> int:
     ap.add_argument("--partition-tokens", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only run the stream-read calibration kernel (4 GiB) and print GB/s")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU; --gpus must be 1 (no multi-GPU path)",
@@ -90,6 +144,9 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
+    if args.calibrate:
+        print(json.dumps({"stream_read_gbps": stream_read_gbps(), "bytes": 4 << 30}), flush=True)
+        return 0
     cfg = CONFIGS[args.config]
     t0 = time.perf_counter()
     wl = config_workload(args.config)
@@ -162,19 +219,20 @@ def main() -> int:
             "max_seq_len": int(lens.max()),
             "num_blocks": wl.num_blocks,
             "cow_pairs": n_cow,
-            "partition_tokens": step.partition_tokens or None,
-            "num_partitions": step.num_parts,
+            "split": step.split,
             "layers_cycled": L,
             "seed": wl.seed,
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "attn_partition_kernel",
+            "kernel": ("attn_balanced_kernel" if step.split["mode"] == "balanced"
+                       else "attn_partition_kernel"),
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": None,
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
             "algorithmic_bytes_per_launch": part_bytes,
             "avg_launch_us": float(np.mean(part)) * 1e6,
         },
@@ -199,6 +257,10 @@ def main() -> int:
                        "gcn_arch": getattr(props, "gcnArchName", "")},
         },
     }
+    res["roofline"]["traffic"] = recorded_traffic(res["roofline"]["kernel"], wl.name)
+    achievable = stream_read_gbps()
+    res["detail"]["stream_read_gbps"] = achievable
+    res["detail"]["partition_frac_of_stream_read"] = achieved / achievable
     if not args.no_cpu_baseline:
         cb = cpu_baseline(wl, args.cpu_budget)
         res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}

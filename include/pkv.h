@@ -111,9 +111,11 @@ pkv_status pkv_copy_blocks(const int32_t* src_dst_pairs, int32_t num_pairs,
                            void* stream);
 
 /* Split-KV partition length (tokens) that pkv_attention_decode uses when its
- * partition_tokens argument is 0.  Returns max_seq_len rounded up to a whole
- * tile (no split) when one partition per sequence is enough, else a multiple
- * of both block_size and 16.  Returns 0 on invalid arguments. */
+ * partition_tokens argument is 0 and it splits by fixed partitions: max_seq_len
+ * rounded up to a whole tile (no split) when one partition per sequence is
+ * enough, else a multiple of both block_size and 16.  Returns 0 when the
+ * automatic plan is the balanced split (shares of equal work per wave group,
+ * see pkv_attention_decode) or on invalid arguments. */
 int32_t pkv_attention_partition_tokens(int32_t num_seqs, int32_t num_q_heads,
                                        int32_t max_seq_len, const pkv_geom* geom);
 
@@ -140,10 +142,13 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *   max_seq_len   host-side upper bound of seq_lens; tokens beyond
  *                 min(max_seq_len, max_blocks_per_seq * block_size) are ignored.
  *   partition_tokens  0 = automatic, else the split-KV partition length (a
- *                 multiple of block_size and of 16).  With more than one
- *                 partition per sequence each partition's (max, sum, weighted
- *                 sum) goes to the workspace and a log-sum-exp merge kernel
- *                 produces out.
+ *                 multiple of block_size and of 16).  With fixed partitions,
+ *                 each partition's (max, sum, weighted sum) goes to the
+ *                 workspace and a log-sum-exp merge kernel produces out.  The
+ *                 automatic plan (up to 4096 sequences) is the balanced split:
+ *                 a persistent grid in which every wave group takes an equal
+ *                 share of all K/V tiles of the batch; a sequence's history
+ *                 that spans several shares is merged the same way.
  *   workspace     device buffer of at least pkv_attention_workspace_bytes(...)
  *                 bytes (may be NULL when that is 0); contents on entry are
  *                 ignored.
@@ -173,6 +178,27 @@ pkv_status pkv_attention_decode_phase(int32_t phases, const void* q, const void*
                                       int32_t partition_tokens, void* workspace,
                                       size_t workspace_bytes, const pkv_geom* geom,
                                       void* stream);
+
+/* Tuning knobs of pkv_attention_decode, read from the environment at each
+ * call (unset or out of range = the library's heuristic):
+ *   PKV_ATTN_HEADS_PER_WAVE  1..4  upper bound on query heads one wave carries
+ *   PKV_ATTN_PREFETCH        2..4  K/V tiles of 16 positions in flight per wave
+ *                                  (bf16 only; fp32 always uses 2)
+ *   PKV_ATTN_WAVES_PER_BLOCK 1,2,4,8  fixed partitions: waves per workgroup
+ *                                  (the waves of one (sequence, partition)
+ *                                  are packed together)
+ *   PKV_ATTN_MODE            1 = fixed partitions, 2 = balanced split
+ * They change speed and register use, never results beyond fp32 rounding
+ * order across query-head groupings (each head's arithmetic is unchanged). */
+
+/* pkv_stream_read -- calibration, not part of the method: reads ``bytes``
+ * (a multiple of 16) from device buffer ``src`` with a plain coalesced
+ * 16-byte-per-lane stream of ``num_workgroups`` x 256 threads, the practical
+ * read-bandwidth ceiling that the attention kernel is compared with.  ``sink``
+ * is a device buffer of num_workgroups uint32 that is only written if the data
+ * hashes to one specific value.  Errors: INVALID_ARG, HIP. */
+pkv_status pkv_stream_read(const void* src, size_t bytes, void* sink, int32_t num_workgroups,
+                           void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* Host block manager (host memory only; one handle must not be used from two */

@@ -9,44 +9,53 @@
 // t % B ([SLOT §locate]).
 //
 // How (MI355X design, not taken from the pages):
-//  * Work item = (sequence, KV head, partition of the sequence's positions).
-//    One wave handles GW query heads of the group against that KV head, so
-//    each K/V byte feeds all of those heads; when the group is larger than GW,
-//    the group's head subsets run as sibling waves of one workgroup (same CU,
-//    so the duplicate K/V reads hit the CU's L1 / the XCD's L2).
-//  * A wave consumes tiles of 16 positions.  Lanes form 8 "streams" of 8
-//    lanes; stream r owns positions r and r+8 of each tile, and lane c of a
-//    stream holds the 16-byte chunks c, c+8, ... of those K and V rows.  Each
-//    load instruction therefore reads 8 full 128-byte row segments; rows of
-//    one block and KV head are 16 B-chunk contiguous, blocks are reached
-//    through the table (contiguous within a block, indirect across blocks).
-//  * q.k: bf16 pairs through v_dot2_f32_bf16 (fp32 accumulate), then a sum over
-//    the 8 lanes of the stream with three DPP adds.
-//  * Online softmax per stream, in log2 units (scale folded with log2 e):
-//    the running reference m is only raised when a tile's maximum exceeds it by
-//    more than 8, so the accumulator is rescaled rarely; since softmax does not
-//    depend on the reference, the result equals the running-max form.
-//  * At the end the 8 streams are merged with DPP row_ror:8 and the gfx950
-//    permlane16/permlane32 swaps (log-sum-exp rescale), then either the
-//    normalised output is written or, with split-KV, the partition's
-//    (reference, sum, weighted sum) go to the workspace for attn_merge_kernel.
-//  * Tiles are double-buffered in registers (loads of tile t+1 are in flight
-//    while tile t is computed); the partition's block ids are fetched once per
-//    64 blocks into a VGPR and read with v_readlane, so every K/V load has a
-//    scalar base and a loop-invariant per-lane offset.
+//  * A "stream" is the K/V history of one (sequence, KV head).  A wave walks a
+//    stretch of it in tiles of 16 positions for GW query heads of the group, so
+//    each K/V byte feeds all of those heads.  When the group has more heads than
+//    one wave carries, sibling waves of one workgroup walk the same tiles (the
+//    repeated reads hit that CU's L1 / the XCD's L2).
+//  * Lanes form 8 sub-streams of 8 lanes: sub-stream r owns positions r and r+8
+//    of each tile, lane c of it holds 16-byte chunks c, c+8, ... of those K and
+//    V rows, so one load instruction reads 8 full 128-byte row segments.
+//  * q.k: bf16 pairs through v_dot2_f32_bf16 (fp32 accumulate) and a sum over
+//    the 8 lanes with three DPP adds.  Online softmax per sub-stream in log2
+//    units; the reference m only moves when a tile's maximum exceeds it by more
+//    than 8 (softmax does not depend on the reference, so the result is the
+//    running-max form's).  At the end the sub-streams are merged with DPP
+//    row_ror:8 and the gfx950 permlane16/permlane32 swaps.
+//  * Tiles sit in a ring of P register buffers (P-1 tiles in flight while one is
+//    consumed); block ids come from a VGPR cache of 64 table entries read with
+//    v_readlane, so each load has a scalar base and a fixed lane offset.
+//  * Balanced mode (default): a persistent grid of as many wave groups as the
+//    GPU holds at once.  All streams, sequence by sequence, form one global
+//    sequence of tiles; group w takes the w-th equal share of it.  A share that
+//    covers a whole stream writes the output; otherwise it writes a (reference,
+//    sum, weighted sum) piece, and attn_merge_balanced_kernel combines the
+//    pieces of each stream by log-sum-exp rescaling.  Every group does the same
+//    amount of work, and no group waits for a launch slot.
+//  * Partition mode (explicit partition_tokens, or batches past the balanced
+//    limits): one work item per (sequence, partition, KV head); the partition
+//    states are merged by attn_merge_kernel.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
+#include <mutex>
+#include <unordered_map>
 
 #include "geom.h"
 #include "pkv_device.h"
 
 namespace {
 
-constexpr int kTile = 16;              // positions per tile (8 streams x 2)
-constexpr int kMaxWavesPerBlock = 4;   // workgroup <= 256 threads
-constexpr float kRescaleSlack = 8.0f;  // log2 units before the reference moves
-constexpr float kRefInit = -1e30f;     // reference of a stream with no position yet
+constexpr int kTile = 16;               // positions per tile (8 sub-streams x 2)
+constexpr int kMaxWavesPerBlock = 8;    // workgroup <= 512 threads
+constexpr float kRescaleSlack = 8.0f;   // log2 units before the reference moves
+constexpr float kRefInit = -1e30f;      // reference of a sub-stream with no position yet
+constexpr int kMaxBalancedSeqs = 4096;  // per-sequence prefix sums live in LDS
+constexpr int kMaxWaveGroups = 8192;    // the workspace is sized for this many groups
+
+enum Mode : int { kPartitionMode = 0, kBalancedMode = 1 };
 
 struct AttnArgs {
   const void* q;
@@ -55,21 +64,28 @@ struct AttnArgs {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   void* out;
-  float* ws_acc;      // [N][Hq][P][D]
-  float* ws_ml;       // [N][Hq][P][2] = (reference, sum)
+  float* ws_acc;            // rows of D floats (unnormalised weighted sums)
+  float2* ws_ml;            // (reference, sum) per row of ws_acc
+  int32_t* ws_base;         // balanced: prefix sums of stream tiles [N+1]
   int64_t block_bytes;
   int32_t row_bytes;
   int32_t max_blocks;
+  int32_t num_seqs;
   int32_t num_q_heads;
-  int32_t group;      // G = Hq / Hkv
-  int32_t waves_per_group;
-  int32_t waves_per_block;
-  int32_t blocks_per_group;
+  int32_t num_kv_heads;
+  int32_t group;            // G = Hq / Hkv
+  int32_t waves_per_group;  // waves sharing one KV head (G / heads per wave)
+  int32_t waves_per_block;  // waves of one workgroup
   int32_t num_blocks;
   int32_t block_shift;
   int32_t len_cap;
+  // partition mode
+  int32_t waves_per_item;   // H_kv * waves_per_group
   int32_t part_tokens;
   int32_t num_parts;
+  // balanced mode
+  int32_t groups_per_block; // wave groups per workgroup
+  int32_t num_groups;       // W: wave groups in the grid
   float scale_log2;
 };
 
@@ -92,8 +108,9 @@ struct TileBuf {
 struct TileInfo {
   int start;      // first position of the tile
   int nvalid;     // valid positions in the tile (1..16)
-  bool ok0, ok1;  // block of positions start+[0,8) / start+[8,16) is in the pool
 };
+
+__device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 
 template <typename T>
 __device__ __forceinline__ void unpack(const uint4& x, float (&f)[16 / sizeof(T)]) {
@@ -139,50 +156,56 @@ __device__ __forceinline__ uint4 pack_chunk(const float* f) {
   return o;
 }
 
-template <typename T, int D, int GW>
+// One wave's attention over a stretch [start, end) of one stream.
+template <typename T, int D, int GW, int P>
 struct Wave {
   using S = Shape<T, D>;
   static constexpr int kCPL = S::kCPL, kEPC = S::kEPC, kNE = S::kNE;
 
   const AttnArgs& a;
   int lane, r, c;
-  const int32_t* trow;   // this sequence's block-table row
-  int blk_last;          // last block index this work item may read
+  const int32_t* trow;   // the sequence's block-table row
+  int blk_last;          // last block index this stretch may read
   int tcache_base;       // first block index held in tcache
   int tcache;            // lane i: block id of index tcache_base + i
-  int64_t head_off;      // byte offset of this KV head inside a pool row
+  int64_t head_off;      // byte offset of the KV head inside a pool row
+  int blk[2];
 
   uint4 q[GW][kCPL];
   float m[GW], l[GW], acc[GW][kNE];
+  float M[GW], lt[GW];   // after run(): merged reference and sum
 
-  __device__ Wave(const AttnArgs& args) : a(args) {}
+  __device__ explicit Wave(const AttnArgs& args) : a(args) {
+    lane = threadIdx.x & 63;
+    r = lane >> 3;
+    c = lane & 7;
+  }
 
+  // Physical block of position ``pos`` (uniform).  Ids out of the pool are
+  // redirected to block 0: memory stays in bounds, the values read for them
+  // are unspecified.
   __device__ __forceinline__ int block_id(int pos) {
     const int idx = pos >> a.block_shift;
     if (idx - tcache_base >= 64) {
       tcache_base = idx;
-      tcache = (idx + lane <= blk_last) ? trow[idx + lane] : -1;
+      tcache = (idx + lane <= blk_last) ? trow[idx + lane] : 0;
+      // Wait for the reload here, in this rare branch; otherwise every
+      // v_readlane below would wait for all loads in flight (tile prefetches
+      // included), since the compiler cannot tell which path wrote tcache.
+      asm volatile("" ::"v"(tcache));
     }
-    return __builtin_amdgcn_readlane(tcache, idx - tcache_base);
+    const int b = __builtin_amdgcn_readlane(tcache, idx - tcache_base);
+    return (b >= 0 && b < a.num_blocks) ? b : 0;
   }
 
   __device__ __forceinline__ TileInfo prepare(int tile_start, int end) {
     TileInfo t;
     t.start = tile_start;
     t.nvalid = min(kTile, end - tile_start);
-    const int b0 = block_id(tile_start);
-    t.ok0 = b0 >= 0 && b0 < a.num_blocks;
-    int b1 = b0;
-    t.ok1 = t.ok0;
-    if (a.block_shift < 4 && t.nvalid > 8) {  // block_size 8: second block
-      b1 = block_id(tile_start + 8);
-      t.ok1 = b1 >= 0 && b1 < a.num_blocks;
-    }
-    blk[0] = t.ok0 ? b0 : 0;
-    blk[1] = t.ok1 ? b1 : 0;
+    blk[0] = block_id(tile_start);
+    blk[1] = (a.block_shift < 4 && t.nvalid > 8) ? block_id(tile_start + 8) : blk[0];
     return t;
   }
-  int blk[2];
 
   __device__ __forceinline__ void load(const TileInfo& t, TileBuf<T, D>& b) {
     const int bmask = (1 << a.block_shift) - 1;
@@ -205,8 +228,8 @@ struct Wave {
   template <bool kMasked>
   __device__ __forceinline__ void consume(const TileInfo& t, const TileBuf<T, D>& b) {
     bool valid[2];
-    valid[0] = r < t.nvalid && t.ok0;
-    valid[1] = r + 8 < t.nvalid && t.ok1;
+    valid[0] = r < t.nvalid;
+    valid[1] = r + 8 < t.nvalid;
 
     float sc[2][GW];
 #pragma unroll
@@ -273,107 +296,74 @@ struct Wave {
     }
   }
 
-  __device__ __forceinline__ void run_tile(const TileInfo& t, const TileBuf<T, D>& b) {
-    if (t.nvalid == kTile && t.ok0 && t.ok1) consume<false>(t, b);
-    else consume<true>(t, b);
-  }
-};
-
-template <typename T, int D, int GW>
-__global__ void __launch_bounds__(256)
-attn_partition_kernel(AttnArgs a) {
-  using S = Shape<T, D>;
-  constexpr int kCPL = S::kCPL, kEPC = S::kEPC, kNE = S::kNE;
-  const int kvh = blockIdx.x / a.blocks_per_group;
-  const int sub = blockIdx.x - kvh * a.blocks_per_group;
-  const int wave = sub * a.waves_per_block + (threadIdx.x >> 6);
-  if (wave >= a.waves_per_group) return;
-  const int part = blockIdx.y;
-  const int s = blockIdx.z;
-
-  Wave<T, D, GW> w(a);
-  w.lane = threadIdx.x & 63;
-  w.r = w.lane >> 3;
-  w.c = w.lane & 7;
-
-  int L = a.seq_lens[s];
-  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-  const int start = part * a.part_tokens;
-  const int h0 = kvh * a.group + wave * GW;
-  char* out_base = static_cast<char*>(a.out) + (int64_t(s) * a.num_q_heads + h0) * (D * S::kES);
-
-  if (start >= L) {
-    // Empty history (L == 0): the output is zero.  With split-KV the merge
-    // kernel writes it instead.
-    if (part == 0 && a.num_parts == 1 && w.r == 0) {
+  // Attention of query heads h0 .. h0+GW-1 of sequence s over positions
+  // [start, end) of KV head kvh (start < end).  Leaves the merged state in M,
+  // lt and acc (identical in every lane holding a given chunk).
+  __device__ __forceinline__ void run(int s, int kvh, int h0, int start, int end) {
+    const char* q_base =
+        static_cast<const char*>(a.q) + (int64_t(s) * a.num_q_heads + h0) * (D * S::kES);
 #pragma unroll
-      for (int hh = 0; hh < GW; ++hh)
+    for (int hh = 0; hh < GW; ++hh) {
 #pragma unroll
-        for (int j = 0; j < kCPL; ++j)
-          *reinterpret_cast<uint4*>(out_base + hh * D * S::kES + (w.c + 8 * j) * 16) =
-              make_uint4(0, 0, 0, 0);
+      for (int j = 0; j < kCPL; ++j)
+        q[hh][j] = *reinterpret_cast<const uint4*>(q_base + hh * D * S::kES + (c + 8 * j) * 16);
+      m[hh] = kRefInit;
+      l[hh] = 0.f;
+#pragma unroll
+      for (int e = 0; e < kNE; ++e) acc[hh][e] = 0.f;
     }
-    return;
-  }
-  const int end = min(start + a.part_tokens, L);
 
-  const char* q_base =
-      static_cast<const char*>(a.q) + (int64_t(s) * a.num_q_heads + h0) * (D * S::kES);
-#pragma unroll
-  for (int hh = 0; hh < GW; ++hh) {
-#pragma unroll
-    for (int j = 0; j < kCPL; ++j)
-      w.q[hh][j] = *reinterpret_cast<const uint4*>(q_base + hh * D * S::kES + (w.c + 8 * j) * 16);
-    w.m[hh] = kRefInit;
-    w.l[hh] = 0.f;
-#pragma unroll
-    for (int e = 0; e < kNE; ++e) w.acc[hh][e] = 0.f;
-  }
+    trow = a.block_tables + int64_t(s) * a.max_blocks;
+    blk_last = (end - 1) >> a.block_shift;
+    const int blk_first = start >> a.block_shift;
+    tcache_base = blk_first;
+    tcache = (blk_first + lane <= blk_last) ? trow[blk_first + lane] : 0;
+    asm volatile("" ::"v"(tcache));
+    head_off = int64_t(kvh) * D * S::kES;
 
-  w.trow = a.block_tables + int64_t(s) * a.max_blocks;
-  w.blk_last = (end - 1) >> a.block_shift;
-  const int blk_first = start >> a.block_shift;
-  w.tcache_base = blk_first;
-  w.tcache = (blk_first + w.lane <= w.blk_last) ? w.trow[blk_first + w.lane] : -1;
-  w.head_off = int64_t(kvh) * D * S::kES;
-
-  const int ntiles = (end - start + kTile - 1) / kTile;
-  TileBuf<T, D> b0, b1;
-  TileInfo t0 = w.prepare(start, end);
-  w.load(t0, b0);
-  for (int t = 0;;) {
-    TileInfo t1;
-    const bool has1 = t + 1 < ntiles;
-    if (has1) {
-      t1 = w.prepare(start + kTile * (t + 1), end);
-      w.load(t1, b1);
+    // Ring of P register tile buffers, unrolled P times so each buffer keeps
+    // its registers.  Tiles 0 .. ntiles-2 are full; the tail (the last <= P
+    // tiles) runs the masked path.
+    const int ntiles = (end - start + kTile - 1) / kTile;
+    TileBuf<T, D> buf[P];
+    TileInfo info[P];
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+      if (k < ntiles) {
+        info[k] = prepare(start + kTile * k, end);
+        load(info[k], buf[k]);
+      }
     }
-    w.run_tile(t0, b0);
-    if (!has1) break;
-    ++t;
-    const bool has2 = t + 1 < ntiles;
-    if (has2) {
-      t0 = w.prepare(start + kTile * (t + 1), end);
-      w.load(t0, b0);
+    int t = 0;
+    for (; t + P < ntiles; t += P) {
+#pragma unroll
+      for (int k = 0; k < P; ++k) {
+        consume<false>(info[k], buf[k]);
+        if (t + k + P < ntiles) {
+          info[k] = prepare(start + kTile * (t + k + P), end);
+          load(info[k], buf[k]);
+        }
+      }
     }
-    w.run_tile(t1, b1);
-    if (!has2) break;
-    ++t;
+#pragma unroll
+    for (int k = 0; k < P; ++k)
+      if (t + k < ntiles) consume<true>(info[k], buf[k]);
+
+    // Merge the 8 sub-streams (log-sum-exp rescale to the common reference).
+#pragma unroll
+    for (int hh = 0; hh < GW; ++hh) {
+      M[hh] = pkv::max_across_groups8(m[hh]);
+      const float wt = pkv::fast_exp2(m[hh] - M[hh]);
+      lt[hh] = pkv::sum_across_groups8(l[hh] * wt);
+#pragma unroll
+      for (int e = 0; e < kNE; ++e) acc[hh][e] = pkv::sum_across_groups8(acc[hh][e] * wt);
+    }
   }
 
-  // Merge the 8 streams (log-sum-exp rescale to the common reference).
-  float lt[GW], M[GW];
-#pragma unroll
-  for (int hh = 0; hh < GW; ++hh) {
-    M[hh] = pkv::max_across_groups8(w.m[hh]);
-    const float wt = pkv::fast_exp2(w.m[hh] - M[hh]);
-    lt[hh] = pkv::sum_across_groups8(w.l[hh] * wt);
-#pragma unroll
-    for (int e = 0; e < kNE; ++e) w.acc[hh][e] = pkv::sum_across_groups8(w.acc[hh][e] * wt);
-  }
-  if (w.r != 0) return;
-
-  if (a.num_parts == 1) {
+  // Normalised output rows of heads h0 .. h0+GW-1 (sub-stream 0 stores).
+  __device__ __forceinline__ void write_out(int s, int h0) {
+    if (r != 0) return;
+    char* out_base = static_cast<char*>(a.out) + (int64_t(s) * a.num_q_heads + h0) * (D * S::kES);
 #pragma unroll
     for (int hh = 0; hh < GW; ++hh) {
       const float inv = 1.0f / lt[hh];
@@ -381,113 +371,342 @@ attn_partition_kernel(AttnArgs a) {
       for (int j = 0; j < kCPL; ++j) {
         float f[kEPC];
 #pragma unroll
-        for (int e = 0; e < kEPC; ++e) f[e] = w.acc[hh][j * kEPC + e] * inv;
-        *reinterpret_cast<uint4*>(out_base + hh * D * S::kES + (w.c + 8 * j) * 16) =
+        for (int e = 0; e < kEPC; ++e) f[e] = acc[hh][j * kEPC + e] * inv;
+        *reinterpret_cast<uint4*>(out_base + hh * D * S::kES + (c + 8 * j) * 16) =
             pack_chunk<T>(f);
       }
     }
-  } else {
+  }
+
+  // Zero output rows (empty history).
+  __device__ __forceinline__ void write_zero(int s, int h0) {
+    if (r != 0) return;
+    char* out_base = static_cast<char*>(a.out) + (int64_t(s) * a.num_q_heads + h0) * (D * S::kES);
+#pragma unroll
+    for (int hh = 0; hh < GW; ++hh)
+#pragma unroll
+      for (int j = 0; j < kCPL; ++j)
+        *reinterpret_cast<uint4*>(out_base + hh * D * S::kES + (c + 8 * j) * 16) =
+            make_uint4(0, 0, 0, 0);
+  }
+
+  // Unnormalised state of head hh to workspace row row0 + hh * row_stride.
+  __device__ __forceinline__ void write_piece(int64_t row0, int64_t row_stride) {
+    if (r != 0) return;
 #pragma unroll
     for (int hh = 0; hh < GW; ++hh) {
-      const int64_t row = (int64_t(s) * a.num_q_heads + h0 + hh) * a.num_parts + part;
+      const int64_t row = row0 + hh * row_stride;
       float* dst = a.ws_acc + row * D;
 #pragma unroll
       for (int j = 0; j < kCPL; ++j) {
 #pragma unroll
         for (int e4 = 0; e4 < kEPC; e4 += 4) {
-          const int elem = (w.c + 8 * j) * kEPC + e4;
+          const int elem = (c + 8 * j) * kEPC + e4;
           const int src = j * kEPC + e4;
           *reinterpret_cast<float4*>(dst + elem) =
-              make_float4(w.acc[hh][src], w.acc[hh][src + 1], w.acc[hh][src + 2],
-                          w.acc[hh][src + 3]);
+              make_float4(acc[hh][src], acc[hh][src + 1], acc[hh][src + 2], acc[hh][src + 3]);
         }
       }
-      if (w.c == 0) *reinterpret_cast<float2*>(a.ws_ml + row * 2) = make_float2(M[hh], lt[hh]);
+      if (c == 0) a.ws_ml[row] = make_float2(M[hh], lt[hh]);
     }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Partition mode: one wave per (sequence, partition, KV head, head subset).
+// ---------------------------------------------------------------------------
+template <typename T, int D, int GW, int P>
+__global__ void __launch_bounds__(64 * kMaxWavesPerBlock)
+attn_partition_kernel(AttnArgs a) {
+  // The waves of one (sequence, partition) are numbered consecutively and
+  // packed into workgroups.
+  const int wi = blockIdx.x * a.waves_per_block + (threadIdx.x >> 6);
+  if (wi >= a.waves_per_item) return;
+  const int kvh = wi / a.waves_per_group;
+  const int sub = wi - kvh * a.waves_per_group;
+  const int part = blockIdx.y;
+  const int s = blockIdx.z;
+  const int h0 = kvh * a.group + sub * GW;
+
+  Wave<T, D, GW, P> w(a);
+  const int L = clamp_len(a.seq_lens[s], a.len_cap);
+  const int start = part * a.part_tokens;
+  if (start >= L) {
+    // Empty history (L == 0): the output is zero.  With more than one
+    // partition the merge kernel writes it instead.
+    if (part == 0 && a.num_parts == 1) w.write_zero(s, h0);
+    return;
+  }
+  w.run(s, kvh, h0, start, min(start + a.part_tokens, L));
+  if (a.num_parts == 1) {
+    w.write_out(s, h0);
+  } else {
+    const int64_t row0 = (int64_t(s) * a.num_q_heads + h0) * a.num_parts + part;
+    w.write_piece(row0, a.num_parts);
   }
 }
 
-// Split-KV merge: one workgroup (4 waves) per (sequence, query head).  Wave w
-// folds partitions w, w+4, ...; the 4 partial results meet in LDS.
+// ---------------------------------------------------------------------------
+// Log-sum-exp merge of n workspace rows row0, row0 + step, ... into one output
+// row, by one 256-thread workgroup:
+//   1. the common reference M = max_p m_p (threads stride over the rows),
+//   2. weights w_p = exp2(m_p - M) into LDS and sum_p w_p l_p,
+//   3. sum_p w_p acc_p: thread (stream, q) accumulates float4 column q of rows
+//      p = stream (mod kStreams), all loads independent,
+//   4. the partial rows meet in LDS; out = acc / l (zeros when n == 0).
+// ---------------------------------------------------------------------------
+constexpr int kMergeThreads = 256;
+constexpr int kMergeChunk = 1024;  // rows whose weights sit in LDS at once
+
 template <typename T, int D>
-__global__ void __launch_bounds__(256)
+__device__ __forceinline__ void merge_rows(const AttnArgs& a, int n, int64_t row0, int64_t step,
+                                           char* dst_row) {
+  constexpr int kQ = D / 4;                        // float4 columns per row
+  constexpr int kStreams = kMergeThreads / kQ;     // rows folded in parallel
+  const int tid = threadIdx.x, wv = tid >> 6;
+  const float4* acc4 = reinterpret_cast<const float4*>(a.ws_acc);
+
+  __shared__ float red[4];
+  __shared__ float wts[kMergeChunk];
+  __shared__ float4 part_out[kStreams][kQ];
+
+  float mx = -INFINITY;
+  for (int p = tid; p < n; p += kMergeThreads) mx = fmaxf(mx, a.ws_ml[row0 + p * step].x);
+  mx = pkv::wave_max(mx);
+  if ((tid & 63) == 0) red[wv] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+
+  const int stream = tid / kQ, q = tid % kQ;
+  float ls = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c0 = 0; c0 < n; c0 += kMergeChunk) {
+    const int c1 = min(n, c0 + kMergeChunk);
+    for (int p = c0 + tid; p < c1; p += kMergeThreads) {
+      const float2 v = a.ws_ml[row0 + p * step];
+      const float wt = pkv::fast_exp2(v.x - M);
+      wts[p - c0] = wt;
+      ls = fmaf(wt, v.y, ls);
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int p = c0 + stream; p < c1; p += kStreams) {
+      const float wt = wts[p - c0];
+      const float4 x = acc4[(row0 + p * step) * kQ + q];
+      o.x = fmaf(wt, x.x, o.x);
+      o.y = fmaf(wt, x.y, o.y);
+      o.z = fmaf(wt, x.z, o.z);
+      o.w = fmaf(wt, x.w, o.w);
+    }
+    __syncthreads();
+  }
+  ls = pkv::wave_sum(ls);
+  if ((tid & 63) == 0) red[wv] = ls;
+  part_out[stream][q] = o;
+  __syncthreads();
+  if (tid >= kQ) return;
+  const float lsum = (red[0] + red[1]) + (red[2] + red[3]);
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  float4 rr = part_out[0][q];
+#pragma unroll
+  for (int k = 1; k < kStreams; ++k) {
+    const float4 x = part_out[k][q];
+    rr.x += x.x; rr.y += x.y; rr.z += x.z; rr.w += x.w;
+  }
+  const float f[4] = {rr.x * inv, rr.y * inv, rr.z * inv, rr.w * inv};
+  if constexpr (sizeof(T) == 2) {
+    reinterpret_cast<uint2*>(dst_row)[q] =
+        make_uint2(pkv::pack_bf16x2(f[0], f[1]), pkv::pack_bf16x2(f[2], f[3]));
+  } else {
+    reinterpret_cast<float4*>(dst_row)[q] = make_float4(f[0], f[1], f[2], f[3]);
+  }
+}
+
+// Partition mode merge: one workgroup per (query head, sequence).
+template <typename T, int D>
+__global__ void __launch_bounds__(kMergeThreads)
 attn_merge_kernel(AttnArgs a) {
-  constexpr int kDPL = D / 64;  // dims per lane
   const int h = blockIdx.x, s = blockIdx.y;
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  int L = a.seq_lens[s];
-  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
+  const int L = clamp_len(a.seq_lens[s], a.len_cap);
   const int np = (L + a.part_tokens - 1) / a.part_tokens;
   const int64_t row0 = (int64_t(s) * a.num_q_heads + h) * a.num_parts;
-  const float* ml = a.ws_ml + row0 * 2;
-  const float* accp = a.ws_acc + row0 * D;
-
-  __shared__ float red_m[4];
-  __shared__ float red_l[4];
-  __shared__ float red_o[4][D];
-
-  float Mw = -INFINITY;
-  for (int p = wv; p < np; p += 4) Mw = fmaxf(Mw, ml[2 * p]);
-  if (lane == 0) red_m[wv] = Mw;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
-
-  float ls = 0.f, o[kDPL];
-#pragma unroll
-  for (int d = 0; d < kDPL; ++d) o[d] = 0.f;
-  for (int p = wv; p < np; p += 4) {
-    const float wt = pkv::fast_exp2(ml[2 * p] - M);
-    ls = fmaf(wt, ml[2 * p + 1], ls);
-    const float* src = accp + int64_t(p) * D + lane * kDPL;
-#pragma unroll
-    for (int d = 0; d < kDPL; ++d) o[d] = fmaf(wt, src[d], o[d]);
-  }
-  if (lane == 0) red_l[wv] = ls;
-#pragma unroll
-  for (int d = 0; d < kDPL; ++d) red_o[wv][lane * kDPL + d] = o[d];
-  __syncthreads();
-  if (wv != 0) return;
-  const float lsum = red_l[0] + red_l[1] + red_l[2] + red_l[3];
-  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;  // np == 0: zeros
   char* dst = static_cast<char*>(a.out) + ((int64_t(s) * a.num_q_heads + h) * D) * sizeof(T);
-  float f[kDPL];
+  merge_rows<T, D>(a, np, row0, 1, dst);
+}
+
+// ---------------------------------------------------------------------------
+// Balanced mode.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int stream_tiles(const AttnArgs& a, int s) {
+  return (clamp_len(a.seq_lens[s], a.len_cap) + kTile - 1) / kTile;
+}
+
+// Share of wave group w in a global order of T tiles cut into W shares:
+// [floor(T*w/W), floor(T*(w+1)/W)).  With W <= T every share is non-empty.
+__device__ __forceinline__ int64_t share_lo(int64_t T, int w, int W) { return T * w / W; }
+
+// The share holding global tile x (0 <= x < T): the largest w with
+// floor(T*w/W) <= x, i.e. floor(((x+1)*W - 1) / T).
+__device__ __forceinline__ int share_of(int64_t x, int64_t T, int W) {
+  return static_cast<int>(((x + 1) * W - 1) / T);
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int d = 0; d < kDPL; ++d) {
-    const int e = lane * kDPL + d;
-    f[d] = ((red_o[0][e] + red_o[1][e]) + (red_o[2][e] + red_o[3][e])) * inv;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
   }
-  if constexpr (sizeof(T) == 2) {
-    if constexpr (kDPL == 2) {
-      reinterpret_cast<uint32_t*>(dst)[lane] = pkv::pack_bf16x2(f[0], f[1]);
-    } else {
-      reinterpret_cast<uint16_t*>(dst)[lane] = uint16_t(pkv::f32_to_bf16_bits(f[0]));
+  return x;
+}
+
+template <typename T, int D, int GW, int P>
+__global__ void __launch_bounds__(64 * kMaxWavesPerBlock)
+attn_balanced_kernel(AttnArgs a) {
+  __shared__ int32_t base[kMaxBalancedSeqs + 1];
+  __shared__ int32_t wave_tot[kMaxWavesPerBlock];
+  const int N = a.num_seqs, Hkv = a.num_kv_heads;
+  const int tid = threadIdx.x, nth = blockDim.x, lane = tid & 63, wv = tid >> 6;
+
+  // base[s] = sum over s' < s of H_kv * tiles(s'): every thread sums a
+  // contiguous run of sequences, then a block-wide exclusive scan.
+  const int per = (N + nth - 1) / nth;
+  const int s0 = tid * per;
+  int tsum = 0;
+  for (int i = 0; i < per; ++i)
+    if (s0 + i < N) tsum += Hkv * stream_tiles(a, s0 + i);
+  const int incl = wave_incl_scan(tsum);
+  if (lane == 63) wave_tot[wv] = incl;
+  __syncthreads();
+  int off = 0, total = 0;
+  for (int k = 0; k < (nth >> 6); ++k) {
+    off += k < wv ? wave_tot[k] : 0;
+    total += wave_tot[k];
+  }
+  int run = off + incl - tsum;
+  for (int i = 0; i < per; ++i) {
+    if (s0 + i < N) {
+      base[s0 + i] = run;
+      run += Hkv * stream_tiles(a, s0 + i);
     }
-  } else {
-#pragma unroll
-    for (int d = 0; d < kDPL; ++d) reinterpret_cast<float*>(dst)[lane * kDPL + d] = f[d];
   }
+  if (tid == 0) base[N] = total;
+  __syncthreads();
+  if (blockIdx.x == 0)  // the merge kernel reads the same prefix sums
+    for (int i = tid; i <= N; i += nth) a.ws_base[i] = base[i];
+
+  const int grp = wv / a.waves_per_group;
+  const int sub = wv - grp * a.waves_per_group;
+  if (grp >= a.groups_per_block || total == 0) return;
+  const int W = min(a.num_groups, total);  // every share non-empty
+  const int gidx = blockIdx.x * a.groups_per_block + grp;
+  if (gidx >= W) return;
+  const int64_t ttot = total;
+  int64_t cur = share_lo(ttot, gidx, W);
+  const int64_t hi = share_lo(ttot, gidx + 1, W);
+
+  Wave<T, D, GW, P> w(a);
+  while (cur < hi) {
+    // The sequence holding global tile `cur`: the largest s with base[s] <= cur.
+    int lo_s = 0, hi_s = N - 1;
+    while (lo_s < hi_s) {
+      const int mid = (lo_s + hi_s + 1) >> 1;
+      if (base[mid] <= cur) lo_s = mid;
+      else hi_s = mid - 1;
+    }
+    const int s = lo_s;
+    const int nt = (base[s + 1] - base[s]) / Hkv;
+    const int rel = static_cast<int>(cur - base[s]);
+    const int kvh = rel / nt;
+    const int t0 = rel - kvh * nt;
+    const int seg = static_cast<int>(min(hi - cur, int64_t(nt - t0)));
+    const int L = clamp_len(a.seq_lens[s], a.len_cap);
+    const int h0 = kvh * a.group + sub * GW;
+    w.run(s, kvh, h0, t0 * kTile, min((t0 + seg) * kTile, L));
+    if (t0 == 0 && seg == nt) {
+      w.write_out(s, h0);  // the whole stream in one share
+    } else {
+      // piece of stream k from share gidx -> row group (k + gidx): unique,
+      // since streams and shares are both contiguous and in the same order.
+      const int64_t k = int64_t(s) * Hkv + kvh;
+      w.write_piece((k + gidx) * a.group + sub * GW, 1);
+    }
+    cur += seg;
+  }
+}
+
+// Balanced mode merge: one workgroup per (query head, sequence); combines the
+// pieces its stream left in consecutive shares (nothing to do when one share
+// held the whole stream, zeros for an empty history).
+template <typename T, int D>
+__global__ void __launch_bounds__(kMergeThreads)
+attn_merge_balanced_kernel(AttnArgs a) {
+  const int h = blockIdx.x, s = blockIdx.y;
+  const int G = a.group;
+  const int g = h / G, j = h - g * G;
+  const int nt = stream_tiles(a, s);
+  char* dst = static_cast<char*>(a.out) + ((int64_t(s) * a.num_q_heads + h) * D) * sizeof(T);
+  if (nt == 0) {
+    merge_rows<T, D>(a, 0, 0, 0, dst);
+    return;
+  }
+  const int64_t ttot = a.ws_base[a.num_seqs];
+  const int W = static_cast<int>(min<int64_t>(a.num_groups, ttot));
+  const int64_t start = int64_t(a.ws_base[s]) + int64_t(g) * nt;
+  const int w0 = share_of(start, ttot, W);
+  const int w1 = share_of(start + nt - 1, ttot, W);
+  if (w0 == w1) return;
+  const int64_t k = int64_t(s) * a.num_kv_heads + g;
+  merge_rows<T, D>(a, w1 - w0 + 1, (k + w0) * G + j, G, dst);
 }
 
 // ---------------------------------------------------------------------------
 // Host side: planning, validation, dispatch.
 // ---------------------------------------------------------------------------
 
-struct Plan {
-  int gw, waves_per_group, waves_per_block, blocks_per_group;
-  int len_cap, part_tokens, num_parts;
-  size_t ws_bytes;
-};
+// Tuning knobs read from the environment at each call (documented in
+// include/pkv.h).  0 = the heuristic.
+int env_knob(const char* name, int lo, int hi) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return 0;
+  const int x = std::atoi(v);
+  return (x >= lo && x <= hi) ? x : 0;
+}
+int knob_heads_per_wave() { return env_knob("PKV_ATTN_HEADS_PER_WAVE", 1, 4); }
+int knob_prefetch() { return env_knob("PKV_ATTN_PREFETCH", 2, 4); }
+int knob_mode() { return env_knob("PKV_ATTN_MODE", 1, 2); }  // 1 partition, 2 balanced
+int knob_waves_per_block() {
+  const int v = env_knob("PKV_ATTN_WAVES_PER_BLOCK", 1, kMaxWavesPerBlock);
+  return (v & (v - 1)) == 0 ? v : 0;
+}
 
-int heads_per_wave(int G) {
+// Query heads per wave: the largest of 4, 3, 2, 1 dividing the group size that
+// fits the register file without spilling (fp32 rows of 128 hold twice the
+// registers of bf16 ones, so they stop at 2).
+int heads_per_wave(int G, int dtype, int head_dim) {
+  int cap = (dtype == PKV_F32 && head_dim == 128) ? 2 : 4;
+  if (const int k = knob_heads_per_wave()) cap = k < cap ? k : cap;
   for (int gw : {4, 3, 2, 1})
-    if (G % gw == 0) return gw;
+    if (gw <= cap && G % gw == 0) return gw;
   return 1;
+}
+
+// Tiles per wave in the register ring.  Two (one in flight while one is
+// consumed) measured best with the balanced split; fixed partitions with few
+// heads per wave gain a little from three.
+int prefetch_depth(int gw, int dtype, bool balanced) {
+  if (dtype == PKV_F32) return 2;
+  if (const int k = knob_prefetch()) return k;
+  return (!balanced && gw <= 2) ? 3 : 2;
 }
 
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
-// Default split-KV partition: 256 positions up to 4096-long contexts, 512
-// beyond; no split when one partition covers the longest sequence.
+// Default split-KV partition of partition mode: 256 positions up to 4096-long
+// contexts, 512 beyond; no split when one partition covers the longest one.
 int auto_partition(int32_t max_seq_len, int32_t block_size) {
   const int unit = block_size > kTile ? block_size : kTile;
   int64_t t = max_seq_len <= 4096 ? 256 : 512;
@@ -495,6 +714,18 @@ int auto_partition(int32_t max_seq_len, int32_t block_size) {
   if (max_seq_len <= t) return static_cast<int>(round_up(max_seq_len > 0 ? max_seq_len : 1, unit));
   return static_cast<int>(t);
 }
+
+struct Plan {
+  int mode;
+  int gw, prefetch, waves_per_group, waves_per_block;
+  int len_cap;
+  // partition mode
+  int waves_per_item, blocks_per_item, part_tokens, num_parts;
+  // balanced mode
+  int groups_per_block;
+  int64_t rows;  // workspace rows of D floats
+  size_t ws_bytes, ws_ml_off, ws_base_off;
+};
 
 pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
                      int32_t max_blocks, int32_t partition_tokens, const pkv_geom* g,
@@ -512,65 +743,174 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
   const int G = num_q_heads / g->num_kv_heads;
   if (G > 64) return pkv::fail(PKV_ERR_UNSUPPORTED, "%s: more than 64 query heads per group", who);
   if (num_seqs > 65535) return pkv::fail(PKV_ERR_INVALID_ARG, "%s: more than 65535 sequences", who);
-  pl->gw = heads_per_wave(G);
-  pl->waves_per_group = G / pl->gw;
-  pl->waves_per_block =
-      pl->waves_per_group < kMaxWavesPerBlock ? pl->waves_per_group : kMaxWavesPerBlock;
-  pl->blocks_per_group = (pl->waves_per_group + pl->waves_per_block - 1) / pl->waves_per_block;
-  const int64_t cap = int64_t(max_blocks) * g->block_size;
-  pl->len_cap = static_cast<int>(max_seq_len < cap ? max_seq_len : cap);
   if (partition_tokens < 0)
     return pkv::fail(PKV_ERR_INVALID_ARG, "%s: partition_tokens < 0", who);
-  if (partition_tokens == 0) {
-    pl->part_tokens = auto_partition(pl->len_cap, g->block_size);
-  } else {
-    if (partition_tokens % kTile != 0 || partition_tokens % g->block_size != 0)
-      return pkv::fail(PKV_ERR_INVALID_ARG,
-                       "%s: partition_tokens %d must be a multiple of 16 and of block_size %d", who,
-                       partition_tokens, g->block_size);
-    pl->part_tokens = partition_tokens;
+  if (partition_tokens > 0 && (partition_tokens % kTile != 0 || partition_tokens % g->block_size != 0))
+    return pkv::fail(PKV_ERR_INVALID_ARG,
+                     "%s: partition_tokens %d must be a multiple of 16 and of block_size %d", who,
+                     partition_tokens, g->block_size);
+  pl->gw = heads_per_wave(G, g->dtype, g->head_dim);
+  pl->waves_per_group = G / pl->gw;
+  const int64_t cap = int64_t(max_blocks) * g->block_size;
+  pl->len_cap = static_cast<int>(max_seq_len < cap ? max_seq_len : cap);
+  const int64_t stream_tiles_max = (int64_t(pl->len_cap) + kTile - 1) / kTile;
+  const int wpg = pl->waves_per_group;
+  const bool balanced_ok = partition_tokens == 0 && num_seqs <= kMaxBalancedSeqs &&
+                           (wpg == 1 || wpg == 2 || wpg == 4 || wpg == 8) &&
+                           int64_t(num_seqs) * g->num_kv_heads * stream_tiles_max < (int64_t(1) << 31);
+  const int km = knob_mode();
+  pl->mode = (balanced_ok && km != 1) ? kBalancedMode : kPartitionMode;
+  pl->prefetch = prefetch_depth(pl->gw, g->dtype, pl->mode == kBalancedMode);
+
+  if (pl->mode == kBalancedMode) {
+    pl->waves_per_block = wpg <= 4 ? 4 : 8;
+    pl->groups_per_block = pl->waves_per_block / wpg;
+    pl->rows = (int64_t(num_seqs) * g->num_kv_heads + kMaxWaveGroups) * G;
+    pl->num_parts = 0;
+    pl->part_tokens = 0;
+    const size_t acc = size_t(pl->rows) * g->head_dim * sizeof(float);
+    pl->ws_ml_off = acc;
+    pl->ws_base_off = acc + size_t(pl->rows) * sizeof(float2);
+    pl->ws_bytes = pl->ws_base_off + round_up(int64_t(num_seqs + 1) * 4, 256);
+    return PKV_OK;
   }
-  const int64_t np = pl->len_cap == 0 ? 1 : (int64_t(pl->len_cap) + pl->part_tokens - 1) / pl->part_tokens;
+
+  pl->waves_per_item = g->num_kv_heads * wpg;
+  int wpb = knob_waves_per_block();
+  if (!wpb) wpb = wpg > 1 ? kMaxWavesPerBlock : 1;  // siblings of a group share a CU
+  pl->waves_per_block = pl->waves_per_item < wpb ? pl->waves_per_item : wpb;
+  pl->blocks_per_item = (pl->waves_per_item + pl->waves_per_block - 1) / pl->waves_per_block;
+  pl->part_tokens = partition_tokens ? partition_tokens : auto_partition(pl->len_cap, g->block_size);
+  const int64_t np =
+      pl->len_cap == 0 ? 1 : (int64_t(pl->len_cap) + pl->part_tokens - 1) / pl->part_tokens;
   if (np > 65535) return pkv::fail(PKV_ERR_INVALID_ARG, "%s: more than 65535 partitions", who);
   pl->num_parts = static_cast<int>(np);
+  pl->groups_per_block = 0;
   if (pl->num_parts > 1) {
-    pl->ws_bytes = size_t(num_seqs) * num_q_heads * pl->num_parts * (g->head_dim + 2) * sizeof(float);
+    pl->rows = int64_t(num_seqs) * num_q_heads * pl->num_parts;
+    pl->ws_ml_off = size_t(pl->rows) * g->head_dim * sizeof(float);
+    pl->ws_base_off = 0;
+    pl->ws_bytes = pl->ws_ml_off + size_t(pl->rows) * sizeof(float2);
   } else {
+    pl->rows = 0;
+    pl->ws_ml_off = pl->ws_base_off = 0;
     pl->ws_bytes = 0;
   }
-  if (int64_t(g->num_kv_heads) * pl->blocks_per_group > 2147483647)
-    return pkv::fail(PKV_ERR_INVALID_ARG, "%s: grid too large", who);
+  return PKV_OK;
+}
+
+// Workgroups of ``kernel`` (at ``threads`` per group) one CU holds at once,
+// times the CU count of the current device; cached per (device, kernel).
+int resident_blocks(const void* kernel, int threads) {
+  static std::mutex mu;
+  static std::unordered_map<uint64_t, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const uint64_t key = (uint64_t(reinterpret_cast<uintptr_t>(kernel)) << 8) ^ uint64_t(dev);
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  const int v = per_cu * cus;
+  std::lock_guard<std::mutex> lk(mu);
+  cache[key] = v;
+  return v;
+}
+
+template <typename T, int D, int GW, int P>
+pkv_status launch_main(const Plan& pl, AttnArgs& a, int num_seqs, hipStream_t st) {
+  if (pl.mode == kBalancedMode) {
+    const void* k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, P>);
+    const int threads = 64 * pl.waves_per_block;
+    int blocks = resident_blocks(k, threads);
+    if (blocks <= 0)
+      return pkv::fail(PKV_ERR_HIP, "pkv_attention_decode: occupancy query failed");
+    const int max_blocks = kMaxWaveGroups / pl.groups_per_block;
+    if (blocks > max_blocks) blocks = max_blocks;
+    a.num_groups = blocks * pl.groups_per_block;
+    hipLaunchKernelGGL((attn_balanced_kernel<T, D, GW, P>), dim3(blocks), dim3(threads), 0, st, a);
+  } else {
+    const dim3 grid(pl.blocks_per_item, pl.num_parts, num_seqs);
+    hipLaunchKernelGGL((attn_partition_kernel<T, D, GW, P>), grid, dim3(64 * pl.waves_per_block),
+                       0, st, a);
+  }
+  if (hipError_t e = hipGetLastError())
+    return pkv::fail(PKV_ERR_HIP, "pkv_attention_decode: launch failed: %s", hipGetErrorString(e));
   return PKV_OK;
 }
 
 template <typename T, int D, int GW>
-void launch_partition(const dim3& grid, const dim3& block, hipStream_t st, const AttnArgs& a) {
-  hipLaunchKernelGGL((attn_partition_kernel<T, D, GW>), grid, block, 0, st, a);
+pkv_status launch_main_p(const Plan& pl, AttnArgs& a, int num_seqs, hipStream_t st) {
+  if constexpr (sizeof(T) == 4) {  // fp32 rows: twice the registers, ring of 2 only
+    return launch_main<T, D, GW, 2>(pl, a, num_seqs, st);
+  } else {
+    switch (pl.prefetch) {
+      case 4: return launch_main<T, D, GW, 4>(pl, a, num_seqs, st);
+      case 3: return launch_main<T, D, GW, 3>(pl, a, num_seqs, st);
+      default: return launch_main<T, D, GW, 2>(pl, a, num_seqs, st);
+    }
+  }
 }
 
-template <typename T, int D>
-pkv_status dispatch(int phases, const Plan& pl, const AttnArgs& a, int num_kv_heads,
-                    int num_seqs, int num_q_heads, hipStream_t st) {
-  if (phases & 1) {
-    const dim3 grid(num_kv_heads * pl.blocks_per_group, pl.num_parts, num_seqs);
-    const dim3 block(64 * pl.waves_per_block);
-    switch (pl.gw) {
-      case 4: launch_partition<T, D, 4>(grid, block, st, a); break;
-      case 3: launch_partition<T, D, 3>(grid, block, st, a); break;
-      case 2: launch_partition<T, D, 2>(grid, block, st, a); break;
-      default: launch_partition<T, D, 1>(grid, block, st, a); break;
+// The grid of the balanced merge depends on W, which the main launch fixes;
+// a phase-2-only call recomputes it the same way.
+template <typename T, int D, int GW>
+int balanced_groups(const Plan& pl) {
+  const void* k = nullptr;
+  if constexpr (sizeof(T) == 4) {
+    k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 2>);
+  } else {
+    switch (pl.prefetch) {
+      case 4: k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 4>); break;
+      case 3: k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 3>); break;
+      default: k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 2>); break;
     }
-    if (hipError_t e = hipGetLastError())
-      return pkv::fail(PKV_ERR_HIP, "pkv_attention_decode: launch failed: %s",
-                       hipGetErrorString(e));
   }
-  if ((phases & 2) && pl.num_parts > 1) {
-    hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3(num_q_heads, num_seqs), dim3(256), 0, st, a);
+  int blocks = resident_blocks(k, 64 * pl.waves_per_block);
+  const int max_blocks = kMaxWaveGroups / pl.groups_per_block;
+  if (blocks > max_blocks) blocks = max_blocks;
+  return blocks * pl.groups_per_block;
+}
+
+template <typename T, int D, int GW>
+pkv_status dispatch_gw(int phases, const Plan& pl, AttnArgs& a, int num_seqs, int num_q_heads,
+                       hipStream_t st) {
+  if (phases & 1) {
+    if (pkv_status s = launch_main_p<T, D, GW>(pl, a, num_seqs, st)) return s;
+  } else if (pl.mode == kBalancedMode) {
+    a.num_groups = balanced_groups<T, D, GW>(pl);
+    if (a.num_groups <= 0)
+      return pkv::fail(PKV_ERR_HIP, "pkv_attention_decode: occupancy query failed");
+  }
+  if (phases & 2) {
+    if (pl.mode == kBalancedMode) {
+      hipLaunchKernelGGL((attn_merge_balanced_kernel<T, D>), dim3(num_q_heads, num_seqs),
+                         dim3(kMergeThreads), 0, st, a);
+    } else if (pl.num_parts > 1) {
+      hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3(num_q_heads, num_seqs),
+                         dim3(kMergeThreads), 0, st, a);
+    }
     if (hipError_t e = hipGetLastError())
       return pkv::fail(PKV_ERR_HIP, "pkv_attention_decode: merge launch failed: %s",
                        hipGetErrorString(e));
   }
   return PKV_OK;
+}
+
+template <typename T, int D>
+pkv_status dispatch(int phases, const Plan& pl, AttnArgs& a, int num_seqs, int num_q_heads,
+                    hipStream_t st) {
+  switch (pl.gw) {
+    case 4: return dispatch_gw<T, D, 4>(phases, pl, a, num_seqs, num_q_heads, st);
+    case 3: return dispatch_gw<T, D, 3>(phases, pl, a, num_seqs, num_q_heads, st);
+    case 2: return dispatch_gw<T, D, 2>(phases, pl, a, num_seqs, num_q_heads, st);
+    default: return dispatch_gw<T, D, 1>(phases, pl, a, num_seqs, num_q_heads, st);
+  }
 }
 
 }  // namespace
@@ -584,6 +924,8 @@ int32_t pkv_attention_partition_tokens(int32_t num_seqs, int32_t num_q_heads,
       geom && geom->block_size > 0 ? (max_seq_len + geom->block_size - 1) / geom->block_size : 0;
   if (make_plan(num_seqs, num_q_heads, max_seq_len, max_blocks, 0, geom,
                 "pkv_attention_partition_tokens", &pl) != PKV_OK)
+    return 0;
+  if (pl.mode == kBalancedMode)  // the split is by shares, not by partitions
     return 0;
   return pl.part_tokens;
 }
@@ -622,7 +964,7 @@ pkv_status pkv_attention_decode_phase(int32_t phases, const void* q, const void*
       !pkv::aligned16(v_cache) || (reinterpret_cast<uintptr_t>(block_tables) & 3u) ||
       (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
     return pkv::fail(PKV_ERR_INVALID_ARG, "%s: misaligned pointer", who);
-  if (pl.num_parts > 1) {
+  if (pl.ws_bytes > 0) {
     if (!workspace || workspace_bytes < pl.ws_bytes)
       return pkv::fail(PKV_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed, %zu given", who,
                        pl.ws_bytes, workspace ? workspace_bytes : size_t(0));
@@ -637,35 +979,37 @@ pkv_status pkv_attention_decode_phase(int32_t phases, const void* q, const void*
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
   a.out = out;
-  a.ws_acc = static_cast<float*>(workspace);
-  a.ws_ml = pl.num_parts > 1
-                ? static_cast<float*>(workspace) +
-                      size_t(num_seqs) * num_q_heads * pl.num_parts * geom->head_dim
-                : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  a.ws_acc = pl.ws_bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  a.ws_ml = pl.ws_bytes ? reinterpret_cast<float2*>(ws + pl.ws_ml_off) : nullptr;
+  a.ws_base = (pl.ws_bytes && pl.mode == kBalancedMode)
+                  ? reinterpret_cast<int32_t*>(ws + pl.ws_base_off)
+                  : nullptr;
   a.row_bytes = geom->num_kv_heads * geom->head_dim * es;
   a.block_bytes = int64_t(geom->block_size) * a.row_bytes;
   a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
+  a.num_kv_heads = geom->num_kv_heads;
   a.group = num_q_heads / geom->num_kv_heads;
   a.waves_per_group = pl.waves_per_group;
   a.waves_per_block = pl.waves_per_block;
-  a.blocks_per_group = pl.blocks_per_group;
   a.num_blocks = geom->num_blocks;
   a.block_shift = pkv::log2_exact(geom->block_size);
   a.len_cap = pl.len_cap;
+  a.waves_per_item = pl.waves_per_item;
   a.part_tokens = pl.part_tokens;
   a.num_parts = pl.num_parts;
+  a.groups_per_block = pl.groups_per_block;
+  a.num_groups = 0;
   a.scale_log2 = static_cast<float>(double(scale) * 1.4426950408889634);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int hkv = geom->num_kv_heads;
   if (geom->dtype == PKV_BF16) {
-    return geom->head_dim == 128
-               ? dispatch<uint16_t, 128>(phases, pl, a, hkv, num_seqs, num_q_heads, st)
-               : dispatch<uint16_t, 64>(phases, pl, a, hkv, num_seqs, num_q_heads, st);
+    return geom->head_dim == 128 ? dispatch<uint16_t, 128>(phases, pl, a, num_seqs, num_q_heads, st)
+                                 : dispatch<uint16_t, 64>(phases, pl, a, num_seqs, num_q_heads, st);
   }
-  return geom->head_dim == 128
-             ? dispatch<float, 128>(phases, pl, a, hkv, num_seqs, num_q_heads, st)
-             : dispatch<float, 64>(phases, pl, a, hkv, num_seqs, num_q_heads, st);
+  return geom->head_dim == 128 ? dispatch<float, 128>(phases, pl, a, num_seqs, num_q_heads, st)
+                               : dispatch<float, 64>(phases, pl, a, num_seqs, num_q_heads, st);
 }
 
 pkv_status pkv_attention_decode(const void* q, const void* k_cache, const void* v_cache,

@@ -52,6 +52,13 @@ __device__ __forceinline__ float sum8(float x) {
   return x;
 }
 
+__device__ __forceinline__ float max8(float x) {
+  x = fmaxf(x, dpp<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
+  return x;
+}
+
 // Reductions across the 8 lanes that share (lane & 7): lane ^ 8, ^ 16, ^ 32.
 __device__ __forceinline__ float sum_across_groups8(float x) {
   x += dpp<kDppRowRor8>(x);
@@ -67,5 +74,9 @@ __device__ __forceinline__ float max_across_groups8(float x) {
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+
+// Whole-wave reductions (every lane of the wave must be active).
+__device__ __forceinline__ float wave_sum(float x) { return sum_across_groups8(sum8(x)); }
+__device__ __forceinline__ float wave_max(float x) { return max_across_groups8(max8(x)); }
 
 }  // namespace pkv

@@ -139,3 +139,15 @@ def attention_decode(q, k_cache, v_cache, block_tables, seq_lens, scale, out=Non
                                            ctypes.byref(g), _stream(stream)),
           "pkv_attention_decode")
     return out
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, num_workgroups: int = 4096,
+                stream=None) -> None:
+    """Read-bandwidth calibration kernel over ``buf`` (see include/pkv.h)."""
+    _need(buf, "buf", None, buf.device)
+    _need(sink, "sink", torch.int32, buf.device)
+    if sink.numel() < num_workgroups:
+        raise ValueError("sink needs num_workgroups entries")
+    nbytes = buf.numel() * buf.element_size()
+    check(lib().pkv_stream_read(_ptr(buf), nbytes - nbytes % 16, _ptr(sink), int(num_workgroups),
+                                _stream(stream)), "pkv_stream_read")

@@ -144,10 +144,15 @@ class DecodeStep:
                                     workspace=ws, stream=stream, phases=phases)
 
     @property
-    def num_parts(self) -> int:
+    def split(self) -> dict:
+        """How pkv_attention_decode splits this batch: fixed partitions (with
+        their length and count) or the balanced split."""
         pt = self.partition_tokens or ops.partition_tokens(
             self.wl.num_seqs, self.wl.num_q_heads, self.max_seq_len, self.k_caches[0])
-        return max(1, -(-self.max_seq_len // pt))
+        if pt == 0:
+            return {"mode": "balanced"}
+        return {"mode": "partitions", "partition_tokens": pt,
+                "num_partitions": max(1, -(-self.max_seq_len // pt))}
 
     def step(self, layer=0, stream=None):
         """copy -> write -> attention on one layer's pools (enqueue only)."""

@@ -202,3 +202,52 @@ def test_config_full_sampled(name):
         r = assert_gate(out[s, hs], ref[s, hs], wl.dtype, f"{name} seq {s}")
     say("  last gate", r)
     assert np.isfinite(out).all()
+
+
+# -- the two work distributions ------------------------------------------------
+
+@pytest.fixture
+def mode_env(monkeypatch):
+    def set_mode(mode):
+        monkeypatch.setenv("PKV_ATTN_MODE", str(mode))
+    return set_mode
+
+
+@pytest.mark.parametrize("mode", [1, 2], ids=["partitions", "balanced"])
+@pytest.mark.parametrize("dtype,B,D,Hq,Hkv", [("bf16", 16, 128, 16, 8), ("bf16", 32, 128, 64, 8),
+                                              ("bf16", 16, 128, 64, 4), ("bf16", 8, 64, 12, 1),
+                                              ("f32", 16, 64, 8, 2)], ids=lambda v: str(v))
+def test_modes_match_oracle(mode_env, mode, dtype, B, D, Hq, Hkv):
+    mode_env(mode)
+    lens = [1, 2, 15, 16, 17, 31, 100, 255, 256, 257, 600, 1000]
+    wl = independent_workload(lens, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=B,
+                              dtype=dtype, seed=31 + Hq)
+    step, ost = run_both(wl)
+    ref = oracle_attention(wl.q, ost.k_pool, ost.v_pool, ost.block_tables, ost.seq_lens,
+                           wl.scale)
+    assert_gate(gpu_out(step), ref, dtype, f"mode {mode}")
+
+
+def test_balanced_stream_across_more_than_1024_shares(mode_env):
+    """One long sequence and one KV head: every wave group holds a piece of the
+    same stream, so the merge folds more than 1024 pieces."""
+    mode_env(2)
+    wl = independent_workload([40000], num_q_heads=4, num_kv_heads=1, head_dim=128,
+                              block_size=16, dtype="bf16", seed=77)
+    step, ost = run_both(wl)
+    ref = oracle_attention(wl.q, ost.k_pool, ost.v_pool, ost.block_tables, ost.seq_lens,
+                           wl.scale)
+    assert_gate(gpu_out(step), ref, "bf16", "one stream, many shares")
+
+
+def test_balanced_many_short_sequences(mode_env):
+    """Far fewer tiles than wave groups (every share a single tile)."""
+    mode_env(2)
+    rng = np.random.default_rng(5)
+    lens = rng.integers(1, 40, size=300)
+    wl = independent_workload(lens, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                              dtype="bf16", seed=12)
+    step, ost = run_both(wl)
+    ref = oracle_attention(wl.q, ost.k_pool, ost.v_pool, ost.block_tables, ost.seq_lens,
+                           wl.scale)
+    assert_gate(gpu_out(step), ref, "bf16", "many short")

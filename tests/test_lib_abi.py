@@ -85,24 +85,37 @@ def test_attention_validation_and_workspace_size():
     assert call(g(), pt=24) == _lib.PKV_ERR_INVALID_ARG
     assert call(g(), scale=float("nan")) == _lib.PKV_ERR_INVALID_ARG
     assert call(g(), N=0) == _lib.PKV_OK
-    # split needs a workspace
+    # a fixed split needs a workspace
     assert call(g(), maxlen=100, pt=32) == _lib.PKV_ERR_INVALID_ARG
     assert "workspace" in last_error()
-    # workspace size: N * Hq * P * (D + 2) floats
+    # fixed partitions: N * Hq * P * (D + 2) floats
     n = lib.pkv_attention_workspace_bytes(2, 8, 100, 32, ctypes.byref(g()))
     assert n == 2 * 8 * 4 * (64 + 2) * 4
-    assert lib.pkv_attention_workspace_bytes(2, 8, 100, 0, ctypes.byref(g())) == 0
+    # the automatic (balanced) split: (N * H_kv + 8192) * G rows of D + 2 floats,
+    # plus the (N + 1) prefix sums rounded up to 256 bytes
+    rows = (2 * 2 + 8192) * 4
+    assert lib.pkv_attention_workspace_bytes(2, 8, 100, 0, ctypes.byref(g())) == \
+        rows * (64 + 2) * 4 + 256
     assert lib.pkv_attention_workspace_bytes(2, 8, 100, 24, ctypes.byref(g())) == \
         ctypes.c_size_t(-1).value
 
 
 @pytest.mark.parametrize("maxlen,B,expect", [(100, 16, 112), (4096, 16, 256), (8192, 16, 512),
                                              (131072, 32, 512), (10, 64, 64), (300, 8, 256)])
-def test_automatic_partition(maxlen, B, expect):
+def test_automatic_partition_beyond_balanced_limit(maxlen, B, expect):
+    """Batches of more than 4096 sequences use fixed partitions; the automatic
+    length is 256 up to 4096-long contexts, 512 beyond, no split if one
+    partition suffices."""
     lib = pkv.lib()
-    got = lib.pkv_attention_partition_tokens(4, 8, maxlen, ctypes.byref(g(nb=8192, B=B)))
+    got = lib.pkv_attention_partition_tokens(5000, 8, maxlen, ctypes.byref(g(nb=8192, B=B)))
     assert got == expect
     assert got % 16 == 0 and got % B == 0
+
+
+def test_automatic_plan_is_balanced_for_moderate_batches():
+    lib = pkv.lib()
+    assert lib.pkv_attention_partition_tokens(256, 32, 8192, ctypes.byref(g(nb=8192, H=8, D=128,
+                                                                             dt=1))) == 0
 
 
 def test_block_manager_errors():
