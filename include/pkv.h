@@ -147,11 +147,14 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *                 workspace and a log-sum-exp merge kernel produces out.  The
  *                 automatic plan (up to 4096 sequences) is the balanced split:
  *                 a persistent grid in which every wave group takes an equal
- *                 share of all K/V tiles of the batch; a sequence's history
- *                 that spans several shares is merged the same way.
+ *                 share of 85 % of all K/V tiles of the batch, and further
+ *                 workgroups, dispatched as those retire, take small chunks of
+ *                 the rest; a sequence's history that spans several of these
+ *                 intervals is merged the same way.
  *   workspace     device buffer of at least pkv_attention_workspace_bytes(...)
  *                 bytes (may be NULL when that is 0); contents on entry are
- *                 ignored.
+ *                 ignored.  Calls that may run at the same time need
+ *                 workspaces of their own.
  * Supported: head_dim 64 or 128; block_size a power of two >= 8;
  * num_q_heads a multiple of num_kv_heads with at most 64 heads per group.
  * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
@@ -183,7 +186,8 @@ pkv_status pkv_attention_decode_phase(int32_t phases, const void* q, const void*
  * call (unset or out of range = the library's heuristic):
  *   PKV_ATTN_HEADS_PER_WAVE  1..4  upper bound on query heads one wave carries
  *   PKV_ATTN_PREFETCH        2..4  K/V tiles of 16 positions in flight per wave
- *                                  (bf16 only; fp32 always uses 2)
+ *                                  (bf16 only, at most 4 / 3 / 2 for 1 / 2 /
+ *                                  3-4 heads per wave; fp32 always uses 2)
  *   PKV_ATTN_WAVES_PER_BLOCK 1,2,4,8  fixed partitions: waves per workgroup
  *                                  (the waves of one (sequence, partition)
  *                                  are packed together)

@@ -27,12 +27,19 @@
 //    consumed); block ids come from a VGPR cache of 64 table entries read with
 //    v_readlane, so each load has a scalar base and a fixed lane offset.
 //  * Balanced mode (default): a persistent grid of as many wave groups as the
-//    GPU holds at once.  All streams, sequence by sequence, form one global
-//    sequence of tiles; group w takes the w-th equal share of it.  A share that
-//    covers a whole stream writes the output; otherwise it writes a (reference,
-//    sum, weighted sum) piece, and attn_merge_balanced_kernel combines the
-//    pieces of each stream by log-sum-exp rescaling.  Every group does the same
-//    amount of work, and no group waits for a launch slot.
+//    GPU holds at once, followed by more workgroups.  All streams, sequence by
+//    sequence, form one global sequence of tiles, cut into intervals: first
+//    one equal static share per resident wave group (85 % of the tiles), then
+//    small chunks, one per wave group of the workgroups that follow.  The
+//    hardware dispatches those as resident workgroups retire, so CUs that
+//    finish their shares early take more chunks.  An interval that covers a
+//    whole stream writes the output; otherwise it writes a (reference, sum,
+//    weighted sum) piece, and attn_merge_balanced_kernel combines the pieces
+//    of each stream by log-sum-exp rescaling.  Equal shares alone do not finish
+//    together: the SIMD issues memory instructions oldest wave first and XCDs
+//    draw different bandwidth, so (a) a wave raises its priority (s_setprio) in
+//    proportion to the part of its share still ahead of it, and (b) the
+//    dispatched chunks absorb what still differs between CUs and XCDs.
 //  * Partition mode (explicit partition_tokens, or batches past the balanced
 //    limits): one work item per (sequence, partition, KV head); the partition
 //    states are merged by attn_merge_kernel.
@@ -54,6 +61,9 @@ constexpr float kRescaleSlack = 8.0f;   // log2 units before the reference moves
 constexpr float kRefInit = -1e30f;      // reference of a sub-stream with no position yet
 constexpr int kMaxBalancedSeqs = 4096;  // per-sequence prefix sums live in LDS
 constexpr int kMaxWaveGroups = 8192;    // the workspace is sized for this many groups
+constexpr int kDynamicPerMille = 150;   // balanced split: tiles handed out dynamically
+constexpr int kMinChunkTiles = 4;       // smallest dynamic chunk
+constexpr int kMaxChunks = 8192;        // the workspace is sized for this many chunks
 
 enum Mode : int { kPartitionMode = 0, kBalancedMode = 1 };
 
@@ -85,7 +95,8 @@ struct AttnArgs {
   int32_t num_parts;
   // balanced mode
   int32_t groups_per_block; // wave groups per workgroup
-  int32_t num_groups;       // W: wave groups in the grid
+  int32_t num_groups;       // W: wave groups of the static (resident) part of the grid
+  int32_t static_blocks;    // workgroups of the static part; the rest run dynamic chunks
   float scale_log2;
 };
 
@@ -111,6 +122,13 @@ struct TileInfo {
 };
 
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
+
+// The wave's index in its workgroup, as a wave-uniform (scalar) value: every
+// quantity derived from it (sequence, head, bounds, block addresses) then lives
+// in SGPRs, and loops over tiles are uniform branches.
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+}
 
 template <typename T>
 __device__ __forceinline__ void unpack(const uint4& x, float (&f)[16 / sizeof(T)]) {
@@ -154,6 +172,14 @@ __device__ __forceinline__ uint4 pack_chunk(const float* f) {
     o.z = __float_as_uint(f[2]); o.w = __float_as_uint(f[3]);
   }
   return o;
+}
+
+// Wave issue priority 0..3 (s_setprio takes an immediate; lv is wave-uniform).
+__device__ __forceinline__ void set_priority(int lv) {
+  if (lv >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (lv == 2) __builtin_amdgcn_s_setprio(2);
+  else if (lv == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
 }
 
 // One wave's attention over a stretch [start, end) of one stream.
@@ -296,6 +322,10 @@ struct Wave {
     }
   }
 
+  // Issue-priority feedback (balanced mode): tiles of the wave's static share
+  // still ahead at the start of this stretch, and the share's length; 0 = off.
+  int prio_rem0 = 0, prio_len = 0;
+
   // Attention of query heads h0 .. h0+GW-1 of sequence s over positions
   // [start, end) of KV head kvh (start < end).  Leaves the merged state in M,
   // lt and acc (identical in every lane holding a given chunk).
@@ -336,6 +366,7 @@ struct Wave {
     }
     int t = 0;
     for (; t + P < ntiles; t += P) {
+      if (prio_len > 0) set_priority(((prio_rem0 - t) * 4) / (prio_len + 1));
 #pragma unroll
       for (int k = 0; k < P; ++k) {
         consume<false>(info[k], buf[k]);
@@ -420,7 +451,7 @@ __global__ void __launch_bounds__(64 * kMaxWavesPerBlock)
 attn_partition_kernel(AttnArgs a) {
   // The waves of one (sequence, partition) are numbered consecutively and
   // packed into workgroups.
-  const int wi = blockIdx.x * a.waves_per_block + (threadIdx.x >> 6);
+  const int wi = blockIdx.x * a.waves_per_block + wave_index();
   if (wi >= a.waves_per_item) return;
   const int kvh = wi / a.waves_per_group;
   const int sub = wi - kvh * a.waves_per_group;
@@ -545,13 +576,38 @@ __device__ __forceinline__ int stream_tiles(const AttnArgs& a, int s) {
 
 // Share of wave group w in a global order of T tiles cut into W shares:
 // [floor(T*w/W), floor(T*(w+1)/W)).  With W <= T every share is non-empty.
-__device__ __forceinline__ int64_t share_lo(int64_t T, int w, int W) { return T * w / W; }
+__device__ __forceinline__ int64_t share_lo(int64_t T, int64_t w, int64_t W) { return T * w / W; }
 
 // The share holding global tile x (0 <= x < T): the largest w with
 // floor(T*w/W) <= x, i.e. floor(((x+1)*W - 1) / T).
-__device__ __forceinline__ int share_of(int64_t x, int64_t T, int W) {
+__device__ __forceinline__ int share_of(int64_t x, int64_t T, int64_t W) {
   return static_cast<int>(((x + 1) * W - 1) / T);
 }
+
+// The balanced split's intervals over the global tile order (all streams,
+// sequence by sequence, KV head by KV head): intervals 0 .. Ws-1 are the static
+// shares of [0, S), intervals Ws .. Ws+K-1 the dynamic chunks of [S, T).  Both
+// kernels derive the same cut from (T, W).
+struct Intervals {
+  int64_t T, S;
+  int Ws, K;
+  __device__ Intervals(int64_t total, int W) : T(total) {
+    const int64_t dyn = total * kDynamicPerMille / 1000;
+    S = total - dyn;
+    Ws = static_cast<int>(S < W ? S : W);
+    // one chunk per static group, of at least kMinChunkTiles tiles
+    int64_t k = (dyn + kMinChunkTiles - 1) / kMinChunkTiles;
+    if (k > W) k = W;
+    K = static_cast<int>(k < kMaxChunks ? k : kMaxChunks);
+  }
+  // First tile of interval j (0 <= j <= Ws + K; lo(Ws) = S, lo(Ws + K) = T).
+  __device__ int64_t lo(int j) const {
+    return j <= Ws ? share_lo(S, j, Ws) : S + share_lo(T - S, j - Ws, K);
+  }
+  __device__ int of(int64_t x) const {
+    return x < S ? share_of(x, S, Ws) : Ws + share_of(x - S, T - S, K);
+  }
+};
 
 __device__ __forceinline__ int wave_incl_scan(int x) {
   const int lane = threadIdx.x & 63;
@@ -563,13 +619,50 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
+// Attention over global tiles [lo, hi) of interval `iv`, stream by stream.
+template <typename T, int D, int GW, int P>
+__device__ __forceinline__ void run_interval(Wave<T, D, GW, P>& w, const AttnArgs& a,
+                                             const int32_t* base, int64_t lo, int64_t hi, int iv,
+                                             int sub) {
+  const int N = a.num_seqs, Hkv = a.num_kv_heads;
+  int64_t cur = lo;
+  while (cur < hi) {
+    // The sequence holding global tile `cur`: the largest s with base[s] <= cur.
+    int lo_s = 0, hi_s = N - 1;
+    while (lo_s < hi_s) {
+      const int mid = (lo_s + hi_s + 1) >> 1;
+      if (base[mid] <= cur) lo_s = mid;
+      else hi_s = mid - 1;
+    }
+    const int s = lo_s;
+    const int nt = (base[s + 1] - base[s]) / Hkv;
+    const int rel = static_cast<int>(cur - base[s]);
+    const int kvh = rel / nt;
+    const int t0 = rel - kvh * nt;
+    const int seg = static_cast<int>(min(hi - cur, int64_t(nt - t0)));
+    const int L = clamp_len(a.seq_lens[s], a.len_cap);
+    const int h0 = kvh * a.group + sub * GW;
+    w.run(s, kvh, h0, t0 * kTile, min((t0 + seg) * kTile, L));
+    if (t0 == 0 && seg == nt) {
+      w.write_out(s, h0);  // the whole stream in one interval
+    } else {
+      // piece of stream k from interval iv -> row group (k + iv): unique,
+      // since streams and intervals are both contiguous and in the same order.
+      const int64_t k = int64_t(s) * Hkv + kvh;
+      w.write_piece((k + iv) * a.group + sub * GW, 1);
+    }
+    if (w.prio_len > 0) w.prio_rem0 -= seg;
+    cur += seg;
+  }
+}
+
 template <typename T, int D, int GW, int P>
 __global__ void __launch_bounds__(64 * kMaxWavesPerBlock)
 attn_balanced_kernel(AttnArgs a) {
   __shared__ int32_t base[kMaxBalancedSeqs + 1];
   __shared__ int32_t wave_tot[kMaxWavesPerBlock];
   const int N = a.num_seqs, Hkv = a.num_kv_heads;
-  const int tid = threadIdx.x, nth = blockDim.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, nth = blockDim.x, lane = tid & 63, wv = wave_index();
 
   // base[s] = sum over s' < s of H_kv * tiles(s'): every thread sums a
   // contiguous run of sequences, then a block-wide exclusive scan.
@@ -601,46 +694,26 @@ attn_balanced_kernel(AttnArgs a) {
   const int grp = wv / a.waves_per_group;
   const int sub = wv - grp * a.waves_per_group;
   if (grp >= a.groups_per_block || total == 0) return;
-  const int W = min(a.num_groups, total);  // every share non-empty
-  const int gidx = blockIdx.x * a.groups_per_block + grp;
-  if (gidx >= W) return;
-  const int64_t ttot = total;
-  int64_t cur = share_lo(ttot, gidx, W);
-  const int64_t hi = share_lo(ttot, gidx + 1, W);
-
+  const Intervals ivs(total, a.num_groups);
   Wave<T, D, GW, P> w(a);
-  while (cur < hi) {
-    // The sequence holding global tile `cur`: the largest s with base[s] <= cur.
-    int lo_s = 0, hi_s = N - 1;
-    while (lo_s < hi_s) {
-      const int mid = (lo_s + hi_s + 1) >> 1;
-      if (base[mid] <= cur) lo_s = mid;
-      else hi_s = mid - 1;
-    }
-    const int s = lo_s;
-    const int nt = (base[s + 1] - base[s]) / Hkv;
-    const int rel = static_cast<int>(cur - base[s]);
-    const int kvh = rel / nt;
-    const int t0 = rel - kvh * nt;
-    const int seg = static_cast<int>(min(hi - cur, int64_t(nt - t0)));
-    const int L = clamp_len(a.seq_lens[s], a.len_cap);
-    const int h0 = kvh * a.group + sub * GW;
-    w.run(s, kvh, h0, t0 * kTile, min((t0 + seg) * kTile, L));
-    if (t0 == 0 && seg == nt) {
-      w.write_out(s, h0);  // the whole stream in one share
-    } else {
-      // piece of stream k from share gidx -> row group (k + gidx): unique,
-      // since streams and shares are both contiguous and in the same order.
-      const int64_t k = int64_t(s) * Hkv + kvh;
-      w.write_piece((k + gidx) * a.group + sub * GW, 1);
-    }
-    cur += seg;
+  if (static_cast<int>(blockIdx.x) < a.static_blocks) {
+    const int gidx = blockIdx.x * a.groups_per_block + grp;
+    if (gidx >= ivs.Ws) return;
+    const int64_t lo = ivs.lo(gidx), hi = ivs.lo(gidx + 1);
+    w.prio_len = static_cast<int>(hi - lo);
+    w.prio_rem0 = w.prio_len;
+    run_interval(w, a, base, lo, hi, gidx, sub);
+    return;
   }
+  const int j = (blockIdx.x - a.static_blocks) * a.groups_per_block + grp;
+  if (j >= ivs.K) return;
+  const int iv = ivs.Ws + j;
+  run_interval(w, a, base, ivs.lo(iv), ivs.lo(iv + 1), iv, sub);
 }
 
 // Balanced mode merge: one workgroup per (query head, sequence); combines the
-// pieces its stream left in consecutive shares (nothing to do when one share
-// held the whole stream, zeros for an empty history).
+// pieces its stream left in consecutive intervals (nothing to do when one
+// interval held the whole stream, zeros for an empty history).
 template <typename T, int D>
 __global__ void __launch_bounds__(kMergeThreads)
 attn_merge_balanced_kernel(AttnArgs a) {
@@ -653,14 +726,13 @@ attn_merge_balanced_kernel(AttnArgs a) {
     merge_rows<T, D>(a, 0, 0, 0, dst);
     return;
   }
-  const int64_t ttot = a.ws_base[a.num_seqs];
-  const int W = static_cast<int>(min<int64_t>(a.num_groups, ttot));
+  const Intervals ivs(a.ws_base[a.num_seqs], a.num_groups);
   const int64_t start = int64_t(a.ws_base[s]) + int64_t(g) * nt;
-  const int w0 = share_of(start, ttot, W);
-  const int w1 = share_of(start + nt - 1, ttot, W);
-  if (w0 == w1) return;
+  const int i0 = ivs.of(start);
+  const int i1 = ivs.of(start + nt - 1);
+  if (i0 == i1) return;
   const int64_t k = int64_t(s) * a.num_kv_heads + g;
-  merge_rows<T, D>(a, w1 - w0 + 1, (k + w0) * G + j, G, dst);
+  merge_rows<T, D>(a, i1 - i0 + 1, (k + i0) * G + j, G, dst);
 }
 
 // ---------------------------------------------------------------------------
@@ -685,22 +757,29 @@ int knob_waves_per_block() {
 
 // Query heads per wave: the largest of 4, 3, 2, 1 dividing the group size that
 // fits the register file without spilling (fp32 rows of 128 hold twice the
-// registers of bf16 ones, so they stop at 2).
+// registers of bf16 ones: one head per wave).
 int heads_per_wave(int G, int dtype, int head_dim) {
-  int cap = (dtype == PKV_F32 && head_dim == 128) ? 2 : 4;
+  int cap = (dtype == PKV_F32 && head_dim == 128) ? 1 : 4;
   if (const int k = knob_heads_per_wave()) cap = k < cap ? k : cap;
   for (int gw : {4, 3, 2, 1})
     if (gw <= cap && G % gw == 0) return gw;
   return 1;
 }
 
+// Deepest register ring that fits without spilling at head_dim 128 (bf16):
+// four tiles for one head per wave, three for two, two beyond.
+template <int GW>
+constexpr int max_prefetch() { return GW >= 3 ? 2 : (GW == 2 ? 3 : 4); }
+
 // Tiles per wave in the register ring.  Two (one in flight while one is
 // consumed) measured best with the balanced split; fixed partitions with few
 // heads per wave gain a little from three.
 int prefetch_depth(int gw, int dtype, bool balanced) {
   if (dtype == PKV_F32) return 2;
-  if (const int k = knob_prefetch()) return k;
-  return (!balanced && gw <= 2) ? 3 : 2;
+  const int cap = gw >= 3 ? 2 : (gw == 2 ? 3 : 4);
+  int p = (!balanced && gw <= 2) ? 3 : 2;
+  if (const int k = knob_prefetch()) p = k;
+  return p < cap ? p : cap;
 }
 
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
@@ -725,6 +804,7 @@ struct Plan {
   int groups_per_block;
   int64_t rows;  // workspace rows of D floats
   size_t ws_bytes, ws_ml_off, ws_base_off;
+  int max_chunks;  // balanced: upper bound of the dynamic chunks
 };
 
 pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
@@ -765,13 +845,20 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
   if (pl->mode == kBalancedMode) {
     pl->waves_per_block = wpg <= 4 ? 4 : 8;
     pl->groups_per_block = pl->waves_per_block / wpg;
-    pl->rows = (int64_t(num_seqs) * g->num_kv_heads + kMaxWaveGroups) * G;
+    // piece rows: (stream + interval) over N * H_kv streams and at most
+    // kMaxWaveGroups static shares + kMaxChunks dynamic chunks
+    pl->rows = (int64_t(num_seqs) * g->num_kv_heads + kMaxWaveGroups + kMaxChunks) * G;
     pl->num_parts = 0;
     pl->part_tokens = 0;
     const size_t acc = size_t(pl->rows) * g->head_dim * sizeof(float);
     pl->ws_ml_off = acc;
     pl->ws_base_off = acc + size_t(pl->rows) * sizeof(float2);
     pl->ws_bytes = pl->ws_base_off + round_up(int64_t(num_seqs + 1) * 4, 256);
+    // dynamic chunks: at most kMaxChunks, at least kMinChunkTiles tiles each,
+    // out of kDynamicPerMille of all tiles (bounded here by max_seq_len)
+    const int64_t tmax = int64_t(num_seqs) * g->num_kv_heads * stream_tiles_max;
+    const int64_t kb = (tmax * kDynamicPerMille / 1000 + kMinChunkTiles - 1) / kMinChunkTiles;
+    pl->max_chunks = static_cast<int>(kb < kMaxChunks ? kb : kMaxChunks);
     return PKV_OK;
   }
 
@@ -786,6 +873,7 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
   if (np > 65535) return pkv::fail(PKV_ERR_INVALID_ARG, "%s: more than 65535 partitions", who);
   pl->num_parts = static_cast<int>(np);
   pl->groups_per_block = 0;
+  pl->max_chunks = 0;
   if (pl->num_parts > 1) {
     pl->rows = int64_t(num_seqs) * num_q_heads * pl->num_parts;
     pl->ws_ml_off = size_t(pl->rows) * g->head_dim * sizeof(float);
@@ -833,7 +921,11 @@ pkv_status launch_main(const Plan& pl, AttnArgs& a, int num_seqs, hipStream_t st
     const int max_blocks = kMaxWaveGroups / pl.groups_per_block;
     if (blocks > max_blocks) blocks = max_blocks;
     a.num_groups = blocks * pl.groups_per_block;
-    hipLaunchKernelGGL((attn_balanced_kernel<T, D, GW, P>), dim3(blocks), dim3(threads), 0, st, a);
+    a.static_blocks = blocks;
+    const int chunks = pl.max_chunks < a.num_groups ? pl.max_chunks : a.num_groups;
+    const int tail = (chunks + pl.groups_per_block - 1) / pl.groups_per_block;
+    hipLaunchKernelGGL((attn_balanced_kernel<T, D, GW, P>), dim3(blocks + tail), dim3(threads), 0,
+                       st, a);
   } else {
     const dim3 grid(pl.blocks_per_item, pl.num_parts, num_seqs);
     hipLaunchKernelGGL((attn_partition_kernel<T, D, GW, P>), grid, dim3(64 * pl.waves_per_block),
@@ -844,33 +936,29 @@ pkv_status launch_main(const Plan& pl, AttnArgs& a, int num_seqs, hipStream_t st
   return PKV_OK;
 }
 
+// Ring depths instantiated for (T, GW): 2 always; 3 and 4 for bf16 where
+// max_prefetch allows (prefetch_depth never asks for more).
+template <typename T, int GW, int P>
+constexpr bool ring_built() { return P == 2 || (sizeof(T) == 2 && P <= max_prefetch<GW>()); }
+
 template <typename T, int D, int GW>
 pkv_status launch_main_p(const Plan& pl, AttnArgs& a, int num_seqs, hipStream_t st) {
-  if constexpr (sizeof(T) == 4) {  // fp32 rows: twice the registers, ring of 2 only
-    return launch_main<T, D, GW, 2>(pl, a, num_seqs, st);
-  } else {
-    switch (pl.prefetch) {
-      case 4: return launch_main<T, D, GW, 4>(pl, a, num_seqs, st);
-      case 3: return launch_main<T, D, GW, 3>(pl, a, num_seqs, st);
-      default: return launch_main<T, D, GW, 2>(pl, a, num_seqs, st);
-    }
-  }
+  if constexpr (ring_built<T, GW, 4>())
+    if (pl.prefetch == 4) return launch_main<T, D, GW, 4>(pl, a, num_seqs, st);
+  if constexpr (ring_built<T, GW, 3>())
+    if (pl.prefetch == 3) return launch_main<T, D, GW, 3>(pl, a, num_seqs, st);
+  return launch_main<T, D, GW, 2>(pl, a, num_seqs, st);
 }
 
 // The grid of the balanced merge depends on W, which the main launch fixes;
 // a phase-2-only call recomputes it the same way.
 template <typename T, int D, int GW>
 int balanced_groups(const Plan& pl) {
-  const void* k = nullptr;
-  if constexpr (sizeof(T) == 4) {
-    k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 2>);
-  } else {
-    switch (pl.prefetch) {
-      case 4: k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 4>); break;
-      case 3: k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 3>); break;
-      default: k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 2>); break;
-    }
-  }
+  const void* k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 2>);
+  if constexpr (ring_built<T, GW, 4>())
+    if (pl.prefetch == 4) k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 4>);
+  if constexpr (ring_built<T, GW, 3>())
+    if (pl.prefetch == 3) k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 3>);
   int blocks = resident_blocks(k, 64 * pl.waves_per_block);
   const int max_blocks = kMaxWaveGroups / pl.groups_per_block;
   if (blocks > max_blocks) blocks = max_blocks;
@@ -905,11 +993,15 @@ pkv_status dispatch_gw(int phases, const Plan& pl, AttnArgs& a, int num_seqs, in
 template <typename T, int D>
 pkv_status dispatch(int phases, const Plan& pl, AttnArgs& a, int num_seqs, int num_q_heads,
                     hipStream_t st) {
-  switch (pl.gw) {
-    case 4: return dispatch_gw<T, D, 4>(phases, pl, a, num_seqs, num_q_heads, st);
-    case 3: return dispatch_gw<T, D, 3>(phases, pl, a, num_seqs, num_q_heads, st);
-    case 2: return dispatch_gw<T, D, 2>(phases, pl, a, num_seqs, num_q_heads, st);
-    default: return dispatch_gw<T, D, 1>(phases, pl, a, num_seqs, num_q_heads, st);
+  if constexpr (sizeof(T) == 4 && D == 128) {  // heads_per_wave() gives 1 here
+    return dispatch_gw<T, D, 1>(phases, pl, a, num_seqs, num_q_heads, st);
+  } else {
+    switch (pl.gw) {
+      case 4: return dispatch_gw<T, D, 4>(phases, pl, a, num_seqs, num_q_heads, st);
+      case 3: return dispatch_gw<T, D, 3>(phases, pl, a, num_seqs, num_q_heads, st);
+      case 2: return dispatch_gw<T, D, 2>(phases, pl, a, num_seqs, num_q_heads, st);
+      default: return dispatch_gw<T, D, 1>(phases, pl, a, num_seqs, num_q_heads, st);
+    }
   }
 }
 
@@ -1002,6 +1094,7 @@ pkv_status pkv_attention_decode_phase(int32_t phases, const void* q, const void*
   a.num_parts = pl.num_parts;
   a.groups_per_block = pl.groups_per_block;
   a.num_groups = 0;
+  a.static_blocks = 0;
   a.scale_log2 = static_cast<float>(double(scale) * 1.4426950408889634);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (geom->dtype == PKV_BF16) {

@@ -91,9 +91,9 @@ def test_attention_validation_and_workspace_size():
     # fixed partitions: N * Hq * P * (D + 2) floats
     n = lib.pkv_attention_workspace_bytes(2, 8, 100, 32, ctypes.byref(g()))
     assert n == 2 * 8 * 4 * (64 + 2) * 4
-    # the automatic (balanced) split: (N * H_kv + 8192) * G rows of D + 2 floats,
-    # plus the (N + 1) prefix sums rounded up to 256 bytes
-    rows = (2 * 2 + 8192) * 4
+    # the automatic (balanced) split: (N * H_kv + 8192 shares + 8192 chunks) * G
+    # rows of D + 2 floats and the (N + 1) prefix sums rounded up to 256 bytes
+    rows = (2 * 2 + 8192 + 8192) * 4
     assert lib.pkv_attention_workspace_bytes(2, 8, 100, 0, ctypes.byref(g())) == \
         rows * (64 + 2) * 4 + 256
     assert lib.pkv_attention_workspace_bytes(2, 8, 100, 24, ctypes.byref(g())) == \
