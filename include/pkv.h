@@ -26,8 +26,10 @@
  *    as [num_blocks * block_size][num_kv_heads][head_dim]: slot = physical
  *    block id * block_size + offset in block ([SLOT §locate], token-slot
  *    equation).
- *  - Element type: ``pkv_geom.dtype`` (fp32 or bf16) for the pools and for every
- *    K/V/Q/output buffer; no conversion is ever made.
+ *  - Element type: ``pkv_geom.dtype`` for the pools.  With fp32 or bf16 pools
+ *    every K/V/Q/output buffer has the pool's type and no conversion is made;
+ *    with the one-byte code types (FP8 e4m3, INT8) tokens, queries and
+ *    outputs are bf16 and the *_quant entry points quantize and dequantize.
  *  - Ownership: the caller allocates and owns every buffer (pools, tokens,
  *    index arrays, query, output, workspace).  The library keeps no pointer
  *    after a call returns and allocates no device memory on these paths.
@@ -61,7 +63,11 @@ typedef int32_t pkv_status;
 #define PKV_ERR_NO_FREE_BLOCKS 3 /* block manager: pool exhausted             */
 #define PKV_ERR_HIP 4            /* the HIP runtime refused a launch          */
 
-typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+/* Element types.  PKV_F32 and PKV_BF16 pools hold values of the model dtype.
+ * PKV_FP8_E4M3 and PKV_INT8 pools hold one-byte codes ([KVM §19.2.4] precision
+ * table; [PFX] section "KV Cache 量化"): their tokens, queries and outputs are
+ * bf16, and the *_quant entry points below convert. */
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2, PKV_INT8 = 3 } pkv_dtype;
 
 /* Geometry of one cache pool pair.  block_size must be a power of two;
  * num_blocks * block_size < 2^31. */
@@ -109,6 +115,44 @@ pkv_status pkv_write(const void* k, const void* v, const int32_t* slot_mapping,
 pkv_status pkv_copy_blocks(const int32_t* src_dst_pairs, int32_t num_pairs,
                            void* k_cache, void* v_cache, const pkv_geom* geom,
                            void* stream);
+
+/* ---- Quantized caches ([KVM §19.2.4]; [PFX] "KV Cache 量化"; [ENG §7.5]) ----
+ *
+ * PKV_FP8_E4M3: codes are OCP e4m3 (1 sign, 4 exponent bits with bias 7, 3
+ *   mantissa bits; largest magnitude 448; S.1111.111 is NaN).  One scale per
+ *   tensor: value = e4m3(code) * k_scale (or v_scale); the engine default the
+ *   pages give is 1.0.  Writing encodes x / scale, computed in fp32, saturated
+ *   to +-448 and rounded to the nearest code (ties to the even code).
+ * PKV_INT8: per-token codes: every (token, KV head) vector of head_dim values
+ *   has its own scale = max|x| / 127 and code = round(x / scale) (fp32, round
+ *   half to even, clamped to +-127; an all-zero vector gets scale 0 and codes
+ *   0); value = code * scale.  The scales live in fp32 pools laid out like the
+ *   slots, [num_blocks * block_size][num_kv_heads].
+ * Quantized pools need head_dim 128. */
+typedef struct pkv_kv_scales {
+  float k_scale;        /* PKV_FP8_E4M3: per-tensor scales (finite, > 0)       */
+  float v_scale;
+  float* k_scales;      /* PKV_INT8: device fp32 [num_blocks*block_size][H_kv] */
+  float* v_scales;      /*   (ignored, may be NULL, for PKV_FP8_E4M3)          */
+} pkv_kv_scales;
+
+/* pkv_write_quant -- quantizing slot write: bf16 token rows k, v (device
+ * [num_tokens][num_kv_heads][head_dim]) are encoded as above and scattered to
+ * slot_mapping[i] as pkv_write does (negative slot = skip; slots must be
+ * distinct); INT8 also stores each (token, head) scale at [slot][head] of the
+ * scale pools.  Errors: INVALID_ARG (including a non-quantized dtype),
+ * UNSUPPORTED (head_dim other than 128), HIP. */
+pkv_status pkv_write_quant(const void* k, const void* v, const int32_t* slot_mapping,
+                           int32_t num_tokens, void* k_cache, void* v_cache,
+                           const pkv_kv_scales* scales, const pkv_geom* geom, void* stream);
+
+/* pkv_copy_blocks_quant -- pkv_copy_blocks for quantized pools: the codes of
+ * each dst block become a bit copy of the src block's, and for PKV_INT8 so do
+ * the scale rows of the block (with per-token scales the copy stays a plain
+ * bit copy, [ENG §7.5]).  Same pair rules and errors as pkv_copy_blocks. */
+pkv_status pkv_copy_blocks_quant(const int32_t* src_dst_pairs, int32_t num_pairs,
+                                 void* k_cache, void* v_cache, const pkv_kv_scales* scales,
+                                 const pkv_geom* geom, void* stream);
 
 /* Split-KV partition length (tokens) that pkv_attention_decode uses when its
  * partition_tokens argument is 0 and it splits by fixed partitions: max_seq_len
@@ -178,6 +222,21 @@ pkv_status pkv_attention_decode_phase(int32_t phases, const void* q, const void*
                                       int32_t max_blocks_per_seq, const int32_t* seq_lens,
                                       float scale, void* out, int32_t num_seqs,
                                       int32_t num_q_heads, int32_t max_seq_len,
+                                      int32_t partition_tokens, void* workspace,
+                                      size_t workspace_bytes, const pkv_geom* geom,
+                                      void* stream);
+
+/* pkv_attention_decode_quant -- pkv_attention_decode_phase over a quantized
+ * cache (PKV_FP8_E4M3 or PKV_INT8 pools, scales as described with
+ * pkv_kv_scales): the same attention of bf16 queries over the dequantized K/V
+ * values, written as bf16.  phases, workspace, partition_tokens and errors as
+ * for pkv_attention_decode_phase; pkv_attention_workspace_bytes and
+ * pkv_attention_partition_tokens take the quantized geometry as well. */
+pkv_status pkv_attention_decode_quant(int32_t phases, const void* q, const void* k_cache,
+                                      const void* v_cache, const pkv_kv_scales* scales,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* seq_lens, float scale, void* out,
+                                      int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
                                       int32_t partition_tokens, void* workspace,
                                       size_t workspace_bytes, const pkv_geom* geom,
                                       void* stream);

@@ -41,8 +41,7 @@ class OracleState:
                 s, n = op[1], op[2]
                 slots, cow = bm.append_slots([s], n)
                 assert not cow, "context appends never write into shared blocks"
-                write(wl.ctx_k[cursor:cursor + n], wl.ctx_v[cursor:cursor + n],
-                      slots, self.k_pool, self.v_pool)
+                self._write(wl.ctx_k[cursor:cursor + n], wl.ctx_v[cursor:cursor + n], slots)
                 self.ctx_slots.extend(slots)
                 if self.keep_values:
                     self.hist_k[s].extend(range(cursor, cursor + n))
@@ -88,10 +87,16 @@ class OracleState:
                 self.hist_k[int(s)].append(("new", i))
                 self.hist_v[int(s)].append(("new", i))
 
+    def _write(self, k, v, slots):
+        write(k, v, slots, self.k_pool, self.v_pool)
+
+    def _copy(self, pairs):
+        copy_blocks(pairs, self.k_pool, self.v_pool)
+
     def decode_device_part(self):
         """copy -> write on the oracle pools."""
-        copy_blocks(self.cow_pairs.tolist(), self.k_pool, self.v_pool)
-        write(self.wl.new_k, self.wl.new_v, self.slot_mapping, self.k_pool, self.v_pool)
+        self._copy(self.cow_pairs.tolist())
+        self._write(self.wl.new_k, self.wl.new_v, self.slot_mapping)
 
     def attention(self, seqs=None):
         from .attention import attention_decode
@@ -118,6 +123,52 @@ def run_step(wl, keep_values=True):
     """Full oracle decode step.  Returns the ``OracleState`` after copy and write
     (attention is computed on demand with ``.attention()``)."""
     st = OracleState(wl, keep_values=keep_values)
+    st.build_context()
+    st.decode_tables()
+    st.decode_device_part()
+    return st
+
+
+class QuantOracleState(OracleState):
+    """The same step over a quantized cache (oracle/quant.py): writes encode
+    the workload's bf16 rows, copies carry INT8 scale rows, attention reads the
+    dequantized pools."""
+
+    def __init__(self, wl, kind, k_scale=1.0, v_scale=1.0, keep_values=False):
+        from . import quant
+        super().__init__(wl, keep_values=keep_values)
+        self.kind, self.k_scale, self.v_scale = kind, float(k_scale), float(v_scale)
+        dt = np.uint8 if kind == quant.FP8 else np.int8
+        self.k_pool = np.zeros(self.k_pool.shape, dtype=dt)
+        self.v_pool = np.zeros(self.v_pool.shape, dtype=dt)
+        if kind == quant.INT8:
+            n = wl.num_blocks * wl.block_size
+            self.k_scales = np.zeros((n, wl.num_kv_heads), np.float32)
+            self.v_scales = np.zeros((n, wl.num_kv_heads), np.float32)
+        else:
+            self.k_scales = self.v_scales = None
+
+    def _write(self, k, v, slots):
+        from . import quant
+        quant.write_quant(k, v, slots, self.k_pool, self.v_pool, self.kind, self.k_scale,
+                          self.v_scale, self.k_scales, self.v_scales)
+
+    def _copy(self, pairs):
+        from . import quant
+        quant.copy_blocks_quant(pairs, self.k_pool, self.v_pool, self.kind, self.k_scales,
+                                self.v_scales)
+
+    def attention(self, seqs=None):
+        from . import quant
+        wl = self.wl
+        return quant.attention_decode_quant(wl.q, self.k_pool, self.v_pool, self.block_tables,
+                                            self.seq_lens, wl.scale, self.kind, self.k_scale,
+                                            self.v_scale, self.k_scales, self.v_scales, seqs=seqs)
+
+
+def run_step_quant(wl, kind, k_scale=1.0, v_scale=1.0):
+    """Full oracle decode step over a quantized cache (see QuantOracleState)."""
+    st = QuantOracleState(wl, kind, k_scale, v_scale)
     st.build_context()
     st.decode_tables()
     st.decode_device_part()

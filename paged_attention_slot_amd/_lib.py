@@ -19,12 +19,17 @@ P_i32 = ctypes.POINTER(ctypes.c_int32)
 P_i64 = ctypes.POINTER(ctypes.c_int64)
 
 PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_NO_FREE_BLOCKS, PKV_ERR_HIP = range(5)
-PKV_F32, PKV_BF16 = 0, 1
+PKV_F32, PKV_BF16, PKV_FP8_E4M3, PKV_INT8 = 0, 1, 2, 3
 
 
 class PkvGeom(ctypes.Structure):
     _fields_ = [("num_blocks", c_i32), ("block_size", c_i32), ("num_kv_heads", c_i32),
                 ("head_dim", c_i32), ("dtype", c_i32)]
+
+
+class PkvKvScales(ctypes.Structure):
+    _fields_ = [("k_scale", c_float), ("v_scale", c_float), ("k_scales", c_void_p),
+                ("v_scales", c_void_p)]
 
 
 # name -> (restype, argtypes); mirrors include/pkv.h
@@ -35,6 +40,16 @@ SIGNATURES = {
                           ctypes.POINTER(PkvGeom), c_void_p]),
     "pkv_copy_blocks": (c_i32, [c_void_p, c_i32, c_void_p, c_void_p, ctypes.POINTER(PkvGeom),
                                 c_void_p]),
+    "pkv_write_quant": (c_i32, [c_void_p, c_void_p, c_void_p, c_i32, c_void_p, c_void_p,
+                                ctypes.POINTER(PkvKvScales), ctypes.POINTER(PkvGeom), c_void_p]),
+    "pkv_copy_blocks_quant": (c_i32, [c_void_p, c_i32, c_void_p, c_void_p,
+                                      ctypes.POINTER(PkvKvScales), ctypes.POINTER(PkvGeom),
+                                      c_void_p]),
+    "pkv_attention_decode_quant": (c_i32, [c_i32, c_void_p, c_void_p, c_void_p,
+                                           ctypes.POINTER(PkvKvScales), c_void_p, c_i32,
+                                           c_void_p, c_float, c_void_p, c_i32, c_i32, c_i32,
+                                           c_i32, c_void_p, c_size, ctypes.POINTER(PkvGeom),
+                                           c_void_p]),
     "pkv_attention_partition_tokens": (c_i32, [c_i32, c_i32, c_i32, ctypes.POINTER(PkvGeom)]),
     "pkv_attention_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32,
                                                ctypes.POINTER(PkvGeom)]),

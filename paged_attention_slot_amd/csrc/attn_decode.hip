@@ -46,6 +46,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 #include <cstdlib>
 #include <mutex>
 #include <unordered_map>
@@ -98,7 +99,21 @@ struct AttnArgs {
   int32_t num_groups;       // W: wave groups of the static (resident) part of the grid
   int32_t static_blocks;    // workgroups of the static part; the rest run dynamic chunks
   float scale_log2;
+  // quantized caches: per-tensor scales (FP8) or fp32 scale pools
+  // [num_blocks * block_size][num_kv_heads] (INT8)
+  float k_scale, v_scale;
+  const float* k_scales;
+  const float* v_scales;
 };
+
+// One-byte cache element types ([KVM §19.2.4], [PFX] "KV Cache 量化"): OCP e4m3
+// codes with a per-tensor scale, and INT8 codes with one scale per (token, KV
+// head).  Queries and outputs of these caches are bf16.
+struct fp8_e4m3 { uint8_t bits; };
+struct int8_code { int8_t bits; };
+template <typename T> constexpr bool kQuant = sizeof(T) == 1;
+template <typename T> constexpr bool kInt8 = std::is_same<T, int8_code>::value;
+template <typename T> using OutT = typename std::conditional<kQuant<T>, uint16_t, T>::type;
 
 template <typename T, int D>
 struct Shape {
@@ -114,6 +129,7 @@ template <typename T, int D>
 struct TileBuf {
   uint4 k[2][Shape<T, D>::kCPL];
   uint4 v[2][Shape<T, D>::kCPL];
+  float ks[2], vs[2];  // INT8: scales of this lane's two positions
 };
 
 struct TileInfo {
@@ -182,11 +198,42 @@ __device__ __forceinline__ void set_priority(int lv) {
   else __builtin_amdgcn_s_setprio(0);
 }
 
+// 16 one-byte codes -> 16 floats (exact): e4m3 through the gfx950 packed
+// fp8 -> f32 conversion, INT8 by sign extension.
+template <typename T>
+__device__ __forceinline__ void decode16(const uint4& x, float (&f)[16]) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (kInt8<T>) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        f[4 * i + j] = static_cast<float>(static_cast<int8_t>((w[i] >> (8 * j)) & 0xFFu));
+    } else {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[i]), false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[i]), true);
+      f[4 * i] = lo[0];
+      f[4 * i + 1] = lo[1];
+      f[4 * i + 2] = hi[0];
+      f[4 * i + 3] = hi[1];
+    }
+  }
+}
+
+// Two floats that bf16 holds exactly -> one bf16 pair (lo in the low half).
+__device__ __forceinline__ uint32_t bf16_pair_exact(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+}
+
 // One wave's attention over a stretch [start, end) of one stream.
 template <typename T, int D, int GW, int P>
 struct Wave {
   using S = Shape<T, D>;
   static constexpr int kCPL = S::kCPL, kEPC = S::kEPC, kNE = S::kNE;
+  // Queries and outputs: the cache type, or bf16 for one-byte codes (lane c
+  // then holds row elements 16c .. 16c+15, i.e. two bf16 chunks).
+  static constexpr int kQES = kQuant<T> ? 2 : S::kES;
+  static constexpr int kQC = kQuant<T> ? 2 : kCPL;
 
   const AttnArgs& a;
   int lane, r, c;
@@ -197,7 +244,8 @@ struct Wave {
   int64_t head_off;      // byte offset of the KV head inside a pool row
   int blk[2];
 
-  uint4 q[GW][kCPL];
+  uint4 q[GW][kQC];
+  int kvh_;              // the KV head (INT8 scale column)
   float m[GW], l[GW], acc[GW][kNE];
   float M[GW], lt[GW];   // after run(): merged reference and sum
 
@@ -248,6 +296,12 @@ struct Wave {
         b.k[i][j] = *reinterpret_cast<const uint4*>(kb + lane_off + 128 * j);
         b.v[i][j] = *reinterpret_cast<const uint4*>(vb + lane_off + 128 * j);
       }
+      if constexpr (kInt8<T>) {
+        // scale of this lane's position (sub-stream r): slot * H_kv + head
+        const int64_t si = (int64_t(blk[i]) * (bmask + 1) + (pos & bmask) + r) * a.num_kv_heads + kvh_;
+        b.ks[i] = a.k_scales[si];
+        b.vs[i] = a.v_scales[si];
+      }
     }
   }
 
@@ -260,14 +314,36 @@ struct Wave {
     float sc[2][GW];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+      if constexpr (kQuant<T>) {
+        // codes -> exact bf16 pairs, dotted with the bf16 query; the K scale
+        // multiplies the score (per tensor for FP8, per position for INT8)
+        float kf[16];
+        decode16<T>(b.k[i][0], kf);
+        uint32_t kp[8];
 #pragma unroll
-      for (int hh = 0; hh < GW; ++hh) {
-        float d = 0.f;
+        for (int w = 0; w < 8; ++w) kp[w] = bf16_pair_exact(kf[2 * w], kf[2 * w + 1]);
+        const float ksc = kInt8<T> ? a.scale_log2 * b.ks[i] : a.scale_log2 * a.k_scale;
 #pragma unroll
-        for (int j = 0; j < kCPL; ++j) d = dot_chunk<T>(q[hh][j], b.k[i][j], d);
-        d = pkv::sum8(d) * a.scale_log2;
-        if constexpr (kMasked) d = valid[i] ? d : -INFINITY;
-        sc[i][hh] = d;
+        for (int hh = 0; hh < GW; ++hh) {
+          const uint32_t qw[8] = {q[hh][0].x, q[hh][0].y, q[hh][0].z, q[hh][0].w,
+                                  q[hh][1].x, q[hh][1].y, q[hh][1].z, q[hh][1].w};
+          float d = 0.f;
+#pragma unroll
+          for (int w = 0; w < 8; ++w) d = pkv::dot2_bf16(qw[w], kp[w], d);
+          d = pkv::sum8(d) * ksc;
+          if constexpr (kMasked) d = valid[i] ? d : -INFINITY;
+          sc[i][hh] = d;
+        }
+      } else {
+#pragma unroll
+        for (int hh = 0; hh < GW; ++hh) {
+          float d = 0.f;
+#pragma unroll
+          for (int j = 0; j < kCPL; ++j) d = dot_chunk<T>(q[hh][j], b.k[i][j], d);
+          d = pkv::sum8(d) * a.scale_log2;
+          if constexpr (kMasked) d = valid[i] ? d : -INFINITY;
+          sc[i][hh] = d;
+        }
       }
     }
 
@@ -301,12 +377,24 @@ struct Wave {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       float vf[kNE];
+      if constexpr (kQuant<T>) {
+        decode16<T>(b.v[i][0], vf);
+        // the V scale rides on the weight p (the sum l keeps the bare p); a
+        // masked position's weight is exactly 0 whatever its scale slot holds
+        const float vsc = kInt8<T> ? b.vs[i] : a.v_scale;
 #pragma unroll
-      for (int j = 0; j < kCPL; ++j) {
-        float tmp[kEPC];
-        unpack<T>(b.v[i][j], tmp);
+        for (int hh = 0; hh < GW; ++hh) {
+          p[i][hh] *= vsc;
+          if constexpr (kMasked) p[i][hh] = valid[i] ? p[i][hh] : 0.f;
+        }
+      } else {
 #pragma unroll
-        for (int e = 0; e < kEPC; ++e) vf[j * kEPC + e] = tmp[e];
+        for (int j = 0; j < kCPL; ++j) {
+          float tmp[kEPC];
+          unpack<T>(b.v[i][j], tmp);
+#pragma unroll
+          for (int e = 0; e < kEPC; ++e) vf[j * kEPC + e] = tmp[e];
+        }
       }
       if constexpr (kMasked) {
         // A masked position may hold any bits (stale slot, foreign block):
@@ -331,12 +419,12 @@ struct Wave {
   // lt and acc (identical in every lane holding a given chunk).
   __device__ __forceinline__ void run(int s, int kvh, int h0, int start, int end) {
     const char* q_base =
-        static_cast<const char*>(a.q) + (int64_t(s) * a.num_q_heads + h0) * (D * S::kES);
+        static_cast<const char*>(a.q) + (int64_t(s) * a.num_q_heads + h0) * (D * kQES);
 #pragma unroll
     for (int hh = 0; hh < GW; ++hh) {
 #pragma unroll
-      for (int j = 0; j < kCPL; ++j)
-        q[hh][j] = *reinterpret_cast<const uint4*>(q_base + hh * D * S::kES + (c + 8 * j) * 16);
+      for (int j = 0; j < kQC; ++j)
+        q[hh][j] = *reinterpret_cast<const uint4*>(q_base + hh * D * kQES + q_chunk_off(j));
       m[hh] = kRefInit;
       l[hh] = 0.f;
 #pragma unroll
@@ -350,6 +438,7 @@ struct Wave {
     tcache = (blk_first + lane <= blk_last) ? trow[blk_first + lane] : 0;
     asm volatile("" ::"v"(tcache));
     head_off = int64_t(kvh) * D * S::kES;
+    kvh_ = kvh;
 
     // Ring of P register tile buffers, unrolled P times so each buffer keeps
     // its registers.  Tiles 0 .. ntiles-2 are full; the tail (the last <= P
@@ -391,20 +480,30 @@ struct Wave {
     }
   }
 
+  // Byte offset, inside a query/output row, of this lane's j-th chunk, and
+  // the row element of lane-local element e (the lane's elements in order).
+  __device__ __forceinline__ int q_chunk_off(int j) const {
+    return kQuant<T> ? 32 * c + 16 * j : (c + 8 * j) * 16;
+  }
+  __device__ __forceinline__ int elem_of(int e) const {
+    return kQuant<T> ? 16 * c + e : (c + 8 * (e / kEPC)) * kEPC + e % kEPC;
+  }
+
   // Normalised output rows of heads h0 .. h0+GW-1 (sub-stream 0 stores).
   __device__ __forceinline__ void write_out(int s, int h0) {
     if (r != 0) return;
-    char* out_base = static_cast<char*>(a.out) + (int64_t(s) * a.num_q_heads + h0) * (D * S::kES);
+    using O = OutT<T>;
+    constexpr int kOE = 16 / sizeof(O);  // output elements per chunk
+    char* out_base = static_cast<char*>(a.out) + (int64_t(s) * a.num_q_heads + h0) * (D * kQES);
 #pragma unroll
     for (int hh = 0; hh < GW; ++hh) {
       const float inv = 1.0f / lt[hh];
 #pragma unroll
-      for (int j = 0; j < kCPL; ++j) {
-        float f[kEPC];
+      for (int j = 0; j < kQC; ++j) {
+        float f[kOE];
 #pragma unroll
-        for (int e = 0; e < kEPC; ++e) f[e] = acc[hh][j * kEPC + e] * inv;
-        *reinterpret_cast<uint4*>(out_base + hh * D * S::kES + (c + 8 * j) * 16) =
-            pack_chunk<T>(f);
+        for (int e = 0; e < kOE; ++e) f[e] = acc[hh][j * kOE + e] * inv;
+        *reinterpret_cast<uint4*>(out_base + hh * D * kQES + q_chunk_off(j)) = pack_chunk<O>(f);
       }
     }
   }
@@ -412,12 +511,12 @@ struct Wave {
   // Zero output rows (empty history).
   __device__ __forceinline__ void write_zero(int s, int h0) {
     if (r != 0) return;
-    char* out_base = static_cast<char*>(a.out) + (int64_t(s) * a.num_q_heads + h0) * (D * S::kES);
+    char* out_base = static_cast<char*>(a.out) + (int64_t(s) * a.num_q_heads + h0) * (D * kQES);
 #pragma unroll
     for (int hh = 0; hh < GW; ++hh)
 #pragma unroll
-      for (int j = 0; j < kCPL; ++j)
-        *reinterpret_cast<uint4*>(out_base + hh * D * S::kES + (c + 8 * j) * 16) =
+      for (int j = 0; j < kQC; ++j)
+        *reinterpret_cast<uint4*>(out_base + hh * D * kQES + q_chunk_off(j)) =
             make_uint4(0, 0, 0, 0);
   }
 
@@ -429,15 +528,9 @@ struct Wave {
       const int64_t row = row0 + hh * row_stride;
       float* dst = a.ws_acc + row * D;
 #pragma unroll
-      for (int j = 0; j < kCPL; ++j) {
-#pragma unroll
-        for (int e4 = 0; e4 < kEPC; e4 += 4) {
-          const int elem = (c + 8 * j) * kEPC + e4;
-          const int src = j * kEPC + e4;
-          *reinterpret_cast<float4*>(dst + elem) =
-              make_float4(acc[hh][src], acc[hh][src + 1], acc[hh][src + 2], acc[hh][src + 3]);
-        }
-      }
+      for (int e4 = 0; e4 < kNE; e4 += 4)
+        *reinterpret_cast<float4*>(dst + elem_of(e4)) =
+            make_float4(acc[hh][e4], acc[hh][e4 + 1], acc[hh][e4 + 2], acc[hh][e4 + 3]);
       if (c == 0) a.ws_ml[row] = make_float2(M[hh], lt[hh]);
     }
   }
@@ -816,6 +909,9 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
   if (num_q_heads % g->num_kv_heads != 0)
     return pkv::fail(PKV_ERR_INVALID_ARG, "%s: num_q_heads %d is not a multiple of num_kv_heads %d",
                      who, num_q_heads, g->num_kv_heads);
+  if (pkv::is_quant(g->dtype) && g->head_dim != 128)
+    return pkv::fail(PKV_ERR_UNSUPPORTED, "%s: head_dim %d (quantized caches: 128)", who,
+                     g->head_dim);
   if (g->head_dim != 64 && g->head_dim != 128)
     return pkv::fail(PKV_ERR_UNSUPPORTED, "%s: head_dim %d (built: 64, 128)", who, g->head_dim);
   if (g->block_size < 8)
@@ -939,7 +1035,7 @@ pkv_status launch_main(const Plan& pl, AttnArgs& a, int num_seqs, hipStream_t st
 // Ring depths instantiated for (T, GW): 2 always; 3 and 4 for bf16 where
 // max_prefetch allows (prefetch_depth never asks for more).
 template <typename T, int GW, int P>
-constexpr bool ring_built() { return P == 2 || (sizeof(T) == 2 && P <= max_prefetch<GW>()); }
+constexpr bool ring_built() { return P == 2 || (sizeof(T) <= 2 && P <= max_prefetch<GW>()); }
 
 template <typename T, int D, int GW>
 pkv_status launch_main_p(const Plan& pl, AttnArgs& a, int num_seqs, hipStream_t st) {
@@ -977,10 +1073,10 @@ pkv_status dispatch_gw(int phases, const Plan& pl, AttnArgs& a, int num_seqs, in
   }
   if (phases & 2) {
     if (pl.mode == kBalancedMode) {
-      hipLaunchKernelGGL((attn_merge_balanced_kernel<T, D>), dim3(num_q_heads, num_seqs),
+      hipLaunchKernelGGL((attn_merge_balanced_kernel<OutT<T>, D>), dim3(num_q_heads, num_seqs),
                          dim3(kMergeThreads), 0, st, a);
     } else if (pl.num_parts > 1) {
-      hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3(num_q_heads, num_seqs),
+      hipLaunchKernelGGL((attn_merge_kernel<OutT<T>, D>), dim3(num_q_heads, num_seqs),
                          dim3(kMergeThreads), 0, st, a);
     }
     if (hipError_t e = hipGetLastError())
@@ -1033,15 +1129,17 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int3
   return pl.ws_bytes;
 }
 
-pkv_status pkv_attention_decode_phase(int32_t phases, const void* q, const void* k_cache,
-                                      const void* v_cache, const int32_t* block_tables,
-                                      int32_t max_blocks_per_seq, const int32_t* seq_lens,
-                                      float scale, void* out, int32_t num_seqs,
-                                      int32_t num_q_heads, int32_t max_seq_len,
-                                      int32_t partition_tokens, void* workspace,
-                                      size_t workspace_bytes, const pkv_geom* geom,
-                                      void* stream) {
-  const char* who = "pkv_attention_decode";
+}  // extern "C"
+
+namespace {
+
+pkv_status attention_impl(const char* who, int32_t phases, const void* q, const void* k_cache,
+                          const void* v_cache, const pkv_kv_scales* scales,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* seq_lens, float scale, void* out, int32_t num_seqs,
+                          int32_t num_q_heads, int32_t max_seq_len, int32_t partition_tokens,
+                          void* workspace, size_t workspace_bytes, const pkv_geom* geom,
+                          void* stream) {
   if (phases < 1 || phases > 3)
     return pkv::fail(PKV_ERR_INVALID_ARG, "%s: phases must be 1, 2 or 3", who);
   Plan pl;
@@ -1049,6 +1147,19 @@ pkv_status pkv_attention_decode_phase(int32_t phases, const void* q, const void*
                                 partition_tokens, geom, who, &pl))
     return st;
   if (!std::isfinite(scale)) return pkv::fail(PKV_ERR_INVALID_ARG, "%s: scale is not finite", who);
+  const bool quant = pkv::is_quant(geom->dtype);
+  if (quant) {
+    if (!scales) return pkv::fail(PKV_ERR_INVALID_ARG, "%s: null scales", who);
+    if (geom->dtype == PKV_FP8_E4M3 &&
+        !(std::isfinite(scales->k_scale) && scales->k_scale > 0.0f &&
+          std::isfinite(scales->v_scale) && scales->v_scale > 0.0f))
+      return pkv::fail(PKV_ERR_INVALID_ARG, "%s: FP8 scales must be finite and > 0", who);
+    if (geom->dtype == PKV_INT8 && num_seqs > 0 &&
+        (!scales->k_scales || !scales->v_scales ||
+         (reinterpret_cast<uintptr_t>(scales->k_scales) & 3u) ||
+         (reinterpret_cast<uintptr_t>(scales->v_scales) & 3u)))
+      return pkv::fail(PKV_ERR_INVALID_ARG, "%s: INT8 scale pools null or misaligned", who);
+  }
   if (num_seqs == 0) return PKV_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out)
     return pkv::fail(PKV_ERR_INVALID_ARG, "%s: null pointer", who);
@@ -1096,13 +1207,59 @@ pkv_status pkv_attention_decode_phase(int32_t phases, const void* q, const void*
   a.num_groups = 0;
   a.static_blocks = 0;
   a.scale_log2 = static_cast<float>(double(scale) * 1.4426950408889634);
+  a.k_scale = quant ? scales->k_scale : 1.0f;
+  a.v_scale = quant ? scales->v_scale : 1.0f;
+  a.k_scales = quant ? scales->k_scales : nullptr;
+  a.v_scales = quant ? scales->v_scales : nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (geom->dtype == PKV_FP8_E4M3)
+    return dispatch<fp8_e4m3, 128>(phases, pl, a, num_seqs, num_q_heads, st);
+  if (geom->dtype == PKV_INT8)
+    return dispatch<int8_code, 128>(phases, pl, a, num_seqs, num_q_heads, st);
   if (geom->dtype == PKV_BF16) {
     return geom->head_dim == 128 ? dispatch<uint16_t, 128>(phases, pl, a, num_seqs, num_q_heads, st)
                                  : dispatch<uint16_t, 64>(phases, pl, a, num_seqs, num_q_heads, st);
   }
   return geom->head_dim == 128 ? dispatch<float, 128>(phases, pl, a, num_seqs, num_q_heads, st)
                                : dispatch<float, 64>(phases, pl, a, num_seqs, num_q_heads, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_attention_decode_phase(int32_t phases, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                      float scale, void* out, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t max_seq_len,
+                                      int32_t partition_tokens, void* workspace,
+                                      size_t workspace_bytes, const pkv_geom* geom,
+                                      void* stream) {
+  const char* who = "pkv_attention_decode";
+  if (geom && pkv::is_quant(geom->dtype))
+    return pkv::fail(PKV_ERR_INVALID_ARG,
+                     "%s: quantized pools need scales (pkv_attention_decode_quant)", who);
+  return attention_impl(who, phases, q, k_cache, v_cache, nullptr, block_tables,
+                        max_blocks_per_seq, seq_lens, scale, out, num_seqs, num_q_heads,
+                        max_seq_len, partition_tokens, workspace, workspace_bytes, geom, stream);
+}
+
+pkv_status pkv_attention_decode_quant(int32_t phases, const void* q, const void* k_cache,
+                                      const void* v_cache, const pkv_kv_scales* scales,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* seq_lens, float scale, void* out,
+                                      int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
+                                      int32_t partition_tokens, void* workspace,
+                                      size_t workspace_bytes, const pkv_geom* geom,
+                                      void* stream) {
+  const char* who = "pkv_attention_decode_quant";
+  if (geom && !pkv::is_quant(geom->dtype))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "%s: dtype %d is not a quantized cache type", who,
+                     geom->dtype);
+  return attention_impl(who, phases, q, k_cache, v_cache, scales, block_tables,
+                        max_blocks_per_seq, seq_lens, scale, out, num_seqs, num_q_heads,
+                        max_seq_len, partition_tokens, workspace, workspace_bytes, geom, stream);
 }
 
 pkv_status pkv_attention_decode(const void* q, const void* k_cache, const void* v_cache,

@@ -7,7 +7,18 @@
 
 namespace pkv {
 
-inline int elem_size(int32_t dtype) { return dtype == PKV_F32 ? 4 : dtype == PKV_BF16 ? 2 : 0; }
+inline int elem_size(int32_t dtype) {
+  switch (dtype) {
+    case PKV_F32: return 4;
+    case PKV_BF16: return 2;
+    case PKV_FP8_E4M3:
+    case PKV_INT8: return 1;
+    default: return 0;
+  }
+}
+
+// One-byte code pools that need scales and bf16 tokens.
+inline bool is_quant(int32_t dtype) { return dtype == PKV_FP8_E4M3 || dtype == PKV_INT8; }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

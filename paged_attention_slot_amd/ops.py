@@ -10,9 +10,11 @@ import ctypes
 
 import torch
 
-from ._lib import PKV_BF16, PKV_F32, PkvGeom, check, lib
+from ._lib import PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_INT8, PkvGeom, PkvKvScales, check, lib
 
-_DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
+_DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16, torch.float8_e4m3fn: PKV_FP8_E4M3,
+           torch.int8: PKV_INT8}
+_QUANT = (torch.float8_e4m3fn, torch.int8)
 
 
 def geom_of(k_cache: torch.Tensor) -> PkvGeom:
@@ -94,21 +96,28 @@ def workspace_bytes(num_seqs: int, num_q_heads: int, max_seq_len: int, k_cache,
     return int(n)
 
 
-def attention_decode(q, k_cache, v_cache, block_tables, seq_lens, scale, out=None,
-                     max_seq_len=None, partition_tokens=0, workspace=None, stream=None,
-                     phases=3):
-    """Decode attention; returns ``out`` [N, H_q, D] (allocated if None).
+def _scales(k_cache, k_scale, v_scale, k_scales, v_scales) -> PkvKvScales:
+    if k_cache.dtype == torch.int8:
+        dev = k_cache.device
+        nb, B, H, _ = k_cache.shape
+        for t, n in ((k_scales, "k_scales"), (v_scales, "v_scales")):
+            if t is None:
+                raise ValueError(f"INT8 pools need {n}")
+            _need(t, n, torch.float32, dev)
+            if t.numel() != nb * B * H:
+                raise ValueError(f"{n} must hold [num_blocks * block_size, num_kv_heads] floats")
+    return PkvKvScales(float(k_scale), float(v_scale), _ptr(k_scales).value or None,
+                       _ptr(v_scales).value or None)
 
-    ``max_seq_len`` is the host-known bound of ``seq_lens`` (default: the
-    capacity of the block tables).  A workspace is allocated here only when the
-    caller passes none and the split needs one; callers that must not
-    allocate pass their own (size from ``workspace_bytes``).  ``phases``: 1 =
-    partition kernel only, 2 = merge only, 3 = both (see include/pkv.h)."""
+
+def _attention(q, k_cache, v_cache, block_tables, seq_lens, scale, out, max_seq_len,
+               partition_tokens, workspace, stream, phases, scales):
     g = geom_of(k_cache)
     dev = k_cache.device
+    quant = k_cache.dtype in _QUANT
     _need(k_cache, "k_cache", None, dev)
     _need(v_cache, "v_cache", k_cache.dtype, dev)
-    _need(q, "q", k_cache.dtype, dev)
+    _need(q, "q", torch.bfloat16 if quant else k_cache.dtype, dev)
     _need(block_tables, "block_tables", torch.int32, dev)
     _need(seq_lens, "seq_lens", torch.int32, dev)
     if v_cache.shape != k_cache.shape:
@@ -132,13 +141,88 @@ def attention_decode(q, k_cache, v_cache, block_tables, seq_lens, scale, out=Non
     if workspace is not None:
         _need(workspace, "workspace", None, dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    check(lib().pkv_attention_decode_phase(int(phases), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                           _ptr(block_tables), max_blocks, _ptr(seq_lens),
-                                           float(scale), _ptr(out), N, Hq, int(max_seq_len),
-                                           int(partition_tokens), _ptr(workspace), ws_bytes,
-                                           ctypes.byref(g), _stream(stream)),
-          "pkv_attention_decode")
+    common = (_ptr(block_tables), max_blocks, _ptr(seq_lens), float(scale), _ptr(out), N, Hq,
+              int(max_seq_len), int(partition_tokens), _ptr(workspace), ws_bytes,
+              ctypes.byref(g), _stream(stream))
+    if quant:
+        check(lib().pkv_attention_decode_quant(int(phases), _ptr(q), _ptr(k_cache),
+                                               _ptr(v_cache), ctypes.byref(scales), *common),
+              "pkv_attention_decode_quant")
+    else:
+        check(lib().pkv_attention_decode_phase(int(phases), _ptr(q), _ptr(k_cache),
+                                               _ptr(v_cache), *common), "pkv_attention_decode")
     return out
+
+
+def attention_decode(q, k_cache, v_cache, block_tables, seq_lens, scale, out=None,
+                     max_seq_len=None, partition_tokens=0, workspace=None, stream=None,
+                     phases=3):
+    """Decode attention; returns ``out`` [N, H_q, D] (allocated if None).
+
+    ``max_seq_len`` is the host-known bound of ``seq_lens`` (default: the
+    capacity of the block tables).  A workspace is allocated here only when the
+    caller passes none and the split needs one; callers that must not
+    allocate pass their own (size from ``workspace_bytes``).  ``phases``: 1 =
+    partition kernel only, 2 = merge only, 3 = both (see include/pkv.h)."""
+    if k_cache.dtype in _QUANT:
+        raise TypeError("quantized pools: use attention_decode_quant")
+    return _attention(q, k_cache, v_cache, block_tables, seq_lens, scale, out, max_seq_len,
+                      partition_tokens, workspace, stream, phases, None)
+
+
+def attention_decode_quant(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale=1.0,
+                           v_scale=1.0, k_scales=None, v_scales=None, out=None,
+                           max_seq_len=None, partition_tokens=0, workspace=None, stream=None,
+                           phases=3):
+    """Decode attention over an FP8 e4m3 (``torch.float8_e4m3fn`` pools,
+    per-tensor ``k_scale``/``v_scale``) or INT8 (``torch.int8`` pools, fp32
+    ``k_scales``/``v_scales`` [num_blocks * block_size, num_kv_heads]) cache;
+    q and out are bf16."""
+    if k_cache.dtype not in _QUANT:
+        raise TypeError("attention_decode_quant needs float8_e4m3fn or int8 pools")
+    sc = _scales(k_cache, k_scale, v_scale, k_scales, v_scales)
+    return _attention(q, k_cache, v_cache, block_tables, seq_lens, scale, out, max_seq_len,
+                      partition_tokens, workspace, stream, phases, sc)
+
+
+def write_quant(k, v, slot_mapping, k_cache, v_cache, k_scale=1.0, v_scale=1.0, k_scales=None,
+                v_scales=None, stream=None) -> None:
+    """Quantize bf16 token rows k/v [T, H_kv, D] into FP8 / INT8 pools at
+    ``slot_mapping`` (INT8 also writes each row's scale)."""
+    g = geom_of(k_cache)
+    dev = k_cache.device
+    if k_cache.dtype not in _QUANT:
+        raise TypeError("write_quant needs float8_e4m3fn or int8 pools")
+    _need(k_cache, "k_cache", None, dev)
+    _need(v_cache, "v_cache", k_cache.dtype, dev)
+    for t, n in ((k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, dev)
+    _need(slot_mapping, "slot_mapping", torch.int32, dev)
+    T = slot_mapping.numel()
+    if k.shape != (T, g.num_kv_heads, g.head_dim) or v.shape != k.shape:
+        raise ValueError("k/v must be [T, num_kv_heads, head_dim]")
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("pool shapes differ")
+    sc = _scales(k_cache, k_scale, v_scale, k_scales, v_scales)
+    check(lib().pkv_write_quant(_ptr(k), _ptr(v), _ptr(slot_mapping), T, _ptr(k_cache),
+                                _ptr(v_cache), ctypes.byref(sc), ctypes.byref(g),
+                                _stream(stream)), "pkv_write_quant")
+
+
+def copy_blocks_quant(pairs, k_cache, v_cache, k_scales=None, v_scales=None,
+                      stream=None) -> None:
+    """Whole-block copies of codes (and INT8 scale rows) for int32 [P, 2] pairs."""
+    g = geom_of(k_cache)
+    dev = k_cache.device
+    _need(k_cache, "k_cache", None, dev)
+    _need(v_cache, "v_cache", k_cache.dtype, dev)
+    _need(pairs, "pairs", torch.int32, dev)
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [P, 2]")
+    sc = _scales(k_cache, 1.0, 1.0, k_scales, v_scales)
+    check(lib().pkv_copy_blocks_quant(_ptr(pairs), pairs.shape[0], _ptr(k_cache), _ptr(v_cache),
+                                      ctypes.byref(sc), ctypes.byref(g), _stream(stream)),
+          "pkv_copy_blocks_quant")
 
 
 def stream_read(buf: torch.Tensor, sink: torch.Tensor, num_workgroups: int = 4096,

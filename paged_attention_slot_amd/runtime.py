@@ -13,6 +13,11 @@ history; page keys in include/pkv.h):
 ``layers`` > 1 keeps that many independent pool pairs with identical block
 tables (one per transformer layer); ``step(layer)`` runs the step on one of
 them, so consecutive steps read different memory as a model's layers do.
+
+``kv_dtype`` "fp8_e4m3" or "int8" keeps the pools as one-byte codes of the
+workload's bf16 values ([KVM §19.2.4]; [PFX] "KV Cache 量化"): writes quantize
+(pkv_write_quant), copies carry INT8 scales (pkv_copy_blocks_quant) and the
+attention dequantizes (pkv_attention_decode_quant).
 """
 from __future__ import annotations
 
@@ -34,19 +39,32 @@ def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
 
 
 def to_host_bits(t: torch.Tensor) -> np.ndarray:
-    """Device tensor -> host array of its stored values (uint16 bits for bf16)."""
+    """Device tensor -> host array of its stored values (uint16 bits for bf16,
+    uint8 codes for FP8 e4m3)."""
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).cpu().numpy()
     return t.cpu().numpy()
+
+
+_CACHE_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16,
+                 "fp8_e4m3": torch.float8_e4m3fn, "int8": torch.int8}
 
 
 class DecodeStep:
     def __init__(self, wl, device=None, layers: int = 1, partition_tokens: int | None = None,
-                 keep_context: bool = False):
+                 keep_context: bool = False, kv_dtype: str | None = None, k_scale: float = 1.0,
+                 v_scale: float = 1.0):
         self.wl = wl
         self.device = torch.device(device or "cuda")
         self.torch_dtype = torch.float32 if wl.dtype == "f32" else torch.bfloat16
         self.layers = int(layers)
+        self.kv_dtype = kv_dtype or wl.dtype
+        self.quant = self.kv_dtype in ("fp8_e4m3", "int8")
+        if self.quant and wl.dtype != "bf16":
+            raise ValueError("quantized caches take bf16 workloads")
+        self.k_scale, self.v_scale = float(k_scale), float(v_scale)
 
         # -- host: block manager replays the trace --------------------------
         bm = BlockManager(wl.num_blocks, wl.block_size, wl.free_order)
@@ -85,13 +103,20 @@ class DecodeStep:
         # -- device ------------------------------------------------------------
         dev = self.device
         shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim)
-        self.k_caches = [torch.zeros(shape, dtype=self.torch_dtype, device=dev)]
-        self.v_caches = [torch.zeros(shape, dtype=self.torch_dtype, device=dev)]
+        cdt = _CACHE_DTYPES[self.kv_dtype]
+        self.k_caches = [torch.zeros(shape, dtype=cdt, device=dev)]
+        self.v_caches = [torch.zeros(shape, dtype=cdt, device=dev)]
+        sshape = (wl.num_blocks * wl.block_size, wl.num_kv_heads)
+        if self.kv_dtype == "int8":
+            self.k_scale_pools = [torch.zeros(sshape, dtype=torch.float32, device=dev)]
+            self.v_scale_pools = [torch.zeros(sshape, dtype=torch.float32, device=dev)]
+        else:
+            self.k_scale_pools = self.v_scale_pools = None
         if wl.ctx_tokens:
             ck = to_device(wl.ctx_k, wl.dtype, dev)
             cv = to_device(wl.ctx_v, wl.dtype, dev)
             cs = torch.from_numpy(ctx_slots).to(dev)
-            ops.write(ck, cv, cs, self.k_caches[0], self.v_caches[0])
+            self._write(ck, cv, cs, 0)
             if keep_context:
                 self.ctx_k_dev, self.ctx_v_dev, self.ctx_slots_dev = ck, cv, cs
             else:
@@ -99,6 +124,9 @@ class DecodeStep:
         for _ in range(1, self.layers):
             self.k_caches.append(self.k_caches[0].clone())
             self.v_caches.append(self.v_caches[0].clone())
+            if self.k_scale_pools is not None:
+                self.k_scale_pools.append(self.k_scale_pools[0].clone())
+                self.v_scale_pools.append(self.v_scale_pools[0].clone())
         self.q = to_device(wl.q, wl.dtype, dev)
         self.new_k = to_device(wl.new_k, wl.dtype, dev)
         self.new_v = to_device(wl.new_v, wl.dtype, dev)
@@ -123,25 +151,46 @@ class DecodeStep:
     def v_cache(self):
         return self.v_caches[0]
 
+    def _scales(self, layer):
+        if self.k_scale_pools is None:
+            return None, None
+        return self.k_scale_pools[layer], self.v_scale_pools[layer]
+
+    def _write(self, k, v, slots, layer, stream=None):
+        if self.quant:
+            ks, vs = self._scales(layer)
+            ops.write_quant(k, v, slots, self.k_caches[layer], self.v_caches[layer],
+                            self.k_scale, self.v_scale, ks, vs, stream=stream)
+        else:
+            ops.write(k, v, slots, self.k_caches[layer], self.v_caches[layer], stream=stream)
+
     def copy(self, layer=0, stream=None):
         if self.cow_pairs.shape[0]:
-            ops.copy_blocks(self.cow_pairs, self.k_caches[layer], self.v_caches[layer],
-                            stream=stream)
+            if self.quant:
+                ks, vs = self._scales(layer)
+                ops.copy_blocks_quant(self.cow_pairs, self.k_caches[layer], self.v_caches[layer],
+                                      ks, vs, stream=stream)
+            else:
+                ops.copy_blocks(self.cow_pairs, self.k_caches[layer], self.v_caches[layer],
+                                stream=stream)
 
     def write(self, layer=0, stream=None):
-        ops.write(self.new_k, self.new_v, self.slot_mapping, self.k_caches[layer],
-                  self.v_caches[layer], stream=stream)
+        self._write(self.new_k, self.new_v, self.slot_mapping, layer, stream)
 
     def attention(self, layer=0, stream=None, out=None, partition_tokens=None, phases=3):
         pt = self.partition_tokens if partition_tokens is None else partition_tokens
         ws = self.workspace
         if pt != self.partition_tokens:
             ws = None  # let the binding size a workspace for this split
+        kw = dict(out=self.out if out is None else out, max_seq_len=self.max_seq_len,
+                  partition_tokens=pt, workspace=ws, stream=stream, phases=phases)
+        if self.quant:
+            ks, vs = self._scales(layer)
+            return ops.attention_decode_quant(self.q, self.k_caches[layer], self.v_caches[layer],
+                                              self.block_tables, self.seq_lens, self.wl.scale,
+                                              self.k_scale, self.v_scale, ks, vs, **kw)
         return ops.attention_decode(self.q, self.k_caches[layer], self.v_caches[layer],
-                                    self.block_tables, self.seq_lens, self.wl.scale,
-                                    out=self.out if out is None else out,
-                                    max_seq_len=self.max_seq_len, partition_tokens=pt,
-                                    workspace=ws, stream=stream, phases=phases)
+                                    self.block_tables, self.seq_lens, self.wl.scale, **kw)
 
     @property
     def split(self) -> dict:

@@ -133,3 +133,45 @@ def test_block_manager_errors():
     assert pkv.lib().pkv_bm_create(0, 4, None) is None
     bad = (ctypes.c_int32 * 3)(0, 0, 1)
     assert pkv.lib().pkv_bm_create(3, 4, bad) is None
+
+
+def test_quantized_entry_points_validate_on_the_host():
+    lib = pkv.lib()
+    x = ctypes.c_void_p(0x1000)
+    fp8 = g(H=2, D=128, dt=_lib.PKV_FP8_E4M3)
+    i8 = g(H=2, D=128, dt=_lib.PKV_INT8)
+    bf = g(H=2, D=128, dt=_lib.PKV_BF16)
+    sc = _lib.PkvKvScales(1.0, 1.0, None, None)
+    # plain calls refuse INT8 pools (scales would be lost) and quantized attention
+    assert lib.pkv_write(x, x, x, 1, x, x, ctypes.byref(i8), None) == _lib.PKV_ERR_INVALID_ARG
+    assert "pkv_write_quant" in last_error()
+    assert lib.pkv_copy_blocks(x, 1, x, x, ctypes.byref(i8), None) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_attention_decode(x, x, x, x, 7, x, 0.1, x, 2, 8, 100, 0, x, 1 << 30,
+                                    ctypes.byref(fp8), None) == _lib.PKV_ERR_INVALID_ARG
+    assert "pkv_attention_decode_quant" in last_error()
+    # the quantized calls refuse model-dtype pools, other head sizes, bad scales
+    assert lib.pkv_write_quant(x, x, x, 1, x, x, ctypes.byref(sc), ctypes.byref(bf), None) == \
+        _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_write_quant(x, x, x, 1, x, x, ctypes.byref(sc),
+                               ctypes.byref(g(H=2, D=64, dt=_lib.PKV_FP8_E4M3)), None) == \
+        _lib.PKV_ERR_UNSUPPORTED
+    bad = _lib.PkvKvScales(0.0, 1.0, None, None)
+    assert lib.pkv_write_quant(x, x, x, 1, x, x, ctypes.byref(bad), ctypes.byref(fp8), None) == \
+        _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_write_quant(x, x, x, 1, x, x, ctypes.byref(sc), ctypes.byref(i8), None) == \
+        _lib.PKV_ERR_INVALID_ARG               # INT8 needs scale pools
+    assert lib.pkv_write_quant(x, x, x, 0, x, x, ctypes.byref(sc), ctypes.byref(fp8), None) == \
+        _lib.PKV_OK
+    assert lib.pkv_copy_blocks_quant(x, 1, x, x, ctypes.byref(sc), ctypes.byref(i8), None) == \
+        _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_copy_blocks_quant(x, 0, x, x, None, ctypes.byref(fp8), None) == _lib.PKV_OK
+
+    def attn(geom, scales):
+        return lib.pkv_attention_decode_quant(3, x, x, x, scales, x, 7, x, 0.1, x, 2, 8, 100, 0,
+                                              x, 1 << 30, ctypes.byref(geom), None)
+    assert attn(bf, ctypes.byref(sc)) == _lib.PKV_ERR_INVALID_ARG
+    assert attn(fp8, None) == _lib.PKV_ERR_INVALID_ARG
+    assert attn(i8, ctypes.byref(sc)) == _lib.PKV_ERR_INVALID_ARG      # null scale pools
+    # workspace sizing takes the quantized geometry like any other
+    assert lib.pkv_attention_workspace_bytes(2, 8, 100, 0, ctypes.byref(fp8)) == \
+        lib.pkv_attention_workspace_bytes(2, 8, 100, 0, ctypes.byref(bf))
