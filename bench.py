@@ -125,6 +125,8 @@ def main() -> int:
     ap.add_argument("--config", default="qwen3-0.6b-layer")
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--partition-tokens", type=int, default=None)
+    ap.add_argument("--kv-dtype", default="model", choices=["model", "fp8_e4m3", "int8"],
+                    help="cache element type: the workload's (default) or one-byte codes")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
@@ -151,13 +153,20 @@ def main() -> int:
     t0 = time.perf_counter()
     wl = config_workload(args.config)
     gen_s = time.perf_counter() - t0
-    step = DecodeStep(wl, layers=args.layers, partition_tokens=args.partition_tokens)
+    quant = args.kv_dtype != "model"
+    step = DecodeStep(wl, layers=args.layers, partition_tokens=args.partition_tokens,
+                      kv_dtype=None if not quant else args.kv_dtype)
     L, K, W = args.layers, args.steps, args.warmup
     N = wl.num_seqs
     lens = wl.seq_lens.astype(np.int64)
-    e = wl.elem_bytes
-    kv_bytes = int(lens.sum()) * 2 * wl.num_kv_heads * wl.head_dim * e
-    q_bytes = N * wl.num_q_heads * wl.head_dim * e
+    e = 1 if quant else wl.elem_bytes          # cache element bytes
+    qe = wl.elem_bytes                         # query / output element bytes
+    # K and V of every cached position; INT8 also reads its two fp32 scales
+    per_pos = 2 * wl.num_kv_heads * wl.head_dim * e + (8 * wl.num_kv_heads
+                                                        if args.kv_dtype == "int8" else 0)
+    kv_bytes = int(lens.sum()) * per_pos
+    q_bytes = N * wl.num_q_heads * wl.head_dim * qe
+    workload_name = wl.name if not quant else f"{wl.name}+{args.kv_dtype}"
     table_bytes = 4 * int(((lens + wl.block_size - 1) // wl.block_size).sum()) + 4 * N
     part_bytes = kv_bytes + q_bytes + table_bytes          # partition kernel, algorithmic
     attn_bytes = part_bytes + q_bytes                      # + the output rows
@@ -204,10 +213,11 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
+        "dtype": args.kv_dtype if quant else wl.dtype,
         "data": "synthetic",
         "config": {
-            "workload": wl.name,
+            "workload": workload_name,
+            "kv_dtype": args.kv_dtype if quant else wl.dtype,
             "num_seqs": N,
             "num_q_heads": wl.num_q_heads,
             "num_kv_heads": wl.num_kv_heads,
@@ -247,7 +257,8 @@ def main() -> int:
             "merge_us_mean": float(np.mean(merge)) * 1e6,
             "copy_write_us_mean": float(np.mean(cw)) * 1e6,
             "device_step_us_mean": float(np.mean(dev_step)) * 1e6,
-            "write_bytes": write_bytes(N, wl.num_kv_heads, wl.head_dim, e),
+            "write_bytes": (write_bytes(N, wl.num_kv_heads, wl.head_dim, e) if not quant else
+                            N * wl.num_kv_heads * wl.head_dim * 2 * (qe + e)),
             "copy_bytes": copy_bytes(n_cow, wl.block_size, wl.num_kv_heads, wl.head_dim, e),
             "decode_tokens_per_s": N / t_step,
             "attended_tokens_per_s": float(lens.sum()) / t_attn,
@@ -257,11 +268,11 @@ def main() -> int:
                        "gcn_arch": getattr(props, "gcnArchName", "")},
         },
     }
-    res["roofline"]["traffic"] = recorded_traffic(res["roofline"]["kernel"], wl.name)
+    res["roofline"]["traffic"] = recorded_traffic(res["roofline"]["kernel"], workload_name)
     achievable = stream_read_gbps()
     res["detail"]["stream_read_gbps"] = achievable
     res["detail"]["partition_frac_of_stream_read"] = achieved / achievable
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not quant:
         cb = cpu_baseline(wl, args.cpu_budget)
         res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
         res["detail"]["cpu_baseline_extra"] = {k: cb[k] for k in ("seconds", "host_cpus",

@@ -245,8 +245,9 @@ pkv_status pkv_attention_decode_quant(int32_t phases, const void* q, const void*
  * call (unset or out of range = the library's heuristic):
  *   PKV_ATTN_HEADS_PER_WAVE  1..4  upper bound on query heads one wave carries
  *   PKV_ATTN_PREFETCH        2..4  K/V tiles of 16 positions in flight per wave
- *                                  (bf16 only, at most 4 / 3 / 2 for 1 / 2 /
- *                                  3-4 heads per wave; fp32 always uses 2)
+ *                                  (bf16: at most 4 / 3 / 2 for 1 / 2 / 3-4
+ *                                  heads per wave; one-byte codes: up to 4;
+ *                                  fp32 always uses 2)
  *   PKV_ATTN_WAVES_PER_BLOCK 1,2,4,8  fixed partitions: waves per workgroup
  *                                  (the waves of one (sequence, partition)
  *                                  are packed together)

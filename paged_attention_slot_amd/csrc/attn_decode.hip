@@ -869,8 +869,10 @@ constexpr int max_prefetch() { return GW >= 3 ? 2 : (GW == 2 ? 3 : 4); }
 // heads per wave gain a little from three.
 int prefetch_depth(int gw, int dtype, bool balanced) {
   if (dtype == PKV_F32) return 2;
-  const int cap = gw >= 3 ? 2 : (gw == 2 ? 3 : 4);
+  // one-byte codes: half-size tiles, so up to 4 fit beside any head count
+  const int cap = pkv::is_quant(dtype) ? 4 : (gw >= 3 ? 2 : (gw == 2 ? 3 : 4));
   int p = (!balanced && gw <= 2) ? 3 : 2;
+  if (pkv::is_quant(dtype) && balanced && gw >= 4) p = 4;  // measured: 3 % on 4-head waves
   if (const int k = knob_prefetch()) p = k;
   return p < cap ? p : cap;
 }
@@ -1033,9 +1035,12 @@ pkv_status launch_main(const Plan& pl, AttnArgs& a, int num_seqs, hipStream_t st
 }
 
 // Ring depths instantiated for (T, GW): 2 always; 3 and 4 for bf16 where
-// max_prefetch allows (prefetch_depth never asks for more).
+// max_prefetch allows, up to 4 for one-byte codes (prefetch_depth never asks
+// for more).
 template <typename T, int GW, int P>
-constexpr bool ring_built() { return P == 2 || (sizeof(T) <= 2 && P <= max_prefetch<GW>()); }
+constexpr bool ring_built() {
+  return P == 2 || (sizeof(T) == 1 && P <= 4) || (sizeof(T) == 2 && P <= max_prefetch<GW>());
+}
 
 template <typename T, int D, int GW>
 pkv_status launch_main_p(const Plan& pl, AttnArgs& a, int num_seqs, hipStream_t st) {
