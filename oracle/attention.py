@@ -19,6 +19,9 @@ Functions:
                              of [KVM §19.2.3] and Fig. 19-5
   attention_split            split-KV: per-partition (max, sum, weighted sum)
                              merged by log-sum-exp rescaling
+  attention_multi            several new query tokens per sequence (a prefill
+                             chunk or tokens to verify), each attending the
+                             history up to and including its own position
 """
 from __future__ import annotations
 
@@ -171,4 +174,35 @@ def attention_split(q, k_pool, v_pool, block_tables, seq_lens, scale, partition_
             states = [partition_state(qr, K[a:a + T, g], V[a:a + T, g], scale)
                       for a in range(0, L, T)]
             out[s, hs] = merge_partitions(states)
+    return out
+
+
+def attention_multi(q, q_offsets, k_pool, v_pool, block_tables, seq_lens, scale):
+    """Multi-token queries.  Sequence s owns query rows q_offsets[s] ..
+    q_offsets[s+1]-1: its n_s newest tokens, already in the cache, so history
+    length L_s counts them.  Query j of s sits at position P = L_s - n_s + j
+    and attends positions 0..P, the causal rule of [KVX §01] (a token sees the
+    history up to itself) applied to each new token; P < 0 (more queries than
+    history) attends nothing and gives zeros.  GQA mapping as for decode.
+    q [total_q, H_q, D] -> out [total_q, H_q, D] (float64)."""
+    q = to_f64(q)
+    total, Hq, D = q.shape
+    Hkv = k_pool.shape[2]
+    G = Hq // Hkv
+    out = np.zeros((total, Hq, D))
+    offs = np.asarray(q_offsets, dtype=np.int64)
+    for s in range(offs.size - 1):
+        n = int(offs[s + 1] - offs[s])
+        if n == 0:
+            continue
+        L = int(seq_lens[s])
+        K, V = gather_history(k_pool, v_pool, block_tables[s], L)
+        K, V = to_f64(K), to_f64(V)
+        for j in range(n):
+            P = L - n + j
+            if P < 0:
+                continue
+            for g in range(Hkv):
+                hs = list(_heads_of_group(Hq, Hkv, g))
+                out[offs[s] + j, hs] = attend(q[offs[s] + j, hs], K[:P + 1, g], V[:P + 1, g], scale)
     return out
