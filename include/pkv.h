@@ -241,6 +241,37 @@ pkv_status pkv_attention_decode_quant(int32_t phases, const void* q, const void*
                                       size_t workspace_bytes, const pkv_geom* geom,
                                       void* stream);
 
+/* pkv_attention_multi -- paged attention for several new query tokens per
+ * sequence: a prefill chunk, or draft tokens to verify ([KVX §01] new-token
+ * attention applied to each new token; [KVM §19.2.3] paged attention; GQA as
+ * for pkv_attention_decode).  Sequence s owns query rows q_offsets[s] ..
+ * q_offsets[s+1]-1 (n_s rows): its newest tokens, whose K/V are already in
+ * the cache, so seq_lens[s] counts them.  Query j of s is at position
+ * P = seq_lens[s] - n_s + j and attends positions 0..P (P < 0: zeros).
+ *   q, out        device bf16 [total_q][num_q_heads][head_dim].
+ *   q_offsets     device int32 [num_seqs + 1], non-decreasing, q_offsets[0] = 0
+ *                 and q_offsets[num_seqs] = total_q; max_q_per_seq bounds every
+ *                 n_s (rows beyond it are not computed).
+ *   block_tables, seq_lens, max_seq_len, max_blocks_per_seq as for decode.
+ *   partition_tokens  0 = automatic, else a multiple of 32: histories are cut
+ *                 into partitions merged by log-sum-exp.
+ *   workspace     pkv_attention_multi_workspace_bytes(...) bytes (NULL if 0).
+ * Runs on the matrix cores (bf16 operands, fp32 accumulation; the softmax
+ * weights enter the P.V product as a sum of two bf16 terms).  Supported: bf16 pools,
+ * head_dim 64 or 128, at most 64 query heads per KV head.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+size_t pkv_attention_multi_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                           int32_t total_q, int32_t max_q_per_seq,
+                                           int32_t max_seq_len, int32_t partition_tokens,
+                                           const pkv_geom* geom);
+pkv_status pkv_attention_multi(const void* q, const int32_t* q_offsets, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* seq_lens, float scale,
+                               void* out, int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
+                               int32_t max_q_per_seq, int32_t max_seq_len,
+                               int32_t partition_tokens, void* workspace,
+                               size_t workspace_bytes, const pkv_geom* geom, void* stream);
+
 /* Tuning knobs of pkv_attention_decode, read from the environment at each
  * call (unset or out of range = the library's heuristic):
  *   PKV_ATTN_HEADS_PER_WAVE  1..4  upper bound on query heads one wave carries

@@ -50,6 +50,11 @@ SIGNATURES = {
                                            c_void_p, c_float, c_void_p, c_i32, c_i32, c_i32,
                                            c_i32, c_void_p, c_size, ctypes.POINTER(PkvGeom),
                                            c_void_p]),
+    "pkv_attention_multi_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                                     ctypes.POINTER(PkvGeom)]),
+    "pkv_attention_multi": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_i32,
+                                    c_void_p, c_float, c_void_p, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                    c_i32, c_void_p, c_size, ctypes.POINTER(PkvGeom), c_void_p]),
     "pkv_attention_partition_tokens": (c_i32, [c_i32, c_i32, c_i32, ctypes.POINTER(PkvGeom)]),
     "pkv_attention_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32,
                                                ctypes.POINTER(PkvGeom)]),

@@ -1,0 +1,424 @@
+// Paged attention for several new query tokens per sequence (a prefill chunk,
+// or draft tokens to verify) on the gfx950 matrix cores: pkv_attention_multi.
+//
+// What is computed ([KVX §01] new-token attention, applied to each new token;
+// [KVM §19.2.3] paged attention; [KVX §02]/[KVX §03] grouped-query heads; page
+// keys in include/pkv.h): sequence s owns query rows q_offsets[s] ..
+// q_offsets[s+1]-1, its n_s newest tokens, already written to the cache, so
+// L_s counts them.  Query j sits at position P = L_s - n_s + j and attends
+// positions 0..P:
+//     out[row][h] = sum_{t <= P} softmax_t(scale * q[row][h] . K_s[t]) V_s[t].
+//
+// How (MI355X design):
+//  * One workgroup per (block of query tokens, partition of positions, KV
+//    head, sequence).  Its rows are (query token, query head of the group)
+//    pairs, 16 per wave, so each K/V byte read serves every head of the group
+//    and every query token of the block.
+//  * K/V arrive in tiles of 32 positions, staged in LDS by the whole
+//    workgroup (V transposed, d-major), read back as MFMA operands.
+//  * Scores as S^T = K Q^T with v_mfma_f32_16x16x32_bf16: a lane's result
+//    fragment holds 8 positions of one query row (its lane & 15), so the
+//    online softmax (log2 units) needs only the ^16 and ^32 lane exchanges,
+//    and the weights P land directly in the operand layout of O^T += V^T P^T
+//    (positions ordered 16(j/4) + 4q + j%4 in both operands).  P enters as
+//    two bf16 terms (hi + lo), so the product keeps fp32-like weights.
+//  * Positions past a row's own (the causal rule) or past the partition are
+//    masked to -inf; tiles are loaded with zeros beyond the history.
+//  * Long histories with few query blocks are split into partitions merged
+//    by log-sum-exp (attn_multi_merge_kernel).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "geom.h"
+#include "pkv_device.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kKT = 32;             // positions per K/V tile
+constexpr float kRefInit = -1e30f;  // reference of a row with no position yet
+
+struct MultiArgs {
+  const uint16_t* q;
+  const int32_t* q_offsets;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  uint16_t* out;
+  float* ws_acc;    // [row * H_q + h][part][D]
+  float2* ws_ml;    // [row * H_q + h][part] (reference, sum)
+  int32_t* ws_np;   // [row * H_q + h]: partitions holding positions <= P
+  int64_t block_elems;
+  int32_t row_elems;
+  int32_t max_blocks;
+  int32_t num_q_heads;
+  int32_t total_q;
+  int32_t group;
+  int32_t num_blocks;
+  int32_t block_shift;
+  int32_t len_cap;
+  int32_t q_per_block;
+  int32_t num_parts;
+  int32_t part_tokens;
+  float scale_log2;
+};
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& x) {
+  return __builtin_bit_cast(bf16x8_t, x);
+}
+
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW)
+attn_multi_kernel(MultiArgs a) {
+  constexpr int kKS = D / 32;            // k-steps of the score product
+  constexpr int kDT = D / 16;            // 16-wide d tiles of the output
+  constexpr int kKStride = D + 8;        // K rows in LDS, bf16 elements (16 B pad)
+  constexpr int kVStride = kKT + 4;      // V^T rows in LDS, bf16 elements (8 B pad)
+  constexpr int kChunksPerRow = D / 8;   // 16-byte chunks per K/V row
+  constexpr int kChunks = kKT * kChunksPerRow;
+  __shared__ __align__(16) uint16_t k_lds[kKT * kKStride];
+  __shared__ __align__(16) uint16_t vt_lds[D * kVStride];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(tid >> 6));
+  const int s = blockIdx.z, g = blockIdx.y;
+  const int qb = blockIdx.x / a.num_parts, part = blockIdx.x - qb * a.num_parts;
+  const int q0 = a.q_offsets[s];
+  const int n = a.q_offsets[s + 1] - q0;
+  const int j0 = qb * a.q_per_block;
+  if (q0 < 0 || j0 >= n) return;  // uniform over the workgroup
+  const int jn = min(a.q_per_block, n - j0);
+  const int Lraw = a.seq_lens[s];
+  const int L = Lraw < 0 ? 0 : (Lraw > a.len_cap ? a.len_cap : Lraw);
+  const int p_first = L - n + j0;          // position of the block's first query
+  const int p_last = p_first + jn - 1;
+  const int t_lo = part * a.part_tokens;
+  const int t_hi = min(t_lo + a.part_tokens, p_last + 1);
+  if (part > 0 && t_lo >= t_hi) return;    // no row of this block reaches this part
+
+  // This lane's row: (query token jl of the block, head hh of the group).
+  const int G = a.group;
+  const int row = 16 * w + (lane & 15);
+  const int jl = row / G, hh = row - jl * G;
+  const bool row_ok = jl < jn && q0 + j0 + jl < a.total_q;  // rows outside q: never touched
+  const int p_row = p_first + jl;
+  const int64_t qh = (int64_t(q0 + j0 + jl) * a.num_q_heads + g * G + hh);  // (row, head) index
+  const int quad = lane >> 4;
+
+  uint4 qf[kKS];
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks)
+    qf[ks] = row_ok ? *reinterpret_cast<const uint4*>(a.q + qh * D + 32 * ks + 8 * quad)
+                    : make_uint4(0, 0, 0, 0);
+
+  float m = kRefInit, lsum = 0.f;
+  f32x4_t o[kDT];
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* trow = a.block_tables + int64_t(s) * a.max_blocks;
+  const int bmask = (1 << a.block_shift) - 1;
+  for (int t0 = t_lo; t0 < t_hi; t0 += kKT) {
+    // Stage the tile: K as [pos][d], V transposed as [d][pos]; zeros past
+    // the history (never unmasked, and they keep the products finite).
+    for (int c = tid; c < kChunks; c += 64 * NW) {
+      const int pr = c / kChunksPerRow, cc = c - pr * kChunksPerRow;
+      const int pos = t0 + pr;
+      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      if (pos < L) {
+        int blk = trow[pos >> a.block_shift];
+        blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
+        const int64_t off = int64_t(blk) * a.block_elems + int64_t(pos & bmask) * a.row_elems +
+                            int64_t(g) * D + cc * 8;
+        kv = *reinterpret_cast<const uint4*>(a.k_cache + off);
+        vv = *reinterpret_cast<const uint4*>(a.v_cache + off);
+      }
+      *reinterpret_cast<uint4*>(k_lds + pr * kKStride + cc * 8) = kv;
+      const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vt_lds[(cc * 8 + 2 * i) * kVStride + pr] = static_cast<uint16_t>(vw[i] & 0xFFFFu);
+        vt_lds[(cc * 8 + 2 * i + 1) * kVStride + pr] = static_cast<uint16_t>(vw[i] >> 16);
+      }
+    }
+    __syncthreads();
+
+    // S^T tiles: positions 16pt + 4 quad + i of row (lane & 15).
+    float sc[8];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(
+            k_lds + (16 * pt + (lane & 15)) * kKStride + 32 * ks + 8 * quad);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(qf[ks]), acc, 0,
+                                                      0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 16 * pt + 4 * quad + i;
+        const bool ok = row_ok && t <= p_row && t < t_hi;
+        const float v = ok ? acc[i] * a.scale_log2 : -INFINITY;
+        sc[4 * pt + i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    }
+    tmax = pkv::max_across_rows16(tmax);
+    const float mn = fmaxf(m, tmax);
+    const float alpha = pkv::fast_exp2(m - mn);
+    m = mn;
+    // Weights as two bf16 terms, p = hi + lo (hi = bf16(p), lo = bf16(p - hi)):
+    // P V then carries p to about 2^-17 relative, like the fp32 sum.
+    uint32_t ph[4], pl[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t h2[2], l2[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float p = pkv::fast_exp2(sc[2 * k + e] - mn);
+        psum += p;
+        h2[e] = pkv::f32_to_bf16_bits(p);
+        l2[e] = pkv::f32_to_bf16_bits(p - __uint_as_float(h2[e] << 16));
+      }
+      ph[k] = h2[0] | (h2[1] << 16);
+      pl[k] = l2[0] | (l2[1] << 16);
+    }
+    psum = pkv::sum_across_rows16(psum);
+    lsum = lsum * alpha + psum;
+    const bf16x8_t pfh = as_bf16x8(make_uint4(ph[0], ph[1], ph[2], ph[3]));
+    const bf16x8_t pfl = as_bf16x8(make_uint4(pl[0], pl[1], pl[2], pl[3]));
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt) {
+      const uint16_t* vrow = vt_lds + (16 * dt + (lane & 15)) * kVStride;
+      const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 4 * quad);
+      const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * quad);
+      f32x4_t acc = o[dt];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= alpha;
+      const bf16x8_t va = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfh, acc, 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfl, acc, 0, 0, 0);
+    }
+    __syncthreads();  // the next tile overwrites LDS
+  }
+
+  if (!row_ok) return;
+  if (a.num_parts == 1) {
+    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+    uint16_t* dst = a.out + qh * D;
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt) {
+      const int d0 = 16 * dt + 4 * quad;
+      *reinterpret_cast<uint2*>(dst + d0) =
+          make_uint2(pkv::pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv),
+                     pkv::pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv));
+    }
+    return;
+  }
+  const int64_t prow = qh * a.num_parts + part;
+  float* dst = a.ws_acc + prow * D;
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt)
+    *reinterpret_cast<float4*>(dst + 16 * dt + 4 * quad) =
+        make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+  if (quad == 0) {
+    a.ws_ml[prow] = make_float2(m, lsum);
+    if (part == 0) {
+      const int np = p_row < 0 ? 0 : min(a.num_parts, p_row / a.part_tokens + 1);
+      a.ws_np[qh] = np;
+    }
+  }
+}
+
+// Log-sum-exp merge of the partitions of one (query row, head): one wave,
+// each lane owns D/64 output elements.
+template <int D>
+__global__ void __launch_bounds__(64)
+attn_multi_merge_kernel(MultiArgs a) {
+  constexpr int kE = D / 64;
+  const int64_t qh = int64_t(blockIdx.y) * a.num_q_heads + blockIdx.x;
+  const int lane = threadIdx.x;
+  const int np_raw = a.ws_np[qh];
+  const int np = np_raw < 0 ? 0 : (np_raw > a.num_parts ? a.num_parts : np_raw);
+  const int64_t base = qh * a.num_parts;
+  float M = -INFINITY;
+  for (int p = lane; p < np; p += 64) M = fmaxf(M, a.ws_ml[base + p].x);
+  M = pkv::wave_max(M);
+  float lsum = 0.f, acc[kE];
+#pragma unroll
+  for (int e = 0; e < kE; ++e) acc[e] = 0.f;
+  for (int p = 0; p < np; ++p) {
+    const float2 ml = a.ws_ml[base + p];
+    const float wgt = pkv::fast_exp2(ml.x - M);
+    lsum = fmaf(wgt, ml.y, lsum);
+    const float* src = a.ws_acc + (base + p) * D;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) acc[e] = fmaf(wgt, src[lane * kE + e], acc[e]);
+  }
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  uint16_t* dst = a.out + qh * D + lane * kE;
+#pragma unroll
+  for (int e = 0; e < kE; ++e) dst[e] = static_cast<uint16_t>(pkv::f32_to_bf16_bits(acc[e] * inv));
+}
+
+struct MultiPlan {
+  int nw, q_per_block, qblocks, part_tokens, num_parts;
+  size_t ws_bytes, ws_ml_off, ws_np_off;
+};
+
+int64_t round_up_to(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+pkv_status multi_plan(int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
+                      int32_t max_q_per_seq, int32_t max_seq_len, int32_t partition_tokens,
+                      const pkv_geom* g, const char* who, MultiPlan* pl) {
+  if (pkv_status st = pkv::check_geom(g, who)) return st;
+  if (g->dtype != PKV_BF16)
+    return pkv::fail(PKV_ERR_UNSUPPORTED, "%s: dtype %d (built: bf16)", who, g->dtype);
+  if (g->head_dim != 64 && g->head_dim != 128)
+    return pkv::fail(PKV_ERR_UNSUPPORTED, "%s: head_dim %d (built: 64, 128)", who, g->head_dim);
+  if (num_seqs < 0 || num_q_heads <= 0 || total_q < 0 || max_q_per_seq < 0 || max_seq_len < 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "%s: negative size", who);
+  if (num_q_heads % g->num_kv_heads != 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "%s: num_q_heads %d is not a multiple of num_kv_heads %d",
+                     who, num_q_heads, g->num_kv_heads);
+  const int G = num_q_heads / g->num_kv_heads;
+  if (G > 64) return pkv::fail(PKV_ERR_UNSUPPORTED, "%s: more than 64 query heads per group", who);
+  if (num_seqs > 65535 || g->num_kv_heads > 65535)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "%s: more than 65535 sequences or KV heads", who);
+  if (partition_tokens < 0 || partition_tokens % kKT != 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "%s: partition_tokens %d must be a multiple of %d",
+                     who, partition_tokens, kKT);
+  const int mq = max_q_per_seq > 0 ? max_q_per_seq : 1;
+  const int per64 = 64 / G;
+  const int rows = (mq < per64 ? mq : per64) * G;
+  pl->nw = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+  pl->q_per_block = 16 * pl->nw / G;
+  pl->qblocks = (mq + pl->q_per_block - 1) / pl->q_per_block;
+  const int len = max_seq_len > 0 ? max_seq_len : 1;
+  if (partition_tokens > 0) {
+    pl->part_tokens = partition_tokens;
+  } else {
+    // Enough workgroups to fill the GPU: split long histories when the
+    // (block, head, sequence) items alone are few; partitions stay >= 256.
+    const int64_t items = int64_t(num_seqs) * g->num_kv_heads * pl->qblocks;
+    int64_t parts = items >= 2048 ? 1 : (2048 + items - 1) / (items > 0 ? items : 1);
+    int64_t pt = round_up_to((len + parts - 1) / parts, kKT);
+    if (pt < 256) pt = 256;
+    pl->part_tokens = static_cast<int>(pt < round_up_to(len, kKT) ? pt : round_up_to(len, kKT));
+  }
+  const int64_t np = (int64_t(len) + pl->part_tokens - 1) / pl->part_tokens;
+  if (np * pl->qblocks > 2147483647LL)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "%s: too many partitions", who);
+  pl->num_parts = static_cast<int>(np);
+  if (pl->num_parts > 1) {
+    const size_t rowsq = size_t(total_q) * num_q_heads;
+    pl->ws_ml_off = rowsq * pl->num_parts * g->head_dim * sizeof(float);
+    pl->ws_np_off = pl->ws_ml_off + rowsq * pl->num_parts * sizeof(float2);
+    pl->ws_bytes = pl->ws_np_off + rowsq * sizeof(int32_t);
+  } else {
+    pl->ws_bytes = pl->ws_ml_off = pl->ws_np_off = 0;
+  }
+  return PKV_OK;
+}
+
+template <int D>
+void launch_multi(const MultiPlan& pl, const MultiArgs& a, int num_seqs, int num_kv_heads,
+                  int total_q, hipStream_t st) {
+  const dim3 grid(pl.qblocks * pl.num_parts, num_kv_heads, num_seqs);
+  switch (pl.nw) {
+    case 1: hipLaunchKernelGGL((attn_multi_kernel<D, 1>), grid, dim3(64), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((attn_multi_kernel<D, 2>), grid, dim3(128), 0, st, a); break;
+    default: hipLaunchKernelGGL((attn_multi_kernel<D, 4>), grid, dim3(256), 0, st, a); break;
+  }
+  if (pl.num_parts > 1 && total_q > 0)
+    hipLaunchKernelGGL((attn_multi_merge_kernel<D>), dim3(a.num_q_heads, total_q), dim3(64), 0,
+                       st, a);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pkv_attention_multi_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                           int32_t total_q, int32_t max_q_per_seq,
+                                           int32_t max_seq_len, int32_t partition_tokens,
+                                           const pkv_geom* geom) {
+  MultiPlan pl;
+  if (multi_plan(num_seqs, num_q_heads, total_q, max_q_per_seq, max_seq_len, partition_tokens,
+                 geom, "pkv_attention_multi_workspace_bytes", &pl) != PKV_OK)
+    return static_cast<size_t>(-1);
+  return pl.ws_bytes;
+}
+
+pkv_status pkv_attention_multi(const void* q, const int32_t* q_offsets, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* seq_lens, float scale,
+                               void* out, int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
+                               int32_t max_q_per_seq, int32_t max_seq_len,
+                               int32_t partition_tokens, void* workspace,
+                               size_t workspace_bytes, const pkv_geom* geom, void* stream) {
+  const char* who = "pkv_attention_multi";
+  MultiPlan pl;
+  if (pkv_status st = multi_plan(num_seqs, num_q_heads, total_q, max_q_per_seq, max_seq_len,
+                                 partition_tokens, geom, who, &pl))
+    return st;
+  if (!std::isfinite(scale)) return pkv::fail(PKV_ERR_INVALID_ARG, "%s: scale is not finite", who);
+  if (max_blocks_per_seq < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "%s: negative size", who);
+  if (num_seqs == 0 || total_q == 0 || max_q_per_seq == 0) return PKV_OK;
+  if (!q || !q_offsets || !k_cache || !v_cache || !block_tables || !seq_lens || !out)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "%s: null pointer", who);
+  if (!pkv::aligned16(q) || !pkv::aligned16(out) || !pkv::aligned16(k_cache) ||
+      !pkv::aligned16(v_cache) || (reinterpret_cast<uintptr_t>(block_tables) & 3u) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u) || (reinterpret_cast<uintptr_t>(q_offsets) & 3u))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "%s: misaligned pointer", who);
+  if (pl.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < pl.ws_bytes)
+      return pkv::fail(PKV_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed, %zu given", who,
+                       pl.ws_bytes, workspace ? workspace_bytes : size_t(0));
+    if (!pkv::aligned16(workspace))
+      return pkv::fail(PKV_ERR_INVALID_ARG, "%s: misaligned workspace", who);
+  }
+  MultiArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_offsets = q_offsets;
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.out = static_cast<uint16_t*>(out);
+  char* ws = static_cast<char*>(workspace);
+  a.ws_acc = pl.ws_bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  a.ws_ml = pl.ws_bytes ? reinterpret_cast<float2*>(ws + pl.ws_ml_off) : nullptr;
+  a.ws_np = pl.ws_bytes ? reinterpret_cast<int32_t*>(ws + pl.ws_np_off) : nullptr;
+  a.row_elems = geom->num_kv_heads * geom->head_dim;
+  a.block_elems = int64_t(geom->block_size) * a.row_elems;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_q_heads = num_q_heads;
+  a.total_q = total_q;
+  a.group = num_q_heads / geom->num_kv_heads;
+  a.num_blocks = geom->num_blocks;
+  a.block_shift = pkv::log2_exact(geom->block_size);
+  const int64_t cap = int64_t(max_blocks_per_seq) * geom->block_size;
+  a.len_cap = static_cast<int32_t>(max_seq_len < cap ? max_seq_len : cap);
+  a.q_per_block = pl.q_per_block;
+  a.num_parts = pl.num_parts;
+  a.part_tokens = pl.part_tokens;
+  a.scale_log2 = static_cast<float>(double(scale) * 1.4426950408889634);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (geom->head_dim == 128)
+    launch_multi<128>(pl, a, num_seqs, geom->num_kv_heads, total_q, st);
+  else
+    launch_multi<64>(pl, a, num_seqs, geom->num_kv_heads, total_q, st);
+  if (hipError_t e = hipGetLastError())
+    return pkv::fail(PKV_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return PKV_OK;
+}
+
+}  // extern "C"

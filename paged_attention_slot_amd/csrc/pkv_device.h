@@ -75,6 +75,20 @@ __device__ __forceinline__ float max_across_groups8(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// Reductions across the 4 lanes that share (lane & 15): lane ^ 16, ^ 32.
+__device__ __forceinline__ float sum_across_rows16(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float max_across_rows16(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Whole-wave reductions (every lane of the wave must be active).
 __device__ __forceinline__ float wave_sum(float x) { return sum_across_groups8(sum8(x)); }
 __device__ __forceinline__ float wave_max(float x) { return max_across_groups8(max8(x)); }

@@ -185,6 +185,50 @@ def attention_decode_quant(q, k_cache, v_cache, block_tables, seq_lens, scale, k
                       partition_tokens, workspace, stream, phases, sc)
 
 
+def attention_multi(q, q_offsets, k_cache, v_cache, block_tables, seq_lens, scale,
+                    max_q_per_seq, out=None, max_seq_len=None, partition_tokens=0,
+                    workspace=None, stream=None):
+    """Attention of several new query tokens per sequence (see include/pkv.h,
+    pkv_attention_multi).  q [total_q, H_q, D] bf16; q_offsets int32 [N+1] on
+    the device; ``max_q_per_seq`` bounds the queries of any sequence."""
+    g = geom_of(k_cache)
+    dev = k_cache.device
+    _need(k_cache, "k_cache", torch.bfloat16, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, dev)
+    _need(q, "q", torch.bfloat16, dev)
+    _need(q_offsets, "q_offsets", torch.int32, dev)
+    _need(block_tables, "block_tables", torch.int32, dev)
+    _need(seq_lens, "seq_lens", torch.int32, dev)
+    total, Hq, D = q.shape
+    N = seq_lens.shape[0]
+    if D != g.head_dim or q_offsets.shape != (N + 1,) or block_tables.shape[0] != N:
+        raise ValueError("shape mismatch between q, q_offsets, block_tables and seq_lens")
+    max_blocks = block_tables.shape[1]
+    if max_seq_len is None:
+        max_seq_len = max_blocks * g.block_size
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.bfloat16, dev)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    need = lib().pkv_attention_multi_workspace_bytes(N, Hq, total, int(max_q_per_seq),
+                                                     int(max_seq_len), int(partition_tokens),
+                                                     ctypes.byref(g))
+    if need == ctypes.c_size_t(-1).value:
+        check(1, "pkv_attention_multi_workspace_bytes")
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().pkv_attention_multi(_ptr(q), _ptr(q_offsets), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(block_tables), max_blocks, _ptr(seq_lens), float(scale),
+                                    _ptr(out), N, Hq, total, int(max_q_per_seq),
+                                    int(max_seq_len), int(partition_tokens), _ptr(workspace),
+                                    ws_bytes, ctypes.byref(g), _stream(stream)),
+          "pkv_attention_multi")
+    return out
+
+
 def write_quant(k, v, slot_mapping, k_cache, v_cache, k_scale=1.0, v_scale=1.0, k_scales=None,
                 v_scales=None, stream=None) -> None:
     """Quantize bf16 token rows k/v [T, H_kv, D] into FP8 / INT8 pools at

@@ -1,0 +1,112 @@
+"""GPU parity of pkv_attention_multi (several new query tokens per sequence)
+against the fp64 oracle attention_multi, through the C ABI.
+
+Pools, block tables and queries are drawn here (bf16 values, shuffled block
+ids, padded tables); every case prints its shapes and seed before running."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle.attention import attention_decode, attention_multi, to_f64  # noqa: E402
+from tests.parity import assert_gate  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from paged_attention_slot_amd import lib
+    lib()
+
+
+def bf16_bits(x):
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def case(seed, lens, nq, Hq, Hkv, D, B, extra_blocks=5):
+    rng = np.random.default_rng(seed)
+    N = len(lens)
+    maxb = max(1, max(-(-L // B) for L in lens))
+    need = sum(-(-L // B) for L in lens)
+    nb = need + extra_blocks
+    perm = rng.permutation(nb).astype(np.int32)
+    tables = np.full((N, maxb), -1, np.int32)
+    k = 0
+    for s, L in enumerate(lens):
+        for b in range(-(-L // B)):
+            tables[s, b] = perm[k]
+            k += 1
+    kp = bf16_bits(rng.normal(0, 1, (nb, B, Hkv, D)))
+    vp = bf16_bits(rng.normal(0, 1, (nb, B, Hkv, D)))
+    offs = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    q = bf16_bits(rng.normal(0, 1, (int(offs[-1]), Hq, D)))
+    return q, offs, kp, vp, tables, np.asarray(lens, np.int32)
+
+
+def run_case(seed, lens, nq, Hq, Hkv, D, B, pt=0, scale=None):
+    from paged_attention_slot_amd import ops
+    say(f"  case seed={seed} N={len(lens)} Hq={Hq} Hkv={Hkv} D={D} B={B} pt={pt} "
+        f"lens={lens[:6]} nq={nq[:6]}")
+    q, offs, kp, vp, tables, lens_a = case(seed, lens, nq, Hq, Hkv, D, B)
+    scale = scale or 1.0 / np.sqrt(D)
+    out = ops.attention_multi(dev_bf16(q), torch.from_numpy(offs).cuda(), dev_bf16(kp),
+                              dev_bf16(vp), torch.from_numpy(tables).cuda(),
+                              torch.from_numpy(lens_a).cuda(), scale, max(nq),
+                              max_seq_len=int(max(lens)), partition_tokens=pt)
+    torch.cuda.synchronize()
+    got = to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16))
+    ref = attention_multi(q, offs, kp, vp, tables, lens_a, scale)
+    return got, ref, (q, offs, kp, vp, tables, lens_a)
+
+
+SHAPES = [  # Hq, Hkv, D, B
+    (16, 8, 128, 16), (32, 8, 128, 16), (64, 8, 128, 32), (8, 8, 128, 8), (16, 1, 128, 16),
+    (64, 1, 128, 16), (12, 4, 64, 64), (6, 2, 64, 16), (32, 1, 64, 8),
+]
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,B", SHAPES, ids=lambda v: str(v))
+def test_chunks_of_mixed_sizes(Hq, Hkv, D, B):
+    lens = [40, 1, 77, 300, 17, 5, 130]
+    nq = [40, 1, 9, 33, 16, 8, 2]          # a whole prompt, decode, chunks, more queries than history
+    got, ref, _ = run_case(300 + Hq + D + B, lens, nq, Hq, Hkv, D, B)
+    say("  gate", assert_gate(got, ref, "bf16", "multi"))
+    assert not got[sum(nq[:5]):sum(nq[:5]) + 3].any()   # positions -3..-1 of sequence 5
+
+
+@pytest.mark.parametrize("pt", [32, 64, 256])
+@pytest.mark.parametrize("Hq,Hkv", [(16, 8), (64, 8), (32, 32)])
+def test_partitions_match_oracle(pt, Hq, Hkv):
+    lens = [700, 33, 1000, 64]
+    nq = [12, 33, 5, 1]
+    got, ref, _ = run_case(400 + pt + Hq, lens, nq, Hq, Hkv, 128, 16, pt=pt)
+    assert_gate(got, ref, "bf16", f"multi pt={pt}")
+
+
+def test_automatic_split_on_a_long_history():
+    lens = [20000, 3000]
+    nq = [4, 4]
+    got, ref, _ = run_case(501, lens, nq, 64, 8, 128, 32)
+    assert_gate(got, ref, "bf16", "long history")
+
+
+def test_empty_sequences_and_single_queries():
+    lens = [10, 50, 0, 33]
+    nq = [0, 1, 0, 1]
+    got, ref, data = run_case(502, lens, nq, 16, 4, 128, 16)
+    assert_gate(got, ref, "bf16", "sparse")
+    q, offs, kp, vp, tables, lens_a = data
+    # one query per sequence is decode attention
+    dec = attention_decode(q, kp, vp, tables[[1, 3]], lens_a[[1, 3]], 1 / np.sqrt(128))
+    assert np.allclose(ref, dec, rtol=0, atol=1e-12)

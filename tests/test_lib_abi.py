@@ -175,3 +175,23 @@ def test_quantized_entry_points_validate_on_the_host():
     # workspace sizing takes the quantized geometry like any other
     assert lib.pkv_attention_workspace_bytes(2, 8, 100, 0, ctypes.byref(fp8)) == \
         lib.pkv_attention_workspace_bytes(2, 8, 100, 0, ctypes.byref(bf))
+
+
+def test_multi_token_entry_point_validates_on_the_host():
+    lib = pkv.lib()
+    x = ctypes.c_void_p(0x1000)
+    bf = g(H=2, D=128, dt=_lib.PKV_BF16)
+
+    def call(geom, Hq=8, total=4, maxq=2, pt=0, ws=None, wsb=0):
+        return lib.pkv_attention_multi(x, x, x, x, x, 7, x, 0.1, x, 2, Hq, total, maxq, 100, pt,
+                                       ws, wsb, ctypes.byref(geom), None)
+    assert call(g(H=2, D=128, dt=_lib.PKV_F32)) == _lib.PKV_ERR_UNSUPPORTED
+    assert call(g(H=2, D=96, dt=_lib.PKV_BF16)) == _lib.PKV_ERR_UNSUPPORTED
+    assert call(bf, Hq=7) == _lib.PKV_ERR_INVALID_ARG
+    assert call(bf, pt=48) == _lib.PKV_ERR_INVALID_ARG       # not a multiple of 32
+    assert call(bf, total=0) == _lib.PKV_OK
+    # a split needs a workspace of the size the sizing call reports
+    n = lib.pkv_attention_multi_workspace_bytes(2, 8, 4, 2, 100, 32, ctypes.byref(bf))
+    assert n == 4 * 8 * 4 * (128 * 4 + 8) + 4 * 8 * 4          # rows * parts * (acc + ml) + np
+    assert call(bf, pt=32) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_attention_multi_workspace_bytes(2, 8, 4, 2, 100, 0, ctypes.byref(bf)) == 0
