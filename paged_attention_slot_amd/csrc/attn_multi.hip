@@ -71,6 +71,12 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& x) {
   return __builtin_bit_cast(bf16x8_t, x);
 }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS accesses,
+// not for its global loads, so the next tile's loads stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int D, int NW>
 __global__ void __launch_bounds__(64 * NW)
 attn_multi_kernel(MultiArgs a) {
@@ -122,30 +128,62 @@ attn_multi_kernel(MultiArgs a) {
 
   const int32_t* trow = a.block_tables + int64_t(s) * a.max_blocks;
   const int bmask = (1 << a.block_shift) - 1;
-  for (int t0 = t_lo; t0 < t_hi; t0 += kKT) {
-    // Stage the tile: K as [pos][d], V transposed as [d][pos]; zeros past
-    // the history (never unmasked, and they keep the products finite).
-    for (int c = tid; c < kChunks; c += 64 * NW) {
+  // Chunks of a tile this thread moves: c = tid + r * 64 * NW.
+  constexpr int kPer = kChunks / (64 * NW);
+  static_assert(kChunks % (64 * NW) == 0, "tile chunks must split evenly");
+  uint4 nk[kPer], nv[kPer];
+  // Issue the global loads of the tile at t0 into nk / nv (zeros past the
+  // history: never unmasked, and they keep the products finite).
+  // The tile's (at most 4, block_size >= 8) block ids are uniform: scalar
+  // loads, which do not queue behind the vector loads still in flight.
+  const int last_idx = L > 0 ? (L - 1) >> a.block_shift : -1;
+  auto fetch = [&](int t0) {
+    const int b0 = t0 >> a.block_shift;
+    int ids[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int idx = b0 + k;
+      const int b = idx <= last_idx ? trow[idx] : 0;
+      ids[k] = (b >= 0 && b < a.num_blocks) ? b : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int c = tid + r * 64 * NW;
       const int pr = c / kChunksPerRow, cc = c - pr * kChunksPerRow;
       const int pos = t0 + pr;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      nk[r] = make_uint4(0, 0, 0, 0);
+      nv[r] = make_uint4(0, 0, 0, 0);
       if (pos < L) {
-        int blk = trow[pos >> a.block_shift];
-        blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
+        const int k = (pos >> a.block_shift) - b0;
+        const int blk = k == 0 ? ids[0] : (k == 1 ? ids[1] : (k == 2 ? ids[2] : ids[3]));
         const int64_t off = int64_t(blk) * a.block_elems + int64_t(pos & bmask) * a.row_elems +
                             int64_t(g) * D + cc * 8;
-        kv = *reinterpret_cast<const uint4*>(a.k_cache + off);
-        vv = *reinterpret_cast<const uint4*>(a.v_cache + off);
+        nk[r] = *reinterpret_cast<const uint4*>(a.k_cache + off);
+        nv[r] = *reinterpret_cast<const uint4*>(a.v_cache + off);
       }
-      *reinterpret_cast<uint4*>(k_lds + pr * kKStride + cc * 8) = kv;
-      const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+    }
+  };
+  // Stage the fetched tile: K as [pos][d], V transposed as [d][pos].
+  auto stage = [&]() {
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int c = tid + r * 64 * NW;
+      const int pr = c / kChunksPerRow, cc = c - pr * kChunksPerRow;
+      *reinterpret_cast<uint4*>(k_lds + pr * kKStride + cc * 8) = nk[r];
+      const uint32_t vw[4] = {nv[r].x, nv[r].y, nv[r].z, nv[r].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         vt_lds[(cc * 8 + 2 * i) * kVStride + pr] = static_cast<uint16_t>(vw[i] & 0xFFFFu);
         vt_lds[(cc * 8 + 2 * i + 1) * kVStride + pr] = static_cast<uint16_t>(vw[i] >> 16);
       }
     }
-    __syncthreads();
+  };
+
+  if (t_lo < t_hi) fetch(t_lo);
+  for (int t0 = t_lo; t0 < t_hi; t0 += kKT) {
+    stage();
+    lds_barrier();
+    if (t0 + kKT < t_hi) fetch(t0 + kKT);  // in flight while this tile computes
 
     // S^T tiles: positions 16pt + 4 quad + i of row (lane & 15).
     float sc[8];
@@ -206,7 +244,7 @@ attn_multi_kernel(MultiArgs a) {
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfh, acc, 0, 0, 0);
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfl, acc, 0, 0, 0);
     }
-    __syncthreads();  // the next tile overwrites LDS
+    lds_barrier();  // every wave is done reading before the next stage
   }
 
   if (!row_ok) return;
@@ -283,6 +321,8 @@ pkv_status multi_plan(int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
     return pkv::fail(PKV_ERR_UNSUPPORTED, "%s: dtype %d (built: bf16)", who, g->dtype);
   if (g->head_dim != 64 && g->head_dim != 128)
     return pkv::fail(PKV_ERR_UNSUPPORTED, "%s: head_dim %d (built: 64, 128)", who, g->head_dim);
+  if (g->block_size < 8)
+    return pkv::fail(PKV_ERR_UNSUPPORTED, "%s: block_size %d < 8", who, g->block_size);
   if (num_seqs < 0 || num_q_heads <= 0 || total_q < 0 || max_q_per_seq < 0 || max_seq_len < 0)
     return pkv::fail(PKV_ERR_INVALID_ARG, "%s: negative size", who);
   if (num_q_heads % g->num_kv_heads != 0)
