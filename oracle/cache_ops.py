@@ -55,3 +55,25 @@ def copy_blocks(pairs, k_pool, v_pool) -> None:
     for a, b in pairs:
         k_pool[b] = k_pool[a]
         v_pool[b] = v_pool[a]
+
+
+def swap_blocks(pairs, src_pool, dst_pool) -> None:
+    """For each (src, dst): block ``dst`` of ``dst_pool`` (every slot, stale
+    ones included) becomes a copy of block ``src`` of ``src_pool``.  This is
+    the data movement of a swap between the device pool and the host pool
+    ([KVM §19.2.6]: the paused request's KV cache goes to CPU memory and comes
+    back; [ENG §8.2]), one pool at a time: K, V, and for INT8 caches the scale
+    pools viewed as [blocks][block_size][heads].  In place.  Rejects pools of
+    different block shape or dtype, ids out of range and a repeated dst."""
+    pairs = [(int(a), int(b)) for a, b in pairs]
+    if src_pool.shape[1:] != dst_pool.shape[1:] or src_pool.dtype != dst_pool.dtype:
+        raise ValueError("pools differ in block shape or dtype")
+    ns, nd = src_pool.shape[0], dst_pool.shape[0]
+    for a, b in pairs:
+        if not (0 <= a < ns and 0 <= b < nd):
+            raise IndexError("block id out of range")
+    dsts = [b for _, b in pairs]
+    if len(set(dsts)) != len(dsts):
+        raise ValueError("repeated dst")
+    for a, b in pairs:
+        dst_pool[b] = src_pool[a]

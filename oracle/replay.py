@@ -3,13 +3,17 @@
 Order of one decode step ([KVX §01]: the new token's K/V are appended before
 its query reads the history): copy-on-write block copies, then the slot-scatter
 write of the new tokens, then attention over every sequence's whole history.
+
+The context trace may also pause sequences by swapping them out to the host
+pool and bring them back ([KVM §19.2.6]); context appends into a block shared
+after a fork copy the block first, as the decode step does.
 """
 from __future__ import annotations
 
 import numpy as np
 
 from .block_manager import BlockManager
-from .cache_ops import copy_blocks, write
+from .cache_ops import copy_blocks, swap_blocks, write
 
 
 class OracleState:
@@ -21,8 +25,13 @@ class OracleState:
         shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim)
         self.k_pool = np.zeros(shape, dtype=dt)
         self.v_pool = np.zeros(shape, dtype=dt)
-        self.bm = BlockManager(wl.num_blocks, wl.block_size, wl.free_order)
+        hshape = (wl.num_host_blocks,) + shape[1:]
+        self.k_host = np.zeros(hshape, dtype=dt)
+        self.v_host = np.zeros(hshape, dtype=dt)
+        self.bm = BlockManager(wl.num_blocks, wl.block_size, wl.free_order,
+                               wl.num_host_blocks, wl.host_free_order)
         self.ctx_slots = []
+        self.swaps = []            # (kind, pairs) of every swap in the trace
         # Token-order histories of every sequence (for the contiguous check).
         self.keep_values = keep_values
         self.hist_k: dict[int, list] = {}
@@ -40,7 +49,7 @@ class OracleState:
             elif kind == "append":
                 s, n = op[1], op[2]
                 slots, cow = bm.append_slots([s], n)
-                assert not cow, "context appends never write into shared blocks"
+                self._copy(cow)
                 self._write(wl.ctx_k[cursor:cursor + n], wl.ctx_v[cursor:cursor + n], slots)
                 self.ctx_slots.extend(slots)
                 if self.keep_values:
@@ -59,6 +68,14 @@ class OracleState:
                 if self.keep_values:
                     self.hist_k[c] = list(self.hist_k[p])
                     self.hist_v[c] = list(self.hist_v[p])
+            elif kind == "swap_out":
+                pairs = bm.swap_out(list(op[1]))
+                self._swap(pairs, to_host=True)
+                self.swaps.append((kind, pairs))
+            elif kind == "swap_in":
+                pairs = bm.swap_in(list(op[1]))
+                self._swap(pairs, to_host=False)
+                self.swaps.append((kind, pairs))
             else:
                 raise ValueError(f"unknown op {kind}")
             bm.check()
@@ -92,6 +109,13 @@ class OracleState:
 
     def _copy(self, pairs):
         copy_blocks(pairs, self.k_pool, self.v_pool)
+
+    def _swap(self, pairs, to_host):
+        for dev, host in ((self.k_pool, self.k_host), (self.v_pool, self.v_host)):
+            if to_host:
+                swap_blocks(pairs, dev, host)
+            else:
+                swap_blocks(pairs, host, dev)
 
     def decode_device_part(self):
         """copy -> write on the oracle pools."""
@@ -141,12 +165,18 @@ class QuantOracleState(OracleState):
         dt = np.uint8 if kind == quant.FP8 else np.int8
         self.k_pool = np.zeros(self.k_pool.shape, dtype=dt)
         self.v_pool = np.zeros(self.v_pool.shape, dtype=dt)
+        self.k_host = np.zeros(self.k_host.shape, dtype=dt)
+        self.v_host = np.zeros(self.v_host.shape, dtype=dt)
         if kind == quant.INT8:
             n = wl.num_blocks * wl.block_size
             self.k_scales = np.zeros((n, wl.num_kv_heads), np.float32)
             self.v_scales = np.zeros((n, wl.num_kv_heads), np.float32)
+            hn = wl.num_host_blocks * wl.block_size
+            self.k_scales_host = np.zeros((hn, wl.num_kv_heads), np.float32)
+            self.v_scales_host = np.zeros((hn, wl.num_kv_heads), np.float32)
         else:
             self.k_scales = self.v_scales = None
+            self.k_scales_host = self.v_scales_host = None
 
     def _write(self, k, v, slots):
         from . import quant
@@ -157,6 +187,19 @@ class QuantOracleState(OracleState):
         from . import quant
         quant.copy_blocks_quant(pairs, self.k_pool, self.v_pool, self.kind, self.k_scales,
                                 self.v_scales)
+
+    def _swap(self, pairs, to_host):
+        super()._swap(pairs, to_host)
+        if self.k_scales is None:
+            return
+        B, H = self.wl.block_size, self.wl.num_kv_heads
+        for dev, host in ((self.k_scales, self.k_scales_host),
+                          (self.v_scales, self.v_scales_host)):
+            d3, h3 = dev.reshape(-1, B, H), host.reshape(-1, B, H)
+            if to_host:
+                swap_blocks(pairs, d3, h3)
+            else:
+                swap_blocks(pairs, h3, d3)
 
     def attention(self, seqs=None):
         from . import quant

@@ -211,12 +211,16 @@ class Workload:
                                          n rows of ``ctx_k``/``ctx_v``
       ("share_prefix", dst, src, ntok)   dst starts with src's first ntok tokens
       ("fork", parent, child)            child starts as a copy of parent
+      ("swap_out", (seq, ...))           the sequences are paused together and
+                                         their KV cache moves to the host pool
+      ("swap_in", (seq, ...))            swapped-out sequences come back
     The decode step then appends one token to every sequence of
     ``decode_seqs`` in that order (K/V rows ``new_k``/``new_v``), and every
     sequence's query row ``q[i]`` attends its whole history including that
     token.  ``seq_lens[i]`` is the length of ``decode_seqs[i]`` after the
     append.  ``free_order`` is the initial free list of physical block ids;
-    blocks are taken from its end.
+    blocks are taken from its end.  ``num_host_blocks`` and
+    ``host_free_order`` describe the host pool the swaps use (none if 0).
     """
     name: str
     num_q_heads: int
@@ -239,6 +243,8 @@ class Workload:
     partition_tokens: int = 0
     seed: int = 0
     meta: dict = field(default_factory=dict)
+    num_host_blocks: int = 0
+    host_free_order: np.ndarray | None = None
 
     @property
     def elem_bytes(self) -> int:
@@ -370,6 +376,67 @@ def shared_prefix_workload(*, prefix_tokens, suffix_lens, forking_parents, sampl
                     q=q, ctx_k=ck, ctx_v=cv, new_k=nk, new_v=nv,
                     scale=1.0 / math.sqrt(head_dim), partition_tokens=partition_tokens,
                     seed=seed, meta={"parents": parents, "children": child_of})
+
+
+def preemption_workload(lens_before, *, swapped, grow, num_q_heads, num_kv_heads, head_dim,
+                        block_size, dtype, seed, forks=(), host_blocks=0, partition_tokens=0,
+                        name="preempt-swap", values=True) -> Workload:
+    """Pause-and-resume trace.  Base sequences 0..n-1 write ``lens_before[s]``
+    context tokens each; then each parent in ``forks`` forks one child (ids n,
+    n+1, ... in order); the sequences of ``swapped`` are swapped out together;
+    every other sequence s appends ``grow[s]`` more tokens (``grow`` covers
+    every id, 0 for the swapped ones), taking first the blocks the swap
+    released; the swapped sequences are swapped back in together; the decode
+    step appends one token to every sequence in id order.  The device pool is
+    sized for every sequence's final length with no sharing, plus 10 %; the
+    host pool (``host_blocks``, default: the swapped sequences' blocks plus
+    10 %) and both free orders are seeded permutations."""
+    lens_before = np.asarray(lens_before, dtype=np.int64)
+    n = lens_before.size
+    forks = [int(p) for p in forks]
+    nseq = n + len(forks)
+    grow = np.asarray(grow, dtype=np.int64)
+    swapped = [int(s) for s in swapped]
+    if grow.size != nseq or np.any(grow < 0) or np.any(lens_before < 0):
+        raise ValueError("grow must give a non-negative count for every sequence")
+    if any(grow[s] for s in swapped):
+        raise ValueError("a swapped-out sequence cannot grow")
+    kids = np.random.SeedSequence(seed).spawn(9)
+    ops = []
+    for s in range(n):
+        ops.append(("add", s))
+        if lens_before[s]:
+            ops.append(("append", s, int(lens_before[s])))
+    before = list(lens_before)
+    for i, p in enumerate(forks):
+        ops.append(("fork", p, n + i))
+        before.append(before[p])
+    before = np.asarray(before, dtype=np.int64)
+    if swapped:
+        ops.append(("swap_out", tuple(swapped)))
+    for s in range(nseq):
+        if grow[s]:
+            ops.append(("append", s, int(grow[s])))
+    if swapped:
+        ops.append(("swap_in", tuple(swapped)))
+    lens = before + grow + 1
+    need = int(np.sum(_ceil_div(lens, block_size)))
+    nb = _slack_pool(need)
+    hneed = int(sum(_ceil_div(before[s], block_size) for s in swapped))
+    nh = host_blocks or _slack_pool(max(hneed, 1))
+    perm = np.random.Generator(np.random.PCG64(kids[_S_PERM])).permutation(nb).astype(np.int32)
+    hperm = np.random.Generator(np.random.PCG64(kids[8])).permutation(nh).astype(np.int32)
+    n_ctx = int(np.sum(lens_before) + np.sum(grow))
+    q, ck, cv, nk, nv = _draw_values(kids, nseq, n_ctx, num_q_heads, num_kv_heads, head_dim,
+                                     dtype, values)
+    return Workload(name=name, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                    head_dim=head_dim, block_size=block_size, dtype=dtype, num_blocks=nb,
+                    free_order=perm, ops=ops, ctx_tokens=n_ctx,
+                    decode_seqs=np.arange(nseq, dtype=np.int64), seq_lens=lens.astype(np.int32),
+                    q=q, ctx_k=ck, ctx_v=cv, new_k=nk, new_v=nv,
+                    scale=1.0 / math.sqrt(head_dim), partition_tokens=partition_tokens,
+                    seed=seed, meta={"swapped": swapped, "forks": forks},
+                    num_host_blocks=nh, host_free_order=hperm)
 
 
 def config_workload(name: str, seed: int | None = None, values: bool = True) -> Workload:
