@@ -154,6 +154,50 @@ pkv_status pkv_copy_blocks_quant(const int32_t* src_dst_pairs, int32_t num_pairs
                                  void* k_cache, void* v_cache, const pkv_kv_scales* scales,
                                  const pkv_geom* geom, void* stream);
 
+/* ---- Block swap to host memory ([KVM §19.2.6]: a paused request's KV cache
+ * moves to CPU memory and comes back when device memory frees; [KVM §19.2.2]
+ * concept table, swap in/out; [ENG §8.2]: CPU memory as a second-level block
+ * pool that attention never sees, because only block tables change) ----------
+ *
+ * The host pool mirrors the device pools' layout with its own block count:
+ * K and V [num_blocks][block_size][num_kv_heads][head_dim] of the cache dtype
+ * and, for PKV_INT8 caches, fp32 scale pools [num_blocks*block_size][H_kv].
+ * It must be pinned host memory allocated through the HIP runtime
+ * (hipHostMalloc, or a framework's pinned allocator built on it): the kernel
+ * reads and writes it directly over the host link.  Pageable memory is
+ * refused (INVALID_ARG).  The caller owns it. */
+typedef struct pkv_host_pool {
+  int32_t num_blocks;   /* host blocks (> 0; num_blocks * block_size < 2^31) */
+  void* k;              /* pinned host pools, 16-byte aligned                */
+  void* v;
+  float* k_scales;      /* PKV_INT8 only (ignored, may be NULL, otherwise)   */
+  float* v_scales;
+} pkv_host_pool;
+
+/* pkv_swap_out -- copy whole device blocks into host blocks.
+ *   pairs  int32 [num_pairs][2] = (device block, host block), device memory
+ *          or pinned host memory; pkv_bm_swap_out returns them.  For each
+ *          pair the host block (every slot, stale ones included) becomes a
+ *          bit copy of the device block: K, V and, for PKV_INT8, both scale
+ *          blocks.
+ *   scales device scale pools (PKV_INT8; may be NULL for other dtypes).
+ * Host destinations must not repeat (a repeated destination races).  Pairs
+ * with an id outside either pool are skipped.  num_pairs == 0 is a no-op.
+ * The host copy is complete, for the host and for later device work, once
+ * the stream has reached this point (e.g. after hipStreamSynchronize).
+ * Errors: INVALID_ARG (bad pointer, memory kind, alignment or size), UNSUPPORTED
+ * (PKV_INT8 with block_size * num_kv_heads not a multiple of 4), HIP. */
+pkv_status pkv_swap_out(const int32_t* pairs, int32_t num_pairs, const void* k_cache,
+                        const void* v_cache, const pkv_kv_scales* scales,
+                        const pkv_host_pool* host, const pkv_geom* geom, void* stream);
+
+/* pkv_swap_in -- the reverse: pairs = (host block, device block), as
+ * pkv_bm_swap_in returns them; each device block becomes a bit copy of the
+ * host block.  Device destinations must not repeat.  Same errors. */
+pkv_status pkv_swap_in(const int32_t* pairs, int32_t num_pairs, const pkv_host_pool* host,
+                       void* k_cache, void* v_cache, const pkv_kv_scales* scales,
+                       const pkv_geom* geom, void* stream);
+
 /* Split-KV partition length (tokens) that pkv_attention_decode uses when its
  * partition_tokens argument is 0 and it splits by fixed partitions: max_seq_len
  * rounded up to a whole tile (no split) when one partition per sequence is
@@ -355,10 +399,57 @@ int32_t pkv_bm_refcount(const pkv_bm* bm, int32_t block);
 int32_t pkv_bm_num_tokens(const pkv_bm* bm, int64_t seq);
 /* Copy the free list (bottom to top) into out[0..cap); *n_out = its length. */
 pkv_status pkv_bm_free_list(const pkv_bm* bm, int32_t* out, int32_t cap, int32_t* n_out);
-/* Invariants ([ENG §7.1], [ENG §7.2]): free list without duplicates; free and
- * referenced blocks partition the pool; every reference count equals the
- * number of table entries naming that block; every table holds
- * ceil(tokens / block_size) blocks.  INVALID_ARG (with a message) on violation. */
+/* ---- Preemption by swap ([KVM §19.2.6]; [ENG §8.2]) --------------------------
+ * A manager may hold a second pool of host blocks with its own free list
+ * (taken from and returned to its end) and reference counts.  Preempting a
+ * sequence by recomputation is pkv_bm_free_seq; preempting it by swap is
+ * pkv_bm_swap_out followed by pkv_swap_out on the returned pairs, and resuming
+ * it is pkv_bm_swap_in followed by pkv_swap_in.  A swapped-out sequence's
+ * table names host blocks; append, fork, share_prefix (either side) and
+ * export refuse it (INVALID_ARG) until it is swapped back in; free_seq
+ * releases its host blocks. */
+
+/* Give the manager its host pool of num_host_blocks blocks (once per manager).
+ * free_order: host int32 permutation of 0..num_host_blocks-1, or NULL. */
+pkv_status pkv_bm_add_host_pool(pkv_bm* bm, int32_t num_host_blocks, const int32_t* free_order);
+
+/* Pause the n distinct resident sequences seqs[0..n) together.  Every distinct
+ * device block their tables name gets one host block (a block shared between
+ * them moves once and stays shared); table entries are remapped, table by
+ * table in order, and each releases its device reference, so blocks no longer
+ * referenced return to the device free list ([KVM §19.2.6]: all of the
+ * request's blocks at once).  pairs_out (host int32 [cap][2]) receives the
+ * (device block, host block) pairs in order of first appearance and
+ * *num_pairs_out their count; pkv_bm_distinct_blocks gives the capacity
+ * needed.  All-or-nothing: NO_FREE_BLOCKS if the host pool has too few free
+ * blocks, INVALID_ARG (unknown, repeated or already swapped sequence, small
+ * capacity); the manager is unchanged on any error. */
+pkv_status pkv_bm_swap_out(pkv_bm* bm, const int64_t* seqs, int32_t n, int32_t* pairs_out,
+                           int32_t cap, int32_t* num_pairs_out);
+
+/* Resume swapped-out sequences: the reverse, with fresh device blocks from the
+ * device free list and (host block, device block) pairs.  NO_FREE_BLOCKS if
+ * the device pool has too few free blocks; all-or-nothing as above. */
+pkv_status pkv_bm_swap_in(pkv_bm* bm, const int64_t* seqs, int32_t n, int32_t* pairs_out,
+                          int32_t cap, int32_t* num_pairs_out);
+
+/* Number of distinct blocks the sequences' tables name (each on its own tier):
+ * the pair count a swap of exactly these sequences produces, and the free
+ * blocks it needs.  -1 on an unknown sequence or bad argument. */
+int32_t pkv_bm_distinct_blocks(const pkv_bm* bm, const int64_t* seqs, int32_t n);
+/* 1 if swapped out, 0 if resident, -1 if unknown. */
+int32_t pkv_bm_is_swapped(const pkv_bm* bm, int64_t seq);
+int32_t pkv_bm_num_free_host(const pkv_bm* bm);
+/* Reference count of a host block (-1 if out of range). */
+int32_t pkv_bm_host_refcount(const pkv_bm* bm, int32_t block);
+/* Copy the host free list (bottom to top) into out[0..cap); *n_out = its length. */
+pkv_status pkv_bm_host_free_list(const pkv_bm* bm, int32_t* out, int32_t cap, int32_t* n_out);
+
+/* Invariants ([ENG §7.1], [ENG §7.2]), for the device pool and the host pool
+ * alike: free list without duplicates; free and referenced blocks partition
+ * the pool; every reference count equals the number of table entries naming
+ * that block (resident tables for the device pool, swapped-out tables for the
+ * host pool); every table holds ceil(tokens / block_size) blocks.  INVALID_ARG (with a message) on violation. */
 pkv_status pkv_bm_check(const pkv_bm* bm);
 
 #ifdef __cplusplus

@@ -33,6 +33,11 @@ class PkvKvScales(ctypes.Structure):
 
 
 # name -> (restype, argtypes); mirrors include/pkv.h
+class PkvHostPool(ctypes.Structure):
+    _fields_ = [("num_blocks", c_i32), ("k", c_void_p), ("v", c_void_p), ("k_scales", c_void_p),
+                ("v_scales", c_void_p)]
+
+
 SIGNATURES = {
     "pkv_version": (c_i32, []),
     "pkv_last_error": (ctypes.c_char_p, []),
@@ -79,6 +84,18 @@ SIGNATURES = {
     "pkv_bm_num_tokens": (c_i32, [c_void_p, c_i64]),
     "pkv_bm_free_list": (c_i32, [c_void_p, P_i32, c_i32, P_i32]),
     "pkv_bm_check": (c_i32, [c_void_p]),
+    "pkv_swap_out": (c_i32, [c_void_p, c_i32, c_void_p, c_void_p, ctypes.POINTER(PkvKvScales),
+                             ctypes.POINTER(PkvHostPool), ctypes.POINTER(PkvGeom), c_void_p]),
+    "pkv_swap_in": (c_i32, [c_void_p, c_i32, ctypes.POINTER(PkvHostPool), c_void_p, c_void_p,
+                            ctypes.POINTER(PkvKvScales), ctypes.POINTER(PkvGeom), c_void_p]),
+    "pkv_bm_add_host_pool": (c_i32, [c_void_p, c_i32, P_i32]),
+    "pkv_bm_swap_out": (c_i32, [c_void_p, P_i64, c_i32, P_i32, c_i32, P_i32]),
+    "pkv_bm_swap_in": (c_i32, [c_void_p, P_i64, c_i32, P_i32, c_i32, P_i32]),
+    "pkv_bm_distinct_blocks": (c_i32, [c_void_p, P_i64, c_i32]),
+    "pkv_bm_is_swapped": (c_i32, [c_void_p, c_i64]),
+    "pkv_bm_num_free_host": (c_i32, [c_void_p]),
+    "pkv_bm_host_refcount": (c_i32, [c_void_p, c_i32]),
+    "pkv_bm_host_free_list": (c_i32, [c_void_p, P_i32, c_i32, P_i32]),
 }
 
 _lock = threading.Lock()

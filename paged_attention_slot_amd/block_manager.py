@@ -23,7 +23,8 @@ def _i64p(a: np.ndarray):
 class BlockManager:
     """Free list, reference counts and block tables, held by ``libpkv``."""
 
-    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+    def __init__(self, num_blocks: int, block_size: int, free_order=None,
+                 num_host_blocks: int = 0, host_free_order=None):
         self._lib = lib()
         self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)
@@ -36,6 +37,16 @@ class BlockManager:
         if not h:
             check(1, "pkv_bm_create")
         self._h = ctypes.c_void_p(h)
+        self.num_host_blocks = int(num_host_blocks)
+        if num_host_blocks:
+            ho = None
+            if host_free_order is not None:
+                ho = np.ascontiguousarray(host_free_order, dtype=np.int32)
+                if ho.size != num_host_blocks:
+                    raise ValueError("host_free_order must have num_host_blocks entries")
+            self._check(self._lib.pkv_bm_add_host_pool(self._h, int(num_host_blocks),
+                                                       None if ho is None else _i32p(ho)),
+                        "add_host_pool")
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -100,3 +111,46 @@ class BlockManager:
 
     def check(self) -> None:
         self._check(self._lib.pkv_bm_check(self._h), "check")
+
+    # -- swap (host tier) -------------------------------------------------------
+    def distinct_blocks(self, seqs) -> int:
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = int(self._lib.pkv_bm_distinct_blocks(self._h, _i64p(s), s.size))
+        if n < 0:
+            raise PkvError(1, "distinct_blocks", "unknown sequence")
+        return n
+
+    def _swap(self, fn, seqs, where):
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        cap = self.distinct_blocks(s) if s.size else 0
+        pairs = np.empty((max(1, cap), 2), dtype=np.int32)
+        n = ctypes.c_int32(0)
+        self._check(fn(self._h, _i64p(s), s.size, _i32p(pairs), cap, ctypes.byref(n)), where)
+        return pairs[:n.value].copy()
+
+    def swap_out(self, seqs) -> np.ndarray:
+        """Pause the sequences; returns int32 [P, 2] (device block, host block)."""
+        return self._swap(self._lib.pkv_bm_swap_out, seqs, "swap_out")
+
+    def swap_in(self, seqs) -> np.ndarray:
+        """Resume the sequences; returns int32 [P, 2] (host block, device block)."""
+        return self._swap(self._lib.pkv_bm_swap_in, seqs, "swap_in")
+
+    def is_swapped(self, seq: int) -> bool:
+        r = int(self._lib.pkv_bm_is_swapped(self._h, int(seq)))
+        if r < 0:
+            raise PkvError(1, "is_swapped", f"unknown sequence {seq}")
+        return bool(r)
+
+    def num_free_host(self) -> int:
+        return int(self._lib.pkv_bm_num_free_host(self._h))
+
+    def host_refcount(self, block: int) -> int:
+        return int(self._lib.pkv_bm_host_refcount(self._h, int(block)))
+
+    def host_free_list(self) -> np.ndarray:
+        out = np.empty(max(1, self.num_host_blocks), dtype=np.int32)
+        n = ctypes.c_int32(0)
+        self._check(self._lib.pkv_bm_host_free_list(self._h, _i32p(out), out.size,
+                                                    ctypes.byref(n)), "host_free_list")
+        return out[:n.value].copy()

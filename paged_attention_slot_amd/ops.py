@@ -10,7 +10,8 @@ import ctypes
 
 import torch
 
-from ._lib import PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_INT8, PkvGeom, PkvKvScales, check, lib
+from ._lib import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_INT8, PkvGeom, PkvHostPool, PkvKvScales,
+                   check, lib)
 
 _DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16, torch.float8_e4m3fn: PKV_FP8_E4M3,
            torch.int8: PKV_INT8}
@@ -267,6 +268,62 @@ def copy_blocks_quant(pairs, k_cache, v_cache, k_scales=None, v_scales=None,
     check(lib().pkv_copy_blocks_quant(_ptr(pairs), pairs.shape[0], _ptr(k_cache), _ptr(v_cache),
                                       ctypes.byref(sc), ctypes.byref(g), _stream(stream)),
           "pkv_copy_blocks_quant")
+
+
+class HostPool:
+    """Pinned host blocks laid out like a device pool pair (K, V and, for INT8
+    pools, the fp32 scale pools), ``num_blocks`` blocks.  Allocated with
+    torch's pinned allocator (HIP host allocation), so kernels reach it."""
+
+    def __init__(self, num_blocks: int, like: torch.Tensor):
+        _, B, H, D = like.shape
+        self.num_blocks = int(num_blocks)
+        self.k = torch.zeros((num_blocks, B, H, D), dtype=like.dtype, pin_memory=True)
+        self.v = torch.zeros(self.k.shape, dtype=like.dtype, pin_memory=True)
+        if like.dtype == torch.int8:
+            self.k_scales = torch.zeros((num_blocks * B, H), dtype=torch.float32, pin_memory=True)
+            self.v_scales = torch.zeros(self.k_scales.shape, dtype=torch.float32,
+                                        pin_memory=True)
+        else:
+            self.k_scales = self.v_scales = None
+
+    def struct(self) -> PkvHostPool:
+        return PkvHostPool(self.num_blocks, _ptr(self.k), _ptr(self.v),
+                           _ptr(self.k_scales).value or None, _ptr(self.v_scales).value or None)
+
+
+def _swap_args(pairs, k_cache, v_cache, host, k_scales, v_scales):
+    g = geom_of(k_cache)
+    dev = k_cache.device
+    _need(k_cache, "k_cache", None, dev)
+    _need(v_cache, "v_cache", k_cache.dtype, dev)
+    if pairs.dtype != torch.int32 or not pairs.is_contiguous() or (
+            pairs.dim() != 2 or pairs.shape[1] != 2):
+        raise ValueError("pairs must be a contiguous int32 [P, 2] tensor")
+    if not pairs.is_cuda and not pairs.is_pinned():
+        raise ValueError("pairs must be a device tensor or pinned host memory")
+    if host.k.dtype != k_cache.dtype or host.k.shape[1:] != k_cache.shape[1:]:
+        raise ValueError("host pool blocks differ from the device pool's")
+    sc = _scales(k_cache, 1.0, 1.0, k_scales, v_scales)
+    return g, sc, host.struct()
+
+
+def swap_out(pairs, k_cache, v_cache, host: HostPool, k_scales=None, v_scales=None,
+             stream=None) -> None:
+    """Copy device blocks to host blocks for (device, host) pairs."""
+    g, sc, hp = _swap_args(pairs, k_cache, v_cache, host, k_scales, v_scales)
+    check(lib().pkv_swap_out(_ptr(pairs), pairs.shape[0], _ptr(k_cache), _ptr(v_cache),
+                             ctypes.byref(sc), ctypes.byref(hp), ctypes.byref(g), _stream(stream)),
+          "pkv_swap_out")
+
+
+def swap_in(pairs, host: HostPool, k_cache, v_cache, k_scales=None, v_scales=None,
+            stream=None) -> None:
+    """Copy host blocks back into device blocks for (host, device) pairs."""
+    g, sc, hp = _swap_args(pairs, k_cache, v_cache, host, k_scales, v_scales)
+    check(lib().pkv_swap_in(_ptr(pairs), pairs.shape[0], ctypes.byref(hp), _ptr(k_cache),
+                            _ptr(v_cache), ctypes.byref(sc), ctypes.byref(g), _stream(stream)),
+          "pkv_swap_in")
 
 
 def stream_read(buf: torch.Tensor, sink: torch.Tensor, num_workgroups: int = 4096,

@@ -14,6 +14,11 @@ history; page keys in include/pkv.h):
 tables (one per transformer layer); ``step(layer)`` runs the step on one of
 them, so consecutive steps read different memory as a model's layers do.
 
+A trace that pauses sequences ("swap_out") and resumes them ("swap_in")
+moves their blocks to a pinned host pool and back with pkv_swap_out /
+pkv_swap_in ([KVM §19.2.6]); context writes, copy-on-write copies and swaps
+then run in trace order.
+
 ``kv_dtype`` "fp8_e4m3" or "int8" keeps the pools as one-byte codes of the
 workload's bf16 values ([KVM §19.2.4]; [PFX] "KV Cache 量化"): writes quantize
 (pkv_write_quant), copies carry INT8 scales (pkv_copy_blocks_quant) and the
@@ -67,9 +72,13 @@ class DecodeStep:
         self.k_scale, self.v_scale = float(k_scale), float(v_scale)
 
         # -- host: block manager replays the trace --------------------------
-        bm = BlockManager(wl.num_blocks, wl.block_size, wl.free_order)
+        bm = BlockManager(wl.num_blocks, wl.block_size, wl.free_order, wl.num_host_blocks,
+                          wl.host_free_order)
         ctx_slots = np.empty(wl.ctx_tokens, dtype=np.int32)
         cur = 0
+        # device work of the trace, in order: ("write", first, end) over
+        # context rows, ("copy", pairs), ("swap_out", pairs), ("swap_in", pairs)
+        events = []
         for op in wl.ops:
             kind = op[0]
             if kind == "add":
@@ -77,17 +86,27 @@ class DecodeStep:
             elif kind == "append":
                 slots, cow = bm.append_slots([op[1]], op[2])
                 if len(cow):
-                    raise RuntimeError("context append wrote into a shared block")
+                    events.append(("copy", cow))
                 ctx_slots[cur:cur + op[2]] = slots
+                if events and events[-1][0] == "write" and events[-1][2] == cur:
+                    events[-1] = ("write", events[-1][1], cur + op[2])
+                else:
+                    events.append(("write", cur, cur + op[2]))
                 cur += op[2]
             elif kind == "share_prefix":
                 bm.share_prefix(op[1], op[2], op[3])
             elif kind == "fork":
                 bm.fork(op[1], op[2])
+            elif kind == "swap_out":
+                events.append(("swap_out", bm.swap_out(list(op[1]))))
+            elif kind == "swap_in":
+                events.append(("swap_in", bm.swap_in(list(op[1]))))
             else:
                 raise ValueError(f"unknown op {kind}")
         assert cur == wl.ctx_tokens
         self.ctx_slots = ctx_slots
+        self.swap_events = [(k, p) for k, p in ((e[0], e[1]) for e in events)
+                            if k in ("swap_out", "swap_in")]
 
         # decode step, host part: one slot per sequence, CoW pairs, tables
         t0 = time.perf_counter()
@@ -112,11 +131,17 @@ class DecodeStep:
             self.v_scale_pools = [torch.zeros(sshape, dtype=torch.float32, device=dev)]
         else:
             self.k_scale_pools = self.v_scale_pools = None
+        self.host = ops.HostPool(wl.num_host_blocks, self.k_caches[0]) \
+            if wl.num_host_blocks else None
         if wl.ctx_tokens:
             ck = to_device(wl.ctx_k, wl.dtype, dev)
             cv = to_device(wl.ctx_v, wl.dtype, dev)
             cs = torch.from_numpy(ctx_slots).to(dev)
-            self._write(ck, cv, cs, 0)
+            for ev in events:
+                if ev[0] == "write":
+                    self._write(ck[ev[1]:ev[2]], cv[ev[1]:ev[2]], cs[ev[1]:ev[2]], 0)
+                else:
+                    self._trace_event(ev[0], ev[1])
             if keep_context:
                 self.ctx_k_dev, self.ctx_v_dev, self.ctx_slots_dev = ck, cv, cs
             else:
@@ -143,6 +168,19 @@ class DecodeStep:
         self.workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=dev) if n else None
         torch.cuda.synchronize(dev)
 
+    def _trace_event(self, kind, pairs, layer=0):
+        pd = torch.from_numpy(np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2))
+        pd = pd.to(self.device)
+        if kind == "copy":
+            self.copy(layer, pairs=pd)
+            return
+        ks, vs = self._scales(layer)
+        kc, vc = self.k_caches[layer], self.v_caches[layer]
+        if kind == "swap_out":
+            ops.swap_out(pd, kc, vc, self.host, ks, vs)
+        else:
+            ops.swap_in(pd, self.host, kc, vc, ks, vs)
+
     @property
     def k_cache(self):
         return self.k_caches[0]
@@ -164,14 +202,15 @@ class DecodeStep:
         else:
             ops.write(k, v, slots, self.k_caches[layer], self.v_caches[layer], stream=stream)
 
-    def copy(self, layer=0, stream=None):
-        if self.cow_pairs.shape[0]:
+    def copy(self, layer=0, stream=None, pairs=None):
+        pairs = self.cow_pairs if pairs is None else pairs
+        if pairs.shape[0]:
             if self.quant:
                 ks, vs = self._scales(layer)
-                ops.copy_blocks_quant(self.cow_pairs, self.k_caches[layer], self.v_caches[layer],
+                ops.copy_blocks_quant(pairs, self.k_caches[layer], self.v_caches[layer],
                                       ks, vs, stream=stream)
             else:
-                ops.copy_blocks(self.cow_pairs, self.k_caches[layer], self.v_caches[layer],
+                ops.copy_blocks(pairs, self.k_caches[layer], self.v_caches[layer],
                                 stream=stream)
 
     def write(self, layer=0, stream=None):

@@ -112,3 +112,65 @@ def test_config_traces_match(name):
     same_state(o, c, seqs)
     ct, cl = c.export(seqs, wl.max_blocks_per_seq)
     assert np.array_equal(cl, wl.seq_lens)
+
+
+def same_tiers(o: OracleBM, c):
+    assert c.num_free_host() == o.num_free_host()
+    assert np.array_equal(c.host_free_list(), np.asarray(o.hfree, dtype=np.int32))
+    for h in range(o.num_host_blocks):
+        assert c.host_refcount(h) == o.href[h]
+    for s in o.tables:
+        assert c.is_swapped(s) == (s in o.swapped)
+
+
+@settings(max_examples=80, deadline=None)
+@given(st.data())
+def test_random_traces_with_swaps_match(data):
+    nb, nh = data.draw(st.integers(2, 40)), data.draw(st.integers(1, 40))
+    B = data.draw(st.sampled_from([1, 2, 4, 8, 16]))
+    rng = np.random.default_rng(data.draw(st.integers(0, 10**6)))
+    perm, hperm = rng.permutation(nb), rng.permutation(nh)
+    o = OracleBM(nb, B, perm, nh, hperm)
+    c = pkv.BlockManager(nb, B, perm, nh, hperm)
+    nxt = 0
+    for _ in range(data.draw(st.integers(1, 50))):
+        res = [s for s in o.tables if s not in o.swapped]
+        swp = sorted(o.swapped)
+        op = data.draw(st.sampled_from(["add", "append", "append", "fork", "free", "out",
+                                        "out", "in", "in"]))
+        if op == "add" or not o.tables:
+            o.add_seq(nxt)
+            c.add_seq(nxt)
+            nxt += 1
+            continue
+        if op in ("append", "fork", "out") and not res or op == "in" and not swp:
+            continue
+        if op == "append":
+            seqs, k = data.draw(st.lists(st.sampled_from(res), min_size=1, max_size=4)), \
+                data.draw(st.integers(1, 7))
+            f = lambda m: m.append_slots(seqs, k)  # noqa: E731
+        elif op == "fork":
+            p, child = data.draw(st.sampled_from(res)), nxt
+            f = lambda m: m.fork(p, child)  # noqa: E731
+            nxt += 1
+        elif op == "free":
+            s = data.draw(st.sampled_from(sorted(o.tables)))
+            f = lambda m: m.free_seq(s)  # noqa: E731
+        else:
+            pool = res if op == "out" else swp
+            seqs = data.draw(st.lists(st.sampled_from(pool), min_size=1, unique=True))
+            f = (lambda m: m.swap_out(seqs)) if op == "out" else (lambda m: m.swap_in(seqs))
+        try:
+            ro, fo = f(o), False
+        except OracleNoFree:
+            fo = True
+        try:
+            rc, fc = f(c), False
+        except pkv.NoFreeBlocks:
+            fc = True
+        assert fo == fc, op
+        if not fo and op in ("out", "in"):
+            assert np.array_equal(rc, np.asarray(ro, dtype=np.int32).reshape(-1, 2))
+        res = [s for s in o.tables if s not in o.swapped]
+        same_state(o, c, res)
+        same_tiers(o, c)

@@ -195,3 +195,68 @@ def test_multi_token_entry_point_validates_on_the_host():
     assert n == 4 * 8 * 4 * (128 * 4 + 8) + 4 * 8 * 4          # rows * parts * (acc + ml) + np
     assert call(bf, pt=32) == _lib.PKV_ERR_INVALID_ARG
     assert lib.pkv_attention_multi_workspace_bytes(2, 8, 4, 2, 100, 0, ctypes.byref(bf)) == 0
+
+
+def test_swap_entry_points_validate_on_the_host():
+    from paged_attention_slot_amd._lib import PkvHostPool, PkvKvScales
+    lib = pkv.lib()
+    x = ctypes.c_void_p(0x1000)
+    hp = PkvHostPool(8, x, x, None, None)
+    for fn, args in ((lib.pkv_swap_out, lambda n, h, geo: (x, n, x, x, None, h, geo, None)),
+                     (lib.pkv_swap_in, lambda n, h, geo: (x, n, h, x, x, None, geo, None))):
+        assert fn(*args(1, ctypes.byref(hp), None)) == _lib.PKV_ERR_INVALID_ARG
+        assert "geometry" in last_error()
+        assert fn(*args(-1, ctypes.byref(hp), ctypes.byref(g()))) == _lib.PKV_ERR_INVALID_ARG
+        assert fn(*args(1, None, ctypes.byref(g()))) == _lib.PKV_ERR_INVALID_ARG
+        assert "host pool" in last_error()
+        for nh in (0, -3, 1 << 27):
+            bad = PkvHostPool(nh, x, x, None, None)
+            assert fn(*args(1, ctypes.byref(bad), ctypes.byref(g()))) == _lib.PKV_ERR_INVALID_ARG
+            assert "host num_blocks" in last_error()
+        assert fn(*args(0, ctypes.byref(hp), ctypes.byref(g()))) == _lib.PKV_OK
+        nul = PkvHostPool(8, x, None, None, None)
+        assert fn(*args(1, ctypes.byref(nul), ctypes.byref(g()))) == _lib.PKV_ERR_INVALID_ARG
+        assert "null pool" in last_error()
+        mis = PkvHostPool(8, x, ctypes.c_void_p(0x1008), None, None)
+        assert fn(*args(1, ctypes.byref(mis), ctypes.byref(g()))) == _lib.PKV_ERR_INVALID_ARG
+        assert "misaligned" in last_error()
+        # INT8: scale blocks of 4 bytes are not supported; missing scales refused
+        i8 = g(B=1, H=1, D=128, dt=_lib.PKV_INT8)
+        assert fn(*args(1, ctypes.byref(hp), ctypes.byref(i8))) == _lib.PKV_ERR_UNSUPPORTED
+        assert fn(*args(1, ctypes.byref(hp), ctypes.byref(g(dt=_lib.PKV_INT8)))) == \
+            _lib.PKV_ERR_INVALID_ARG
+    sc = PkvKvScales(1.0, 1.0, x, None)
+    hp8 = PkvHostPool(8, x, x, x, x)
+    assert lib.pkv_swap_out(x, 1, x, x, ctypes.byref(sc), ctypes.byref(hp8),
+                            ctypes.byref(g(dt=_lib.PKV_INT8)), None) == _lib.PKV_ERR_INVALID_ARG
+    assert "null pool" in last_error()
+
+
+def test_block_manager_swap_errors():
+    bm = pkv.BlockManager(8, 4, num_host_blocks=4)
+    bm.add_seq(0)
+    bm.append_slots([0], 9)                  # 3 blocks
+    bm.add_seq(1)
+    bm.append_slots([1], 9)
+    with pytest.raises(pkv.NoFreeBlocks):
+        bm.swap_out([0, 1])                  # 6 > 4 host blocks
+    assert bm.num_free_host() == 4 and not bm.is_swapped(0)
+    p = bm.swap_out([0])
+    assert p.shape == (3, 2) and bm.is_swapped(0)
+    for call in (lambda: bm.append_slots([0], 1), lambda: bm.export([0], 4),
+                 lambda: bm.fork(0, 5), lambda: bm.swap_out([0]), lambda: bm.swap_in([1]),
+                 lambda: bm.swap_out([1, 1])):
+        with pytest.raises(pkv.PkvError):
+            call()
+    lib = pkv.lib()
+    seqs = (ctypes.c_int64 * 1)(0)
+    n = ctypes.c_int32(-1)
+    # capacity too small: refused, state unchanged
+    st = lib.pkv_bm_swap_in(bm._h, seqs, 1, None, 0, ctypes.byref(n))
+    assert st == _lib.PKV_ERR_INVALID_ARG and "capacity" in last_error() and bm.is_swapped(0)
+    assert lib.pkv_bm_add_host_pool(bm._h, 4, None) == _lib.PKV_ERR_INVALID_ARG
+    with pytest.raises(pkv.PkvError):
+        bm.distinct_blocks([42])
+    bm.free_seq(0)
+    assert bm.num_free_host() == 4
+    bm.check()

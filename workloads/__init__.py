@@ -439,6 +439,35 @@ def preemption_workload(lens_before, *, swapped, grow, num_q_heads, num_kv_heads
                     num_host_blocks=nh, host_free_order=hperm)
 
 
+def preemption_config_workload(name: str, swap_fraction: float = 0.25, grow_tokens: int = 64,
+                               seed: int | None = None, values: bool = True) -> Workload:
+    """A pause-and-resume trace on a named independent-sequence configuration:
+    its sequences (at the configuration's lengths minus the decode token)
+    are built, the latest ``swap_fraction`` of them are swapped out together
+    (latecomers first, [KVM §19.2.6]), every other one grows by
+    ``grow_tokens`` tokens into the released blocks, the paused ones come back
+    and the decode step runs over all of them."""
+    c = CONFIGS[name]
+    if c.prefix_tokens or c.fixed_lens and len(c.fixed_lens) < 2:
+        raise ValueError("needs a configuration of several independent sequences")
+    seed = c.seed if seed is None else seed
+    kids = np.random.SeedSequence(seed).spawn(8)
+    if c.fixed_lens:
+        lens = np.asarray(c.fixed_lens, dtype=np.int64)
+    else:
+        g = np.random.Generator(np.random.PCG64(kids[_S_LENS]))
+        lens = g.integers(c.len_range[0], c.len_range[1] + 1, size=c.num_seqs)
+    n = lens.size
+    k = max(1, int(round(n * swap_fraction)))
+    swapped = list(range(n - k, n))
+    grow = np.where(np.arange(n) < n - k, grow_tokens, 0)
+    return preemption_workload(lens - 1, swapped=swapped, grow=grow, num_q_heads=c.num_q_heads,
+                               num_kv_heads=c.num_kv_heads, head_dim=c.head_dim,
+                               block_size=c.block_size, dtype=c.dtype, seed=seed,
+                               partition_tokens=c.partition_tokens, name=f"{c.name}-preempt",
+                               values=values)
+
+
 def config_workload(name: str, seed: int | None = None, values: bool = True) -> Workload:
     """The named configuration's workload (seed defaults to the config's).
     ``values=False`` skips drawing q/K/V (trace and sizes only)."""
