@@ -3,6 +3,8 @@
 block-table GQA decode attention through libpkv.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--layers L]
+    python bench.py --path multi [--config NAME] [--query-tokens n]
+    python bench.py --path swap [--config NAME]
 
 A step is one pass of the device hot path over one batch: pkv_copy_blocks
 (when the batch has copy-on-write pairs), pkv_write of one new token per
@@ -11,6 +13,13 @@ Inputs are resident in HBM before the timed region.  ``--layers`` pool pairs
 with identical block tables are cycled, one per step, so that consecutive steps
 read different memory (as a model's layers do) and no step is served from the
 previous step's cached lines.  Prints one JSON line.
+
+``--path multi`` times pkv_attention_multi instead: n new query tokens per
+sequence of the configuration (tokens to verify, or a prefill chunk), each
+attending the history up to its own position.  ``--path swap`` times a
+preemption round trip on the configuration's shape: the latest quarter of the
+sequences leave the HBM pools for pinned host memory (pkv_swap_out) and come
+back (pkv_swap_in); its roofline is the host link's.
 """
 from __future__ import annotations
 
@@ -25,7 +34,16 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
+# PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 encoding / 8 bits
+PCIE_PEAK_GBPS = 32.0 * 16 * 128 / 130 / 8
 METRIC = "paged decode attention KV-read GB/s (% of MI355X HBM peak); tokens/s"
+KERNEL_SOURCES = {
+    "attn_balanced_kernel": ("attn_decode.hip", "pkv_device.h"),
+    "attn_partition_kernel": ("attn_decode.hip", "pkv_device.h"),
+    "attn_multi_kernel": ("attn_multi.hip", "pkv_device.h"),
+    "swap_blocks_kernel": ("swap.hip",),
+}
 
 
 def cpu_baseline(wl, budget_s: float) -> dict:
@@ -65,13 +83,12 @@ def cpu_baseline(wl, budget_s: float) -> dict:
             "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
-def kernel_source_sha256() -> str:
-    """Hash of the attention kernel's sources (matches profile records)."""
+def kernel_source_sha256(kernel: str = "attn_balanced_kernel") -> str:
+    """Hash of a kernel's sources (matches profile records)."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("paged_attention_slot_amd/csrc/attn_decode.hip",
-              "paged_attention_slot_amd/csrc/pkv_device.h"):
-        with open(os.path.join(ROOT, f), "rb") as fh:
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "paged_attention_slot_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
@@ -81,7 +98,7 @@ def recorded_traffic(kernel: str, workload: str):
     kernel and workload, if the kernel sources are unchanged since; else None."""
     import glob
     import re
-    sha = kernel_source_sha256()
+    sha = kernel_source_sha256(kernel)
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         with open(path) as fh:
             for m in re.finditer(r"<!-- pkv-traffic (\{.*?\}) -->", fh.read()):
@@ -117,12 +134,268 @@ def stream_read_gbps(nbytes: int = 4 << 30, iters: int = 10, workgroups: int = 8
     return nbytes / t / 1e9
 
 
+def _common(args, wl, metric, value, unit, t_step, dtype, config, roofline, detail):
+    return {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": t_step * 1e3, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+            "config": config, "roofline": roofline, "cpu_baseline": None, "detail": detail}
+
+
+def _threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return int(os.environ.get("OMP_NUM_THREADS", "1"))
+
+
+def _timed(fn, K, W, marks):
+    """Run ``fn(i, rec)`` W times untimed, then K times with ``marks`` HIP
+    events per step recorded by ``rec(j)``; returns (wall seconds per step,
+    array [K, marks-1] of event intervals in seconds)."""
+    import numpy as np
+    import torch
+    for i in range(W):
+        fn(i, lambda j: None)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(marks)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        fn(i, lambda j, i=i: ev[i][j].record())
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / K
+    iv = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(marks - 1)]
+                   for i in range(K)]) * 1e-3
+    return wall, iv
+
+
+def bench_multi(args) -> int:
+    """pkv_attention_multi over the configuration's batch, n query tokens per
+    sequence at the end of each history."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    from paged_attention_slot_amd import lib, ops
+    from paged_attention_slot_amd.runtime import DecodeStep
+    from workloads import config_workload, multi_queries
+
+    n = int(args.query_tokens)
+    t0 = time.perf_counter()
+    wl = config_workload(args.config)
+    step = DecodeStep(wl, layers=args.layers)
+    for layer in range(args.layers):       # the decode token completes every history
+        step.copy(layer)
+        step.write(layer)
+    N, Hq, Hkv, D = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    lens = wl.seq_lens.astype(np.int64)
+    qh, offs = multi_queries(wl, n)            # at most L new tokens per sequence
+    nq = np.diff(offs).astype(np.int64)
+    total = int(offs[-1])
+    gen_s = time.perf_counter() - t0
+    dev = step.device
+    if wl.dtype != "bf16":
+        raise SystemExit("bench.py --path multi: the multi-token kernel takes bf16 caches")
+    q = torch.from_numpy(qh.view(np.int16)).to(dev).view(torch.bfloat16)
+    qo = torch.from_numpy(offs).to(dev)
+    out = torch.empty_like(q)
+    need = lib().pkv_attention_multi_workspace_bytes(
+        N, Hq, total, n, int(lens.max()), 0, ctypes.byref(ops.geom_of(step.k_cache)))
+    ws = torch.empty(max(int(need), 16), dtype=torch.uint8, device=dev)
+    e = wl.elem_bytes
+    # algorithmic bytes: every cached position's K and V read once, q read,
+    # out written, table entries and lengths read
+    kv_bytes = int(lens.sum()) * 2 * Hkv * D * e
+    io_bytes = 2 * total * Hq * D * e + 4 * int(((lens + wl.block_size - 1)
+                                                 // wl.block_size).sum()) + 8 * N
+    alg_bytes = kv_bytes + io_bytes
+    # flops: query j of a sequence of length L sits at position L - n + j and
+    # attends its own position and all before it (q.k and p.v: 4*D per pair)
+    pairs = int(sum(int(((L - k) + 1 + L) * k // 2) for L, k in zip(lens, nq)))
+    flops = 4.0 * D * Hq * pairs
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    L_ = args.layers
+
+    def run(i, rec):
+        rec(0)
+        ops.attention_multi(q, qo, step.k_caches[i % L_], step.v_caches[i % L_],
+                            step.block_tables, step.seq_lens, wl.scale, n, out=out,
+                            max_seq_len=step.max_seq_len, workspace=ws)
+        rec(1)
+    t_step, iv = _timed(run, args.steps, args.warmup, 2)
+    t_k = float(np.mean(iv[:, 0]))
+    mfma = flops / alg_bytes > ridge
+    achieved = (flops / t_k / 1e12) if mfma else (alg_bytes / t_k / 1e9)
+    peak = MFMA_BF16_PEAK_TFLOPS if mfma else HBM_PEAK_GBPS
+    name = f"{wl.name}+multi{n}"
+    roof = {"bound": "mfma" if mfma else "hbm", "kernel": "attn_multi_kernel",
+            "achieved": achieved, "peak": peak, "unit": "TFLOP/s" if mfma else "GB/s",
+            "frac": achieved / peak, "traffic": None,
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
+            "algorithmic_bytes_per_launch": alg_bytes, "flops_per_launch": flops,
+            "avg_launch_us": t_k * 1e6,
+            "note": "event time covers the main kernel and the partition merge"}
+    roof["traffic"] = recorded_traffic("attn_multi_kernel", name)
+    config = {"workload": name, "num_seqs": N, "query_tokens_per_seq": n, "total_queries": total,
+              "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "block_size": wl.block_size,
+              "sum_seq_lens": int(lens.sum()), "max_seq_len": int(lens.max()),
+              "layers_cycled": L_, "seed": wl.seed}
+    detail = {"kv_bytes": kv_bytes, "hbm_gbps": alg_bytes / t_k / 1e9,
+              "tflops": flops / t_k / 1e12, "queries_per_s": total / t_step,
+              "input_generation_s": gen_s, "workspace_bytes": int(need)}
+    res = _common(args, wl, "paged multi-token attention GB/s of K/V (new query tokens per "
+                  "sequence over the cached history)", alg_bytes / t_step / 1e9, "GB/s", t_step,
+                  wl.dtype, config, roof, detail)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = multi_cpu_baseline(wl, step, qh, offs, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def multi_cpu_baseline(wl, step, qh, offs, budget_s):
+    """The oracle's attention_multi, sequence by sequence over the batch until
+    the budget is spent.  Each sequence's blocks are copied to host arrays
+    first (untimed)."""
+    import numpy as np
+    import torch
+
+    from oracle.attention import attention_multi
+    from paged_attention_slot_amd.runtime import to_host_bits
+    B = wl.block_size
+    done, el = [], 0.0
+    while el <= budget_s:
+        s = len(done) % wl.num_seqs
+        L = int(wl.seq_lens[s])
+        nb = -(-L // B)
+        ids = torch.from_numpy(step.block_tables_h[s, :nb].astype(np.int64)).to(step.device)
+        kp = to_host_bits(step.k_cache.index_select(0, ids))
+        vp = to_host_bits(step.v_cache.index_select(0, ids))
+        table = np.arange(nb, dtype=np.int32)[None]
+        q = qh[offs[s]:offs[s + 1]]
+        t0 = time.perf_counter()
+        attention_multi(q, np.asarray([0, q.shape[0]], np.int32), kp, vp, table,
+                        np.asarray([L], np.int32), wl.scale)
+        el += time.perf_counter() - t0
+        done.append(s)
+    lens = wl.seq_lens[done].astype(np.int64)
+    kv = int(lens.sum()) * 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
+    return {"value": kv / el / 1e9, "unit": "GB/s", "cores": _threads(), "kind": "oracle",
+            "sample": f"{len(done)} sequences' multi-token attention ({int(lens.sum())} cached "
+                      f"positions, {kv / 1e6:.1f} MB of K/V) in {el:.2f} s of oracle time; "
+                      f"fp64 NumPy, one process"}
+
+
+def bench_swap(args) -> int:
+    """Preemption round trip on the configuration's shape: the paused
+    sequences' blocks go to pinned host memory and come back."""
+    import numpy as np
+    import torch
+
+    from paged_attention_slot_amd import ops
+    from paged_attention_slot_amd.runtime import DecodeStep
+    from workloads import preemption_config_workload
+
+    t0 = time.perf_counter()
+    wl = preemption_config_workload(args.config)
+    gen_s = time.perf_counter() - t0
+    step = DecodeStep(wl)
+    (_, p_out), (_, p_in) = step.swap_events
+    # One step moves the paused sequences from their current device blocks
+    # (where swap-in put them) to their host blocks and back again.
+    back = np.ascontiguousarray(p_in[:, ::-1])
+    dev = step.device
+    po = torch.from_numpy(back).to(dev)
+    pi = torch.from_numpy(np.ascontiguousarray(p_in)).to(dev)
+    P = int(po.shape[0])
+    bb = wl.block_size * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
+    launch_bytes = P * bb * 2                      # K and V blocks per launch
+    kc, vc, host = step.k_cache, step.v_cache, step.host
+
+    def run(i, rec):
+        rec(0)
+        ops.swap_out(po, kc, vc, host)
+        rec(1)
+        ops.swap_in(pi, host, kc, vc)
+        rec(2)
+    t_step, iv = _timed(run, args.steps, args.warmup, 3)
+    t_out, t_in = float(np.mean(iv[:, 0])), float(np.mean(iv[:, 1]))
+    # the link's practical rate: one contiguous copy-engine transfer of the
+    # same size each way
+    dbuf = torch.empty(launch_bytes, dtype=torch.uint8, device=dev)
+    hbuf = torch.empty(launch_bytes, dtype=torch.uint8, pin_memory=True)
+
+    def cal(i, rec):
+        rec(0)
+        hbuf.copy_(dbuf, non_blocking=True)
+        rec(1)
+        dbuf.copy_(hbuf, non_blocking=True)
+        rec(2)
+    _, ic = _timed(cal, 5, 1, 3)
+    d2h, h2d = launch_bytes / np.mean(ic[:, 0]) / 1e9, launch_bytes / np.mean(ic[:, 1]) / 1e9
+    achieved = launch_bytes / t_out / 1e9
+    name = f"{wl.name}"
+    roof = {"bound": "pcie", "kernel": "swap_blocks_kernel", "achieved": achieved,
+            "peak": PCIE_PEAK_GBPS, "unit": "GB/s", "frac": achieved / PCIE_PEAK_GBPS,
+            "traffic": recorded_traffic("swap_blocks_kernel", name),
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
+            "algorithmic_bytes_per_launch": launch_bytes, "avg_launch_us": t_out * 1e6,
+            "note": "swap-out launch (device to host); peak = PCIe 5.0 x16, one direction"}
+    config = {"workload": name, "num_seqs": wl.num_seqs, "paused_seqs": len(wl.meta["swapped"]),
+              "blocks_per_direction": P, "block_bytes_kv": 2 * bb,
+              "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+              "block_size": wl.block_size, "num_blocks": wl.num_blocks,
+              "host_blocks": wl.num_host_blocks, "seed": wl.seed}
+    detail = {"swap_out_us": t_out * 1e6, "swap_in_us": t_in * 1e6,
+              "swap_out_gbps": launch_bytes / t_out / 1e9,
+              "swap_in_gbps": launch_bytes / t_in / 1e9,
+              "contiguous_copy_d2h_gbps": float(d2h), "contiguous_copy_h2d_gbps": float(h2d),
+              "swap_out_frac_of_contiguous_copy": float(launch_bytes / t_out / 1e9 / d2h),
+              "swap_in_frac_of_contiguous_copy": float(launch_bytes / t_in / 1e9 / h2d),
+              "input_generation_s": gen_s}
+    res = _common(args, wl, "KV block swap GB/s over the host link (swap-out + swap-in of the "
+                  "paused sequences)", 2 * launch_bytes / t_step / 1e9, "GB/s", t_step, wl.dtype,
+                  config, roof, detail)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = swap_cpu_baseline(wl, step, back, p_in, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def swap_cpu_baseline(wl, step, p_out, p_in, budget_s):
+    """The oracle's swap_blocks over the same pair lists, out and back, on host
+    copies of the pools, until the budget is spent."""
+    import numpy as np
+
+    from oracle.cache_ops import swap_blocks
+    from paged_attention_slot_amd.runtime import to_host_bits
+    kp, vp = to_host_bits(step.k_cache), to_host_bits(step.v_cache)
+    hk = np.zeros((wl.num_host_blocks,) + kp.shape[1:], kp.dtype)
+    hv = np.zeros_like(hk)
+    rounds, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 <= budget_s:
+        swap_blocks(p_out, kp, hk)
+        swap_blocks(p_out, vp, hv)
+        swap_blocks(p_in, hk, kp)
+        swap_blocks(p_in, hv, vp)
+        rounds += 1
+    el = time.perf_counter() - t0
+    nbytes = rounds * 2 * len(p_out) * kp[0].nbytes * 2
+    return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rounds} out-and-back rounds of {len(p_out)} block pairs (K and V) "
+                      f"between host arrays in {el:.2f} s; NumPy block copies, one thread"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--path", default="decode", choices=["decode", "multi", "swap"],
+                    help="decode step (default), multi-token query attention, or block swap")
     ap.add_argument("--config", default="qwen3-0.6b-layer")
+    ap.add_argument("--query-tokens", type=int, default=4,
+                    help="--path multi: new query tokens per sequence")
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--partition-tokens", type=int, default=None)
     ap.add_argument("--kv-dtype", default="model", choices=["model", "fp8_e4m3", "int8"],
@@ -149,6 +422,10 @@ def main() -> int:
     if args.calibrate:
         print(json.dumps({"stream_read_gbps": stream_read_gbps(), "bytes": 4 << 30}), flush=True)
         return 0
+    if args.path == "multi":
+        return bench_multi(args)
+    if args.path == "swap":
+        return bench_swap(args)
     cfg = CONFIGS[args.config]
     t0 = time.perf_counter()
     wl = config_workload(args.config)

@@ -110,3 +110,46 @@ def test_empty_sequences_and_single_queries():
     # one query per sequence is decode attention
     dec = attention_decode(q, kp, vp, tables[[1, 3]], lens_a[[1, 3]], 1 / np.sqrt(128))
     assert np.allclose(ref, dec, rtol=0, atol=1e-12)
+
+
+def test_bench_configuration_sampled():
+    """The multi-token measurement's own launch (qwen3-0.6b layer, 4 tokens per
+    sequence, automatic partitions, library-sized workspace) on sampled
+    sequences: shortest, longest and four drawn ones, each against the oracle
+    over that sequence's blocks."""
+    import ctypes
+
+    from paged_attention_slot_amd import lib, ops
+    from paged_attention_slot_amd.runtime import DecodeStep, to_host_bits
+    from workloads import config_workload, multi_queries
+    wl = config_workload("qwen3-0.6b-layer")
+    say(f"  case {wl.name} + 4 query tokens: N={wl.num_seqs} seed={wl.seed}")
+    step = DecodeStep(wl)
+    step.copy()
+    step.write()
+    qh, offs = multi_queries(wl, 4)
+    total = int(offs[-1])
+    need = lib().pkv_attention_multi_workspace_bytes(
+        wl.num_seqs, wl.num_q_heads, total, 4, step.max_seq_len, 0,
+        ctypes.byref(ops.geom_of(step.k_cache)))
+    ws = torch.empty(max(int(need), 16), dtype=torch.uint8, device="cuda")
+    out = ops.attention_multi(dev_bf16(qh), torch.from_numpy(offs).cuda(), step.k_cache,
+                              step.v_cache, step.block_tables, step.seq_lens, wl.scale, 4,
+                              max_seq_len=step.max_seq_len, workspace=ws)
+    torch.cuda.synchronize()
+    got_all = to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16))
+    lens = wl.seq_lens
+    rng = np.random.default_rng(7)
+    sample = sorted({int(np.argmin(lens)), int(np.argmax(lens)),
+                     *rng.choice(wl.num_seqs, 4, replace=False).tolist()})
+    for s in sample:
+        L = int(lens[s])
+        nb = -(-L // wl.block_size)
+        ids = torch.from_numpy(step.block_tables_h[s, :nb].astype(np.int64)).cuda()
+        kp = to_host_bits(step.k_cache.index_select(0, ids))
+        vp = to_host_bits(step.v_cache.index_select(0, ids))
+        q = qh[offs[s]:offs[s + 1]]
+        ref = attention_multi(q, np.asarray([0, q.shape[0]], np.int32), kp, vp,
+                              np.arange(nb, dtype=np.int32)[None], np.asarray([L], np.int32),
+                              wl.scale)
+        assert_gate(got_all[offs[s]:offs[s + 1]], ref, "bf16", f"bench multi seq {s} L={L}")

@@ -468,6 +468,18 @@ def preemption_config_workload(name: str, swap_fraction: float = 0.25, grow_toke
                                values=values)
 
 
+def multi_queries(wl: Workload, n: int):
+    """Queries for n new tokens per sequence of ``wl`` (its n newest cached
+    tokens; fewer when a history is shorter): bf16 bit patterns
+    [total, num_q_heads, head_dim] drawn N(0, 1) from SeedSequence(seed + 1000),
+    and the int32 offsets [num_seqs + 1] of each sequence's rows."""
+    nq = np.minimum(int(n), wl.seq_lens.astype(np.int64))
+    offs = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    q = normal_array(np.random.SeedSequence(wl.seed + 1000),
+                     (int(offs[-1]), wl.num_q_heads, wl.head_dim), wl.dtype)
+    return q, offs
+
+
 def config_workload(name: str, seed: int | None = None, values: bool = True) -> Workload:
     """The named configuration's workload (seed defaults to the config's).
     ``values=False`` skips drawing q/K/V (trace and sizes only)."""
