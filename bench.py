@@ -320,8 +320,8 @@ def bench_swap(args) -> int:
         rec(2)
     t_step, iv = _timed(run, args.steps, args.warmup, 3)
     t_out, t_in = float(np.mean(iv[:, 0])), float(np.mean(iv[:, 1]))
-    # the link's practical rate: one contiguous copy-engine transfer of the
-    # same size each way
+    # the link's practical rate: the runtime's copy of one contiguous buffer
+    # of the same size each way
     dbuf = torch.empty(launch_bytes, dtype=torch.uint8, device=dev)
     hbuf = torch.empty(launch_bytes, dtype=torch.uint8, pin_memory=True)
 
@@ -340,7 +340,8 @@ def bench_swap(args) -> int:
             "traffic": recorded_traffic("swap_blocks_kernel", name),
             "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
             "algorithmic_bytes_per_launch": launch_bytes, "avg_launch_us": t_out * 1e6,
-            "note": "swap-out launch (device to host); peak = PCIe 5.0 x16, one direction"}
+            "note": "swap-out launch (device to host); peak = PCIe 5.0 x16, one direction; "
+                    "traffic counts every moved byte once read and once written"}
     config = {"workload": name, "num_seqs": wl.num_seqs, "paused_seqs": len(wl.meta["swapped"]),
               "blocks_per_direction": P, "block_bytes_kv": 2 * bb,
               "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,

@@ -4,7 +4,7 @@
 // A paused request's KV cache moves to CPU memory and back whole blocks at a
 // time ([KVM §19.2.6]; [ENG §8.2]: CPU memory as a second-level block pool,
 // unseen by attention because only the block table changes).  The block lists
-// are scattered on both sides, so instead of one copy-engine request per block
+// are scattered on both sides, so instead of one runtime copy request per block
 // a single launch moves them all: one workgroup per (pair, pool) reads the
 // source block with coalesced 16-byte loads and writes it straight into the
 // destination, the host side being reached over the host link through its
