@@ -5,6 +5,7 @@ block-table GQA decode attention through libpkv.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--layers L]
     python bench.py --path multi [--config NAME] [--query-tokens n]
     python bench.py --path swap [--config NAME]
+    python bench.py --path shared [--config NAME]
 
 A step is one pass of the device hot path over one batch: pkv_copy_blocks
 (when the batch has copy-on-write pairs), pkv_write of one new token per
@@ -19,7 +20,9 @@ sequence of the configuration (tokens to verify, or a prefill chunk), each
 attending the history up to its own position.  ``--path swap`` times a
 preemption round trip on the configuration's shape: the latest quarter of the
 sequences leave the HBM pools for pinned host memory (pkv_swap_out) and come
-back (pkv_swap_in); its roofline is the host link's.
+back (pkv_swap_in); its roofline is the host link's.  ``--path shared`` times
+pkv_attention_decode_shared on the shared-prefix configuration (by default):
+each group's prefix is read once per block of rows, not once per sequence.
 """
 from __future__ import annotations
 
@@ -286,6 +289,93 @@ def multi_cpu_baseline(wl, step, qh, offs, budget_s):
                       f"fp64 NumPy, one process"}
 
 
+def bench_shared(args) -> int:
+    """pkv_attention_decode_shared over the configuration's decode step, with
+    the plain decode kernel timed on the same pools beside it."""
+    import numpy as np
+
+    from paged_attention_slot_amd.runtime import DecodeStep
+    from workloads import config_workload
+
+    t0 = time.perf_counter()
+    wl = config_workload(args.config)
+    gen_s = time.perf_counter() - t0
+    if wl.dtype != "bf16":
+        raise SystemExit("bench.py --path shared: the shared-prefix kernels take bf16 caches")
+    step = DecodeStep(wl, layers=args.layers)
+    for layer in range(args.layers):
+        step.copy(layer)
+        step.write(layer)
+    gs, pl, mg, mp = step.shared_groups()
+    lens = wl.seq_lens.astype(np.int64)
+    per_pos = 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
+    logical = int(lens.sum()) * per_pos
+    # unique positions: distinct (block, offset) slots the batch attends
+    B = wl.block_size
+    slots = set()
+    for s in range(wl.num_seqs):
+        t = np.arange(int(lens[s]))
+        slots.update((step.block_tables_h[s, t // B].astype(np.int64) * B + t % B).tolist())
+    unique = len(slots) * per_pos
+    # algorithmic bytes of this design: each group's prefix once per block of
+    # member rows, each sequence's own positions once, q and out
+    starts, plens = gs.cpu().numpy(), pl.cpu().numpy()
+    G = wl.num_q_heads // wl.num_kv_heads
+    per64 = 64 // G
+    mpb = 16 * (1 if min(mg, per64) * G <= 16 else 2 if min(mg, per64) * G <= 32 else 4) // G
+    pre_reads = own = 0
+    for g in range(plens.size):
+        n = int(starts[g + 1] - starts[g])
+        P = int(plens[g]) if n >= 2 else 0
+        pre_reads += -(-n // mpb) * P if P else 0
+        own += int(np.sum(lens[starts[g]:starts[g + 1]] - np.minimum(P, lens[starts[g]:starts[g + 1]])))
+    qo = 2 * wl.num_seqs * wl.num_q_heads * wl.head_dim * wl.elem_bytes
+    alg = (pre_reads + own) * per_pos + qo
+    L_ = args.layers
+
+    def run(i, rec):
+        rec(0)
+        step.attention_shared(i % L_)
+        rec(1)
+    t_step, iv = _timed(run, args.steps, args.warmup, 2)
+    t_sh = float(np.mean(iv[:, 0]))
+
+    def run_plain(i, rec):
+        rec(0)
+        step.attention(i % L_)
+        rec(1)
+    _, ivp = _timed(run_plain, args.steps, args.warmup, 2)
+    t_plain = float(np.mean(ivp[:, 0]))
+    achieved = alg / t_sh / 1e9
+    roof = {"bound": "hbm", "kernel": "attn_prefix_kernel + attn_suffix_kernel + merge",
+            "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
+            "algorithmic_bytes_per_launch": alg, "avg_launch_us": t_sh * 1e6,
+            "note": "algorithmic bytes: each group's prefix once per block of member rows, "
+                    "every sequence's own positions once, q and out; event time covers the "
+                    "three kernels"}
+    config = {"workload": f"{wl.name}+shared", "num_seqs": wl.num_seqs,
+              "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+              "head_dim": wl.head_dim, "block_size": B, "groups": int(plens.size),
+              "max_group_size": int(mg), "max_prefix_len": int(mp),
+              "sum_seq_lens": int(lens.sum()), "layers_cycled": L_, "seed": wl.seed}
+    detail = {"logical_kv_bytes": logical, "unique_kv_bytes": unique,
+              "logical_gbps": logical / t_sh / 1e9, "unique_gbps": unique / t_sh / 1e9,
+              "shared_us": t_sh * 1e6, "plain_decode_us": t_plain * 1e6,
+              "speedup_vs_plain_decode": t_plain / t_sh,
+              "plain_decode_logical_gbps": logical / t_plain / 1e9,
+              "input_generation_s": gen_s}
+    res = _common(args, wl, "paged decode attention KV-read GB/s, logical (shared prefix read "
+                  "once per group)", logical / t_step / 1e9, "GB/s", t_step, wl.dtype, config,
+                  roof, detail)
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(wl, args.cpu_budget)
+        res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def bench_swap(args) -> int:
     """Preemption round trip on the configuration's shape: the paused
     sequences' blocks go to pinned host memory and come back."""
@@ -392,9 +482,12 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--path", default="decode", choices=["decode", "multi", "swap"],
-                    help="decode step (default), multi-token query attention, or block swap")
-    ap.add_argument("--config", default="qwen3-0.6b-layer")
+    ap.add_argument("--path", default="decode", choices=["decode", "multi", "swap", "shared"],
+                    help="decode step (default), multi-token query attention, block swap, or "
+                         "shared-prefix decode attention")
+    ap.add_argument("--config", default=None,
+                    help="workload (default: qwen3-0.6b-layer; shared-prefix-cow for --path "
+                         "shared)")
     ap.add_argument("--query-tokens", type=int, default=4,
                     help="--path multi: new query tokens per sequence")
     ap.add_argument("--layers", type=int, default=4)
@@ -423,8 +516,12 @@ def main() -> int:
     if args.calibrate:
         print(json.dumps({"stream_read_gbps": stream_read_gbps(), "bytes": 4 << 30}), flush=True)
         return 0
+    if args.config is None:
+        args.config = "shared-prefix-cow" if args.path == "shared" else "qwen3-0.6b-layer"
     if args.path == "multi":
         return bench_multi(args)
+    if args.path == "shared":
+        return bench_shared(args)
     if args.path == "swap":
         return bench_swap(args)
     cfg = CONFIGS[args.config]

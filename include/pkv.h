@@ -154,6 +154,59 @@ pkv_status pkv_copy_blocks_quant(const int32_t* src_dst_pairs, int32_t num_pairs
                                  void* k_cache, void* v_cache, const pkv_kv_scales* scales,
                                  const pkv_geom* geom, void* stream);
 
+/* ---- Shared-prefix decode attention ([KVM §19.2.5]: requests that reuse a
+ * prefix point their tables at the same physical blocks; [KVX §04], [KVX §05]:
+ * paging dedupes the storage, whether the reads are shared depends on the
+ * kernel) --------------------------------------------------------------------
+ *
+ * pkv_attention_decode_shared computes exactly what pkv_attention_decode
+ * computes (bf16 pools) but reads each group's shared prefix once per block of
+ * up to 64 (member, query head) rows instead of once per sequence: prefix
+ * positions of all members on the matrix cores, then every sequence's own
+ * positions, then a log-sum-exp merge of the fp32 partial states.
+ *   group_starts  device int32 [num_groups + 1]: group g is sequences
+ *                 group_starts[g] .. group_starts[g+1]-1 (non-decreasing,
+ *                 from 0 to num_seqs);
+ *   prefix_lens   device int32 [num_groups]: tokens of the shared prefix
+ *                 (rounded down to whole blocks; a group of one shares
+ *                 nothing); the members' tables must hold the same blocks for
+ *                 those tokens -- pkv_prefix_groups produces such groups.  A
+ *                 member shorter than the prefix attends only its own tokens.
+ *   max_group_size, max_prefix_len  host bounds that size the grid (a group
+ *                 larger than max_group_size shares nothing).
+ * Other arguments as pkv_attention_decode (q, out [num_seqs][H_q][D] bf16).
+ * The workspace is required (pkv_attention_shared_workspace_bytes).  Groups
+ * that break the contract give unspecified values, never out-of-pool reads.
+ * Errors: INVALID_ARG, UNSUPPORTED (not bf16; head_dim other than 64/128;
+ * block_size < 8; more than 64 query heads per KV head), HIP. */
+size_t pkv_attention_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                            int32_t num_groups, int32_t max_group_size,
+                                            int32_t max_prefix_len, int32_t max_seq_len,
+                                            const pkv_geom* geom);
+pkv_status pkv_attention_decode_shared(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* seq_lens, const int32_t* group_starts,
+                                       const int32_t* prefix_lens, int32_t num_groups,
+                                       int32_t max_group_size, int32_t max_prefix_len,
+                                       float scale, void* out, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t max_seq_len,
+                                       void* workspace, size_t workspace_bytes,
+                                       const pkv_geom* geom, void* stream);
+
+/* pkv_prefix_groups -- groups of a batch, from its host block tables [num_seqs]
+ * [max_blocks] and lengths: maximal runs of consecutive sequences whose first
+ * valid entry is the same block; a group's prefix is the longest run of leading
+ * entries that every member holds as valid entries (entry i valid when i <
+ * ceil(L / block_size)) and that agree, in tokens; a group of one shares
+ * nothing.  Outputs (host): group_starts_out [num_seqs + 1], prefix_lens_out
+ * [num_seqs] (the first *num_groups_out entries are used), the largest group
+ * and prefix.  Errors: INVALID_ARG. */
+pkv_status pkv_prefix_groups(const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks,
+                             const int32_t* seq_lens, int32_t block_size,
+                             int32_t* group_starts_out, int32_t* prefix_lens_out,
+                             int32_t* num_groups_out, int32_t* max_group_size_out,
+                             int32_t* max_prefix_len_out);
+
 /* ---- Block swap to host memory ([KVM §19.2.6]: a paused request's KV cache
  * moves to CPU memory and comes back when device memory frees; [KVM §19.2.2]
  * concept table, swap in/out; [ENG §8.2]: CPU memory as a second-level block

@@ -9,37 +9,25 @@
 // positions 0..P:
 //     out[row][h] = sum_{t <= P} softmax_t(scale * q[row][h] . K_s[t]) V_s[t].
 //
-// How (MI355X design):
-//  * One workgroup per (block of query tokens, partition of positions, KV
-//    head, sequence).  Its rows are (query token, query head of the group)
-//    pairs, 16 per wave, so each K/V byte read serves every head of the group
-//    and every query token of the block.
-//  * K/V arrive in tiles of 32 positions, staged in LDS by the whole
-//    workgroup (V transposed, d-major), read back as MFMA operands.
-//  * Scores as S^T = K Q^T with v_mfma_f32_16x16x32_bf16: a lane's result
-//    fragment holds 8 positions of one query row (its lane & 15), so the
-//    online softmax (log2 units) needs only the ^16 and ^32 lane exchanges,
-//    and the weights P land directly in the operand layout of O^T += V^T P^T
-//    (positions ordered 16(j/4) + 4q + j%4 in both operands).  P enters as
-//    two bf16 terms (hi + lo), so the product keeps fp32-like weights.
-//  * Positions past a row's own (the causal rule) or past the partition are
-//    masked to -inf; tiles are loaded with zeros beyond the history.
-//  * Long histories with few query blocks are split into partitions merged
-//    by log-sum-exp (attn_multi_merge_kernel).
+// How (MI355X design): one workgroup per (block of query tokens, partition
+// of positions, KV head, sequence).  Its rows are (query token, query head of
+// the group) pairs, 16 per wave, so each K/V byte read serves every head of
+// the group and every query token of the block; the pass itself (LDS-staged
+// tiles, scores and P V on the matrix cores, online softmax) is
+// pkv::mfma::attend.  Positions past a row's own (the causal rule) are
+// masked.  Long histories with few query blocks are split into partitions
+// merged by log-sum-exp (attn_multi_merge_kernel).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 
 #include "geom.h"
+#include "mfma_attend.h"
 #include "pkv_device.h"
 
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-constexpr int kKT = 32;             // positions per K/V tile
-constexpr float kRefInit = -1e30f;  // reference of a row with no position yet
+using pkv::mfma::kKT;
 
 struct MultiArgs {
   const uint16_t* q;
@@ -67,27 +55,11 @@ struct MultiArgs {
   float scale_log2;
 };
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& x) {
-  return __builtin_bit_cast(bf16x8_t, x);
-}
-
-// Workgroup barrier that orders LDS only: waits for this wave's LDS accesses,
-// not for its global loads, so the next tile's loads stay in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 template <int D, int NW>
 __global__ void __launch_bounds__(64 * NW)
 attn_multi_kernel(MultiArgs a) {
-  constexpr int kKS = D / 32;            // k-steps of the score product
-  constexpr int kDT = D / 16;            // 16-wide d tiles of the output
-  constexpr int kKStride = D + 8;        // K rows in LDS, bf16 elements (16 B pad)
-  constexpr int kVStride = kKT + 4;      // V^T rows in LDS, bf16 elements (8 B pad)
-  constexpr int kChunksPerRow = D / 8;   // 16-byte chunks per K/V row
-  constexpr int kChunks = kKT * kChunksPerRow;
-  __shared__ __align__(16) uint16_t k_lds[kKT * kKStride];
-  __shared__ __align__(16) uint16_t vt_lds[D * kVStride];
+  __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D>()];
+  __shared__ __align__(16) uint16_t vt_lds[pkv::mfma::vt_lds_elems<D>()];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(tid >> 6));
@@ -113,165 +85,23 @@ attn_multi_kernel(MultiArgs a) {
   const bool row_ok = jl < jn && q0 + j0 + jl < a.total_q;  // rows outside q: never touched
   const int p_row = p_first + jl;
   const int64_t qh = (int64_t(q0 + j0 + jl) * a.num_q_heads + g * G + hh);  // (row, head) index
-  const int quad = lane >> 4;
 
-  uint4 qf[kKS];
-#pragma unroll
-  for (int ks = 0; ks < kKS; ++ks)
-    qf[ks] = row_ok ? *reinterpret_cast<const uint4*>(a.q + qh * D + 32 * ks + 8 * quad)
-                    : make_uint4(0, 0, 0, 0);
-
-  float m = kRefInit, lsum = 0.f;
-  f32x4_t o[kDT];
-#pragma unroll
-  for (int dt = 0; dt < kDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int32_t* trow = a.block_tables + int64_t(s) * a.max_blocks;
-  const int bmask = (1 << a.block_shift) - 1;
-  // Chunks of a tile this thread moves: c = tid + r * 64 * NW.
-  constexpr int kPer = kChunks / (64 * NW);
-  static_assert(kChunks % (64 * NW) == 0, "tile chunks must split evenly");
-  uint4 nk[kPer], nv[kPer];
-  // Issue the global loads of the tile at t0 into nk / nv (zeros past the
-  // history: never unmasked, and they keep the products finite).
-  // The tile's (at most 4, block_size >= 8) block ids are uniform: scalar
-  // loads, which do not queue behind the vector loads still in flight.
-  const int last_idx = L > 0 ? (L - 1) >> a.block_shift : -1;
-  auto fetch = [&](int t0) {
-    const int b0 = t0 >> a.block_shift;
-    int ids[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int idx = b0 + k;
-      const int b = idx <= last_idx ? trow[idx] : 0;
-      ids[k] = (b >= 0 && b < a.num_blocks) ? b : 0;
-    }
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-      const int c = tid + r * 64 * NW;
-      const int pr = c / kChunksPerRow, cc = c - pr * kChunksPerRow;
-      const int pos = t0 + pr;
-      nk[r] = make_uint4(0, 0, 0, 0);
-      nv[r] = make_uint4(0, 0, 0, 0);
-      if (pos < L) {
-        const int k = (pos >> a.block_shift) - b0;
-        const int blk = k == 0 ? ids[0] : (k == 1 ? ids[1] : (k == 2 ? ids[2] : ids[3]));
-        const int64_t off = int64_t(blk) * a.block_elems + int64_t(pos & bmask) * a.row_elems +
-                            int64_t(g) * D + cc * 8;
-        nk[r] = *reinterpret_cast<const uint4*>(a.k_cache + off);
-        nv[r] = *reinterpret_cast<const uint4*>(a.v_cache + off);
-      }
-    }
-  };
-  // Stage the fetched tile: K as [pos][d], V transposed as [d][pos].
-  auto stage = [&]() {
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-      const int c = tid + r * 64 * NW;
-      const int pr = c / kChunksPerRow, cc = c - pr * kChunksPerRow;
-      *reinterpret_cast<uint4*>(k_lds + pr * kKStride + cc * 8) = nk[r];
-      const uint32_t vw[4] = {nv[r].x, nv[r].y, nv[r].z, nv[r].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        vt_lds[(cc * 8 + 2 * i) * kVStride + pr] = static_cast<uint16_t>(vw[i] & 0xFFFFu);
-        vt_lds[(cc * 8 + 2 * i + 1) * kVStride + pr] = static_cast<uint16_t>(vw[i] >> 16);
-      }
-    }
-  };
-
-  if (t_lo < t_hi) fetch(t_lo);
-  for (int t0 = t_lo; t0 < t_hi; t0 += kKT) {
-    stage();
-    lds_barrier();
-    if (t0 + kKT < t_hi) fetch(t0 + kKT);  // in flight while this tile computes
-
-    // S^T tiles: positions 16pt + 4 quad + i of row (lane & 15).
-    float sc[8];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int pt = 0; pt < 2; ++pt) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(
-            k_lds + (16 * pt + (lane & 15)) * kKStride + 32 * ks + 8 * quad);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(qf[ks]), acc, 0,
-                                                      0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 16 * pt + 4 * quad + i;
-        const bool ok = row_ok && t <= p_row && t < t_hi;
-        const float v = ok ? acc[i] * a.scale_log2 : -INFINITY;
-        sc[4 * pt + i] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    }
-    tmax = pkv::max_across_rows16(tmax);
-    const float mn = fmaxf(m, tmax);
-    const float alpha = pkv::fast_exp2(m - mn);
-    m = mn;
-    // Weights as two bf16 terms, p = hi + lo (hi = bf16(p), lo = bf16(p - hi)):
-    // P V then carries p to about 2^-17 relative, like the fp32 sum.
-    uint32_t ph[4], pl[4];
-    float psum = 0.f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t h2[2], l2[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float p = pkv::fast_exp2(sc[2 * k + e] - mn);
-        psum += p;
-        h2[e] = pkv::f32_to_bf16_bits(p);
-        l2[e] = pkv::f32_to_bf16_bits(p - __uint_as_float(h2[e] << 16));
-      }
-      ph[k] = h2[0] | (h2[1] << 16);
-      pl[k] = l2[0] | (l2[1] << 16);
-    }
-    psum = pkv::sum_across_rows16(psum);
-    lsum = lsum * alpha + psum;
-    const bf16x8_t pfh = as_bf16x8(make_uint4(ph[0], ph[1], ph[2], ph[3]));
-    const bf16x8_t pfl = as_bf16x8(make_uint4(pl[0], pl[1], pl[2], pl[3]));
-#pragma unroll
-    for (int dt = 0; dt < kDT; ++dt) {
-      const uint16_t* vrow = vt_lds + (16 * dt + (lane & 15)) * kVStride;
-      const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 4 * quad);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * quad);
-      f32x4_t acc = o[dt];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] *= alpha;
-      const bf16x8_t va = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfh, acc, 0, 0, 0);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfl, acc, 0, 0, 0);
-    }
-    lds_barrier();  // every wave is done reading before the next stage
-  }
+  const pkv::mfma::History hist{a.k_cache, a.v_cache, a.block_tables + int64_t(s) * a.max_blocks,
+                                L, g, a.block_elems, a.row_elems, a.num_blocks, a.block_shift};
+  pkv::mfma::RowAcc<D> r;
+  pkv::mfma::attend<D, NW>(hist, t_lo, t_hi, a.q + qh * D, row_ok, p_row, a.scale_log2, k_lds,
+                           vt_lds, r);
 
   if (!row_ok) return;
   if (a.num_parts == 1) {
-    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-    uint16_t* dst = a.out + qh * D;
-#pragma unroll
-    for (int dt = 0; dt < kDT; ++dt) {
-      const int d0 = 16 * dt + 4 * quad;
-      *reinterpret_cast<uint2*>(dst + d0) =
-          make_uint2(pkv::pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv),
-                     pkv::pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv));
-    }
+    pkv::mfma::store_row_bf16<D>(r, a.out + qh * D);
     return;
   }
   const int64_t prow = qh * a.num_parts + part;
-  float* dst = a.ws_acc + prow * D;
-#pragma unroll
-  for (int dt = 0; dt < kDT; ++dt)
-    *reinterpret_cast<float4*>(dst + 16 * dt + 4 * quad) =
-        make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-  if (quad == 0) {
-    a.ws_ml[prow] = make_float2(m, lsum);
-    if (part == 0) {
-      const int np = p_row < 0 ? 0 : min(a.num_parts, p_row / a.part_tokens + 1);
-      a.ws_np[qh] = np;
-    }
+  pkv::mfma::store_piece<D>(r, a.ws_acc + prow * D, a.ws_ml + prow);
+  if ((lane >> 4) == 0 && part == 0) {
+    const int np = p_row < 0 ? 0 : min(a.num_parts, p_row / a.part_tokens + 1);
+    a.ws_np[qh] = np;
   }
 }
 

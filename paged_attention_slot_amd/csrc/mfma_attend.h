@@ -1,0 +1,248 @@
+// One workgroup's pass of paged attention on the gfx950 matrix cores: up to
+// 16 query rows per wave against the K/V of one KV head over a range of
+// positions read through one block-table row ([KVM §19.2.3] paged attention;
+// [KVX §01] the attention of one query; page keys in include/pkv.h).  Shared
+// by the multi-token kernel and the shared-prefix kernels.
+//
+//  * K/V arrive in tiles of 32 positions, staged in LDS by the whole
+//    workgroup (V transposed, d-major), read back as MFMA operands; the next
+//    tile's loads are issued before the current tile's matrix work and a
+//    barrier that waits only for LDS keeps them in flight.
+//  * Scores as S^T = K Q^T with v_mfma_f32_16x16x32_bf16: a lane's result
+//    fragment holds 8 positions of one query row (its lane & 15), so the
+//    online softmax (log2 units) needs only the ^16 and ^32 lane exchanges,
+//    and the weights P land directly in the operand layout of O^T += V^T P^T
+//    (positions ordered 16(j/4) + 4q + j%4 in both operands).  P enters as
+//    two bf16 terms (hi + lo), so the product keeps fp32-like weights.
+//  * A row sees positions t <= p_row inside [t_lo, t_hi); tiles are loaded
+//    with zeros past the history.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "pkv_device.h"
+
+namespace pkv {
+namespace mfma {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kKT = 32;             // positions per K/V tile
+constexpr float kRefInit = -1e30f;  // reference of a row with no position yet
+
+template <int D> constexpr int k_lds_elems() { return kKT * (D + 8); }
+template <int D> constexpr int vt_lds_elems() { return D * (kKT + 4); }
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& x) {
+  return __builtin_bit_cast(bf16x8_t, x);
+}
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS accesses,
+// not for its global loads, so the next tile's loads stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The K/V history a workgroup reads: one KV head through one table row.
+struct History {
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* trow;   // block table row
+  int32_t len;           // positions < len are in the table; zeros past it
+  int32_t g;             // KV head
+  int64_t block_elems;
+  int32_t row_elems;
+  int32_t num_blocks;
+  int32_t block_shift;
+};
+
+// A row's running state in log2 units: reference m, sum of weights lsum, and
+// the unnormalised weighted sum as this lane's fragment: o[dt][i] holds
+// d = 16 dt + 4 (lane >> 4) + i of row (lane & 15).
+template <int D>
+struct RowAcc {
+  float m;
+  float lsum;
+  f32x4_t o[D / 16];
+};
+
+// The NW waves of the workgroup walk positions [t_lo, t_hi) of ``h`` together
+// (every wave must call this with the same range).  ``q`` points at this
+// lane's query row (D bf16, 16-byte aligned); it is read only if row_ok.
+template <int D, int NW>
+__device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, const uint16_t* q,
+                                       bool row_ok, int p_row, float scale_log2,
+                                       uint16_t* k_lds, uint16_t* vt_lds, RowAcc<D>& r) {
+  constexpr int kKS = D / 32;            // k-steps of the score product
+  constexpr int kDT = D / 16;            // 16-wide d tiles of the output
+  constexpr int kKStride = D + 8;        // K rows in LDS, bf16 elements (16 B pad)
+  constexpr int kVStride = kKT + 4;      // V^T rows in LDS, bf16 elements (8 B pad)
+  constexpr int kChunksPerRow = D / 8;   // 16-byte chunks per K/V row
+  constexpr int kChunks = kKT * kChunksPerRow;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int quad = lane >> 4;
+
+  uint4 qf[kKS];
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks)
+    qf[ks] = row_ok ? *reinterpret_cast<const uint4*>(q + 32 * ks + 8 * quad)
+                    : make_uint4(0, 0, 0, 0);
+
+  r.m = kRefInit;
+  r.lsum = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt) r.o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int L = h.len;
+  const int bmask = (1 << h.block_shift) - 1;
+  // Chunks of a tile this thread moves: c = tid + r * 64 * NW.
+  constexpr int kPer = kChunks / (64 * NW);
+  static_assert(kChunks % (64 * NW) == 0, "tile chunks must split evenly");
+  uint4 nk[kPer], nv[kPer];
+  // Issue the global loads of the tile at t0 into nk / nv (zeros past the
+  // history: never unmasked, and they keep the products finite).
+  // The tile's (at most 4, block_size >= 8) block ids are uniform: scalar
+  // loads, which do not queue behind the vector loads still in flight.
+  const int last_idx = L > 0 ? (L - 1) >> h.block_shift : -1;
+  auto fetch = [&](int t0) {
+    const int b0 = t0 >> h.block_shift;
+    int ids[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int idx = b0 + k;
+      const int b = idx <= last_idx ? h.trow[idx] : 0;
+      ids[k] = (b >= 0 && b < h.num_blocks) ? b : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + i * 64 * NW;
+      const int pr = c / kChunksPerRow, cc = c - pr * kChunksPerRow;
+      const int pos = t0 + pr;
+      nk[i] = make_uint4(0, 0, 0, 0);
+      nv[i] = make_uint4(0, 0, 0, 0);
+      if (pos < L) {
+        const int k = (pos >> h.block_shift) - b0;
+        const int blk = k == 0 ? ids[0] : (k == 1 ? ids[1] : (k == 2 ? ids[2] : ids[3]));
+        const int64_t off = int64_t(blk) * h.block_elems + int64_t(pos & bmask) * h.row_elems +
+                            int64_t(h.g) * D + cc * 8;
+        nk[i] = *reinterpret_cast<const uint4*>(h.k_cache + off);
+        nv[i] = *reinterpret_cast<const uint4*>(h.v_cache + off);
+      }
+    }
+  };
+  // Stage the fetched tile: K as [pos][d], V transposed as [d][pos].
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + i * 64 * NW;
+      const int pr = c / kChunksPerRow, cc = c - pr * kChunksPerRow;
+      *reinterpret_cast<uint4*>(k_lds + pr * kKStride + cc * 8) = nk[i];
+      const uint32_t vw[4] = {nv[i].x, nv[i].y, nv[i].z, nv[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vt_lds[(cc * 8 + 2 * e) * kVStride + pr] = static_cast<uint16_t>(vw[e] & 0xFFFFu);
+        vt_lds[(cc * 8 + 2 * e + 1) * kVStride + pr] = static_cast<uint16_t>(vw[e] >> 16);
+      }
+    }
+  };
+
+  if (t_lo < t_hi) fetch(t_lo);
+  for (int t0 = t_lo; t0 < t_hi; t0 += kKT) {
+    stage();
+    lds_barrier();
+    if (t0 + kKT < t_hi) fetch(t0 + kKT);  // in flight while this tile computes
+
+    // S^T tiles: positions 16pt + 4 quad + i of row (lane & 15).
+    float sc[8];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(
+            k_lds + (16 * pt + (lane & 15)) * kKStride + 32 * ks + 8 * quad);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(qf[ks]), acc, 0,
+                                                      0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 16 * pt + 4 * quad + i;
+        const bool ok = row_ok && t <= p_row && t < t_hi;
+        const float v = ok ? acc[i] * scale_log2 : -INFINITY;
+        sc[4 * pt + i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    }
+    tmax = max_across_rows16(tmax);
+    const float mn = fmaxf(r.m, tmax);
+    const float alpha = fast_exp2(r.m - mn);
+    r.m = mn;
+    // Weights as two bf16 terms, p = hi + lo (hi = bf16(p), lo = bf16(p - hi)):
+    // P V then carries p to about 2^-17 relative, like the fp32 sum.
+    uint32_t ph[4], pl[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t h2[2], l2[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float p = fast_exp2(sc[2 * k + e] - mn);
+        psum += p;
+        h2[e] = f32_to_bf16_bits(p);
+        l2[e] = f32_to_bf16_bits(p - __uint_as_float(h2[e] << 16));
+      }
+      ph[k] = h2[0] | (h2[1] << 16);
+      pl[k] = l2[0] | (l2[1] << 16);
+    }
+    psum = sum_across_rows16(psum);
+    r.lsum = r.lsum * alpha + psum;
+    const bf16x8_t pfh = as_bf16x8(make_uint4(ph[0], ph[1], ph[2], ph[3]));
+    const bf16x8_t pfl = as_bf16x8(make_uint4(pl[0], pl[1], pl[2], pl[3]));
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt) {
+      const uint16_t* vrow = vt_lds + (16 * dt + (lane & 15)) * kVStride;
+      const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 4 * quad);
+      const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * quad);
+      f32x4_t acc = r.o[dt];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= alpha;
+      const bf16x8_t va = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfh, acc, 0, 0, 0);
+      r.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfl, acc, 0, 0, 0);
+    }
+    lds_barrier();  // every wave is done reading before the next stage
+  }
+}
+
+// Store this lane's fragment of a row's state as a piece: D floats of
+// weighted sum at acc, (reference, sum) at ml (written by the quad-0 lanes).
+template <int D>
+__device__ __forceinline__ void store_piece(const RowAcc<D>& r, float* acc, float2* ml) {
+  const int quad = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+    *reinterpret_cast<float4*>(acc + 16 * dt + 4 * quad) =
+        make_float4(r.o[dt][0], r.o[dt][1], r.o[dt][2], r.o[dt][3]);
+  if (quad == 0) *ml = make_float2(r.m, r.lsum);
+}
+
+// Store a row's normalised result as bf16.
+template <int D>
+__device__ __forceinline__ void store_row_bf16(const RowAcc<D>& r, uint16_t* dst) {
+  const int quad = (threadIdx.x & 63) >> 4;
+  const float inv = r.lsum > 0.f ? 1.0f / r.lsum : 0.f;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    const int d0 = 16 * dt + 4 * quad;
+    *reinterpret_cast<uint2*>(dst + d0) =
+        make_uint2(pack_bf16x2(r.o[dt][0] * inv, r.o[dt][1] * inv),
+                   pack_bf16x2(r.o[dt][2] * inv, r.o[dt][3] * inv));
+  }
+}
+
+}  // namespace mfma
+}  // namespace pkv

@@ -270,6 +270,74 @@ def copy_blocks_quant(pairs, k_cache, v_cache, k_scales=None, v_scales=None,
           "pkv_copy_blocks_quant")
 
 
+def prefix_groups(block_tables, seq_lens, block_size: int):
+    """Shared-prefix groups of a batch from host tables (see include/pkv.h,
+    pkv_prefix_groups).  Returns (group_starts int32 [G+1], prefix_lens int32
+    [G], max_group_size, max_prefix_len)."""
+    import numpy as np
+    t = np.ascontiguousarray(block_tables, dtype=np.int32)
+    L = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    n = int(L.size)
+    mb = int(t.shape[1]) if t.ndim == 2 else 0
+    starts = np.empty(n + 1, np.int32)
+    plens = np.empty(max(n, 1), np.int32)
+    ng, mg, mp = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    P = ctypes.POINTER(ctypes.c_int32)
+    check(lib().pkv_prefix_groups(t.ctypes.data_as(P), n, mb, L.ctypes.data_as(P),
+                                  int(block_size), starts.ctypes.data_as(P),
+                                  plens.ctypes.data_as(P), ctypes.byref(ng), ctypes.byref(mg),
+                                  ctypes.byref(mp)), "pkv_prefix_groups")
+    return starts[:ng.value + 1].copy(), plens[:ng.value].copy(), mg.value, mp.value
+
+
+def shared_workspace_bytes(num_seqs, num_q_heads, num_groups, max_group_size, max_prefix_len,
+                           max_seq_len, k_cache) -> int:
+    g = geom_of(k_cache)
+    n = lib().pkv_attention_shared_workspace_bytes(int(num_seqs), int(num_q_heads),
+                                                   int(num_groups), int(max_group_size),
+                                                   int(max_prefix_len), int(max_seq_len),
+                                                   ctypes.byref(g))
+    if n == ctypes.c_size_t(-1).value:
+        check(1, "pkv_attention_shared_workspace_bytes")
+    return int(n)
+
+
+def attention_decode_shared(q, k_cache, v_cache, block_tables, seq_lens, scale, group_starts,
+                            prefix_lens, max_group_size, max_prefix_len, out=None,
+                            max_seq_len=None, workspace=None, stream=None):
+    """Decode attention reading each group's shared prefix once (see
+    include/pkv.h, pkv_attention_decode_shared).  group_starts / prefix_lens are
+    int32 device tensors as pkv_prefix_groups returns them."""
+    g = geom_of(k_cache)
+    dev = k_cache.device
+    for t, n, dt in ((k_cache, "k_cache", torch.bfloat16), (v_cache, "v_cache", torch.bfloat16),
+                     (q, "q", torch.bfloat16), (block_tables, "block_tables", torch.int32),
+                     (seq_lens, "seq_lens", torch.int32), (group_starts, "group_starts", torch.int32),
+                     (prefix_lens, "prefix_lens", torch.int32)):
+        _need(t, n, dt, dev)
+    N, Hq, D = q.shape
+    if D != g.head_dim or block_tables.shape[0] != N or seq_lens.shape != (N,):
+        raise ValueError("shape mismatch between q, block_tables and seq_lens")
+    ng = int(prefix_lens.shape[0])
+    if group_starts.shape != (ng + 1,):
+        raise ValueError("group_starts must hold num_groups + 1 entries")
+    max_blocks = block_tables.shape[1]
+    if max_seq_len is None:
+        max_seq_len = max_blocks * g.block_size
+    if out is None:
+        out = torch.empty_like(q)
+    need = shared_workspace_bytes(N, Hq, ng, max_group_size, max_prefix_len, max_seq_len, k_cache)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    check(lib().pkv_attention_decode_shared(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), max_blocks, _ptr(seq_lens),
+        _ptr(group_starts), _ptr(prefix_lens), ng, int(max_group_size), int(max_prefix_len),
+        float(scale), _ptr(out), N, Hq, int(max_seq_len), _ptr(workspace), ws_bytes,
+        ctypes.byref(g), _stream(stream)), "pkv_attention_decode_shared")
+    return out
+
+
 class HostPool:
     """Pinned host blocks laid out like a device pool pair (K, V and, for INT8
     pools, the fp32 scale pools), ``num_blocks`` blocks.  Allocated with

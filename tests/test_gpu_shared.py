@@ -1,0 +1,140 @@
+"""GPU parity of pkv_attention_decode_shared (shared prefix read once per group)
+through the C ABI against the oracle's decode attention (the definition: the
+groups change which reads serve which positions, not the result).
+
+Cases: the 176-sequence shared-prefix configuration (one group, 2048 shared
+tokens) in the launch configuration its measurement times; small families with
+prefixes ending inside a block, forks, several groups, group sizes beyond one
+row block, head dims 64/128, group sizes G of 1 to 16; hand-built tables where
+members are shorter than the shared blocks, empty sequences, and a grid bound
+(max_group_size) below a group's size.  Every case prints its shape first."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle.attention import attention_decode, to_f64  # noqa: E402
+from oracle.replay import run_step  # noqa: E402
+from oracle.shared import prefix_groups  # noqa: E402
+from tests.parity import assert_gate  # noqa: E402
+from workloads import config_workload, shared_prefix_workload  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from paged_attention_slot_amd import lib
+    lib()
+
+
+def run_wl(wl, groups_expected=None):
+    from paged_attention_slot_amd.runtime import DecodeStep, to_host_bits
+    say(f"  case {wl.name}: N={wl.num_seqs} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} "
+        f"D={wl.head_dim} B={wl.block_size} seed={wl.seed}")
+    step = DecodeStep(wl)
+    step.copy()
+    step.write()
+    gs, pl, mg, mp = step.shared_groups()
+    say(f"  groups={pl.numel()} max_group={mg} max_prefix={mp}")
+    if groups_expected is not None:
+        assert (gs.cpu().tolist(), pl.cpu().tolist()) == groups_expected
+    step.attention_shared()
+    torch.cuda.synchronize()
+    got = to_f64(to_host_bits(step.out))
+    ost = run_step(wl, keep_values=False)
+    s0, p0 = prefix_groups(ost.block_tables, ost.seq_lens, wl.block_size)
+    assert np.array_equal(s0, gs.cpu().numpy()) and np.array_equal(p0, pl.cpu().numpy())
+    return got, ost.attention(), step
+
+
+def test_shared_prefix_config_full():
+    wl = config_workload("shared-prefix-cow")
+    got, ref, _ = run_wl(wl, ([0, 176], [2048]))
+    say("  gate", assert_gate(got, ref, "bf16", "shared-prefix-cow"))
+
+
+FAMILIES = [  # prefix, suffix lens, forking parents, samples, Hq, Hkv, D, B
+    (64, [3, 16, 7, 1, 12, 30, 9], 4, 4, 16, 4, 128, 16),
+    (40, [3, 9, 1, 20, 33], 2, 3, 8, 8, 128, 16),      # prefix ends inside a block
+    (512, [100, 1, 37, 250], 1, 2, 32, 8, 128, 32),
+    (96, [5, 8, 13] * 12, 0, 1, 16, 1, 128, 8),         # 36 members x G = 16: many row blocks
+    (130, [4, 70, 9], 1, 3, 12, 4, 64, 64),
+    (33, [1, 2, 3, 4, 5, 6, 7, 8, 9, 10], 3, 2, 2, 2, 64, 8),
+]
+
+
+@pytest.mark.parametrize("prefix,suffix,fp,spf,Hq,Hkv,D,B", FAMILIES, ids=lambda v: str(v))
+def test_families(prefix, suffix, fp, spf, Hq, Hkv, D, B):
+    wl = shared_prefix_workload(prefix_tokens=prefix, suffix_lens=suffix, forking_parents=fp,
+                                samples_per_fork=spf, num_q_heads=Hq, num_kv_heads=Hkv,
+                                head_dim=D, block_size=B, dtype="bf16", seed=prefix + B,
+                                name=f"family-p{prefix}")
+    # pools sized for block-aligned prefixes; a partial prefix block is
+    # copied once per sharer
+    extra = len(suffix) + 8
+    wl.num_blocks += extra
+    wl.free_order = np.random.default_rng(prefix).permutation(wl.num_blocks).astype(np.int32)
+    got, ref, _ = run_wl(wl)
+    assert_gate(got, ref, "bf16", wl.name)
+
+
+def hand_case(tables, lens, Hq, Hkv, D, B, nb, seed):
+    from paged_attention_slot_amd import ops
+    rng = np.random.default_rng(seed)
+
+    def bf(shape):
+        u = rng.normal(0, 1, shape).astype(np.float32).view(np.uint32)
+        return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    kp, vp = bf((nb, B, Hkv, D)), bf((nb, B, Hkv, D))
+    q = bf((len(lens), Hq, D))
+    dev = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)  # noqa: E731
+    tables = np.asarray(tables, np.int32)
+    lens = np.asarray(lens, np.int32)
+    ref = attention_decode(q, kp, vp, tables, lens, 1 / np.sqrt(D))
+    return ops, (t(q), t(kp), t(vp), torch.from_numpy(tables).to(dev),
+                 torch.from_numpy(lens).to(dev)), ref
+
+
+def test_members_shorter_than_the_shared_blocks_and_empty_sequences():
+    """Sequences 0-2 hold the same three blocks with 40, 33 and 48 tokens (the
+    shared prefix of 48 tokens is longer than two of them); sequence 3 is
+    empty; 4-5 share one block, then differ."""
+    from paged_attention_slot_amd.runtime import to_host_bits
+    B = 16
+    tables = [[5, 7, 9, -1], [5, 7, 9, -1], [5, 7, 9, -1], [-1, -1, -1, -1],
+              [2, 3, 4, -1], [2, 6, -1, -1]]
+    lens = [40, 33, 48, 0, 40, 20]
+    ops, (q, kp, vp, tb, ln), ref = hand_case(tables, lens, 8, 2, 128, B, 12, 11)
+    starts, plens, mg, mp = ops.prefix_groups(np.asarray(tables, np.int32),
+                                              np.asarray(lens, np.int32), B)
+    assert starts.tolist() == [0, 3, 4, 6] and plens.tolist() == [48, 0, 16]
+    for bound, name in ((mg, "grid fits"), (1, "groups beyond the grid share nothing")):
+        say(f"  hand case: max_group_size={bound} ({name})")
+        out = ops.attention_decode_shared(q, kp, vp, tb, ln, 1 / np.sqrt(128),
+                                          torch.from_numpy(starts).cuda(),
+                                          torch.from_numpy(plens).cuda(), bound, mp,
+                                          max_seq_len=48)
+        torch.cuda.synchronize()
+        got = to_f64(to_host_bits(out))
+        assert_gate(got, ref, "bf16", name)
+        assert not got[3].any()
+
+
+def test_matches_the_plain_decode_kernel_on_the_config():
+    """Both entry points on the same pools: each within the gate of the
+    oracle, and within twice the gate of each other."""
+    from paged_attention_slot_amd.runtime import to_host_bits
+    wl = config_workload("shared-prefix-cow")
+    got, ref, step = run_wl(wl)
+    step.attention()
+    torch.cuda.synchronize()
+    plain = to_f64(to_host_bits(step.out))
+    assert_gate(plain, ref, "bf16", "plain decode")
+    assert np.max(np.abs(got - plain)) < 2 * (2e-3 + 2 ** -8)
