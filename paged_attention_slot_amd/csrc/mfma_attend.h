@@ -98,9 +98,15 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
 
   const int L = h.len;
   const int bmask = (1 << h.block_shift) - 1;
-  // Chunks of a tile this thread moves: c = tid + r * 64 * NW.
+  // Chunks of a tile this thread moves: the same 8-element d slice (chunk cc)
+  // of kPer consecutive positions pg * kPer .. + kPer - 1, so that V^T takes
+  // kPer-element stores per d instead of one store per element (the global
+  // loads stay coalesced: 16 lanes read one contiguous K/V row).
   constexpr int kPer = kChunks / (64 * NW);
   static_assert(kChunks % (64 * NW) == 0, "tile chunks must split evenly");
+  static_assert(kPer == 1 || kPer == 2 || kPer == 4 || kPer == 8, "1, 2, 4 or 8 positions");
+  const int cc = tid % kChunksPerRow;
+  const int pg = tid / kChunksPerRow;
   uint4 nk[kPer], nv[kPer];
   // Issue the global loads of the tile at t0 into nk / nv (zeros past the
   // history: never unmasked, and they keep the products finite).
@@ -118,9 +124,7 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
     }
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int c = tid + i * 64 * NW;
-      const int pr = c / kChunksPerRow, cc = c - pr * kChunksPerRow;
-      const int pos = t0 + pr;
+      const int pos = t0 + pg * kPer + i;
       nk[i] = make_uint4(0, 0, 0, 0);
       nv[i] = make_uint4(0, 0, 0, 0);
       if (pos < L) {
@@ -133,18 +137,44 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
       }
     }
   };
-  // Stage the fetched tile: K as [pos][d], V transposed as [d][pos].
+  // Stage the fetched tile: K as [pos][d], V transposed as [d][pos] with one
+  // store of kPer positions per d.
   auto stage = [&]() {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = tid + i * 64 * NW;
-      const int pr = c / kChunksPerRow, cc = c - pr * kChunksPerRow;
-      *reinterpret_cast<uint4*>(k_lds + pr * kKStride + cc * 8) = nk[i];
-      const uint32_t vw[4] = {nv[i].x, nv[i].y, nv[i].z, nv[i].w};
+    for (int i = 0; i < kPer; ++i)
+      *reinterpret_cast<uint4*>(k_lds + (pg * kPer + i) * kKStride + cc * 8) = nk[i];
+    uint32_t vw[kPer][4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vt_lds[(cc * 8 + 2 * e) * kVStride + pr] = static_cast<uint16_t>(vw[e] & 0xFFFFu);
-        vt_lds[(cc * 8 + 2 * e + 1) * kVStride + pr] = static_cast<uint16_t>(vw[e] >> 16);
+    for (int i = 0; i < kPer; ++i) {
+      vw[i][0] = nv[i].x;
+      vw[i][1] = nv[i].y;
+      vw[i][2] = nv[i].z;
+      vw[i][3] = nv[i].w;
+    }
+    if constexpr (kPer == 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vt_lds[(cc * 8 + e) * kVStride + pg] = static_cast<uint16_t>(vw[0][e >> 1] >> (16 * (e & 1)));
+      return;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // element e of the chunk (d = 8 cc + e) across the kPer positions
+      uint32_t col[kPer > 1 ? kPer / 2 : 1];
+#pragma unroll
+      for (int j = 0; j < kPer / 2; ++j) {
+        const uint32_t a0 = vw[2 * j][e >> 1], a1 = vw[2 * j + 1][e >> 1];
+        col[j] = (e & 1) ? ((a0 >> 16) | (a1 & 0xFFFF0000u)) : ((a0 & 0xFFFFu) | (a1 << 16));
+      }
+      // V^T rows are 72 bytes apart: 8-byte aligned stores only.
+      uint16_t* dst = vt_lds + (cc * 8 + e) * kVStride + pg * kPer;
+      if constexpr (kPer == 8) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(col[0], col[1]);
+        *reinterpret_cast<uint2*>(dst + 4) = make_uint2(col[2], col[3]);
+      } else if constexpr (kPer == 4) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(col[0], col[1]);
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) = col[0];
       }
     }
   };
