@@ -59,7 +59,7 @@ template <int D, int NW>
 __global__ void __launch_bounds__(64 * NW)
 attn_multi_kernel(MultiArgs a) {
   __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D>()];
-  __shared__ __align__(16) uint16_t vt_lds[pkv::mfma::vt_lds_elems<D>()];
+  __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D>()];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(tid >> 6));
@@ -90,7 +90,7 @@ attn_multi_kernel(MultiArgs a) {
                                 L, g, a.block_elems, a.row_elems, a.num_blocks, a.block_shift};
   pkv::mfma::RowAcc<D> r;
   pkv::mfma::attend<D, NW>(hist, t_lo, t_hi, a.q + qh * D, row_ok, p_row, a.scale_log2, k_lds,
-                           vt_lds, r);
+                           v_lds, r);
 
   if (!row_ok) return;
   if (a.num_parts == 1) {

@@ -103,7 +103,7 @@ template <int D, int NW>
 __global__ void __launch_bounds__(64 * NW)
 attn_prefix_kernel(SharedArgs a) {
   __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D>()];
-  __shared__ __align__(16) uint16_t vt_lds[pkv::mfma::vt_lds_elems<D>()];
+  __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D>()];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int gi = blockIdx.z, g = blockIdx.y;
@@ -129,7 +129,7 @@ attn_prefix_kernel(SharedArgs a) {
                                 P, g, a.block_elems, a.row_elems, a.num_blocks, a.block_shift};
   pkv::mfma::RowAcc<D> r;
   pkv::mfma::attend<D, NW>(hist, t_lo, t_hi, a.q + qh * D, row_ok, L - 1, a.scale_log2, k_lds,
-                           vt_lds, r);
+                           v_lds, r);
   if (!row_ok) return;
   const int64_t slot = qh * (a.pre_parts + a.suf_parts) + part;
   pkv::mfma::store_piece<D>(r, a.ws_acc + slot * D, a.ws_ml + slot);
@@ -140,7 +140,7 @@ template <int D, int NW>
 __global__ void __launch_bounds__(64 * NW)
 attn_suffix_kernel(SharedArgs a) {
   __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D>()];
-  __shared__ __align__(16) uint16_t vt_lds[pkv::mfma::vt_lds_elems<D>()];
+  __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D>()];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int s = blockIdx.z, g = blockIdx.y, part = blockIdx.x;
@@ -158,7 +158,7 @@ attn_suffix_kernel(SharedArgs a) {
                                 L, g, a.block_elems, a.row_elems, a.num_blocks, a.block_shift};
   pkv::mfma::RowAcc<D> r;
   pkv::mfma::attend<D, NW>(hist, t_lo, t_hi, a.q + qh * D, row_ok, L - 1, a.scale_log2, k_lds,
-                           vt_lds, r);
+                           v_lds, r);
   if (!row_ok) return;
   const int64_t slot = qh * (a.pre_parts + a.suf_parts) + a.pre_parts + part;
   pkv::mfma::store_piece<D>(r, a.ws_acc + slot * D, a.ws_ml + slot);

@@ -5,9 +5,12 @@
 // by the multi-token kernel and the shared-prefix kernels.
 //
 //  * K/V arrive in tiles of 32 positions, staged in LDS by the whole
-//    workgroup (V transposed, d-major), read back as MFMA operands; the next
-//    tile's loads are issued before the current tile's matrix work and a
-//    barrier that waits only for LDS keeps them in flight.
+//    workgroup as [position][d] rows, read back as MFMA operands: K with
+//    plain 16-byte reads, V through gfx950's transposing LDS read
+//    (ds_read_b64_tr_b16), which hands each lane the 4 positions of one d
+//    that the V^T operand needs; the next tile's loads are issued before the
+//    current tile's matrix work and a barrier that waits only for LDS keeps
+//    them in flight.
 //  * Scores as S^T = K Q^T with v_mfma_f32_16x16x32_bf16: a lane's result
 //    fragment holds 8 positions of one query row (its lane & 15), so the
 //    online softmax (log2 units) needs only the ^16 and ^32 lane exchanges,
@@ -34,7 +37,18 @@ constexpr int kKT = 32;             // positions per K/V tile
 constexpr float kRefInit = -1e30f;  // reference of a row with no position yet
 
 template <int D> constexpr int k_lds_elems() { return kKT * (D + 8); }
-template <int D> constexpr int vt_lds_elems() { return D * (kKT + 4); }
+template <int D> constexpr int v_lds_elems() { return kKT * (D + 8); }
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16 (lane layout checked with a one-wave probe): within each
+// group of 16 lanes, lane j receives element j % 4 of the 8-byte words that
+// lanes j / 4, j / 4 + 4, j / 4 + 8, j / 4 + 12 address.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& x) {
   return __builtin_bit_cast(bf16x8_t, x);
@@ -75,11 +89,10 @@ struct RowAcc {
 template <int D, int NW>
 __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, const uint16_t* q,
                                        bool row_ok, int p_row, float scale_log2,
-                                       uint16_t* k_lds, uint16_t* vt_lds, RowAcc<D>& r) {
+                                       uint16_t* k_lds, uint16_t* v_lds, RowAcc<D>& r) {
   constexpr int kKS = D / 32;            // k-steps of the score product
   constexpr int kDT = D / 16;            // 16-wide d tiles of the output
-  constexpr int kKStride = D + 8;        // K rows in LDS, bf16 elements (16 B pad)
-  constexpr int kVStride = kKT + 4;      // V^T rows in LDS, bf16 elements (8 B pad)
+  constexpr int kKStride = D + 8;        // K and V rows in LDS, bf16 elements (16 B pad)
   constexpr int kChunksPerRow = D / 8;   // 16-byte chunks per K/V row
   constexpr int kChunks = kKT * kChunksPerRow;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -99,12 +112,10 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
   const int L = h.len;
   const int bmask = (1 << h.block_shift) - 1;
   // Chunks of a tile this thread moves: the same 8-element d slice (chunk cc)
-  // of kPer consecutive positions pg * kPer .. + kPer - 1, so that V^T takes
-  // kPer-element stores per d instead of one store per element (the global
-  // loads stay coalesced: 16 lanes read one contiguous K/V row).
+  // of kPer consecutive positions pg * kPer .. + kPer - 1 (the global loads
+  // stay coalesced: 16 lanes read one contiguous K/V row).
   constexpr int kPer = kChunks / (64 * NW);
   static_assert(kChunks % (64 * NW) == 0, "tile chunks must split evenly");
-  static_assert(kPer == 1 || kPer == 2 || kPer == 4 || kPer == 8, "1, 2, 4 or 8 positions");
   const int cc = tid % kChunksPerRow;
   const int pg = tid / kChunksPerRow;
   uint4 nk[kPer], nv[kPer];
@@ -137,47 +148,19 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
       }
     }
   };
-  // Stage the fetched tile: K as [pos][d], V transposed as [d][pos] with one
-  // store of kPer positions per d.
+  // Stage the fetched tile: K and V as [pos][d].
   auto stage = [&]() {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i)
-      *reinterpret_cast<uint4*>(k_lds + (pg * kPer + i) * kKStride + cc * 8) = nk[i];
-    uint32_t vw[kPer][4];
-#pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      vw[i][0] = nv[i].x;
-      vw[i][1] = nv[i].y;
-      vw[i][2] = nv[i].z;
-      vw[i][3] = nv[i].w;
-    }
-    if constexpr (kPer == 1) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        vt_lds[(cc * 8 + e) * kVStride + pg] = static_cast<uint16_t>(vw[0][e >> 1] >> (16 * (e & 1)));
-      return;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      // element e of the chunk (d = 8 cc + e) across the kPer positions
-      uint32_t col[kPer > 1 ? kPer / 2 : 1];
-#pragma unroll
-      for (int j = 0; j < kPer / 2; ++j) {
-        const uint32_t a0 = vw[2 * j][e >> 1], a1 = vw[2 * j + 1][e >> 1];
-        col[j] = (e & 1) ? ((a0 >> 16) | (a1 & 0xFFFF0000u)) : ((a0 & 0xFFFFu) | (a1 << 16));
-      }
-      // V^T rows are 72 bytes apart: 8-byte aligned stores only.
-      uint16_t* dst = vt_lds + (cc * 8 + e) * kVStride + pg * kPer;
-      if constexpr (kPer == 8) {
-        *reinterpret_cast<uint2*>(dst) = make_uint2(col[0], col[1]);
-        *reinterpret_cast<uint2*>(dst + 4) = make_uint2(col[2], col[3]);
-      } else if constexpr (kPer == 4) {
-        *reinterpret_cast<uint2*>(dst) = make_uint2(col[0], col[1]);
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = col[0];
-      }
+      const int off = (pg * kPer + i) * kKStride + cc * 8;
+      *reinterpret_cast<uint4*>(k_lds + off) = nk[i];
+      *reinterpret_cast<uint4*>(v_lds + off) = nv[i];
     }
   };
+  // This lane's V^T reads: row 4 (lane >> 4) + (lane & 15) / 4 (+ 16 for the
+  // second half of the k dimension), columns 4 ((lane & 15) % 4) .. + 3 of
+  // each 16-wide d tile.
+  const uint16_t* v_rd = v_lds + (4 * quad + ((lane & 15) >> 2)) * kKStride + 4 * (lane & 3);
 
   if (t_lo < t_hi) fetch(t_lo);
   for (int t0 = t_lo; t0 < t_hi; t0 += kKT) {
@@ -234,9 +217,9 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
     const bf16x8_t pfl = as_bf16x8(make_uint4(pl[0], pl[1], pl[2], pl[3]));
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt) {
-      const uint16_t* vrow = vt_lds + (16 * dt + (lane & 15)) * kVStride;
-      const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 4 * quad);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * quad);
+      // V^T[16 dt + (lane & 15)][positions 4 quad .. + 3 and 16 + 4 quad .. + 3]
+      const uint2 lo = lds_read_tr16(v_rd + 16 * dt);
+      const uint2 hi = lds_read_tr16(v_rd + 16 * kKStride + 16 * dt);
       f32x4_t acc = r.o[dt];
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] *= alpha;
