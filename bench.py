@@ -306,7 +306,7 @@ def bench_shared(args) -> int:
     for layer in range(args.layers):
         step.copy(layer)
         step.write(layer)
-    gs, pl, mg, mp = step.shared_groups()
+    gs, pl, mg, mp, ms = step.shared_groups()
     lens = wl.seq_lens.astype(np.int64)
     per_pos = 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
     logical = int(lens.sum()) * per_pos
@@ -358,7 +358,7 @@ def bench_shared(args) -> int:
     config = {"workload": f"{wl.name}+shared", "num_seqs": wl.num_seqs,
               "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
               "head_dim": wl.head_dim, "block_size": B, "groups": int(plens.size),
-              "max_group_size": int(mg), "max_prefix_len": int(mp),
+              "max_group_size": int(mg), "max_prefix_len": int(mp), "max_suffix_len": int(ms),
               "sum_seq_lens": int(lens.sum()), "layers_cycled": L_, "seed": wl.seed}
     detail = {"logical_kv_bytes": logical, "unique_kv_bytes": unique,
               "logical_gbps": logical / t_sh / 1e9, "unique_gbps": unique / t_sh / 1e9,

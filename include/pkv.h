@@ -174,6 +174,10 @@ pkv_status pkv_copy_blocks_quant(const int32_t* src_dst_pairs, int32_t num_pairs
  *                 member shorter than the prefix attends only its own tokens.
  *   max_group_size, max_prefix_len  host bounds that size the grid (a group
  *                 larger than max_group_size shares nothing).
+ *   max_suffix_len  host hint: the longest run of positions after a
+ *                 sequence's shared prefix (pkv_prefix_groups reports it);
+ *                 it only sizes the suffix partitions (0 = max_seq_len; a
+ *                 longer suffix is still attended in full).
  * Other arguments as pkv_attention_decode (q, out [num_seqs][H_q][D] bf16).
  * The workspace is required (pkv_attention_shared_workspace_bytes).  Groups
  * that break the contract give unspecified values, never out-of-pool reads.
@@ -181,15 +185,15 @@ pkv_status pkv_copy_blocks_quant(const int32_t* src_dst_pairs, int32_t num_pairs
  * block_size < 8; more than 64 query heads per KV head), HIP. */
 size_t pkv_attention_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                             int32_t num_groups, int32_t max_group_size,
-                                            int32_t max_prefix_len, int32_t max_seq_len,
-                                            const pkv_geom* geom);
+                                            int32_t max_prefix_len, int32_t max_suffix_len,
+                                            int32_t max_seq_len, const pkv_geom* geom);
 pkv_status pkv_attention_decode_shared(const void* q, const void* k_cache, const void* v_cache,
                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
                                        const int32_t* seq_lens, const int32_t* group_starts,
                                        const int32_t* prefix_lens, int32_t num_groups,
                                        int32_t max_group_size, int32_t max_prefix_len,
-                                       float scale, void* out, int32_t num_seqs,
-                                       int32_t num_q_heads, int32_t max_seq_len,
+                                       int32_t max_suffix_len, float scale, void* out,
+                                       int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
                                        void* workspace, size_t workspace_bytes,
                                        const pkv_geom* geom, void* stream);
 
@@ -200,12 +204,13 @@ pkv_status pkv_attention_decode_shared(const void* q, const void* k_cache, const
  * ceil(L / block_size)) and that agree, in tokens; a group of one shares
  * nothing.  Outputs (host): group_starts_out [num_seqs + 1], prefix_lens_out
  * [num_seqs] (the first *num_groups_out entries are used), the largest group
- * and prefix.  Errors: INVALID_ARG. */
+ * and prefix, and the most positions any sequence has after its group's
+ * prefix.  Errors: INVALID_ARG. */
 pkv_status pkv_prefix_groups(const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks,
                              const int32_t* seq_lens, int32_t block_size,
                              int32_t* group_starts_out, int32_t* prefix_lens_out,
                              int32_t* num_groups_out, int32_t* max_group_size_out,
-                             int32_t* max_prefix_len_out);
+                             int32_t* max_prefix_len_out, int32_t* max_suffix_len_out);
 
 /* ---- Block swap to host memory ([KVM §19.2.6]: a paused request's KV cache
  * moves to CPU memory and comes back when device memory frees; [KVM §19.2.2]

@@ -89,8 +89,9 @@ attn_multi_kernel(MultiArgs a) {
   const pkv::mfma::History hist{a.k_cache, a.v_cache, a.block_tables + int64_t(s) * a.max_blocks,
                                 L, g, a.block_elems, a.row_elems, a.num_blocks, a.block_shift};
   pkv::mfma::RowAcc<D> r;
-  pkv::mfma::attend<D, NW>(hist, t_lo, t_hi, a.q + qh * D, row_ok, p_row, a.scale_log2, k_lds,
-                           v_lds, r);
+  pkv::mfma::start(r);
+  pkv::mfma::attend<D, NW, (NW >= 2 ? 2 : 1)>(hist, t_lo, t_hi, a.q + qh * D, row_ok, p_row,
+                                             a.scale_log2, k_lds, v_lds, r);
 
   if (!row_ok) return;
   if (a.num_parts == 1) {

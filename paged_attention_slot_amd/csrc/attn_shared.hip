@@ -128,8 +128,9 @@ attn_prefix_kernel(SharedArgs a) {
   const pkv::mfma::History hist{a.k_cache, a.v_cache, a.block_tables + int64_t(first) * a.max_blocks,
                                 P, g, a.block_elems, a.row_elems, a.num_blocks, a.block_shift};
   pkv::mfma::RowAcc<D> r;
-  pkv::mfma::attend<D, NW>(hist, t_lo, t_hi, a.q + qh * D, row_ok, L - 1, a.scale_log2, k_lds,
-                           v_lds, r);
+  pkv::mfma::start(r);
+  pkv::mfma::attend<D, NW, (NW >= 2 ? 2 : 1)>(hist, t_lo, t_hi, a.q + qh * D, row_ok, L - 1,
+                                             a.scale_log2, k_lds, v_lds, r);
   if (!row_ok) return;
   const int64_t slot = qh * (a.pre_parts + a.suf_parts) + part;
   pkv::mfma::store_piece<D>(r, a.ws_acc + slot * D, a.ws_ml + slot);
@@ -146,9 +147,7 @@ attn_suffix_kernel(SharedArgs a) {
   const int s = blockIdx.z, g = blockIdx.y, part = blockIdx.x;
   const int L = clamp_len(a.seq_lens[s], a.len_cap);
   const int P = seq_prefix(a, s, L);
-  const int t_lo = P + part * a.suf_tokens;
-  const int t_hi = min(t_lo + a.suf_tokens, L);
-  if (t_lo >= t_hi) return;  // the merge counts only parts holding positions
+  if (P + part * a.suf_tokens >= L) return;  // the merge counts only parts holding positions
 
   const int G = a.group;
   const int hh = 16 * w + (lane & 15);
@@ -157,8 +156,13 @@ attn_suffix_kernel(SharedArgs a) {
   const pkv::mfma::History hist{a.k_cache, a.v_cache, a.block_tables + int64_t(s) * a.max_blocks,
                                 L, g, a.block_elems, a.row_elems, a.num_blocks, a.block_shift};
   pkv::mfma::RowAcc<D> r;
-  pkv::mfma::attend<D, NW>(hist, t_lo, t_hi, a.q + qh * D, row_ok, L - 1, a.scale_log2, k_lds,
-                           v_lds, r);
+  pkv::mfma::start(r);
+  // Partitions part, part + suf_parts, ...: a suffix longer than the grid was
+  // sized for is folded into the same piece.
+  for (int t_lo = P + part * a.suf_tokens; t_lo < L; t_lo += a.suf_parts * a.suf_tokens)
+    pkv::mfma::attend<D, NW, (NW >= 2 ? 2 : 1)>(hist, t_lo, min(t_lo + a.suf_tokens, L),
+                                               a.q + qh * D, row_ok, L - 1, a.scale_log2, k_lds,
+                                               v_lds, r);
   if (!row_ok) return;
   const int64_t slot = qh * (a.pre_parts + a.suf_parts) + a.pre_parts + part;
   pkv::mfma::store_piece<D>(r, a.ws_acc + slot * D, a.ws_ml + slot);
@@ -175,7 +179,7 @@ attn_shared_merge_kernel(SharedArgs a) {
   const int L = clamp_len(a.seq_lens[s], a.len_cap);
   const int P = seq_prefix(a, s, L);
   const int np_pre = (P + a.pre_tokens - 1) / a.pre_tokens;
-  const int np_suf = (L - P + a.suf_tokens - 1) / a.suf_tokens;
+  const int np_suf = min(a.suf_parts, (L - P + a.suf_tokens - 1) / a.suf_tokens);
   const int64_t qh = int64_t(s) * a.num_q_heads + h;
   const int64_t base = qh * (a.pre_parts + a.suf_parts);
   float M = -INFINITY;
@@ -221,8 +225,8 @@ struct SharedPlan {
 };
 
 pkv_status shared_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_groups,
-                       int32_t max_group_size, int32_t max_prefix_len, int32_t max_seq_len,
-                       const pkv_geom* g, const char* who, SharedPlan* pl) {
+                       int32_t max_group_size, int32_t max_prefix_len, int32_t max_suffix_len,
+                       int32_t max_seq_len, const pkv_geom* g, const char* who, SharedPlan* pl) {
   if (pkv_status st = pkv::check_geom(g, who)) return st;
   if (g->dtype != PKV_BF16)
     return pkv::fail(PKV_ERR_UNSUPPORTED, "%s: dtype %d (built: bf16)", who, g->dtype);
@@ -253,9 +257,16 @@ pkv_status shared_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_groups
   const int seq_len = max_seq_len > 0 ? max_seq_len : 1;
   pl->pre_tokens =
       part_tokens_for(int64_t(num_groups) * g->num_kv_heads * pl->row_blocks, pre_len);
-  pl->suf_tokens = part_tokens_for(int64_t(num_seqs) * g->num_kv_heads, seq_len);
+  // Suffix partitions from the longest suffix (a hint: longer suffixes are
+  // folded into the grid's pieces): short critical paths, about 4096 items.
+  const int suf_len = max_suffix_len > 0 && max_suffix_len < seq_len ? max_suffix_len : seq_len;
+  const int64_t suf_items = int64_t(num_seqs) * g->num_kv_heads;
+  const int64_t want = suf_items >= 4096 ? 1 : (4096 + suf_items - 1) / (suf_items > 0 ? suf_items : 1);
+  int64_t spt = round_up_to((suf_len + want - 1) / want, kKT);
+  if (spt < 64) spt = 64;
+  pl->suf_tokens = static_cast<int>(spt);
   pl->pre_parts = (pre_len + pl->pre_tokens - 1) / pl->pre_tokens;
-  pl->suf_parts = (seq_len + pl->suf_tokens - 1) / pl->suf_tokens;
+  pl->suf_parts = static_cast<int>((suf_len + spt - 1) / spt);
   if (int64_t(pl->row_blocks) * pl->pre_parts > 2147483647LL)
     return pkv::fail(PKV_ERR_INVALID_ARG, "%s: too many prefix work items", who);
   const size_t slots = size_t(num_seqs) * num_q_heads * (pl->pre_parts + pl->suf_parts);
@@ -290,11 +301,12 @@ extern "C" {
 
 size_t pkv_attention_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                             int32_t num_groups, int32_t max_group_size,
-                                            int32_t max_prefix_len, int32_t max_seq_len,
-                                            const pkv_geom* geom) {
+                                            int32_t max_prefix_len, int32_t max_suffix_len,
+                                            int32_t max_seq_len, const pkv_geom* geom) {
   SharedPlan pl;
-  if (shared_plan(num_seqs, num_q_heads, num_groups, max_group_size, max_prefix_len, max_seq_len,
-                  geom, "pkv_attention_shared_workspace_bytes", &pl) != PKV_OK)
+  if (shared_plan(num_seqs, num_q_heads, num_groups, max_group_size, max_prefix_len,
+                  max_suffix_len, max_seq_len, geom, "pkv_attention_shared_workspace_bytes",
+                  &pl) != PKV_OK)
     return static_cast<size_t>(-1);
   return pl.ws_bytes;
 }
@@ -304,14 +316,15 @@ pkv_status pkv_attention_decode_shared(const void* q, const void* k_cache, const
                                        const int32_t* seq_lens, const int32_t* group_starts,
                                        const int32_t* prefix_lens, int32_t num_groups,
                                        int32_t max_group_size, int32_t max_prefix_len,
-                                       float scale, void* out, int32_t num_seqs,
+                                       int32_t max_suffix_len, float scale, void* out,
+                                       int32_t num_seqs,
                                        int32_t num_q_heads, int32_t max_seq_len,
                                        void* workspace, size_t workspace_bytes,
                                        const pkv_geom* geom, void* stream) {
   const char* who = "pkv_attention_decode_shared";
   SharedPlan pl;
   if (pkv_status st = shared_plan(num_seqs, num_q_heads, num_groups, max_group_size,
-                                  max_prefix_len, max_seq_len, geom, who, &pl))
+                                  max_prefix_len, max_suffix_len, max_seq_len, geom, who, &pl))
     return st;
   if (!std::isfinite(scale)) return pkv::fail(PKV_ERR_INVALID_ARG, "%s: scale is not finite", who);
   if (max_blocks_per_seq < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "%s: negative size", who);

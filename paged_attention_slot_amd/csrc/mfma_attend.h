@@ -83,10 +83,22 @@ struct RowAcc {
   f32x4_t o[D / 16];
 };
 
+// An empty state (no position seen).
+template <int D>
+__device__ __forceinline__ void start(RowAcc<D>& r) {
+  r.m = kRefInit;
+  r.lsum = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) r.o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
 // The NW waves of the workgroup walk positions [t_lo, t_hi) of ``h`` together
-// (every wave must call this with the same range).  ``q`` points at this
-// lane's query row (D bf16, 16-byte aligned); it is read only if row_ok.
-template <int D, int NW>
+// (every wave must call this with the same range), folding them into ``r``
+// (start() it first; further calls continue the same online softmax).
+// ``q`` points at this lane's query row (D bf16, 16-byte aligned); it is read
+// only if row_ok.  PD tiles are in flight ahead of the one being computed
+// (PD register buffers of K/V per thread).
+template <int D, int NW, int PD = 1>
 __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, const uint16_t* q,
                                        bool row_ok, int p_row, float scale_log2,
                                        uint16_t* k_lds, uint16_t* v_lds, RowAcc<D>& r) {
@@ -104,11 +116,6 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
     qf[ks] = row_ok ? *reinterpret_cast<const uint4*>(q + 32 * ks + 8 * quad)
                     : make_uint4(0, 0, 0, 0);
 
-  r.m = kRefInit;
-  r.lsum = 0.f;
-#pragma unroll
-  for (int dt = 0; dt < kDT; ++dt) r.o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
   const int L = h.len;
   const int bmask = (1 << h.block_shift) - 1;
   // Chunks of a tile this thread moves: the same 8-element d slice (chunk cc)
@@ -118,13 +125,13 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
   static_assert(kChunks % (64 * NW) == 0, "tile chunks must split evenly");
   const int cc = tid % kChunksPerRow;
   const int pg = tid / kChunksPerRow;
-  uint4 nk[kPer], nv[kPer];
-  // Issue the global loads of the tile at t0 into nk / nv (zeros past the
+  uint4 nk[PD][kPer], nv[PD][kPer];
+  // Issue the global loads of the tile at t0 into buffer j (zeros past the
   // history: never unmasked, and they keep the products finite).
   // The tile's (at most 4, block_size >= 8) block ids are uniform: scalar
   // loads, which do not queue behind the vector loads still in flight.
   const int last_idx = L > 0 ? (L - 1) >> h.block_shift : -1;
-  auto fetch = [&](int t0) {
+  auto fetch = [&](int j, int t0) {
     const int b0 = t0 >> h.block_shift;
     int ids[4];
 #pragma unroll
@@ -136,25 +143,25 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int pos = t0 + pg * kPer + i;
-      nk[i] = make_uint4(0, 0, 0, 0);
-      nv[i] = make_uint4(0, 0, 0, 0);
+      nk[j][i] = make_uint4(0, 0, 0, 0);
+      nv[j][i] = make_uint4(0, 0, 0, 0);
       if (pos < L) {
         const int k = (pos >> h.block_shift) - b0;
         const int blk = k == 0 ? ids[0] : (k == 1 ? ids[1] : (k == 2 ? ids[2] : ids[3]));
         const int64_t off = int64_t(blk) * h.block_elems + int64_t(pos & bmask) * h.row_elems +
                             int64_t(h.g) * D + cc * 8;
-        nk[i] = *reinterpret_cast<const uint4*>(h.k_cache + off);
-        nv[i] = *reinterpret_cast<const uint4*>(h.v_cache + off);
+        nk[j][i] = *reinterpret_cast<const uint4*>(h.k_cache + off);
+        nv[j][i] = *reinterpret_cast<const uint4*>(h.v_cache + off);
       }
     }
   };
-  // Stage the fetched tile: K and V as [pos][d].
-  auto stage = [&]() {
+  // Stage the tile of buffer j: K and V as [pos][d].
+  auto stage = [&](int j) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int off = (pg * kPer + i) * kKStride + cc * 8;
-      *reinterpret_cast<uint4*>(k_lds + off) = nk[i];
-      *reinterpret_cast<uint4*>(v_lds + off) = nv[i];
+      *reinterpret_cast<uint4*>(k_lds + off) = nk[j][i];
+      *reinterpret_cast<uint4*>(v_lds + off) = nv[j][i];
     }
   };
   // This lane's V^T reads: row 4 (lane >> 4) + (lane & 15) / 4 (+ 16 for the
@@ -162,12 +169,8 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
   // each 16-wide d tile.
   const uint16_t* v_rd = v_lds + (4 * quad + ((lane & 15) >> 2)) * kKStride + 4 * (lane & 3);
 
-  if (t_lo < t_hi) fetch(t_lo);
-  for (int t0 = t_lo; t0 < t_hi; t0 += kKT) {
-    stage();
-    lds_barrier();
-    if (t0 + kKT < t_hi) fetch(t0 + kKT);  // in flight while this tile computes
-
+  // One staged tile's matrix work.
+  auto compute = [&](int t0) {
     // S^T tiles: positions 16pt + 4 quad + i of row (lane & 15).
     float sc[8];
     float tmax = -INFINITY;
@@ -227,7 +230,23 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfh, acc, 0, 0, 0);
       r.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfl, acc, 0, 0, 0);
     }
-    lds_barrier();  // every wave is done reading before the next stage
+  };
+
+#pragma unroll
+  for (int j = 0; j < PD; ++j)
+    if (t_lo + j * kKT < t_hi) fetch(j, t_lo + j * kKT);
+  for (int t0 = t_lo; t0 < t_hi; t0 += PD * kKT) {
+#pragma unroll
+    for (int j = 0; j < PD; ++j) {
+      const int t = t0 + j * kKT;
+      if (t >= t_hi) break;  // uniform
+      stage(j);
+      lds_barrier();
+      // the buffer just staged takes the tile PD ahead, in flight meanwhile
+      if (t + PD * kKT < t_hi) fetch(j, t + PD * kKT);
+      compute(t);
+      lds_barrier();  // every wave is done reading before the next stage
+    }
   }
 }
 

@@ -273,7 +273,7 @@ def copy_blocks_quant(pairs, k_cache, v_cache, k_scales=None, v_scales=None,
 def prefix_groups(block_tables, seq_lens, block_size: int):
     """Shared-prefix groups of a batch from host tables (see include/pkv.h,
     pkv_prefix_groups).  Returns (group_starts int32 [G+1], prefix_lens int32
-    [G], max_group_size, max_prefix_len)."""
+    [G], max_group_size, max_prefix_len, max_suffix_len)."""
     import numpy as np
     t = np.ascontiguousarray(block_tables, dtype=np.int32)
     L = np.ascontiguousarray(seq_lens, dtype=np.int32)
@@ -281,30 +281,31 @@ def prefix_groups(block_tables, seq_lens, block_size: int):
     mb = int(t.shape[1]) if t.ndim == 2 else 0
     starts = np.empty(n + 1, np.int32)
     plens = np.empty(max(n, 1), np.int32)
-    ng, mg, mp = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    ng, mg, mp, ms = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
     P = ctypes.POINTER(ctypes.c_int32)
     check(lib().pkv_prefix_groups(t.ctypes.data_as(P), n, mb, L.ctypes.data_as(P),
                                   int(block_size), starts.ctypes.data_as(P),
                                   plens.ctypes.data_as(P), ctypes.byref(ng), ctypes.byref(mg),
-                                  ctypes.byref(mp)), "pkv_prefix_groups")
-    return starts[:ng.value + 1].copy(), plens[:ng.value].copy(), mg.value, mp.value
+                                  ctypes.byref(mp), ctypes.byref(ms)), "pkv_prefix_groups")
+    return (starts[:ng.value + 1].copy(), plens[:ng.value].copy(), mg.value, mp.value,
+            ms.value)
 
 
 def shared_workspace_bytes(num_seqs, num_q_heads, num_groups, max_group_size, max_prefix_len,
-                           max_seq_len, k_cache) -> int:
+                           max_suffix_len, max_seq_len, k_cache) -> int:
     g = geom_of(k_cache)
     n = lib().pkv_attention_shared_workspace_bytes(int(num_seqs), int(num_q_heads),
                                                    int(num_groups), int(max_group_size),
-                                                   int(max_prefix_len), int(max_seq_len),
-                                                   ctypes.byref(g))
+                                                   int(max_prefix_len), int(max_suffix_len),
+                                                   int(max_seq_len), ctypes.byref(g))
     if n == ctypes.c_size_t(-1).value:
         check(1, "pkv_attention_shared_workspace_bytes")
     return int(n)
 
 
 def attention_decode_shared(q, k_cache, v_cache, block_tables, seq_lens, scale, group_starts,
-                            prefix_lens, max_group_size, max_prefix_len, out=None,
-                            max_seq_len=None, workspace=None, stream=None):
+                            prefix_lens, max_group_size, max_prefix_len, max_suffix_len=0,
+                            out=None, max_seq_len=None, workspace=None, stream=None):
     """Decode attention reading each group's shared prefix once (see
     include/pkv.h, pkv_attention_decode_shared).  group_starts / prefix_lens are
     int32 device tensors as pkv_prefix_groups returns them."""
@@ -326,14 +327,16 @@ def attention_decode_shared(q, k_cache, v_cache, block_tables, seq_lens, scale, 
         max_seq_len = max_blocks * g.block_size
     if out is None:
         out = torch.empty_like(q)
-    need = shared_workspace_bytes(N, Hq, ng, max_group_size, max_prefix_len, max_seq_len, k_cache)
+    need = shared_workspace_bytes(N, Hq, ng, max_group_size, max_prefix_len, max_suffix_len,
+                                  max_seq_len, k_cache)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
     check(lib().pkv_attention_decode_shared(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), max_blocks, _ptr(seq_lens),
         _ptr(group_starts), _ptr(prefix_lens), ng, int(max_group_size), int(max_prefix_len),
-        float(scale), _ptr(out), N, Hq, int(max_seq_len), _ptr(workspace), ws_bytes,
+        int(max_suffix_len), float(scale), _ptr(out), N, Hq, int(max_seq_len), _ptr(workspace),
+        ws_bytes,
         ctypes.byref(g), _stream(stream)), "pkv_attention_decode_shared")
     return out
 

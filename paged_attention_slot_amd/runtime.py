@@ -235,22 +235,22 @@ class DecodeStep:
         """Shared-prefix groups of the step's tables (pkv_prefix_groups), as
         device tensors plus their host bounds; computed once."""
         if getattr(self, "_groups", None) is None:
-            starts, plens, mg, mp = ops.prefix_groups(self.block_tables_h, self.seq_lens_h,
-                                                      self.wl.block_size)
+            starts, plens, mg, mp, ms = ops.prefix_groups(self.block_tables_h, self.seq_lens_h,
+                                                          self.wl.block_size)
             self._groups = (torch.from_numpy(starts).to(self.device),
-                            torch.from_numpy(plens).to(self.device), mg, mp)
+                            torch.from_numpy(plens).to(self.device), mg, mp, ms)
             n = ops.shared_workspace_bytes(self.wl.num_seqs, self.wl.num_q_heads, plens.size, mg,
-                                           mp, self.max_seq_len, self.k_caches[0])
+                                           mp, ms, self.max_seq_len, self.k_caches[0])
             self._shared_ws = torch.empty(max(n, 16), dtype=torch.uint8, device=self.device)
         return self._groups
 
     def attention_shared(self, layer=0, stream=None, out=None):
         """Decode attention reading each shared prefix once
         (pkv_attention_decode_shared); bf16 pools only."""
-        gs, pl, mg, mp = self.shared_groups()
+        gs, pl, mg, mp, ms = self.shared_groups()
         return ops.attention_decode_shared(
             self.q, self.k_caches[layer], self.v_caches[layer], self.block_tables, self.seq_lens,
-            self.wl.scale, gs, pl, mg, mp, out=self.out if out is None else out,
+            self.wl.scale, gs, pl, mg, mp, ms, out=self.out if out is None else out,
             max_seq_len=self.max_seq_len, workspace=self._shared_ws, stream=stream)
 
     @property

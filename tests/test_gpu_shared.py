@@ -6,8 +6,9 @@ Cases: the 176-sequence shared-prefix configuration (one group, 2048 shared
 tokens) in the launch configuration its measurement times; small families with
 prefixes ending inside a block, forks, several groups, group sizes beyond one
 row block, head dims 64/128, group sizes G of 1 to 16; hand-built tables where
-members are shorter than the shared blocks, empty sequences, and a grid bound
-(max_group_size) below a group's size.  Every case prints its shape first."""
+members are shorter than the shared blocks, empty sequences, a grid bound
+(max_group_size) below a group's size, and a suffix-length hint too small (the
+extra partitions are folded in).  Every case prints its shape first."""
 import numpy as np
 import pytest
 
@@ -40,8 +41,8 @@ def run_wl(wl, groups_expected=None):
     step = DecodeStep(wl)
     step.copy()
     step.write()
-    gs, pl, mg, mp = step.shared_groups()
-    say(f"  groups={pl.numel()} max_group={mg} max_prefix={mp}")
+    gs, pl, mg, mp, ms = step.shared_groups()
+    say(f"  groups={pl.numel()} max_group={mg} max_prefix={mp} max_suffix={ms}")
     if groups_expected is not None:
         assert (gs.cpu().tolist(), pl.cpu().tolist()) == groups_expected
     step.attention_shared()
@@ -105,22 +106,24 @@ def hand_case(tables, lens, Hq, Hkv, D, B, nb, seed):
 def test_members_shorter_than_the_shared_blocks_and_empty_sequences():
     """Sequences 0-2 hold the same three blocks with 40, 33 and 48 tokens (the
     shared prefix of 48 tokens is longer than two of them); sequence 3 is
-    empty; 4-5 share one block, then differ."""
+    empty; 4-5 share one block, then differ (sequence 4 has 74 positions
+    after it: more than one suffix partition of 64)."""
     from paged_attention_slot_amd.runtime import to_host_bits
     B = 16
-    tables = [[5, 7, 9, -1], [5, 7, 9, -1], [5, 7, 9, -1], [-1, -1, -1, -1],
-              [2, 3, 4, -1], [2, 6, -1, -1]]
-    lens = [40, 33, 48, 0, 40, 20]
+    tables = [[5, 7, 9, -1, -1, -1]] * 3 + [[-1] * 6, [2, 3, 4, 8, 10, 11],
+                                            [2, 6, -1, -1, -1, -1]]
+    lens = [40, 33, 48, 0, 90, 20]
     ops, (q, kp, vp, tb, ln), ref = hand_case(tables, lens, 8, 2, 128, B, 12, 11)
-    starts, plens, mg, mp = ops.prefix_groups(np.asarray(tables, np.int32),
-                                              np.asarray(lens, np.int32), B)
-    assert starts.tolist() == [0, 3, 4, 6] and plens.tolist() == [48, 0, 16]
-    for bound, name in ((mg, "grid fits"), (1, "groups beyond the grid share nothing")):
-        say(f"  hand case: max_group_size={bound} ({name})")
+    starts, plens, mg, mp, ms = ops.prefix_groups(np.asarray(tables, np.int32),
+                                                  np.asarray(lens, np.int32), B)
+    assert starts.tolist() == [0, 3, 4, 6] and plens.tolist() == [48, 0, 16] and ms == 74
+    for bound, hint, name in ((mg, ms, "grid fits"), (1, ms, "groups beyond the grid share nothing"),
+                              (mg, 1, "suffix hint too small: extra partitions folded in")):
+        say(f"  hand case: max_group_size={bound} max_suffix_len={hint} ({name})")
         out = ops.attention_decode_shared(q, kp, vp, tb, ln, 1 / np.sqrt(128),
                                           torch.from_numpy(starts).cuda(),
-                                          torch.from_numpy(plens).cuda(), bound, mp,
-                                          max_seq_len=48)
+                                          torch.from_numpy(plens).cuda(), bound, mp, hint,
+                                          max_seq_len=96)
         torch.cuda.synchronize()
         got = to_f64(to_host_bits(out))
         assert_gate(got, ref, "bf16", name)

@@ -18,8 +18,10 @@ from paged_attention_slot_amd._lib import PkvGeom  # noqa: E402
 
 def same(tables, lens, B):
     s0, p0 = oracle_groups(tables, lens, B)
-    s1, p1, mg, mp = ops.prefix_groups(tables, lens, B)
+    s1, p1, mg, mp, ms = ops.prefix_groups(tables, lens, B)
     assert np.array_equal(s0, s1) and np.array_equal(p0, p1)
+    pre = np.repeat(np.where(np.diff(s0) >= 2, p0, 0), np.diff(s0))   # each sequence's prefix
+    assert ms == (int(np.max(lens - np.minimum(pre, lens))) if lens.size else 0)
     assert mg == (int(np.diff(s0).max()) if lens.size else 0)
     assert mp == (int(p0.max()) if p0.size else 0)
 
@@ -64,8 +66,8 @@ def test_shared_attention_validates_on_the_host():
     g = PkvGeom(16, 16, 2, 128, _lib.PKV_BF16)
 
     def call(geo=g, ng=1, mg=4, mp=32, N=4, ws=x, wsb=1 << 30, scale=0.1, q=x):
-        return lib.pkv_attention_decode_shared(q, x, x, x, 8, x, x, x, ng, mg, mp, scale, x, N, 4,
-                                               128, ws, wsb, ctypes.byref(geo), None)
+        return lib.pkv_attention_decode_shared(q, x, x, x, 8, x, x, x, ng, mg, mp, 0, scale, x, N,
+                                               4, 128, ws, wsb, ctypes.byref(geo), None)
     assert call(geo=PkvGeom(16, 16, 2, 128, _lib.PKV_F32)) == _lib.PKV_ERR_UNSUPPORTED
     assert call(geo=PkvGeom(16, 4, 2, 128, _lib.PKV_BF16)) == _lib.PKV_ERR_UNSUPPORTED
     assert call(geo=PkvGeom(16, 16, 2, 96, _lib.PKV_BF16)) == _lib.PKV_ERR_UNSUPPORTED
@@ -77,11 +79,11 @@ def test_shared_attention_validates_on_the_host():
     assert call(wsb=16) == _lib.PKV_ERR_INVALID_ARG
     assert call(q=ctypes.c_void_p(0x1004)) == _lib.PKV_ERR_INVALID_ARG
     assert call(N=0, ng=0) == _lib.PKV_OK                     # empty batch: nothing enqueued
-    need = lib.pkv_attention_shared_workspace_bytes(4, 4, 1, 4, 32, 128, ctypes.byref(g))
+    need = lib.pkv_attention_shared_workspace_bytes(4, 4, 1, 4, 32, 0, 128, ctypes.byref(g))
     assert 0 < need < (1 << 30)
     n = ctypes.c_int32()
-    assert lib.pkv_prefix_groups(None, 2, 4, None, 16, None, None, None, None, None) == \
+    assert lib.pkv_prefix_groups(None, 2, 4, None, 16, None, None, None, None, None, None) == \
         _lib.PKV_ERR_INVALID_ARG
     out = (ctypes.c_int32 * 8)()
-    assert lib.pkv_prefix_groups(None, 0, 0, None, 16, out, out, ctypes.byref(n), out, out) == \
-        _lib.PKV_OK and n.value == 0
+    assert lib.pkv_prefix_groups(None, 0, 0, None, 16, out, out, ctypes.byref(n), out, out,
+                                 out) == _lib.PKV_OK and n.value == 0
