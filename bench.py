@@ -13,7 +13,10 @@ sequence, then pkv_attention_decode (partition kernel, then the split-KV merge).
 Inputs are resident in HBM before the timed region.  ``--layers`` pool pairs
 with identical block tables are cycled, one per step, so that consecutive steps
 read different memory (as a model's layers do) and no step is served from the
-previous step's cached lines.  Prints one JSON line.
+previous step's cached lines.  The timed steps replay each layer's step as a
+HIP graph captured once (``--no-graph``: eager launches); the attention
+kernel's own duration comes from an eager pass with HIP events around it.
+Prints one JSON line.
 
 ``--path multi`` times pkv_attention_multi instead: n new query tokens per
 sequence of the configuration (tokens to verify, or a prefill chunk), each
@@ -504,6 +507,9 @@ def main() -> int:
     ap.add_argument("--partition-tokens", type=int, default=None)
     ap.add_argument("--kv-dtype", default="model", choices=["model", "fp8_e4m3", "int8"],
                     help="cache element type: the workload's (default) or one-byte codes")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="decode path: time eager launches instead of replaying the step as a "
+                         "HIP graph")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
@@ -561,6 +567,8 @@ def main() -> int:
         step.step(i % L)
     torch.cuda.synchronize()
 
+    # Kernel durations: eager launches with HIP events around each phase on
+    # the launch stream.
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -576,7 +584,27 @@ def main() -> int:
         step.attention(layer, phases=2)
         e3.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
+    eager_wall = time.perf_counter() - t_start
+    wall = eager_wall
+    graph_wall = None
+    if not args.no_graph:
+        # The step (copy -> write -> attention + merge) of each layer captured
+        # once as a HIP graph and replayed: launches cost no host time.
+        graphs = []
+        for layer in range(L):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step.step(layer)
+            graphs.append(g)
+        for i in range(W):
+            graphs[i % L].replay()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for i in range(K):
+            graphs[i % L].replay()
+        torch.cuda.synchronize()
+        graph_wall = time.perf_counter() - t_start
+        wall = graph_wall
 
     cw = np.array([a.elapsed_time(b) for a, b, _, _ in ev]) * 1e-3
     part = np.array([b.elapsed_time(c) for _, b, c, _ in ev]) * 1e-3
@@ -642,6 +670,9 @@ def main() -> int:
             "merge_us_mean": float(np.mean(merge)) * 1e6,
             "copy_write_us_mean": float(np.mean(cw)) * 1e6,
             "device_step_us_mean": float(np.mean(dev_step)) * 1e6,
+            "step_timing": "hip graph replay" if graph_wall is not None else "eager launches",
+            "eager_ms_per_step": eager_wall / K * 1e3,
+            "graph_ms_per_step": None if graph_wall is None else graph_wall / K * 1e3,
             "write_bytes": (write_bytes(N, wl.num_kv_heads, wl.head_dim, e) if not quant else
                             N * wl.num_kv_heads * wl.head_dim * 2 * (qe + e)),
             "copy_bytes": copy_bytes(n_cow, wl.block_size, wl.num_kv_heads, wl.head_dim, e),
