@@ -40,6 +40,13 @@ template <int D> constexpr int k_lds_elems() { return kKT * (D + 8); }
 template <int D> constexpr int v_lds_elems() { return kKT * (D + 8); }
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2v_t));
+}
 
 // ds_read_b64_tr_b16 (lane layout checked with a one-wave probe): within each
 // group of 16 lanes, lane j receives element j % 4 of the 8-byte words that
@@ -203,16 +210,12 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
     float psum = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      uint32_t h2[2], l2[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float p = fast_exp2(sc[2 * k + e] - mn);
-        psum += p;
-        h2[e] = f32_to_bf16_bits(p);
-        l2[e] = f32_to_bf16_bits(p - __uint_as_float(h2[e] << 16));
-      }
-      ph[k] = h2[0] | (h2[1] << 16);
-      pl[k] = l2[0] | (l2[1] << 16);
+      const float p0 = fast_exp2(sc[2 * k] - mn);
+      const float p1 = fast_exp2(sc[2 * k + 1] - mn);
+      psum += p0 + p1;
+      const uint32_t h = cvt_pk_bf16(p0, p1);
+      ph[k] = h;
+      pl[k] = cvt_pk_bf16(p0 - __uint_as_float(h << 16), p1 - __uint_as_float(h & 0xFFFF0000u));
     }
     psum = sum_across_rows16(psum);
     r.lsum = r.lsum * alpha + psum;
