@@ -207,8 +207,9 @@ def bench_multi(args) -> int:
     q = torch.from_numpy(qh.view(np.int16)).to(dev).view(torch.bfloat16)
     qo = torch.from_numpy(offs).to(dev)
     out = torch.empty_like(q)
+    pt = int(args.partition_tokens or 0)
     need = lib().pkv_attention_multi_workspace_bytes(
-        N, Hq, total, n, int(lens.max()), 0, ctypes.byref(ops.geom_of(step.k_cache)))
+        N, Hq, total, n, int(lens.max()), pt, ctypes.byref(ops.geom_of(step.k_cache)))
     ws = torch.empty(max(int(need), 16), dtype=torch.uint8, device=dev)
     e = wl.elem_bytes
     # algorithmic bytes: every cached position's K and V read once, q read,
@@ -228,7 +229,7 @@ def bench_multi(args) -> int:
         rec(0)
         ops.attention_multi(q, qo, step.k_caches[i % L_], step.v_caches[i % L_],
                             step.block_tables, step.seq_lens, wl.scale, n, out=out,
-                            max_seq_len=step.max_seq_len, workspace=ws)
+                            max_seq_len=step.max_seq_len, partition_tokens=pt, workspace=ws)
         rec(1)
     t_step, iv = _timed(run, args.steps, args.warmup, 2)
     t_k = float(np.mean(iv[:, 0]))
@@ -245,6 +246,7 @@ def bench_multi(args) -> int:
             "note": "event time covers the main kernel and the partition merge"}
     roof["traffic"] = recorded_traffic("attn_multi_kernel", name)
     config = {"workload": name, "num_seqs": N, "query_tokens_per_seq": n, "total_queries": total,
+              "partition_tokens": pt or "automatic",
               "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "block_size": wl.block_size,
               "sum_seq_lens": int(lens.sum()), "max_seq_len": int(lens.max()),
               "layers_cycled": L_, "seed": wl.seed}

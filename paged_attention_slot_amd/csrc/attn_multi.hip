@@ -50,6 +50,8 @@ struct MultiArgs {
   int32_t block_shift;
   int32_t len_cap;
   int32_t q_per_block;
+  int32_t num_qblocks;
+  int32_t num_kv_heads;
   int32_t num_parts;
   int32_t part_tokens;
   float scale_log2;
@@ -63,8 +65,19 @@ attn_multi_kernel(MultiArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(tid >> 6));
-  const int s = blockIdx.z, g = blockIdx.y;
-  const int qb = blockIdx.x / a.num_parts, part = blockIdx.x - qb * a.num_parts;
+  // grid = (query blocks * H_kv * sequences, partitions).  Workgroups go to
+  // the XCDs round robin in launch order, so the XCD of (x, part) follows x.
+  // Rotating the item by the partition (item = x + part) spreads both every
+  // partition over all XCDs and the partitions of one item (one long history)
+  // over different XCDs; partition-fastest order put all of partition p on
+  // one XCD whenever the partition count divides 8.
+  const int qbs = a.num_qblocks;
+  const int items = qbs * a.num_kv_heads * static_cast<int>(gridDim.x / (qbs * a.num_kv_heads));
+  const int part = blockIdx.y;
+  const int item = static_cast<int>((blockIdx.x + uint32_t(part)) % uint32_t(items));
+  const int qb = item % qbs;
+  const int g = (item / qbs) % a.num_kv_heads;
+  const int s = item / (qbs * a.num_kv_heads);
   const int q0 = a.q_offsets[s];
   const int n = a.q_offsets[s + 1] - q0;
   const int j0 = qb * a.q_per_block;
@@ -176,17 +189,18 @@ pkv_status multi_plan(int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
   if (partition_tokens > 0) {
     pl->part_tokens = partition_tokens;
   } else {
-    // Enough workgroups to fill the GPU: split long histories when the
-    // (block, head, sequence) items alone are few; partitions stay >= 256.
+    // Enough workgroups to fill the GPU: split long histories into about
+    // 3072 workgroups when the (block, head, sequence) items alone are fewer
+    // than 2048; partitions stay >= 256.
     const int64_t items = int64_t(num_seqs) * g->num_kv_heads * pl->qblocks;
-    int64_t parts = items >= 2048 ? 1 : (2048 + items - 1) / (items > 0 ? items : 1);
+    int64_t parts = items >= 2048 ? 1 : (3072 + items - 1) / (items > 0 ? items : 1);
     int64_t pt = round_up_to((len + parts - 1) / parts, kKT);
     if (pt < 256) pt = 256;
     pl->part_tokens = static_cast<int>(pt < round_up_to(len, kKT) ? pt : round_up_to(len, kKT));
   }
   const int64_t np = (int64_t(len) + pl->part_tokens - 1) / pl->part_tokens;
-  if (np * pl->qblocks > 2147483647LL)
-    return pkv::fail(PKV_ERR_INVALID_ARG, "%s: too many partitions", who);
+  if (np > 65535 || int64_t(pl->qblocks) * g->num_kv_heads * num_seqs > 2147483647LL)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "%s: too many partitions or query blocks", who);
   pl->num_parts = static_cast<int>(np);
   if (pl->num_parts > 1) {
     const size_t rowsq = size_t(total_q) * num_q_heads;
@@ -202,7 +216,7 @@ pkv_status multi_plan(int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
 template <int D>
 void launch_multi(const MultiPlan& pl, const MultiArgs& a, int num_seqs, int num_kv_heads,
                   int total_q, hipStream_t st) {
-  const dim3 grid(pl.qblocks * pl.num_parts, num_kv_heads, num_seqs);
+  const dim3 grid(pl.qblocks * num_kv_heads * num_seqs, pl.num_parts);
   switch (pl.nw) {
     case 1: hipLaunchKernelGGL((attn_multi_kernel<D, 1>), grid, dim3(64), 0, st, a); break;
     case 2: hipLaunchKernelGGL((attn_multi_kernel<D, 2>), grid, dim3(128), 0, st, a); break;
@@ -279,6 +293,8 @@ pkv_status pkv_attention_multi(const void* q, const int32_t* q_offsets, const vo
   const int64_t cap = int64_t(max_blocks_per_seq) * geom->block_size;
   a.len_cap = static_cast<int32_t>(max_seq_len < cap ? max_seq_len : cap);
   a.q_per_block = pl.q_per_block;
+  a.num_qblocks = pl.qblocks;
+  a.num_kv_heads = geom->num_kv_heads;
   a.num_parts = pl.num_parts;
   a.part_tokens = pl.part_tokens;
   a.scale_log2 = static_cast<float>(double(scale) * 1.4426950408889634);
