@@ -103,8 +103,9 @@ attn_multi_kernel(MultiArgs a) {
                                 L, g, a.block_elems, a.row_elems, a.num_blocks, a.block_shift};
   pkv::mfma::RowAcc<D> r;
   pkv::mfma::start(r);
+  // every row of the block sees the positions up to its first query's
   pkv::mfma::attend<D, NW, (NW >= 2 ? 2 : 1)>(hist, t_lo, t_hi, a.q + qh * D, row_ok, p_row,
-                                             a.scale_log2, k_lds, v_lds, r);
+                                             p_first, a.scale_log2, k_lds, v_lds, r);
 
   if (!row_ok) return;
   if (a.num_parts == 1) {

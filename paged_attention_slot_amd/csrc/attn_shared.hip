@@ -127,10 +127,15 @@ attn_prefix_kernel(SharedArgs a) {
   // The prefix is read through the group's first member's table.
   const pkv::mfma::History hist{a.k_cache, a.v_cache, a.block_tables + int64_t(first) * a.max_blocks,
                                 P, g, a.block_elems, a.row_elems, a.num_blocks, a.block_shift};
+  // Positions every member of the block sees: up to the shortest one's last
+  // (one member's length per lane, then a wave minimum: one round trip).
+  int lmin = lane < jn ? clamp_len(a.seq_lens[first + j0 + lane], a.len_cap) : a.len_cap;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) lmin = min(lmin, __shfl_xor(lmin, off));
   pkv::mfma::RowAcc<D> r;
   pkv::mfma::start(r);
   pkv::mfma::attend<D, NW, (NW >= 2 ? 2 : 1)>(hist, t_lo, t_hi, a.q + qh * D, row_ok, L - 1,
-                                             a.scale_log2, k_lds, v_lds, r);
+                                             lmin - 1, a.scale_log2, k_lds, v_lds, r);
   if (!row_ok) return;
   const int64_t slot = qh * (a.pre_parts + a.suf_parts) + part;
   pkv::mfma::store_piece<D>(r, a.ws_acc + slot * D, a.ws_ml + slot);
@@ -161,8 +166,8 @@ attn_suffix_kernel(SharedArgs a) {
   // sized for is folded into the same piece.
   for (int t_lo = P + part * a.suf_tokens; t_lo < L; t_lo += a.suf_parts * a.suf_tokens)
     pkv::mfma::attend<D, NW, (NW >= 2 ? 2 : 1)>(hist, t_lo, min(t_lo + a.suf_tokens, L),
-                                               a.q + qh * D, row_ok, L - 1, a.scale_log2, k_lds,
-                                               v_lds, r);
+                                               a.q + qh * D, row_ok, L - 1, L - 1, a.scale_log2,
+                                               k_lds, v_lds, r);
   if (!row_ok) return;
   const int64_t slot = qh * (a.pre_parts + a.suf_parts) + a.pre_parts + part;
   pkv::mfma::store_piece<D>(r, a.ws_acc + slot * D, a.ws_ml + slot);

@@ -103,12 +103,24 @@ __device__ __forceinline__ void start(RowAcc<D>& r) {
 // (every wave must call this with the same range), folding them into ``r``
 // (start() it first; further calls continue the same online softmax).
 // ``q`` points at this lane's query row (D bf16, 16-byte aligned); it is read
-// only if row_ok.  PD tiles are in flight ahead of the one being computed
-// (PD register buffers of K/V per thread).
+// only if row_ok.  p_all (the same in every lane) is a position every live
+// row of the workgroup sees: tiles entirely at or before it, and inside
+// [t_lo, t_hi), skip the per-score mask.  t_lo must be a multiple of 8 (a
+// lane's positions of a tile then lie in one block).  PD tiles are in flight
+// ahead of the one being computed (PD register buffers of K/V per thread).
+//
+// With one wave (latency-bound, few rows) the reference m of a row moves
+// lazily: only when some row of the wave sees a score more than kSlack (log2
+// units) above its reference is the state rescaled, so weights stay <=
+// 2^kSlack and most tiles skip the rescale.  With more waves (matrix-bound)
+// every tile rescales: the branch would keep the compiler from interleaving
+// the tile's matrix work with its softmax (measured 20 % slower).
 template <int D, int NW, int PD = 1>
 __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, const uint16_t* q,
-                                       bool row_ok, int p_row, float scale_log2,
+                                       bool row_ok, int p_row, int p_all, float scale_log2,
                                        uint16_t* k_lds, uint16_t* v_lds, RowAcc<D>& r) {
+  constexpr float kSlack = 8.0f;
+  constexpr bool kLazy = NW == 1;
   constexpr int kKS = D / 32;            // k-steps of the score product
   constexpr int kDT = D / 16;            // 16-wide d tiles of the output
   constexpr int kKStride = D + 8;        // K and V rows in LDS, bf16 elements (16 B pad)
@@ -147,18 +159,30 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
       const int b = idx <= last_idx ? h.trow[idx] : 0;
       ids[k] = (b >= 0 && b < h.num_blocks) ? b : 0;
     }
+    // This lane's kPer positions p0 .. p0 + kPer - 1 lie in one block (t0 is
+    // a multiple of 8, kPer divides 8 and the block size).
+    const int p0 = t0 + pg * kPer;
+    const int k = (p0 >> h.block_shift) - b0;
+    const int blk = k == 0 ? ids[0] : (k == 1 ? ids[1] : (k == 2 ? ids[2] : ids[3]));
+    const int64_t off0 = int64_t(blk) * h.block_elems + int64_t(p0 & bmask) * h.row_elems +
+                         int64_t(h.g) * D + cc * 8;
+    const uint16_t* kb = h.k_cache + off0;
+    const uint16_t* vb = h.v_cache + off0;
+    if (t0 + kKT <= L) {  // uniform: the whole tile is history
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int pos = t0 + pg * kPer + i;
-      nk[j][i] = make_uint4(0, 0, 0, 0);
-      nv[j][i] = make_uint4(0, 0, 0, 0);
-      if (pos < L) {
-        const int k = (pos >> h.block_shift) - b0;
-        const int blk = k == 0 ? ids[0] : (k == 1 ? ids[1] : (k == 2 ? ids[2] : ids[3]));
-        const int64_t off = int64_t(blk) * h.block_elems + int64_t(pos & bmask) * h.row_elems +
-                            int64_t(h.g) * D + cc * 8;
-        nk[j][i] = *reinterpret_cast<const uint4*>(h.k_cache + off);
-        nv[j][i] = *reinterpret_cast<const uint4*>(h.v_cache + off);
+      for (int i = 0; i < kPer; ++i) {
+        nk[j][i] = *reinterpret_cast<const uint4*>(kb + i * h.row_elems);
+        nv[j][i] = *reinterpret_cast<const uint4*>(vb + i * h.row_elems);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        nk[j][i] = make_uint4(0, 0, 0, 0);
+        nv[j][i] = make_uint4(0, 0, 0, 0);
+        if (p0 + i < L) {
+          nk[j][i] = *reinterpret_cast<const uint4*>(kb + i * h.row_elems);
+          nv[j][i] = *reinterpret_cast<const uint4*>(vb + i * h.row_elems);
+        }
       }
     }
   };
@@ -178,6 +202,8 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
 
   // One staged tile's matrix work.
   auto compute = [&](int t0) {
+    // Uniform: every live row sees every position of the tile.
+    const bool full = t0 + kKT - 1 <= p_all && t0 + kKT <= t_hi;
     // S^T tiles: positions 16pt + 4 quad + i of row (lane & 15).
     float sc[8];
     float tmax = -INFINITY;
@@ -193,32 +219,42 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 16 * pt + 4 * quad + i;
-        const bool ok = row_ok && t <= p_row && t < t_hi;
-        const float v = ok ? acc[i] * scale_log2 : -INFINITY;
+        float v = acc[i] * scale_log2;
+        if (!full) {
+          const int t = t0 + 16 * pt + 4 * quad + i;
+          v = (row_ok && t <= p_row && t < t_hi) ? v : -INFINITY;
+        }
         sc[4 * pt + i] = v;
         tmax = fmaxf(tmax, v);
       }
     }
     tmax = max_across_rows16(tmax);
-    const float mn = fmaxf(r.m, tmax);
-    const float alpha = fast_exp2(r.m - mn);
-    r.m = mn;
+    if (!kLazy || __builtin_amdgcn_ballot_w64(tmax > r.m + kSlack) != 0) {  // uniform
+      const float mn = fmaxf(r.m, tmax);
+      const float alpha = fast_exp2(r.m - mn);
+      r.m = mn;
+      r.lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.o[dt][i] *= alpha;
+    }
+    const float mref = r.m;
     // Weights as two bf16 terms, p = hi + lo (hi = bf16(p), lo = bf16(p - hi)):
     // P V then carries p to about 2^-17 relative, like the fp32 sum.
     uint32_t ph[4], pl[4];
     float psum = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float p0 = fast_exp2(sc[2 * k] - mn);
-      const float p1 = fast_exp2(sc[2 * k + 1] - mn);
+      const float p0 = fast_exp2(sc[2 * k] - mref);
+      const float p1 = fast_exp2(sc[2 * k + 1] - mref);
       psum += p0 + p1;
       const uint32_t h = cvt_pk_bf16(p0, p1);
       ph[k] = h;
       pl[k] = cvt_pk_bf16(p0 - __uint_as_float(h << 16), p1 - __uint_as_float(h & 0xFFFF0000u));
     }
     psum = sum_across_rows16(psum);
-    r.lsum = r.lsum * alpha + psum;
+    r.lsum += psum;
     const bf16x8_t pfh = as_bf16x8(make_uint4(ph[0], ph[1], ph[2], ph[3]));
     const bf16x8_t pfl = as_bf16x8(make_uint4(pl[0], pl[1], pl[2], pl[3]));
 #pragma unroll
@@ -226,14 +262,10 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
       // V^T[16 dt + (lane & 15)][positions 4 quad .. + 3 and 16 + 4 quad .. + 3]
       const uint2 lo = lds_read_tr16(v_rd + 16 * dt);
       const uint2 hi = lds_read_tr16(v_rd + 16 * kKStride + 16 * dt);
-      f32x4_t acc = r.o[dt];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] *= alpha;
       const bf16x8_t va = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfh, acc, 0, 0, 0);
+      f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfh, r.o[dt], 0, 0, 0);
       r.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfl, acc, 0, 0, 0);
-    }
-  };
+    }  };
 
 #pragma unroll
   for (int j = 0; j < PD; ++j)
