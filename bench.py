@@ -189,9 +189,10 @@ def bench_multi(args) -> int:
     from workloads import config_workload, multi_queries
 
     n = int(args.query_tokens)
+    quant = args.kv_dtype != "model"
     t0 = time.perf_counter()
     wl = config_workload(args.config)
-    step = DecodeStep(wl, layers=args.layers)
+    step = DecodeStep(wl, layers=args.layers, kv_dtype=args.kv_dtype if quant else None)
     for layer in range(args.layers):       # the decode token completes every history
         step.copy(layer)
         step.write(layer)
@@ -211,10 +212,11 @@ def bench_multi(args) -> int:
     need = lib().pkv_attention_multi_workspace_bytes(
         N, Hq, total, n, int(lens.max()), pt, ctypes.byref(ops.geom_of(step.k_cache)))
     ws = torch.empty(max(int(need), 16), dtype=torch.uint8, device=dev)
+    e = 1 if quant else wl.elem_bytes
+    # algorithmic bytes: every cached position's K and V read once (INT8: and
+    # its two scales), q read, out written, table entries and lengths read
+    kv_bytes = int(lens.sum()) * (2 * Hkv * D * e + (8 * Hkv if args.kv_dtype == "int8" else 0))
     e = wl.elem_bytes
-    # algorithmic bytes: every cached position's K and V read once, q read,
-    # out written, table entries and lengths read
-    kv_bytes = int(lens.sum()) * 2 * Hkv * D * e
     io_bytes = 2 * total * Hq * D * e + 4 * int(((lens + wl.block_size - 1)
                                                  // wl.block_size).sum()) + 8 * N
     alg_bytes = kv_bytes + io_bytes
@@ -226,17 +228,20 @@ def bench_multi(args) -> int:
     L_ = args.layers
 
     def run(i, rec):
+        ks, vs = step._scales(i % L_)
         rec(0)
         ops.attention_multi(q, qo, step.k_caches[i % L_], step.v_caches[i % L_],
                             step.block_tables, step.seq_lens, wl.scale, n, out=out,
-                            max_seq_len=step.max_seq_len, partition_tokens=pt, workspace=ws)
+                            max_seq_len=step.max_seq_len, partition_tokens=pt, workspace=ws,
+                            k_scale=step.k_scale, v_scale=step.v_scale, k_scales=ks,
+                            v_scales=vs)
         rec(1)
     t_step, iv = _timed(run, args.steps, args.warmup, 2)
     t_k = float(np.mean(iv[:, 0]))
     mfma = flops / alg_bytes > ridge
     achieved = (flops / t_k / 1e12) if mfma else (alg_bytes / t_k / 1e9)
     peak = MFMA_BF16_PEAK_TFLOPS if mfma else HBM_PEAK_GBPS
-    name = f"{wl.name}+multi{n}"
+    name = f"{wl.name}+multi{n}" + (f"+{args.kv_dtype}" if quant else "")
     roof = {"bound": "mfma" if mfma else "hbm", "kernel": "attn_multi_kernel",
             "achieved": achieved, "peak": peak, "unit": "TFLOP/s" if mfma else "GB/s",
             "frac": achieved / peak, "traffic": None,
@@ -255,8 +260,8 @@ def bench_multi(args) -> int:
               "input_generation_s": gen_s, "workspace_bytes": int(need)}
     res = _common(args, wl, "paged multi-token attention GB/s of K/V (new query tokens per "
                   "sequence over the cached history)", alg_bytes / t_step / 1e9, "GB/s", t_step,
-                  wl.dtype, config, roof, detail)
-    if not args.no_cpu_baseline:
+                  args.kv_dtype if quant else wl.dtype, config, roof, detail)
+    if not args.no_cpu_baseline and not quant:
         res["cpu_baseline"] = multi_cpu_baseline(wl, step, qh, offs, args.cpu_budget)
     print(json.dumps(res), flush=True)
     return 0
@@ -303,18 +308,20 @@ def bench_shared(args) -> int:
     from paged_attention_slot_amd.runtime import DecodeStep
     from workloads import config_workload
 
+    quant = args.kv_dtype != "model"
     t0 = time.perf_counter()
     wl = config_workload(args.config)
     gen_s = time.perf_counter() - t0
     if wl.dtype != "bf16":
-        raise SystemExit("bench.py --path shared: the shared-prefix kernels take bf16 caches")
-    step = DecodeStep(wl, layers=args.layers)
+        raise SystemExit("bench.py --path shared: the shared-prefix kernels take bf16 workloads")
+    step = DecodeStep(wl, layers=args.layers, kv_dtype=args.kv_dtype if quant else None)
     for layer in range(args.layers):
         step.copy(layer)
         step.write(layer)
     gs, pl, mg, mp, ms = step.shared_groups()
     lens = wl.seq_lens.astype(np.int64)
-    per_pos = 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
+    per_pos = (2 * wl.num_kv_heads * wl.head_dim * (1 if quant else wl.elem_bytes) +
+               (8 * wl.num_kv_heads if args.kv_dtype == "int8" else 0))
     logical = int(lens.sum()) * per_pos
     # unique positions: distinct (block, offset) slots the batch attends
     B = wl.block_size
@@ -368,8 +375,9 @@ def bench_shared(args) -> int:
                     "exceed the HBM peak because each group's prefix is read once per block "
                     "of member rows; detail.unique_gbps counts every distinct cached "
                     "position once"}
-    roof["traffic"] = recorded_traffic("attn_shared", f"{wl.name}+shared")
-    config = {"workload": f"{wl.name}+shared", "num_seqs": wl.num_seqs,
+    roof["traffic"] = recorded_traffic("attn_shared", sname)
+    sname = f"{wl.name}+shared" + (f"+{args.kv_dtype}" if quant else "")
+    config = {"workload": sname, "num_seqs": wl.num_seqs,
               "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
               "head_dim": wl.head_dim, "block_size": B, "groups": int(plens.size),
               "max_group_size": int(mg), "max_prefix_len": int(mp), "max_suffix_len": int(ms),
@@ -382,9 +390,9 @@ def bench_shared(args) -> int:
               "plain_decode_logical_gbps": logical / t_plain / 1e9,
               "input_generation_s": gen_s}
     res = _common(args, wl, "paged decode attention KV-read GB/s, logical (shared prefix read "
-                  "once per group)", logical / t_step / 1e9, "GB/s", t_step, wl.dtype, config,
-                  roof, detail)
-    if not args.no_cpu_baseline:
+                  "once per group)", logical / t_step / 1e9, "GB/s", t_step,
+                  args.kv_dtype if quant else wl.dtype, config, roof, detail)
+    if not args.no_cpu_baseline and not quant:
         cb = cpu_baseline(wl, args.cpu_budget)
         res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
     print(json.dumps(res), flush=True)

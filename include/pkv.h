@@ -197,6 +197,17 @@ pkv_status pkv_attention_decode_shared(const void* q, const void* k_cache, const
                                        void* workspace, size_t workspace_bytes,
                                        const pkv_geom* geom, void* stream);
 
+/* pkv_attention_decode_shared_quant -- the same over an FP8 e4m3 or INT8 cache
+ * (scales as pkv_kv_scales; head_dim 128); codes decoded exactly, scales
+ * applied to scores and weights.  Workspace as for the bf16 call. */
+pkv_status pkv_attention_decode_shared_quant(
+    const void* q, const void* k_cache, const void* v_cache, const pkv_kv_scales* scales,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+    const int32_t* group_starts, const int32_t* prefix_lens, int32_t num_groups,
+    int32_t max_group_size, int32_t max_prefix_len, int32_t max_suffix_len, float scale,
+    void* out, int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len, void* workspace,
+    size_t workspace_bytes, const pkv_geom* geom, void* stream);
+
 /* pkv_prefix_groups -- groups of a batch, from its host block tables [num_seqs]
  * [max_blocks] and lengths: maximal runs of consecutive sequences whose first
  * valid entry is the same block; a group's prefix is the longest run of leading
@@ -373,6 +384,22 @@ pkv_status pkv_attention_multi(const void* q, const int32_t* q_offsets, const vo
                                int32_t max_q_per_seq, int32_t max_seq_len,
                                int32_t partition_tokens, void* workspace,
                                size_t workspace_bytes, const pkv_geom* geom, void* stream);
+
+/* pkv_attention_multi_quant -- pkv_attention_multi over an FP8 e4m3 or INT8
+ * cache (scales as described with pkv_kv_scales; head_dim 128): the codes are
+ * decoded exactly when tiles are staged and the scales applied to the scores
+ * (K) and weights (V), so the result is the attention over the dequantized
+ * values; q and out stay bf16.  Workspace: pkv_attention_multi_workspace_bytes
+ * with the quantized geometry.  Errors as pkv_attention_multi, INVALID_ARG
+ * for a non-quantized dtype or missing scales. */
+pkv_status pkv_attention_multi_quant(const void* q, const int32_t* q_offsets, const void* k_cache,
+                                     const void* v_cache, const pkv_kv_scales* scales,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* seq_lens, float scale, void* out,
+                                     int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
+                                     int32_t max_q_per_seq, int32_t max_seq_len,
+                                     int32_t partition_tokens, void* workspace,
+                                     size_t workspace_bytes, const pkv_geom* geom, void* stream);
 
 /* Tuning knobs of pkv_attention_decode, read from the environment at each
  * call (unset or out of range = the library's heuristic):

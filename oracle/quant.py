@@ -156,3 +156,13 @@ def attention_decode_quant(q_bf16, k_pool, v_pool, block_tables, seq_lens, scale
     kd = dequantize_pool(k_pool, kind, k_scale, k_scales)
     vd = dequantize_pool(v_pool, kind, v_scale, v_scales)
     return attention_decode(q_bf16, kd, vd, block_tables, seq_lens, scale, seqs=seqs)
+
+
+def attention_multi_quant(q_bf16, q_offsets, k_pool, v_pool, block_tables, seq_lens, scale, kind,
+                          k_scale=1.0, v_scale=1.0, k_scales=None, v_scales=None):
+    """Multi-token query attention over a quantized cache: the definition of
+    oracle.attention.attention_multi applied to the dequantized pools."""
+    from .attention import attention_multi
+    kd = dequantize_pool(k_pool, kind, k_scale, k_scales)
+    vd = dequantize_pool(v_pool, kind, v_scale, v_scales)
+    return attention_multi(q_bf16, q_offsets, kd, vd, block_tables, seq_lens, scale)

@@ -96,6 +96,17 @@ SIGNATURES = {
                                             c_void_p, c_size, ctypes.POINTER(PkvGeom), c_void_p]),
     "pkv_prefix_groups": (c_i32, [P_i32, c_i32, c_i32, P_i32, c_i32, P_i32, P_i32, P_i32, P_i32,
                                   P_i32, P_i32]),
+    "pkv_attention_multi_quant": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p,
+                                          ctypes.POINTER(PkvKvScales), c_void_p, c_i32, c_void_p,
+                                          c_float, c_void_p, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                          c_i32, c_void_p, c_size, ctypes.POINTER(PkvGeom),
+                                          c_void_p]),
+    "pkv_attention_decode_shared_quant": (c_i32, [c_void_p, c_void_p, c_void_p,
+                                                  ctypes.POINTER(PkvKvScales), c_void_p, c_i32,
+                                                  c_void_p, c_void_p, c_void_p, c_i32, c_i32, c_i32,
+                                                  c_i32, c_float, c_void_p, c_i32, c_i32, c_i32,
+                                                  c_void_p, c_size, ctypes.POINTER(PkvGeom),
+                                                  c_void_p]),
     "pkv_bm_add_host_pool": (c_i32, [c_void_p, c_i32, P_i32]),
     "pkv_bm_swap_out": (c_i32, [c_void_p, P_i64, c_i32, P_i32, c_i32, P_i32]),
     "pkv_bm_swap_in": (c_i32, [c_void_p, P_i64, c_i32, P_i32, c_i32, P_i32]),

@@ -32,8 +32,8 @@ using pkv::mfma::kKT;
 struct MultiArgs {
   const uint16_t* q;
   const int32_t* q_offsets;
-  const uint16_t* k_cache;
-  const uint16_t* v_cache;
+  const void* k_cache;      // bf16 bits or one-byte codes
+  const void* v_cache;
   const int32_t* block_tables;
   const int32_t* seq_lens;
   uint16_t* out;
@@ -54,14 +54,18 @@ struct MultiArgs {
   int32_t num_kv_heads;
   int32_t num_parts;
   int32_t part_tokens;
-  float scale_log2;
+  float scale_log2;         // FP8: the K tensor scale folded in
+  float v_scale;            // FP8
+  const float* k_scales;    // INT8
+  const float* v_scales;
 };
 
-template <int D, int NW>
+template <int D, int NW, int Q>
 __global__ void __launch_bounds__(64 * NW)
 attn_multi_kernel(MultiArgs a) {
   __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D>()];
   __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D>()];
+  __shared__ float s_lds[Q == pkv::mfma::kInt8 ? 2 * kKT : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(tid >> 6));
@@ -99,13 +103,16 @@ attn_multi_kernel(MultiArgs a) {
   const int p_row = p_first + jl;
   const int64_t qh = (int64_t(q0 + j0 + jl) * a.num_q_heads + g * G + hh);  // (row, head) index
 
-  const pkv::mfma::History hist{a.k_cache, a.v_cache, a.block_tables + int64_t(s) * a.max_blocks,
-                                L, g, a.block_elems, a.row_elems, a.num_blocks, a.block_shift};
+  const pkv::mfma::History hist{a.k_cache,    a.v_cache,      a.block_tables + int64_t(s) * a.max_blocks,
+                                L,            g,              a.block_elems,
+                                a.row_elems,  a.num_blocks,   a.block_shift,
+                                a.num_kv_heads, a.v_scale,    a.k_scales,
+                                a.v_scales};
   pkv::mfma::RowAcc<D> r;
   pkv::mfma::start(r);
   // every row of the block sees the positions up to its first query's
-  pkv::mfma::attend<D, NW, (NW >= 2 ? 2 : 1)>(hist, t_lo, t_hi, a.q + qh * D, row_ok, p_row,
-                                             p_first, a.scale_log2, k_lds, v_lds, r);
+  pkv::mfma::attend<D, NW, (NW >= 2 ? 2 : 1), Q>(hist, t_lo, t_hi, a.q + qh * D, row_ok, p_row,
+                                                p_first, a.scale_log2, k_lds, v_lds, r, s_lds);
 
   if (!row_ok) return;
   if (a.num_parts == 1) {
@@ -158,14 +165,22 @@ struct MultiPlan {
 
 int64_t round_up_to(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
+// Which cache types a caller accepts: 0 = bf16 only, 1 = one-byte codes only,
+// 2 = any of them (workspace sizing).
 pkv_status multi_plan(int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
                       int32_t max_q_per_seq, int32_t max_seq_len, int32_t partition_tokens,
-                      const pkv_geom* g, const char* who, MultiPlan* pl) {
+                      const pkv_geom* g, const char* who, MultiPlan* pl, int types = 0) {
   if (pkv_status st = pkv::check_geom(g, who)) return st;
-  if (g->dtype != PKV_BF16)
-    return pkv::fail(PKV_ERR_UNSUPPORTED, "%s: dtype %d (built: bf16)", who, g->dtype);
+  const bool quant = pkv::is_quant(g->dtype);
+  if ((types == 0 && g->dtype != PKV_BF16) || (types == 1 && !quant) ||
+      (types == 2 && g->dtype != PKV_BF16 && !quant))
+    return pkv::fail(types == 1 ? PKV_ERR_INVALID_ARG : PKV_ERR_UNSUPPORTED,
+                     "%s: dtype %d is not %s", who, g->dtype,
+                     types == 1 ? "a quantized cache type" : "bf16 or a quantized cache type");
   if (g->head_dim != 64 && g->head_dim != 128)
     return pkv::fail(PKV_ERR_UNSUPPORTED, "%s: head_dim %d (built: 64, 128)", who, g->head_dim);
+  if (quant && g->head_dim != 128)
+    return pkv::fail(PKV_ERR_UNSUPPORTED, "%s: quantized pools need head_dim 128", who);
   if (g->block_size < 8)
     return pkv::fail(PKV_ERR_UNSUPPORTED, "%s: block_size %d < 8", who, g->block_size);
   if (num_seqs < 0 || num_q_heads <= 0 || total_q < 0 || max_q_per_seq < 0 || max_seq_len < 0)
@@ -214,47 +229,45 @@ pkv_status multi_plan(int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
   return PKV_OK;
 }
 
-template <int D>
+template <int D, int Q>
 void launch_multi(const MultiPlan& pl, const MultiArgs& a, int num_seqs, int num_kv_heads,
                   int total_q, hipStream_t st) {
   const dim3 grid(pl.qblocks * num_kv_heads * num_seqs, pl.num_parts);
   switch (pl.nw) {
-    case 1: hipLaunchKernelGGL((attn_multi_kernel<D, 1>), grid, dim3(64), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((attn_multi_kernel<D, 2>), grid, dim3(128), 0, st, a); break;
-    default: hipLaunchKernelGGL((attn_multi_kernel<D, 4>), grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((attn_multi_kernel<D, 1, Q>), grid, dim3(64), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((attn_multi_kernel<D, 2, Q>), grid, dim3(128), 0, st, a); break;
+    default: hipLaunchKernelGGL((attn_multi_kernel<D, 4, Q>), grid, dim3(256), 0, st, a); break;
   }
   if (pl.num_parts > 1 && total_q > 0)
     hipLaunchKernelGGL((attn_multi_merge_kernel<D>), dim3(a.num_q_heads, total_q), dim3(64), 0,
                        st, a);
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t pkv_attention_multi_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
-                                           int32_t total_q, int32_t max_q_per_seq,
-                                           int32_t max_seq_len, int32_t partition_tokens,
-                                           const pkv_geom* geom) {
-  MultiPlan pl;
-  if (multi_plan(num_seqs, num_q_heads, total_q, max_q_per_seq, max_seq_len, partition_tokens,
-                 geom, "pkv_attention_multi_workspace_bytes", &pl) != PKV_OK)
-    return static_cast<size_t>(-1);
-  return pl.ws_bytes;
-}
-
-pkv_status pkv_attention_multi(const void* q, const int32_t* q_offsets, const void* k_cache,
-                               const void* v_cache, const int32_t* block_tables,
-                               int32_t max_blocks_per_seq, const int32_t* seq_lens, float scale,
-                               void* out, int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
-                               int32_t max_q_per_seq, int32_t max_seq_len,
-                               int32_t partition_tokens, void* workspace,
-                               size_t workspace_bytes, const pkv_geom* geom, void* stream) {
-  const char* who = "pkv_attention_multi";
+pkv_status multi_impl(const char* who, int types, const void* q, const int32_t* q_offsets,
+                      const void* k_cache, const void* v_cache, const pkv_kv_scales* scales,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* seq_lens, float scale, void* out, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t total_q, int32_t max_q_per_seq,
+                      int32_t max_seq_len, int32_t partition_tokens, void* workspace,
+                      size_t workspace_bytes, const pkv_geom* geom, void* stream) {
   MultiPlan pl;
   if (pkv_status st = multi_plan(num_seqs, num_q_heads, total_q, max_q_per_seq, max_seq_len,
-                                 partition_tokens, geom, who, &pl))
+                                 partition_tokens, geom, who, &pl, types))
     return st;
+  const int kind = geom->dtype == PKV_FP8_E4M3 ? pkv::mfma::kFp8
+                 : geom->dtype == PKV_INT8 ? pkv::mfma::kInt8 : pkv::mfma::kBf16;
+  if (kind != pkv::mfma::kBf16) {
+    if (!scales) return pkv::fail(PKV_ERR_INVALID_ARG, "%s: null scales", who);
+    if (kind == pkv::mfma::kFp8 &&
+        !(std::isfinite(scales->k_scale) && scales->k_scale > 0.f &&
+          std::isfinite(scales->v_scale) && scales->v_scale > 0.f))
+      return pkv::fail(PKV_ERR_INVALID_ARG, "%s: FP8 scales must be finite and > 0", who);
+    if (kind == pkv::mfma::kInt8 &&
+        (!scales->k_scales || !scales->v_scales ||
+         (reinterpret_cast<uintptr_t>(scales->k_scales) & 3u) ||
+         (reinterpret_cast<uintptr_t>(scales->v_scales) & 3u)))
+      return pkv::fail(PKV_ERR_INVALID_ARG, "%s: INT8 scale pools missing or misaligned", who);
+  }
   if (!std::isfinite(scale)) return pkv::fail(PKV_ERR_INVALID_ARG, "%s: scale is not finite", who);
   if (max_blocks_per_seq < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "%s: negative size", who);
   if (num_seqs == 0 || total_q == 0 || max_q_per_seq == 0) return PKV_OK;
@@ -274,8 +287,8 @@ pkv_status pkv_attention_multi(const void* q, const int32_t* q_offsets, const vo
   MultiArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.q_offsets = q_offsets;
-  a.k_cache = static_cast<const uint16_t*>(k_cache);
-  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
   a.out = static_cast<uint16_t*>(out);
@@ -298,15 +311,66 @@ pkv_status pkv_attention_multi(const void* q, const int32_t* q_offsets, const vo
   a.num_kv_heads = geom->num_kv_heads;
   a.num_parts = pl.num_parts;
   a.part_tokens = pl.part_tokens;
-  a.scale_log2 = static_cast<float>(double(scale) * 1.4426950408889634);
+  a.scale_log2 = static_cast<float>(double(scale) * 1.4426950408889634 *
+                                    (kind == pkv::mfma::kFp8 ? double(scales->k_scale) : 1.0));
+  a.v_scale = kind == pkv::mfma::kFp8 ? scales->v_scale : 1.f;
+  a.k_scales = kind == pkv::mfma::kInt8 ? scales->k_scales : nullptr;
+  a.v_scales = kind == pkv::mfma::kInt8 ? scales->v_scales : nullptr;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (geom->head_dim == 128)
-    launch_multi<128>(pl, a, num_seqs, geom->num_kv_heads, total_q, st);
+  if (kind == pkv::mfma::kFp8)
+    launch_multi<128, pkv::mfma::kFp8>(pl, a, num_seqs, geom->num_kv_heads, total_q, st);
+  else if (kind == pkv::mfma::kInt8)
+    launch_multi<128, pkv::mfma::kInt8>(pl, a, num_seqs, geom->num_kv_heads, total_q, st);
+  else if (geom->head_dim == 128)
+    launch_multi<128, pkv::mfma::kBf16>(pl, a, num_seqs, geom->num_kv_heads, total_q, st);
   else
-    launch_multi<64>(pl, a, num_seqs, geom->num_kv_heads, total_q, st);
+    launch_multi<64, pkv::mfma::kBf16>(pl, a, num_seqs, geom->num_kv_heads, total_q, st);
   if (hipError_t e = hipGetLastError())
     return pkv::fail(PKV_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return PKV_OK;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+size_t pkv_attention_multi_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                           int32_t total_q, int32_t max_q_per_seq,
+                                           int32_t max_seq_len, int32_t partition_tokens,
+                                           const pkv_geom* geom) {
+  MultiPlan pl;
+  if (multi_plan(num_seqs, num_q_heads, total_q, max_q_per_seq, max_seq_len, partition_tokens,
+                 geom, "pkv_attention_multi_workspace_bytes", &pl, 2) != PKV_OK)
+    return static_cast<size_t>(-1);
+  return pl.ws_bytes;
+}
+
+pkv_status pkv_attention_multi(const void* q, const int32_t* q_offsets, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* seq_lens, float scale,
+                               void* out, int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
+                               int32_t max_q_per_seq, int32_t max_seq_len,
+                               int32_t partition_tokens, void* workspace,
+                               size_t workspace_bytes, const pkv_geom* geom, void* stream) {
+  return multi_impl("pkv_attention_multi", 0, q, q_offsets, k_cache, v_cache, nullptr,
+                    block_tables, max_blocks_per_seq, seq_lens, scale, out, num_seqs, num_q_heads,
+                    total_q, max_q_per_seq, max_seq_len, partition_tokens, workspace,
+                    workspace_bytes, geom, stream);
+}
+
+pkv_status pkv_attention_multi_quant(const void* q, const int32_t* q_offsets, const void* k_cache,
+                                     const void* v_cache, const pkv_kv_scales* scales,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* seq_lens, float scale, void* out,
+                                     int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
+                                     int32_t max_q_per_seq, int32_t max_seq_len,
+                                     int32_t partition_tokens, void* workspace,
+                                     size_t workspace_bytes, const pkv_geom* geom, void* stream) {
+  return multi_impl("pkv_attention_multi_quant", 1, q, q_offsets, k_cache, v_cache, scales,
+                    block_tables, max_blocks_per_seq, seq_lens, scale, out, num_seqs, num_q_heads,
+                    total_q, max_q_per_seq, max_seq_len, partition_tokens, workspace,
+                    workspace_bytes, geom, stream);
 }
 
 }  // extern "C"

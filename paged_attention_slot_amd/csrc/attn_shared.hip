@@ -38,8 +38,8 @@ using pkv::mfma::kKT;
 
 struct SharedArgs {
   const uint16_t* q;
-  const uint16_t* k_cache;
-  const uint16_t* v_cache;
+  const void* k_cache;           // bf16 bits or one-byte codes
+  const void* v_cache;
   const int32_t* block_tables;
   const int32_t* seq_lens;
   const int32_t* group_starts;   // [num_groups + 1]
@@ -62,7 +62,11 @@ struct SharedArgs {
   int32_t members_per_block;     // prefix kernel: members per workgroup
   int32_t pre_parts, pre_tokens; // prefix partitions: count and length
   int32_t suf_parts, suf_tokens; // suffix partitions
-  float scale_log2;
+  int32_t num_kv_heads;
+  float scale_log2;              // FP8: the K tensor scale folded in
+  float v_scale;                 // FP8
+  const float* k_scales;         // INT8
+  const float* v_scales;
 };
 
 __device__ __forceinline__ int clamp_len(int v, int cap) { return v < 0 ? 0 : (v > cap ? cap : v); }
@@ -99,11 +103,12 @@ __device__ __forceinline__ int seq_prefix(const SharedArgs& a, int s, int L) {
 }
 
 // grid = (row blocks * pre_parts, H_kv, num_groups).
-template <int D, int NW>
+template <int D, int NW, int Q>
 __global__ void __launch_bounds__(64 * NW)
 attn_prefix_kernel(SharedArgs a) {
   __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D>()];
   __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D>()];
+  __shared__ float s_lds[Q == pkv::mfma::kInt8 ? 2 * kKT : 1];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int gi = blockIdx.z, g = blockIdx.y;
@@ -125,8 +130,11 @@ attn_prefix_kernel(SharedArgs a) {
   const int L = clamp_len(a.seq_lens[s], a.len_cap);
   const int64_t qh = int64_t(s) * a.num_q_heads + g * G + hh;
   // The prefix is read through the group's first member's table.
-  const pkv::mfma::History hist{a.k_cache, a.v_cache, a.block_tables + int64_t(first) * a.max_blocks,
-                                P, g, a.block_elems, a.row_elems, a.num_blocks, a.block_shift};
+  const pkv::mfma::History hist{a.k_cache,      a.v_cache,     a.block_tables + int64_t(first) * a.max_blocks,
+                                P,              g,             a.block_elems,
+                                a.row_elems,    a.num_blocks,  a.block_shift,
+                                a.num_kv_heads, a.v_scale,     a.k_scales,
+                                a.v_scales};
   // Positions every member of the block sees: up to the shortest one's last
   // (one member's length per lane, then a wave minimum: one round trip).
   int lmin = lane < jn ? clamp_len(a.seq_lens[first + j0 + lane], a.len_cap) : a.len_cap;
@@ -134,19 +142,20 @@ attn_prefix_kernel(SharedArgs a) {
   for (int off = 32; off >= 1; off >>= 1) lmin = min(lmin, __shfl_xor(lmin, off));
   pkv::mfma::RowAcc<D> r;
   pkv::mfma::start(r);
-  pkv::mfma::attend<D, NW, (NW >= 2 ? 2 : 1)>(hist, t_lo, t_hi, a.q + qh * D, row_ok, L - 1,
-                                             lmin - 1, a.scale_log2, k_lds, v_lds, r);
+  pkv::mfma::attend<D, NW, (NW >= 2 ? 2 : 1), Q>(hist, t_lo, t_hi, a.q + qh * D, row_ok, L - 1,
+                                                lmin - 1, a.scale_log2, k_lds, v_lds, r, s_lds);
   if (!row_ok) return;
   const int64_t slot = qh * (a.pre_parts + a.suf_parts) + part;
   pkv::mfma::store_piece<D>(r, a.ws_acc + slot * D, a.ws_ml + slot);
 }
 
 // grid = (suf_parts, H_kv, num_seqs).
-template <int D, int NW>
+template <int D, int NW, int Q>
 __global__ void __launch_bounds__(64 * NW)
 attn_suffix_kernel(SharedArgs a) {
   __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D>()];
   __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D>()];
+  __shared__ float s_lds[Q == pkv::mfma::kInt8 ? 2 * kKT : 1];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int s = blockIdx.z, g = blockIdx.y, part = blockIdx.x;
@@ -158,16 +167,19 @@ attn_suffix_kernel(SharedArgs a) {
   const int hh = 16 * w + (lane & 15);
   const bool row_ok = hh < G;
   const int64_t qh = int64_t(s) * a.num_q_heads + g * G + (row_ok ? hh : 0);
-  const pkv::mfma::History hist{a.k_cache, a.v_cache, a.block_tables + int64_t(s) * a.max_blocks,
-                                L, g, a.block_elems, a.row_elems, a.num_blocks, a.block_shift};
+  const pkv::mfma::History hist{a.k_cache,      a.v_cache,     a.block_tables + int64_t(s) * a.max_blocks,
+                                L,              g,             a.block_elems,
+                                a.row_elems,    a.num_blocks,  a.block_shift,
+                                a.num_kv_heads, a.v_scale,     a.k_scales,
+                                a.v_scales};
   pkv::mfma::RowAcc<D> r;
   pkv::mfma::start(r);
   // Partitions part, part + suf_parts, ...: a suffix longer than the grid was
   // sized for is folded into the same piece.
   for (int t_lo = P + part * a.suf_tokens; t_lo < L; t_lo += a.suf_parts * a.suf_tokens)
-    pkv::mfma::attend<D, NW, (NW >= 2 ? 2 : 1)>(hist, t_lo, min(t_lo + a.suf_tokens, L),
-                                               a.q + qh * D, row_ok, L - 1, L - 1, a.scale_log2,
-                                               k_lds, v_lds, r);
+    pkv::mfma::attend<D, NW, (NW >= 2 ? 2 : 1), Q>(hist, t_lo, min(t_lo + a.suf_tokens, L),
+                                                  a.q + qh * D, row_ok, L - 1, L - 1,
+                                                  a.scale_log2, k_lds, v_lds, r, s_lds);
   if (!row_ok) return;
   const int64_t slot = qh * (a.pre_parts + a.suf_parts) + a.pre_parts + part;
   pkv::mfma::store_piece<D>(r, a.ws_acc + slot * D, a.ws_ml + slot);
@@ -231,12 +243,20 @@ struct SharedPlan {
 
 pkv_status shared_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_groups,
                        int32_t max_group_size, int32_t max_prefix_len, int32_t max_suffix_len,
-                       int32_t max_seq_len, const pkv_geom* g, const char* who, SharedPlan* pl) {
+                       int32_t max_seq_len, const pkv_geom* g, const char* who, SharedPlan* pl,
+                       int types = 0) {
+  // types: 0 = bf16 only, 1 = one-byte codes only, 2 = any (workspace sizing)
   if (pkv_status st = pkv::check_geom(g, who)) return st;
-  if (g->dtype != PKV_BF16)
-    return pkv::fail(PKV_ERR_UNSUPPORTED, "%s: dtype %d (built: bf16)", who, g->dtype);
+  const bool quant = pkv::is_quant(g->dtype);
+  if ((types == 0 && g->dtype != PKV_BF16) || (types == 1 && !quant) ||
+      (types == 2 && g->dtype != PKV_BF16 && !quant))
+    return pkv::fail(types == 1 ? PKV_ERR_INVALID_ARG : PKV_ERR_UNSUPPORTED,
+                     "%s: dtype %d is not %s", who, g->dtype,
+                     types == 1 ? "a quantized cache type" : "bf16 or a quantized cache type");
   if (g->head_dim != 64 && g->head_dim != 128)
     return pkv::fail(PKV_ERR_UNSUPPORTED, "%s: head_dim %d (built: 64, 128)", who, g->head_dim);
+  if (quant && g->head_dim != 128)
+    return pkv::fail(PKV_ERR_UNSUPPORTED, "%s: quantized pools need head_dim 128", who);
   if (g->block_size < 8)
     return pkv::fail(PKV_ERR_UNSUPPORTED, "%s: block_size %d < 8", who, g->block_size);
   if (num_seqs < 0 || num_q_heads <= 0 || num_groups < 0 || max_group_size < 0 ||
@@ -280,57 +300,54 @@ pkv_status shared_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_groups
   return PKV_OK;
 }
 
-template <int D>
+template <int D, int Q>
 void launch_shared(const SharedPlan& pl, const SharedArgs& a, int num_kv_heads, hipStream_t st) {
   if (a.num_groups > 0 && a.max_prefix > 0) {
     const dim3 grid(pl.row_blocks * pl.pre_parts, num_kv_heads, a.num_groups);
     switch (pl.nw_pre) {
-      case 1: hipLaunchKernelGGL((attn_prefix_kernel<D, 1>), grid, dim3(64), 0, st, a); break;
-      case 2: hipLaunchKernelGGL((attn_prefix_kernel<D, 2>), grid, dim3(128), 0, st, a); break;
-      default: hipLaunchKernelGGL((attn_prefix_kernel<D, 4>), grid, dim3(256), 0, st, a); break;
+      case 1: hipLaunchKernelGGL((attn_prefix_kernel<D, 1, Q>), grid, dim3(64), 0, st, a); break;
+      case 2: hipLaunchKernelGGL((attn_prefix_kernel<D, 2, Q>), grid, dim3(128), 0, st, a); break;
+      default: hipLaunchKernelGGL((attn_prefix_kernel<D, 4, Q>), grid, dim3(256), 0, st, a); break;
     }
   }
   const dim3 grid(pl.suf_parts, num_kv_heads, a.num_seqs);
   switch (pl.nw_suf) {
-    case 1: hipLaunchKernelGGL((attn_suffix_kernel<D, 1>), grid, dim3(64), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((attn_suffix_kernel<D, 2>), grid, dim3(128), 0, st, a); break;
-    default: hipLaunchKernelGGL((attn_suffix_kernel<D, 4>), grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((attn_suffix_kernel<D, 1, Q>), grid, dim3(64), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((attn_suffix_kernel<D, 2, Q>), grid, dim3(128), 0, st, a); break;
+    default: hipLaunchKernelGGL((attn_suffix_kernel<D, 4, Q>), grid, dim3(256), 0, st, a); break;
   }
   hipLaunchKernelGGL((attn_shared_merge_kernel<D>), dim3(a.num_q_heads, a.num_seqs), dim3(64), 0,
                      st, a);
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t pkv_attention_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
-                                            int32_t num_groups, int32_t max_group_size,
-                                            int32_t max_prefix_len, int32_t max_suffix_len,
-                                            int32_t max_seq_len, const pkv_geom* geom) {
-  SharedPlan pl;
-  if (shared_plan(num_seqs, num_q_heads, num_groups, max_group_size, max_prefix_len,
-                  max_suffix_len, max_seq_len, geom, "pkv_attention_shared_workspace_bytes",
-                  &pl) != PKV_OK)
-    return static_cast<size_t>(-1);
-  return pl.ws_bytes;
-}
-
-pkv_status pkv_attention_decode_shared(const void* q, const void* k_cache, const void* v_cache,
-                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                       const int32_t* seq_lens, const int32_t* group_starts,
-                                       const int32_t* prefix_lens, int32_t num_groups,
-                                       int32_t max_group_size, int32_t max_prefix_len,
-                                       int32_t max_suffix_len, float scale, void* out,
-                                       int32_t num_seqs,
-                                       int32_t num_q_heads, int32_t max_seq_len,
-                                       void* workspace, size_t workspace_bytes,
-                                       const pkv_geom* geom, void* stream) {
-  const char* who = "pkv_attention_decode_shared";
+pkv_status shared_impl(const char* who, int types, const void* q, const void* k_cache,
+                       const void* v_cache, const pkv_kv_scales* scales,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* seq_lens, const int32_t* group_starts,
+                       const int32_t* prefix_lens, int32_t num_groups, int32_t max_group_size,
+                       int32_t max_prefix_len, int32_t max_suffix_len, float scale, void* out,
+                       int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
+                       void* workspace, size_t workspace_bytes, const pkv_geom* geom,
+                       void* stream) {
   SharedPlan pl;
   if (pkv_status st = shared_plan(num_seqs, num_q_heads, num_groups, max_group_size,
-                                  max_prefix_len, max_suffix_len, max_seq_len, geom, who, &pl))
+                                  max_prefix_len, max_suffix_len, max_seq_len, geom, who, &pl,
+                                  types))
     return st;
+  const int kind = geom->dtype == PKV_FP8_E4M3 ? pkv::mfma::kFp8
+                 : geom->dtype == PKV_INT8 ? pkv::mfma::kInt8 : pkv::mfma::kBf16;
+  if (kind != pkv::mfma::kBf16) {
+    if (!scales) return pkv::fail(PKV_ERR_INVALID_ARG, "%s: null scales", who);
+    if (kind == pkv::mfma::kFp8 &&
+        !(std::isfinite(scales->k_scale) && scales->k_scale > 0.f &&
+          std::isfinite(scales->v_scale) && scales->v_scale > 0.f))
+      return pkv::fail(PKV_ERR_INVALID_ARG, "%s: FP8 scales must be finite and > 0", who);
+    if (kind == pkv::mfma::kInt8 &&
+        (!scales->k_scales || !scales->v_scales ||
+         (reinterpret_cast<uintptr_t>(scales->k_scales) & 3u) ||
+         (reinterpret_cast<uintptr_t>(scales->v_scales) & 3u)))
+      return pkv::fail(PKV_ERR_INVALID_ARG, "%s: INT8 scale pools missing or misaligned", who);
+  }
   if (!std::isfinite(scale)) return pkv::fail(PKV_ERR_INVALID_ARG, "%s: scale is not finite", who);
   if (max_blocks_per_seq < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "%s: negative size", who);
   if (num_seqs == 0) return PKV_OK;
@@ -350,8 +367,9 @@ pkv_status pkv_attention_decode_shared(const void* q, const void* k_cache, const
     return pkv::fail(PKV_ERR_INVALID_ARG, "%s: misaligned workspace", who);
   SharedArgs a;
   a.q = static_cast<const uint16_t*>(q);
-  a.k_cache = static_cast<const uint16_t*>(k_cache);
-  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_kv_heads = geom->num_kv_heads;
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
   a.group_starts = group_starts;
@@ -378,15 +396,69 @@ pkv_status pkv_attention_decode_shared(const void* q, const void* k_cache, const
   a.pre_tokens = pl.pre_tokens;
   a.suf_parts = pl.suf_parts;
   a.suf_tokens = pl.suf_tokens;
-  a.scale_log2 = static_cast<float>(double(scale) * 1.4426950408889634);
+  a.scale_log2 = static_cast<float>(double(scale) * 1.4426950408889634 *
+                                    (kind == pkv::mfma::kFp8 ? double(scales->k_scale) : 1.0));
+  a.v_scale = kind == pkv::mfma::kFp8 ? scales->v_scale : 1.f;
+  a.k_scales = kind == pkv::mfma::kInt8 ? scales->k_scales : nullptr;
+  a.v_scales = kind == pkv::mfma::kInt8 ? scales->v_scales : nullptr;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (geom->head_dim == 128)
-    launch_shared<128>(pl, a, geom->num_kv_heads, st);
+  if (kind == pkv::mfma::kFp8)
+    launch_shared<128, pkv::mfma::kFp8>(pl, a, geom->num_kv_heads, st);
+  else if (kind == pkv::mfma::kInt8)
+    launch_shared<128, pkv::mfma::kInt8>(pl, a, geom->num_kv_heads, st);
+  else if (geom->head_dim == 128)
+    launch_shared<128, pkv::mfma::kBf16>(pl, a, geom->num_kv_heads, st);
   else
-    launch_shared<64>(pl, a, geom->num_kv_heads, st);
+    launch_shared<64, pkv::mfma::kBf16>(pl, a, geom->num_kv_heads, st);
   if (hipError_t e = hipGetLastError())
     return pkv::fail(PKV_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return PKV_OK;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+size_t pkv_attention_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                            int32_t num_groups, int32_t max_group_size,
+                                            int32_t max_prefix_len, int32_t max_suffix_len,
+                                            int32_t max_seq_len, const pkv_geom* geom) {
+  SharedPlan pl;
+  if (shared_plan(num_seqs, num_q_heads, num_groups, max_group_size, max_prefix_len,
+                  max_suffix_len, max_seq_len, geom, "pkv_attention_shared_workspace_bytes",
+                  &pl, 2) != PKV_OK)
+    return static_cast<size_t>(-1);
+  return pl.ws_bytes;
+}
+
+pkv_status pkv_attention_decode_shared(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* seq_lens, const int32_t* group_starts,
+                                       const int32_t* prefix_lens, int32_t num_groups,
+                                       int32_t max_group_size, int32_t max_prefix_len,
+                                       int32_t max_suffix_len, float scale, void* out,
+                                       int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
+                                       void* workspace, size_t workspace_bytes,
+                                       const pkv_geom* geom, void* stream) {
+  return shared_impl("pkv_attention_decode_shared", 0, q, k_cache, v_cache, nullptr, block_tables,
+                     max_blocks_per_seq, seq_lens, group_starts, prefix_lens, num_groups,
+                     max_group_size, max_prefix_len, max_suffix_len, scale, out, num_seqs,
+                     num_q_heads, max_seq_len, workspace, workspace_bytes, geom, stream);
+}
+
+pkv_status pkv_attention_decode_shared_quant(
+    const void* q, const void* k_cache, const void* v_cache, const pkv_kv_scales* scales,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+    const int32_t* group_starts, const int32_t* prefix_lens, int32_t num_groups,
+    int32_t max_group_size, int32_t max_prefix_len, int32_t max_suffix_len, float scale,
+    void* out, int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len, void* workspace,
+    size_t workspace_bytes, const pkv_geom* geom, void* stream) {
+  return shared_impl("pkv_attention_decode_shared_quant", 1, q, k_cache, v_cache, scales,
+                     block_tables, max_blocks_per_seq, seq_lens, group_starts, prefix_lens,
+                     num_groups, max_group_size, max_prefix_len, max_suffix_len, scale, out,
+                     num_seqs, num_q_heads, max_seq_len, workspace, workspace_bytes, geom,
+                     stream);
 }
 
 }  // extern "C"

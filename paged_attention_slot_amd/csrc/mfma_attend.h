@@ -19,6 +19,12 @@
 //    two bf16 terms (hi + lo), so the product keeps fp32-like weights.
 //  * A row sees positions t <= p_row inside [t_lo, t_hi); tiles are loaded
 //    with zeros past the history.
+//  * One-byte caches ([KVM §19.2.4] precision table; [PFX] "KV Cache 量化"):
+//    FP8 e4m3 and INT8 codes are decoded exactly to bf16 pairs when a tile is
+//    staged, so the matrix work is the bf16 one.  The FP8 K scale is folded
+//    into the score scale by the caller and the V scale multiplies the
+//    weights; INT8's per-(slot, head) K scale multiplies each score and its V
+//    scale each weight (the sum of weights keeps the bare weights).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -67,10 +73,13 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Element kinds of the cache pools.
+enum Kind : int { kBf16 = 0, kFp8 = 1, kInt8 = 2 };
+
 // The K/V history a workgroup reads: one KV head through one table row.
 struct History {
-  const uint16_t* k_cache;
-  const uint16_t* v_cache;
+  const void* k_cache;   // pools of the element kind (bf16 bits or one-byte codes)
+  const void* v_cache;
   const int32_t* trow;   // block table row
   int32_t len;           // positions < len are in the table; zeros past it
   int32_t g;             // KV head
@@ -78,7 +87,37 @@ struct History {
   int32_t row_elems;
   int32_t num_blocks;
   int32_t block_shift;
+  int32_t num_kv_heads;
+  float v_scale;             // FP8: the V tensor scale
+  const float* k_scales;     // INT8: fp32 [slot][num_kv_heads]
+  const float* v_scales;
 };
+
+// Sixteen one-byte codes -> sixteen floats (exact).
+template <int Q>
+__device__ __forceinline__ void decode_codes(const uint4& x, float (&f)[16]) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (Q == kInt8) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        f[4 * i + j] = static_cast<float>(static_cast<int8_t>((w[i] >> (8 * j)) & 0xFFu));
+    } else {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[i]), false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[i]), true);
+      f[4 * i] = lo[0];
+      f[4 * i + 1] = lo[1];
+      f[4 * i + 2] = hi[0];
+      f[4 * i + 3] = hi[1];
+    }
+  }
+}
+
+// Two floats that bf16 holds exactly (decoded codes) -> one bf16 pair.
+__device__ __forceinline__ uint32_t bf16_pair_exact(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+}
 
 // A row's running state in log2 units: reference m, sum of weights lsum, and
 // the unnormalised weighted sum as this lane's fragment: o[dt][i] holds
@@ -103,7 +142,8 @@ __device__ __forceinline__ void start(RowAcc<D>& r) {
 // (every wave must call this with the same range), folding them into ``r``
 // (start() it first; further calls continue the same online softmax).
 // ``q`` points at this lane's query row (D bf16, 16-byte aligned); it is read
-// only if row_ok.  p_all (the same in every lane) is a position every live
+// only if row_ok.  Q is the pools' element kind; INT8 needs ``s_lds`` (64
+// floats of LDS) for a tile's scales.  p_all (the same in every lane) is a position every live
 // row of the workgroup sees: tiles entirely at or before it, and inside
 // [t_lo, t_hi), skip the per-score mask.  t_lo must be a multiple of 8 (a
 // lane's positions of a tile then lie in one block).  PD tiles are in flight
@@ -115,16 +155,19 @@ __device__ __forceinline__ void start(RowAcc<D>& r) {
 // 2^kSlack and most tiles skip the rescale.  With more waves (matrix-bound)
 // every tile rescales: the branch would keep the compiler from interleaving
 // the tile's matrix work with its softmax (measured 20 % slower).
-template <int D, int NW, int PD = 1>
+template <int D, int NW, int PD = 1, int Q = kBf16>
 __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, const uint16_t* q,
                                        bool row_ok, int p_row, int p_all, float scale_log2,
-                                       uint16_t* k_lds, uint16_t* v_lds, RowAcc<D>& r) {
+                                       uint16_t* k_lds, uint16_t* v_lds, RowAcc<D>& r,
+                                       float* s_lds = nullptr) {
   constexpr float kSlack = 8.0f;
   constexpr bool kLazy = NW == 1;
+  constexpr int kEB = Q == kBf16 ? 2 : 1;   // bytes per element
   constexpr int kKS = D / 32;            // k-steps of the score product
   constexpr int kDT = D / 16;            // 16-wide d tiles of the output
   constexpr int kKStride = D + 8;        // K and V rows in LDS, bf16 elements (16 B pad)
-  constexpr int kChunksPerRow = D / 8;   // 16-byte chunks per K/V row
+  constexpr int kEPC = 16 / kEB;         // elements per 16-byte chunk
+  constexpr int kChunksPerRow = D / kEPC;  // 16-byte chunks per K/V row
   constexpr int kChunks = kKT * kChunksPerRow;
   const int tid = threadIdx.x, lane = tid & 63;
   const int quad = lane >> 4;
@@ -137,7 +180,7 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
 
   const int L = h.len;
   const int bmask = (1 << h.block_shift) - 1;
-  // Chunks of a tile this thread moves: the same 8-element d slice (chunk cc)
+  // Chunks of a tile this thread moves: the same kEPC-element d slice (chunk cc)
   // of kPer consecutive positions pg * kPer .. + kPer - 1 (the global loads
   // stay coalesced: 16 lanes read one contiguous K/V row).
   constexpr int kPer = kChunks / (64 * NW);
@@ -145,6 +188,7 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
   const int cc = tid % kChunksPerRow;
   const int pg = tid / kChunksPerRow;
   uint4 nk[PD][kPer], nv[PD][kPer];
+  float nks[PD], nvs[PD];  // INT8: this lane's position scales (lanes < 32)
   // Issue the global loads of the tile at t0 into buffer j (zeros past the
   // history: never unmasked, and they keep the products finite).
   // The tile's (at most 4, block_size >= 8) block ids are uniform: scalar
@@ -164,15 +208,16 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
     const int p0 = t0 + pg * kPer;
     const int k = (p0 >> h.block_shift) - b0;
     const int blk = k == 0 ? ids[0] : (k == 1 ? ids[1] : (k == 2 ? ids[2] : ids[3]));
-    const int64_t off0 = int64_t(blk) * h.block_elems + int64_t(p0 & bmask) * h.row_elems +
-                         int64_t(h.g) * D + cc * 8;
-    const uint16_t* kb = h.k_cache + off0;
-    const uint16_t* vb = h.v_cache + off0;
+    const int64_t off0 = (int64_t(blk) * h.block_elems + int64_t(p0 & bmask) * h.row_elems +
+                          int64_t(h.g) * D + cc * kEPC) * kEB;
+    const char* kb = static_cast<const char*>(h.k_cache) + off0;
+    const char* vb = static_cast<const char*>(h.v_cache) + off0;
+    const int64_t rstep = int64_t(h.row_elems) * kEB;
     if (t0 + kKT <= L) {  // uniform: the whole tile is history
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
-        nk[j][i] = *reinterpret_cast<const uint4*>(kb + i * h.row_elems);
-        nv[j][i] = *reinterpret_cast<const uint4*>(vb + i * h.row_elems);
+        nk[j][i] = *reinterpret_cast<const uint4*>(kb + i * rstep);
+        nv[j][i] = *reinterpret_cast<const uint4*>(vb + i * rstep);
       }
     } else {
 #pragma unroll
@@ -180,19 +225,54 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
         nk[j][i] = make_uint4(0, 0, 0, 0);
         nv[j][i] = make_uint4(0, 0, 0, 0);
         if (p0 + i < L) {
-          nk[j][i] = *reinterpret_cast<const uint4*>(kb + i * h.row_elems);
-          nv[j][i] = *reinterpret_cast<const uint4*>(vb + i * h.row_elems);
+          nk[j][i] = *reinterpret_cast<const uint4*>(kb + i * rstep);
+          nv[j][i] = *reinterpret_cast<const uint4*>(vb + i * rstep);
         }
       }
     }
+    if constexpr (Q == kInt8) {
+      // Lane t < 32 fetches the scales of position t0 + t (0 past the
+      // history, so an unwritten slot never reaches a weight).
+      nks[j] = 0.f;
+      nvs[j] = 0.f;
+      const int pos = t0 + tid;
+      if (tid < kKT && pos < L) {
+        const int kp = (pos >> h.block_shift) - b0;
+        const int bp = kp == 0 ? ids[0] : (kp == 1 ? ids[1] : (kp == 2 ? ids[2] : ids[3]));
+        const int64_t si = (int64_t(bp) * (1 << h.block_shift) + (pos & bmask)) * h.num_kv_heads + h.g;
+        nks[j] = h.k_scales[si];
+        nvs[j] = h.v_scales[si];
+      }
+    }
   };
-  // Stage the tile of buffer j: K and V as [pos][d].
+  // Stage the tile of buffer j: K and V as [pos][d] bf16 (codes decoded).
   auto stage = [&](int j) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int off = (pg * kPer + i) * kKStride + cc * 8;
-      *reinterpret_cast<uint4*>(k_lds + off) = nk[j][i];
-      *reinterpret_cast<uint4*>(v_lds + off) = nv[j][i];
+      const int off = (pg * kPer + i) * kKStride + cc * kEPC;
+      if constexpr (Q == kBf16) {
+        *reinterpret_cast<uint4*>(k_lds + off) = nk[j][i];
+        *reinterpret_cast<uint4*>(v_lds + off) = nv[j][i];
+      } else {
+        float f[16];
+        uint32_t w[8];
+        decode_codes<Q>(nk[j][i], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = bf16_pair_exact(f[2 * e], f[2 * e + 1]);
+        *reinterpret_cast<uint4*>(k_lds + off) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(k_lds + off + 8) = make_uint4(w[4], w[5], w[6], w[7]);
+        decode_codes<Q>(nv[j][i], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = bf16_pair_exact(f[2 * e], f[2 * e + 1]);
+        *reinterpret_cast<uint4*>(v_lds + off) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(v_lds + off + 8) = make_uint4(w[4], w[5], w[6], w[7]);
+      }
+    }
+    if constexpr (Q == kInt8) {
+      if (tid < kKT) {
+        s_lds[tid] = nks[j];
+        s_lds[kKT + tid] = nvs[j];
+      }
     }
   };
   // This lane's V^T reads: row 4 (lane >> 4) + (lane & 15) / 4 (+ 16 for the
@@ -220,6 +300,7 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float v = acc[i] * scale_log2;
+        if constexpr (Q == kInt8) v *= s_lds[16 * pt + 4 * quad + i];
         if (!full) {
           const int t = t0 + 16 * pt + 4 * quad + i;
           v = (row_ok && t <= p_row && t < t_hi) ? v : -INFINITY;
@@ -246,9 +327,17 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
     float psum = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float p0 = fast_exp2(sc[2 * k] - mref);
-      const float p1 = fast_exp2(sc[2 * k + 1] - mref);
+      float p0 = fast_exp2(sc[2 * k] - mref);
+      float p1 = fast_exp2(sc[2 * k + 1] - mref);
       psum += p0 + p1;
+      // score element e = 2k (+1) sits at tile position 16 (e / 4) + 4 quad + e % 4
+      if constexpr (Q == kFp8) {
+        p0 *= h.v_scale;
+        p1 *= h.v_scale;
+      } else if constexpr (Q == kInt8) {
+        p0 *= s_lds[kKT + 16 * ((2 * k) >> 2) + 4 * quad + ((2 * k) & 3)];
+        p1 *= s_lds[kKT + 16 * ((2 * k + 1) >> 2) + 4 * quad + ((2 * k + 1) & 3)];
+      }
       const uint32_t h = cvt_pk_bf16(p0, p1);
       ph[k] = h;
       pl[k] = cvt_pk_bf16(p0 - __uint_as_float(h << 16), p1 - __uint_as_float(h & 0xFFFF0000u));

@@ -188,14 +188,17 @@ def attention_decode_quant(q, k_cache, v_cache, block_tables, seq_lens, scale, k
 
 def attention_multi(q, q_offsets, k_cache, v_cache, block_tables, seq_lens, scale,
                     max_q_per_seq, out=None, max_seq_len=None, partition_tokens=0,
-                    workspace=None, stream=None):
+                    workspace=None, stream=None, k_scale=1.0, v_scale=1.0, k_scales=None,
+                    v_scales=None):
     """Attention of several new query tokens per sequence (see include/pkv.h,
-    pkv_attention_multi).  q [total_q, H_q, D] bf16; q_offsets int32 [N+1] on
-    the device; ``max_q_per_seq`` bounds the queries of any sequence."""
+    pkv_attention_multi; with FP8/INT8 pools pkv_attention_multi_quant and the
+    scales).  q [total_q, H_q, D] bf16; q_offsets int32 [N+1] on the device;
+    ``max_q_per_seq`` bounds the queries of any sequence."""
     g = geom_of(k_cache)
     dev = k_cache.device
-    _need(k_cache, "k_cache", torch.bfloat16, dev)
-    _need(v_cache, "v_cache", torch.bfloat16, dev)
+    quant = k_cache.dtype in _QUANT
+    _need(k_cache, "k_cache", None if quant else torch.bfloat16, dev)
+    _need(v_cache, "v_cache", k_cache.dtype, dev)
     _need(q, "q", torch.bfloat16, dev)
     _need(q_offsets, "q_offsets", torch.int32, dev)
     _need(block_tables, "block_tables", torch.int32, dev)
@@ -221,6 +224,14 @@ def attention_multi(q, q_offsets, k_cache, v_cache, block_tables, seq_lens, scal
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if quant:
+        sc = _scales(k_cache, k_scale, v_scale, k_scales, v_scales)
+        check(lib().pkv_attention_multi_quant(
+            _ptr(q), _ptr(q_offsets), _ptr(k_cache), _ptr(v_cache), ctypes.byref(sc),
+            _ptr(block_tables), max_blocks, _ptr(seq_lens), float(scale), _ptr(out), N, Hq, total,
+            int(max_q_per_seq), int(max_seq_len), int(partition_tokens), _ptr(workspace),
+            ws_bytes, ctypes.byref(g), _stream(stream)), "pkv_attention_multi_quant")
+        return out
     check(lib().pkv_attention_multi(_ptr(q), _ptr(q_offsets), _ptr(k_cache), _ptr(v_cache),
                                     _ptr(block_tables), max_blocks, _ptr(seq_lens), float(scale),
                                     _ptr(out), N, Hq, total, int(max_q_per_seq),
@@ -305,13 +316,16 @@ def shared_workspace_bytes(num_seqs, num_q_heads, num_groups, max_group_size, ma
 
 def attention_decode_shared(q, k_cache, v_cache, block_tables, seq_lens, scale, group_starts,
                             prefix_lens, max_group_size, max_prefix_len, max_suffix_len=0,
-                            out=None, max_seq_len=None, workspace=None, stream=None):
+                            out=None, max_seq_len=None, workspace=None, stream=None,
+                            k_scale=1.0, v_scale=1.0, k_scales=None, v_scales=None):
     """Decode attention reading each group's shared prefix once (see
     include/pkv.h, pkv_attention_decode_shared).  group_starts / prefix_lens are
     int32 device tensors as pkv_prefix_groups returns them."""
     g = geom_of(k_cache)
     dev = k_cache.device
-    for t, n, dt in ((k_cache, "k_cache", torch.bfloat16), (v_cache, "v_cache", torch.bfloat16),
+    quant = k_cache.dtype in _QUANT
+    kdt = k_cache.dtype if quant else torch.bfloat16
+    for t, n, dt in ((k_cache, "k_cache", kdt), (v_cache, "v_cache", kdt),
                      (q, "q", torch.bfloat16), (block_tables, "block_tables", torch.int32),
                      (seq_lens, "seq_lens", torch.int32), (group_starts, "group_starts", torch.int32),
                      (prefix_lens, "prefix_lens", torch.int32)):
@@ -332,6 +346,15 @@ def attention_decode_shared(q, k_cache, v_cache, block_tables, seq_lens, scale, 
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
+    if quant:
+        sc = _scales(k_cache, k_scale, v_scale, k_scales, v_scales)
+        check(lib().pkv_attention_decode_shared_quant(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(sc), _ptr(block_tables),
+            max_blocks, _ptr(seq_lens), _ptr(group_starts), _ptr(prefix_lens), ng,
+            int(max_group_size), int(max_prefix_len), int(max_suffix_len), float(scale), _ptr(out),
+            N, Hq, int(max_seq_len), _ptr(workspace), ws_bytes, ctypes.byref(g), _stream(stream)),
+            "pkv_attention_decode_shared_quant")
+        return out
     check(lib().pkv_attention_decode_shared(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), max_blocks, _ptr(seq_lens),
         _ptr(group_starts), _ptr(prefix_lens), ng, int(max_group_size), int(max_prefix_len),

@@ -246,12 +246,14 @@ class DecodeStep:
 
     def attention_shared(self, layer=0, stream=None, out=None):
         """Decode attention reading each shared prefix once
-        (pkv_attention_decode_shared); bf16 pools only."""
+        (pkv_attention_decode_shared, or its _quant form for FP8/INT8 pools)."""
         gs, pl, mg, mp, ms = self.shared_groups()
+        ks, vs = self._scales(layer)
         return ops.attention_decode_shared(
             self.q, self.k_caches[layer], self.v_caches[layer], self.block_tables, self.seq_lens,
             self.wl.scale, gs, pl, mg, mp, ms, out=self.out if out is None else out,
-            max_seq_len=self.max_seq_len, workspace=self._shared_ws, stream=stream)
+            max_seq_len=self.max_seq_len, workspace=self._shared_ws, stream=stream,
+            k_scale=self.k_scale, v_scale=self.v_scale, k_scales=ks, v_scales=vs)
 
     @property
     def split(self) -> dict:

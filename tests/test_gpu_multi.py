@@ -153,3 +153,66 @@ def test_bench_configuration_sampled():
                               np.arange(nb, dtype=np.int32)[None], np.asarray([L], np.int32),
                               wl.scale)
         assert_gate(got_all[offs[s]:offs[s + 1]], ref, "bf16", f"bench multi seq {s} L={L}")
+
+
+# -- one-byte caches (pkv_attention_multi_quant) -------------------------------
+
+def quant_case(seed, lens, nq, Hq, Hkv, B, kind, scale_kv=(1.0, 1.0)):
+    """Codes drawn with the oracle's encoders from N(0, 1) values (FP8 with
+    per-tensor scales: the encoded value is x / scale); INT8 with per-(slot,
+    head) scales.  Slots past each history hold NaN scales (never read into
+    an output)."""
+    from oracle import quant
+    D = 128
+    q, offs, kp, vp, tables, lens_a = case(seed, lens, nq, Hq, Hkv, D, B)
+    rng = np.random.default_rng(seed + 1)
+    nb = kp.shape[0]
+    x_k = rng.normal(0, 1, (nb, B, Hkv, D)).astype(np.float32)
+    x_v = rng.normal(0, 1, (nb, B, Hkv, D)).astype(np.float32)
+    if kind == quant.FP8:
+        ks, vs = scale_kv
+        return q, offs, quant.e4m3_encode(x_k / ks), quant.e4m3_encode(x_v / vs), tables, \
+            lens_a, dict(k_scale=ks, v_scale=vs)
+    kc, ksc = quant.int8_quantize_rows(x_k)
+    vc, vsc = quant.int8_quantize_rows(x_v)
+    ksc, vsc = ksc.reshape(nb * B, Hkv), vsc.reshape(nb * B, Hkv)
+    used = np.zeros(nb * B, bool)
+    for s, L in enumerate(lens_a):
+        t = np.arange(int(L))
+        used[tables[s, t // B].astype(np.int64) * B + t % B] = True
+    ksc[~used] = np.nan
+    vsc[~used] = np.nan
+    return q, offs, kc, vc, tables, lens_a, dict(k_scales=ksc, v_scales=vsc)
+
+
+@pytest.mark.parametrize("kind", ["fp8_e4m3", "int8"])
+@pytest.mark.parametrize("Hq,Hkv,B,pt", [(16, 8, 16, 0), (32, 8, 16, 64), (64, 8, 32, 0),
+                                          (8, 8, 8, 32), (16, 1, 16, 0)])
+def test_quantized_caches_match_oracle(kind, Hq, Hkv, B, pt):
+    from oracle import quant
+    from paged_attention_slot_amd import ops
+    lens = [40, 1, 77, 300, 17, 5, 130]
+    nq = [40, 1, 9, 33, 16, 8, 2]
+    scales = (0.5, 2.0) if kind == quant.FP8 else (1.0, 1.0)
+    say(f"  case {kind} Hq={Hq} Hkv={Hkv} B={B} pt={pt} scales={scales}")
+    q, offs, kc, vc, tables, lens_a, sc = quant_case(600 + Hq + B, lens, nq, Hq, Hkv, B, kind,
+                                                     scales)
+    dev = torch.device("cuda:0")
+    tdt = torch.float8_e4m3fn if kind == quant.FP8 else torch.int8
+    kt = torch.from_numpy(kc).to(dev).view(tdt)
+    vt = torch.from_numpy(vc).to(dev).view(tdt)
+    kw = {}
+    if kind == quant.FP8:
+        kw = dict(k_scale=sc["k_scale"], v_scale=sc["v_scale"])
+    else:
+        kw = dict(k_scales=torch.from_numpy(sc["k_scales"]).to(dev),
+                  v_scales=torch.from_numpy(sc["v_scales"]).to(dev))
+    scale = 1.0 / np.sqrt(128)
+    out = ops.attention_multi(dev_bf16(q), torch.from_numpy(offs).to(dev), kt, vt,
+                              torch.from_numpy(tables).to(dev), torch.from_numpy(lens_a).to(dev),
+                              scale, max(nq), max_seq_len=int(max(lens)), partition_tokens=pt,
+                              **kw)
+    torch.cuda.synchronize()
+    got = to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16))
+    ref = quant.attention_multi_quant(q, offs, kc, vc, tables, lens_a, scale, kind, **sc)
+    say("  gate", assert_gate(got, ref, "bf16", f"multi {kind}"))

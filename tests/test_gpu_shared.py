@@ -141,3 +141,44 @@ def test_matches_the_plain_decode_kernel_on_the_config():
     plain = to_f64(to_host_bits(step.out))
     assert_gate(plain, ref, "bf16", "plain decode")
     assert np.max(np.abs(got - plain)) < 2 * (2e-3 + 2 ** -8)
+
+
+# -- one-byte caches (pkv_attention_decode_shared_quant) ------------------------
+
+@pytest.mark.parametrize("kind", ["fp8_e4m3", "int8"])
+@pytest.mark.parametrize("fam", [0, 1, 2], ids=["forks", "partial-prefix", "large-groups"])
+def test_quantized_families(kind, fam):
+    from oracle.replay import run_step_quant
+    from paged_attention_slot_amd.runtime import DecodeStep, to_host_bits
+    prefix, suffix, fp, spf, Hq, Hkv, D, B = [FAMILIES[0], FAMILIES[1], FAMILIES[3]][fam]
+    wl = shared_prefix_workload(prefix_tokens=prefix, suffix_lens=suffix, forking_parents=fp,
+                                samples_per_fork=spf, num_q_heads=Hq, num_kv_heads=Hkv,
+                                head_dim=D, block_size=B, dtype="bf16", seed=prefix + B + 1,
+                                name=f"family-p{prefix}-{kind}")
+    wl.num_blocks += len(suffix) + 8
+    wl.free_order = np.random.default_rng(prefix).permutation(wl.num_blocks).astype(np.int32)
+    ks, vs = (0.5, 2.0) if kind == "fp8_e4m3" else (1.0, 1.0)
+    say(f"  case {wl.name}: N={wl.num_seqs} Hq={Hq} Hkv={Hkv} B={B} scales={ks},{vs}")
+    step = DecodeStep(wl, kv_dtype=kind, k_scale=ks, v_scale=vs)
+    step.copy()
+    step.write()
+    step.attention_shared()
+    torch.cuda.synchronize()
+    got = to_f64(to_host_bits(step.out))
+    ost = run_step_quant(wl, kind, ks, vs)
+    assert_gate(got, ost.attention(), "bf16", wl.name)
+
+
+def test_shared_prefix_config_full_fp8():
+    from oracle.replay import run_step_quant
+    from paged_attention_slot_amd.runtime import DecodeStep, to_host_bits
+    wl = config_workload("shared-prefix-cow")
+    say(f"  case {wl.name} fp8_e4m3: N={wl.num_seqs}")
+    step = DecodeStep(wl, kv_dtype="fp8_e4m3")
+    step.copy()
+    step.write()
+    step.attention_shared()
+    torch.cuda.synchronize()
+    got = to_f64(to_host_bits(step.out))
+    ost = run_step_quant(wl, "fp8_e4m3")
+    say("  gate", assert_gate(got, ost.attention(), "bf16", "shared-prefix-cow fp8"))

@@ -260,3 +260,36 @@ def test_block_manager_swap_errors():
     bm.free_seq(0)
     assert bm.num_free_host() == 4
     bm.check()
+
+
+def test_quantized_matrix_core_entry_points_validate_on_the_host():
+    from paged_attention_slot_amd._lib import PkvKvScales
+    lib = pkv.lib()
+    x = ctypes.c_void_p(0x1000)
+    fp8 = g(nb=16, B=16, H=2, D=128, dt=_lib.PKV_FP8_E4M3)
+    i8 = g(nb=16, B=16, H=2, D=128, dt=_lib.PKV_INT8)
+    bf = g(nb=16, B=16, H=2, D=128, dt=_lib.PKV_BF16)
+    good = PkvKvScales(1.0, 1.0, x, x)
+
+    def multi(geo, sc=good):
+        return lib.pkv_attention_multi_quant(x, x, x, x, None if sc is None else ctypes.byref(sc),
+                                             x, 4, x, 0.1, x, 2, 4, 4, 2, 64, 0, x, 1 << 30,
+                                             ctypes.byref(geo), None)
+
+    def shared(geo, sc=good):
+        return lib.pkv_attention_decode_shared_quant(
+            x, x, x, None if sc is None else ctypes.byref(sc), x, 4, x, x, x, 1, 2, 32, 0, 0.1,
+            x, 2, 4, 64, x, 1 << 30, ctypes.byref(geo), None)
+    for fn in (multi, shared):
+        assert fn(bf) == _lib.PKV_ERR_INVALID_ARG and "quantized" in last_error()
+        assert fn(g(nb=16, B=16, H=2, D=64, dt=_lib.PKV_FP8_E4M3)) == _lib.PKV_ERR_UNSUPPORTED
+        assert fn(fp8, None) == _lib.PKV_ERR_INVALID_ARG and "scales" in last_error()
+        assert fn(fp8, PkvKvScales(0.0, 1.0, None, None)) == _lib.PKV_ERR_INVALID_ARG
+        assert fn(fp8, PkvKvScales(1.0, float("inf"), None, None)) == _lib.PKV_ERR_INVALID_ARG
+        assert fn(i8, PkvKvScales(1.0, 1.0, None, x)) == _lib.PKV_ERR_INVALID_ARG
+        assert fn(i8, PkvKvScales(1.0, 1.0, ctypes.c_void_p(0x1002), x)) == _lib.PKV_ERR_INVALID_ARG
+    # the bf16 entry points refuse one-byte pools, the workspace sizes accept them
+    assert lib.pkv_attention_multi(x, x, x, x, x, 4, x, 0.1, x, 2, 4, 4, 2, 64, 0, x, 1 << 30,
+                                   ctypes.byref(fp8), None) == _lib.PKV_ERR_UNSUPPORTED
+    assert lib.pkv_attention_multi_workspace_bytes(2, 4, 4, 2, 64, 32, ctypes.byref(i8)) > 0
+    assert lib.pkv_attention_shared_workspace_bytes(2, 4, 1, 2, 32, 0, 64, ctypes.byref(fp8)) > 0
