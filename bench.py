@@ -117,28 +117,45 @@ def recorded_traffic(kernel: str, workload: str):
     return None
 
 
-def stream_read_gbps(nbytes: int = 4 << 30, iters: int = 10, workgroups: int = 8192) -> float:
+def stream_read_gbps(nbytes: int = 4 << 30, iters: int = 10, workgroups: int = 8192,
+                     buffers: int = 1) -> float:
     """Achievable read rate on this device: libpkv's plain coalesced stream
-    kernel over ``nbytes`` (median of ``iters`` runs, HIP events)."""
+    kernel over ``nbytes`` (median of ``iters`` runs, HIP events).  With
+    ``buffers`` > 1 the runs cycle over that many buffers of ``nbytes``, as the
+    measured steps cycle over layer pools, so no run finds its bytes in the
+    last-level cache."""
     import numpy as np
     import torch
 
     from paged_attention_slot_amd import ops
-    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    nbytes -= nbytes % 16
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(buffers)]
     sink = torch.zeros(workgroups, dtype=torch.int32, device="cuda")
-    ops.stream_read(buf, sink, workgroups)
+    for buf in bufs:
+        ops.stream_read(buf, sink, workgroups)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(iters)]
     torch.cuda.synchronize()
-    for a, b in ev:
+    for i, (a, b) in enumerate(ev):
         a.record()
-        ops.stream_read(buf, sink, workgroups)
+        ops.stream_read(bufs[i % buffers], sink, workgroups)
         b.record()
     torch.cuda.synchronize()
     t = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3
-    del buf
+    del bufs
     torch.cuda.empty_cache()
     return nbytes / t / 1e9
+
+
+def stream_read_same_size_gbps(nbytes: int, buffers: int) -> dict:
+    """The calibration stream at one launch's algorithmic bytes: the rate a
+    plain coalesced read of that size reaches, launch ramp and drain
+    included (best of three grid sizes)."""
+    rates = {wg: stream_read_gbps(nbytes, iters=20, workgroups=wg, buffers=buffers)
+             for wg in (2048, 4096, 8192)}
+    best = max(rates, key=rates.get)
+    return {"bytes": nbytes - nbytes % 16, "buffers": buffers, "gbps": rates[best],
+            "workgroups": best}
 
 
 def _common(args, wl, metric, value, unit, t_step, dtype, config, roofline, detail):
@@ -375,8 +392,8 @@ def bench_shared(args) -> int:
                     "exceed the HBM peak because each group's prefix is read once per block "
                     "of member rows; detail.unique_gbps counts every distinct cached "
                     "position once"}
-    roof["traffic"] = recorded_traffic("attn_shared", sname)
     sname = f"{wl.name}+shared" + (f"+{args.kv_dtype}" if quant else "")
+    roof["traffic"] = recorded_traffic("attn_shared", sname)
     config = {"workload": sname, "num_seqs": wl.num_seqs,
               "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
               "head_dim": wl.head_dim, "block_size": B, "groups": int(plens.size),
@@ -698,6 +715,9 @@ def main() -> int:
     achievable = stream_read_gbps()
     res["detail"]["stream_read_gbps"] = achievable
     res["detail"]["partition_frac_of_stream_read"] = achieved / achievable
+    same = stream_read_same_size_gbps(part_bytes, max(L, 4))
+    res["detail"]["stream_read_same_size"] = same
+    res["detail"]["partition_frac_of_same_size_stream_read"] = achieved / same["gbps"]
     if not args.no_cpu_baseline and not quant:
         cb = cpu_baseline(wl, args.cpu_budget)
         res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
