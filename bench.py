@@ -537,6 +537,10 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true",
                     help="decode path: time eager launches instead of replaying the step as a "
                          "HIP graph")
+    ap.add_argument("--unfused", action="store_true",
+                    help="decode path: append with the separate write kernel "
+                         "(pkv_write, then pkv_attention_decode) instead of the fused "
+                         "pkv_attention_decode_append")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
@@ -586,12 +590,18 @@ def main() -> int:
     q_bytes = N * wl.num_q_heads * wl.head_dim * qe
     workload_name = wl.name if not quant else f"{wl.name}+{args.kv_dtype}"
     table_bytes = 4 * int(((lens + wl.block_size - 1) // wl.block_size).sum()) + 4 * N
+    # the step's append folded into the attention kernel (bf16/f32 pools):
+    # it also reads the new-token rows and writes them to their slots
+    fused = not quant and not args.unfused
+    new_bytes = 2 * N * wl.num_kv_heads * wl.head_dim * e
     part_bytes = kv_bytes + q_bytes + table_bytes          # partition kernel, algorithmic
+    if fused:
+        part_bytes += 2 * new_bytes + 4 * N
     attn_bytes = part_bytes + q_bytes                      # + the output rows
     n_cow = int(step.cow_pairs.shape[0])
 
     for i in range(W):
-        step.step(i % L)
+        step.step(i % L, fused=fused)
     torch.cuda.synchronize()
 
     # Kernel durations: eager launches with HIP events around each phase on
@@ -604,24 +614,31 @@ def main() -> int:
         e0, e1, e2, e3 = ev[i]
         e0.record()
         step.copy(layer)
-        step.write(layer)
-        e1.record()
-        step.attention(layer, phases=1)
-        e2.record()
-        step.attention(layer, phases=2)
+        if fused:
+            e1.record()
+            step.attention_append(layer, phases=1)
+            e2.record()
+            step.attention_append(layer, phases=2)
+        else:
+            step.write(layer)
+            e1.record()
+            step.attention(layer, phases=1)
+            e2.record()
+            step.attention(layer, phases=2)
         e3.record()
     torch.cuda.synchronize()
     eager_wall = time.perf_counter() - t_start
     wall = eager_wall
     graph_wall = None
     if not args.no_graph:
-        # The step (copy -> write -> attention + merge) of each layer captured
-        # once as a HIP graph and replayed: launches cost no host time.
+        # The step (copy -> append + attention -> merge, or copy -> write ->
+        # attention -> merge) of each layer captured once as a HIP graph and
+        # replayed: launches cost no host time.
         graphs = []
         for layer in range(L):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step.step(layer)
+                step.step(layer, fused=fused)
             graphs.append(g)
         for i in range(W):
             graphs[i % L].replay()
@@ -695,6 +712,7 @@ def main() -> int:
             "partition_us_p10_p90": [float(np.percentile(part, 10)) * 1e6,
                                      float(np.percentile(part, 90)) * 1e6],
             "merge_us_mean": float(np.mean(merge)) * 1e6,
+            "append": "fused into the attention kernel" if fused else "separate write kernel",
             "copy_write_us_mean": float(np.mean(cw)) * 1e6,
             "device_step_us_mean": float(np.mean(dev_step)) * 1e6,
             "step_timing": "hip graph replay" if graph_wall is not None else "eager launches",

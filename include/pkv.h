@@ -339,6 +339,38 @@ pkv_status pkv_attention_decode_phase(int32_t phases, const void* q, const void*
                                       size_t workspace_bytes, const pkv_geom* geom,
                                       void* stream);
 
+/* pkv_attention_decode_append -- the KV append and the decode attention of one
+ * step in one enqueued computation ([KVX §01]: the new token's K/V join the
+ * cache before its query reads the history; [KVM §19.2.3] slot write and
+ * paged attention).  The result equals
+ *     pkv_write(k_new, v_new, slot_mapping, num_seqs, k_cache, v_cache, ...)
+ *     followed by pkv_attention_decode_phase(phases, ...)
+ * when slot_mapping[s] is the slot of position seq_lens[s] - 1 of sequence s
+ * (its table entry for block (L_s - 1) / block_size at offset
+ * (L_s - 1) % block_size), as the block manager hands it out: the attention
+ * takes that position's K/V from k_new/v_new row s, and the wave that attends
+ * it stores the row to the slot (bit copy).
+ *   k_new, v_new  device [num_seqs][num_kv_heads][head_dim], pool dtype.
+ *   slot_mapping  device int32 [num_seqs]; negative or out-of-pool slots are
+ *                 not written (the attention still uses k_new/v_new).
+ *   k_cache, v_cache  modified in place at those slots only.
+ * Sequences with L_s == 0, or with L_s beyond max_seq_len or the table
+ * capacity, have no new position and write nothing.  The slot's block must
+ * not be read by another sequence of the same call (copy-on-write makes the
+ * block a sequence appends to its own).  phases as for
+ * pkv_attention_decode_phase (the store happens in phase 1).  Pools of
+ * dtype bf16 or f32; UNSUPPORTED for one-byte codes.  Other arguments and
+ * errors as for pkv_attention_decode. */
+pkv_status pkv_attention_decode_append(int32_t phases, const void* q, const void* k_new,
+                                       const void* v_new, const int32_t* slot_mapping,
+                                       void* k_cache, void* v_cache, const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                       float scale, void* out, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t max_seq_len,
+                                       int32_t partition_tokens, void* workspace,
+                                       size_t workspace_bytes, const pkv_geom* geom,
+                                       void* stream);
+
 /* pkv_attention_decode_quant -- pkv_attention_decode_phase over a quantized
  * cache (PKV_FP8_E4M3 or PKV_INT8 pools, scales as described with
  * pkv_kv_scales): the same attention of bf16 queries over the dequantized K/V

@@ -70,6 +70,11 @@ SIGNATURES = {
                                            c_void_p, c_float, c_void_p, c_i32, c_i32, c_i32,
                                            c_i32, c_void_p, c_size, ctypes.POINTER(PkvGeom),
                                            c_void_p]),
+    "pkv_attention_decode_append": (c_i32, [c_i32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                            c_void_p, c_void_p, c_void_p, c_i32, c_void_p,
+                                            c_float, c_void_p, c_i32, c_i32, c_i32, c_i32,
+                                            c_void_p, c_size, ctypes.POINTER(PkvGeom),
+                                            c_void_p]),
     "pkv_stream_read": (c_i32, [c_void_p, c_size, c_void_p, c_i32, c_void_p]),
     "pkv_bm_create": (c_void_p, [c_i32, c_i32, P_i32]),
     "pkv_bm_destroy": (None, [c_void_p]),

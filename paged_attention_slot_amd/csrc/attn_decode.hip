@@ -104,6 +104,12 @@ struct AttnArgs {
   float k_scale, v_scale;
   const float* k_scales;
   const float* v_scales;
+  // fused append (pkv_attention_decode_append), else null: the new token of
+  // sequence s is k_new/v_new row s ([num_seqs][num_kv_heads][D]), stored to
+  // slot new_slots[s] of the pools by the wave that attends it
+  const void* k_new;
+  const void* v_new;
+  const int32_t* new_slots;
 };
 
 // One-byte cache element types ([KVM §19.2.4], [PFX] "KV Cache 量化"): OCP e4m3
@@ -246,6 +252,13 @@ struct Wave {
 
   uint4 q[GW][kQC];
   int kvh_;              // the KV head (INT8 scale column)
+  // Fused append: position newpos_ of this stretch is the new token, read
+  // from the k_new/v_new row at new_row_off_ instead of the pools; the writer
+  // wave also stores it to slot new_slot_.  newpos_ < 0: no new token here.
+  int newpos_ = -1;
+  bool writer_ = false;
+  int new_slot_ = -1;
+  int64_t new_row_off_ = 0;
   float m[GW], l[GW], acc[GW][kNE];
   float M[GW], lt[GW];   // after run(): merged reference and sum
 
@@ -291,16 +304,58 @@ struct Wave {
       const char* kb = static_cast<const char*>(a.k_cache) + off;
       const char* vb = static_cast<const char*>(a.v_cache) + off;
       const int lane_off = r * a.row_bytes + c * 16;
+      bool plain = true;
+      if constexpr (!kQuant<T>) {
+        if (newpos_ >= pos && newpos_ < pos + 8) {  // uniform: the new token is in this half
+          // its sub-stream's lanes read the input row, the others the pool
+          const bool mine = pos + r == newpos_;
+          const char* kl = mine ? static_cast<const char*>(a.k_new) + new_row_off_ + c * 16
+                                : kb + lane_off;
+          const char* vl = mine ? static_cast<const char*>(a.v_new) + new_row_off_ + c * 16
+                                : vb + lane_off;
 #pragma unroll
-      for (int j = 0; j < kCPL; ++j) {
-        b.k[i][j] = *reinterpret_cast<const uint4*>(kb + lane_off + 128 * j);
-        b.v[i][j] = *reinterpret_cast<const uint4*>(vb + lane_off + 128 * j);
+          for (int j = 0; j < kCPL; ++j) {
+            b.k[i][j] = *reinterpret_cast<const uint4*>(kl + 128 * j);
+            b.v[i][j] = *reinterpret_cast<const uint4*>(vl + 128 * j);
+          }
+          plain = false;
+        }
+      }
+      if (plain) {
+#pragma unroll
+        for (int j = 0; j < kCPL; ++j) {
+          b.k[i][j] = *reinterpret_cast<const uint4*>(kb + lane_off + 128 * j);
+          b.v[i][j] = *reinterpret_cast<const uint4*>(vb + lane_off + 128 * j);
+        }
       }
       if constexpr (kInt8<T>) {
         // scale of this lane's position (sub-stream r): slot * H_kv + head
         const int64_t si = (int64_t(blk[i]) * (bmask + 1) + (pos & bmask) + r) * a.num_kv_heads + kvh_;
         b.ks[i] = a.k_scales[si];
         b.vs[i] = a.v_scales[si];
+      }
+    }
+  }
+
+  // Fused append: the lanes holding the new token (its row, read from the
+  // input into this tile buffer) store it to its slot.  Slots outside the
+  // pool are skipped, as pkv_write skips them.
+  __device__ __forceinline__ void store_new(const TileInfo& t, const TileBuf<T, D>& b) {
+    const int64_t num_slots = int64_t(a.num_blocks) << a.block_shift;
+    if (new_slot_ < 0 || new_slot_ >= num_slots) return;
+    const int bmask = (1 << a.block_shift) - 1;
+    const int64_t off = int64_t(new_slot_ >> a.block_shift) * a.block_bytes +
+                        int64_t(new_slot_ & bmask) * a.row_bytes + head_off + c * 16;
+    char* kd = static_cast<char*>(const_cast<void*>(a.k_cache)) + off;
+    char* vd = static_cast<char*>(const_cast<void*>(a.v_cache)) + off;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (t.start + 8 * i + r == newpos_) {
+#pragma unroll
+        for (int j = 0; j < kCPL; ++j) {
+          *reinterpret_cast<uint4*>(kd + 128 * j) = b.k[i][j];
+          *reinterpret_cast<uint4*>(vd + 128 * j) = b.v[i][j];
+        }
       }
     }
   }
@@ -416,8 +471,19 @@ struct Wave {
 
   // Attention of query heads h0 .. h0+GW-1 of sequence s over positions
   // [start, end) of KV head kvh (start < end).  Leaves the merged state in M,
-  // lt and acc (identical in every lane holding a given chunk).
-  __device__ __forceinline__ void run(int s, int kvh, int h0, int start, int end) {
+  // lt and acc (identical in every lane holding a given chunk).  newpos >= 0
+  // (fused append, always end - 1): that position is the new token, and a
+  // writer wave stores it to the pools.
+  __device__ __forceinline__ void run(int s, int kvh, int h0, int start, int end, int newpos = -1,
+                                      bool writer = false) {
+    if constexpr (!kQuant<T>) {
+      newpos_ = newpos;
+      writer_ = newpos >= 0 && writer;
+      if (newpos >= 0) {
+        new_row_off_ = (int64_t(s) * a.num_kv_heads + kvh) * (D * S::kES);
+        new_slot_ = writer_ ? a.new_slots[s] : -1;
+      }
+    }
     const char* q_base =
         static_cast<const char*>(a.q) + (int64_t(s) * a.num_q_heads + h0) * (D * kQES);
 #pragma unroll
@@ -466,8 +532,13 @@ struct Wave {
       }
     }
 #pragma unroll
-    for (int k = 0; k < P; ++k)
-      if (t + k < ntiles) consume<true>(info[k], buf[k]);
+    for (int k = 0; k < P; ++k) {
+      if (t + k < ntiles) {
+        consume<true>(info[k], buf[k]);
+        if constexpr (!kQuant<T>)
+          if (writer_ && t + k == ntiles - 1) store_new(info[k], buf[k]);
+      }
+    }
 
     // Merge the 8 sub-streams (log-sum-exp rescale to the common reference).
 #pragma unroll
@@ -553,7 +624,8 @@ attn_partition_kernel(AttnArgs a) {
   const int h0 = kvh * a.group + sub * GW;
 
   Wave<T, D, GW, P> w(a);
-  const int L = clamp_len(a.seq_lens[s], a.len_cap);
+  const int Lraw = a.seq_lens[s];
+  const int L = clamp_len(Lraw, a.len_cap);
   const int start = part * a.part_tokens;
   if (start >= L) {
     // Empty history (L == 0): the output is zero.  With more than one
@@ -561,7 +633,9 @@ attn_partition_kernel(AttnArgs a) {
     if (part == 0 && a.num_parts == 1) w.write_zero(s, h0);
     return;
   }
-  w.run(s, kvh, h0, start, min(start + a.part_tokens, L));
+  const int end = min(start + a.part_tokens, L);
+  const bool app = a.k_new != nullptr && end == L && L == Lraw;  // holds the new token
+  w.run(s, kvh, h0, start, end, app ? L - 1 : -1, sub == 0);
   if (a.num_parts == 1) {
     w.write_out(s, h0);
   } else {
@@ -733,9 +807,12 @@ __device__ __forceinline__ void run_interval(Wave<T, D, GW, P>& w, const AttnArg
     const int kvh = rel / nt;
     const int t0 = rel - kvh * nt;
     const int seg = static_cast<int>(min(hi - cur, int64_t(nt - t0)));
-    const int L = clamp_len(a.seq_lens[s], a.len_cap);
+    const int Lraw = a.seq_lens[s];
+    const int L = clamp_len(Lraw, a.len_cap);
     const int h0 = kvh * a.group + sub * GW;
-    w.run(s, kvh, h0, t0 * kTile, min((t0 + seg) * kTile, L));
+    // the stream's last tile holds the new token (fused append)
+    const bool app = a.k_new != nullptr && t0 + seg == nt && L == Lraw;
+    w.run(s, kvh, h0, t0 * kTile, min((t0 + seg) * kTile, L), app ? L - 1 : -1, sub == 0);
     if (t0 == 0 && seg == nt) {
       w.write_out(s, h0);  // the whole stream in one interval
     } else {
@@ -1138,13 +1215,21 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int3
 
 namespace {
 
+// New token of the fused append (pkv_attention_decode_append), else all null.
+struct NewToken {
+  bool on = false;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const int32_t* slots = nullptr;
+};
+
 pkv_status attention_impl(const char* who, int32_t phases, const void* q, const void* k_cache,
                           const void* v_cache, const pkv_kv_scales* scales,
                           const int32_t* block_tables, int32_t max_blocks_per_seq,
                           const int32_t* seq_lens, float scale, void* out, int32_t num_seqs,
                           int32_t num_q_heads, int32_t max_seq_len, int32_t partition_tokens,
                           void* workspace, size_t workspace_bytes, const pkv_geom* geom,
-                          void* stream) {
+                          void* stream, const NewToken& nt = NewToken()) {
   if (phases < 1 || phases > 3)
     return pkv::fail(PKV_ERR_INVALID_ARG, "%s: phases must be 1, 2 or 3", who);
   Plan pl;
@@ -1153,6 +1238,9 @@ pkv_status attention_impl(const char* who, int32_t phases, const void* q, const 
     return st;
   if (!std::isfinite(scale)) return pkv::fail(PKV_ERR_INVALID_ARG, "%s: scale is not finite", who);
   const bool quant = pkv::is_quant(geom->dtype);
+  const bool append = nt.on;
+  if (append && quant)
+    return pkv::fail(PKV_ERR_UNSUPPORTED, "%s: quantized pools (write with pkv_write_quant)", who);
   if (quant) {
     if (!scales) return pkv::fail(PKV_ERR_INVALID_ARG, "%s: null scales", who);
     if (geom->dtype == PKV_FP8_E4M3 &&
@@ -1168,6 +1256,9 @@ pkv_status attention_impl(const char* who, int32_t phases, const void* q, const 
   if (num_seqs == 0) return PKV_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out)
     return pkv::fail(PKV_ERR_INVALID_ARG, "%s: null pointer", who);
+  if (append && (!nt.k || !nt.v || !nt.slots || !pkv::aligned16(nt.k) || !pkv::aligned16(nt.v) ||
+                 (reinterpret_cast<uintptr_t>(nt.slots) & 3u)))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "%s: new-token pointer null or misaligned", who);
   if (!pkv::aligned16(q) || !pkv::aligned16(out) || !pkv::aligned16(k_cache) ||
       !pkv::aligned16(v_cache) || (reinterpret_cast<uintptr_t>(block_tables) & 3u) ||
       (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
@@ -1216,6 +1307,9 @@ pkv_status attention_impl(const char* who, int32_t phases, const void* q, const 
   a.v_scale = quant ? scales->v_scale : 1.0f;
   a.k_scales = quant ? scales->k_scales : nullptr;
   a.v_scales = quant ? scales->v_scales : nullptr;
+  a.k_new = nt.k;
+  a.v_new = nt.v;
+  a.new_slots = nt.slots;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (geom->dtype == PKV_FP8_E4M3)
     return dispatch<fp8_e4m3, 128>(phases, pl, a, num_seqs, num_q_heads, st);
@@ -1265,6 +1359,26 @@ pkv_status pkv_attention_decode_quant(int32_t phases, const void* q, const void*
   return attention_impl(who, phases, q, k_cache, v_cache, scales, block_tables,
                         max_blocks_per_seq, seq_lens, scale, out, num_seqs, num_q_heads,
                         max_seq_len, partition_tokens, workspace, workspace_bytes, geom, stream);
+}
+
+pkv_status pkv_attention_decode_append(int32_t phases, const void* q, const void* k_new,
+                                       const void* v_new, const int32_t* slot_mapping,
+                                       void* k_cache, void* v_cache, const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                       float scale, void* out, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t max_seq_len,
+                                       int32_t partition_tokens, void* workspace,
+                                       size_t workspace_bytes, const pkv_geom* geom,
+                                       void* stream) {
+  NewToken nt;
+  nt.on = true;
+  nt.k = k_new;
+  nt.v = v_new;
+  nt.slots = slot_mapping;
+  return attention_impl("pkv_attention_decode_append", phases, q, k_cache, v_cache, nullptr,
+                        block_tables, max_blocks_per_seq, seq_lens, scale, out, num_seqs,
+                        num_q_heads, max_seq_len, partition_tokens, workspace, workspace_bytes,
+                        geom, stream, nt);
 }
 
 pkv_status pkv_attention_decode(const void* q, const void* k_cache, const void* v_cache,

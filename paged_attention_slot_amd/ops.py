@@ -112,7 +112,7 @@ def _scales(k_cache, k_scale, v_scale, k_scales, v_scales) -> PkvKvScales:
 
 
 def _attention(q, k_cache, v_cache, block_tables, seq_lens, scale, out, max_seq_len,
-               partition_tokens, workspace, stream, phases, scales):
+               partition_tokens, workspace, stream, phases, scales, new=None):
     g = geom_of(k_cache)
     dev = k_cache.device
     quant = k_cache.dtype in _QUANT
@@ -145,7 +145,12 @@ def _attention(q, k_cache, v_cache, block_tables, seq_lens, scale, out, max_seq_
     common = (_ptr(block_tables), max_blocks, _ptr(seq_lens), float(scale), _ptr(out), N, Hq,
               int(max_seq_len), int(partition_tokens), _ptr(workspace), ws_bytes,
               ctypes.byref(g), _stream(stream))
-    if quant:
+    if new is not None:
+        k_new, v_new, slots = new
+        check(lib().pkv_attention_decode_append(int(phases), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                                _ptr(slots), _ptr(k_cache), _ptr(v_cache),
+                                                *common), "pkv_attention_decode_append")
+    elif quant:
         check(lib().pkv_attention_decode_quant(int(phases), _ptr(q), _ptr(k_cache),
                                                _ptr(v_cache), ctypes.byref(scales), *common),
               "pkv_attention_decode_quant")
@@ -169,6 +174,29 @@ def attention_decode(q, k_cache, v_cache, block_tables, seq_lens, scale, out=Non
         raise TypeError("quantized pools: use attention_decode_quant")
     return _attention(q, k_cache, v_cache, block_tables, seq_lens, scale, out, max_seq_len,
                       partition_tokens, workspace, stream, phases, None)
+
+
+def attention_decode_append(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
+                            seq_lens, scale, out=None, max_seq_len=None, partition_tokens=0,
+                            workspace=None, stream=None, phases=3):
+    """The step's KV append and decode attention in one computation
+    (pkv_attention_decode_append): k_new/v_new [N, H_kv, D] in the pool dtype,
+    slot_mapping int32 [N] the slot of each sequence's newest position; the
+    pools are written at those slots.  Returns ``out``."""
+    if k_cache.dtype in _QUANT:
+        raise TypeError("attention_decode_append takes bf16 or f32 pools")
+    dev = k_cache.device
+    _need(k_new, "k_new", k_cache.dtype, dev)
+    _need(v_new, "v_new", k_cache.dtype, dev)
+    _need(slot_mapping, "slot_mapping", torch.int32, dev)
+    N = seq_lens.shape[0]
+    g = geom_of(k_cache)
+    if k_new.shape != (N, g.num_kv_heads, g.head_dim) or v_new.shape != k_new.shape or \
+            slot_mapping.shape != (N,):
+        raise ValueError("k_new/v_new must be [N, H_kv, D] and slot_mapping [N]")
+    return _attention(q, k_cache, v_cache, block_tables, seq_lens, scale, out, max_seq_len,
+                      partition_tokens, workspace, stream, phases, None,
+                      new=(k_new, v_new, slot_mapping))
 
 
 def attention_decode_quant(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale=1.0,

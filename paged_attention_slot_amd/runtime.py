@@ -10,6 +10,10 @@ history; page keys in include/pkv.h):
     pkv_write       (one new token per sequence)
     pkv_attention_decode (+ split-KV merge)
 
+or, with ``step(fused=True)``, the write folded into the attention
+(pkv_attention_decode_append: the wave that attends a sequence's newest
+position takes it from the new-token rows and stores it to its slot).
+
 ``layers`` > 1 keeps that many independent pool pairs with identical block
 tables (one per transformer layer); ``step(layer)`` runs the step on one of
 them, so consecutive steps read different memory as a model's layers do.
@@ -231,6 +235,18 @@ class DecodeStep:
         return ops.attention_decode(self.q, self.k_caches[layer], self.v_caches[layer],
                                     self.block_tables, self.seq_lens, self.wl.scale, **kw)
 
+    def attention_append(self, layer=0, stream=None, out=None, phases=3):
+        """The new token's append and the attention in one computation
+        (pkv_attention_decode_append; bf16/f32 pools)."""
+        if self.quant:
+            raise ValueError("the fused append takes bf16 or f32 pools")
+        return ops.attention_decode_append(
+            self.q, self.new_k, self.new_v, self.slot_mapping, self.k_caches[layer],
+            self.v_caches[layer], self.block_tables, self.seq_lens, self.wl.scale,
+            out=self.out if out is None else out, max_seq_len=self.max_seq_len,
+            partition_tokens=self.partition_tokens, workspace=self.workspace, stream=stream,
+            phases=phases)
+
     def shared_groups(self):
         """Shared-prefix groups of the step's tables (pkv_prefix_groups), as
         device tensors plus their host bounds; computed once."""
@@ -266,8 +282,11 @@ class DecodeStep:
         return {"mode": "partitions", "partition_tokens": pt,
                 "num_partitions": max(1, -(-self.max_seq_len // pt))}
 
-    def step(self, layer=0, stream=None):
-        """copy -> write -> attention on one layer's pools (enqueue only)."""
+    def step(self, layer=0, stream=None, fused=False):
+        """copy -> write -> attention on one layer's pools (enqueue only);
+        ``fused``: copy -> append + attention (pkv_attention_decode_append)."""
         self.copy(layer, stream)
+        if fused:
+            return self.attention_append(layer, stream)
         self.write(layer, stream)
         return self.attention(layer, stream)

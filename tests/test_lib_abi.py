@@ -293,3 +293,27 @@ def test_quantized_matrix_core_entry_points_validate_on_the_host():
                                    ctypes.byref(fp8), None) == _lib.PKV_ERR_UNSUPPORTED
     assert lib.pkv_attention_multi_workspace_bytes(2, 4, 4, 2, 64, 32, ctypes.byref(i8)) > 0
     assert lib.pkv_attention_shared_workspace_bytes(2, 4, 1, 2, 32, 0, 64, ctypes.byref(fp8)) > 0
+
+
+def test_fused_append_entry_point_validates_on_the_host():
+    lib = pkv.lib()
+    x = ctypes.c_void_p(0x1000)
+    bad = ctypes.c_void_p(0x1004)
+
+    def call(geom, kn=x, vn=x, sl=x, N=2, phases=3):
+        return lib.pkv_attention_decode_append(phases, x, kn, vn, sl, x, x, x, 7, x, 0.1, x, N, 8,
+                                               100, 0, None, 0, ctypes.byref(geom), None)
+
+    # one-byte pools are refused before anything else
+    assert call(g(H=2, D=128, dt=_lib.PKV_FP8_E4M3)) == _lib.PKV_ERR_UNSUPPORTED
+    assert call(g(H=2, D=128, dt=_lib.PKV_INT8)) == _lib.PKV_ERR_UNSUPPORTED
+    assert call(g(), N=0) == _lib.PKV_OK
+    assert call(g(), kn=None) == _lib.PKV_ERR_INVALID_ARG
+    assert "new-token" in last_error()
+    assert call(g(), sl=None) == _lib.PKV_ERR_INVALID_ARG
+    assert call(g(), vn=bad) == _lib.PKV_ERR_INVALID_ARG
+    assert call(g(), phases=4) == _lib.PKV_ERR_INVALID_ARG
+    assert call(g(D=96)) == _lib.PKV_ERR_UNSUPPORTED
+    # the balanced split needs a workspace
+    assert call(g()) == _lib.PKV_ERR_INVALID_ARG
+    assert "workspace" in last_error()
