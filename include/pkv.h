@@ -340,25 +340,25 @@ pkv_status pkv_attention_decode_phase(int32_t phases, const void* q, const void*
                                       void* stream);
 
 /* pkv_attention_decode_append -- the KV append and the decode attention of one
- * step in one enqueued computation ([KVX §01]: the new token's K/V join the
- * cache before its query reads the history; [KVM §19.2.3] slot write and
- * paged attention).  The result equals
- *     pkv_write(k_new, v_new, slot_mapping, num_seqs, k_cache, v_cache, ...)
- *     followed by pkv_attention_decode_phase(phases, ...)
- * when slot_mapping[s] is the slot of position seq_lens[s] - 1 of sequence s
+ * step ([KVX §01]: the new token's K/V join the cache before its query reads
+ * the history; [KVM §19.2.3] slot write and paged attention).  The new token
+ * of sequence s is its position L_s - 1 (L_s = seq_lens[s]); its K/V rows are
+ * stored (bit copy) to slot slot_mapping[s] when that slot is in the pool and
+ * 1 <= L_s <= min(max_seq_len, max_blocks_per_seq * block_size); otherwise
+ * nothing is written for s.  With slot_mapping[s] the slot of position L_s - 1
  * (its table entry for block (L_s - 1) / block_size at offset
- * (L_s - 1) % block_size), as the block manager hands it out: the attention
- * takes that position's K/V from k_new/v_new row s, and the wave that attends
- * it stores the row to the slot (bit copy).
+ * (L_s - 1) % block_size, as the block manager hands it out) the result is
+ * exactly pkv_write(k_new, v_new, slot_mapping, num_seqs, ...) followed by
+ * pkv_attention_decode_phase(phases, ...).  For waves of up to two query heads
+ * the attention kernel does the append itself: the wave that attends position
+ * L_s - 1 takes its K/V from the new-token rows and stores them to the slot;
+ * with more heads per wave a copy kernel runs first.
  *   k_new, v_new  device [num_seqs][num_kv_heads][head_dim], pool dtype.
- *   slot_mapping  device int32 [num_seqs]; negative or out-of-pool slots are
- *                 not written (the attention still uses k_new/v_new).
+ *   slot_mapping  device int32 [num_seqs].
  *   k_cache, v_cache  modified in place at those slots only.
- * Sequences with L_s == 0, or with L_s beyond max_seq_len or the table
- * capacity, have no new position and write nothing.  The slot's block must
- * not be read by another sequence of the same call (copy-on-write makes the
- * block a sequence appends to its own).  phases as for
- * pkv_attention_decode_phase (the store happens in phase 1).  Pools of
+ * The slot's block must not be read by another sequence of the same call
+ * (copy-on-write makes the block a sequence appends to its own).  phases as
+ * for pkv_attention_decode_phase (the append happens in phase 1).  Pools of
  * dtype bf16 or f32; UNSUPPORTED for one-byte codes.  Other arguments and
  * errors as for pkv_attention_decode. */
 pkv_status pkv_attention_decode_append(int32_t phases, const void* q, const void* k_new,
@@ -444,6 +444,8 @@ pkv_status pkv_attention_multi_quant(const void* q, const int32_t* q_offsets, co
  *                                  (the waves of one (sequence, partition)
  *                                  are packed together)
  *   PKV_ATTN_MODE            1 = fixed partitions, 2 = balanced split
+ *   PKV_ATTN_APPEND          pkv_attention_decode_append: 1 = copy kernel
+ *                                  first, 2 = folded into the attention kernel
  * They change speed and register use, never results beyond fp32 rounding
  * order across query-head groupings (each head's arithmetic is unchanged). */
 

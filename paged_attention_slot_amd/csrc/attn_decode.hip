@@ -231,9 +231,11 @@ __device__ __forceinline__ uint32_t bf16_pair_exact(float lo, float hi) {
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
 }
 
-// One wave's attention over a stretch [start, end) of one stream.
-template <typename T, int D, int GW, int P>
+// One wave's attention over a stretch [start, end) of one stream.  kAppend:
+// the fused-append variant (pkv_attention_decode_append), bf16/f32 only.
+template <typename T, int D, int GW, int P, bool kAppend = false>
 struct Wave {
+  static_assert(!kAppend || !kQuant<T>, "the fused append takes bf16 or f32 pools");
   using S = Shape<T, D>;
   static constexpr int kCPL = S::kCPL, kEPC = S::kEPC, kNE = S::kNE;
   // Queries and outputs: the cache type, or bf16 for one-byte codes (lane c
@@ -305,9 +307,9 @@ struct Wave {
       const char* vb = static_cast<const char*>(a.v_cache) + off;
       const int lane_off = r * a.row_bytes + c * 16;
       bool plain = true;
-      if constexpr (!kQuant<T>) {
+      if constexpr (kAppend) {
         if (newpos_ >= pos && newpos_ < pos + 8) {  // uniform: the new token is in this half
-          // its sub-stream's lanes read the input row, the others the pool
+          // its sub-stream's lanes read the new-token row, the others the pool
           const bool mine = pos + r == newpos_;
           const char* kl = mine ? static_cast<const char*>(a.k_new) + new_row_off_ + c * 16
                                 : kb + lane_off;
@@ -338,11 +340,8 @@ struct Wave {
   }
 
   // Fused append: the lanes holding the new token (its row, read from the
-  // input into this tile buffer) store it to its slot.  Slots outside the
-  // pool are skipped, as pkv_write skips them.
+  // input into this tile buffer) store it to its slot (checked in run()).
   __device__ __forceinline__ void store_new(const TileInfo& t, const TileBuf<T, D>& b) {
-    const int64_t num_slots = int64_t(a.num_blocks) << a.block_shift;
-    if (new_slot_ < 0 || new_slot_ >= num_slots) return;
     const int bmask = (1 << a.block_shift) - 1;
     const int64_t off = int64_t(new_slot_ >> a.block_shift) * a.block_bytes +
                         int64_t(new_slot_ & bmask) * a.row_bytes + head_off + c * 16;
@@ -476,12 +475,19 @@ struct Wave {
   // writer wave stores it to the pools.
   __device__ __forceinline__ void run(int s, int kvh, int h0, int start, int end, int newpos = -1,
                                       bool writer = false) {
-    if constexpr (!kQuant<T>) {
-      newpos_ = newpos;
-      writer_ = newpos >= 0 && writer;
+    if constexpr (kAppend) {
+      // a slot outside the pool is not written, so that position is then
+      // read from the pool like any other
+      newpos_ = -1;
+      writer_ = false;
       if (newpos >= 0) {
-        new_row_off_ = (int64_t(s) * a.num_kv_heads + kvh) * (D * S::kES);
-        new_slot_ = writer_ ? a.new_slots[s] : -1;
+        const int slot = a.new_slots[s];
+        if (slot >= 0 && int64_t(slot) < (int64_t(a.num_blocks) << a.block_shift)) {
+          newpos_ = newpos;
+          writer_ = writer;
+          new_slot_ = slot;
+          new_row_off_ = (int64_t(s) * a.num_kv_heads + kvh) * (D * S::kES);
+        }
       }
     }
     const char* q_base =
@@ -535,7 +541,7 @@ struct Wave {
     for (int k = 0; k < P; ++k) {
       if (t + k < ntiles) {
         consume<true>(info[k], buf[k]);
-        if constexpr (!kQuant<T>)
+        if constexpr (kAppend)
           if (writer_ && t + k == ntiles - 1) store_new(info[k], buf[k]);
       }
     }
@@ -610,7 +616,7 @@ struct Wave {
 // ---------------------------------------------------------------------------
 // Partition mode: one wave per (sequence, partition, KV head, head subset).
 // ---------------------------------------------------------------------------
-template <typename T, int D, int GW, int P>
+template <typename T, int D, int GW, int P, bool kAppend>
 __global__ void __launch_bounds__(64 * kMaxWavesPerBlock)
 attn_partition_kernel(AttnArgs a) {
   // The waves of one (sequence, partition) are numbered consecutively and
@@ -623,7 +629,7 @@ attn_partition_kernel(AttnArgs a) {
   const int s = blockIdx.z;
   const int h0 = kvh * a.group + sub * GW;
 
-  Wave<T, D, GW, P> w(a);
+  Wave<T, D, GW, P, kAppend> w(a);
   const int Lraw = a.seq_lens[s];
   const int L = clamp_len(Lraw, a.len_cap);
   const int start = part * a.part_tokens;
@@ -634,7 +640,7 @@ attn_partition_kernel(AttnArgs a) {
     return;
   }
   const int end = min(start + a.part_tokens, L);
-  const bool app = a.k_new != nullptr && end == L && L == Lraw;  // holds the new token
+  const bool app = kAppend && end == L && L == Lraw;  // holds the new token
   w.run(s, kvh, h0, start, end, app ? L - 1 : -1, sub == 0);
   if (a.num_parts == 1) {
     w.write_out(s, h0);
@@ -733,6 +739,29 @@ attn_merge_kernel(AttnArgs a) {
   merge_rows<T, D>(a, np, row0, 1, dst);
 }
 
+// The append of pkv_attention_decode_append where the attention kernel does
+// not fold it in (waves of three or more query heads, whose issue slots the
+// attention already fills): one workgroup per sequence copies the new K and V
+// rows to the slot, under the same conditions as the folded store (a slot in
+// the pool, 1 <= L_s <= len_cap).
+constexpr int kAppendThreads = 256;
+
+__global__ void __launch_bounds__(kAppendThreads)
+append_rows_kernel(const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
+                   const int32_t* __restrict__ slots, const int32_t* __restrict__ seq_lens,
+                   uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, int32_t row_chunks,
+                   int64_t num_slots, int32_t len_cap) {
+  const int s = blockIdx.x;
+  const int L = seq_lens[s];
+  const int slot = slots[s];
+  if (L < 1 || L > len_cap || slot < 0 || slot >= num_slots) return;
+  const int64_t src = int64_t(s) * row_chunks, dst = int64_t(slot) * row_chunks;
+  for (int i = threadIdx.x; i < 2 * row_chunks; i += kAppendThreads) {
+    if (i < row_chunks) k_cache[dst + i] = k_new[src + i];
+    else v_cache[dst + i - row_chunks] = v_new[src + i - row_chunks];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Balanced mode.
 // ---------------------------------------------------------------------------
@@ -787,8 +816,8 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 }
 
 // Attention over global tiles [lo, hi) of interval `iv`, stream by stream.
-template <typename T, int D, int GW, int P>
-__device__ __forceinline__ void run_interval(Wave<T, D, GW, P>& w, const AttnArgs& a,
+template <typename T, int D, int GW, int P, bool kAppend>
+__device__ __forceinline__ void run_interval(Wave<T, D, GW, P, kAppend>& w, const AttnArgs& a,
                                              const int32_t* base, int64_t lo, int64_t hi, int iv,
                                              int sub) {
   const int N = a.num_seqs, Hkv = a.num_kv_heads;
@@ -811,7 +840,7 @@ __device__ __forceinline__ void run_interval(Wave<T, D, GW, P>& w, const AttnArg
     const int L = clamp_len(Lraw, a.len_cap);
     const int h0 = kvh * a.group + sub * GW;
     // the stream's last tile holds the new token (fused append)
-    const bool app = a.k_new != nullptr && t0 + seg == nt && L == Lraw;
+    const bool app = kAppend && t0 + seg == nt && L == Lraw;
     w.run(s, kvh, h0, t0 * kTile, min((t0 + seg) * kTile, L), app ? L - 1 : -1, sub == 0);
     if (t0 == 0 && seg == nt) {
       w.write_out(s, h0);  // the whole stream in one interval
@@ -826,7 +855,7 @@ __device__ __forceinline__ void run_interval(Wave<T, D, GW, P>& w, const AttnArg
   }
 }
 
-template <typename T, int D, int GW, int P>
+template <typename T, int D, int GW, int P, bool kAppend>
 __global__ void __launch_bounds__(64 * kMaxWavesPerBlock)
 attn_balanced_kernel(AttnArgs a) {
   __shared__ int32_t base[kMaxBalancedSeqs + 1];
@@ -865,7 +894,7 @@ attn_balanced_kernel(AttnArgs a) {
   const int sub = wv - grp * a.waves_per_group;
   if (grp >= a.groups_per_block || total == 0) return;
   const Intervals ivs(total, a.num_groups);
-  Wave<T, D, GW, P> w(a);
+  Wave<T, D, GW, P, kAppend> w(a);
   if (static_cast<int>(blockIdx.x) < a.static_blocks) {
     const int gidx = blockIdx.x * a.groups_per_block + grp;
     if (gidx >= ivs.Ws) return;
@@ -920,6 +949,7 @@ int env_knob(const char* name, int lo, int hi) {
 int knob_heads_per_wave() { return env_knob("PKV_ATTN_HEADS_PER_WAVE", 1, 4); }
 int knob_prefetch() { return env_knob("PKV_ATTN_PREFETCH", 2, 4); }
 int knob_mode() { return env_knob("PKV_ATTN_MODE", 1, 2); }  // 1 partition, 2 balanced
+int knob_append() { return env_knob("PKV_ATTN_APPEND", 1, 2); }  // 1 copy kernel, 2 folded
 int knob_waves_per_block() {
   const int v = env_knob("PKV_ATTN_WAVES_PER_BLOCK", 1, kMaxWavesPerBlock);
   return (v & (v - 1)) == 0 ? v : 0;
@@ -1085,10 +1115,10 @@ int resident_blocks(const void* kernel, int threads) {
   return v;
 }
 
-template <typename T, int D, int GW, int P>
+template <typename T, int D, int GW, int P, bool kAppend>
 pkv_status launch_main(const Plan& pl, AttnArgs& a, int num_seqs, hipStream_t st) {
   if (pl.mode == kBalancedMode) {
-    const void* k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, P>);
+    const void* k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, P, kAppend>);
     const int threads = 64 * pl.waves_per_block;
     int blocks = resident_blocks(k, threads);
     if (blocks <= 0)
@@ -1099,11 +1129,11 @@ pkv_status launch_main(const Plan& pl, AttnArgs& a, int num_seqs, hipStream_t st
     a.static_blocks = blocks;
     const int chunks = pl.max_chunks < a.num_groups ? pl.max_chunks : a.num_groups;
     const int tail = (chunks + pl.groups_per_block - 1) / pl.groups_per_block;
-    hipLaunchKernelGGL((attn_balanced_kernel<T, D, GW, P>), dim3(blocks + tail), dim3(threads), 0,
+    hipLaunchKernelGGL((attn_balanced_kernel<T, D, GW, P, kAppend>), dim3(blocks + tail), dim3(threads), 0,
                        st, a);
   } else {
     const dim3 grid(pl.blocks_per_item, pl.num_parts, num_seqs);
-    hipLaunchKernelGGL((attn_partition_kernel<T, D, GW, P>), grid, dim3(64 * pl.waves_per_block),
+    hipLaunchKernelGGL((attn_partition_kernel<T, D, GW, P, kAppend>), grid, dim3(64 * pl.waves_per_block),
                        0, st, a);
   }
   if (hipError_t e = hipGetLastError())
@@ -1119,24 +1149,26 @@ constexpr bool ring_built() {
   return P == 2 || (sizeof(T) == 1 && P <= 4) || (sizeof(T) == 2 && P <= max_prefetch<GW>());
 }
 
-template <typename T, int D, int GW>
+template <typename T, int D, int GW, bool kAppend>
 pkv_status launch_main_p(const Plan& pl, AttnArgs& a, int num_seqs, hipStream_t st) {
   if constexpr (ring_built<T, GW, 4>())
-    if (pl.prefetch == 4) return launch_main<T, D, GW, 4>(pl, a, num_seqs, st);
+    if (pl.prefetch == 4) return launch_main<T, D, GW, 4, kAppend>(pl, a, num_seqs, st);
   if constexpr (ring_built<T, GW, 3>())
-    if (pl.prefetch == 3) return launch_main<T, D, GW, 3>(pl, a, num_seqs, st);
-  return launch_main<T, D, GW, 2>(pl, a, num_seqs, st);
+    if (pl.prefetch == 3) return launch_main<T, D, GW, 3, kAppend>(pl, a, num_seqs, st);
+  return launch_main<T, D, GW, 2, kAppend>(pl, a, num_seqs, st);
 }
 
 // The grid of the balanced merge depends on W, which the main launch fixes;
 // a phase-2-only call recomputes it the same way.
-template <typename T, int D, int GW>
+template <typename T, int D, int GW, bool kAppend>
 int balanced_groups(const Plan& pl) {
-  const void* k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 2>);
+  const void* k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 2, kAppend>);
   if constexpr (ring_built<T, GW, 4>())
-    if (pl.prefetch == 4) k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 4>);
+    if (pl.prefetch == 4)
+      k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 4, kAppend>);
   if constexpr (ring_built<T, GW, 3>())
-    if (pl.prefetch == 3) k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 3>);
+    if (pl.prefetch == 3)
+      k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 3, kAppend>);
   int blocks = resident_blocks(k, 64 * pl.waves_per_block);
   const int max_blocks = kMaxWaveGroups / pl.groups_per_block;
   if (blocks > max_blocks) blocks = max_blocks;
@@ -1146,10 +1178,23 @@ int balanced_groups(const Plan& pl) {
 template <typename T, int D, int GW>
 pkv_status dispatch_gw(int phases, const Plan& pl, AttnArgs& a, int num_seqs, int num_q_heads,
                        hipStream_t st) {
+  // the fused-append variant (bf16/f32 pools only) has its own occupancy,
+  // so a phase-2-only call derives W from the same variant as phase 1
+  const bool append = !kQuant<T> && a.k_new != nullptr;
   if (phases & 1) {
-    if (pkv_status s = launch_main_p<T, D, GW>(pl, a, num_seqs, st)) return s;
+    pkv_status s;
+    if constexpr (!kQuant<T>)
+      s = append ? launch_main_p<T, D, GW, true>(pl, a, num_seqs, st)
+                 : launch_main_p<T, D, GW, false>(pl, a, num_seqs, st);
+    else
+      s = launch_main_p<T, D, GW, false>(pl, a, num_seqs, st);
+    if (s) return s;
   } else if (pl.mode == kBalancedMode) {
-    a.num_groups = balanced_groups<T, D, GW>(pl);
+    if constexpr (!kQuant<T>)
+      a.num_groups = append ? balanced_groups<T, D, GW, true>(pl)
+                            : balanced_groups<T, D, GW, false>(pl);
+    else
+      a.num_groups = balanced_groups<T, D, GW, false>(pl);
     if (a.num_groups <= 0)
       return pkv::fail(PKV_ERR_HIP, "pkv_attention_decode: occupancy query failed");
   }
@@ -1307,10 +1352,23 @@ pkv_status attention_impl(const char* who, int32_t phases, const void* q, const 
   a.v_scale = quant ? scales->v_scale : 1.0f;
   a.k_scales = quant ? scales->k_scales : nullptr;
   a.v_scales = quant ? scales->v_scales : nullptr;
-  a.k_new = nt.k;
-  a.v_new = nt.v;
-  a.new_slots = nt.slots;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // The append rides in the attention kernel for waves of up to two query
+  // heads; with more the kernel is issue-bound and a copy launch costs less.
+  const int ka = knob_append();
+  const bool fold = append && (ka ? ka == 2 : pl.gw <= 2);
+  a.k_new = fold ? nt.k : nullptr;
+  a.v_new = fold ? nt.v : nullptr;
+  a.new_slots = fold ? nt.slots : nullptr;
+  if (append && !fold && (phases & 1)) {
+    hipLaunchKernelGGL(append_rows_kernel, dim3(num_seqs), dim3(kAppendThreads), 0, st,
+                       static_cast<const uint4*>(nt.k), static_cast<const uint4*>(nt.v), nt.slots,
+                       seq_lens, static_cast<uint4*>(const_cast<void*>(k_cache)),
+                       static_cast<uint4*>(const_cast<void*>(v_cache)), a.row_bytes / 16,
+                       int64_t(geom->num_blocks) * geom->block_size, pl.len_cap);
+    if (hipError_t e = hipGetLastError())
+      return pkv::fail(PKV_ERR_HIP, "%s: append launch failed: %s", who, hipGetErrorString(e));
+  }
   if (geom->dtype == PKV_FP8_E4M3)
     return dispatch<fp8_e4m3, 128>(phases, pl, a, num_seqs, num_q_heads, st);
   if (geom->dtype == PKV_INT8)
