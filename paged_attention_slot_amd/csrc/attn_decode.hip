@@ -652,65 +652,74 @@ attn_partition_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of n workspace rows row0, row0 + step, ... into one output
-// row, by one 256-thread workgroup:
-//   1. the common reference M = max_p m_p (threads stride over the rows),
-//   2. weights w_p = exp2(m_p - M) into LDS and sum_p w_p l_p,
-//   3. sum_p w_p acc_p: thread (stream, q) accumulates float4 column q of rows
-//      p = stream (mod kStreams), all loads independent,
-//   4. the partial rows meet in LDS; out = acc / l (zeros when n == 0).
+// row, by one 256-thread workgroup, in chunks of 64 rows with one memory round
+// trip each: every thread (stream, q) loads float4 column q of its rows of the
+// chunk (p = stream mod kStreams) while wave 0 loads the chunk's 64 (m, l)
+// pairs; wave 0 moves the running reference to M' = max(M, max m_p), puts the
+// weights w_p = exp2(m_p - M') and the rescale exp2(M - M') in LDS and keeps
+// sum_p w_p l_p; after one barrier every thread rescales its partial row and
+// adds its weighted rows.  The partial rows meet in LDS at the end; out = acc /
+// l (zeros when n == 0).
 // ---------------------------------------------------------------------------
 constexpr int kMergeThreads = 256;
-constexpr int kMergeChunk = 1024;  // rows whose weights sit in LDS at once
+constexpr int kMergeRows = 64;  // rows per chunk (one per lane of wave 0)
 
 template <typename T, int D>
 __device__ __forceinline__ void merge_rows(const AttnArgs& a, int n, int64_t row0, int64_t step,
                                            char* dst_row) {
   constexpr int kQ = D / 4;                        // float4 columns per row
   constexpr int kStreams = kMergeThreads / kQ;     // rows folded in parallel
-  const int tid = threadIdx.x, wv = tid >> 6;
+  constexpr int kPer = kMergeRows / kStreams;      // rows per thread per chunk
+  const int tid = threadIdx.x, lane = tid & 63;
+  const bool lead = wave_index() == 0;
   const float4* acc4 = reinterpret_cast<const float4*>(a.ws_acc);
 
-  __shared__ float red[4];
-  __shared__ float wts[kMergeChunk];
+  // double-buffered: wave 0 fills chunk c + 1's weights only after every
+  // wave has passed chunk c's barrier, i.e. finished reading chunk c - 1's
+  __shared__ float wts[2][kMergeRows];
+  __shared__ float rescale[2];
+  __shared__ float lsum_sh;
   __shared__ float4 part_out[kStreams][kQ];
 
-  float mx = -INFINITY;
-  for (int p = tid; p < n; p += kMergeThreads) mx = fmaxf(mx, a.ws_ml[row0 + p * step].x);
-  mx = pkv::wave_max(mx);
-  if ((tid & 63) == 0) red[wv] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-
   const int stream = tid / kQ, q = tid % kQ;
-  float ls = 0.f;
+  float M = -INFINITY, ls = 0.f;  // wave 0's running reference and sum
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c0 = 0; c0 < n; c0 += kMergeChunk) {
-    const int c1 = min(n, c0 + kMergeChunk);
-    for (int p = c0 + tid; p < c1; p += kMergeThreads) {
-      const float2 v = a.ws_ml[row0 + p * step];
-      const float wt = pkv::fast_exp2(v.x - M);
-      wts[p - c0] = wt;
-      ls = fmaf(wt, v.y, ls);
+  int buf = 0;
+  for (int c0 = 0; c0 < n; c0 += kMergeRows, buf ^= 1) {
+    float4 x[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int p = c0 + stream + kStreams * k;
+      x[k] = p < n ? acc4[(row0 + p * step) * kQ + q] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (lead) {
+      const int p = c0 + lane;
+      const float2 v = p < n ? a.ws_ml[row0 + p * step] : make_float2(-INFINITY, 0.f);
+      const float Mn = fmaxf(M, pkv::wave_max(v.x));
+      const float al = M == -INFINITY ? 0.f : pkv::fast_exp2(M - Mn);
+      const float wt = p < n ? pkv::fast_exp2(v.x - Mn) : 0.f;
+      ls = ls * al + pkv::wave_sum(wt * v.y);
+      M = Mn;
+      wts[buf][lane] = wt;
+      if (lane == 0) rescale[buf] = al;
     }
     __syncthreads();
-#pragma unroll 4
-    for (int p = c0 + stream; p < c1; p += kStreams) {
-      const float wt = wts[p - c0];
-      const float4 x = acc4[(row0 + p * step) * kQ + q];
-      o.x = fmaf(wt, x.x, o.x);
-      o.y = fmaf(wt, x.y, o.y);
-      o.z = fmaf(wt, x.z, o.z);
-      o.w = fmaf(wt, x.w, o.w);
+    const float al = rescale[buf];
+    o.x *= al; o.y *= al; o.z *= al; o.w *= al;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const float wt = wts[buf][stream + kStreams * k];
+      o.x = fmaf(wt, x[k].x, o.x);
+      o.y = fmaf(wt, x[k].y, o.y);
+      o.z = fmaf(wt, x[k].z, o.z);
+      o.w = fmaf(wt, x[k].w, o.w);
     }
-    __syncthreads();
   }
-  ls = pkv::wave_sum(ls);
-  if ((tid & 63) == 0) red[wv] = ls;
   part_out[stream][q] = o;
+  if (lead && lane == 0) lsum_sh = ls;
   __syncthreads();
   if (tid >= kQ) return;
-  const float lsum = (red[0] + red[1]) + (red[2] + red[3]);
+  const float lsum = lsum_sh;
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
   float4 rr = part_out[0][q];
 #pragma unroll
