@@ -63,9 +63,9 @@ struct MultiArgs {
 template <int D, int NW, int Q>
 __global__ void __launch_bounds__(64 * NW)
 attn_multi_kernel(MultiArgs a) {
-  __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D>()];
-  __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D>()];
-  __shared__ float s_lds[Q == pkv::mfma::kInt8 ? 2 * kKT : 1];
+  __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D, NW>()];
+  __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D, NW>()];
+  __shared__ float s_lds[pkv::mfma::s_lds_elems<Q, NW>()];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(tid >> 6));
@@ -196,9 +196,13 @@ pkv_status multi_plan(int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
     return pkv::fail(PKV_ERR_INVALID_ARG, "%s: partition_tokens %d must be a multiple of %d",
                      who, partition_tokens, kKT);
   const int mq = max_q_per_seq > 0 ? max_q_per_seq : 1;
-  const int per64 = 64 / G;
-  const int rows = (mq < per64 ? mq : per64) * G;
-  pl->nw = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+  // 16 rows per wave, up to 4 waves; 8 (128 rows) for longer chunks of
+  // bf16 rows of 128, whose K/V tiles then serve twice the rows per staging
+  // (one-byte and 64-wide tiles have 256 chunks, too few for 8 waves)
+  const bool wide = g->head_dim == 128 && !quant;
+  const int cap = (wide ? 128 : 64) / G;
+  const int rows = (mq < cap ? mq : cap) * G;
+  pl->nw = rows <= 16 ? 1 : (rows <= 32 ? 2 : (rows <= 64 ? 4 : 8));
   pl->q_per_block = 16 * pl->nw / G;
   pl->qblocks = (mq + pl->q_per_block - 1) / pl->q_per_block;
   const int len = max_seq_len > 0 ? max_seq_len : 1;
@@ -236,7 +240,11 @@ void launch_multi(const MultiPlan& pl, const MultiArgs& a, int num_seqs, int num
   switch (pl.nw) {
     case 1: hipLaunchKernelGGL((attn_multi_kernel<D, 1, Q>), grid, dim3(64), 0, st, a); break;
     case 2: hipLaunchKernelGGL((attn_multi_kernel<D, 2, Q>), grid, dim3(128), 0, st, a); break;
-    default: hipLaunchKernelGGL((attn_multi_kernel<D, 4, Q>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((attn_multi_kernel<D, 4, Q>), grid, dim3(256), 0, st, a); break;
+    default:
+      if constexpr (D == 128 && Q == pkv::mfma::kBf16)  // the plan's condition for 8 waves
+        hipLaunchKernelGGL((attn_multi_kernel<D, 8, Q>), grid, dim3(512), 0, st, a);
+      break;
   }
   if (pl.num_parts > 1 && total_q > 0)
     hipLaunchKernelGGL((attn_multi_merge_kernel<D>), dim3(a.num_q_heads, total_q), dim3(64), 0,

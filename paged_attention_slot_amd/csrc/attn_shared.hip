@@ -106,9 +106,9 @@ __device__ __forceinline__ int seq_prefix(const SharedArgs& a, int s, int L) {
 template <int D, int NW, int Q>
 __global__ void __launch_bounds__(64 * NW)
 attn_prefix_kernel(SharedArgs a) {
-  __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D>()];
-  __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D>()];
-  __shared__ float s_lds[Q == pkv::mfma::kInt8 ? 2 * kKT : 1];
+  __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D, NW>()];
+  __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D, NW>()];
+  __shared__ float s_lds[pkv::mfma::s_lds_elems<Q, NW>()];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int gi = blockIdx.z, g = blockIdx.y;
@@ -136,8 +136,10 @@ attn_prefix_kernel(SharedArgs a) {
                                 a.num_kv_heads, a.v_scale,     a.k_scales,
                                 a.v_scales};
   // Positions every member of the block sees: up to the shortest one's last
-  // (one member's length per lane, then a wave minimum: one round trip).
-  int lmin = lane < jn ? clamp_len(a.seq_lens[first + j0 + lane], a.len_cap) : a.len_cap;
+  // (members' lengths strided over the lanes, then a wave minimum).
+  int lmin = a.len_cap;
+  for (int m = lane; m < jn; m += 64)
+    lmin = min(lmin, clamp_len(a.seq_lens[first + j0 + m], a.len_cap));
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) lmin = min(lmin, __shfl_xor(lmin, off));
   pkv::mfma::RowAcc<D> r;
@@ -153,9 +155,9 @@ attn_prefix_kernel(SharedArgs a) {
 template <int D, int NW, int Q>
 __global__ void __launch_bounds__(64 * NW)
 attn_suffix_kernel(SharedArgs a) {
-  __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D>()];
-  __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D>()];
-  __shared__ float s_lds[Q == pkv::mfma::kInt8 ? 2 * kKT : 1];
+  __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D, NW>()];
+  __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D, NW>()];
+  __shared__ float s_lds[pkv::mfma::s_lds_elems<Q, NW>()];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int s = blockIdx.z, g = blockIdx.y, part = blockIdx.x;
@@ -272,6 +274,8 @@ pkv_status shared_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_groups
   if (num_seqs > 65535 || num_groups > 65535 || g->num_kv_heads > 65535)
     return pkv::fail(PKV_ERR_INVALID_ARG, "%s: more than 65535 sequences, groups or KV heads", who);
   const int mg = max_group_size > 0 ? max_group_size : 1;
+  // 16 (member, head) rows per wave, up to 4 waves (eight measured no faster
+  // on the shared-prefix configuration)
   const int per64 = 64 / G;
   const int rows = (mg < per64 ? mg : per64) * G;
   pl->nw_pre = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);

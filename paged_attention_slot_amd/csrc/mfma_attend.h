@@ -8,9 +8,13 @@
 //    workgroup as [position][d] rows, read back as MFMA operands: K with
 //    plain 16-byte reads, V through gfx950's transposing LDS read
 //    (ds_read_b64_tr_b16), which hands each lane the 4 positions of one d
-//    that the V^T operand needs; the next tile's loads are issued before the
-//    current tile's matrix work and a barrier that waits only for LDS keeps
-//    them in flight.
+//    that the V^T operand needs.  With several waves two LDS tile buffers are
+//    used in turn, so one barrier per tile separates a tile's staging from
+//    its reading (a wave stages tile i + 1 only after the barrier of tile i,
+//    which every wave passes only once done with tile i - 1 in the same
+//    buffer); a single wave's LDS accesses run in order, so it uses one.  The next
+//    tile's global loads are issued before the current tile's matrix work,
+//    and the barrier waits only for LDS, so they stay in flight.
 //  * Scores as S^T = K Q^T with v_mfma_f32_16x16x32_bf16: a lane's result
 //    fragment holds 8 positions of one query row (its lane & 15), so the
 //    online softmax (log2 units) needs only the ^16 and ^32 lane exchanges,
@@ -42,8 +46,19 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kKT = 32;             // positions per K/V tile
 constexpr float kRefInit = -1e30f;  // reference of a row with no position yet
 
-template <int D> constexpr int k_lds_elems() { return kKT * (D + 8); }
-template <int D> constexpr int v_lds_elems() { return kKT * (D + 8); }
+// LDS of one workgroup of NW waves: K/V tile buffers (two for several
+// waves: the next tile is staged into one while the other is read; one
+// wave's LDS accesses run in order, so it needs one), and for INT8 the
+// tiles' position scales.
+// Row strides in LDS (bf16 elements): K rows padded by 16 bytes, so the
+// 16-byte operand reads of 8 consecutive rows fall in different banks; V rows
+// by 32 bytes, so the transposing reads (4 rows x 4 eight-byte columns per 16
+// lanes) do.
+template <int D> constexpr int k_stride() { return D + 8; }
+template <int D> constexpr int v_stride() { return D + 16; }
+template <int NW> constexpr int lds_tiles() { return NW == 1 ? 1 : 2; }
+template <int D, int NW> constexpr int k_lds_elems() { return lds_tiles<NW>() * kKT * k_stride<D>(); }
+template <int D, int NW> constexpr int v_lds_elems() { return lds_tiles<NW>() * kKT * v_stride<D>(); }
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -75,6 +90,9 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Element kinds of the cache pools.
 enum Kind : int { kBf16 = 0, kFp8 = 1, kInt8 = 2 };
+template <int Q, int NW> constexpr int s_lds_elems() {
+  return Q == kInt8 ? lds_tiles<NW>() * 2 * kKT : 1;
+}
 
 // The K/V history a workgroup reads: one KV head through one table row.
 struct History {
@@ -142,8 +160,9 @@ __device__ __forceinline__ void start(RowAcc<D>& r) {
 // (every wave must call this with the same range), folding them into ``r``
 // (start() it first; further calls continue the same online softmax).
 // ``q`` points at this lane's query row (D bf16, 16-byte aligned); it is read
-// only if row_ok.  Q is the pools' element kind; INT8 needs ``s_lds`` (64
-// floats of LDS) for a tile's scales.  p_all (the same in every lane) is a position every live
+// only if row_ok.  k_lds / v_lds hold k_lds_elems<D, NW>() elements.  Q is
+// the pools' element kind; INT8 needs ``s_lds`` (s_lds_elems<Q, NW>() floats
+// of LDS) for the tiles' scales.  p_all (the same in every lane) is a position every live
 // row of the workgroup sees: tiles entirely at or before it, and inside
 // [t_lo, t_hi), skip the per-score mask.  t_lo must be a multiple of 8 (a
 // lane's positions of a tile then lie in one block).  PD tiles are in flight
@@ -165,7 +184,8 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
   constexpr int kEB = Q == kBf16 ? 2 : 1;   // bytes per element
   constexpr int kKS = D / 32;            // k-steps of the score product
   constexpr int kDT = D / 16;            // 16-wide d tiles of the output
-  constexpr int kKStride = D + 8;        // K and V rows in LDS, bf16 elements (16 B pad)
+  constexpr int kKStride = k_stride<D>();  // K rows in LDS, bf16 elements
+  constexpr int kVStride = v_stride<D>();  // V rows
   constexpr int kEPC = 16 / kEB;         // elements per 16-byte chunk
   constexpr int kChunksPerRow = D / kEPC;  // 16-byte chunks per K/V row
   constexpr int kChunks = kKT * kChunksPerRow;
@@ -246,13 +266,16 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
     }
   };
   // Stage the tile of buffer j: K and V as [pos][d] bf16 (codes decoded).
-  auto stage = [&](int j) {
+  constexpr int kTileElems = kKT * kKStride;   // one LDS tile buffer of K
+  constexpr int kVTileElems = kKT * kVStride;  // and of V
+  auto stage = [&](int j, int buf) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int off = (pg * kPer + i) * kKStride + cc * kEPC;
+      const int off = buf * kTileElems + (pg * kPer + i) * kKStride + cc * kEPC;
+      const int voff = buf * kVTileElems + (pg * kPer + i) * kVStride + cc * kEPC;
       if constexpr (Q == kBf16) {
         *reinterpret_cast<uint4*>(k_lds + off) = nk[j][i];
-        *reinterpret_cast<uint4*>(v_lds + off) = nv[j][i];
+        *reinterpret_cast<uint4*>(v_lds + voff) = nv[j][i];
       } else {
         float f[16];
         uint32_t w[8];
@@ -264,24 +287,27 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
         decode_codes<Q>(nv[j][i], f);
 #pragma unroll
         for (int e = 0; e < 8; ++e) w[e] = bf16_pair_exact(f[2 * e], f[2 * e + 1]);
-        *reinterpret_cast<uint4*>(v_lds + off) = make_uint4(w[0], w[1], w[2], w[3]);
-        *reinterpret_cast<uint4*>(v_lds + off + 8) = make_uint4(w[4], w[5], w[6], w[7]);
+        *reinterpret_cast<uint4*>(v_lds + voff) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(v_lds + voff + 8) = make_uint4(w[4], w[5], w[6], w[7]);
       }
     }
     if constexpr (Q == kInt8) {
       if (tid < kKT) {
-        s_lds[tid] = nks[j];
-        s_lds[kKT + tid] = nvs[j];
+        s_lds[2 * kKT * buf + tid] = nks[j];
+        s_lds[2 * kKT * buf + kKT + tid] = nvs[j];
       }
     }
   };
   // This lane's V^T reads: row 4 (lane >> 4) + (lane & 15) / 4 (+ 16 for the
   // second half of the k dimension), columns 4 ((lane & 15) % 4) .. + 3 of
   // each 16-wide d tile.
-  const uint16_t* v_rd = v_lds + (4 * quad + ((lane & 15) >> 2)) * kKStride + 4 * (lane & 3);
+  const uint16_t* v_rd = v_lds + (4 * quad + ((lane & 15) >> 2)) * kVStride + 4 * (lane & 3);
 
-  // One staged tile's matrix work.
-  auto compute = [&](int t0) {
+  // One staged tile's matrix work (LDS tile buffer buf).
+  auto compute = [&](int t0, int buf) {
+    const uint16_t* kt = k_lds + buf * kTileElems;
+    const uint16_t* vt = v_rd + buf * kVTileElems;
+    const float* st = s_lds + 2 * kKT * buf;
     // Uniform: every live row sees every position of the tile.
     const bool full = t0 + kKT - 1 <= p_all && t0 + kKT <= t_hi;
     // S^T tiles: positions 16pt + 4 quad + i of row (lane & 15).
@@ -293,14 +319,14 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks) {
         const uint4 ka = *reinterpret_cast<const uint4*>(
-            k_lds + (16 * pt + (lane & 15)) * kKStride + 32 * ks + 8 * quad);
+            kt + (16 * pt + (lane & 15)) * kKStride + 32 * ks + 8 * quad);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(qf[ks]), acc, 0,
                                                       0, 0);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float v = acc[i] * scale_log2;
-        if constexpr (Q == kInt8) v *= s_lds[16 * pt + 4 * quad + i];
+        if constexpr (Q == kInt8) v *= st[16 * pt + 4 * quad + i];
         if (!full) {
           const int t = t0 + 16 * pt + 4 * quad + i;
           v = (row_ok && t <= p_row && t < t_hi) ? v : -INFINITY;
@@ -335,12 +361,12 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
         p0 *= h.v_scale;
         p1 *= h.v_scale;
       } else if constexpr (Q == kInt8) {
-        p0 *= s_lds[kKT + 16 * ((2 * k) >> 2) + 4 * quad + ((2 * k) & 3)];
-        p1 *= s_lds[kKT + 16 * ((2 * k + 1) >> 2) + 4 * quad + ((2 * k + 1) & 3)];
+        p0 *= st[kKT + 16 * ((2 * k) >> 2) + 4 * quad + ((2 * k) & 3)];
+        p1 *= st[kKT + 16 * ((2 * k + 1) >> 2) + 4 * quad + ((2 * k + 1) & 3)];
       }
-      const uint32_t h = cvt_pk_bf16(p0, p1);
-      ph[k] = h;
-      pl[k] = cvt_pk_bf16(p0 - __uint_as_float(h << 16), p1 - __uint_as_float(h & 0xFFFF0000u));
+      const uint32_t hw = cvt_pk_bf16(p0, p1);
+      ph[k] = hw;
+      pl[k] = cvt_pk_bf16(p0 - __uint_as_float(hw << 16), p1 - __uint_as_float(hw & 0xFFFF0000u));
     }
     psum = sum_across_rows16(psum);
     r.lsum += psum;
@@ -349,29 +375,34 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt) {
       // V^T[16 dt + (lane & 15)][positions 4 quad .. + 3 and 16 + 4 quad .. + 3]
-      const uint2 lo = lds_read_tr16(v_rd + 16 * dt);
-      const uint2 hi = lds_read_tr16(v_rd + 16 * kKStride + 16 * dt);
+      const uint2 lo = lds_read_tr16(vt + 16 * dt);
+      const uint2 hi = lds_read_tr16(vt + 16 * kVStride + 16 * dt);
       const bf16x8_t va = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
       f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfh, r.o[dt], 0, 0, 0);
       r.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfl, acc, 0, 0, 0);
-    }  };
+    }
+  };
 
 #pragma unroll
   for (int j = 0; j < PD; ++j)
     if (t_lo + j * kKT < t_hi) fetch(j, t_lo + j * kKT);
+  int buf = 0;
   for (int t0 = t_lo; t0 < t_hi; t0 += PD * kKT) {
 #pragma unroll
     for (int j = 0; j < PD; ++j) {
       const int t = t0 + j * kKT;
       if (t >= t_hi) break;  // uniform
-      stage(j);
+      stage(j, buf);
       lds_barrier();
-      // the buffer just staged takes the tile PD ahead, in flight meanwhile
+      // the register buffer just staged takes the tile PD ahead, in flight
+      // meanwhile
       if (t + PD * kKT < t_hi) fetch(j, t + PD * kKT);
-      compute(t);
-      lds_barrier();  // every wave is done reading before the next stage
+      compute(t, buf);
+      if constexpr (lds_tiles<NW>() == 2) buf ^= 1;
     }
   }
+  // the caller may reuse the LDS (another pass) right after
+  lds_barrier();
 }
 
 // Store this lane's fragment of a row's state as a piece: D floats of

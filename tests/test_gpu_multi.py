@@ -85,6 +85,18 @@ def test_chunks_of_mixed_sizes(Hq, Hkv, D, B):
     assert not got[sum(nq[:5]):sum(nq[:5]) + 3].any()   # positions -3..-1 of sequence 5
 
 
+@pytest.mark.parametrize("Hq,Hkv,D,B", [(32, 8, 128, 16), (12, 4, 64, 32), (16, 16, 128, 8)],
+                         ids=lambda v: str(v))
+def test_long_prefill_chunks(Hq, Hkv, D, B):
+    """Prefill-shaped chunks (hundreds of query tokens per sequence: workgroups
+    of four waves with two 16-row blocks each, ragged last query block, a
+    group size of 3 whose rows straddle tokens) against the oracle."""
+    lens = [512, 700, 301, 64]
+    nq = [512, 200, 301, 13]
+    got, ref, _ = run_case(700 + Hq + D, lens, nq, Hq, Hkv, D, B)
+    say("  gate", assert_gate(got, ref, "bf16", "prefill chunks"))
+
+
 @pytest.mark.parametrize("pt", [32, 64, 256])
 @pytest.mark.parametrize("Hq,Hkv", [(16, 8), (64, 8), (32, 32)])
 def test_partitions_match_oracle(pt, Hq, Hkv):

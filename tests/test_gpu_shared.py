@@ -130,6 +130,28 @@ def test_members_shorter_than_the_shared_blocks_and_empty_sequences():
         assert not got[3].any()
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (8, 2)])
+def test_groups_of_more_than_64_members_of_varying_lengths(Hq, Hkv):
+    """100 sequences on the same three blocks with lengths 20..48 (the shortest
+    at member 90, in the second row block for G = 1): every member masks at
+    its own length, and each row block's common limit is its own shortest
+    member's."""
+    from paged_attention_slot_amd.runtime import to_host_bits
+    B, n = 16, 100
+    rng = np.random.default_rng(21)
+    lens = rng.integers(24, 49, n).astype(np.int32)
+    lens[90] = 20
+    tables = [[5, 7, 9]] * n
+    ops, (q, kp, vp, tb, ln), ref = hand_case(tables, lens, Hq, Hkv, 128, B, 12, 12)
+    starts, plens, mg, mp, ms = ops.prefix_groups(np.asarray(tables, np.int32), lens, B)
+    say(f"  case {n} members Hq={Hq} Hkv={Hkv}: groups={starts.tolist()} prefix={plens.tolist()}")
+    out = ops.attention_decode_shared(q, kp, vp, tb, ln, 1 / np.sqrt(128),
+                                      torch.from_numpy(starts).cuda(),
+                                      torch.from_numpy(plens).cuda(), mg, mp, ms, max_seq_len=48)
+    torch.cuda.synchronize()
+    assert_gate(to_f64(to_host_bits(out)), ref, "bf16", f"{n} members")
+
+
 def test_matches_the_plain_decode_kernel_on_the_config():
     """Both entry points on the same pools: each within the gate of the
     oracle, and within twice the gate of each other."""
