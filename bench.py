@@ -692,8 +692,8 @@ def main() -> int:
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("attn_balanced_kernel" if step.split["mode"] == "balanced"
-                       else "attn_partition_kernel"),
+            "kernel": {"balanced": "attn_balanced_kernel", "partitions": "attn_partition_kernel",
+                       "matrix": "attn_multi_kernel"}[step.split["mode"]],
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

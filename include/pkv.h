@@ -270,11 +270,24 @@ pkv_status pkv_swap_in(const int32_t* pairs, int32_t num_pairs, const pkv_host_p
 /* Split-KV partition length (tokens) that pkv_attention_decode uses when its
  * partition_tokens argument is 0 and it splits by fixed partitions: max_seq_len
  * rounded up to a whole tile (no split) when one partition per sequence is
- * enough, else a multiple of both block_size and 16.  Returns 0 when the
- * automatic plan is the balanced split (shares of equal work per wave group,
- * see pkv_attention_decode) or on invalid arguments. */
+ * enough, else a multiple of both block_size and 16 (of 32 on the matrix-core
+ * route).  Returns 0 when the automatic plan is the balanced split (shares of
+ * equal work per wave group, see pkv_attention_decode) or on invalid
+ * arguments. */
 int32_t pkv_attention_partition_tokens(int32_t num_seqs, int32_t num_q_heads,
                                        int32_t max_seq_len, const pkv_geom* geom);
+
+/* Which kernels pkv_attention_decode (and its _phase, _append and _quant
+ * forms) runs for these sizes: PKV_ROUTE_PARTITIONS (vector kernels, fixed
+ * partitions), PKV_ROUTE_BALANCED (vector kernels, the balanced split) or
+ * PKV_ROUTE_MATRIX (groups of 8 or more query heads per KV head at head_dim
+ * 128, bf16 or one-byte pools, partition_tokens 0 or a multiple of 32: the
+ * matrix-core pass of pkv_attention_multi with one query per sequence, fixed
+ * partitions merged by log-sum-exp; PKV_ATTN_MODE overrides).  -1 on invalid
+ * arguments. */
+enum { PKV_ROUTE_PARTITIONS = 0, PKV_ROUTE_BALANCED = 1, PKV_ROUTE_MATRIX = 2 };
+int32_t pkv_attention_decode_route(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
+                                   int32_t partition_tokens, const pkv_geom* geom);
 
 /* Workspace bytes pkv_attention_decode needs for these sizes (0 when no split
  * happens).  partition_tokens as for pkv_attention_decode (0 = automatic).
@@ -307,7 +320,12 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *                 share of 85 % of all K/V tiles of the batch, and further
  *                 workgroups, dispatched as those retire, take small chunks of
  *                 the rest; a sequence's history that spans several of these
- *                 intervals is merged the same way.
+ *                 intervals is merged the same way.  Groups of 8 or more
+ *                 query heads per KV head (head_dim 128) run on the matrix
+ *                 cores instead, with fixed partitions (a multiple of 32;
+ *                 automatic: about 3072 (sequence, KV head, partition) items
+ *                 of at least 256 positions); see
+ *                 pkv_attention_decode_route.
  *   workspace     device buffer of at least pkv_attention_workspace_bytes(...)
  *                 bytes (may be NULL when that is 0); contents on entry are
  *                 ignored.  Calls that may run at the same time need
@@ -443,7 +461,10 @@ pkv_status pkv_attention_multi_quant(const void* q, const int32_t* q_offsets, co
  *   PKV_ATTN_WAVES_PER_BLOCK 1,2,4,8  fixed partitions: waves per workgroup
  *                                  (the waves of one (sequence, partition)
  *                                  are packed together)
- *   PKV_ATTN_MODE            1 = fixed partitions, 2 = balanced split
+ *   PKV_ATTN_MODE            1 = fixed partitions, 2 = balanced split,
+ *                                  3 = the matrix-core route where it applies
+ *   PKV_ATTN_PARTS_PER_WG    1..65535  matrix-core passes: consecutive
+ *                                  partitions one workgroup walks
  *   PKV_ATTN_APPEND          pkv_attention_decode_append: 1 = copy kernel
  *                                  first, 2 = folded into the attention kernel
  * They change speed and register use, never results beyond fp32 rounding

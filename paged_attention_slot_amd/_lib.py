@@ -20,6 +20,7 @@ P_i64 = ctypes.POINTER(ctypes.c_int64)
 
 PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_NO_FREE_BLOCKS, PKV_ERR_HIP = range(5)
 PKV_F32, PKV_BF16, PKV_FP8_E4M3, PKV_INT8 = 0, 1, 2, 3
+PKV_ROUTE_PARTITIONS, PKV_ROUTE_BALANCED, PKV_ROUTE_MATRIX = 0, 1, 2
 
 
 class PkvGeom(ctypes.Structure):
@@ -61,6 +62,7 @@ SIGNATURES = {
                                     c_void_p, c_float, c_void_p, c_i32, c_i32, c_i32, c_i32, c_i32,
                                     c_i32, c_void_p, c_size, ctypes.POINTER(PkvGeom), c_void_p]),
     "pkv_attention_partition_tokens": (c_i32, [c_i32, c_i32, c_i32, ctypes.POINTER(PkvGeom)]),
+    "pkv_attention_decode_route": (c_i32, [c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(PkvGeom)]),
     "pkv_attention_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32,
                                                ctypes.POINTER(PkvGeom)]),
     "pkv_attention_decode": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_i32, c_void_p,

@@ -52,6 +52,8 @@
 #include <unordered_map>
 
 #include "geom.h"
+#include "lse_merge.h"
+#include "mfma_route.h"
 #include "pkv_device.h"
 
 namespace {
@@ -66,7 +68,7 @@ constexpr int kDynamicPerMille = 150;   // balanced split: tiles handed out dyna
 constexpr int kMinChunkTiles = 4;       // smallest dynamic chunk
 constexpr int kMaxChunks = 8192;        // the workspace is sized for this many chunks
 
-enum Mode : int { kPartitionMode = 0, kBalancedMode = 1 };
+enum Mode : int { kPartitionMode = 0, kBalancedMode = 1, kMatrixMode = 2 };
 
 struct AttnArgs {
   const void* q;
@@ -651,90 +653,8 @@ attn_partition_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of n workspace rows row0, row0 + step, ... into one output
-// row, by one 256-thread workgroup, in chunks of 64 rows with one memory round
-// trip each: every thread (stream, q) loads float4 column q of its rows of the
-// chunk (p = stream mod kStreams) while wave 0 loads the chunk's 64 (m, l)
-// pairs; wave 0 moves the running reference to M' = max(M, max m_p), puts the
-// weights w_p = exp2(m_p - M') and the rescale exp2(M - M') in LDS and keeps
-// sum_p w_p l_p; after one barrier every thread rescales its partial row and
-// adds its weighted rows.  The partial rows meet in LDS at the end; out = acc /
-// l (zeros when n == 0).
-// ---------------------------------------------------------------------------
-constexpr int kMergeThreads = 256;
-constexpr int kMergeRows = 64;  // rows per chunk (one per lane of wave 0)
-
-template <typename T, int D>
-__device__ __forceinline__ void merge_rows(const AttnArgs& a, int n, int64_t row0, int64_t step,
-                                           char* dst_row) {
-  constexpr int kQ = D / 4;                        // float4 columns per row
-  constexpr int kStreams = kMergeThreads / kQ;     // rows folded in parallel
-  constexpr int kPer = kMergeRows / kStreams;      // rows per thread per chunk
-  const int tid = threadIdx.x, lane = tid & 63;
-  const bool lead = wave_index() == 0;
-  const float4* acc4 = reinterpret_cast<const float4*>(a.ws_acc);
-
-  // double-buffered: wave 0 fills chunk c + 1's weights only after every
-  // wave has passed chunk c's barrier, i.e. finished reading chunk c - 1's
-  __shared__ float wts[2][kMergeRows];
-  __shared__ float rescale[2];
-  __shared__ float lsum_sh;
-  __shared__ float4 part_out[kStreams][kQ];
-
-  const int stream = tid / kQ, q = tid % kQ;
-  float M = -INFINITY, ls = 0.f;  // wave 0's running reference and sum
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  int buf = 0;
-  for (int c0 = 0; c0 < n; c0 += kMergeRows, buf ^= 1) {
-    float4 x[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int p = c0 + stream + kStreams * k;
-      x[k] = p < n ? acc4[(row0 + p * step) * kQ + q] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    if (lead) {
-      const int p = c0 + lane;
-      const float2 v = p < n ? a.ws_ml[row0 + p * step] : make_float2(-INFINITY, 0.f);
-      const float Mn = fmaxf(M, pkv::wave_max(v.x));
-      const float al = M == -INFINITY ? 0.f : pkv::fast_exp2(M - Mn);
-      const float wt = p < n ? pkv::fast_exp2(v.x - Mn) : 0.f;
-      ls = ls * al + pkv::wave_sum(wt * v.y);
-      M = Mn;
-      wts[buf][lane] = wt;
-      if (lane == 0) rescale[buf] = al;
-    }
-    __syncthreads();
-    const float al = rescale[buf];
-    o.x *= al; o.y *= al; o.z *= al; o.w *= al;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const float wt = wts[buf][stream + kStreams * k];
-      o.x = fmaf(wt, x[k].x, o.x);
-      o.y = fmaf(wt, x[k].y, o.y);
-      o.z = fmaf(wt, x[k].z, o.z);
-      o.w = fmaf(wt, x[k].w, o.w);
-    }
-  }
-  part_out[stream][q] = o;
-  if (lead && lane == 0) lsum_sh = ls;
-  __syncthreads();
-  if (tid >= kQ) return;
-  const float lsum = lsum_sh;
-  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-  float4 rr = part_out[0][q];
-#pragma unroll
-  for (int k = 1; k < kStreams; ++k) {
-    const float4 x = part_out[k][q];
-    rr.x += x.x; rr.y += x.y; rr.z += x.z; rr.w += x.w;
-  }
-  const float f[4] = {rr.x * inv, rr.y * inv, rr.z * inv, rr.w * inv};
-  if constexpr (sizeof(T) == 2) {
-    reinterpret_cast<uint2*>(dst_row)[q] =
-        make_uint2(pkv::pack_bf16x2(f[0], f[1]), pkv::pack_bf16x2(f[2], f[3]));
-  } else {
-    reinterpret_cast<float4*>(dst_row)[q] = make_float4(f[0], f[1], f[2], f[3]);
-  }
-}
+using pkv::kMergeThreads;
+using pkv::merge_rows;
 
 // Partition mode merge: one workgroup per (query head, sequence).
 template <typename T, int D>
@@ -745,7 +665,7 @@ attn_merge_kernel(AttnArgs a) {
   const int np = (L + a.part_tokens - 1) / a.part_tokens;
   const int64_t row0 = (int64_t(s) * a.num_q_heads + h) * a.num_parts;
   char* dst = static_cast<char*>(a.out) + ((int64_t(s) * a.num_q_heads + h) * D) * sizeof(T);
-  merge_rows<T, D>(a, np, row0, 1, dst);
+  merge_rows<T, D>(a.ws_acc, a.ws_ml, np, row0, 1, dst);
 }
 
 // The append of pkv_attention_decode_append where the attention kernel does
@@ -931,7 +851,7 @@ attn_merge_balanced_kernel(AttnArgs a) {
   const int nt = stream_tiles(a, s);
   char* dst = static_cast<char*>(a.out) + ((int64_t(s) * a.num_q_heads + h) * D) * sizeof(T);
   if (nt == 0) {
-    merge_rows<T, D>(a, 0, 0, 0, dst);
+    merge_rows<T, D>(a.ws_acc, a.ws_ml, 0, 0, 0, dst);
     return;
   }
   const Intervals ivs(a.ws_base[a.num_seqs], a.num_groups);
@@ -940,7 +860,7 @@ attn_merge_balanced_kernel(AttnArgs a) {
   const int i1 = ivs.of(start + nt - 1);
   if (i0 == i1) return;
   const int64_t k = int64_t(s) * a.num_kv_heads + g;
-  merge_rows<T, D>(a, i1 - i0 + 1, (k + i0) * G + j, G, dst);
+  merge_rows<T, D>(a.ws_acc, a.ws_ml, i1 - i0 + 1, (k + i0) * G + j, G, dst);
 }
 
 // ---------------------------------------------------------------------------
@@ -957,7 +877,8 @@ int env_knob(const char* name, int lo, int hi) {
 }
 int knob_heads_per_wave() { return env_knob("PKV_ATTN_HEADS_PER_WAVE", 1, 4); }
 int knob_prefetch() { return env_knob("PKV_ATTN_PREFETCH", 2, 4); }
-int knob_mode() { return env_knob("PKV_ATTN_MODE", 1, 2); }  // 1 partition, 2 balanced
+// 1 partitions, 2 balanced, 3 matrix cores
+int knob_mode() { return env_knob("PKV_ATTN_MODE", 1, 3); }
 int knob_append() { return env_knob("PKV_ATTN_APPEND", 1, 2); }  // 1 copy kernel, 2 folded
 int knob_waves_per_block() {
   const int v = env_knob("PKV_ATTN_WAVES_PER_BLOCK", 1, kMaxWavesPerBlock);
@@ -1053,6 +974,45 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
                            (wpg == 1 || wpg == 2 || wpg == 4 || wpg == 8) &&
                            int64_t(num_seqs) * g->num_kv_heads * stream_tiles_max < (int64_t(1) << 31);
   const int km = knob_mode();
+  // Groups of 8 or more query heads per KV head go to the matrix cores: the
+  // vector kernels are bound by instruction issue there (a wave carries at
+  // most 4 heads), while the matrix-core pass does the q.k and p.v products
+  // for 16 heads at once and keeps only the softmax on the vector units.
+  const bool matrix_ok = g->head_dim == 128 && (g->dtype == PKV_BF16 || pkv::is_quant(g->dtype)) &&
+                         partition_tokens % 32 == 0 && g->num_kv_heads <= 65535;
+  if (matrix_ok && (km == 3 || (km == 0 && G >= 8))) {
+    pl->mode = kMatrixMode;
+    pl->prefetch = 0;
+    pl->waves_per_block = pl->waves_per_item = pl->blocks_per_item = 0;
+    pl->groups_per_block = 0;
+    pl->max_chunks = 0;
+    // automatic partitions: about 3072 (sequence, KV head, partition) items
+    // of at least 256 positions
+    const int64_t len = pl->len_cap > 0 ? pl->len_cap : 1;
+    int64_t pt = partition_tokens;
+    if (pt == 0) {
+      const int64_t items = int64_t(num_seqs) * g->num_kv_heads;
+      const int64_t parts = items >= 2048 ? 1 : (3072 + items - 1) / (items > 0 ? items : 1);
+      pt = round_up((len + parts - 1) / parts, 32);
+      if (pt < 256) pt = 256;
+      if (pt > round_up(len, 32)) pt = round_up(len, 32);
+    }
+    const int64_t np = (len + pt - 1) / pt;
+    if (np > 65535) return pkv::fail(PKV_ERR_INVALID_ARG, "%s: more than 65535 partitions", who);
+    pl->part_tokens = static_cast<int>(pt);
+    pl->num_parts = static_cast<int>(np);
+    if (pl->num_parts > 1) {
+      pl->rows = int64_t(num_seqs) * num_q_heads * pl->num_parts;
+      pl->ws_ml_off = size_t(pl->rows) * g->head_dim * sizeof(float);
+      pl->ws_base_off = 0;
+      pl->ws_bytes = pl->ws_ml_off + size_t(pl->rows) * sizeof(float2);
+    } else {
+      pl->rows = 0;
+      pl->ws_ml_off = pl->ws_base_off = 0;
+      pl->ws_bytes = 0;
+    }
+    return PKV_OK;
+  }
   pl->mode = (balanced_ok && km != 1) ? kBalancedMode : kPartitionMode;
   pl->prefetch = prefetch_depth(pl->gw, g->dtype, pl->mode == kBalancedMode);
 
@@ -1254,6 +1214,18 @@ int32_t pkv_attention_partition_tokens(int32_t num_seqs, int32_t num_q_heads,
   return pl.part_tokens;
 }
 
+int32_t pkv_attention_decode_route(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
+                                   int32_t partition_tokens, const pkv_geom* geom) {
+  Plan pl;
+  const int32_t max_blocks =
+      geom && geom->block_size > 0 ? (max_seq_len + geom->block_size - 1) / geom->block_size : 0;
+  if (make_plan(num_seqs, num_q_heads, max_seq_len, max_blocks, partition_tokens, geom,
+                "pkv_attention_decode_route", &pl) != PKV_OK)
+    return -1;
+  return pl.mode == kMatrixMode ? PKV_ROUTE_MATRIX
+         : pl.mode == kBalancedMode ? PKV_ROUTE_BALANCED : PKV_ROUTE_PARTITIONS;
+}
+
 size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
                                      int32_t partition_tokens, const pkv_geom* geom) {
   Plan pl;
@@ -1365,7 +1337,7 @@ pkv_status attention_impl(const char* who, int32_t phases, const void* q, const 
   // The append rides in the attention kernel for waves of up to two query
   // heads; with more the kernel is issue-bound and a copy launch costs less.
   const int ka = knob_append();
-  const bool fold = append && (ka ? ka == 2 : pl.gw <= 2);
+  const bool fold = append && pl.mode != kMatrixMode && (ka ? ka == 2 : pl.gw <= 2);
   a.k_new = fold ? nt.k : nullptr;
   a.v_new = fold ? nt.v : nullptr;
   a.new_slots = fold ? nt.slots : nullptr;
@@ -1377,6 +1349,24 @@ pkv_status attention_impl(const char* who, int32_t phases, const void* q, const 
                        int64_t(geom->num_blocks) * geom->block_size, pl.len_cap);
     if (hipError_t e = hipGetLastError())
       return pkv::fail(PKV_ERR_HIP, "%s: append launch failed: %s", who, hipGetErrorString(e));
+  }
+  if (pl.mode == kMatrixMode) {
+    if (phases & 1) {
+      const int kind = geom->dtype == PKV_FP8_E4M3 ? 1 : (geom->dtype == PKV_INT8 ? 2 : 0);
+      if (pkv_status e = pkv::mfma_decode(q, k_cache, v_cache, kind, a.k_scale, a.v_scale,
+                                          a.k_scales, a.v_scales, block_tables,
+                                          max_blocks_per_seq, seq_lens, scale, out, num_seqs,
+                                          num_q_heads, pl.len_cap, pl.part_tokens, pl.num_parts,
+                                          a.ws_acc, a.ws_ml, geom, st))
+        return e;
+    }
+    if ((phases & 2) && pl.num_parts > 1) {
+      hipLaunchKernelGGL((attn_merge_kernel<uint16_t, 128>), dim3(num_q_heads, num_seqs),
+                         dim3(kMergeThreads), 0, st, a);
+      if (hipError_t e = hipGetLastError())
+        return pkv::fail(PKV_ERR_HIP, "%s: merge launch failed: %s", who, hipGetErrorString(e));
+    }
+    return PKV_OK;
   }
   if (geom->dtype == PKV_FP8_E4M3)
     return dispatch<fp8_e4m3, 128>(phases, pl, a, num_seqs, num_q_heads, st);

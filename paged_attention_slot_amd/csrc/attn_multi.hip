@@ -20,9 +20,12 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
 
 #include "geom.h"
+#include "lse_merge.h"
 #include "mfma_attend.h"
+#include "mfma_route.h"
 #include "pkv_device.h"
 
 namespace {
@@ -31,7 +34,7 @@ using pkv::mfma::kKT;
 
 struct MultiArgs {
   const uint16_t* q;
-  const int32_t* q_offsets;
+  const int32_t* q_offsets;  // null: one query per sequence, row s (decode)
   const void* k_cache;      // bf16 bits or one-byte codes
   const void* v_cache;
   const int32_t* block_tables;
@@ -39,7 +42,7 @@ struct MultiArgs {
   uint16_t* out;
   float* ws_acc;    // [row * H_q + h][part][D]
   float2* ws_ml;    // [row * H_q + h][part] (reference, sum)
-  int32_t* ws_np;   // [row * H_q + h]: partitions holding positions <= P
+  int32_t* ws_np;   // [row * H_q + h]: partitions holding positions <= P (or null)
   int64_t block_elems;
   int32_t row_elems;
   int32_t max_blocks;
@@ -54,6 +57,7 @@ struct MultiArgs {
   int32_t num_kv_heads;
   int32_t num_parts;
   int32_t part_tokens;
+  int32_t parts_per_wg;     // consecutive partitions one workgroup walks
   float scale_log2;         // FP8: the K tensor scale folded in
   float v_scale;            // FP8
   const float* k_scales;    // INT8
@@ -69,21 +73,21 @@ attn_multi_kernel(MultiArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(tid >> 6));
-  // grid = (query blocks * H_kv * sequences, partitions).  Workgroups go to
-  // the XCDs round robin in launch order, so the XCD of (x, part) follows x.
-  // Rotating the item by the partition (item = x + part) spreads both every
-  // partition over all XCDs and the partitions of one item (one long history)
-  // over different XCDs; partition-fastest order put all of partition p on
-  // one XCD whenever the partition count divides 8.
+  // grid = (query blocks * H_kv * sequences, runs of parts_per_wg
+  // partitions).  Workgroups go to the XCDs round robin in launch order, so
+  // the XCD of (x, run) follows x.  Rotating the item by the run (item = x +
+  // run) spreads both every run over all XCDs and the runs of one item (one
+  // long history) over different XCDs; run-fastest order put all of run p on
+  // one XCD whenever the run count divides 8.
   const int qbs = a.num_qblocks;
   const int items = qbs * a.num_kv_heads * static_cast<int>(gridDim.x / (qbs * a.num_kv_heads));
-  const int part = blockIdx.y;
-  const int item = static_cast<int>((blockIdx.x + uint32_t(part)) % uint32_t(items));
+  const int run = blockIdx.y;
+  const int item = static_cast<int>((blockIdx.x + uint32_t(run)) % uint32_t(items));
   const int qb = item % qbs;
   const int g = (item / qbs) % a.num_kv_heads;
   const int s = item / (qbs * a.num_kv_heads);
-  const int q0 = a.q_offsets[s];
-  const int n = a.q_offsets[s + 1] - q0;
+  const int q0 = a.q_offsets ? a.q_offsets[s] : s;
+  const int n = a.q_offsets ? a.q_offsets[s + 1] - q0 : 1;
   const int j0 = qb * a.q_per_block;
   if (q0 < 0 || j0 >= n) return;  // uniform over the workgroup
   const int jn = min(a.q_per_block, n - j0);
@@ -91,9 +95,10 @@ attn_multi_kernel(MultiArgs a) {
   const int L = Lraw < 0 ? 0 : (Lraw > a.len_cap ? a.len_cap : Lraw);
   const int p_first = L - n + j0;          // position of the block's first query
   const int p_last = p_first + jn - 1;
-  const int t_lo = part * a.part_tokens;
-  const int t_hi = min(t_lo + a.part_tokens, p_last + 1);
-  if (part > 0 && t_lo >= t_hi) return;    // no row of this block reaches this part
+  const int part0 = run * a.parts_per_wg;
+  const int t_lo = part0 * a.part_tokens;
+  const int t_hi = min(min(part0 + a.parts_per_wg, a.num_parts) * a.part_tokens, p_last + 1);
+  if (run > 0 && t_lo >= t_hi) return;     // no row of this block reaches these parts
 
   // This lane's row: (query token jl of the block, head hh of the group).
   const int G = a.group;
@@ -110,18 +115,23 @@ attn_multi_kernel(MultiArgs a) {
                                 a.v_scales};
   pkv::mfma::RowAcc<D> r;
   pkv::mfma::start(r);
-  // every row of the block sees the positions up to its first query's
-  pkv::mfma::attend<D, NW, (NW >= 2 ? 2 : 1), Q>(hist, t_lo, t_hi, a.q + qh * D, row_ok, p_row,
-                                                p_first, a.scale_log2, k_lds, v_lds, r, s_lds);
-
-  if (!row_ok) return;
+  constexpr int kPD = NW >= 2 ? 2 : 1;
   if (a.num_parts == 1) {
-    pkv::mfma::store_row_bf16<D>(r, a.out + qh * D);
+    // every row of the block sees the positions up to its first query's
+    pkv::mfma::attend<D, NW, kPD, Q>(hist, t_lo, t_hi, a.q + qh * D, row_ok, p_row, p_first,
+                                     a.scale_log2, k_lds, v_lds, r, s_lds);
+    if (row_ok) pkv::mfma::store_row_bf16<D>(r, a.out + qh * D);
     return;
   }
-  const int64_t prow = qh * a.num_parts + part;
-  pkv::mfma::store_piece<D>(r, a.ws_acc + prow * D, a.ws_ml + prow);
-  if ((lane >> 4) == 0 && part == 0) {
+  // one piece per partition of the run, at [row, head][partition]
+  const auto emit = [&](int t, pkv::mfma::RowAcc<D>& rr) {
+    if (!row_ok) return;
+    const int64_t prow = qh * a.num_parts + t / a.part_tokens;
+    pkv::mfma::store_piece<D>(rr, a.ws_acc + prow * D, a.ws_ml + prow);
+  };
+  pkv::mfma::attend<D, NW, kPD, Q>(hist, t_lo, t_hi, a.q + qh * D, row_ok, p_row, p_first,
+                                   a.scale_log2, k_lds, v_lds, r, s_lds, a.part_tokens, emit);
+  if (row_ok && a.ws_np && (lane >> 4) == 0 && run == 0) {
     const int np = p_row < 0 ? 0 : min(a.num_parts, p_row / a.part_tokens + 1);
     a.ws_np[qh] = np;
   }
@@ -158,12 +168,33 @@ attn_multi_merge_kernel(MultiArgs a) {
   for (int e = 0; e < kE; ++e) dst[e] = static_cast<uint16_t>(pkv::f32_to_bf16_bits(acc[e] * inv));
 }
 
+// The same merge for many partitions: one 256-thread workgroup per (query
+// row, head), 64 pieces per memory round trip (pkv::merge_rows).
+template <int D>
+__global__ void __launch_bounds__(pkv::kMergeThreads)
+attn_multi_merge_wide_kernel(MultiArgs a) {
+  const int64_t qh = int64_t(blockIdx.y) * a.num_q_heads + blockIdx.x;
+  const int np_raw = a.ws_np[qh];
+  const int np = np_raw < 0 ? 0 : (np_raw > a.num_parts ? a.num_parts : np_raw);
+  pkv::merge_rows<uint16_t, D>(a.ws_acc, a.ws_ml, np, qh * a.num_parts, 1,
+                               reinterpret_cast<char*>(a.out + qh * D));
+}
+
 struct MultiPlan {
-  int nw, q_per_block, qblocks, part_tokens, num_parts;
+  int nw, q_per_block, qblocks, part_tokens, num_parts, parts_per_wg, runs;
   size_t ws_bytes, ws_ml_off, ws_np_off;
 };
 
 int64_t round_up_to(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+// PKV_ATTN_PARTS_PER_WG (tuning, documented in include/pkv.h): partitions one
+// matrix-core workgroup walks; 0 = the heuristic.
+int knob_parts_per_wg() {
+  const char* v = std::getenv("PKV_ATTN_PARTS_PER_WG");
+  if (!v || !*v) return 0;
+  const int x = std::atoi(v);
+  return (x >= 1 && x <= 65535) ? x : 0;
+}
 
 // Which cache types a caller accepts: 0 = bf16 only, 1 = one-byte codes only,
 // 2 = any of them (workspace sizing).
@@ -222,6 +253,14 @@ pkv_status multi_plan(int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
   if (np > 65535 || int64_t(pl->qblocks) * g->num_kv_heads * num_seqs > 2147483647LL)
     return pkv::fail(PKV_ERR_INVALID_ARG, "%s: too many partitions or query blocks", who);
   pl->num_parts = static_cast<int>(np);
+  // Runs of consecutive partitions per workgroup: about 3072 workgroups for
+  // many short partitions (each workgroup's ramp then covers several).
+  const int64_t wgs = int64_t(num_seqs) * g->num_kv_heads * pl->qblocks * np;
+  int64_t ppw = wgs > 4096 ? (wgs + 3071) / 3072 : 1;
+  if (const int k = knob_parts_per_wg()) ppw = k;
+  if (ppw > np) ppw = np;
+  pl->parts_per_wg = static_cast<int>(ppw);
+  pl->runs = static_cast<int>((np + ppw - 1) / ppw);
   if (pl->num_parts > 1) {
     const size_t rowsq = size_t(total_q) * num_q_heads;
     pl->ws_ml_off = rowsq * pl->num_parts * g->head_dim * sizeof(float);
@@ -233,10 +272,11 @@ pkv_status multi_plan(int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
   return PKV_OK;
 }
 
+// The main kernel only (no merge).
 template <int D, int Q>
-void launch_multi(const MultiPlan& pl, const MultiArgs& a, int num_seqs, int num_kv_heads,
-                  int total_q, hipStream_t st) {
-  const dim3 grid(pl.qblocks * num_kv_heads * num_seqs, pl.num_parts);
+void launch_multi_main(const MultiPlan& pl, const MultiArgs& a, int num_seqs, int num_kv_heads,
+                       hipStream_t st) {
+  const dim3 grid(pl.qblocks * num_kv_heads * num_seqs, pl.runs);
   switch (pl.nw) {
     case 1: hipLaunchKernelGGL((attn_multi_kernel<D, 1, Q>), grid, dim3(64), 0, st, a); break;
     case 2: hipLaunchKernelGGL((attn_multi_kernel<D, 2, Q>), grid, dim3(128), 0, st, a); break;
@@ -246,7 +286,16 @@ void launch_multi(const MultiPlan& pl, const MultiArgs& a, int num_seqs, int num
         hipLaunchKernelGGL((attn_multi_kernel<D, 8, Q>), grid, dim3(512), 0, st, a);
       break;
   }
-  if (pl.num_parts > 1 && total_q > 0)
+}
+
+template <int D, int Q>
+void launch_multi(const MultiPlan& pl, const MultiArgs& a, int num_seqs, int num_kv_heads,
+                  int total_q, hipStream_t st) {
+  launch_multi_main<D, Q>(pl, a, num_seqs, num_kv_heads, st);
+  if (pl.num_parts > 16 && total_q > 0)
+    hipLaunchKernelGGL((attn_multi_merge_wide_kernel<D>), dim3(a.num_q_heads, total_q),
+                       dim3(pkv::kMergeThreads), 0, st, a);
+  else if (pl.num_parts > 1 && total_q > 0)
     hipLaunchKernelGGL((attn_multi_merge_kernel<D>), dim3(a.num_q_heads, total_q), dim3(64), 0,
                        st, a);
 }
@@ -319,6 +368,7 @@ pkv_status multi_impl(const char* who, int types, const void* q, const int32_t* 
   a.num_kv_heads = geom->num_kv_heads;
   a.num_parts = pl.num_parts;
   a.part_tokens = pl.part_tokens;
+  a.parts_per_wg = pl.parts_per_wg;
   a.scale_log2 = static_cast<float>(double(scale) * 1.4426950408889634 *
                                     (kind == pkv::mfma::kFp8 ? double(scales->k_scale) : 1.0));
   a.v_scale = kind == pkv::mfma::kFp8 ? scales->v_scale : 1.f;
@@ -340,6 +390,75 @@ pkv_status multi_impl(const char* who, int types, const void* q, const int32_t* 
 
 
 }  // namespace
+
+namespace pkv {
+
+pkv_status mfma_decode(const void* q, const void* k_cache, const void* v_cache, int kind,
+                       float k_scale, float v_scale, const float* k_scales,
+                       const float* v_scales, const int32_t* block_tables, int32_t max_blocks,
+                       const int32_t* seq_lens, float scale, void* out, int32_t num_seqs,
+                       int32_t num_q_heads, int32_t len_cap, int32_t part_tokens,
+                       int32_t num_parts, float* ws_acc, float2* ws_ml, const pkv_geom* g,
+                       hipStream_t st) {
+  const int G = num_q_heads / g->num_kv_heads;
+  MultiPlan pl;
+  pl.nw = G <= 16 ? 1 : (G <= 32 ? 2 : 4);
+  pl.q_per_block = 16 * pl.nw / G;
+  if (pl.q_per_block < 1) pl.q_per_block = 1;
+  pl.qblocks = 1;
+  pl.part_tokens = part_tokens;
+  pl.num_parts = num_parts;
+  const int64_t wgs = int64_t(num_seqs) * g->num_kv_heads * num_parts;
+  int64_t ppw = wgs > 4096 ? (wgs + 3071) / 3072 : 1;
+  if (const int k = knob_parts_per_wg()) ppw = k;
+  if (ppw > num_parts) ppw = num_parts;
+  pl.parts_per_wg = static_cast<int>(ppw);
+  pl.runs = static_cast<int>((num_parts + ppw - 1) / ppw);
+  pl.ws_bytes = pl.ws_ml_off = pl.ws_np_off = 0;
+  MultiArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_offsets = nullptr;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.out = static_cast<uint16_t*>(out);
+  a.ws_acc = ws_acc;
+  a.ws_ml = ws_ml;
+  a.ws_np = nullptr;
+  a.row_elems = g->num_kv_heads * g->head_dim;
+  a.block_elems = int64_t(g->block_size) * a.row_elems;
+  a.max_blocks = max_blocks;
+  a.num_q_heads = num_q_heads;
+  a.total_q = num_seqs;
+  a.group = G;
+  a.num_blocks = g->num_blocks;
+  a.block_shift = pkv::log2_exact(g->block_size);
+  a.len_cap = len_cap;
+  a.q_per_block = pl.q_per_block;
+  a.num_qblocks = 1;
+  a.num_kv_heads = g->num_kv_heads;
+  a.num_parts = num_parts;
+  a.part_tokens = part_tokens;
+  a.parts_per_wg = pl.parts_per_wg;
+  a.scale_log2 = static_cast<float>(double(scale) * 1.4426950408889634 *
+                                    (kind == pkv::mfma::kFp8 ? double(k_scale) : 1.0));
+  a.v_scale = kind == pkv::mfma::kFp8 ? v_scale : 1.f;
+  a.k_scales = kind == pkv::mfma::kInt8 ? k_scales : nullptr;
+  a.v_scales = kind == pkv::mfma::kInt8 ? v_scales : nullptr;
+  if (kind == pkv::mfma::kFp8)
+    launch_multi_main<128, pkv::mfma::kFp8>(pl, a, num_seqs, g->num_kv_heads, st);
+  else if (kind == pkv::mfma::kInt8)
+    launch_multi_main<128, pkv::mfma::kInt8>(pl, a, num_seqs, g->num_kv_heads, st);
+  else
+    launch_multi_main<128, pkv::mfma::kBf16>(pl, a, num_seqs, g->num_kv_heads, st);
+  if (hipError_t e = hipGetLastError())
+    return pkv::fail(PKV_ERR_HIP, "pkv_attention_decode: matrix-core launch failed: %s",
+                     hipGetErrorString(e));
+  return PKV_OK;
+}
+
+}  // namespace pkv
 
 extern "C" {
 

@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "pkv_device.h"
 
@@ -174,11 +175,23 @@ __device__ __forceinline__ void start(RowAcc<D>& r) {
 // 2^kSlack and most tiles skip the rescale.  With more waves (matrix-bound)
 // every tile rescales: the branch would keep the compiler from interleaving
 // the tile's matrix work with its softmax (measured 20 % slower).
-template <int D, int NW, int PD = 1, int Q = kBf16>
+//
+// Segments: with an ``emit`` functor, [t_lo, t_hi) is walked as consecutive
+// segments of ``seg`` positions (t_lo and seg multiples of the tile): after a
+// segment's last tile emit(t, r) receives the start t of that tile and the
+// segment's state, and the state starts afresh, while the tile stream (loads
+// in flight, LDS buffers) runs on across the boundary.  One workgroup can so
+// produce the pieces of several split-KV partitions in one pass.
+struct NoEmit {
+  template <class R> __device__ void operator()(int, R&) const {}
+};
+
+template <int D, int NW, int PD = 1, int Q = kBf16, class Emit = NoEmit>
 __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, const uint16_t* q,
                                        bool row_ok, int p_row, int p_all, float scale_log2,
                                        uint16_t* k_lds, uint16_t* v_lds, RowAcc<D>& r,
-                                       float* s_lds = nullptr) {
+                                       float* s_lds = nullptr, int seg = 0,
+                                       const Emit& emit = Emit()) {
   constexpr float kSlack = 8.0f;
   constexpr bool kLazy = NW == 1;
   constexpr int kEB = Q == kBf16 ? 2 : 1;   // bytes per element
@@ -399,6 +412,13 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
       if (t + PD * kKT < t_hi) fetch(j, t + PD * kKT);
       compute(t, buf);
       if constexpr (lds_tiles<NW>() == 2) buf ^= 1;
+      if constexpr (!std::is_same<Emit, NoEmit>::value) {
+        const int te = t + kKT;
+        if (te >= t_hi || (te - t_lo) % seg == 0) {  // uniform: a segment is complete
+          emit(t, r);
+          start(r);
+        }
+      }
     }
   }
   // the caller may reuse the LDS (another pass) right after

@@ -87,6 +87,21 @@ def partition_tokens(num_seqs: int, num_q_heads: int, max_seq_len: int, k_cache)
                                                     ctypes.byref(g)))
 
 
+ROUTES = {0: "partitions", 1: "balanced", 2: "matrix"}
+
+
+def decode_route(num_seqs: int, num_q_heads: int, max_seq_len: int, k_cache,
+                 partition_tokens: int = 0) -> str:
+    """Which kernels pkv_attention_decode runs for these sizes: "partitions",
+    "balanced" or "matrix" (pkv_attention_decode_route)."""
+    g = geom_of(k_cache)
+    r = lib().pkv_attention_decode_route(num_seqs, num_q_heads, max_seq_len,
+                                         int(partition_tokens), ctypes.byref(g))
+    if r < 0:
+        check(1, "pkv_attention_decode_route")
+    return ROUTES[int(r)]
+
+
 def workspace_bytes(num_seqs: int, num_q_heads: int, max_seq_len: int, k_cache,
                     partition_tokens: int = 0) -> int:
     g = geom_of(k_cache)

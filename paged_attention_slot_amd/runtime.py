@@ -273,13 +273,16 @@ class DecodeStep:
 
     @property
     def split(self) -> dict:
-        """How pkv_attention_decode splits this batch: fixed partitions (with
-        their length and count) or the balanced split."""
+        """How pkv_attention_decode runs this batch: the kernels ("route":
+        vector kernels with fixed partitions or the balanced split, or the
+        matrix-core pass) and the partition length and count."""
+        route = ops.decode_route(self.wl.num_seqs, self.wl.num_q_heads, self.max_seq_len,
+                                 self.k_caches[0], self.partition_tokens)
+        if route == "balanced":
+            return {"mode": "balanced"}
         pt = self.partition_tokens or ops.partition_tokens(
             self.wl.num_seqs, self.wl.num_q_heads, self.max_seq_len, self.k_caches[0])
-        if pt == 0:
-            return {"mode": "balanced"}
-        return {"mode": "partitions", "partition_tokens": pt,
+        return {"mode": "matrix" if route == "matrix" else "partitions", "partition_tokens": pt,
                 "num_partitions": max(1, -(-self.max_seq_len // pt))}
 
     def step(self, layer=0, stream=None, fused=False):

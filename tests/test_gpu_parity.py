@@ -103,6 +103,31 @@ def test_small_write_and_attention(dtype, B, D, Hq, Hkv):
                 assert np.array_equal(out[i, h], to_f64(wl.new_v[i, h // G]))
 
 
+@pytest.mark.parametrize("ppw", [None, "3"])
+@pytest.mark.parametrize("pt", [0, 32, 96, 512])
+def test_matrix_route_matches_oracle(pt, ppw, monkeypatch):
+    """Groups of 8 query heads per KV head take the matrix-core route, with
+    automatic or given partitions, and with runs of 3 partitions per
+    workgroup (PKV_ATTN_PARTS_PER_WG): outputs against the oracle's split (or
+    unsplit) attention."""
+    if ppw:
+        monkeypatch.setenv("PKV_ATTN_PARTS_PER_WG", ppw)
+    wl = independent_workload([1, 15, 16, 17, 64, 200, 333, 1500], num_q_heads=64,
+                              num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16",
+                              seed=17 + pt)
+    step, ost = run_both(wl, partition_tokens=pt)
+    say(f"  split {step.split} runs={ppw}")
+    assert step.split["mode"] == "matrix"
+    got = gpu_out(step)
+    if pt:
+        ref = oracle_split(wl.q, ost.k_pool, ost.v_pool, ost.block_tables, ost.seq_lens,
+                           wl.scale, pt)
+    else:
+        ref = oracle_attention(wl.q, ost.k_pool, ost.v_pool, ost.block_tables, ost.seq_lens,
+                               wl.scale)
+    say("  gate", assert_gate(got, ref, "bf16", f"matrix route pt={pt}"))
+
+
 @pytest.mark.parametrize("pt", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("dtype,B", [("bf16", 16), ("f32", 16), ("bf16", 32)])
 def test_split_kv_matches_oracle_and_unsplit(pt, dtype, B):

@@ -317,3 +317,31 @@ def test_fused_append_entry_point_validates_on_the_host():
     # the balanced split needs a workspace
     assert call(g()) == _lib.PKV_ERR_INVALID_ARG
     assert "workspace" in last_error()
+
+
+def test_decode_route_query():
+    """pkv_attention_decode_route: 8+ query heads per KV head at head_dim 128
+    (bf16 or one-byte pools, partitions a multiple of 32) take the matrix
+    cores; narrower groups, fp32 pools, 64-wide heads and 16-token partitions
+    stay on the vector kernels; bad arguments give -1."""
+    lib = pkv.lib()
+
+    def route(N, Hq, H, D, dt, pt=0, maxlen=4096):
+        return lib.pkv_attention_decode_route(N, Hq, maxlen, pt,
+                                              ctypes.byref(g(nb=8192, H=H, D=D, dt=dt)))
+
+    M, B, P = _lib.PKV_ROUTE_MATRIX, _lib.PKV_ROUTE_BALANCED, _lib.PKV_ROUTE_PARTITIONS
+    assert route(4, 64, 8, 128, _lib.PKV_BF16) == M
+    assert route(4, 64, 8, 128, _lib.PKV_BF16, pt=512) == M
+    assert route(4, 64, 8, 128, _lib.PKV_FP8_E4M3) == M
+    assert route(4, 64, 8, 128, _lib.PKV_INT8) == M
+    assert route(4, 64, 8, 128, _lib.PKV_BF16, pt=16) == P
+    assert route(64, 16, 8, 128, _lib.PKV_BF16) == B
+    assert route(64, 32, 8, 128, _lib.PKV_BF16) == B
+    assert route(4, 64, 8, 64, _lib.PKV_BF16) == B
+    assert route(4, 64, 8, 128, _lib.PKV_F32) == B
+    assert route(4, 63, 8, 128, _lib.PKV_BF16) == -1
+    # the workspace of the matrix route: N * Hq * partitions rows of D + 2 floats
+    n = lib.pkv_attention_workspace_bytes(4, 64, 131072, 512,
+                                          ctypes.byref(g(nb=8192, H=8, D=128, dt=1)))
+    assert n == 4 * 64 * 256 * (128 + 2) * 4
