@@ -45,9 +45,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 PCIE_PEAK_GBPS = 32.0 * 16 * 128 / 130 / 8
 METRIC = "paged decode attention KV-read GB/s (% of MI355X HBM peak); tokens/s"
 KERNEL_SOURCES = {
-    "attn_balanced_kernel": ("attn_decode.hip", "pkv_device.h"),
-    "attn_partition_kernel": ("attn_decode.hip", "pkv_device.h"),
-    "attn_multi_kernel": ("attn_multi.hip", "mfma_attend.h", "pkv_device.h"),
+    "attn_balanced_kernel": ("attn_decode.hip", "lse_merge.h", "pkv_device.h"),
+    "attn_partition_kernel": ("attn_decode.hip", "lse_merge.h", "pkv_device.h"),
+    "attn_multi_kernel": ("attn_multi.hip", "mfma_attend.h", "mfma_route.h", "lse_merge.h",
+                          "pkv_device.h"),
     "attn_shared": ("attn_shared.hip", "mfma_attend.h", "pkv_device.h"),
     "swap_blocks_kernel": ("swap.hip",),
 }
