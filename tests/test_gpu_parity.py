@@ -110,6 +110,7 @@ def test_matrix_route_matches_oracle(pt, ppw, monkeypatch):
     automatic or given partitions, and with runs of 3 partitions per
     workgroup (PKV_ATTN_PARTS_PER_WG): outputs against the oracle's split (or
     unsplit) attention."""
+    monkeypatch.delenv("PKV_ATTN_MODE", raising=False)  # the route under test is the default
     if ppw:
         monkeypatch.setenv("PKV_ATTN_PARTS_PER_WG", ppw)
     wl = independent_workload([1, 15, 16, 17, 64, 200, 333, 1500], num_q_heads=64,
