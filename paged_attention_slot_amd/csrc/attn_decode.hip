@@ -112,6 +112,8 @@ struct AttnArgs {
   const void* k_new;
   const void* v_new;
   const int32_t* new_slots;
+  void* k_dst;   // the pools again, writable (the appended rows' destination)
+  void* v_dst;
 };
 
 // One-byte cache element types ([KVM §19.2.4], [PFX] "KV Cache 量化"): OCP e4m3
@@ -347,8 +349,8 @@ struct Wave {
     const int bmask = (1 << a.block_shift) - 1;
     const int64_t off = int64_t(new_slot_ >> a.block_shift) * a.block_bytes +
                         int64_t(new_slot_ & bmask) * a.row_bytes + head_off + c * 16;
-    char* kd = static_cast<char*>(const_cast<void*>(a.k_cache)) + off;
-    char* vd = static_cast<char*>(const_cast<void*>(a.v_cache)) + off;
+    char* kd = static_cast<char*>(a.k_dst) + off;
+    char* vd = static_cast<char*>(a.v_dst) + off;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       if (t.start + 8 * i + r == newpos_) {
@@ -1247,6 +1249,8 @@ struct NewToken {
   const void* k = nullptr;
   const void* v = nullptr;
   const int32_t* slots = nullptr;
+  void* k_cache = nullptr;  // the pools, writable
+  void* v_cache = nullptr;
 };
 
 pkv_status attention_impl(const char* who, int32_t phases, const void* q, const void* k_cache,
@@ -1341,11 +1345,13 @@ pkv_status attention_impl(const char* who, int32_t phases, const void* q, const 
   a.k_new = fold ? nt.k : nullptr;
   a.v_new = fold ? nt.v : nullptr;
   a.new_slots = fold ? nt.slots : nullptr;
+  a.k_dst = fold ? nt.k_cache : nullptr;
+  a.v_dst = fold ? nt.v_cache : nullptr;
   if (append && !fold && (phases & 1)) {
     hipLaunchKernelGGL(append_rows_kernel, dim3(num_seqs), dim3(kAppendThreads), 0, st,
                        static_cast<const uint4*>(nt.k), static_cast<const uint4*>(nt.v), nt.slots,
-                       seq_lens, static_cast<uint4*>(const_cast<void*>(k_cache)),
-                       static_cast<uint4*>(const_cast<void*>(v_cache)), a.row_bytes / 16,
+                       seq_lens, static_cast<uint4*>(nt.k_cache),
+                       static_cast<uint4*>(nt.v_cache), a.row_bytes / 16,
                        int64_t(geom->num_blocks) * geom->block_size, pl.len_cap);
     if (hipError_t e = hipGetLastError())
       return pkv::fail(PKV_ERR_HIP, "%s: append launch failed: %s", who, hipGetErrorString(e));
@@ -1432,6 +1438,8 @@ pkv_status pkv_attention_decode_append(int32_t phases, const void* q, const void
   nt.k = k_new;
   nt.v = v_new;
   nt.slots = slot_mapping;
+  nt.k_cache = k_cache;
+  nt.v_cache = v_cache;
   return attention_impl("pkv_attention_decode_append", phases, q, k_cache, v_cache, nullptr,
                         block_tables, max_blocks_per_seq, seq_lens, scale, out, num_seqs,
                         num_q_heads, max_seq_len, partition_tokens, workspace, workspace_bytes,
