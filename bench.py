@@ -54,17 +54,19 @@ KERNEL_SOURCES = {
 }
 
 
-def cpu_baseline(wl, budget_s: float) -> dict:
+def cpu_baseline(wl, budget_s: float, kv_dtype: str | None = None) -> dict:
     """The CPU oracle (fp64 NumPy, as it stands) on a bounded sample of the same
     workload: its block manager and writes first (untimed), then copy + write of
     the step and attention sequence by sequence, cycling over the batch, until
-    ``budget_s`` elapses."""
+    ``budget_s`` elapses.  ``kv_dtype`` "fp8_e4m3" / "int8": the oracle of the
+    quantized caches (its attention dequantizes the pools, then attends)."""
     import numpy as np
 
     from oracle.attention import attention_decode
-    from oracle.replay import OracleState
+    from oracle.replay import OracleState, QuantOracleState
 
-    st = OracleState(wl, keep_values=False)
+    st = (QuantOracleState(wl, kv_dtype, keep_values=False) if kv_dtype
+          else OracleState(wl, keep_values=False))
     st.build_context()
     st.decode_tables()
     t0 = time.perf_counter()
@@ -72,12 +74,17 @@ def cpu_baseline(wl, budget_s: float) -> dict:
     done = []
     while time.perf_counter() - t0 <= budget_s:
         s = len(done) % wl.num_seqs
-        attention_decode(wl.q, st.k_pool, st.v_pool, st.block_tables, st.seq_lens, wl.scale,
-                         seqs=[s])
+        if kv_dtype:
+            st.attention(seqs=[s])
+        else:
+            attention_decode(wl.q, st.k_pool, st.v_pool, st.block_tables, st.seq_lens, wl.scale,
+                             seqs=[s])
         done.append(s)
     el = time.perf_counter() - t0
     lens = st.seq_lens[done].astype(np.int64)
-    kv = int(lens.sum()) * 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
+    e = 1 if kv_dtype else wl.elem_bytes
+    kv = int(lens.sum()) * (2 * wl.num_kv_heads * wl.head_dim * e +
+                            (8 * wl.num_kv_heads if kv_dtype == "int8" else 0))
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -737,8 +744,8 @@ def main() -> int:
     same = stream_read_same_size_gbps(part_bytes, max(L, 4))
     res["detail"]["stream_read_same_size"] = same
     res["detail"]["partition_frac_of_same_size_stream_read"] = achieved / same["gbps"]
-    if not args.no_cpu_baseline and not quant:
-        cb = cpu_baseline(wl, args.cpu_budget)
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(wl, args.cpu_budget, args.kv_dtype if quant else None)
         res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
         res["detail"]["cpu_baseline_extra"] = {k: cb[k] for k in ("seconds", "host_cpus",
                                                                   "affinity_cpus")}
