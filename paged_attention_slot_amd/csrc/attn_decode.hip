@@ -375,11 +375,20 @@ struct Wave {
       if constexpr (kQuant<T>) {
         // codes -> exact bf16 pairs, dotted with the bf16 query; the K scale
         // multiplies the score (per tensor for FP8, per position for INT8)
-        float kf[16];
-        decode16<T>(b.k[i][0], kf);
         uint32_t kp[8];
+        if constexpr (kInt8<T>) {
+          float kf[16];
+          decode16<T>(b.k[i][0], kf);
 #pragma unroll
-        for (int w = 0; w < 8; ++w) kp[w] = bf16_pair_exact(kf[2 * w], kf[2 * w + 1]);
+          for (int w = 0; w < 8; ++w) kp[w] = bf16_pair_exact(kf[2 * w], kf[2 * w + 1]);
+        } else {
+          const uint32_t kw[4] = {b.k[i][0].x, b.k[i][0].y, b.k[i][0].z, b.k[i][0].w};
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            kp[2 * w] = pkv::fp8x2_to_bf16x2(kw[w], false);
+            kp[2 * w + 1] = pkv::fp8x2_to_bf16x2(kw[w], true);
+          }
+        }
         const float ksc = kInt8<T> ? a.scale_log2 * b.ks[i] : a.scale_log2 * a.k_scale;
 #pragma unroll
         for (int hh = 0; hh < GW; ++hh) {

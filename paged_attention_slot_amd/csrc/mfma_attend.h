@@ -289,6 +289,25 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
       if constexpr (Q == kBf16) {
         *reinterpret_cast<uint4*>(k_lds + off) = nk[j][i];
         *reinterpret_cast<uint4*>(v_lds + voff) = nv[j][i];
+      } else if constexpr (Q == kFp8) {
+        // code pairs straight to bf16 pairs (packed conversion)
+        const uint32_t kw[4] = {nk[j][i].x, nk[j][i].y, nk[j][i].z, nk[j][i].w};
+        const uint32_t vw[4] = {nv[j][i].x, nv[j][i].y, nv[j][i].z, nv[j][i].w};
+        uint32_t w[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w[2 * e] = fp8x2_to_bf16x2(kw[e], false);
+          w[2 * e + 1] = fp8x2_to_bf16x2(kw[e], true);
+        }
+        *reinterpret_cast<uint4*>(k_lds + off) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(k_lds + off + 8) = make_uint4(w[4], w[5], w[6], w[7]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w[2 * e] = fp8x2_to_bf16x2(vw[e], false);
+          w[2 * e + 1] = fp8x2_to_bf16x2(vw[e], true);
+        }
+        *reinterpret_cast<uint4*>(v_lds + voff) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(v_lds + voff + 8) = make_uint4(w[4], w[5], w[6], w[7]);
       } else {
         float f[16];
         uint32_t w[8];

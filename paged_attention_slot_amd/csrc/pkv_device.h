@@ -30,6 +30,16 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Two OCP e4m3 codes (bytes 0-1 of w, or 2-3 with hi) -> two bf16 in one word,
+// the first code in the low half: gfx950's packed conversion with a unit
+// scale.  Exact (every finite e4m3 value is a bf16 value); checked bit for bit
+// against the fp8 -> f32 conversion for all code pairs without a NaN.
+typedef __bf16 bf16x2_native_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi) {
+  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
+
 // DPP controls (GCN/CDNA encoding).
 enum : int {
   kDppQuadXor1 = 0xB1,      // quad_perm [1,0,3,2]
