@@ -114,6 +114,7 @@ struct AttnArgs {
   const int32_t* new_slots;
   void* k_dst;   // the pools again, writable (the appended rows' destination)
   void* v_dst;
+  int32_t stream_kv;  // 1: non-temporal K/V loads; 0: cacheable (shared blocks)
 };
 
 // One-byte cache element types ([KVM §19.2.4], [PFX] "KV Cache 量化"): OCP e4m3
@@ -237,7 +238,10 @@ __device__ __forceinline__ uint32_t bf16_pair_exact(float lo, float hi) {
 
 // One wave's attention over a stretch [start, end) of one stream.  kAppend:
 // the fused-append variant (pkv_attention_decode_append), bf16/f32 only.
-template <typename T, int D, int GW, int P, bool kAppend = false>
+// kStream: the K/V tiles are read with non-temporal loads (each byte read
+// once per call); off for batches whose sequences share blocks, so the
+// re-read blocks stay cacheable.
+template <typename T, int D, int GW, int P, bool kAppend = false, bool kStream = true>
 struct Wave {
   static_assert(!kAppend || !kQuant<T>, "the fused append takes bf16 or f32 pools");
   using S = Shape<T, D>;
@@ -291,6 +295,11 @@ struct Wave {
     return (b >= 0 && b < a.num_blocks) ? b : 0;
   }
 
+  static __device__ __forceinline__ uint4 kv_load(const char* p) {
+    if constexpr (kStream) return pkv::load_stream(p);
+    else return *reinterpret_cast<const uint4*>(p);
+  }
+
   __device__ __forceinline__ TileInfo prepare(int tile_start, int end) {
     TileInfo t;
     t.start = tile_start;
@@ -321,8 +330,8 @@ struct Wave {
                                 : vb + lane_off;
 #pragma unroll
           for (int j = 0; j < kCPL; ++j) {
-            b.k[i][j] = *reinterpret_cast<const uint4*>(kl + 128 * j);
-            b.v[i][j] = *reinterpret_cast<const uint4*>(vl + 128 * j);
+            b.k[i][j] = kv_load(kl + 128 * j);
+            b.v[i][j] = kv_load(vl + 128 * j);
           }
           plain = false;
         }
@@ -330,8 +339,8 @@ struct Wave {
       if (plain) {
 #pragma unroll
         for (int j = 0; j < kCPL; ++j) {
-          b.k[i][j] = *reinterpret_cast<const uint4*>(kb + lane_off + 128 * j);
-          b.v[i][j] = *reinterpret_cast<const uint4*>(vb + lane_off + 128 * j);
+          b.k[i][j] = kv_load(kb + lane_off + 128 * j);
+          b.v[i][j] = kv_load(vb + lane_off + 128 * j);
         }
       }
       if constexpr (kInt8<T>) {
@@ -629,7 +638,7 @@ struct Wave {
 // ---------------------------------------------------------------------------
 // Partition mode: one wave per (sequence, partition, KV head, head subset).
 // ---------------------------------------------------------------------------
-template <typename T, int D, int GW, int P, bool kAppend>
+template <typename T, int D, int GW, int P, bool kAppend, bool kStream>
 __global__ void __launch_bounds__(64 * kMaxWavesPerBlock)
 attn_partition_kernel(AttnArgs a) {
   // The waves of one (sequence, partition) are numbered consecutively and
@@ -642,7 +651,7 @@ attn_partition_kernel(AttnArgs a) {
   const int s = blockIdx.z;
   const int h0 = kvh * a.group + sub * GW;
 
-  Wave<T, D, GW, P, kAppend> w(a);
+  Wave<T, D, GW, P, kAppend, kStream> w(a);
   const int Lraw = a.seq_lens[s];
   const int L = clamp_len(Lraw, a.len_cap);
   const int start = part * a.part_tokens;
@@ -756,8 +765,9 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 }
 
 // Attention over global tiles [lo, hi) of interval `iv`, stream by stream.
-template <typename T, int D, int GW, int P, bool kAppend>
-__device__ __forceinline__ void run_interval(Wave<T, D, GW, P, kAppend>& w, const AttnArgs& a,
+template <typename T, int D, int GW, int P, bool kAppend, bool kStream>
+__device__ __forceinline__ void run_interval(Wave<T, D, GW, P, kAppend, kStream>& w,
+                                             const AttnArgs& a,
                                              const int32_t* base, int64_t lo, int64_t hi, int iv,
                                              int sub) {
   const int N = a.num_seqs, Hkv = a.num_kv_heads;
@@ -795,7 +805,7 @@ __device__ __forceinline__ void run_interval(Wave<T, D, GW, P, kAppend>& w, cons
   }
 }
 
-template <typename T, int D, int GW, int P, bool kAppend>
+template <typename T, int D, int GW, int P, bool kAppend, bool kStream>
 __global__ void __launch_bounds__(64 * kMaxWavesPerBlock)
 attn_balanced_kernel(AttnArgs a) {
   __shared__ int32_t base[kMaxBalancedSeqs + 1];
@@ -834,7 +844,7 @@ attn_balanced_kernel(AttnArgs a) {
   const int sub = wv - grp * a.waves_per_group;
   if (grp >= a.groups_per_block || total == 0) return;
   const Intervals ivs(total, a.num_groups);
-  Wave<T, D, GW, P, kAppend> w(a);
+  Wave<T, D, GW, P, kAppend, kStream> w(a);
   if (static_cast<int>(blockIdx.x) < a.static_blocks) {
     const int gidx = blockIdx.x * a.groups_per_block + grp;
     if (gidx >= ivs.Ws) return;
@@ -1095,10 +1105,11 @@ int resident_blocks(const void* kernel, int threads) {
   return v;
 }
 
-template <typename T, int D, int GW, int P, bool kAppend>
+template <typename T, int D, int GW, int P, bool kAppend, bool kStream = true>
 pkv_status launch_main(const Plan& pl, AttnArgs& a, int num_seqs, hipStream_t st) {
   if (pl.mode == kBalancedMode) {
-    const void* k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, P, kAppend>);
+    const void* k =
+        reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, P, kAppend, kStream>);
     const int threads = 64 * pl.waves_per_block;
     int blocks = resident_blocks(k, threads);
     if (blocks <= 0)
@@ -1109,11 +1120,13 @@ pkv_status launch_main(const Plan& pl, AttnArgs& a, int num_seqs, hipStream_t st
     a.static_blocks = blocks;
     const int chunks = pl.max_chunks < a.num_groups ? pl.max_chunks : a.num_groups;
     const int tail = (chunks + pl.groups_per_block - 1) / pl.groups_per_block;
-    hipLaunchKernelGGL((attn_balanced_kernel<T, D, GW, P, kAppend>), dim3(blocks + tail), dim3(threads), 0,
+    hipLaunchKernelGGL((attn_balanced_kernel<T, D, GW, P, kAppend, kStream>), dim3(blocks + tail),
+                       dim3(threads), 0,
                        st, a);
   } else {
     const dim3 grid(pl.blocks_per_item, pl.num_parts, num_seqs);
-    hipLaunchKernelGGL((attn_partition_kernel<T, D, GW, P, kAppend>), grid, dim3(64 * pl.waves_per_block),
+    hipLaunchKernelGGL((attn_partition_kernel<T, D, GW, P, kAppend, kStream>), grid,
+                       dim3(64 * pl.waves_per_block),
                        0, st, a);
   }
   if (hipError_t e = hipGetLastError())
@@ -1140,15 +1153,16 @@ pkv_status launch_main_p(const Plan& pl, AttnArgs& a, int num_seqs, hipStream_t 
 
 // The grid of the balanced merge depends on W, which the main launch fixes;
 // a phase-2-only call recomputes it the same way.
-template <typename T, int D, int GW, bool kAppend>
+template <typename T, int D, int GW, bool kAppend, bool kStream = true>
 int balanced_groups(const Plan& pl) {
-  const void* k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 2, kAppend>);
-  if constexpr (ring_built<T, GW, 4>())
+  const void* k =
+      reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 2, kAppend, kStream>);
+  if constexpr (kStream && ring_built<T, GW, 4>())
     if (pl.prefetch == 4)
-      k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 4, kAppend>);
-  if constexpr (ring_built<T, GW, 3>())
+      k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 4, kAppend, true>);
+  if constexpr (kStream && ring_built<T, GW, 3>())
     if (pl.prefetch == 3)
-      k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 3, kAppend>);
+      k = reinterpret_cast<const void*>(&attn_balanced_kernel<T, D, GW, 3, kAppend, true>);
   int blocks = resident_blocks(k, 64 * pl.waves_per_block);
   const int max_blocks = kMaxWaveGroups / pl.groups_per_block;
   if (blocks > max_blocks) blocks = max_blocks;
@@ -1158,19 +1172,25 @@ int balanced_groups(const Plan& pl) {
 template <typename T, int D, int GW>
 pkv_status dispatch_gw(int phases, const Plan& pl, AttnArgs& a, int num_seqs, int num_q_heads,
                        hipStream_t st) {
-  // the fused-append variant (bf16/f32 pools only) has its own occupancy,
-  // so a phase-2-only call derives W from the same variant as phase 1
+  // the fused-append variant (bf16/f32 pools only) and the cacheable-load
+  // variant (ring of 2, no fused append) have their own occupancy, so a
+  // phase-2-only call derives W from the same variant as phase 1
   const bool append = !kQuant<T> && a.k_new != nullptr;
+  const bool cached = !a.stream_kv;
   if (phases & 1) {
     pkv_status s;
-    if constexpr (!kQuant<T>)
+    if (cached)
+      s = launch_main<T, D, GW, 2, false, false>(pl, a, num_seqs, st);
+    else if constexpr (!kQuant<T>)
       s = append ? launch_main_p<T, D, GW, true>(pl, a, num_seqs, st)
                  : launch_main_p<T, D, GW, false>(pl, a, num_seqs, st);
     else
       s = launch_main_p<T, D, GW, false>(pl, a, num_seqs, st);
     if (s) return s;
   } else if (pl.mode == kBalancedMode) {
-    if constexpr (!kQuant<T>)
+    if (cached)
+      a.num_groups = balanced_groups<T, D, GW, false, false>(pl);
+    else if constexpr (!kQuant<T>)
       a.num_groups = append ? balanced_groups<T, D, GW, true>(pl)
                             : balanced_groups<T, D, GW, false>(pl);
     else
@@ -1269,8 +1289,11 @@ pkv_status attention_impl(const char* who, int32_t phases, const void* q, const 
                           int32_t num_q_heads, int32_t max_seq_len, int32_t partition_tokens,
                           void* workspace, size_t workspace_bytes, const pkv_geom* geom,
                           void* stream, const NewToken& nt = NewToken()) {
-  if (phases < 1 || phases > 3)
-    return pkv::fail(PKV_ERR_INVALID_ARG, "%s: phases must be 1, 2 or 3", who);
+  if ((phases & ~(3 | PKV_KV_SHARED)) || !(phases & 3))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "%s: phases must be 1, 2 or 3 (optionally | PKV_KV_SHARED)",
+                     who);
+  const bool kv_shared = (phases & PKV_KV_SHARED) != 0;
+  phases &= 3;
   Plan pl;
   if (pkv_status st = make_plan(num_seqs, num_q_heads, max_seq_len, max_blocks_per_seq,
                                 partition_tokens, geom, who, &pl))
@@ -1350,7 +1373,8 @@ pkv_status attention_impl(const char* who, int32_t phases, const void* q, const 
   // The append rides in the attention kernel for waves of up to two query
   // heads; with more the kernel is issue-bound and a copy launch costs less.
   const int ka = knob_append();
-  const bool fold = append && pl.mode != kMatrixMode && (ka ? ka == 2 : pl.gw <= 2);
+  const bool fold = append && !kv_shared && pl.mode != kMatrixMode && (ka ? ka == 2 : pl.gw <= 2);
+  a.stream_kv = kv_shared ? 0 : 1;
   a.k_new = fold ? nt.k : nullptr;
   a.v_new = fold ? nt.v : nullptr;
   a.new_slots = fold ? nt.slots : nullptr;
@@ -1372,7 +1396,7 @@ pkv_status attention_impl(const char* who, int32_t phases, const void* q, const 
                                           a.k_scales, a.v_scales, block_tables,
                                           max_blocks_per_seq, seq_lens, scale, out, num_seqs,
                                           num_q_heads, pl.len_cap, pl.part_tokens, pl.num_parts,
-                                          a.ws_acc, a.ws_ml, geom, st))
+                                          a.ws_acc, a.ws_ml, !kv_shared, geom, st))
         return e;
     }
     if ((phases & 2) && pl.num_parts > 1) {

@@ -64,7 +64,7 @@ struct MultiArgs {
   const float* v_scales;
 };
 
-template <int D, int NW, int Q>
+template <int D, int NW, int Q, bool kStream>
 __global__ void __launch_bounds__(64 * NW)
 attn_multi_kernel(MultiArgs a) {
   __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D, NW>()];
@@ -118,8 +118,8 @@ attn_multi_kernel(MultiArgs a) {
   constexpr int kPD = NW >= 2 ? 2 : 1;
   if (a.num_parts == 1) {
     // every row of the block sees the positions up to its first query's
-    pkv::mfma::attend<D, NW, kPD, Q>(hist, t_lo, t_hi, a.q + qh * D, row_ok, p_row, p_first,
-                                     a.scale_log2, k_lds, v_lds, r, s_lds);
+    pkv::mfma::attend<D, NW, kPD, Q, kStream>(hist, t_lo, t_hi, a.q + qh * D, row_ok, p_row,
+                                              p_first, a.scale_log2, k_lds, v_lds, r, s_lds);
     if (row_ok) pkv::mfma::store_row_bf16<D>(r, a.out + qh * D);
     return;
   }
@@ -129,8 +129,9 @@ attn_multi_kernel(MultiArgs a) {
     const int64_t prow = qh * a.num_parts + t / a.part_tokens;
     pkv::mfma::store_piece<D>(rr, a.ws_acc + prow * D, a.ws_ml + prow);
   };
-  pkv::mfma::attend<D, NW, kPD, Q>(hist, t_lo, t_hi, a.q + qh * D, row_ok, p_row, p_first,
-                                   a.scale_log2, k_lds, v_lds, r, s_lds, a.part_tokens, emit);
+  pkv::mfma::attend<D, NW, kPD, Q, kStream>(hist, t_lo, t_hi, a.q + qh * D, row_ok, p_row,
+                                            p_first, a.scale_log2, k_lds, v_lds, r, s_lds,
+                                            a.part_tokens, emit);
   if (row_ok && a.ws_np && (lane >> 4) == 0 && run == 0) {
     const int np = p_row < 0 ? 0 : min(a.num_parts, p_row / a.part_tokens + 1);
     a.ws_np[qh] = np;
@@ -272,18 +273,34 @@ pkv_status multi_plan(int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
   return PKV_OK;
 }
 
-// The main kernel only (no merge).
+template <int D, int Q, bool kStream>
+void launch_multi_variant(const MultiPlan& pl, const MultiArgs& a, int num_seqs,
+                          int num_kv_heads, hipStream_t st);
+
+// The main kernel only (no merge).  K/V are streamed with non-temporal loads
+// when each (sequence, KV head) history is read by one query block and the
+// caller does not report shared blocks; with several query blocks (prefill
+// chunks) every block re-reads the history, which then stays cacheable.
 template <int D, int Q>
 void launch_multi_main(const MultiPlan& pl, const MultiArgs& a, int num_seqs, int num_kv_heads,
-                       hipStream_t st) {
+                       hipStream_t st, bool shared_blocks = false) {
+  if (pl.qblocks == 1 && !shared_blocks)
+    launch_multi_variant<D, Q, true>(pl, a, num_seqs, num_kv_heads, st);
+  else
+    launch_multi_variant<D, Q, false>(pl, a, num_seqs, num_kv_heads, st);
+}
+
+template <int D, int Q, bool kStream>
+void launch_multi_variant(const MultiPlan& pl, const MultiArgs& a, int num_seqs,
+                          int num_kv_heads, hipStream_t st) {
   const dim3 grid(pl.qblocks * num_kv_heads * num_seqs, pl.runs);
   switch (pl.nw) {
-    case 1: hipLaunchKernelGGL((attn_multi_kernel<D, 1, Q>), grid, dim3(64), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((attn_multi_kernel<D, 2, Q>), grid, dim3(128), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((attn_multi_kernel<D, 4, Q>), grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((attn_multi_kernel<D, 1, Q, kStream>), grid, dim3(64), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((attn_multi_kernel<D, 2, Q, kStream>), grid, dim3(128), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((attn_multi_kernel<D, 4, Q, kStream>), grid, dim3(256), 0, st, a); break;
     default:
       if constexpr (D == 128 && Q == pkv::mfma::kBf16)  // the plan's condition for 8 waves
-        hipLaunchKernelGGL((attn_multi_kernel<D, 8, Q>), grid, dim3(512), 0, st, a);
+        hipLaunchKernelGGL((attn_multi_kernel<D, 8, Q, kStream>), grid, dim3(512), 0, st, a);
       break;
   }
 }
@@ -398,8 +415,8 @@ pkv_status mfma_decode(const void* q, const void* k_cache, const void* v_cache, 
                        const float* v_scales, const int32_t* block_tables, int32_t max_blocks,
                        const int32_t* seq_lens, float scale, void* out, int32_t num_seqs,
                        int32_t num_q_heads, int32_t len_cap, int32_t part_tokens,
-                       int32_t num_parts, float* ws_acc, float2* ws_ml, const pkv_geom* g,
-                       hipStream_t st) {
+                       int32_t num_parts, float* ws_acc, float2* ws_ml, bool stream_kv,
+                       const pkv_geom* g, hipStream_t st) {
   const int G = num_q_heads / g->num_kv_heads;
   MultiPlan pl;
   pl.nw = G <= 16 ? 1 : (G <= 32 ? 2 : 4);
@@ -447,11 +464,11 @@ pkv_status mfma_decode(const void* q, const void* k_cache, const void* v_cache, 
   a.k_scales = kind == pkv::mfma::kInt8 ? k_scales : nullptr;
   a.v_scales = kind == pkv::mfma::kInt8 ? v_scales : nullptr;
   if (kind == pkv::mfma::kFp8)
-    launch_multi_main<128, pkv::mfma::kFp8>(pl, a, num_seqs, g->num_kv_heads, st);
+    launch_multi_main<128, pkv::mfma::kFp8>(pl, a, num_seqs, g->num_kv_heads, st, !stream_kv);
   else if (kind == pkv::mfma::kInt8)
-    launch_multi_main<128, pkv::mfma::kInt8>(pl, a, num_seqs, g->num_kv_heads, st);
+    launch_multi_main<128, pkv::mfma::kInt8>(pl, a, num_seqs, g->num_kv_heads, st, !stream_kv);
   else
-    launch_multi_main<128, pkv::mfma::kBf16>(pl, a, num_seqs, g->num_kv_heads, st);
+    launch_multi_main<128, pkv::mfma::kBf16>(pl, a, num_seqs, g->num_kv_heads, st, !stream_kv);
   if (hipError_t e = hipGetLastError())
     return pkv::fail(PKV_ERR_HIP, "pkv_attention_decode: matrix-core launch failed: %s",
                      hipGetErrorString(e));

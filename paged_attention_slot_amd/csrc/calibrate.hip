@@ -1,9 +1,11 @@
-// Read-bandwidth calibration for gfx950 (pkv_stream_read): a plain,
-// perfectly coalesced 16-byte-per-lane stream over a buffer.  Its rate is the
+// Read-bandwidth calibration for gfx950 (pkv_stream_read): a perfectly
+// coalesced 16-byte-per-lane stream over a buffer, with the non-temporal
+// loads the attention kernels use for their K/V stream.  Its rate is the
 // practical ceiling of an HBM-bound kernel on this device, measured the same
 // way as the attention kernels.
 #include <hip/hip_runtime.h>
 
+#include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace {
@@ -19,12 +21,12 @@ stream_read_kernel(const uint4* __restrict__ src, int64_t n16, uint32_t* __restr
   for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
     uint4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = src[i + u * stride];
+    for (int u = 0; u < kUnroll; ++u) v[u] = pkv::load_stream(src + i + u * stride);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (; i < n16; i += stride) {
-    const uint4 v = src[i];
+    const uint4 v = pkv::load_stream(src + i);
     x ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   // Keeps the loads alive; the branch is data-dependent but cheap.

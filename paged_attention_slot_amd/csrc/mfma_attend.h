@@ -186,7 +186,7 @@ struct NoEmit {
   template <class R> __device__ void operator()(int, R&) const {}
 };
 
-template <int D, int NW, int PD = 1, int Q = kBf16, class Emit = NoEmit>
+template <int D, int NW, int PD = 1, int Q = kBf16, bool kStream = false, class Emit = NoEmit>
 __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, const uint16_t* q,
                                        bool row_ok, int p_row, int p_all, float scale_log2,
                                        uint16_t* k_lds, uint16_t* v_lds, RowAcc<D>& r,
@@ -227,6 +227,11 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
   // The tile's (at most 4, block_size >= 8) block ids are uniform: scalar
   // loads, which do not queue behind the vector loads still in flight.
   const int last_idx = L > 0 ? (L - 1) >> h.block_shift : -1;
+  // K/V tile loads: non-temporal when the caller reads each byte once
+  const auto kv_load = [](const char* p) {
+    if constexpr (kStream) return load_stream(p);
+    else return *reinterpret_cast<const uint4*>(p);
+  };
   auto fetch = [&](int j, int t0) {
     const int b0 = t0 >> h.block_shift;
     int ids[4];
@@ -249,8 +254,8 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
     if (t0 + kKT <= L) {  // uniform: the whole tile is history
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
-        nk[j][i] = *reinterpret_cast<const uint4*>(kb + i * rstep);
-        nv[j][i] = *reinterpret_cast<const uint4*>(vb + i * rstep);
+        nk[j][i] = kv_load(kb + i * rstep);
+        nv[j][i] = kv_load(vb + i * rstep);
       }
     } else {
 #pragma unroll
@@ -258,8 +263,8 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
         nk[j][i] = make_uint4(0, 0, 0, 0);
         nv[j][i] = make_uint4(0, 0, 0, 0);
         if (p0 + i < L) {
-          nk[j][i] = *reinterpret_cast<const uint4*>(kb + i * rstep);
-          nv[j][i] = *reinterpret_cast<const uint4*>(vb + i * rstep);
+          nk[j][i] = kv_load(kb + i * rstep);
+          nv[j][i] = kv_load(vb + i * rstep);
         }
       }
     }

@@ -126,8 +126,11 @@ def _scales(k_cache, k_scale, v_scale, k_scales, v_scales) -> PkvKvScales:
                        _ptr(v_scales).value or None)
 
 
+KV_SHARED = 4  # PKV_KV_SHARED: or-ed into phases when sequences share blocks
+
+
 def _attention(q, k_cache, v_cache, block_tables, seq_lens, scale, out, max_seq_len,
-               partition_tokens, workspace, stream, phases, scales, new=None):
+               partition_tokens, workspace, stream, phases, scales, new=None, kv_shared=False):
     g = geom_of(k_cache)
     dev = k_cache.device
     quant = k_cache.dtype in _QUANT
@@ -160,6 +163,7 @@ def _attention(q, k_cache, v_cache, block_tables, seq_lens, scale, out, max_seq_
     common = (_ptr(block_tables), max_blocks, _ptr(seq_lens), float(scale), _ptr(out), N, Hq,
               int(max_seq_len), int(partition_tokens), _ptr(workspace), ws_bytes,
               ctypes.byref(g), _stream(stream))
+    phases = int(phases) | (KV_SHARED if kv_shared else 0)
     if new is not None:
         k_new, v_new, slots = new
         check(lib().pkv_attention_decode_append(int(phases), _ptr(q), _ptr(k_new), _ptr(v_new),
@@ -177,7 +181,7 @@ def _attention(q, k_cache, v_cache, block_tables, seq_lens, scale, out, max_seq_
 
 def attention_decode(q, k_cache, v_cache, block_tables, seq_lens, scale, out=None,
                      max_seq_len=None, partition_tokens=0, workspace=None, stream=None,
-                     phases=3):
+                     phases=3, kv_shared=False):
     """Decode attention; returns ``out`` [N, H_q, D] (allocated if None).
 
     ``max_seq_len`` is the host-known bound of ``seq_lens`` (default: the
@@ -188,12 +192,12 @@ def attention_decode(q, k_cache, v_cache, block_tables, seq_lens, scale, out=Non
     if k_cache.dtype in _QUANT:
         raise TypeError("quantized pools: use attention_decode_quant")
     return _attention(q, k_cache, v_cache, block_tables, seq_lens, scale, out, max_seq_len,
-                      partition_tokens, workspace, stream, phases, None)
+                      partition_tokens, workspace, stream, phases, None, kv_shared=kv_shared)
 
 
 def attention_decode_append(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
                             seq_lens, scale, out=None, max_seq_len=None, partition_tokens=0,
-                            workspace=None, stream=None, phases=3):
+                            workspace=None, stream=None, phases=3, kv_shared=False):
     """The step's KV append and decode attention in one computation
     (pkv_attention_decode_append): k_new/v_new [N, H_kv, D] in the pool dtype,
     slot_mapping int32 [N] the slot of each sequence's newest position; the
@@ -211,13 +215,13 @@ def attention_decode_append(q, k_new, v_new, slot_mapping, k_cache, v_cache, blo
         raise ValueError("k_new/v_new must be [N, H_kv, D] and slot_mapping [N]")
     return _attention(q, k_cache, v_cache, block_tables, seq_lens, scale, out, max_seq_len,
                       partition_tokens, workspace, stream, phases, None,
-                      new=(k_new, v_new, slot_mapping))
+                      new=(k_new, v_new, slot_mapping), kv_shared=kv_shared)
 
 
 def attention_decode_quant(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale=1.0,
                            v_scale=1.0, k_scales=None, v_scales=None, out=None,
                            max_seq_len=None, partition_tokens=0, workspace=None, stream=None,
-                           phases=3):
+                           phases=3, kv_shared=False):
     """Decode attention over an FP8 e4m3 (``torch.float8_e4m3fn`` pools,
     per-tensor ``k_scale``/``v_scale``) or INT8 (``torch.int8`` pools, fp32
     ``k_scales``/``v_scales`` [num_blocks * block_size, num_kv_heads]) cache;
@@ -226,7 +230,7 @@ def attention_decode_quant(q, k_cache, v_cache, block_tables, seq_lens, scale, k
         raise TypeError("attention_decode_quant needs float8_e4m3fn or int8 pools")
     sc = _scales(k_cache, k_scale, v_scale, k_scales, v_scales)
     return _attention(q, k_cache, v_cache, block_tables, seq_lens, scale, out, max_seq_len,
-                      partition_tokens, workspace, stream, phases, sc)
+                      partition_tokens, workspace, stream, phases, sc, kv_shared=kv_shared)
 
 
 def attention_multi(q, q_offsets, k_cache, v_cache, block_tables, seq_lens, scale,

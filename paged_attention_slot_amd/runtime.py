@@ -57,6 +57,17 @@ def to_host_bits(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
 
 
+def shares_blocks(tables: np.ndarray, lens: np.ndarray, block_size: int) -> bool:
+    """Whether two sequences of the batch read the same physical block (prefix
+    sharing, forks): the attention then keeps K/V loads cacheable
+    (PKV_KV_SHARED)."""
+    used = [tables[s, :-(-int(L) // block_size)] for s, L in enumerate(lens) if L > 0]
+    if not used:
+        return False
+    ids = np.concatenate(used)
+    return np.unique(ids).size < ids.size
+
+
 _CACHE_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16,
                  "fp8_e4m3": torch.float8_e4m3fn, "int8": torch.int8}
 
@@ -120,6 +131,7 @@ class DecodeStep:
         self.bm = bm
         self.slot_mapping_h, self.cow_pairs_h = slots, cow
         self.block_tables_h, self.seq_lens_h = tables, lens
+        self.kv_shared = shares_blocks(tables, lens, wl.block_size)
         if not np.array_equal(lens, wl.seq_lens):
             raise RuntimeError("block manager lengths differ from the workload's")
 
@@ -226,7 +238,8 @@ class DecodeStep:
         if pt != self.partition_tokens:
             ws = None  # let the binding size a workspace for this split
         kw = dict(out=self.out if out is None else out, max_seq_len=self.max_seq_len,
-                  partition_tokens=pt, workspace=ws, stream=stream, phases=phases)
+                  partition_tokens=pt, workspace=ws, stream=stream, phases=phases,
+                  kv_shared=self.kv_shared)
         if self.quant:
             ks, vs = self._scales(layer)
             return ops.attention_decode_quant(self.q, self.k_caches[layer], self.v_caches[layer],
@@ -245,7 +258,7 @@ class DecodeStep:
             self.v_caches[layer], self.block_tables, self.seq_lens, self.wl.scale,
             out=self.out if out is None else out, max_seq_len=self.max_seq_len,
             partition_tokens=self.partition_tokens, workspace=self.workspace, stream=stream,
-            phases=phases)
+            phases=phases, kv_shared=self.kv_shared)
 
     def shared_groups(self):
         """Shared-prefix groups of the step's tables (pkv_prefix_groups), as

@@ -103,6 +103,20 @@ def test_small_write_and_attention(dtype, B, D, Hq, Hkv):
                 assert np.array_equal(out[i, h], to_f64(wl.new_v[i, h // G]))
 
 
+@pytest.mark.parametrize("name", ["qwen3-0.6b-layer", "shared-prefix-cow", "llama3.1-70b-longctx"])
+def test_cacheable_and_streaming_loads_agree(name):
+    """PKV_KV_SHARED only changes how K/V are loaded (cacheable instead of
+    non-temporal), so both give bit-identical outputs, whichever the batch."""
+    wl = config_workload(name)
+    step, _ = run_both(wl, attention=False)
+    a = host_bits(step.attention(out=torch.empty_like(step.q)))
+    step.kv_shared = not step.kv_shared
+    b = host_bits(step.attention(out=torch.empty_like(step.q)))
+    torch.cuda.synchronize()
+    say(f"  kv_shared (detected) = {not step.kv_shared}, split {step.split}")
+    assert np.array_equal(a, b)
+
+
 @pytest.mark.parametrize("ppw", [None, "3"])
 @pytest.mark.parametrize("pt", [0, 32, 96, 512])
 def test_matrix_route_matches_oracle(pt, ppw, monkeypatch):

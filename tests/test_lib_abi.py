@@ -85,6 +85,12 @@ def test_attention_validation_and_workspace_size():
     assert call(g(), pt=24) == _lib.PKV_ERR_INVALID_ARG
     assert call(g(), scale=float("nan")) == _lib.PKV_ERR_INVALID_ARG
     assert call(g(), N=0) == _lib.PKV_OK
+    # phases: 1, 2 or 3, optionally with PKV_KV_SHARED (4)
+    for bad in (0, 4, 8, 11):
+        assert lib.pkv_attention_decode_phase(bad, x, x, x, x, 7, x, 0.1, x, 2, 8, 100, 0, None,
+                                              0, ctypes.byref(g()), None) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_attention_decode_phase(7, x, x, x, x, 7, x, 0.1, x, 0, 8, 100, 0, None, 0,
+                                          ctypes.byref(g()), None) == _lib.PKV_OK
     # a fixed split needs a workspace
     assert call(g(), maxlen=100, pt=32) == _lib.PKV_ERR_INVALID_ARG
     assert "workspace" in last_error()
