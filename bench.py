@@ -720,9 +720,12 @@ def main() -> int:
             "partition_us_p10_p90": [float(np.percentile(part, 10)) * 1e6,
                                      float(np.percentile(part, 90)) * 1e6],
             "merge_us_mean": float(np.mean(merge)) * 1e6,
-            "append": "fused into the attention kernel" if fused else "separate write kernel",
+            "append": (("folded into the attention kernel" if step.append_folded else
+                        "row-copy kernel, then the attention (pkv_attention_decode_append)")
+                       if fused else "separate write kernel"),
             "kv_loads": ("cacheable (the batch shares blocks)" if step.kv_shared
-                         else "non-temporal (every block read once)"),
+                         else "non-temporal where one wave or query block covers a KV head's "
+                              "group (each block read once)"),
             "copy_write_us_mean": float(np.mean(cw)) * 1e6,
             "device_step_us_mean": float(np.mean(dev_step)) * 1e6,
             "step_timing": "hip graph replay" if graph_wall is not None else "eager launches",

@@ -289,6 +289,16 @@ enum { PKV_ROUTE_PARTITIONS = 0, PKV_ROUTE_BALANCED = 1, PKV_ROUTE_MATRIX = 2 };
 int32_t pkv_attention_decode_route(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
                                    int32_t partition_tokens, const pkv_geom* geom);
 
+/* Whether pkv_attention_decode_append stores the new K/V rows from inside
+ * the attention kernel (1) or launches a row-copy kernel before it (0) for
+ * these sizes: the results are the same either way; this reports which
+ * kernels run, for profiling.  kv_shared: nonzero when the call carries
+ * PKV_KV_SHARED.  bf16 and f32 pools only; -1 on invalid arguments or a
+ * one-byte pool dtype. */
+int32_t pkv_attention_decode_append_folded(int32_t num_seqs, int32_t num_q_heads,
+                                           int32_t max_seq_len, int32_t partition_tokens,
+                                           int32_t kv_shared, const pkv_geom* geom);
+
 /* Workspace bytes pkv_attention_decode needs for these sizes (0 when no split
  * happens).  partition_tokens as for pkv_attention_decode (0 = automatic).
  * Returns (size_t)-1 on invalid arguments. */
@@ -351,7 +361,9 @@ pkv_status pkv_attention_decode(const void* q, const void* k_cache, const void* 
  * K/V with cacheable loads and a block read by many sequences is served from
  * the caches; without it every K/V byte is assumed to be read once per call
  * and is streamed with non-temporal loads (faster by 8-9 % on unshared
- * batches, up to 40 % slower on shared ones).  Same results either way.
+ * batches, up to 40 % slower on shared ones) where one wave carries a KV
+ * head's whole query group (groups split over several waves re-read each
+ * tile and keep cacheable loads).  Same results either way.
  * Arguments and errors as for pkv_attention_decode; INVALID_ARG for any
  * other phases value. */
 #define PKV_KV_SHARED 4
@@ -474,6 +486,7 @@ pkv_status pkv_attention_multi_quant(const void* q, const int32_t* q_offsets, co
  *                                  partitions one workgroup walks
  *   PKV_ATTN_APPEND          pkv_attention_decode_append: 1 = copy kernel
  *                                  first, 2 = folded into the attention kernel
+ *                                  (vector routes with non-temporal loads only)
  * They change speed and register use, never results beyond fp32 rounding
  * order across query-head groupings (each head's arithmetic is unchanged). */
 

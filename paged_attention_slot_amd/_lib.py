@@ -63,6 +63,8 @@ SIGNATURES = {
                                     c_i32, c_void_p, c_size, ctypes.POINTER(PkvGeom), c_void_p]),
     "pkv_attention_partition_tokens": (c_i32, [c_i32, c_i32, c_i32, ctypes.POINTER(PkvGeom)]),
     "pkv_attention_decode_route": (c_i32, [c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(PkvGeom)]),
+    "pkv_attention_decode_append_folded": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32,
+                                                    ctypes.POINTER(PkvGeom)]),
     "pkv_attention_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32,
                                                ctypes.POINTER(PkvGeom)]),
     "pkv_attention_decode": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_i32, c_void_p,

@@ -239,7 +239,8 @@ __device__ __forceinline__ uint32_t bf16_pair_exact(float lo, float hi) {
 // One wave's attention over a stretch [start, end) of one stream.  kAppend:
 // the fused-append variant (pkv_attention_decode_append), bf16/f32 only.
 // kStream: the K/V tiles are read with non-temporal loads (each byte read
-// once per call); off for batches whose sequences share blocks, so the
+// once per call); off for batches whose sequences share blocks and for
+// groups split over sibling waves (which walk the same tiles), so the
 // re-read blocks stay cacheable.
 template <typename T, int D, int GW, int P, bool kAppend = false, bool kStream = true>
 struct Wave {
@@ -1230,6 +1231,27 @@ pkv_status dispatch(int phases, const Plan& pl, AttnArgs& a, int num_seqs, int n
 
 }  // namespace
 
+// Whether the vector kernels stream K/V with non-temporal loads: only when
+// every cached byte is read once, i.e. no block is shared between sequences
+// and one wave carries a KV head's whole query group.  Sibling waves of a
+// split group walk the same tiles just apart; the second read is served by
+// the L1 or the L2 only if the first left the lines cacheable (streaming
+// them cost 15 % on groups of 8 split over two waves).
+bool streams_kv(const Plan& pl, bool kv_shared) {
+  return !kv_shared && pl.waves_per_group == 1;
+}
+
+// Whether pkv_attention_decode_append stores the new rows from inside the
+// attention kernel: on the vector routes for waves of up to two query heads
+// (with more the kernel is issue-bound and a copy launch costs less), and
+// only where the kernel streams K/V: the cacheable-load kernels are built
+// without the folded store.
+bool folds_append(const Plan& pl, bool kv_shared) {
+  if (!streams_kv(pl, kv_shared) || pl.mode == kMatrixMode) return false;
+  const int ka = knob_append();
+  return ka ? ka == 2 : pl.gw <= 2;
+}
+
 extern "C" {
 
 int32_t pkv_attention_partition_tokens(int32_t num_seqs, int32_t num_q_heads,
@@ -1255,6 +1277,23 @@ int32_t pkv_attention_decode_route(int32_t num_seqs, int32_t num_q_heads, int32_
     return -1;
   return pl.mode == kMatrixMode ? PKV_ROUTE_MATRIX
          : pl.mode == kBalancedMode ? PKV_ROUTE_BALANCED : PKV_ROUTE_PARTITIONS;
+}
+
+int32_t pkv_attention_decode_append_folded(int32_t num_seqs, int32_t num_q_heads,
+                                           int32_t max_seq_len, int32_t partition_tokens,
+                                           int32_t kv_shared, const pkv_geom* geom) {
+  Plan pl;
+  const int32_t max_blocks =
+      geom && geom->block_size > 0 ? (max_seq_len + geom->block_size - 1) / geom->block_size : 0;
+  if (make_plan(num_seqs, num_q_heads, max_seq_len, max_blocks, partition_tokens, geom,
+                "pkv_attention_decode_append_folded", &pl) != PKV_OK)
+    return -1;
+  if (pkv::is_quant(geom->dtype)) {
+    pkv::fail(PKV_ERR_UNSUPPORTED,
+              "pkv_attention_decode_append_folded: the fused append takes bf16 or f32 pools");
+    return -1;
+  }
+  return folds_append(pl, kv_shared != 0) ? 1 : 0;
 }
 
 size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
@@ -1370,11 +1409,8 @@ pkv_status attention_impl(const char* who, int32_t phases, const void* q, const 
   a.k_scales = quant ? scales->k_scales : nullptr;
   a.v_scales = quant ? scales->v_scales : nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // The append rides in the attention kernel for waves of up to two query
-  // heads; with more the kernel is issue-bound and a copy launch costs less.
-  const int ka = knob_append();
-  const bool fold = append && !kv_shared && pl.mode != kMatrixMode && (ka ? ka == 2 : pl.gw <= 2);
-  a.stream_kv = kv_shared ? 0 : 1;
+  const bool fold = append && folds_append(pl, kv_shared);
+  a.stream_kv = streams_kv(pl, kv_shared) ? 1 : 0;
   a.k_new = fold ? nt.k : nullptr;
   a.v_new = fold ? nt.v : nullptr;
   a.new_slots = fold ? nt.slots : nullptr;

@@ -102,6 +102,20 @@ def decode_route(num_seqs: int, num_q_heads: int, max_seq_len: int, k_cache,
     return ROUTES[int(r)]
 
 
+def append_folded(num_seqs: int, num_q_heads: int, max_seq_len: int, k_cache,
+                  partition_tokens: int = 0, kv_shared: bool = False) -> bool:
+    """Whether pkv_attention_decode_append stores the new rows from inside the
+    attention kernel (True) or launches a row-copy kernel first (False)
+    (pkv_attention_decode_append_folded)."""
+    g = geom_of(k_cache)
+    r = lib().pkv_attention_decode_append_folded(num_seqs, num_q_heads, max_seq_len,
+                                                 int(partition_tokens), int(bool(kv_shared)),
+                                                 ctypes.byref(g))
+    if r < 0:
+        check(1, "pkv_attention_decode_append_folded")
+    return bool(r)
+
+
 def workspace_bytes(num_seqs: int, num_q_heads: int, max_seq_len: int, k_cache,
                     partition_tokens: int = 0) -> int:
     g = geom_of(k_cache)

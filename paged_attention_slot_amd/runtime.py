@@ -298,6 +298,13 @@ class DecodeStep:
         return {"mode": "matrix" if route == "matrix" else "partitions", "partition_tokens": pt,
                 "num_partitions": max(1, -(-self.max_seq_len // pt))}
 
+    @property
+    def append_folded(self) -> bool:
+        """Whether attention_append() stores the new rows from inside the
+        attention kernel (else a row-copy kernel runs first)."""
+        return ops.append_folded(self.wl.num_seqs, self.wl.num_q_heads, self.max_seq_len,
+                                 self.k_caches[0], self.partition_tokens or 0, self.kv_shared)
+
     def step(self, layer=0, stream=None, fused=False):
         """copy -> write -> attention on one layer's pools (enqueue only);
         ``fused``: copy -> append + attention (pkv_attention_decode_append)."""

@@ -325,6 +325,36 @@ def test_fused_append_entry_point_validates_on_the_host():
     assert "workspace" in last_error()
 
 
+def test_append_fold_query(monkeypatch):
+    """pkv_attention_decode_append_folded: the append rides in the attention
+    kernel on the vector routes for waves of up to two query heads, not on
+    batches that share blocks or whose query groups span several waves (both
+    keep cacheable loads), not on the matrix route; one-byte pools give -1
+    (the fused append refuses them)."""
+    monkeypatch.delenv("PKV_ATTN_APPEND", raising=False)
+    monkeypatch.delenv("PKV_ATTN_MODE", raising=False)
+    monkeypatch.delenv("PKV_ATTN_HEADS_PER_WAVE", raising=False)
+    lib = pkv.lib()
+
+    def folded(N, Hq, H, D, dt, shared=0, pt=0, maxlen=4096):
+        return lib.pkv_attention_decode_append_folded(
+            N, Hq, maxlen, pt, shared, ctypes.byref(g(nb=8192, H=H, D=D, dt=dt)))
+
+    assert folded(64, 16, 8, 128, _lib.PKV_BF16) == 1          # 2 heads per wave
+    assert folded(64, 16, 8, 128, _lib.PKV_BF16, shared=1) == 0
+    assert folded(64, 16, 8, 128, _lib.PKV_BF16, pt=256) == 1  # fixed partitions
+    assert folded(64, 8, 8, 128, _lib.PKV_F32) == 1            # 1 head per wave
+    assert folded(64, 16, 8, 128, _lib.PKV_F32) == 0           # group split over 2 waves
+    assert folded(64, 32, 8, 128, _lib.PKV_BF16) == 0          # 4 heads per wave
+    assert folded(4, 64, 8, 128, _lib.PKV_BF16) == 0           # matrix route
+    assert folded(4, 64, 8, 128, _lib.PKV_FP8_E4M3) == -1
+    assert folded(4, 63, 8, 128, _lib.PKV_BF16) == -1
+    monkeypatch.setenv("PKV_ATTN_APPEND", "2")
+    assert folded(64, 32, 8, 128, _lib.PKV_BF16) == 1
+    monkeypatch.setenv("PKV_ATTN_APPEND", "1")
+    assert folded(64, 16, 8, 128, _lib.PKV_BF16) == 0
+
+
 def test_decode_route_query():
     """pkv_attention_decode_route: 8+ query heads per KV head at head_dim 128
     (bf16 or one-byte pools, partitions a multiple of 32) take the matrix
