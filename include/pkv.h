@@ -335,7 +335,11 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *                 cores instead, with fixed partitions (a multiple of 32;
  *                 automatic: about 3072 (sequence, KV head, partition) items
  *                 of at least 256 positions); see
- *                 pkv_attention_decode_route.
+ *                 pkv_attention_decode_route.  There a workgroup folds the
+ *                 positions it walks into one piece: single partitions when
+ *                 they alone fill the GPU, else equal shares of each history
+ *                 (about 3072 workgroups in all), which equals the merge of
+ *                 the partition pieces up to fp32 rounding order.
  *   workspace     device buffer of at least pkv_attention_workspace_bytes(...)
  *                 bytes (may be NULL when that is 0); contents on entry are
  *                 ignored.  Calls that may run at the same time need
@@ -483,7 +487,9 @@ pkv_status pkv_attention_multi_quant(const void* q, const int32_t* q_offsets, co
  *   PKV_ATTN_MODE            1 = fixed partitions, 2 = balanced split,
  *                                  3 = the matrix-core route where it applies
  *   PKV_ATTN_PARTS_PER_WG    1..65535  matrix-core passes: consecutive
- *                                  partitions one workgroup walks
+ *                                  partitions one workgroup walks (the decode
+ *                                  route folds them into one piece, instead
+ *                                  of its equal shares)
  *   PKV_ATTN_APPEND          pkv_attention_decode_append: 1 = copy kernel
  *                                  first, 2 = folded into the attention kernel
  *                                  (vector routes with non-temporal loads only)

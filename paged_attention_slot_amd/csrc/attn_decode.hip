@@ -95,7 +95,9 @@ struct AttnArgs {
   // partition mode
   int32_t waves_per_item;   // H_kv * waves_per_group
   int32_t part_tokens;
-  int32_t num_parts;
+  int32_t num_parts;        // workspace rows per (sequence, query head)
+  int32_t piece_tokens;     // positions per workspace row: part_tokens, or the
+                            // matrix-core route's run (pkv::decode_runs)
   // balanced mode
   int32_t groups_per_block; // wave groups per workgroup
   int32_t num_groups;       // W: wave groups of the static (resident) part of the grid
@@ -683,7 +685,7 @@ __global__ void __launch_bounds__(kMergeThreads)
 attn_merge_kernel(AttnArgs a) {
   const int h = blockIdx.x, s = blockIdx.y;
   const int L = clamp_len(a.seq_lens[s], a.len_cap);
-  const int np = (L + a.part_tokens - 1) / a.part_tokens;
+  const int np = (L + a.piece_tokens - 1) / a.piece_tokens;
   const int64_t row0 = (int64_t(s) * a.num_q_heads + h) * a.num_parts;
   char* dst = static_cast<char*>(a.out) + ((int64_t(s) * a.num_q_heads + h) * D) * sizeof(T);
   merge_rows<T, D>(a.ws_acc, a.ws_ml, np, row0, 1, dst);
@@ -954,6 +956,8 @@ struct Plan {
   int len_cap;
   // partition mode
   int waves_per_item, blocks_per_item, part_tokens, num_parts;
+  // matrix mode: how runs of workgroups cut each history
+  pkv::DecodeRuns runs;
   // balanced mode
   int groups_per_block;
   int64_t rows;  // workspace rows of D floats
@@ -1023,8 +1027,10 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
     if (np > 65535) return pkv::fail(PKV_ERR_INVALID_ARG, "%s: more than 65535 partitions", who);
     pl->part_tokens = static_cast<int>(pt);
     pl->num_parts = static_cast<int>(np);
+    pl->runs = pkv::decode_runs(num_seqs, g->num_kv_heads, pl->len_cap, pl->part_tokens,
+                                pl->num_parts);
     if (pl->num_parts > 1) {
-      pl->rows = int64_t(num_seqs) * num_q_heads * pl->num_parts;
+      pl->rows = int64_t(num_seqs) * num_q_heads * pl->runs.runs;
       pl->ws_ml_off = size_t(pl->rows) * g->head_dim * sizeof(float);
       pl->ws_base_off = 0;
       pl->ws_bytes = pl->ws_ml_off + size_t(pl->rows) * sizeof(float2);
@@ -1399,7 +1405,8 @@ pkv_status attention_impl(const char* who, int32_t phases, const void* q, const 
   a.len_cap = pl.len_cap;
   a.waves_per_item = pl.waves_per_item;
   a.part_tokens = pl.part_tokens;
-  a.num_parts = pl.num_parts;
+  a.num_parts = pl.mode == kMatrixMode ? pl.runs.runs : pl.num_parts;
+  a.piece_tokens = pl.mode == kMatrixMode ? pl.runs.run_tokens : pl.part_tokens;
   a.groups_per_block = pl.groups_per_block;
   a.num_groups = 0;
   a.static_blocks = 0;
@@ -1432,7 +1439,7 @@ pkv_status attention_impl(const char* who, int32_t phases, const void* q, const 
                                           a.k_scales, a.v_scales, block_tables,
                                           max_blocks_per_seq, seq_lens, scale, out, num_seqs,
                                           num_q_heads, pl.len_cap, pl.part_tokens, pl.num_parts,
-                                          a.ws_acc, a.ws_ml, !kv_shared, geom, st))
+                                          pl.runs, a.ws_acc, a.ws_ml, !kv_shared, geom, st))
         return e;
     }
     if ((phases & 2) && pl.num_parts > 1) {

@@ -57,7 +57,9 @@ struct MultiArgs {
   int32_t num_kv_heads;
   int32_t num_parts;
   int32_t part_tokens;
-  int32_t parts_per_wg;     // consecutive partitions one workgroup walks
+  int32_t run_tokens;       // positions one workgroup walks (a multiple of 32)
+  int32_t piece_tokens;     // a piece ends at each multiple of this (and at t_hi)
+  int32_t piece_stride;     // workspace rows per (row, head)
   float scale_log2;         // FP8: the K tensor scale folded in
   float v_scale;            // FP8
   const float* k_scales;    // INT8
@@ -73,8 +75,8 @@ attn_multi_kernel(MultiArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(tid >> 6));
-  // grid = (query blocks * H_kv * sequences, runs of parts_per_wg
-  // partitions).  Workgroups go to the XCDs round robin in launch order, so
+  // grid = (query blocks * H_kv * sequences, runs of run_tokens
+  // positions).  Workgroups go to the XCDs round robin in launch order, so
   // the XCD of (x, run) follows x.  Rotating the item by the run (item = x +
   // run) spreads both every run over all XCDs and the runs of one item (one
   // long history) over different XCDs; run-fastest order put all of run p on
@@ -95,9 +97,8 @@ attn_multi_kernel(MultiArgs a) {
   const int L = Lraw < 0 ? 0 : (Lraw > a.len_cap ? a.len_cap : Lraw);
   const int p_first = L - n + j0;          // position of the block's first query
   const int p_last = p_first + jn - 1;
-  const int part0 = run * a.parts_per_wg;
-  const int t_lo = part0 * a.part_tokens;
-  const int t_hi = min(min(part0 + a.parts_per_wg, a.num_parts) * a.part_tokens, p_last + 1);
+  const int t_lo = run * a.run_tokens;
+  const int t_hi = min(min(t_lo + a.run_tokens, a.num_parts * a.part_tokens), p_last + 1);
   if (run > 0 && t_lo >= t_hi) return;     // no row of this block reaches these parts
 
   // This lane's row: (query token jl of the block, head hh of the group).
@@ -123,15 +124,17 @@ attn_multi_kernel(MultiArgs a) {
     if (row_ok) pkv::mfma::store_row_bf16<D>(r, a.out + qh * D);
     return;
   }
-  // one piece per partition of the run, at [row, head][partition]
+  // one piece per piece_tokens positions (a partition, or the whole run on
+  // the decode route), at [row, head][piece]; t_lo is a multiple of
+  // piece_tokens
   const auto emit = [&](int t, pkv::mfma::RowAcc<D>& rr) {
     if (!row_ok) return;
-    const int64_t prow = qh * a.num_parts + t / a.part_tokens;
+    const int64_t prow = qh * a.piece_stride + t / a.piece_tokens;
     pkv::mfma::store_piece<D>(rr, a.ws_acc + prow * D, a.ws_ml + prow);
   };
   pkv::mfma::attend<D, NW, kPD, Q, kStream>(hist, t_lo, t_hi, a.q + qh * D, row_ok, p_row,
                                             p_first, a.scale_log2, k_lds, v_lds, r, s_lds,
-                                            a.part_tokens, emit);
+                                            a.piece_tokens, emit);
   if (row_ok && a.ws_np && (lane >> 4) == 0 && run == 0) {
     const int np = p_row < 0 ? 0 : min(a.num_parts, p_row / a.part_tokens + 1);
     a.ws_np[qh] = np;
@@ -182,7 +185,7 @@ attn_multi_merge_wide_kernel(MultiArgs a) {
 }
 
 struct MultiPlan {
-  int nw, q_per_block, qblocks, part_tokens, num_parts, parts_per_wg, runs;
+  int nw, q_per_block, qblocks, part_tokens, num_parts, run_tokens, runs;
   size_t ws_bytes, ws_ml_off, ws_np_off;
 };
 
@@ -260,7 +263,7 @@ pkv_status multi_plan(int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
   int64_t ppw = wgs > 4096 ? (wgs + 3071) / 3072 : 1;
   if (const int k = knob_parts_per_wg()) ppw = k;
   if (ppw > np) ppw = np;
-  pl->parts_per_wg = static_cast<int>(ppw);
+  pl->run_tokens = static_cast<int>(ppw * pl->part_tokens);
   pl->runs = static_cast<int>((np + ppw - 1) / ppw);
   if (pl->num_parts > 1) {
     const size_t rowsq = size_t(total_q) * num_q_heads;
@@ -385,7 +388,9 @@ pkv_status multi_impl(const char* who, int types, const void* q, const int32_t* 
   a.num_kv_heads = geom->num_kv_heads;
   a.num_parts = pl.num_parts;
   a.part_tokens = pl.part_tokens;
-  a.parts_per_wg = pl.parts_per_wg;
+  a.run_tokens = pl.run_tokens;
+  a.piece_tokens = pl.part_tokens;
+  a.piece_stride = pl.num_parts;
   a.scale_log2 = static_cast<float>(double(scale) * 1.4426950408889634 *
                                     (kind == pkv::mfma::kFp8 ? double(scales->k_scale) : 1.0));
   a.v_scale = kind == pkv::mfma::kFp8 ? scales->v_scale : 1.f;
@@ -410,13 +415,38 @@ pkv_status multi_impl(const char* who, int types, const void* q, const int32_t* 
 
 namespace pkv {
 
+DecodeRuns decode_runs(int32_t num_seqs, int32_t num_kv_heads, int32_t len_cap,
+                       int32_t part_tokens, int32_t num_parts) {
+  DecodeRuns d;
+  const int64_t items = int64_t(num_seqs) * num_kv_heads;
+  const int64_t wgs = items * num_parts;
+  const int knob = knob_parts_per_wg();
+  if (knob) {
+    const int64_t ppw = knob < num_parts ? knob : num_parts;
+    d.run_tokens = static_cast<int32_t>(ppw * part_tokens);
+    d.runs = static_cast<int32_t>((num_parts + ppw - 1) / ppw);
+  } else if (wgs > 4096) {
+    // equal shares: about 3072 / items runs per history, cut at tiles
+    const int64_t tiles = len_cap > 0 ? (int64_t(len_cap) + kKT - 1) / kKT : 1;
+    int64_t w = (3072 + items - 1) / (items > 0 ? items : 1);
+    if (w > tiles) w = tiles;
+    const int64_t r = (tiles + w - 1) / w;
+    d.run_tokens = static_cast<int32_t>(r * kKT);
+    d.runs = static_cast<int32_t>((tiles + r - 1) / r);
+  } else {
+    d.run_tokens = part_tokens;
+    d.runs = num_parts;
+  }
+  return d;
+}
+
 pkv_status mfma_decode(const void* q, const void* k_cache, const void* v_cache, int kind,
                        float k_scale, float v_scale, const float* k_scales,
                        const float* v_scales, const int32_t* block_tables, int32_t max_blocks,
                        const int32_t* seq_lens, float scale, void* out, int32_t num_seqs,
                        int32_t num_q_heads, int32_t len_cap, int32_t part_tokens,
-                       int32_t num_parts, float* ws_acc, float2* ws_ml, bool stream_kv,
-                       const pkv_geom* g, hipStream_t st) {
+                       int32_t num_parts, const DecodeRuns& runs, float* ws_acc,
+                       float2* ws_ml, bool stream_kv, const pkv_geom* g, hipStream_t st) {
   const int G = num_q_heads / g->num_kv_heads;
   MultiPlan pl;
   pl.nw = G <= 16 ? 1 : (G <= 32 ? 2 : 4);
@@ -425,12 +455,8 @@ pkv_status mfma_decode(const void* q, const void* k_cache, const void* v_cache, 
   pl.qblocks = 1;
   pl.part_tokens = part_tokens;
   pl.num_parts = num_parts;
-  const int64_t wgs = int64_t(num_seqs) * g->num_kv_heads * num_parts;
-  int64_t ppw = wgs > 4096 ? (wgs + 3071) / 3072 : 1;
-  if (const int k = knob_parts_per_wg()) ppw = k;
-  if (ppw > num_parts) ppw = num_parts;
-  pl.parts_per_wg = static_cast<int>(ppw);
-  pl.runs = static_cast<int>((num_parts + ppw - 1) / ppw);
+  pl.run_tokens = runs.run_tokens;
+  pl.runs = runs.runs;
   pl.ws_bytes = pl.ws_ml_off = pl.ws_np_off = 0;
   MultiArgs a;
   a.q = static_cast<const uint16_t*>(q);
@@ -457,7 +483,9 @@ pkv_status mfma_decode(const void* q, const void* k_cache, const void* v_cache, 
   a.num_kv_heads = g->num_kv_heads;
   a.num_parts = num_parts;
   a.part_tokens = part_tokens;
-  a.parts_per_wg = pl.parts_per_wg;
+  a.run_tokens = runs.run_tokens;
+  a.piece_tokens = runs.run_tokens;
+  a.piece_stride = runs.runs;
   a.scale_log2 = static_cast<float>(double(scale) * 1.4426950408889634 *
                                     (kind == pkv::mfma::kFp8 ? double(k_scale) : 1.0));
   a.v_scale = kind == pkv::mfma::kFp8 ? v_scale : 1.f;

@@ -176,10 +176,10 @@ __device__ __forceinline__ void start(RowAcc<D>& r) {
 // every tile rescales: the branch would keep the compiler from interleaving
 // the tile's matrix work with its softmax (measured 20 % slower).
 //
-// Segments: with an ``emit`` functor, [t_lo, t_hi) is walked as consecutive
-// segments of ``seg`` positions (t_lo and seg multiples of the tile): after a
-// segment's last tile emit(t, r) receives the start t of that tile and the
-// segment's state, and the state starts afresh, while the tile stream (loads
+// Segments: with an ``emit`` functor, [t_lo, t_hi) is cut at the multiples
+// of ``seg`` (t_lo and seg multiples of the tile): after a segment's last
+// tile emit(t, r) receives the start t of that tile and the segment's state,
+// and the state starts afresh, while the tile stream (loads
 // in flight, LDS buffers) runs on across the boundary.  One workgroup can so
 // produce the pieces of several split-KV partitions in one pass.
 struct NoEmit {
@@ -224,9 +224,16 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
   float nks[PD], nvs[PD];  // INT8: this lane's position scales (lanes < 32)
   // Issue the global loads of the tile at t0 into buffer j (zeros past the
   // history: never unmasked, and they keep the products finite).
-  // The tile's (at most 4, block_size >= 8) block ids are uniform: scalar
-  // loads, which do not queue behind the vector loads still in flight.
+  // The tile's (at most 4, block_size >= 8) block ids come from a window of
+  // 64 table entries held one per lane (tcache: entry tcache_base + lane) and
+  // read with v_readlane, so a tile's loads do not wait for a table read:
+  // the window is reloaded only when a tile reaches past it.
   const int last_idx = L > 0 ? (L - 1) >> h.block_shift : -1;
+  int tcache_base = t_lo >> h.block_shift;
+  int tcache = tcache_base + lane <= last_idx ? h.trow[tcache_base + lane] : 0;
+  // Wait for the window here; otherwise the first v_readlane would wait for
+  // every load in flight, since the compiler cannot tell which path wrote it.
+  asm volatile("" ::"v"(tcache));
   // K/V tile loads: non-temporal when the caller reads each byte once
   const auto kv_load = [](const char* p) {
     if constexpr (kStream) return load_stream(p);
@@ -234,11 +241,16 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
   };
   auto fetch = [&](int j, int t0) {
     const int b0 = t0 >> h.block_shift;
+    if (b0 + 3 - tcache_base >= 64) {  // uniform, rare: move the window to b0
+      tcache_base = b0;
+      tcache = b0 + lane <= last_idx ? h.trow[b0 + lane] : 0;
+      asm volatile("" ::"v"(tcache));
+    }
     int ids[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int idx = b0 + k;
-      const int b = idx <= last_idx ? h.trow[idx] : 0;
+      const int b = idx <= last_idx ? __builtin_amdgcn_readlane(tcache, idx - tcache_base) : 0;
       ids[k] = (b >= 0 && b < h.num_blocks) ? b : 0;
     }
     // This lane's kPer positions p0 .. p0 + kPer - 1 lie in one block (t0 is
@@ -438,7 +450,7 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
       if constexpr (lds_tiles<NW>() == 2) buf ^= 1;
       if constexpr (!std::is_same<Emit, NoEmit>::value) {
         const int te = t + kKT;
-        if (te >= t_hi || (te - t_lo) % seg == 0) {  // uniform: a segment is complete
+        if (te >= t_hi || te % seg == 0) {  // uniform: a segment is complete
           emit(t, r);
           start(r);
         }

@@ -288,15 +288,24 @@ class DecodeStep:
     def split(self) -> dict:
         """How pkv_attention_decode runs this batch: the kernels ("route":
         vector kernels with fixed partitions or the balanced split, or the
-        matrix-core pass) and the partition length and count."""
+        matrix-core pass) and the partition length and count; on the
+        matrix-core route also the workgroups per (sequence, KV head), each of
+        which folds its positions into one piece."""
         route = ops.decode_route(self.wl.num_seqs, self.wl.num_q_heads, self.max_seq_len,
                                  self.k_caches[0], self.partition_tokens)
         if route == "balanced":
             return {"mode": "balanced"}
         pt = self.partition_tokens or ops.partition_tokens(
             self.wl.num_seqs, self.wl.num_q_heads, self.max_seq_len, self.k_caches[0])
-        return {"mode": "matrix" if route == "matrix" else "partitions", "partition_tokens": pt,
-                "num_partitions": max(1, -(-self.max_seq_len // pt))}
+        split = {"mode": "matrix" if route == "matrix" else "partitions", "partition_tokens": pt,
+                 "num_partitions": max(1, -(-self.max_seq_len // pt))}
+        if route == "matrix":
+            # one workspace row of D + 2 floats per (sequence, query head, run)
+            ws = ops.workspace_bytes(self.wl.num_seqs, self.wl.num_q_heads, self.max_seq_len,
+                                     self.k_caches[0], self.partition_tokens)
+            row = self.wl.num_seqs * self.wl.num_q_heads * (self.wl.head_dim + 2) * 4
+            split["workgroups_per_history"] = ws // row if ws else 1
+        return split
 
     @property
     def append_folded(self) -> bool:

@@ -143,6 +143,43 @@ def test_matrix_route_matches_oracle(pt, ppw, monkeypatch):
     say("  gate", assert_gate(got, ref, "bf16", f"matrix route pt={pt}"))
 
 
+@pytest.mark.parametrize("pt", [32, 64, 96])
+def test_matrix_route_equal_shares(pt, monkeypatch):
+    """More short partitions than the GPU holds at once on the matrix-core
+    route: workgroups take equal shares of 160 positions (cutting the 96-token
+    partitions) and fold each share into one piece, so the workspace holds
+    fewer rows than partitions.  Outputs against the oracle's split
+    attention; then again with one history emptied, which must give zeros."""
+    from paged_attention_slot_amd import ops
+    monkeypatch.delenv("PKV_ATTN_MODE", raising=False)
+    monkeypatch.delenv("PKV_ATTN_PARTS_PER_WG", raising=False)
+    wl = independent_workload([1, 2, 31, 33, 500, 2047, 6000, 7500], num_q_heads=64,
+                              num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16",
+                              seed=40 + pt)
+    step, ost = run_both(wl, partition_tokens=pt)
+    assert step.split["mode"] == "matrix"
+    n_parts = -(-wl.max_seq_len // pt)
+    whole = wl.num_seqs * wl.num_q_heads * n_parts * (128 + 2) * 4
+    ws = ops.workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.max_seq_len, step.k_cache, pt)
+    say(f"  workspace {ws} bytes, {whole} for one piece per partition")
+    assert 0 < ws < whole
+    got = gpu_out(step)
+    ref = oracle_split(wl.q, ost.k_pool, ost.v_pool, ost.block_tables, ost.seq_lens, wl.scale,
+                       pt)
+    say("  gate", assert_gate(got, ref, "bf16", f"equal shares pt={pt}"))
+    lens = step.seq_lens.clone()
+    lens[5] = 0
+    out = torch.full_like(step.q, 7.0)
+    ops.attention_decode(step.q, step.k_cache, step.v_cache, step.block_tables, lens, wl.scale,
+                         out=out, max_seq_len=wl.max_seq_len, partition_tokens=pt)
+    torch.cuda.synchronize()
+    o = to_f64(host_bits(out))
+    assert not o[5].any()
+    ref = oracle_split(wl.q, ost.k_pool, ost.v_pool, ost.block_tables, lens.cpu().numpy(),
+                       wl.scale, pt)
+    assert_gate(o, ref, "bf16", f"equal shares, one empty history, pt={pt}")
+
+
 @pytest.mark.parametrize("pt", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("dtype,B", [("bf16", 16), ("f32", 16), ("bf16", 32)])
 def test_split_kv_matches_oracle_and_unsplit(pt, dtype, B):

@@ -377,7 +377,13 @@ def test_decode_route_query():
     assert route(4, 64, 8, 64, _lib.PKV_BF16) == B
     assert route(4, 64, 8, 128, _lib.PKV_F32) == B
     assert route(4, 63, 8, 128, _lib.PKV_BF16) == -1
-    # the workspace of the matrix route: N * Hq * partitions rows of D + 2 floats
+    # the workspace of the matrix route: N * Hq * runs rows of D + 2 floats.
+    # 256 partitions of 512 over 32 (sequence, KV head) histories are more
+    # than the GPU holds at once: 96 equal shares of 1376 positions each
     n = lib.pkv_attention_workspace_bytes(4, 64, 131072, 512,
                                           ctypes.byref(g(nb=8192, H=8, D=128, dt=1)))
-    assert n == 4 * 64 * 256 * (128 + 2) * 4
+    assert n == 4 * 64 * 96 * (128 + 2) * 4
+    # few partitions fill the GPU as whole partitions: one piece each
+    n = lib.pkv_attention_workspace_bytes(4, 64, 4096, 512,
+                                          ctypes.byref(g(nb=8192, H=8, D=128, dt=1)))
+    assert n == 4 * 64 * 8 * (128 + 2) * 4
