@@ -1029,7 +1029,7 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
     pl->num_parts = static_cast<int>(np);
     pl->runs = pkv::decode_runs(num_seqs, g->num_kv_heads, pl->len_cap, pl->part_tokens,
                                 pl->num_parts);
-    if (pl->num_parts > 1) {
+    if (pl->runs.runs > 1) {
       pl->rows = int64_t(num_seqs) * num_q_heads * pl->runs.runs;
       pl->ws_ml_off = size_t(pl->rows) * g->head_dim * sizeof(float);
       pl->ws_base_off = 0;
@@ -1442,7 +1442,7 @@ pkv_status attention_impl(const char* who, int32_t phases, const void* q, const 
                                           pl.runs, a.ws_acc, a.ws_ml, !kv_shared, geom, st))
         return e;
     }
-    if ((phases & 2) && pl.num_parts > 1) {
+    if ((phases & 2) && pl.runs.runs > 1) {
       hipLaunchKernelGGL((attn_merge_kernel<uint16_t, 128>), dim3(num_q_heads, num_seqs),
                          dim3(kMergeThreads), 0, st, a);
       if (hipError_t e = hipGetLastError())

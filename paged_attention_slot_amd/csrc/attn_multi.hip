@@ -117,8 +117,9 @@ attn_multi_kernel(MultiArgs a) {
   pkv::mfma::RowAcc<D> r;
   pkv::mfma::start(r);
   constexpr int kPD = NW >= 2 ? 2 : 1;
-  if (a.num_parts == 1) {
-    // every row of the block sees the positions up to its first query's
+  if (a.piece_stride == 1) {
+    // one run covers the history: every row of the block sees the positions
+    // up to its first query's
     pkv::mfma::attend<D, NW, kPD, Q, kStream>(hist, t_lo, t_hi, a.q + qh * D, row_ok, p_row,
                                               p_first, a.scale_log2, k_lds, v_lds, r, s_lds);
     if (row_ok) pkv::mfma::store_row_bf16<D>(r, a.out + qh * D);
@@ -136,7 +137,7 @@ attn_multi_kernel(MultiArgs a) {
                                             p_first, a.scale_log2, k_lds, v_lds, r, s_lds,
                                             a.piece_tokens, emit);
   if (row_ok && a.ws_np && (lane >> 4) == 0 && run == 0) {
-    const int np = p_row < 0 ? 0 : min(a.num_parts, p_row / a.part_tokens + 1);
+    const int np = p_row < 0 ? 0 : min(a.piece_stride, p_row / a.piece_tokens + 1);
     a.ws_np[qh] = np;
   }
 }
@@ -150,8 +151,8 @@ attn_multi_merge_kernel(MultiArgs a) {
   const int64_t qh = int64_t(blockIdx.y) * a.num_q_heads + blockIdx.x;
   const int lane = threadIdx.x;
   const int np_raw = a.ws_np[qh];
-  const int np = np_raw < 0 ? 0 : (np_raw > a.num_parts ? a.num_parts : np_raw);
-  const int64_t base = qh * a.num_parts;
+  const int np = np_raw < 0 ? 0 : (np_raw > a.piece_stride ? a.piece_stride : np_raw);
+  const int64_t base = qh * a.piece_stride;
   float M = -INFINITY;
   for (int p = lane; p < np; p += 64) M = fmaxf(M, a.ws_ml[base + p].x);
   M = pkv::wave_max(M);
@@ -179,8 +180,8 @@ __global__ void __launch_bounds__(pkv::kMergeThreads)
 attn_multi_merge_wide_kernel(MultiArgs a) {
   const int64_t qh = int64_t(blockIdx.y) * a.num_q_heads + blockIdx.x;
   const int np_raw = a.ws_np[qh];
-  const int np = np_raw < 0 ? 0 : (np_raw > a.num_parts ? a.num_parts : np_raw);
-  pkv::merge_rows<uint16_t, D>(a.ws_acc, a.ws_ml, np, qh * a.num_parts, 1,
+  const int np = np_raw < 0 ? 0 : (np_raw > a.piece_stride ? a.piece_stride : np_raw);
+  pkv::merge_rows<uint16_t, D>(a.ws_acc, a.ws_ml, np, qh * a.piece_stride, 1,
                                reinterpret_cast<char*>(a.out + qh * D));
 }
 
@@ -257,18 +258,18 @@ pkv_status multi_plan(int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
   if (np > 65535 || int64_t(pl->qblocks) * g->num_kv_heads * num_seqs > 2147483647LL)
     return pkv::fail(PKV_ERR_INVALID_ARG, "%s: too many partitions or query blocks", who);
   pl->num_parts = static_cast<int>(np);
-  // Runs of consecutive partitions per workgroup: about 3072 workgroups for
-  // many short partitions (each workgroup's ramp then covers several).
-  const int64_t wgs = int64_t(num_seqs) * g->num_kv_heads * pl->qblocks * np;
-  int64_t ppw = wgs > 4096 ? (wgs + 3071) / 3072 : 1;
-  if (const int k = knob_parts_per_wg()) ppw = k;
-  if (ppw > np) ppw = np;
-  pl->run_tokens = static_cast<int>(ppw * pl->part_tokens);
-  pl->runs = static_cast<int>((np + ppw - 1) / ppw);
-  if (pl->num_parts > 1) {
+  // Runs of positions per workgroup, each folded into one piece (as on the
+  // decode route): single partitions when they fill the GPU, else equal
+  // shares of about 3072 workgroups.
+  const pkv::DecodeRuns dr =
+      pkv::decode_runs(static_cast<int32_t>(int64_t(num_seqs) * pl->qblocks), g->num_kv_heads,
+                       len, pl->part_tokens, pl->num_parts);
+  pl->run_tokens = dr.run_tokens;
+  pl->runs = dr.runs;
+  if (pl->runs > 1) {
     const size_t rowsq = size_t(total_q) * num_q_heads;
-    pl->ws_ml_off = rowsq * pl->num_parts * g->head_dim * sizeof(float);
-    pl->ws_np_off = pl->ws_ml_off + rowsq * pl->num_parts * sizeof(float2);
+    pl->ws_ml_off = rowsq * pl->runs * g->head_dim * sizeof(float);
+    pl->ws_np_off = pl->ws_ml_off + rowsq * pl->runs * sizeof(float2);
     pl->ws_bytes = pl->ws_np_off + rowsq * sizeof(int32_t);
   } else {
     pl->ws_bytes = pl->ws_ml_off = pl->ws_np_off = 0;
@@ -312,10 +313,10 @@ template <int D, int Q>
 void launch_multi(const MultiPlan& pl, const MultiArgs& a, int num_seqs, int num_kv_heads,
                   int total_q, hipStream_t st) {
   launch_multi_main<D, Q>(pl, a, num_seqs, num_kv_heads, st);
-  if (pl.num_parts > 16 && total_q > 0)
+  if (pl.runs > 16 && total_q > 0)
     hipLaunchKernelGGL((attn_multi_merge_wide_kernel<D>), dim3(a.num_q_heads, total_q),
                        dim3(pkv::kMergeThreads), 0, st, a);
-  else if (pl.num_parts > 1 && total_q > 0)
+  else if (pl.runs > 1 && total_q > 0)
     hipLaunchKernelGGL((attn_multi_merge_kernel<D>), dim3(a.num_q_heads, total_q), dim3(64), 0,
                        st, a);
 }
@@ -389,8 +390,8 @@ pkv_status multi_impl(const char* who, int types, const void* q, const int32_t* 
   a.num_parts = pl.num_parts;
   a.part_tokens = pl.part_tokens;
   a.run_tokens = pl.run_tokens;
-  a.piece_tokens = pl.part_tokens;
-  a.piece_stride = pl.num_parts;
+  a.piece_tokens = pl.run_tokens;
+  a.piece_stride = pl.runs;
   a.scale_log2 = static_cast<float>(double(scale) * 1.4426950408889634 *
                                     (kind == pkv::mfma::kFp8 ? double(scales->k_scale) : 1.0));
   a.v_scale = kind == pkv::mfma::kFp8 ? scales->v_scale : 1.f;
