@@ -51,14 +51,17 @@ constexpr float kRefInit = -1e30f;  // reference of a row with no position yet
 // waves: the next tile is staged into one while the other is read; one
 // wave's LDS accesses run in order, so it needs one), and for INT8 the
 // tiles' position scales.
-// Row strides in LDS (bf16 elements): K rows padded by 16 bytes, so the
-// 16-byte operand reads of 8 consecutive rows fall in different banks; V rows
-// by 32 bytes, so the transposing reads (4 rows x 4 eight-byte columns per 16
-// lanes) do.
-template <int D> constexpr int k_stride() { return D + 8; }
+// Row strides in LDS (bf16 elements): V rows padded by 32 bytes, so the
+// transposing reads (4 rows x 4 eight-byte columns per 16 lanes) fall in
+// different banks.  K rows by 32 bytes too with several waves: a 16-byte
+// pad left the operand reads conflicting (the bank-conflict counter read
+// about one cycle per LDS instruction on 512-token prefill; 0 with 32), but
+// single-wave workgroups keep 16 bytes, where the larger tile would cost
+// one resident workgroup per CU.
+template <int D, int NW> constexpr int k_stride() { return NW == 1 ? D + 8 : D + 16; }
 template <int D> constexpr int v_stride() { return D + 16; }
 template <int NW> constexpr int lds_tiles() { return NW == 1 ? 1 : 2; }
-template <int D, int NW> constexpr int k_lds_elems() { return lds_tiles<NW>() * kKT * k_stride<D>(); }
+template <int D, int NW> constexpr int k_lds_elems() { return lds_tiles<NW>() * kKT * k_stride<D, NW>(); }
 template <int D, int NW> constexpr int v_lds_elems() { return lds_tiles<NW>() * kKT * v_stride<D>(); }
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -197,7 +200,7 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
   constexpr int kEB = Q == kBf16 ? 2 : 1;   // bytes per element
   constexpr int kKS = D / 32;            // k-steps of the score product
   constexpr int kDT = D / 16;            // 16-wide d tiles of the output
-  constexpr int kKStride = k_stride<D>();  // K rows in LDS, bf16 elements
+  constexpr int kKStride = k_stride<D, NW>();  // K rows in LDS, bf16 elements
   constexpr int kVStride = v_stride<D>();  // V rows
   constexpr int kEPC = 16 / kEB;         // elements per 16-byte chunk
   constexpr int kChunksPerRow = D / kEPC;  // 16-byte chunks per K/V row
@@ -205,11 +208,19 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
   const int tid = threadIdx.x, lane = tid & 63;
   const int quad = lane >> 4;
 
+  // Scores are scaled inside the exponent (one fma with the reference) and
+  // their max is taken unscaled, which needs a positive scale: a negative
+  // one flips the query's signs instead (exact in bf16), and the magnitude
+  // is kept off zero so a masked score never meets 0 * -inf.
+  const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
+  scale_log2 = fmaxf(fabsf(scale_log2), 1e-30f);
   uint4 qf[kKS];
 #pragma unroll
-  for (int ks = 0; ks < kKS; ++ks)
+  for (int ks = 0; ks < kKS; ++ks) {
     qf[ks] = row_ok ? *reinterpret_cast<const uint4*>(q + 32 * ks + 8 * quad)
                     : make_uint4(0, 0, 0, 0);
+    qf[ks] = make_uint4(qf[ks].x ^ qsign, qf[ks].y ^ qsign, qf[ks].z ^ qsign, qf[ks].w ^ qsign);
+  }
 
   const int L = h.len;
   const int bmask = (1 << h.block_shift) - 1;
@@ -351,17 +362,14 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
   // second half of the k dimension), columns 4 ((lane & 15) % 4) .. + 3 of
   // each 16-wide d tile.
   const uint16_t* v_rd = v_lds + (4 * quad + ((lane & 15) >> 2)) * kVStride + 4 * (lane & 3);
+  // Last position this lane's row sees (-1: none): the mask of a tile that
+  // not every live row sees whole is one compare per score against it.
+  const int row_lim = row_ok ? (p_row < t_hi - 1 ? p_row : t_hi - 1) : -1;
 
-  // One staged tile's matrix work (LDS tile buffer buf).
-  auto compute = [&](int t0, int buf) {
+  // A staged tile's scores S^T = K Q^T (LDS tile buffer buf): s[pt][i] is
+  // position 16 pt + 4 quad + i of the tile for row (lane & 15).
+  auto qk = [&](int buf, f32x4_t (&s)[2]) {
     const uint16_t* kt = k_lds + buf * kTileElems;
-    const uint16_t* vt = v_rd + buf * kVTileElems;
-    const float* st = s_lds + 2 * kKT * buf;
-    // Uniform: every live row sees every position of the tile.
-    const bool full = t0 + kKT - 1 <= p_all && t0 + kKT <= t_hi;
-    // S^T tiles: positions 16pt + 4 quad + i of row (lane & 15).
-    float sc[8];
-    float tmax = -INFINITY;
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -372,19 +380,34 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(qf[ks]), acc, 0,
                                                       0, 0);
       }
+      s[pt] = acc;
+    }
+  };
+  // The rest of a tile's work from its scores: mask, online softmax, P V.
+  auto softmax_pv = [&](int t0, int buf, const f32x4_t (&s)[2]) {
+    const uint16_t* vt = v_rd + buf * kVTileElems;
+    const float* st = s_lds + 2 * kKT * buf;
+    // Uniform: every live row sees every position of the tile.
+    const bool full = t0 + kKT - 1 <= p_all && t0 + kKT <= t_hi;
+    // Score e = 4 pt + i sits at position t0 + 16 pt + 4 quad + i, visible
+    // to this lane's row iff 16 pt + i <= vis.
+    const int vis = row_lim - t0 - 4 * quad;
+    float sc[8];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float v = acc[i] * scale_log2;
-        if constexpr (Q == kInt8) v *= st[16 * pt + 4 * quad + i];
-        if (!full) {
-          const int t = t0 + 16 * pt + 4 * quad + i;
-          v = (row_ok && t <= p_row && t < t_hi) ? v : -INFINITY;
-        }
+        // bf16 and FP8: unscaled here; INT8: scaled with its key scale
+        float v = s[pt][i];
+        if constexpr (Q == kInt8) v *= scale_log2 * st[16 * pt + 4 * quad + i];
+        if (!full) v = 16 * pt + i <= vis ? v : -INFINITY;
         sc[4 * pt + i] = v;
         tmax = fmaxf(tmax, v);
       }
     }
     tmax = max_across_rows16(tmax);
+    if constexpr (Q != kInt8) tmax *= scale_log2;
     if (!kLazy || __builtin_amdgcn_ballot_w64(tmax > r.m + kSlack) != 0) {  // uniform
       const float mn = fmaxf(r.m, tmax);
       const float alpha = fast_exp2(r.m - mn);
@@ -402,8 +425,14 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
     float psum = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      float p0 = fast_exp2(sc[2 * k] - mref);
-      float p1 = fast_exp2(sc[2 * k + 1] - mref);
+      float p0, p1;
+      if constexpr (Q == kInt8) {
+        p0 = fast_exp2(sc[2 * k] - mref);
+        p1 = fast_exp2(sc[2 * k + 1] - mref);
+      } else {
+        p0 = fast_exp2(fmaf(sc[2 * k], scale_log2, -mref));
+        p1 = fast_exp2(fmaf(sc[2 * k + 1], scale_log2, -mref));
+      }
       psum += p0 + p1;
       // score element e = 2k (+1) sits at tile position 16 (e / 4) + 4 quad + e % 4
       if constexpr (Q == kFp8) {
@@ -431,6 +460,16 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
       r.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfl, acc, 0, 0, 0);
     }
   };
+  // Segment end after the tile at t (see above).
+  auto segment_end = [&](int t) {
+    if constexpr (!std::is_same<Emit, NoEmit>::value) {
+      const int te = t + kKT;
+      if (te >= t_hi || te % seg == 0) {  // uniform: a segment is complete
+        emit(t, r);
+        start(r);
+      }
+    }
+  };
 
 #pragma unroll
   for (int j = 0; j < PD; ++j)
@@ -446,15 +485,11 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
       // the register buffer just staged takes the tile PD ahead, in flight
       // meanwhile
       if (t + PD * kKT < t_hi) fetch(j, t + PD * kKT);
-      compute(t, buf);
+      f32x4_t sv[2];
+      qk(buf, sv);
+      softmax_pv(t, buf, sv);
       if constexpr (lds_tiles<NW>() == 2) buf ^= 1;
-      if constexpr (!std::is_same<Emit, NoEmit>::value) {
-        const int te = t + kKT;
-        if (te >= t_hi || te % seg == 0) {  // uniform: a segment is complete
-          emit(t, r);
-          start(r);
-        }
-      }
+      segment_end(t);
     }
   }
   // the caller may reuse the LDS (another pass) right after
