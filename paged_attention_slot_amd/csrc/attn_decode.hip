@@ -79,7 +79,7 @@ struct AttnArgs {
   void* out;
   float* ws_acc;            // rows of D floats (unnormalised weighted sums)
   float2* ws_ml;            // (reference, sum) per row of ws_acc
-  int32_t* ws_base;         // balanced: prefix sums of stream tiles [N+1]
+  int32_t* ws_span;         // balanced: first and last interval of each stream [N*H_kv][2]
   int64_t block_bytes;
   int32_t row_bytes;
   int32_t max_blocks;
@@ -726,16 +726,10 @@ __device__ __forceinline__ int stream_tiles(const AttnArgs& a, int s) {
 // [floor(T*w/W), floor(T*(w+1)/W)).  With W <= T every share is non-empty.
 __device__ __forceinline__ int64_t share_lo(int64_t T, int64_t w, int64_t W) { return T * w / W; }
 
-// The share holding global tile x (0 <= x < T): the largest w with
-// floor(T*w/W) <= x, i.e. floor(((x+1)*W - 1) / T).
-__device__ __forceinline__ int share_of(int64_t x, int64_t T, int64_t W) {
-  return static_cast<int>(((x + 1) * W - 1) / T);
-}
 
 // The balanced split's intervals over the global tile order (all streams,
 // sequence by sequence, KV head by KV head): intervals 0 .. Ws-1 are the static
-// shares of [0, S), intervals Ws .. Ws+K-1 the dynamic chunks of [S, T).  Both
-// kernels derive the same cut from (T, W).
+// shares of [0, S), intervals Ws .. Ws+K-1 the dynamic chunks of [S, T).
 struct Intervals {
   int64_t T, S;
   int Ws, K;
@@ -751,9 +745,6 @@ struct Intervals {
   // First tile of interval j (0 <= j <= Ws + K; lo(Ws) = S, lo(Ws + K) = T).
   __device__ int64_t lo(int j) const {
     return j <= Ws ? share_lo(S, j, Ws) : S + share_lo(T - S, j - Ws, K);
-  }
-  __device__ int of(int64_t x) const {
-    return x < S ? share_of(x, S, Ws) : Ws + share_of(x - S, T - S, K);
   }
 };
 
@@ -795,6 +786,12 @@ __device__ __forceinline__ void run_interval(Wave<T, D, GW, P, kAppend, kStream>
     // the stream's last tile holds the new token (fused append)
     const bool app = kAppend && t0 + seg == nt && L == Lraw;
     w.run(s, kvh, h0, t0 * kTile, min((t0 + seg) * kTile, L), app ? L - 1 : -1, sub == 0);
+    // the stream's first and last intervals, for the merge
+    const int64_t ks = int64_t(s) * Hkv + kvh;
+    if (sub == 0 && w.lane == 0) {
+      if (t0 == 0) a.ws_span[2 * ks] = iv;
+      if (t0 + seg == nt) a.ws_span[2 * ks + 1] = iv;
+    }
     if (t0 == 0 && seg == nt) {
       w.write_out(s, h0);  // the whole stream in one interval
     } else {
@@ -840,8 +837,6 @@ attn_balanced_kernel(AttnArgs a) {
   }
   if (tid == 0) base[N] = total;
   __syncthreads();
-  if (blockIdx.x == 0)  // the merge kernel reads the same prefix sums
-    for (int i = tid; i <= N; i += nth) a.ws_base[i] = base[i];
 
   const int grp = wv / a.waves_per_group;
   const int sub = wv - grp * a.waves_per_group;
@@ -864,8 +859,9 @@ attn_balanced_kernel(AttnArgs a) {
 }
 
 // Balanced mode merge: one workgroup per (query head, sequence); combines the
-// pieces its stream left in consecutive intervals (nothing to do when one
-// interval held the whole stream, zeros for an empty history).
+// pieces its stream left in consecutive intervals, first to last as the
+// attention kernel recorded them (nothing to do when one interval held the
+// whole stream, zeros for an empty history).
 template <typename T, int D>
 __global__ void __launch_bounds__(kMergeThreads)
 attn_merge_balanced_kernel(AttnArgs a) {
@@ -878,12 +874,9 @@ attn_merge_balanced_kernel(AttnArgs a) {
     merge_rows<T, D>(a.ws_acc, a.ws_ml, 0, 0, 0, dst);
     return;
   }
-  const Intervals ivs(a.ws_base[a.num_seqs], a.num_groups);
-  const int64_t start = int64_t(a.ws_base[s]) + int64_t(g) * nt;
-  const int i0 = ivs.of(start);
-  const int i1 = ivs.of(start + nt - 1);
-  if (i0 == i1) return;
   const int64_t k = int64_t(s) * a.num_kv_heads + g;
+  const int i0 = a.ws_span[2 * k], i1 = a.ws_span[2 * k + 1];
+  if (i0 == i1) return;
   merge_rows<T, D>(a.ws_acc, a.ws_ml, i1 - i0 + 1, (k + i0) * G + j, G, dst);
 }
 
@@ -961,7 +954,7 @@ struct Plan {
   // balanced mode
   int groups_per_block;
   int64_t rows;  // workspace rows of D floats
-  size_t ws_bytes, ws_ml_off, ws_base_off;
+  size_t ws_bytes, ws_ml_off, ws_span_off;
   int max_chunks;  // balanced: upper bound of the dynamic chunks
 };
 
@@ -1032,11 +1025,11 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
     if (pl->runs.runs > 1) {
       pl->rows = int64_t(num_seqs) * num_q_heads * pl->runs.runs;
       pl->ws_ml_off = size_t(pl->rows) * g->head_dim * sizeof(float);
-      pl->ws_base_off = 0;
+      pl->ws_span_off = 0;
       pl->ws_bytes = pl->ws_ml_off + size_t(pl->rows) * sizeof(float2);
     } else {
       pl->rows = 0;
-      pl->ws_ml_off = pl->ws_base_off = 0;
+      pl->ws_ml_off = pl->ws_span_off = 0;
       pl->ws_bytes = 0;
     }
     return PKV_OK;
@@ -1054,8 +1047,8 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
     pl->part_tokens = 0;
     const size_t acc = size_t(pl->rows) * g->head_dim * sizeof(float);
     pl->ws_ml_off = acc;
-    pl->ws_base_off = acc + size_t(pl->rows) * sizeof(float2);
-    pl->ws_bytes = pl->ws_base_off + round_up(int64_t(num_seqs + 1) * 4, 256);
+    pl->ws_span_off = acc + size_t(pl->rows) * sizeof(float2);
+    pl->ws_bytes = pl->ws_span_off + round_up(int64_t(num_seqs) * g->num_kv_heads * 8, 256);
     // dynamic chunks: at most kMaxChunks, at least kMinChunkTiles tiles each,
     // out of kDynamicPerMille of all tiles (bounded here by max_seq_len)
     const int64_t tmax = int64_t(num_seqs) * g->num_kv_heads * stream_tiles_max;
@@ -1079,11 +1072,11 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
   if (pl->num_parts > 1) {
     pl->rows = int64_t(num_seqs) * num_q_heads * pl->num_parts;
     pl->ws_ml_off = size_t(pl->rows) * g->head_dim * sizeof(float);
-    pl->ws_base_off = 0;
+    pl->ws_span_off = 0;
     pl->ws_bytes = pl->ws_ml_off + size_t(pl->rows) * sizeof(float2);
   } else {
     pl->rows = 0;
-    pl->ws_ml_off = pl->ws_base_off = 0;
+    pl->ws_ml_off = pl->ws_span_off = 0;
     pl->ws_bytes = 0;
   }
   return PKV_OK;
@@ -1388,8 +1381,8 @@ pkv_status attention_impl(const char* who, int32_t phases, const void* q, const 
   char* ws = static_cast<char*>(workspace);
   a.ws_acc = pl.ws_bytes ? reinterpret_cast<float*>(ws) : nullptr;
   a.ws_ml = pl.ws_bytes ? reinterpret_cast<float2*>(ws + pl.ws_ml_off) : nullptr;
-  a.ws_base = (pl.ws_bytes && pl.mode == kBalancedMode)
-                  ? reinterpret_cast<int32_t*>(ws + pl.ws_base_off)
+  a.ws_span = (pl.ws_bytes && pl.mode == kBalancedMode)
+                  ? reinterpret_cast<int32_t*>(ws + pl.ws_span_off)
                   : nullptr;
   a.row_bytes = geom->num_kv_heads * geom->head_dim * es;
   a.block_bytes = int64_t(geom->block_size) * a.row_bytes;
