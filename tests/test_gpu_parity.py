@@ -180,6 +180,36 @@ def test_matrix_route_equal_shares(pt, monkeypatch):
     assert_gate(o, ref, "bf16", f"equal shares, one empty history, pt={pt}")
 
 
+@pytest.mark.parametrize("Hq,pt,shared", [(16, None, False), (16, None, True), (32, 64, False),
+                                          (64, None, False), (64, 32, False)],
+                         ids=["balanced", "balanced-cacheable", "partitions", "matrix",
+                              "matrix-shares"])
+def test_split_phases_match_one_call(Hq, pt, shared, monkeypatch):
+    """pkv_attention_decode_phase: the per-partition phase, then the merge
+    phase in a call of its own (which reads what the first left in the
+    workspace: pieces, and on the balanced split each stream's first and last
+    interval), gives the bits of one call with both phases; a second merge
+    call gives them again."""
+    monkeypatch.delenv("PKV_ATTN_MODE", raising=False)
+    monkeypatch.delenv("PKV_ATTN_PARTS_PER_WG", raising=False)
+    wl = independent_workload([1, 15, 16, 17, 64, 200, 333, 1500, 2047, 3000], num_q_heads=Hq,
+                              num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16",
+                              seed=60 + Hq + (pt or 0))
+    step, _ = run_both(wl, partition_tokens=pt, attention=False)
+    step.kv_shared = shared
+    say(f"  split {step.split} kv_shared={shared}")
+    one = host_bits(step.attention(out=torch.empty_like(step.q)))
+    out = torch.empty_like(step.q)
+    step.attention(out=out, phases=1)
+    step.attention(out=out, phases=2)
+    first = host_bits(out)
+    step.attention(out=out, phases=2)
+    again = host_bits(out)
+    torch.cuda.synchronize()
+    assert np.array_equal(one, first), "phase 1 then phase 2 differs from one call"
+    assert np.array_equal(one, again), "a second merge call differs"
+
+
 @pytest.mark.parametrize("pt", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("dtype,B", [("bf16", 16), ("f32", 16), ("bf16", 32)])
 def test_split_kv_matches_oracle_and_unsplit(pt, dtype, B):
