@@ -7,9 +7,12 @@ block-table GQA decode attention through libpkv.
     python bench.py --path swap [--config NAME]
     python bench.py --path shared [--config NAME]
 
-A step is one pass of the device hot path over one batch: pkv_copy_blocks
-(when the batch has copy-on-write pairs), pkv_write of one new token per
-sequence, then pkv_attention_decode (partition kernel, then the split-KV merge).
+A step is one pass of the device hot path over one batch (by default the
+llama3-8b-layer batch: 256 sequences of 512-8192 tokens, 32 query / 8 KV heads,
+head_dim 128, bf16, block size 16): pkv_copy_blocks (when the batch has
+copy-on-write pairs), then the append of one new token per sequence and the
+decode attention (pkv_attention_decode_append; ``--unfused``: pkv_write, then
+pkv_attention_decode), with the split-KV merge.
 Inputs are resident in HBM before the timed region.  ``--layers`` pool pairs
 with identical block tables are cycled, one per step, so that consecutive steps
 read different memory (as a model's layers do) and no step is served from the
@@ -534,8 +537,8 @@ def main() -> int:
                     help="decode step (default), multi-token query attention, block swap, or "
                          "shared-prefix decode attention")
     ap.add_argument("--config", default=None,
-                    help="workload (default: qwen3-0.6b-layer; shared-prefix-cow for --path "
-                         "shared)")
+                    help="workload (default: llama3-8b-layer, the largest configuration of "
+                         "the decode step on one GPU; shared-prefix-cow for --path shared)")
     ap.add_argument("--query-tokens", type=int, default=4,
                     help="--path multi: new query tokens per sequence")
     ap.add_argument("--layers", type=int, default=4)
@@ -572,7 +575,7 @@ def main() -> int:
         print(json.dumps({"stream_read_gbps": stream_read_gbps(), "bytes": 4 << 30}), flush=True)
         return 0
     if args.config is None:
-        args.config = "shared-prefix-cow" if args.path == "shared" else "qwen3-0.6b-layer"
+        args.config = "shared-prefix-cow" if args.path == "shared" else "llama3-8b-layer"
     if args.path == "multi":
         return bench_multi(args)
     if args.path == "shared":

@@ -15,8 +15,9 @@ gives a zero output (a reading; the pages are silent).
 Functions:
   attention_decode           the plain definition above (gather, then softmax)
   attention_contiguous       the same over K/V stacked in token order, no paging
-  attention_blockwise_online the block-by-block running max / running sum form
-                             of [KVM §19.2.3] and Fig. 19-5
+  attention_blockwise_online block by block: each block's own (max, sum,
+                             weighted sum) folded into a running state, the
+                             online-softmax form of [KVM §19.2.3], Fig. 19-5
   attention_split            split-KV: per-partition (max, sum, weighted sum)
                              merged by log-sum-exp rescaling
   attention_multi            several new query tokens per sequence (a prefill
@@ -97,39 +98,40 @@ def attention_contiguous(q, k_seqs, v_seqs, scale):
 
 
 def attention_blockwise_online(q_s, k_pool, v_pool, table, length, scale):
-    """One sequence, walked block by block as in [KVM §19.2.3] (Fig. 19-5):
-    for every block, the scores of its filled slots, the block max, a new
-    running max, rescaling of the running sum and running output by
-    exp(old max - new max), then adding exp(score - new max) and the
-    correspondingly weighted V rows; divide by the running sum at the end.
+    """One sequence, one physical block at a time (the way [KVM §19.2.3] and
+    Fig. 19-5 walk a request): the filled slots of each block give that
+    block's own state (``partition_state``), and a running state absorbs it by
+    ``fold_states``, so no score row longer than a block is ever held.  The
+    result is the running state's weighted sum over its sum.
     q_s [H_q, D] -> [H_q, D] float64."""
     Hq, D = q_s.shape
     B, Hkv = k_pool.shape[1], k_pool.shape[2]
-    G = Hq // Hkv
+    L = int(length)
+    out = np.zeros((Hq, D))
+    if L == 0:
+        return out
     qf = to_f64(q_s)
-    run_max = np.full(Hq, -np.inf)
-    run_sum = np.zeros(Hq)
-    run_out = np.zeros((Hq, D))
-    remaining = int(length)
-    for phys in table:
-        if remaining <= 0:
-            break
-        valid = min(B, remaining)
-        remaining -= valid
-        Kb = to_f64(k_pool[phys, :valid])                 # [valid, H_kv, D]
-        Vb = to_f64(v_pool[phys, :valid])
-        Kq = Kb[:, np.arange(Hq) // G, :]                 # [valid, H_q, D]
-        Vq = Vb[:, np.arange(Hq) // G, :]
-        scores = scale * np.einsum("hd,vhd->hv", qf, Kq)  # [H_q, valid]
-        new_max = np.maximum(run_max, scores.max(axis=1))
-        alpha = np.exp(run_max - new_max)
-        w = np.exp(scores - new_max[:, None])
-        run_sum = run_sum * alpha + w.sum(axis=1)
-        run_out = run_out * alpha[:, None] + np.einsum("hv,vhd->hd", w, Vq)
-        run_max = new_max
-    if length == 0:
-        return np.zeros((Hq, D))
-    return run_out / run_sum[:, None]
+    nblk = -(-L // B)
+    for g in range(Hkv):
+        hs = list(_heads_of_group(Hq, Hkv, g))
+        state = None
+        for j in range(nblk):
+            filled = min(B, L - j * B)          # slots of block j inside the history
+            blk = int(table[j])
+            piece = partition_state(qf[hs], to_f64(k_pool[blk, :filled, g]),
+                                    to_f64(v_pool[blk, :filled, g]), scale)
+            state = piece if state is None else fold_states(state, piece)
+        m, l, acc = state
+        out[hs] = acc / l[:, None]
+    return out
+
+
+def fold_states(a, b):
+    """Two (max, sum, weighted sum) states of disjoint position sets -> the
+    state of their union: both are rescaled to the larger max, exp(m - M)."""
+    M = np.maximum(a[0], b[0])
+    wa, wb = np.exp(a[0] - M), np.exp(b[0] - M)
+    return M, wa * a[1] + wb * b[1], wa[:, None] * a[2] + wb[:, None] * b[2]
 
 
 def partition_state(q_rows, K, V, scale):

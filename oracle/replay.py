@@ -23,8 +23,14 @@ class OracleState:
         self.wl = wl
         dt = np.float32 if wl.dtype == "f32" else np.uint16
         shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim)
-        self.k_pool = np.zeros(shape, dtype=dt)
-        self.v_pool = np.zeros(shape, dtype=dt)
+        if wl.pool_init is not None:
+            # slots never written keep these bits ([ENG §3.2]: nothing clears
+            # a block)
+            self.k_pool = np.array(wl.pool_init[0], dtype=dt, copy=True).reshape(shape)
+            self.v_pool = np.array(wl.pool_init[1], dtype=dt, copy=True).reshape(shape)
+        else:
+            self.k_pool = np.zeros(shape, dtype=dt)
+            self.v_pool = np.zeros(shape, dtype=dt)
         hshape = (wl.num_host_blocks,) + shape[1:]
         self.k_host = np.zeros(hshape, dtype=dt)
         self.v_host = np.zeros(hshape, dtype=dt)
@@ -76,6 +82,10 @@ class OracleState:
                 pairs = bm.swap_in(list(op[1]))
                 self._swap(pairs, to_host=False)
                 self.swaps.append((kind, pairs))
+            elif kind == "free":
+                bm.free_seq(op[1])
+                if self.keep_values:
+                    del self.hist_k[op[1]], self.hist_v[op[1]]
             else:
                 raise ValueError(f"unknown op {kind}")
             bm.check()

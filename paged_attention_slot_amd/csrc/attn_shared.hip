@@ -129,19 +129,30 @@ attn_prefix_kernel(SharedArgs a) {
   const int s = first + j0 + (row_ok ? jl : 0);
   const int L = clamp_len(a.seq_lens[s], a.len_cap);
   const int64_t qh = int64_t(s) * a.num_q_heads + g * G + hh;
-  // The prefix is read through the group's first member's table.
+  // Positions every member of the block sees: up to the shortest one's last;
+  // positions some member sees: up to the longest one's last (members'
+  // lengths strided over the lanes, then a wave minimum and maximum).
+  int lmin = a.len_cap, lmax = 0;
+  for (int m = lane; m < jn; m += 64) {
+    const int lm = clamp_len(a.seq_lens[first + j0 + m], a.len_cap);
+    lmin = min(lmin, lm);
+    lmax = max(lmax, lm);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    lmin = min(lmin, __shfl_xor(lmin, off));
+    lmax = max(lmax, __shfl_xor(lmax, off));
+  }
+  // The prefix is read through the group's first member's table.  A shared
+  // last block may be only partly written when no member has appended since
+  // the fork: the History stops at the longest member, so slots past it load
+  // as zeros instead of whatever bits they hold (a masked score with a NaN or
+  // infinite V row would still put 0 * NaN into the products).
   const pkv::mfma::History hist{a.k_cache,      a.v_cache,     a.block_tables + int64_t(first) * a.max_blocks,
-                                P,              g,             a.block_elems,
+                                min(P, lmax),   g,             a.block_elems,
                                 a.row_elems,    a.num_blocks,  a.block_shift,
                                 a.num_kv_heads, a.v_scale,     a.k_scales,
                                 a.v_scales};
-  // Positions every member of the block sees: up to the shortest one's last
-  // (members' lengths strided over the lanes, then a wave minimum).
-  int lmin = a.len_cap;
-  for (int m = lane; m < jn; m += 64)
-    lmin = min(lmin, clamp_len(a.seq_lens[first + j0 + m], a.len_cap));
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) lmin = min(lmin, __shfl_xor(lmin, off));
   pkv::mfma::RowAcc<D> r;
   pkv::mfma::start(r);
   pkv::mfma::attend<D, NW, (NW >= 2 ? 2 : 1), Q>(hist, t_lo, t_hi, a.q + qh * D, row_ok, L - 1,

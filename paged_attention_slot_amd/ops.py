@@ -33,6 +33,28 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _scratch(nbytes: int, dev, stream, phases: int = 3) -> torch.Tensor:
+    """A workspace for one call, when the caller passes none.  A call of one
+    phase alone needs the caller's workspace (the other phase reads what this
+    one leaves there).  On a side stream the buffer is recorded on it, so the
+    caching allocator does not hand it out again before the call's kernels
+    have finished with it."""
+    if (phases & 3) != 3:
+        raise ValueError("a single-phase call needs the caller's workspace "
+                         "(the two phases communicate through it)")
+    t = torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=dev)
+    if stream is not None:
+        t.record_stream(stream)
+    return t
+
+
+def _out_like(q: torch.Tensor, stream) -> torch.Tensor:
+    out = torch.empty_like(q)
+    if stream is not None:
+        out.record_stream(stream)
+    return out
+
+
 def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
@@ -163,14 +185,14 @@ def _attention(q, k_cache, v_cache, block_tables, seq_lens, scale, out, max_seq_
     if max_seq_len is None:
         max_seq_len = max_blocks * g.block_size
     if out is None:
-        out = torch.empty_like(q)
+        out = _out_like(q, stream)
     else:
         _need(out, "out", q.dtype, dev)
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
     need = workspace_bytes(N, Hq, max_seq_len, k_cache, partition_tokens)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _scratch(need, dev, stream, phases)
     if workspace is not None:
         _need(workspace, "workspace", None, dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -272,7 +294,7 @@ def attention_multi(q, q_offsets, k_cache, v_cache, block_tables, seq_lens, scal
     if max_seq_len is None:
         max_seq_len = max_blocks * g.block_size
     if out is None:
-        out = torch.empty_like(q)
+        out = _out_like(q, stream)
     else:
         _need(out, "out", torch.bfloat16, dev)
         if out.shape != q.shape:
@@ -283,7 +305,7 @@ def attention_multi(q, q_offsets, k_cache, v_cache, block_tables, seq_lens, scal
     if need == ctypes.c_size_t(-1).value:
         check(1, "pkv_attention_multi_workspace_bytes")
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _scratch(need, dev, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if quant:
         sc = _scales(k_cache, k_scale, v_scale, k_scales, v_scales)
@@ -401,11 +423,11 @@ def attention_decode_shared(q, k_cache, v_cache, block_tables, seq_lens, scale, 
     if max_seq_len is None:
         max_seq_len = max_blocks * g.block_size
     if out is None:
-        out = torch.empty_like(q)
+        out = _out_like(q, stream)
     need = shared_workspace_bytes(N, Hq, ng, max_group_size, max_prefix_len, max_suffix_len,
                                   max_seq_len, k_cache)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        workspace = _scratch(need, dev, stream)
     ws_bytes = workspace.numel() * workspace.element_size()
     if quant:
         sc = _scales(k_cache, k_scale, v_scale, k_scales, v_scales)

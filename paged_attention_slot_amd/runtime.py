@@ -116,6 +116,12 @@ class DecodeStep:
                 events.append(("swap_out", bm.swap_out(list(op[1]))))
             elif kind == "swap_in":
                 events.append(("swap_in", bm.swap_in(list(op[1]))))
+            elif kind == "free":
+                bm.free_seq(op[1])
+                # the freed slots may be written again by later appends:
+                # those writes must not join the same launch as earlier ones
+                # (one pkv_write takes distinct slots)
+                events.append(("free", None))
             else:
                 raise ValueError(f"unknown op {kind}")
         assert cur == wl.ctx_tokens
@@ -139,8 +145,13 @@ class DecodeStep:
         dev = self.device
         shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim)
         cdt = _CACHE_DTYPES[self.kv_dtype]
-        self.k_caches = [torch.zeros(shape, dtype=cdt, device=dev)]
-        self.v_caches = [torch.zeros(shape, dtype=cdt, device=dev)]
+        if wl.pool_init is not None and not self.quant:
+            # the bits never-written slots hold (stale data of earlier owners)
+            self.k_caches = [to_device(wl.pool_init[0], wl.dtype, dev)]
+            self.v_caches = [to_device(wl.pool_init[1], wl.dtype, dev)]
+        else:
+            self.k_caches = [torch.zeros(shape, dtype=cdt, device=dev)]
+            self.v_caches = [torch.zeros(shape, dtype=cdt, device=dev)]
         sshape = (wl.num_blocks * wl.block_size, wl.num_kv_heads)
         if self.kv_dtype == "int8":
             self.k_scale_pools = [torch.zeros(sshape, dtype=torch.float32, device=dev)]
@@ -156,6 +167,8 @@ class DecodeStep:
             for ev in events:
                 if ev[0] == "write":
                     self._write(ck[ev[1]:ev[2]], cv[ev[1]:ev[2]], cs[ev[1]:ev[2]], 0)
+                elif ev[0] == "free":
+                    continue
                 else:
                     self._trace_event(ev[0], ev[1])
             if keep_context:

@@ -210,11 +210,12 @@ def test_split_phases_match_one_call(Hq, pt, shared, monkeypatch):
     assert np.array_equal(one, again), "a second merge call differs"
 
 
-@pytest.mark.parametrize("pt", [16, 32, 64, 128, 256])
-@pytest.mark.parametrize("dtype,B", [("bf16", 16), ("f32", 16), ("bf16", 32)])
+SPLITS = [(pt, dtype, B) for pt in (16, 32, 64, 128, 256)
+          for dtype, B in (("bf16", 16), ("f32", 16), ("bf16", 32)) if pt % B == 0]
+
+
+@pytest.mark.parametrize("pt,dtype,B", SPLITS, ids=lambda v: str(v))
 def test_split_kv_matches_oracle_and_unsplit(pt, dtype, B):
-    if pt % B:
-        pytest.skip("partition must be a multiple of the block size")
     wl = independent_workload([1, 15, 16, 17, 64, 200, 333, 513], num_q_heads=16,
                               num_kv_heads=4, head_dim=128, block_size=B, dtype=dtype, seed=7)
     step, ost = run_both(wl, partition_tokens=pt)
@@ -272,43 +273,67 @@ def test_copy_on_write_family_small():
 
 # -- full-size configurations, in the bench's launch configuration -----------
 
-def sampled_pairs(wl, rng, n_seqs, heads_per_seq):
-    seqs = np.sort(rng.choice(wl.num_seqs, size=min(n_seqs, wl.num_seqs), replace=False))
-    heads = {int(s): np.sort(rng.choice(wl.num_q_heads, size=heads_per_seq, replace=False))
-             for s in seqs}
-    return seqs, heads
+_ORACLE = {}
 
 
-@pytest.mark.parametrize("name", ["tiny", "qwen3-0.6b-layer", "shared-prefix-cow"])
-def test_config_full(name):
-    wl = config_workload(name)
-    step, ost = run_both(wl)
+def oracle_of(name):
+    """The oracle's pools, tables and attention of a configuration, computed
+    once for the two forms of its step (kept for one configuration at a
+    time)."""
+    if name not in _ORACLE:
+        _ORACLE.clear()
+        wl = config_workload(name)
+        ost = run_step(wl, keep_values=False)
+        ref = oracle_attention(wl.q, ost.k_pool, ost.v_pool, ost.block_tables, ost.seq_lens,
+                               wl.scale)
+        _ORACLE[name] = (wl, ost, ref)
+    return _ORACLE[name]
+
+
+CONFIGS = ["tiny", "qwen3-0.6b-layer", "llama3-8b-layer", "shared-prefix-cow",
+           "llama3.1-70b-longctx"]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["write-then-attention", "append-folded"])
+@pytest.mark.parametrize("name", CONFIGS)
+def test_config_full(name, fused):
+    """Every output element of every configuration against the oracle, pools
+    bit-exact.  ``fused``: the step as the bench times it (copy, then
+    pkv_attention_decode_append: the append inside the attention or its
+    row-copy kernel), else copy -> write -> attention."""
+    from paged_attention_slot_amd.runtime import DecodeStep
+    wl, ost, ref = oracle_of(name)
+    say(f"  case {name}: N={wl.num_seqs} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} "
+        f"D={wl.head_dim} B={wl.block_size} {wl.dtype} maxlen={wl.max_seq_len} fused={fused}")
+    step = DecodeStep(wl)
+    assert np.array_equal(step.slot_mapping_h, ost.slot_mapping)
+    assert np.array_equal(step.cow_pairs_h.reshape(-1, 2), ost.cow_pairs.reshape(-1, 2))
+    assert np.array_equal(step.block_tables_h, ost.block_tables)
+    say(f"  split {step.split} kv_shared={step.kv_shared} "
+        f"folded={step.append_folded if fused else None}")
+    step.step(fused=fused)
+    torch.cuda.synchronize()
     check_pools(step, ost)
-    ref = oracle_attention(wl.q, ost.k_pool, ost.v_pool, ost.block_tables, ost.seq_lens,
-                           wl.scale)
     out = gpu_out(step)
+    assert np.isfinite(out).all()
     r = assert_gate(out, ref, wl.dtype, name)
     say("  gate", r)
     if name == "tiny":
         # the page's self-check bound, fp32 end to end
         assert r["max_abs"] < 1e-5
+    del step
+    torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name", ["llama3-8b-layer", "llama3.1-70b-longctx"])
-def test_config_full_sampled(name):
-    wl = config_workload(name)
-    step, ost = run_both(wl)
-    check_pools(step, ost)
-    out = gpu_out(step)
-    rng = np.random.default_rng(17)
-    seqs, heads = sampled_pairs(wl, rng, 12 if wl.num_seqs > 4 else 4, 8)
-    ref = oracle_attention(wl.q, ost.k_pool, ost.v_pool, ost.block_tables, ost.seq_lens,
-                           wl.scale, seqs=[int(s) for s in seqs])
-    for s in seqs:
-        hs = heads[int(s)]
-        r = assert_gate(out[s, hs], ref[s, hs], wl.dtype, f"{name} seq {s}")
-    say("  last gate", r)
-    assert np.isfinite(out).all()
+def test_long_context_config_partitions_against_oracle_split():
+    """The long-context configuration at its 512-token partitions against the
+    oracle's split attention with the same partitions (the log-sum-exp merge
+    of 256 pieces per history), every element."""
+    wl, ost, _ = oracle_of("llama3.1-70b-longctx")
+    step, _ = run_both(wl)
+    ref = oracle_split(wl.q, ost.k_pool, ost.v_pool, ost.block_tables, ost.seq_lens, wl.scale,
+                       512)
+    say("  gate", assert_gate(gpu_out(step), ref, "bf16", "long context, 512-token partitions"))
 
 
 # -- the two work distributions ------------------------------------------------

@@ -214,6 +214,8 @@ class Workload:
       ("swap_out", (seq, ...))           the sequences are paused together and
                                          their KV cache moves to the host pool
       ("swap_in", (seq, ...))            swapped-out sequences come back
+      ("free", seq)                      the sequence ends; its blocks go back to
+                                         the free list with their data in place
     The decode step then appends one token to every sequence of
     ``decode_seqs`` in that order (K/V rows ``new_k``/``new_v``), and every
     sequence's query row ``q[i]`` attends its whole history including that
@@ -221,6 +223,9 @@ class Workload:
     append.  ``free_order`` is the initial free list of physical block ids;
     blocks are taken from its end.  ``num_host_blocks`` and
     ``host_free_order`` describe the host pool the swaps use (none if 0).
+    ``pool_init`` (None: zeros) holds the bits both pools start with, as
+    (k_init, v_init) arrays of the pool's shape and stored type: the content
+    of slots never written in the trace.
     """
     name: str
     num_q_heads: int
@@ -245,6 +250,7 @@ class Workload:
     meta: dict = field(default_factory=dict)
     num_host_blocks: int = 0
     host_free_order: np.ndarray | None = None
+    pool_init: tuple | None = None
 
     @property
     def elem_bytes(self) -> int:
@@ -466,6 +472,99 @@ def preemption_config_workload(name: str, swap_fraction: float = 0.25, grow_toke
                                block_size=c.block_size, dtype=c.dtype, seed=seed,
                                partition_tokens=c.partition_tokens, name=f"{c.name}-preempt",
                                values=values)
+
+
+# Non-finite and extreme bit patterns of each stored type: quiet NaN, +Inf,
+# -Inf, the largest finite value and its negation.
+_STALE_BITS = {
+    "bf16": np.array([0x7FC0, 0x7F80, 0xFF80, 0x7F7F, 0xFF7F], dtype=np.uint16),
+    "f32": np.array([0x7FC00000, 0x7F800000, 0xFF800000, 0x7F7FFFFF, 0xFF7FFFFF],
+                    dtype=np.uint32),
+}
+
+
+def stale_pool_bits(shape, dtype: str, seed: int):
+    """Pool contents before any write ([ENG §3.2] and the release section of
+    [SLOT]: freed blocks keep whatever they held): every element one of
+    NaN, +Inf, -Inf, +max, -max, drawn uniformly from SeedSequence(seed).
+    Returns (k_init, v_init) in the stored type (uint16 bf16 bits or
+    float32)."""
+    kids = np.random.SeedSequence(seed).spawn(2)
+    pats = _STALE_BITS[dtype]
+    out = []
+    for kid in kids:
+        g = np.random.Generator(np.random.PCG64(kid))
+        bits = pats[g.integers(0, pats.size, size=int(np.prod(shape)))].reshape(shape)
+        out.append(bits if dtype == "bf16" else bits.view(np.float32))
+    return tuple(out)
+
+
+def with_stale_pools(wl: Workload, seed: int | None = None) -> Workload:
+    """The same workload with both pools starting from stale non-finite bits
+    (``stale_pool_bits``, seed defaults to the workload's + 2000)."""
+    shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim)
+    wl.pool_init = stale_pool_bits(shape, wl.dtype, (wl.seed + 2000) if seed is None else seed)
+    wl.name = f"{wl.name}+stale"
+    return wl
+
+
+def churn_workload(first_lens, freed, second_lens, *, num_q_heads, num_kv_heads, head_dim,
+                   block_size, dtype, seed, forks=(), name="churn", values=True) -> Workload:
+    """A pool that has been used before.  Sequences 0..n1-1 write
+    ``first_lens`` context tokens; the sequences in ``freed`` end (their
+    blocks return to the free list, data left in place); sequences n1.. then
+    write ``second_lens`` tokens each, taking the freed blocks first (most
+    recently freed first); each sequence of ``forks`` (live ones, in order)
+    forks one child (ids after all others), so the child shares its parent's
+    partly filled last block; the decode step appends one token to every live
+    sequence in ascending id.  The pool holds the blocks of the first round
+    plus 10 %, or the peak need if that is larger."""
+    first = np.asarray(first_lens, dtype=np.int64)
+    second = np.asarray(second_lens, dtype=np.int64)
+    n1, n2 = first.size, second.size
+    freed = sorted(int(s) for s in freed)
+    forks = [int(p) for p in forks]
+    kids = np.random.SeedSequence(seed).spawn(8)
+    ops = []
+    for s in range(n1):
+        ops.append(("add", s))
+        if first[s]:
+            ops.append(("append", s, int(first[s])))
+    for s in freed:
+        ops.append(("free", s))
+    for i in range(n2):
+        s = n1 + i
+        ops.append(("add", s))
+        if second[i]:
+            ops.append(("append", s, int(second[i])))
+    live = [s for s in range(n1) if s not in freed] + list(range(n1, n1 + n2))
+    length = {s: int(first[s]) for s in range(n1)}
+    length.update({n1 + i: int(second[i]) for i in range(n2)})
+    nxt = n1 + n2
+    for p in forks:
+        if p not in live:
+            raise ValueError("only a live sequence can fork")
+        ops.append(("fork", p, nxt))
+        length[nxt] = length[p]
+        live.append(nxt)
+        nxt += 1
+    lens = np.array([length[s] + 1 for s in live], dtype=np.int64)
+    # peak need: the first round, and the end state with a private copy for
+    # every fork (copy-on-write at the decode append)
+    need_first = int(np.sum(_ceil_div(first, block_size)))
+    need_end = int(np.sum(_ceil_div(lens, block_size)))
+    nb = max(_slack_pool(need_first), _slack_pool(need_end))
+    perm = np.random.Generator(np.random.PCG64(kids[_S_PERM])).permutation(nb).astype(np.int32)
+    n_ctx = int(np.sum(first) + np.sum(second))
+    q, ck, cv, nk, nv = _draw_values(kids, len(live), n_ctx, num_q_heads, num_kv_heads,
+                                     head_dim, dtype, values)
+    return Workload(name=name, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                    head_dim=head_dim, block_size=block_size, dtype=dtype, num_blocks=nb,
+                    free_order=perm, ops=ops, ctx_tokens=n_ctx,
+                    decode_seqs=np.asarray(live, dtype=np.int64), seq_lens=lens.astype(np.int32),
+                    q=q, ctx_k=ck, ctx_v=cv, new_k=nk, new_v=nv,
+                    scale=1.0 / math.sqrt(head_dim), seed=seed,
+                    meta={"freed": freed, "forks": forks})
 
 
 def multi_queries(wl: Workload, n: int):
