@@ -117,6 +117,7 @@ struct AttnArgs {
   void* k_dst;   // the pools again, writable (the appended rows' destination)
   void* v_dst;
   int32_t stream_kv;  // 1: non-temporal K/V loads; 0: cacheable (shared blocks)
+  int32_t merge_lanes;  // balanced merge: piece lanes per (head, column)
 };
 
 // One-byte cache element types ([KVM §19.2.4], [PFX] "KV Cache 量化"): OCP e4m3
@@ -858,26 +859,120 @@ attn_balanced_kernel(AttnArgs a) {
   run_interval(w, a, base, ivs.lo(iv), ivs.lo(iv + 1), iv, sub);
 }
 
-// Balanced mode merge: one workgroup per (query head, sequence); combines the
-// pieces its stream left in consecutive intervals, first to last as the
-// attention kernel recorded them (nothing to do when one interval held the
-// whole stream, zeros for an empty history).
+// Balanced mode merge: one workgroup per (stream, block of its query heads).
+// Its threads are (piece lane pp, head, float4 column): after one round trip
+// for the length and the stream's first and last interval (as the attention
+// kernel recorded them), piece lane pp folds pieces pp, pp + P, ... of its
+// head's rows, issuing the loads of kMergeBatch of them at once, so up to
+// P * kMergeBatch pieces take one more round trip; the P partial states then
+// meet in LDS and are combined in a fixed order.  Nothing to do when one
+// interval held the whole stream (the attention kernel wrote the rows); zeros
+// for an empty history.
+constexpr int kMergeBalancedThreads = 256;
+constexpr int kMergeBatch = 8;
+
+// Heads of a group per merge workgroup, and workgroups per stream.
+__host__ __device__ constexpr int merge_heads_per_block(int G, int D) {
+  return G < kMergeBalancedThreads / (D / 4) ? G : kMergeBalancedThreads / (D / 4);
+}
+
+// grid = (ceil(G / heads per block), num_seqs * H_kv)
 template <typename T, int D>
-__global__ void __launch_bounds__(kMergeThreads)
+__global__ void __launch_bounds__(kMergeBalancedThreads)
+__attribute__((amdgpu_waves_per_eu(1, 4)))  // registers for a whole batch in flight
 attn_merge_balanced_kernel(AttnArgs a) {
-  const int h = blockIdx.x, s = blockIdx.y;
+  constexpr int kQ = D / 4;  // float4 columns per row
+  __shared__ float part[kMergeBalancedThreads][6];  // (reference, sum, 4 columns)
   const int G = a.group;
-  const int g = h / G, j = h - g * G;
-  const int nt = stream_tiles(a, s);
-  char* dst = static_cast<char*>(a.out) + ((int64_t(s) * a.num_q_heads + h) * D) * sizeof(T);
-  if (nt == 0) {
-    merge_rows<T, D>(a.ws_acc, a.ws_ml, 0, 0, 0, dst);
+  const int HB = merge_heads_per_block(G, D);
+  const int cols = HB * kQ;
+  const int P = a.merge_lanes;  // piece lanes: blockDim.x = cols * P <= 256
+  const int tid = threadIdx.x;
+  const int col = tid % cols, pp = tid / cols;
+  const int hl = col / kQ, q = col % kQ;
+  const int j = blockIdx.x * HB + hl;  // head within the group
+  const int64_t k = blockIdx.y;        // stream: s * H_kv + g
+  const int s = static_cast<int>(k / a.num_kv_heads);
+  const int g = static_cast<int>(k - int64_t(s) * a.num_kv_heads);
+  const bool live = pp < P && j < G;
+  // the length and the record in one round trip (the record is stale, and
+  // unused, for an empty history)
+  const int Lraw = a.seq_lens[s];
+  const int2 span = reinterpret_cast<const int2*>(a.ws_span)[k];
+  asm volatile("" ::"v"(span.x), "v"(span.y));  // issued before the branch
+  const int nt = (clamp_len(Lraw, a.len_cap) + kTile - 1) / kTile;
+  char* dst = static_cast<char*>(a.out) +
+              ((int64_t(s) * a.num_q_heads + g * G + j) * D + 4 * q) * sizeof(T);
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+  float M = -INFINITY, lsum = 0.f;
+  if (nt > 0) {  // uniform over the workgroup
+    const int i0 = span.x, i1 = span.y;
+    if (i0 == i1) return;  // the attention kernel wrote these rows
+    const int n = i1 - i0 + 1;
+    // row indices fit in 32 bits (the workspace holds fewer than 2^31 / D rows)
+    const int row0 = static_cast<int>((k + i0) * G) + (j < G ? j : 0);
+    const float4* acc4 = reinterpret_cast<const float4*>(a.ws_acc) + q;
+    for (int p0 = pp; live && p0 < n; p0 += P * kMergeBatch) {
+      // pieces past the last one re-read it and weigh 0
+      float2 ml[kMergeBatch];
+      float4 x[kMergeBatch];
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) {
+        const int row = row0 + min(p0 + i * P, n - 1) * G;
+        ml[i] = a.ws_ml[row];
+        x[i] = acc4[row * kQ];
+      }
+      float Mn = M;
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) Mn = fmaxf(Mn, ml[i].x);
+      const float al = M == -INFINITY ? 0.f : pkv::fast_exp2(M - Mn);
+      lsum *= al;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] *= al;
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) {
+        const float wgt = p0 + i * P < n ? pkv::fast_exp2(ml[i].x - Mn) : 0.f;
+        lsum = fmaf(wgt, ml[i].y, lsum);
+        o[0] = fmaf(wgt, x[i].x, o[0]);
+        o[1] = fmaf(wgt, x[i].y, o[1]);
+        o[2] = fmaf(wgt, x[i].z, o[2]);
+        o[3] = fmaf(wgt, x[i].w, o[3]);
+      }
+      M = Mn;
+    }
+    if (P > 1) {
+      part[tid][0] = M;
+      part[tid][1] = lsum;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part[tid][2 + e] = o[e];
+      __syncthreads();
+      if (pp != 0) return;
+      // lane 0's state rescaled with the others, lanes in order
+      float Mt = M;
+      for (int r = 1; r < P; ++r) Mt = fmaxf(Mt, part[r * cols + col][0]);
+      const float w0 = M == -INFINITY ? 0.f : pkv::fast_exp2(M - Mt);
+      lsum *= w0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] *= w0;
+      for (int r = 1; r < P; ++r) {
+        const float* pr = part[r * cols + col];
+        const float wr = pr[0] == -INFINITY ? 0.f : pkv::fast_exp2(pr[0] - Mt);
+        lsum = fmaf(wr, pr[1], lsum);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = fmaf(wr, pr[2 + e], o[e]);
+      }
+    }
+  } else if (pp != 0) {
     return;
   }
-  const int64_t k = int64_t(s) * a.num_kv_heads + g;
-  const int i0 = a.ws_span[2 * k], i1 = a.ws_span[2 * k + 1];
-  if (i0 == i1) return;
-  merge_rows<T, D>(a.ws_acc, a.ws_ml, i1 - i0 + 1, (k + i0) * G + j, G, dst);
+  if (j >= G) return;
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<uint2*>(dst) =
+        make_uint2(pkv::pack_bf16x2(o[0] * inv, o[1] * inv), pkv::pack_bf16x2(o[2] * inv, o[3] * inv));
+  } else {
+    *reinterpret_cast<float4*>(dst) = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1200,8 +1295,21 @@ pkv_status dispatch_gw(int phases, const Plan& pl, AttnArgs& a, int num_seqs, in
   }
   if (phases & 2) {
     if (pl.mode == kBalancedMode) {
-      hipLaunchKernelGGL((attn_merge_balanced_kernel<OutT<T>, D>), dim3(num_q_heads, num_seqs),
-                         dim3(kMergeThreads), 0, st, a);
+      // piece lanes from the average pieces per stream (intervals plus
+      // streams over streams): about two batches' worth per lane group, so
+      // most streams take one round trip, without idle lanes on batches
+      // whose streams are cut into a few pieces only
+      const int hb = merge_heads_per_block(a.group, D);
+      const int cols = hb * (D / 4);
+      const int64_t streams = int64_t(num_seqs) * a.num_kv_heads;
+      const int64_t chunks = pl.max_chunks < a.num_groups ? pl.max_chunks : a.num_groups;
+      const int64_t avg = (a.num_groups + chunks + streams + streams - 1) / streams;
+      int lanes = 1;
+      while (lanes * kMergeBatch < 2 * avg && 2 * lanes * cols <= kMergeBalancedThreads) lanes *= 2;
+      a.merge_lanes = lanes;
+      hipLaunchKernelGGL((attn_merge_balanced_kernel<OutT<T>, D>),
+                         dim3((a.group + hb - 1) / hb, num_seqs * a.num_kv_heads),
+                         dim3(cols * lanes), 0, st, a);
     } else if (pl.num_parts > 1) {
       hipLaunchKernelGGL((attn_merge_kernel<OutT<T>, D>), dim3(num_q_heads, num_seqs),
                          dim3(kMergeThreads), 0, st, a);
