@@ -354,6 +354,29 @@ pkv_status pkv_attention_decode(const void* q, const void* k_cache, const void* 
                                 int32_t partition_tokens, void* workspace,
                                 size_t workspace_bytes, const pkv_geom* geom, void* stream);
 
+/* pkv_attention_decode_noalloc -- pkv_attention_decode (both phases) for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The workspace is a
+ * device array inside the library of 64 MiB (PKV_NOALLOC_SCRATCH_BYTES), one
+ * per GPU, held from the library's load to the end of the process; its device
+ * address is looked up on the first call on each device (with that device
+ * current).  The call allocates nothing (no hipMalloc, no allocating library
+ * routine).  Arguments as for pkv_attention_decode without workspace and
+ * workspace_bytes; bf16 and f32 pools.  Sizes whose workspace
+ * (pkv_attention_workspace_bytes) exceeds the scratch are rejected with
+ * PKV_ERR_INVALID_ARG before anything is enqueued.  Every call on one GPU
+ * shares that GPU's scratch, which keeps the last call's contents (nothing in
+ * it has to start at zero): calls that may overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+pkv_status pkv_attention_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* seq_lens, float scale, void* out,
+                                        int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t max_seq_len, int32_t partition_tokens,
+                                        const pkv_geom* geom, void* stream);
+
 /* pkv_attention_decode_phase -- the same computation in two enqueued phases,
  * for callers that time, overlap or order them separately.  phases: 1 = the
  * per-partition kernel only (writes out directly when one partition covers

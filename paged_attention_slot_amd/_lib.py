@@ -21,6 +21,7 @@ P_i64 = ctypes.POINTER(ctypes.c_int64)
 PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_NO_FREE_BLOCKS, PKV_ERR_HIP = range(5)
 PKV_F32, PKV_BF16, PKV_FP8_E4M3, PKV_INT8 = 0, 1, 2, 3
 PKV_ROUTE_PARTITIONS, PKV_ROUTE_BALANCED, PKV_ROUTE_MATRIX = 0, 1, 2
+PKV_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class PkvGeom(ctypes.Structure):
@@ -70,6 +71,9 @@ SIGNATURES = {
     "pkv_attention_decode": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_i32, c_void_p,
                                      c_float, c_void_p, c_i32, c_i32, c_i32, c_i32, c_void_p,
                                      c_size, ctypes.POINTER(PkvGeom), c_void_p]),
+    "pkv_attention_decode_noalloc": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, c_i32,
+                                             c_void_p, c_float, c_void_p, c_i32, c_i32, c_i32,
+                                             c_i32, ctypes.POINTER(PkvGeom), c_void_p]),
     "pkv_attention_decode_phase": (c_i32, [c_i32, c_void_p, c_void_p, c_void_p, c_void_p, c_i32,
                                            c_void_p, c_float, c_void_p, c_i32, c_i32, c_i32,
                                            c_i32, c_void_p, c_size, ctypes.POINTER(PkvGeom),

@@ -1635,3 +1635,75 @@ pkv_status pkv_attention_decode(const void* q, const void* k_cache, const void* 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// pkv_attention_decode_noalloc: pkv_attention_decode with its workspace in a
+// file-scope device array instead of a caller's buffer, for callers that
+// cannot allocate.  Each device holds its own copy of the array from module
+// load to process end.  In host code ``scratch`` names a host-side stand-in,
+// not device memory: the kernels get the array's device address, looked up
+// once per device with that device current.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = PKV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The device address of ``scratch`` on the current device, looked up on the
+// first call there.
+pkv_status scratch_on_current_device(const char* who, void** out) {
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev))
+    return pkv::fail(PKV_ERR_HIP, "%s: hipGetDevice failed: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return pkv::fail(PKV_ERR_UNSUPPORTED, "%s: device %d beyond the %d the scratch table holds",
+                     who, dev, kMaxScratchDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)))
+      return pkv::fail(PKV_ERR_HIP, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s",
+                       who, dev, hipGetErrorString(e));
+    if (!ptr)
+      return pkv::fail(PKV_ERR_HIP, "%s: no device address for scratch on device %d", who, dev);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_attention_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* seq_lens, float scale, void* out,
+                                        int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t max_seq_len, int32_t partition_tokens,
+                                        const pkv_geom* geom, void* stream) {
+  const char* who = "pkv_attention_decode_noalloc";
+  if (geom && pkv::is_quant(geom->dtype))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "%s: quantized pools are not taken here", who);
+  Plan pl;
+  if (pkv_status st = make_plan(num_seqs, num_q_heads, max_seq_len, max_blocks_per_seq,
+                                partition_tokens, geom, who, &pl))
+    return st;
+  if (pl.ws_bytes > kScratchBytes)
+    return pkv::fail(PKV_ERR_INVALID_ARG,
+                     "%s: these sizes need %zu bytes of workspace, beyond the %zu bytes of the "
+                     "library's scratch (use pkv_attention_decode with a workspace)",
+                     who, pl.ws_bytes, kScratchBytes);
+  void* ws = nullptr;
+  if (pl.ws_bytes > 0 && num_seqs > 0)
+    if (pkv_status st = scratch_on_current_device(who, &ws)) return st;
+  return attention_impl(who, 3, q, k_cache, v_cache, nullptr, block_tables, max_blocks_per_seq,
+                        seq_lens, scale, out, num_seqs, num_q_heads, max_seq_len,
+                        partition_tokens, ws, ws ? kScratchBytes : 0, geom, stream);
+}
+
+}  // extern "C"

@@ -231,6 +231,34 @@ def attention_decode(q, k_cache, v_cache, block_tables, seq_lens, scale, out=Non
                       partition_tokens, workspace, stream, phases, None, kv_shared=kv_shared)
 
 
+def attention_decode_noalloc(q, k_cache, v_cache, block_tables, seq_lens, scale, out,
+                             max_seq_len=None, partition_tokens=0, stream=None):
+    """pkv_attention_decode_noalloc: decode attention with the library's own
+    device scratch as the workspace (nothing is allocated; ``out`` is the
+    caller's).  Calls that may overlap on one GPU race on that scratch."""
+    if k_cache.dtype in _QUANT:
+        raise TypeError("attention_decode_noalloc takes bf16 or f32 pools")
+    g = geom_of(k_cache)
+    dev = k_cache.device
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (q, "q"), (out, "out")):
+        _need(t, n, k_cache.dtype, dev)
+    _need(block_tables, "block_tables", torch.int32, dev)
+    _need(seq_lens, "seq_lens", torch.int32, dev)
+    N, Hq, D = q.shape
+    if v_cache.shape != k_cache.shape or out.shape != q.shape or D != g.head_dim or \
+            block_tables.dim() != 2 or block_tables.shape[0] != N or seq_lens.shape != (N,):
+        raise ValueError("shape mismatch between q, out, block_tables, seq_lens and the pools")
+    max_blocks = block_tables.shape[1]
+    if max_seq_len is None:
+        max_seq_len = max_blocks * g.block_size
+    check(lib().pkv_attention_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                             _ptr(block_tables), max_blocks, _ptr(seq_lens),
+                                             float(scale), _ptr(out), N, Hq, int(max_seq_len),
+                                             int(partition_tokens), ctypes.byref(g),
+                                             _stream(stream)), "pkv_attention_decode_noalloc")
+    return out
+
+
 def attention_decode_append(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
                             seq_lens, scale, out=None, max_seq_len=None, partition_tokens=0,
                             workspace=None, stream=None, phases=3, kv_shared=False):

@@ -387,3 +387,19 @@ def test_decode_route_query():
     n = lib.pkv_attention_workspace_bytes(4, 64, 4096, 512,
                                           ctypes.byref(g(nb=8192, H=8, D=128, dt=1)))
     assert n == 4 * 64 * 8 * (128 + 2) * 4
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch():
+    """pkv_attention_decode_noalloc refuses, on the host and before anything
+    is enqueued, sizes whose workspace exceeds the library's scratch."""
+    lib = pkv.lib()
+    geo = PkvGeom(1 << 20, 16, 8, 128, _lib.PKV_BF16)
+    need = lib.pkv_attention_workspace_bytes(4096, 32, 8192, 0, ctypes.byref(geo))
+    assert need > _lib.PKV_NOALLOC_SCRATCH_BYTES
+    st = lib.pkv_attention_decode_noalloc(None, None, None, None, 512, None, 0.1, None, 4096, 32,
+                                          8192, 0, ctypes.byref(geo), None)
+    assert st == _lib.PKV_ERR_INVALID_ARG
+    assert "scratch" in last_error() and str(need) in last_error()
+    q8 = PkvGeom(1 << 20, 16, 8, 128, _lib.PKV_FP8_E4M3)
+    assert lib.pkv_attention_decode_noalloc(None, None, None, None, 1, None, 0.1, None, 1, 8, 16,
+                                            0, ctypes.byref(q8), None) == _lib.PKV_ERR_INVALID_ARG
