@@ -277,6 +277,24 @@ pkv_status pkv_swap_in(const int32_t* pairs, int32_t num_pairs, const pkv_host_p
 int32_t pkv_attention_partition_tokens(int32_t num_seqs, int32_t num_q_heads,
                                        int32_t max_seq_len, const pkv_geom* geom);
 
+/* Positions one split-KV piece of pkv_attention_decode covers for these
+ * arguments (partition_tokens as passed to it, 0 = automatic): what a given
+ * partition length binds on each route.  On the vector kernels with fixed
+ * partitions a piece is exactly one partition (the result is the log-sum-exp
+ * merge of the partitions' states).  On the matrix-core route the partition
+ * length is the finest split asked for: when there are more (sequence, KV
+ * head, partition) items than the GPU holds at once, one workgroup walks an
+ * equal share of a history, cut at whole 32-position tiles, and folds it into
+ * one piece (the merge of its partitions' states up to fp32 rounding order),
+ * so a piece can span several partitions: for 4 histories of 131,072
+ * positions, 8 KV heads and 512-token partitions, 96 pieces of 1,376
+ * positions each.  Returns the history length rounded up to a whole tile
+ * when nothing is split, 0 on the balanced split (its pieces are intervals of
+ * the batch's global tile order, not of one history) or on invalid
+ * arguments. */
+int32_t pkv_attention_piece_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
+                                   int32_t partition_tokens, const pkv_geom* geom);
+
 /* Which kernels pkv_attention_decode (and its _phase, _append and _quant
  * forms) runs for these sizes: PKV_ROUTE_PARTITIONS (vector kernels, fixed
  * partitions), PKV_ROUTE_BALANCED (vector kernels, the balanced split) or
@@ -339,7 +357,10 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *                 positions it walks into one piece: single partitions when
  *                 they alone fill the GPU, else equal shares of each history
  *                 (about 3072 workgroups in all), which equals the merge of
- *                 the partition pieces up to fp32 rounding order.
+ *                 the partition pieces up to fp32 rounding order.  So on that
+ *                 route partition_tokens is the finest split asked for, not
+ *                 the split that runs: pkv_attention_piece_tokens says what
+ *                 one piece covers.
  *   workspace     device buffer of at least pkv_attention_workspace_bytes(...)
  *                 bytes (may be NULL when that is 0); contents on entry are
  *                 ignored.  Calls that may run at the same time need
@@ -497,8 +518,14 @@ pkv_status pkv_attention_multi_quant(const void* q, const int32_t* q_offsets, co
                                      int32_t partition_tokens, void* workspace,
                                      size_t workspace_bytes, const pkv_geom* geom, void* stream);
 
-/* Tuning knobs of pkv_attention_decode, read from the environment at each
- * call (unset or out of range = the library's heuristic):
+/* Tuning knobs of the attention entry points.  Each starts from the
+ * environment variable of its name, read once per process at the first use
+ * of any knob (unset or out of range = 0, the library's heuristic); later
+ * changes to the environment have no effect.  pkv_set_tuning sets a knob
+ * (0 = back to the heuristic; INVALID_ARG for an unknown name or a value out
+ * of range); pkv_get_tuning returns its current value, -1 for an unknown
+ * name.  Knobs are process-wide: a change applies to calls enqueued after it.
+ * Names and ranges:
  *   PKV_ATTN_HEADS_PER_WAVE  1..4  upper bound on query heads one wave carries
  *   PKV_ATTN_PREFETCH        2..4  K/V tiles of 16 positions in flight per wave
  *                                  (bf16: at most 4 / 3 / 2 for 1 / 2 / 3-4
@@ -518,6 +545,8 @@ pkv_status pkv_attention_multi_quant(const void* q, const int32_t* q_offsets, co
  *                                  (vector routes with non-temporal loads only)
  * They change speed and register use, never results beyond fp32 rounding
  * order across query-head groupings (each head's arithmetic is unchanged). */
+pkv_status pkv_set_tuning(const char* name, int32_t value);
+int32_t pkv_get_tuning(const char* name);
 
 /* pkv_stream_read -- calibration, not part of the method: reads ``bytes``
  * (a multiple of 16) from device buffer ``src`` with a coalesced
@@ -543,7 +572,10 @@ typedef struct pkv_bm pkv_bm;
 pkv_bm* pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order);
 void pkv_bm_destroy(pkv_bm* bm);
 
-/* New empty sequence.  INVALID_ARG if the id exists. */
+/* New empty sequence: an empty block table of its own ([KVM §19.2.2] block
+ * partitioning: every request has an independent block table; [ENG §5.1]
+ * one table row per sequence, grown as the sequence grows).  INVALID_ARG if
+ * the id exists. */
 pkv_status pkv_bm_add_seq(pkv_bm* bm, int64_t seq);
 
 /* Empty sequence dst takes src's first num_tokens tokens by reference: the
@@ -577,17 +609,26 @@ pkv_status pkv_bm_append_slots(pkv_bm* bm, const int64_t* seqs, int32_t n,
 pkv_status pkv_bm_free_seq(pkv_bm* bm, int64_t seq);
 
 /* Block tables of seqs[0..n) as host int32 [n][max_blocks] padded with -1, and
- * their token counts (host int32 [n]).  INVALID_ARG if a table is longer than
- * max_blocks or a sequence is unknown. */
+ * their token counts (host int32 [n]): the batched form the kernel takes
+ * ([ENG §5.1] a two-dimensional array, sequence by logical block, one int
+ * block id per entry ([ENG §2.1]); [ENG §5.2] the kernel receives the table
+ * pointer).  INVALID_ARG if a table is longer than max_blocks or a sequence is
+ * unknown. */
 pkv_status pkv_bm_export(const pkv_bm* bm, const int64_t* seqs, int32_t n, int32_t max_blocks,
                          int32_t* block_tables_out, int32_t* seq_lens_out);
 
+/* Blocks on the free list ([ENG §3.2]: every physical block is either named
+ * by a logical block or on the free list). */
 int32_t pkv_bm_num_free(const pkv_bm* bm);
-/* Reference count of a block (-1 if out of range). */
+/* Reference count of a block: the number of table entries naming it ([KVM
+ * §19.2.2] copy-on-write: a shared block keeps a reference count; [ENG §4.2]);
+ * -1 if out of range. */
 int32_t pkv_bm_refcount(const pkv_bm* bm, int32_t block);
-/* Tokens in a sequence (-1 if unknown). */
+/* Tokens in a sequence: its write position ([ENG §2.1] the per-sequence
+ * offset kept apart from the table); -1 if unknown. */
 int32_t pkv_bm_num_tokens(const pkv_bm* bm, int64_t seq);
-/* Copy the free list (bottom to top) into out[0..cap); *n_out = its length. */
+/* Copy the free list (bottom to top; blocks are taken from and returned to
+ * the top, [KVM §19.2.3]) into out[0..cap); *n_out = its length. */
 pkv_status pkv_bm_free_list(const pkv_bm* bm, int32_t* out, int32_t cap, int32_t* n_out);
 /* ---- Preemption by swap ([KVM §19.2.6]; [ENG §8.2]) --------------------------
  * A manager may hold a second pool of host blocks with its own free list

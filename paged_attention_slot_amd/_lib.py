@@ -43,6 +43,8 @@ class PkvHostPool(ctypes.Structure):
 SIGNATURES = {
     "pkv_version": (c_i32, []),
     "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_set_tuning": (c_i32, [ctypes.c_char_p, c_i32]),
+    "pkv_get_tuning": (c_i32, [ctypes.c_char_p]),
     "pkv_write": (c_i32, [c_void_p, c_void_p, c_void_p, c_i32, c_void_p, c_void_p,
                           ctypes.POINTER(PkvGeom), c_void_p]),
     "pkv_copy_blocks": (c_i32, [c_void_p, c_i32, c_void_p, c_void_p, ctypes.POINTER(PkvGeom),
@@ -63,6 +65,7 @@ SIGNATURES = {
                                     c_void_p, c_float, c_void_p, c_i32, c_i32, c_i32, c_i32, c_i32,
                                     c_i32, c_void_p, c_size, ctypes.POINTER(PkvGeom), c_void_p]),
     "pkv_attention_partition_tokens": (c_i32, [c_i32, c_i32, c_i32, ctypes.POINTER(PkvGeom)]),
+    "pkv_attention_piece_tokens": (c_i32, [c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(PkvGeom)]),
     "pkv_attention_decode_route": (c_i32, [c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(PkvGeom)]),
     "pkv_attention_decode_append_folded": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32,
                                                     ctypes.POINTER(PkvGeom)]),

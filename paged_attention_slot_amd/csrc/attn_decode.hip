@@ -979,23 +979,14 @@ attn_merge_balanced_kernel(AttnArgs a) {
 // Host side: planning, validation, dispatch.
 // ---------------------------------------------------------------------------
 
-// Tuning knobs read from the environment at each call (documented in
-// include/pkv.h).  0 = the heuristic.
-int env_knob(const char* name, int lo, int hi) {
-  const char* v = std::getenv(name);
-  if (!v || !*v) return 0;
-  const int x = std::atoi(v);
-  return (x >= lo && x <= hi) ? x : 0;
-}
-int knob_heads_per_wave() { return env_knob("PKV_ATTN_HEADS_PER_WAVE", 1, 4); }
-int knob_prefetch() { return env_knob("PKV_ATTN_PREFETCH", 2, 4); }
+// Tuning knobs (pkv_set_tuning in include/pkv.h; the environment is read once
+// per process).  0 = the heuristic.
+int knob_heads_per_wave() { return pkv::tuning(pkv::kKnobHeadsPerWave); }
+int knob_prefetch() { return pkv::tuning(pkv::kKnobPrefetch); }
 // 1 partitions, 2 balanced, 3 matrix cores
-int knob_mode() { return env_knob("PKV_ATTN_MODE", 1, 3); }
-int knob_append() { return env_knob("PKV_ATTN_APPEND", 1, 2); }  // 1 copy kernel, 2 folded
-int knob_waves_per_block() {
-  const int v = env_knob("PKV_ATTN_WAVES_PER_BLOCK", 1, kMaxWavesPerBlock);
-  return (v & (v - 1)) == 0 ? v : 0;
-}
+int knob_mode() { return pkv::tuning(pkv::kKnobMode); }
+int knob_append() { return pkv::tuning(pkv::kKnobAppend); }  // 1 copy kernel, 2 folded
+int knob_waves_per_block() { return pkv::tuning(pkv::kKnobWavesPerBlock); }
 
 // Query heads per wave: the largest of 4, 3, 2, 1 dividing the group size that
 // fits the register file without spilling (fp32 rows of 128 hold twice the
@@ -1371,6 +1362,19 @@ int32_t pkv_attention_partition_tokens(int32_t num_seqs, int32_t num_q_heads,
     return 0;
   if (pl.mode == kBalancedMode)  // the split is by shares, not by partitions
     return 0;
+  return pl.part_tokens;
+}
+
+int32_t pkv_attention_piece_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
+                                   int32_t partition_tokens, const pkv_geom* geom) {
+  Plan pl;
+  const int32_t max_blocks =
+      geom && geom->block_size > 0 ? (max_seq_len + geom->block_size - 1) / geom->block_size : 0;
+  if (make_plan(num_seqs, num_q_heads, max_seq_len, max_blocks, partition_tokens, geom,
+                "pkv_attention_piece_tokens", &pl) != PKV_OK)
+    return 0;
+  if (pl.mode == kBalancedMode) return 0;
+  if (pl.mode == kMatrixMode) return pl.runs.run_tokens;
   return pl.part_tokens;
 }
 

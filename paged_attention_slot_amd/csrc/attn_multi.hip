@@ -192,14 +192,9 @@ struct MultiPlan {
 
 int64_t round_up_to(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
-// PKV_ATTN_PARTS_PER_WG (tuning, documented in include/pkv.h): partitions one
+// PKV_ATTN_PARTS_PER_WG (pkv_set_tuning in include/pkv.h): partitions one
 // matrix-core workgroup walks; 0 = the heuristic.
-int knob_parts_per_wg() {
-  const char* v = std::getenv("PKV_ATTN_PARTS_PER_WG");
-  if (!v || !*v) return 0;
-  const int x = std::atoi(v);
-  return (x >= 1 && x <= 65535) ? x : 0;
-}
+int knob_parts_per_wg() { return pkv::tuning(pkv::kKnobPartsPerWg); }
 
 // Which cache types a caller accepts: 0 = bf16 only, 1 = one-byte codes only,
 // 2 = any of them (workspace sizing).

@@ -33,6 +33,19 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def set_tuning(name: str, value: int) -> None:
+    """Set a tuning knob of the attention entry points (pkv_set_tuning; 0 =
+    the library's heuristic)."""
+    check(lib().pkv_set_tuning(name.encode(), int(value)), "pkv_set_tuning")
+
+
+def get_tuning(name: str) -> int:
+    v = lib().pkv_get_tuning(name.encode())
+    if v < 0:
+        raise KeyError(name)
+    return int(v)
+
+
 def _scratch(nbytes: int, dev, stream, phases: int = 3) -> torch.Tensor:
     """A workspace for one call, when the caller passes none.  A call of one
     phase alone needs the caller's workspace (the other phase reads what this
@@ -107,6 +120,15 @@ def partition_tokens(num_seqs: int, num_q_heads: int, max_seq_len: int, k_cache)
     g = geom_of(k_cache)
     return int(lib().pkv_attention_partition_tokens(num_seqs, num_q_heads, max_seq_len,
                                                     ctypes.byref(g)))
+
+
+def piece_tokens(num_seqs: int, num_q_heads: int, max_seq_len: int, k_cache,
+                 partition_tokens: int = 0) -> int:
+    """Positions one split-KV piece covers (pkv_attention_piece_tokens; 0 on
+    the balanced split)."""
+    g = geom_of(k_cache)
+    return int(lib().pkv_attention_piece_tokens(num_seqs, num_q_heads, max_seq_len,
+                                                int(partition_tokens), ctypes.byref(g)))
 
 
 ROUTES = {0: "partitions", 1: "balanced", 2: "matrix"}

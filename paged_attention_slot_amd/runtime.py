@@ -311,7 +311,10 @@ class DecodeStep:
         pt = self.partition_tokens or ops.partition_tokens(
             self.wl.num_seqs, self.wl.num_q_heads, self.max_seq_len, self.k_caches[0])
         split = {"mode": "matrix" if route == "matrix" else "partitions", "partition_tokens": pt,
-                 "num_partitions": max(1, -(-self.max_seq_len // pt))}
+                 "num_partitions": max(1, -(-self.max_seq_len // pt)),
+                 "piece_tokens": ops.piece_tokens(self.wl.num_seqs, self.wl.num_q_heads,
+                                                  self.max_seq_len, self.k_caches[0],
+                                                  self.partition_tokens)}
         if route == "matrix":
             # one workspace row of D + 2 floats per (sequence, query head, run)
             ws = ops.workspace_bytes(self.wl.num_seqs, self.wl.num_q_heads, self.max_seq_len,

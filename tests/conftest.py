@@ -24,3 +24,19 @@ def load_golden(name):
 @pytest.fixture
 def golden():
     return load_golden
+
+
+@pytest.fixture
+def tuning():
+    """Set libpkv tuning knobs for one test (pkv_set_tuning); every knob the
+    test touched is put back to its value before the test."""
+    from paged_attention_slot_amd import ops
+    saved = {}
+
+    def set_knob(name, value):
+        if name not in saved:
+            saved[name] = ops.get_tuning(name)
+        ops.set_tuning(name, int(value or 0))
+    yield set_knob
+    for name, value in saved.items():
+        ops.set_tuning(name, value)

@@ -107,12 +107,12 @@ def test_partitions_match_oracle(pt, Hq, Hkv):
 
 
 @pytest.mark.parametrize("pt", [32, 96])
-def test_equal_shares_fold_partitions(pt, monkeypatch):
+def test_equal_shares_fold_partitions(pt, tuning):
     """More (query block, KV head, partition) items than the GPU holds at
     once: each workgroup takes an equal share of one history (cut at tiles,
     not at partitions) and folds it into one piece; a row merges the pieces of
     the shares that start at or before its causal limit."""
-    monkeypatch.delenv("PKV_ATTN_PARTS_PER_WG", raising=False)
+    tuning("PKV_ATTN_PARTS_PER_WG", 0)
     lens = [7500, 33, 6000, 2047, 1, 500, 7000, 4096]
     nq = [2, 1, 2, 1, 1, 2, 2, 1]
     got, ref, _ = run_case(900 + pt, lens, nq, 64, 8, 128, 16, pt=pt)

@@ -119,14 +119,13 @@ def test_cacheable_and_streaming_loads_agree(name):
 
 @pytest.mark.parametrize("ppw", [None, "3"])
 @pytest.mark.parametrize("pt", [0, 32, 96, 512])
-def test_matrix_route_matches_oracle(pt, ppw, monkeypatch):
+def test_matrix_route_matches_oracle(pt, ppw, tuning):
     """Groups of 8 query heads per KV head take the matrix-core route, with
     automatic or given partitions, and with runs of 3 partitions per
     workgroup (PKV_ATTN_PARTS_PER_WG): outputs against the oracle's split (or
     unsplit) attention."""
-    monkeypatch.delenv("PKV_ATTN_MODE", raising=False)  # the route under test is the default
-    if ppw:
-        monkeypatch.setenv("PKV_ATTN_PARTS_PER_WG", ppw)
+    tuning("PKV_ATTN_MODE", 0)  # the route under test is the default
+    tuning("PKV_ATTN_PARTS_PER_WG", int(ppw) if ppw else 0)
     wl = independent_workload([1, 15, 16, 17, 64, 200, 333, 1500], num_q_heads=64,
                               num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16",
                               seed=17 + pt)
@@ -144,15 +143,15 @@ def test_matrix_route_matches_oracle(pt, ppw, monkeypatch):
 
 
 @pytest.mark.parametrize("pt", [32, 64, 96])
-def test_matrix_route_equal_shares(pt, monkeypatch):
+def test_matrix_route_equal_shares(pt, tuning):
     """More short partitions than the GPU holds at once on the matrix-core
     route: workgroups take equal shares of 160 positions (cutting the 96-token
     partitions) and fold each share into one piece, so the workspace holds
     fewer rows than partitions.  Outputs against the oracle's split
     attention; then again with one history emptied, which must give zeros."""
     from paged_attention_slot_amd import ops
-    monkeypatch.delenv("PKV_ATTN_MODE", raising=False)
-    monkeypatch.delenv("PKV_ATTN_PARTS_PER_WG", raising=False)
+    tuning("PKV_ATTN_MODE", 0)
+    tuning("PKV_ATTN_PARTS_PER_WG", 0)
     wl = independent_workload([1, 2, 31, 33, 500, 2047, 6000, 7500], num_q_heads=64,
                               num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16",
                               seed=40 + pt)
@@ -184,14 +183,14 @@ def test_matrix_route_equal_shares(pt, monkeypatch):
                                           (64, None, False), (64, 32, False)],
                          ids=["balanced", "balanced-cacheable", "partitions", "matrix",
                               "matrix-shares"])
-def test_split_phases_match_one_call(Hq, pt, shared, monkeypatch):
+def test_split_phases_match_one_call(Hq, pt, shared, tuning):
     """pkv_attention_decode_phase: the per-partition phase, then the merge
     phase in a call of its own (which reads what the first left in the
     workspace: pieces, and on the balanced split each stream's first and last
     interval), gives the bits of one call with both phases; a second merge
     call gives them again."""
-    monkeypatch.delenv("PKV_ATTN_MODE", raising=False)
-    monkeypatch.delenv("PKV_ATTN_PARTS_PER_WG", raising=False)
+    tuning("PKV_ATTN_MODE", 0)
+    tuning("PKV_ATTN_PARTS_PER_WG", 0)
     wl = independent_workload([1, 15, 16, 17, 64, 200, 333, 1500, 2047, 3000], num_q_heads=Hq,
                               num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16",
                               seed=60 + Hq + (pt or 0))
@@ -339,9 +338,9 @@ def test_long_context_config_partitions_against_oracle_split():
 # -- the two work distributions ------------------------------------------------
 
 @pytest.fixture
-def mode_env(monkeypatch):
+def mode_env(tuning):
     def set_mode(mode):
-        monkeypatch.setenv("PKV_ATTN_MODE", str(mode))
+        tuning("PKV_ATTN_MODE", mode)
     return set_mode
 
 

@@ -103,13 +103,9 @@ ROUTES = [  # id, Hq, Hkv, D, B, dtype, mode env, forks, fused
 
 
 @pytest.mark.parametrize("rid,Hq,Hkv,D,B,dtype,mode,forks,fused", ROUTES, ids=[r[0] for r in ROUTES])
-def test_decode_routes_on_stale_pools(rid, Hq, Hkv, D, B, dtype, mode, forks, fused,
-                                      monkeypatch):
-    monkeypatch.delenv("PKV_ATTN_PARTS_PER_WG", raising=False)
-    if mode:
-        monkeypatch.setenv("PKV_ATTN_MODE", mode)
-    else:
-        monkeypatch.delenv("PKV_ATTN_MODE", raising=False)
+def test_decode_routes_on_stale_pools(rid, Hq, Hkv, D, B, dtype, mode, forks, fused, tuning):
+    tuning("PKV_ATTN_PARTS_PER_WG", 0)
+    tuning("PKV_ATTN_MODE", int(mode) if mode else 0)
     wl = stale_churn(Hq, Hkv, D, B, dtype, FORKS if forks else None, seed=300 + Hq + B + D)
     step, ost = build(wl)
     say(f"  route {step.split} kv_shared={step.kv_shared} fused={fused} "
@@ -127,11 +123,11 @@ def test_decode_routes_on_stale_pools(rid, Hq, Hkv, D, B, dtype, mode, forks, fu
 
 
 @pytest.mark.parametrize("pt", [32, 64])
-def test_split_partitions_on_stale_pools(pt, monkeypatch):
+def test_split_partitions_on_stale_pools(pt, tuning):
     """Given partitions (vector and matrix-core routes) against the oracle's
     split attention."""
-    monkeypatch.delenv("PKV_ATTN_MODE", raising=False)
-    monkeypatch.delenv("PKV_ATTN_PARTS_PER_WG", raising=False)
+    tuning("PKV_ATTN_MODE", 0)
+    tuning("PKV_ATTN_PARTS_PER_WG", 0)
     for Hq in (16, 64):
         wl = stale_churn(Hq, 8, 128, 16, "bf16", None, seed=400 + pt + Hq)
         step, ost = build(wl, partition_tokens=pt)
@@ -194,7 +190,7 @@ def test_multi_token_queries_on_stale_pools():
     check_out(out, ref, "bf16", "multi-token, 4 per sequence")
 
 
-def test_shared_partial_last_block_before_any_append():
+def test_shared_partial_last_block_before_any_append(tuning):
     """A fork family (and a second group) whose shared last block is only
     partly written and no member has appended since: every member is shorter
     than the shared blocks, whose remaining slots hold NaN / Inf.  The
@@ -230,12 +226,8 @@ def test_shared_partial_last_block_before_any_append():
                                       max_seq_len=int(lens.max()))
     torch.cuda.synchronize()
     check_out(out, ref, "bf16", "shared kernels, partly written shared block")
-    for mode in ("1", "2"):
-        import os
-        os.environ["PKV_ATTN_MODE"] = mode
-        try:
-            o = ops.attention_decode(qd, kd, vd, tb, ln, scale, max_seq_len=int(lens.max()))
-            torch.cuda.synchronize()
-        finally:
-            del os.environ["PKV_ATTN_MODE"]
+    for mode in (1, 2):
+        tuning("PKV_ATTN_MODE", mode)
+        o = ops.attention_decode(qd, kd, vd, tb, ln, scale, max_seq_len=int(lens.max()))
+        torch.cuda.synchronize()
         check_out(o, ref, "bf16", f"decode mode {mode}, partly written shared block")

@@ -325,15 +325,15 @@ def test_fused_append_entry_point_validates_on_the_host():
     assert "workspace" in last_error()
 
 
-def test_append_fold_query(monkeypatch):
+def test_append_fold_query(tuning):
     """pkv_attention_decode_append_folded: the append rides in the attention
     kernel on the vector routes for waves of up to two query heads, not on
     batches that share blocks or whose query groups span several waves (both
     keep cacheable loads), not on the matrix route; one-byte pools give -1
     (the fused append refuses them)."""
-    monkeypatch.delenv("PKV_ATTN_APPEND", raising=False)
-    monkeypatch.delenv("PKV_ATTN_MODE", raising=False)
-    monkeypatch.delenv("PKV_ATTN_HEADS_PER_WAVE", raising=False)
+    tuning("PKV_ATTN_APPEND", 0)
+    tuning("PKV_ATTN_MODE", 0)
+    tuning("PKV_ATTN_HEADS_PER_WAVE", 0)
     lib = pkv.lib()
 
     def folded(N, Hq, H, D, dt, shared=0, pt=0, maxlen=4096):
@@ -349,9 +349,9 @@ def test_append_fold_query(monkeypatch):
     assert folded(4, 64, 8, 128, _lib.PKV_BF16) == 0           # matrix route
     assert folded(4, 64, 8, 128, _lib.PKV_FP8_E4M3) == -1
     assert folded(4, 63, 8, 128, _lib.PKV_BF16) == -1
-    monkeypatch.setenv("PKV_ATTN_APPEND", "2")
+    tuning("PKV_ATTN_APPEND", 2)
     assert folded(64, 32, 8, 128, _lib.PKV_BF16) == 1
-    monkeypatch.setenv("PKV_ATTN_APPEND", "1")
+    tuning("PKV_ATTN_APPEND", 1)
     assert folded(64, 16, 8, 128, _lib.PKV_BF16) == 0
 
 
@@ -403,3 +403,46 @@ def test_noalloc_rejects_sizes_beyond_its_scratch():
     q8 = PkvGeom(1 << 20, 16, 8, 128, _lib.PKV_FP8_E4M3)
     assert lib.pkv_attention_decode_noalloc(None, None, None, None, 1, None, 0.1, None, 1, 8, 16,
                                             0, ctypes.byref(q8), None) == _lib.PKV_ERR_INVALID_ARG
+
+
+def test_tuning_knobs_read_once_and_set_through_the_abi(tuning):
+    """Knobs start from the environment once per process; later environment
+    changes do nothing, pkv_set_tuning does (and refuses unknown names and
+    values out of range)."""
+    lib = pkv.lib()
+    geo = ctypes.byref(g(nb=8192, H=8, D=128, dt=_lib.PKV_BF16))
+    tuning("PKV_ATTN_MODE", 0)
+    assert lib.pkv_attention_decode_route(64, 16, 4096, 0, geo) == _lib.PKV_ROUTE_BALANCED
+    os.environ["PKV_ATTN_MODE"] = "1"
+    try:
+        assert lib.pkv_attention_decode_route(64, 16, 4096, 0, geo) == _lib.PKV_ROUTE_BALANCED
+    finally:
+        del os.environ["PKV_ATTN_MODE"]
+    tuning("PKV_ATTN_MODE", 1)
+    assert lib.pkv_get_tuning(b"PKV_ATTN_MODE") == 1
+    assert lib.pkv_attention_decode_route(64, 16, 4096, 0, geo) == _lib.PKV_ROUTE_PARTITIONS
+    assert lib.pkv_set_tuning(b"PKV_ATTN_MODE", 4) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_set_tuning(b"PKV_ATTN_WAVES_PER_BLOCK", 3) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_set_tuning(b"PKV_NOT_A_KNOB", 1) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_get_tuning(b"PKV_NOT_A_KNOB") == -1
+    assert lib.pkv_get_tuning(b"PKV_ATTN_MODE") == 1
+
+
+def test_piece_tokens_query():
+    """pkv_attention_piece_tokens: what one split-KV piece covers.  Fixed
+    partitions on the vector kernels: one partition.  The matrix-core route
+    with more partitions than the GPU holds at once: equal shares that fold
+    several partitions (the long-context shape: 96 pieces of 1,376 positions
+    for 512-token partitions); with few partitions, one partition each.  The
+    balanced split: 0."""
+    lib = pkv.lib()
+
+    def piece(N, Hq, maxlen, pt, H=8, D=128, B=16, dt=_lib.PKV_BF16, nb=8192):
+        return lib.pkv_attention_piece_tokens(N, Hq, maxlen, pt,
+                                              ctypes.byref(g(nb=nb, B=B, H=H, D=D, dt=dt)))
+
+    assert piece(4, 64, 131072, 512, B=32, nb=18022) == 1376
+    assert piece(4, 64, 4096, 512) == 512
+    assert piece(64, 16, 4096, 256) == 256
+    assert piece(64, 16, 4096, 0) == 0            # balanced split
+    assert piece(4, 63, 4096, 0) == 0             # invalid: 63 heads over 8
