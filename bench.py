@@ -53,6 +53,8 @@ KERNEL_SOURCES = {
     "attn_multi_kernel": ("attn_multi.hip", "mfma_attend.h", "mfma_route.h", "lse_merge.h",
                           "pkv_device.h"),
     "attn_shared": ("attn_shared.hip", "mfma_attend.h", "pkv_device.h"),
+    "attn_mfma_balanced_kernel": ("attn_decode.hip", "mfma_attend.h", "lse_merge.h",
+                                  "pkv_device.h"),
     "swap_blocks_kernel": ("swap.hip",),
 }
 
@@ -729,6 +731,7 @@ def main() -> int:
         "roofline": {
             "bound": "hbm",
             "kernel": {"balanced": "attn_balanced_kernel", "partitions": "attn_partition_kernel",
+                       "matrix-balanced": "attn_mfma_balanced_kernel",
                        "matrix": "attn_multi_kernel"}[step.split["mode"]],
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,

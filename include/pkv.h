@@ -301,9 +301,13 @@ int32_t pkv_attention_piece_tokens(int32_t num_seqs, int32_t num_q_heads, int32_
  * PKV_ROUTE_MATRIX (groups of 8 or more query heads per KV head at head_dim
  * 128, bf16 or one-byte pools, partition_tokens 0 or a multiple of 32: the
  * matrix-core pass of pkv_attention_multi with one query per sequence, fixed
- * partitions merged by log-sum-exp; PKV_ATTN_MODE overrides).  -1 on invalid
- * arguments. */
-enum { PKV_ROUTE_PARTITIONS = 0, PKV_ROUTE_BALANCED = 1, PKV_ROUTE_MATRIX = 2 };
+ * partitions merged by log-sum-exp) or PKV_ROUTE_MATRIX_BALANCED (one-byte
+ * pools with 2 to 7 query heads per KV head, partition_tokens 0: the balanced
+ * split's intervals walked by one-wave workgroups on the matrix cores, the
+ * group's heads as the rows of the products).  PKV_ATTN_MODE overrides.  -1
+ * on invalid arguments. */
+enum { PKV_ROUTE_PARTITIONS = 0, PKV_ROUTE_BALANCED = 1, PKV_ROUTE_MATRIX = 2,
+       PKV_ROUTE_MATRIX_BALANCED = 3 };
 int32_t pkv_attention_decode_route(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
                                    int32_t partition_tokens, const pkv_geom* geom);
 
@@ -535,7 +539,10 @@ pkv_status pkv_attention_multi_quant(const void* q, const int32_t* q_offsets, co
  *                                  (the waves of one (sequence, partition)
  *                                  are packed together)
  *   PKV_ATTN_MODE            1 = fixed partitions, 2 = balanced split,
- *                                  3 = the matrix-core route where it applies
+ *                                  3 = the matrix-core route where it applies,
+ *                                  4 = the balanced split on the matrix cores
+ *                                  where it applies (head_dim 128, bf16 or
+ *                                  one-byte pools, up to 16 heads per group)
  *   PKV_ATTN_PARTS_PER_WG    1..65535  matrix-core passes: consecutive
  *                                  partitions one workgroup walks (the decode
  *                                  route folds them into one piece, instead

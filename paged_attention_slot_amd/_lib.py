@@ -20,7 +20,7 @@ P_i64 = ctypes.POINTER(ctypes.c_int64)
 
 PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_NO_FREE_BLOCKS, PKV_ERR_HIP = range(5)
 PKV_F32, PKV_BF16, PKV_FP8_E4M3, PKV_INT8 = 0, 1, 2, 3
-PKV_ROUTE_PARTITIONS, PKV_ROUTE_BALANCED, PKV_ROUTE_MATRIX = 0, 1, 2
+PKV_ROUTE_PARTITIONS, PKV_ROUTE_BALANCED, PKV_ROUTE_MATRIX, PKV_ROUTE_MATRIX_BALANCED = 0, 1, 2, 3
 PKV_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 

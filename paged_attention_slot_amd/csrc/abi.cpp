@@ -18,7 +18,7 @@ struct KnobDef {
 };
 const KnobDef kKnobs[pkv::kKnobCount] = {
     {"PKV_ATTN_HEADS_PER_WAVE", 1, 4, false}, {"PKV_ATTN_PREFETCH", 2, 4, false},
-    {"PKV_ATTN_MODE", 1, 3, false},           {"PKV_ATTN_APPEND", 1, 2, false},
+    {"PKV_ATTN_MODE", 1, 4, false},           {"PKV_ATTN_APPEND", 1, 2, false},
     {"PKV_ATTN_WAVES_PER_BLOCK", 1, 8, true}, {"PKV_ATTN_PARTS_PER_WG", 1, 65535, false},
 };
 std::atomic<int> g_knob[pkv::kKnobCount];

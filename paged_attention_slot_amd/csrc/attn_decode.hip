@@ -53,6 +53,7 @@
 
 #include "geom.h"
 #include "lse_merge.h"
+#include "mfma_attend.h"
 #include "mfma_route.h"
 #include "pkv_device.h"
 
@@ -68,7 +69,7 @@ constexpr int kDynamicPerMille = 150;   // balanced split: tiles handed out dyna
 constexpr int kMinChunkTiles = 4;       // smallest dynamic chunk
 constexpr int kMaxChunks = 8192;        // the workspace is sized for this many chunks
 
-enum Mode : int { kPartitionMode = 0, kBalancedMode = 1, kMatrixMode = 2 };
+enum Mode : int { kPartitionMode = 0, kBalancedMode = 1, kMatrixMode = 2, kMatrixBalancedMode = 3 };
 
 struct AttnArgs {
   const void* q;
@@ -118,6 +119,7 @@ struct AttnArgs {
   void* v_dst;
   int32_t stream_kv;  // 1: non-temporal K/V loads; 0: cacheable (shared blocks)
   int32_t merge_lanes;  // balanced merge: piece lanes per (head, column)
+  int32_t merge_heads;  // balanced merge: query heads per workgroup
 };
 
 // One-byte cache element types ([KVM §19.2.4], [PFX] "KV Cache 量化"): OCP e4m3
@@ -236,7 +238,8 @@ __device__ __forceinline__ void decode16(const uint4& x, float (&f)[16]) {
 
 // Two floats that bf16 holds exactly -> one bf16 pair (lo in the low half).
 __device__ __forceinline__ uint32_t bf16_pair_exact(float lo, float hi) {
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+  // the high halves of both words in one byte permute (v_perm_b32)
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
 // One wave's attention over a stretch [start, end) of one stream.  kAppend:
@@ -871,11 +874,6 @@ attn_balanced_kernel(AttnArgs a) {
 constexpr int kMergeBalancedThreads = 256;
 constexpr int kMergeBatch = 8;
 
-// Heads of a group per merge workgroup, and workgroups per stream.
-__host__ __device__ constexpr int merge_heads_per_block(int G, int D) {
-  return G < kMergeBalancedThreads / (D / 4) ? G : kMergeBalancedThreads / (D / 4);
-}
-
 // grid = (ceil(G / heads per block), num_seqs * H_kv)
 template <typename T, int D>
 __global__ void __launch_bounds__(kMergeBalancedThreads)
@@ -884,7 +882,7 @@ attn_merge_balanced_kernel(AttnArgs a) {
   constexpr int kQ = D / 4;  // float4 columns per row
   __shared__ float part[kMergeBalancedThreads][6];  // (reference, sum, 4 columns)
   const int G = a.group;
-  const int HB = merge_heads_per_block(G, D);
+  const int HB = a.merge_heads;  // blockDim.x = HB * kQ * P <= 256
   const int cols = HB * kQ;
   const int P = a.merge_lanes;  // piece lanes: blockDim.x = cols * P <= 256
   const int tid = threadIdx.x;
@@ -972,6 +970,122 @@ attn_merge_balanced_kernel(AttnArgs a) {
         make_uint2(pkv::pack_bf16x2(o[0] * inv, o[1] * inv), pkv::pack_bf16x2(o[2] * inv, o[3] * inv));
   } else {
     *reinterpret_cast<float4*>(dst) = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Balanced split on the matrix cores: the balanced split's intervals over the
+// batch's global tile order (tiles of 32 positions here), each walked by a
+// one-wave workgroup with the matrix-core pass of the multi-token kernel
+// (pkv::mfma::attend): the G <= 16 query heads of a KV head are the rows of
+// the 16-row products, so q.k and p.v run on the matrix cores and only the
+// softmax stays on the vector units.  For one-byte codes the vector kernels
+// are bound by instruction issue (decoding the codes, then a multiply-add per
+// (element, position, head)), while here a 32-position tile of all G heads
+// costs 24 matrix instructions and the softmax of one tile.  Pieces and
+// records are the balanced split's, so attn_merge_balanced_kernel merges
+// them.
+// ---------------------------------------------------------------------------
+constexpr int kMT = pkv::mfma::kKT;  // positions per tile on the matrix cores
+
+__device__ __forceinline__ int stream_tiles32(const AttnArgs& a, int s) {
+  return (clamp_len(a.seq_lens[s], a.len_cap) + kMT - 1) / kMT;
+}
+
+// grid = static workgroups (the resident ones) + dynamic chunks, 64 threads;
+// dynamic LDS: (num_seqs + 1) int32 prefix sums.
+template <int Q, bool kStream>
+__global__ void __launch_bounds__(64)
+attn_mfma_balanced_kernel(AttnArgs a) {
+  constexpr int D = 128;
+  extern __shared__ int32_t base[];
+  __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D, 1>()];
+  __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D, 1>()];
+  __shared__ float s_lds[pkv::mfma::s_lds_elems<Q, 1>()];
+  const int N = a.num_seqs, Hkv = a.num_kv_heads;
+  const int lane = threadIdx.x & 63;
+
+  // base[s] = sum over s' < s of H_kv * tiles(s'): each lane sums a run of
+  // sequences, then a wave scan.
+  const int per = (N + 63) / 64;
+  const int s0 = lane * per;
+  int tsum = 0;
+  for (int i = 0; i < per; ++i)
+    if (s0 + i < N) tsum += Hkv * stream_tiles32(a, s0 + i);
+  const int incl = wave_incl_scan(tsum);
+  const int total = __shfl(incl, 63, 64);
+  int run = incl - tsum;
+  for (int i = 0; i < per; ++i) {
+    if (s0 + i < N) {
+      base[s0 + i] = run;
+      run += Hkv * stream_tiles32(a, s0 + i);
+    }
+  }
+  if (lane == 0) base[N] = total;
+  __syncthreads();
+  if (total == 0) return;
+  const Intervals ivs(total, a.num_groups);
+  int iv;
+  if (static_cast<int>(blockIdx.x) < a.static_blocks) {
+    iv = blockIdx.x;
+    if (iv >= ivs.Ws) return;
+  } else {
+    const int j = blockIdx.x - a.static_blocks;
+    if (j >= ivs.K) return;
+    iv = ivs.Ws + j;
+  }
+  const int64_t lo = ivs.lo(iv), hi = ivs.lo(iv + 1);
+
+  const int G = a.group;
+  const int row = lane & 15;
+  const bool row_ok = row < G;
+  constexpr int kEB = Q == pkv::mfma::kBf16 ? 2 : 1;
+  const float scale_log2 = Q == pkv::mfma::kFp8 ? a.scale_log2 * a.k_scale : a.scale_log2;
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+  int64_t cur = lo;
+  while (cur < hi) {
+    // the sequence holding global tile cur: the largest s with base[s] <= cur
+    int lo_s = 0, hi_s = N - 1;
+    while (lo_s < hi_s) {
+      const int mid = (lo_s + hi_s + 1) >> 1;
+      if (base[mid] <= cur) lo_s = mid;
+      else hi_s = mid - 1;
+    }
+    const int s = lo_s;
+    const int nt = (base[s + 1] - base[s]) / Hkv;
+    const int rel = static_cast<int>(cur - base[s]);
+    const int kvh = rel / nt;
+    const int t0 = rel - kvh * nt;
+    const int seg = static_cast<int>(min(hi - cur, int64_t(nt - t0)));
+    const int L = clamp_len(a.seq_lens[s], a.len_cap);
+    const pkv::mfma::History hist{a.k_cache,      a.v_cache,    a.block_tables + int64_t(s) * a.max_blocks,
+                                  L,              kvh,          a.block_bytes / kEB,
+                                  a.row_bytes / kEB, a.num_blocks, a.block_shift,
+                                  Hkv,            a.v_scale,    a.k_scales,
+                                  a.v_scales};
+    const int64_t qh = int64_t(s) * a.num_q_heads + kvh * G + (row_ok ? row : 0);
+    pkv::mfma::RowAcc<D> r;
+    pkv::mfma::start(r);
+    // one-byte tiles are half the registers: two in flight ahead of the one
+    // being computed, at the same occupancy
+    constexpr int kPD = Q == pkv::mfma::kBf16 ? 1 : 2;
+    pkv::mfma::attend<D, 1, kPD, Q, kStream>(hist, t0 * kMT, min((t0 + seg) * kMT, L),
+                                             q + qh * D, row_ok, L - 1, L - 1, scale_log2, k_lds,
+                                             v_lds, r, s_lds);
+    const int64_t k = int64_t(s) * Hkv + kvh;
+    if (lane == 0) {  // the stream's first and last intervals, for the merge
+      if (t0 == 0) a.ws_span[2 * k] = iv;
+      if (t0 + seg == nt) a.ws_span[2 * k + 1] = iv;
+    }
+    if (t0 == 0 && seg == nt) {
+      if (row_ok) pkv::mfma::store_row_bf16<D>(r, out + qh * D);
+    } else if (row_ok) {
+      // row group (k + iv), as on the vector kernels' balanced split
+      const int64_t prow = (k + iv) * G + row;
+      pkv::mfma::store_piece<D>(r, a.ws_acc + prow * D, a.ws_ml + prow);
+    }
+    cur += seg;
   }
 }
 
@@ -1085,6 +1199,31 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
   // for 16 heads at once and keeps only the softmax on the vector units.
   const bool matrix_ok = g->head_dim == 128 && (g->dtype == PKV_BF16 || pkv::is_quant(g->dtype)) &&
                          partition_tokens % 32 == 0 && g->num_kv_heads <= 65535;
+  // One-byte codes with 2 to 7 query heads per KV head: the balanced split on
+  // the matrix cores (the vector kernels are issue-bound decoding the codes).
+  const int64_t tiles32_max = (int64_t(pl->len_cap) + 31) / 32;
+  const bool mbal_ok = matrix_ok && partition_tokens == 0 && num_seqs <= kMaxBalancedSeqs &&
+                       G <= 16 && int64_t(num_seqs) * g->num_kv_heads * tiles32_max < (int64_t(1) << 31);
+  if (mbal_ok && (km == 4 || (km == 0 && pkv::is_quant(g->dtype) && G >= 2 && G < 8))) {
+    pl->mode = kMatrixBalancedMode;
+    pl->gw = G;
+    pl->waves_per_group = 1;
+    pl->prefetch = 0;
+    pl->waves_per_block = 1;
+    pl->waves_per_item = pl->blocks_per_item = 0;
+    pl->groups_per_block = 1;
+    pl->num_parts = 0;
+    pl->part_tokens = 0;
+    pl->rows = (int64_t(num_seqs) * g->num_kv_heads + kMaxWaveGroups + kMaxChunks) * G;
+    const size_t acc = size_t(pl->rows) * g->head_dim * sizeof(float);
+    pl->ws_ml_off = acc;
+    pl->ws_span_off = acc + size_t(pl->rows) * sizeof(float2);
+    pl->ws_bytes = pl->ws_span_off + round_up(int64_t(num_seqs) * g->num_kv_heads * 8, 256);
+    const int64_t tmax = int64_t(num_seqs) * g->num_kv_heads * tiles32_max;
+    const int64_t kb = (tmax * kDynamicPerMille / 1000 + kMinChunkTiles - 1) / kMinChunkTiles;
+    pl->max_chunks = static_cast<int>(kb < kMaxChunks ? kb : kMaxChunks);
+    return PKV_OK;
+  }
   if (matrix_ok && (km == 3 || (km == 0 && G >= 8))) {
     pl->mode = kMatrixMode;
     pl->prefetch = 0;
@@ -1170,25 +1309,79 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
 
 // Workgroups of ``kernel`` (at ``threads`` per group) one CU holds at once,
 // times the CU count of the current device; cached per (device, kernel).
-int resident_blocks(const void* kernel, int threads) {
+int resident_blocks(const void* kernel, int threads, size_t dyn_lds = 0) {
   static std::mutex mu;
   static std::unordered_map<uint64_t, int> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  const uint64_t key = (uint64_t(reinterpret_cast<uintptr_t>(kernel)) << 8) ^ uint64_t(dev);
+  const uint64_t key = (uint64_t(reinterpret_cast<uintptr_t>(kernel)) << 8) ^ uint64_t(dev) ^
+                       (uint64_t(dyn_lds) << 40);
   {
     std::lock_guard<std::mutex> lk(mu);
     auto it = cache.find(key);
     if (it != cache.end()) return it->second;
   }
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, dyn_lds) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   const int v = per_cu * cus;
   std::lock_guard<std::mutex> lk(mu);
   cache[key] = v;
   return v;
+}
+
+// The balanced split's merge (both balanced kernels).  Piece lanes from the
+// average pieces per stream (intervals plus streams over streams): about two
+// batches' worth per lane group, so most streams take one round trip, without
+// idle lanes on batches whose streams are cut into a few pieces only.
+// a.num_groups is the static part's wave groups.
+template <typename O, int D>
+void launch_balanced_merge(const Plan& pl, AttnArgs& a, int num_seqs, hipStream_t st) {
+  constexpr int kQ = D / 4;
+  const int64_t streams = int64_t(num_seqs) * a.num_kv_heads;
+  const int64_t chunks = pl.max_chunks < a.num_groups ? pl.max_chunks : a.num_groups;
+  const int64_t avg = (a.num_groups + chunks + streams + streams - 1) / streams;
+  // lanes first (few streams cut into many pieces: up to 256 / kQ lanes, the
+  // heads then spread over more workgroups), then as many heads per
+  // workgroup as the 256 threads hold
+  int lanes = 1;
+  while (lanes * kMergeBatch < 2 * avg && 2 * lanes * kQ <= kMergeBalancedThreads) lanes *= 2;
+  int hb = kMergeBalancedThreads / (kQ * lanes);
+  if (hb > a.group) hb = a.group;
+  if (hb < 1) hb = 1;
+  a.merge_lanes = lanes;
+  a.merge_heads = hb;
+  hipLaunchKernelGGL((attn_merge_balanced_kernel<O, D>),
+                     dim3((a.group + hb - 1) / hb, num_seqs * a.num_kv_heads),
+                     dim3(hb * kQ * lanes), 0, st, a);
+}
+
+// The matrix-core balanced kernel of a cache kind, streaming or cacheable
+// K/V loads.
+const void* mfma_balanced_kernel_of(int kind, bool stream) {
+  if (kind == pkv::mfma::kFp8)
+    return stream ? reinterpret_cast<const void*>(&attn_mfma_balanced_kernel<pkv::mfma::kFp8, true>)
+                  : reinterpret_cast<const void*>(&attn_mfma_balanced_kernel<pkv::mfma::kFp8, false>);
+  if (kind == pkv::mfma::kInt8)
+    return stream ? reinterpret_cast<const void*>(&attn_mfma_balanced_kernel<pkv::mfma::kInt8, true>)
+                  : reinterpret_cast<const void*>(&attn_mfma_balanced_kernel<pkv::mfma::kInt8, false>);
+  return stream ? reinterpret_cast<const void*>(&attn_mfma_balanced_kernel<pkv::mfma::kBf16, true>)
+                : reinterpret_cast<const void*>(&attn_mfma_balanced_kernel<pkv::mfma::kBf16, false>);
+}
+
+void launch_mfma_balanced(int kind, bool stream, int grid, size_t lds, hipStream_t st,
+                          const AttnArgs& a) {
+  if (kind == pkv::mfma::kFp8) {
+    if (stream) hipLaunchKernelGGL((attn_mfma_balanced_kernel<pkv::mfma::kFp8, true>), dim3(grid), dim3(64), lds, st, a);
+    else hipLaunchKernelGGL((attn_mfma_balanced_kernel<pkv::mfma::kFp8, false>), dim3(grid), dim3(64), lds, st, a);
+  } else if (kind == pkv::mfma::kInt8) {
+    if (stream) hipLaunchKernelGGL((attn_mfma_balanced_kernel<pkv::mfma::kInt8, true>), dim3(grid), dim3(64), lds, st, a);
+    else hipLaunchKernelGGL((attn_mfma_balanced_kernel<pkv::mfma::kInt8, false>), dim3(grid), dim3(64), lds, st, a);
+  } else {
+    if (stream) hipLaunchKernelGGL((attn_mfma_balanced_kernel<pkv::mfma::kBf16, true>), dim3(grid), dim3(64), lds, st, a);
+    else hipLaunchKernelGGL((attn_mfma_balanced_kernel<pkv::mfma::kBf16, false>), dim3(grid), dim3(64), lds, st, a);
+  }
 }
 
 template <typename T, int D, int GW, int P, bool kAppend, bool kStream = true>
@@ -1286,21 +1479,7 @@ pkv_status dispatch_gw(int phases, const Plan& pl, AttnArgs& a, int num_seqs, in
   }
   if (phases & 2) {
     if (pl.mode == kBalancedMode) {
-      // piece lanes from the average pieces per stream (intervals plus
-      // streams over streams): about two batches' worth per lane group, so
-      // most streams take one round trip, without idle lanes on batches
-      // whose streams are cut into a few pieces only
-      const int hb = merge_heads_per_block(a.group, D);
-      const int cols = hb * (D / 4);
-      const int64_t streams = int64_t(num_seqs) * a.num_kv_heads;
-      const int64_t chunks = pl.max_chunks < a.num_groups ? pl.max_chunks : a.num_groups;
-      const int64_t avg = (a.num_groups + chunks + streams + streams - 1) / streams;
-      int lanes = 1;
-      while (lanes * kMergeBatch < 2 * avg && 2 * lanes * cols <= kMergeBalancedThreads) lanes *= 2;
-      a.merge_lanes = lanes;
-      hipLaunchKernelGGL((attn_merge_balanced_kernel<OutT<T>, D>),
-                         dim3((a.group + hb - 1) / hb, num_seqs * a.num_kv_heads),
-                         dim3(cols * lanes), 0, st, a);
+      launch_balanced_merge<OutT<T>, D>(pl, a, num_seqs, st);
     } else if (pl.num_parts > 1) {
       hipLaunchKernelGGL((attn_merge_kernel<OutT<T>, D>), dim3(num_q_heads, num_seqs),
                          dim3(kMergeThreads), 0, st, a);
@@ -1345,7 +1524,8 @@ bool streams_kv(const Plan& pl, bool kv_shared) {
 // only where the kernel streams K/V: the cacheable-load kernels are built
 // without the folded store.
 bool folds_append(const Plan& pl, bool kv_shared) {
-  if (!streams_kv(pl, kv_shared) || pl.mode == kMatrixMode) return false;
+  if (!streams_kv(pl, kv_shared) || pl.mode == kMatrixMode || pl.mode == kMatrixBalancedMode)
+    return false;
   const int ka = knob_append();
   return ka ? ka == 2 : pl.gw <= 2;
 }
@@ -1360,7 +1540,7 @@ int32_t pkv_attention_partition_tokens(int32_t num_seqs, int32_t num_q_heads,
   if (make_plan(num_seqs, num_q_heads, max_seq_len, max_blocks, 0, geom,
                 "pkv_attention_partition_tokens", &pl) != PKV_OK)
     return 0;
-  if (pl.mode == kBalancedMode)  // the split is by shares, not by partitions
+  if (pl.mode == kBalancedMode || pl.mode == kMatrixBalancedMode)  // shares, not partitions
     return 0;
   return pl.part_tokens;
 }
@@ -1373,7 +1553,7 @@ int32_t pkv_attention_piece_tokens(int32_t num_seqs, int32_t num_q_heads, int32_
   if (make_plan(num_seqs, num_q_heads, max_seq_len, max_blocks, partition_tokens, geom,
                 "pkv_attention_piece_tokens", &pl) != PKV_OK)
     return 0;
-  if (pl.mode == kBalancedMode) return 0;
+  if (pl.mode == kBalancedMode || pl.mode == kMatrixBalancedMode) return 0;
   if (pl.mode == kMatrixMode) return pl.runs.run_tokens;
   return pl.part_tokens;
 }
@@ -1386,8 +1566,10 @@ int32_t pkv_attention_decode_route(int32_t num_seqs, int32_t num_q_heads, int32_
   if (make_plan(num_seqs, num_q_heads, max_seq_len, max_blocks, partition_tokens, geom,
                 "pkv_attention_decode_route", &pl) != PKV_OK)
     return -1;
-  return pl.mode == kMatrixMode ? PKV_ROUTE_MATRIX
-         : pl.mode == kBalancedMode ? PKV_ROUTE_BALANCED : PKV_ROUTE_PARTITIONS;
+  return pl.mode == kMatrixMode           ? PKV_ROUTE_MATRIX
+         : pl.mode == kMatrixBalancedMode ? PKV_ROUTE_MATRIX_BALANCED
+         : pl.mode == kBalancedMode       ? PKV_ROUTE_BALANCED
+                                          : PKV_ROUTE_PARTITIONS;
 }
 
 int32_t pkv_attention_decode_append_folded(int32_t num_seqs, int32_t num_q_heads,
@@ -1493,7 +1675,7 @@ pkv_status attention_impl(const char* who, int32_t phases, const void* q, const 
   char* ws = static_cast<char*>(workspace);
   a.ws_acc = pl.ws_bytes ? reinterpret_cast<float*>(ws) : nullptr;
   a.ws_ml = pl.ws_bytes ? reinterpret_cast<float2*>(ws + pl.ws_ml_off) : nullptr;
-  a.ws_span = (pl.ws_bytes && pl.mode == kBalancedMode)
+  a.ws_span = (pl.ws_bytes && (pl.mode == kBalancedMode || pl.mode == kMatrixBalancedMode))
                   ? reinterpret_cast<int32_t*>(ws + pl.ws_span_off)
                   : nullptr;
   a.row_bytes = geom->num_kv_heads * geom->head_dim * es;
@@ -1536,6 +1718,26 @@ pkv_status attention_impl(const char* who, int32_t phases, const void* q, const 
                        int64_t(geom->num_blocks) * geom->block_size, pl.len_cap);
     if (hipError_t e = hipGetLastError())
       return pkv::fail(PKV_ERR_HIP, "%s: append launch failed: %s", who, hipGetErrorString(e));
+  }
+  if (pl.mode == kMatrixBalancedMode) {
+    const int kind = geom->dtype == PKV_FP8_E4M3 ? pkv::mfma::kFp8
+                     : (geom->dtype == PKV_INT8 ? pkv::mfma::kInt8 : pkv::mfma::kBf16);
+    const size_t lds = size_t(num_seqs + 1) * sizeof(int32_t);
+    const void* kern = mfma_balanced_kernel_of(kind, a.stream_kv != 0);
+    int blocks = resident_blocks(kern, 64, lds);
+    if (blocks <= 0)
+      return pkv::fail(PKV_ERR_HIP, "%s: occupancy query failed", who);
+    if (blocks > kMaxWaveGroups) blocks = kMaxWaveGroups;
+    a.num_groups = blocks;
+    a.static_blocks = blocks;
+    if (phases & 1) {
+      const int chunks = pl.max_chunks < a.num_groups ? pl.max_chunks : a.num_groups;
+      launch_mfma_balanced(kind, a.stream_kv != 0, blocks + chunks, lds, st, a);
+    }
+    if (phases & 2) launch_balanced_merge<uint16_t, 128>(pl, a, num_seqs, st);
+    if (hipError_t e = hipGetLastError())
+      return pkv::fail(PKV_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+    return PKV_OK;
   }
   if (pl.mode == kMatrixMode) {
     if (phases & 1) {

@@ -138,7 +138,8 @@ __device__ __forceinline__ void decode_codes(const uint4& x, float (&f)[16]) {
 
 // Two floats that bf16 holds exactly (decoded codes) -> one bf16 pair.
 __device__ __forceinline__ uint32_t bf16_pair_exact(float lo, float hi) {
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+  // the high halves of both words in one byte permute (v_perm_b32)
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
 // A row's running state in log2 units: reference m, sum of weights lsum, and

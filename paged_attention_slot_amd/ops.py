@@ -131,7 +131,7 @@ def piece_tokens(num_seqs: int, num_q_heads: int, max_seq_len: int, k_cache,
                                                 int(partition_tokens), ctypes.byref(g)))
 
 
-ROUTES = {0: "partitions", 1: "balanced", 2: "matrix"}
+ROUTES = {0: "partitions", 1: "balanced", 2: "matrix", 3: "matrix-balanced"}
 
 
 def decode_route(num_seqs: int, num_q_heads: int, max_seq_len: int, k_cache,

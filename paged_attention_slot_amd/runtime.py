@@ -306,8 +306,8 @@ class DecodeStep:
         which folds its positions into one piece."""
         route = ops.decode_route(self.wl.num_seqs, self.wl.num_q_heads, self.max_seq_len,
                                  self.k_caches[0], self.partition_tokens)
-        if route == "balanced":
-            return {"mode": "balanced"}
+        if route in ("balanced", "matrix-balanced"):
+            return {"mode": route}
         pt = self.partition_tokens or ops.partition_tokens(
             self.wl.num_seqs, self.wl.num_q_heads, self.max_seq_len, self.k_caches[0])
         split = {"mode": "matrix" if route == "matrix" else "partitions", "partition_tokens": pt,

@@ -359,6 +359,36 @@ def test_modes_match_oracle(mode_env, mode, dtype, B, D, Hq, Hkv):
     assert_gate(gpu_out(step), ref, dtype, f"mode {mode}")
 
 
+MBAL = [  # B, Hq, Hkv
+    (16, 16, 8), (16, 32, 8), (32, 64, 8), (8, 32, 2), (16, 128, 8), (64, 24, 4),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv", MBAL, ids=lambda v: str(v))
+def test_matrix_balanced_route_matches_oracle(mode_env, B, Hq, Hkv):
+    """The balanced split on the matrix cores (PKV_ATTN_MODE=4; the default
+    for one-byte pools with 2-7 heads per group) on bf16 pools: ragged
+    lengths from 1 to a few thousand (streams cut by many intervals, streams
+    inside one), every element against the oracle; then the two phases in
+    separate calls give the same bits."""
+    mode_env(4)
+    lens = [1, 2, 31, 32, 33, 100, 257, 600, 1000, 2500, 4100, 17]
+    wl = independent_workload(lens, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128,
+                              block_size=B, dtype="bf16", seed=90 + B + Hq)
+    step, ost = run_both(wl)
+    say(f"  split {step.split}")
+    assert step.split["mode"] == "matrix-balanced"
+    ref = oracle_attention(wl.q, ost.k_pool, ost.v_pool, ost.block_tables, ost.seq_lens,
+                           wl.scale)
+    one = host_bits(step.out)
+    say("  gate", assert_gate(to_f64(one), ref, "bf16", "matrix-balanced"))
+    out = torch.empty_like(step.q)
+    step.attention(out=out, phases=1)
+    step.attention(out=out, phases=2)
+    torch.cuda.synchronize()
+    assert np.array_equal(one, host_bits(out))
+
+
 def test_balanced_stream_across_more_than_1024_shares(mode_env):
     """One long sequence and one KV head: every wave group holds a piece of the
     same stream, so the merge folds more than 1024 pieces."""

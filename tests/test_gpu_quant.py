@@ -85,12 +85,13 @@ def test_small_write_and_attention(kind, B, D, Hq, Hkv):
 
 
 @pytest.mark.parametrize("kind", KINDS)
-@pytest.mark.parametrize("mode", [1, 2], ids=["partitions", "balanced"])
+@pytest.mark.parametrize("mode", [1, 2, 4], ids=["partitions", "balanced", "matrix-balanced"])
 def test_modes_and_splits(kind, mode, tuning):
     tuning("PKV_ATTN_MODE", mode)
     wl = independent_workload([1, 2, 15, 16, 17, 31, 100, 256, 257, 600, 1000], num_q_heads=32,
                               num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16", seed=41)
-    step, ost = run_both(wl, kind, partition_tokens=0 if mode == 2 else 64)
+    step, ost = run_both(wl, kind, partition_tokens=64 if mode == 1 else 0)
+    say(f"  split {step.split}")
     assert_gate(gpu_out(step), ost.attention(), "bf16", f"{kind} mode {mode}")
 
 

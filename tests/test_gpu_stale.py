@@ -98,6 +98,8 @@ ROUTES = [  # id, Hq, Hkv, D, B, dtype, mode env, forks, fused
     ("balanced-bf16-forks-cacheable", 32, 8, 128, 16, "bf16", "2", True, True),
     ("partitions-f32-forks", 8, 2, 64, 8, "f32", "1", True, False),
     ("matrix-bf16", 64, 8, 128, 16, "bf16", None, False, False),
+    ("matrix-balanced-bf16", 32, 8, 128, 16, "bf16", "4", False, True),
+    ("matrix-balanced-bf16-forks", 16, 8, 128, 32, "bf16", "4", True, False),
     ("matrix-bf16-B32-forks", 64, 8, 128, 32, "bf16", None, True, True),
 ]
 

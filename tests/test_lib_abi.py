@@ -377,6 +377,13 @@ def test_decode_route_query():
     assert route(4, 64, 8, 64, _lib.PKV_BF16) == B
     assert route(4, 64, 8, 128, _lib.PKV_F32) == B
     assert route(4, 63, 8, 128, _lib.PKV_BF16) == -1
+    # one-byte pools with 2-7 heads per group: the balanced split on the
+    # matrix cores (automatic partitions only)
+    MB = _lib.PKV_ROUTE_MATRIX_BALANCED
+    assert route(256, 32, 8, 128, _lib.PKV_FP8_E4M3) == MB
+    assert route(64, 16, 8, 128, _lib.PKV_INT8) == MB
+    assert route(64, 16, 8, 128, _lib.PKV_INT8, pt=256) == P
+    assert route(64, 8, 8, 128, _lib.PKV_FP8_E4M3) == B     # one head per group
     # the workspace of the matrix route: N * Hq * runs rows of D + 2 floats.
     # 256 partitions of 512 over 32 (sequence, KV head) histories are more
     # than the GPU holds at once: 96 equal shares of 1376 positions each
@@ -421,7 +428,7 @@ def test_tuning_knobs_read_once_and_set_through_the_abi(tuning):
     tuning("PKV_ATTN_MODE", 1)
     assert lib.pkv_get_tuning(b"PKV_ATTN_MODE") == 1
     assert lib.pkv_attention_decode_route(64, 16, 4096, 0, geo) == _lib.PKV_ROUTE_PARTITIONS
-    assert lib.pkv_set_tuning(b"PKV_ATTN_MODE", 4) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_set_tuning(b"PKV_ATTN_MODE", 5) == _lib.PKV_ERR_INVALID_ARG
     assert lib.pkv_set_tuning(b"PKV_ATTN_WAVES_PER_BLOCK", 3) == _lib.PKV_ERR_INVALID_ARG
     assert lib.pkv_set_tuning(b"PKV_NOT_A_KNOB", 1) == _lib.PKV_ERR_INVALID_ARG
     assert lib.pkv_get_tuning(b"PKV_NOT_A_KNOB") == -1
