@@ -301,11 +301,11 @@ int32_t pkv_attention_piece_tokens(int32_t num_seqs, int32_t num_q_heads, int32_
  * PKV_ROUTE_MATRIX (groups of 8 or more query heads per KV head at head_dim
  * 128, bf16 or one-byte pools, partition_tokens 0 or a multiple of 32: the
  * matrix-core pass of pkv_attention_multi with one query per sequence, fixed
- * partitions merged by log-sum-exp) or PKV_ROUTE_MATRIX_BALANCED (one-byte
- * pools with 2 to 7 query heads per KV head, partition_tokens 0: the balanced
- * split's intervals walked by one-wave workgroups on the matrix cores, the
- * group's heads as the rows of the products).  PKV_ATTN_MODE overrides.  -1
- * on invalid arguments. */
+ * partitions merged by log-sum-exp) or PKV_ROUTE_MATRIX_BALANCED (2 to 7
+ * query heads per KV head at head_dim 128, bf16 or one-byte pools,
+ * partition_tokens 0: the balanced split's intervals walked by one-wave
+ * workgroups on the matrix cores, the group's heads as the rows of the
+ * products).  PKV_ATTN_MODE overrides.  -1 on invalid arguments. */
 enum { PKV_ROUTE_PARTITIONS = 0, PKV_ROUTE_BALANCED = 1, PKV_ROUTE_MATRIX = 2,
        PKV_ROUTE_MATRIX_BALANCED = 3 };
 int32_t pkv_attention_decode_route(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
@@ -352,7 +352,12 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *                 share of 85 % of all K/V tiles of the batch, and further
  *                 workgroups, dispatched as those retire, take small chunks of
  *                 the rest; a sequence's history that spans several of these
- *                 intervals is merged the same way.  Groups of 8 or more
+ *                 intervals is merged the same way.  With 2 to 7 query heads
+ *                 per KV head at head_dim 128 (bf16 or one-byte pools) the
+ *                 intervals (of 32-position tiles) are walked on the matrix
+ *                 cores, the group's heads as the rows of the products; with
+ *                 one head per group, head_dim 64 or fp32 pools, on the
+ *                 vector units.  Groups of 8 or more
  *                 query heads per KV head (head_dim 128) run on the matrix
  *                 cores instead, with fixed partitions (a multiple of 32;
  *                 automatic: about 3072 (sequence, KV head, partition) items
@@ -438,10 +443,11 @@ pkv_status pkv_attention_decode_phase(int32_t phases, const void* q, const void*
  * (its table entry for block (L_s - 1) / block_size at offset
  * (L_s - 1) % block_size, as the block manager hands it out) the result is
  * exactly pkv_write(k_new, v_new, slot_mapping, num_seqs, ...) followed by
- * pkv_attention_decode_phase(phases, ...).  For waves of up to two query heads
+ * pkv_attention_decode_phase(phases, ...).  On the balanced split on the
+ * matrix cores, and on the vector kernels for waves of up to two query heads,
  * the attention kernel does the append itself: the wave that attends position
  * L_s - 1 takes its K/V from the new-token rows and stores them to the slot;
- * with more heads per wave a copy kernel runs first.
+ * elsewhere a copy kernel runs first.
  *   k_new, v_new  device [num_seqs][num_kv_heads][head_dim], pool dtype.
  *   slot_mapping  device int32 [num_seqs].
  *   k_cache, v_cache  modified in place at those slots only.

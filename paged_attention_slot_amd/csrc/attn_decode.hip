@@ -993,8 +993,11 @@ __device__ __forceinline__ int stream_tiles32(const AttnArgs& a, int s) {
 }
 
 // grid = static workgroups (the resident ones) + dynamic chunks, 64 threads;
-// dynamic LDS: (num_seqs + 1) int32 prefix sums.
-template <int Q, bool kStream>
+// dynamic LDS: (num_seqs + 1) int32 prefix sums.  kAppend (bf16): the step's
+// append folded in, as on the vector kernels: the wave walking a stream's last
+// tile reads the newest position from the new-token rows and stores it to its
+// slot.
+template <int Q, bool kStream, bool kAppend = false>
 __global__ void __launch_bounds__(64)
 attn_mfma_balanced_kernel(AttnArgs a) {
   constexpr int D = 128;
@@ -1058,7 +1061,21 @@ attn_mfma_balanced_kernel(AttnArgs a) {
     const int kvh = rel / nt;
     const int t0 = rel - kvh * nt;
     const int seg = static_cast<int>(min(hi - cur, int64_t(nt - t0)));
-    const int L = clamp_len(a.seq_lens[s], a.len_cap);
+    const int Lraw = a.seq_lens[s];
+    const int L = clamp_len(Lraw, a.len_cap);
+    pkv::mfma::NewRow nr{nullptr, nullptr, nullptr, nullptr, -1};
+    if constexpr (kAppend) {
+      // the stream's last tile holds the new token; a slot outside the pool
+      // is not written, and that position is then read from the pool
+      const int slot = a.new_slots[s];
+      if (t0 + seg == nt && L == Lraw && slot >= 0 &&
+          int64_t(slot) < (int64_t(a.num_blocks) << a.block_shift)) {
+        const int64_t row = (int64_t(s) * Hkv + kvh) * D;
+        const int64_t dst = int64_t(slot) * (a.row_bytes / 2) + int64_t(kvh) * D;
+        nr = {static_cast<const uint16_t*>(a.k_new) + row, static_cast<const uint16_t*>(a.v_new) + row,
+              static_cast<uint16_t*>(a.k_dst) + dst, static_cast<uint16_t*>(a.v_dst) + dst, L - 1};
+      }
+    }
     const pkv::mfma::History hist{a.k_cache,      a.v_cache,    a.block_tables + int64_t(s) * a.max_blocks,
                                   L,              kvh,          a.block_bytes / kEB,
                                   a.row_bytes / kEB, a.num_blocks, a.block_shift,
@@ -1070,9 +1087,9 @@ attn_mfma_balanced_kernel(AttnArgs a) {
     // one-byte tiles are half the registers: two in flight ahead of the one
     // being computed, at the same occupancy
     constexpr int kPD = Q == pkv::mfma::kBf16 ? 1 : 2;
-    pkv::mfma::attend<D, 1, kPD, Q, kStream>(hist, t0 * kMT, min((t0 + seg) * kMT, L),
-                                             q + qh * D, row_ok, L - 1, L - 1, scale_log2, k_lds,
-                                             v_lds, r, s_lds);
+    pkv::mfma::attend<D, 1, kPD, Q, kStream, pkv::mfma::NoEmit, kAppend>(
+        hist, t0 * kMT, min((t0 + seg) * kMT, L), q + qh * D, row_ok, L - 1, L - 1, scale_log2,
+        k_lds, v_lds, r, s_lds, 0, pkv::mfma::NoEmit(), nr);
     const int64_t k = int64_t(s) * Hkv + kvh;
     if (lane == 0) {  // the stream's first and last intervals, for the merge
       if (t0 == 0) a.ws_span[2 * k] = iv;
@@ -1199,12 +1216,16 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
   // for 16 heads at once and keeps only the softmax on the vector units.
   const bool matrix_ok = g->head_dim == 128 && (g->dtype == PKV_BF16 || pkv::is_quant(g->dtype)) &&
                          partition_tokens % 32 == 0 && g->num_kv_heads <= 65535;
-  // One-byte codes with 2 to 7 query heads per KV head: the balanced split on
-  // the matrix cores (the vector kernels are issue-bound decoding the codes).
+  // 2 to 7 query heads per KV head (head_dim 128, bf16 or one-byte codes):
+  // the balanced split on the matrix cores.  For one-byte codes the vector
+  // kernels are issue-bound decoding the codes; for bf16 the matrix cores
+  // match them on unshared batches (the llama3-8b layer: 718 against 720 us,
+  // the qwen layer: 91.7 against 95.4 us) and beat them where blocks are
+  // shared (the shared-prefix config: 153.5 against 177.0 us).
   const int64_t tiles32_max = (int64_t(pl->len_cap) + 31) / 32;
   const bool mbal_ok = matrix_ok && partition_tokens == 0 && num_seqs <= kMaxBalancedSeqs &&
                        G <= 16 && int64_t(num_seqs) * g->num_kv_heads * tiles32_max < (int64_t(1) << 31);
-  if (mbal_ok && (km == 4 || (km == 0 && pkv::is_quant(g->dtype) && G >= 2 && G < 8))) {
+  if (mbal_ok && (km == 4 || (km == 0 && G >= 2 && G < 8))) {
     pl->mode = kMatrixBalancedMode;
     pl->gw = G;
     pl->waves_per_group = 1;
@@ -1358,29 +1379,44 @@ void launch_balanced_merge(const Plan& pl, AttnArgs& a, int num_seqs, hipStream_
 }
 
 // The matrix-core balanced kernel of a cache kind, streaming or cacheable
-// K/V loads.
-const void* mfma_balanced_kernel_of(int kind, bool stream) {
-  if (kind == pkv::mfma::kFp8)
-    return stream ? reinterpret_cast<const void*>(&attn_mfma_balanced_kernel<pkv::mfma::kFp8, true>)
-                  : reinterpret_cast<const void*>(&attn_mfma_balanced_kernel<pkv::mfma::kFp8, false>);
-  if (kind == pkv::mfma::kInt8)
-    return stream ? reinterpret_cast<const void*>(&attn_mfma_balanced_kernel<pkv::mfma::kInt8, true>)
-                  : reinterpret_cast<const void*>(&attn_mfma_balanced_kernel<pkv::mfma::kInt8, false>);
-  return stream ? reinterpret_cast<const void*>(&attn_mfma_balanced_kernel<pkv::mfma::kBf16, true>)
-                : reinterpret_cast<const void*>(&attn_mfma_balanced_kernel<pkv::mfma::kBf16, false>);
+// K/V loads, with the append folded in (bf16 only) or not.
+template <int Q, bool kStream, bool kAppend>
+const void* mbal_ptr() {
+  return reinterpret_cast<const void*>(&attn_mfma_balanced_kernel<Q, kStream, kAppend>);
 }
 
-void launch_mfma_balanced(int kind, bool stream, int grid, size_t lds, hipStream_t st,
-                          const AttnArgs& a) {
-  if (kind == pkv::mfma::kFp8) {
-    if (stream) hipLaunchKernelGGL((attn_mfma_balanced_kernel<pkv::mfma::kFp8, true>), dim3(grid), dim3(64), lds, st, a);
-    else hipLaunchKernelGGL((attn_mfma_balanced_kernel<pkv::mfma::kFp8, false>), dim3(grid), dim3(64), lds, st, a);
+const void* mfma_balanced_kernel_of(int kind, bool stream, bool append) {
+  using pkv::mfma::kBf16;
+  using pkv::mfma::kFp8;
+  if (kind == kFp8) return stream ? mbal_ptr<kFp8, true, false>() : mbal_ptr<kFp8, false, false>();
+  if (kind == pkv::mfma::kInt8)
+    return stream ? mbal_ptr<pkv::mfma::kInt8, true, false>() : mbal_ptr<pkv::mfma::kInt8, false, false>();
+  if (append) return stream ? mbal_ptr<kBf16, true, true>() : mbal_ptr<kBf16, false, true>();
+  return stream ? mbal_ptr<kBf16, true, false>() : mbal_ptr<kBf16, false, false>();
+}
+
+template <int Q, bool kStream, bool kAppend>
+void launch_mbal(int grid, size_t lds, hipStream_t st, const AttnArgs& a) {
+  hipLaunchKernelGGL((attn_mfma_balanced_kernel<Q, kStream, kAppend>), dim3(grid), dim3(64), lds,
+                     st, a);
+}
+
+void launch_mfma_balanced(int kind, bool stream, bool append, int grid, size_t lds,
+                          hipStream_t st, const AttnArgs& a) {
+  using pkv::mfma::kBf16;
+  using pkv::mfma::kFp8;
+  if (kind == kFp8) {
+    if (stream) launch_mbal<kFp8, true, false>(grid, lds, st, a);
+    else launch_mbal<kFp8, false, false>(grid, lds, st, a);
   } else if (kind == pkv::mfma::kInt8) {
-    if (stream) hipLaunchKernelGGL((attn_mfma_balanced_kernel<pkv::mfma::kInt8, true>), dim3(grid), dim3(64), lds, st, a);
-    else hipLaunchKernelGGL((attn_mfma_balanced_kernel<pkv::mfma::kInt8, false>), dim3(grid), dim3(64), lds, st, a);
+    if (stream) launch_mbal<pkv::mfma::kInt8, true, false>(grid, lds, st, a);
+    else launch_mbal<pkv::mfma::kInt8, false, false>(grid, lds, st, a);
+  } else if (append) {
+    if (stream) launch_mbal<kBf16, true, true>(grid, lds, st, a);
+    else launch_mbal<kBf16, false, true>(grid, lds, st, a);
   } else {
-    if (stream) hipLaunchKernelGGL((attn_mfma_balanced_kernel<pkv::mfma::kBf16, true>), dim3(grid), dim3(64), lds, st, a);
-    else hipLaunchKernelGGL((attn_mfma_balanced_kernel<pkv::mfma::kBf16, false>), dim3(grid), dim3(64), lds, st, a);
+    if (stream) launch_mbal<kBf16, true, false>(grid, lds, st, a);
+    else launch_mbal<kBf16, false, false>(grid, lds, st, a);
   }
 }
 
@@ -1524,8 +1560,8 @@ bool streams_kv(const Plan& pl, bool kv_shared) {
 // only where the kernel streams K/V: the cacheable-load kernels are built
 // without the folded store.
 bool folds_append(const Plan& pl, bool kv_shared) {
-  if (!streams_kv(pl, kv_shared) || pl.mode == kMatrixMode || pl.mode == kMatrixBalancedMode)
-    return false;
+  if (pl.mode == kMatrixBalancedMode) return knob_append() != 1;  // bf16: folded unless asked
+  if (!streams_kv(pl, kv_shared) || pl.mode == kMatrixMode) return false;
   const int ka = knob_append();
   return ka ? ka == 2 : pl.gw <= 2;
 }
@@ -1723,7 +1759,8 @@ pkv_status attention_impl(const char* who, int32_t phases, const void* q, const 
     const int kind = geom->dtype == PKV_FP8_E4M3 ? pkv::mfma::kFp8
                      : (geom->dtype == PKV_INT8 ? pkv::mfma::kInt8 : pkv::mfma::kBf16);
     const size_t lds = size_t(num_seqs + 1) * sizeof(int32_t);
-    const void* kern = mfma_balanced_kernel_of(kind, a.stream_kv != 0);
+    const bool folded = a.k_new != nullptr;
+    const void* kern = mfma_balanced_kernel_of(kind, a.stream_kv != 0, folded);
     int blocks = resident_blocks(kern, 64, lds);
     if (blocks <= 0)
       return pkv::fail(PKV_ERR_HIP, "%s: occupancy query failed", who);
@@ -1732,7 +1769,7 @@ pkv_status attention_impl(const char* who, int32_t phases, const void* q, const 
     a.static_blocks = blocks;
     if (phases & 1) {
       const int chunks = pl.max_chunks < a.num_groups ? pl.max_chunks : a.num_groups;
-      launch_mfma_balanced(kind, a.stream_kv != 0, blocks + chunks, lds, st, a);
+      launch_mfma_balanced(kind, a.stream_kv != 0, folded, blocks + chunks, lds, st, a);
     }
     if (phases & 2) launch_balanced_merge<uint16_t, 128>(pl, a, num_seqs, st);
     if (hipError_t e = hipGetLastError())

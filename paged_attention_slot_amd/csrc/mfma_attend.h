@@ -190,12 +190,27 @@ struct NoEmit {
   template <class R> __device__ void operator()(int, R&) const {}
 };
 
-template <int D, int NW, int PD = 1, int Q = kBf16, bool kStream = false, class Emit = NoEmit>
+// The step's append folded into the pass (bf16 pools; kAppend): position
+// ``pos`` of the history is the new token, whose K/V row for this KV head is
+// read from ``k``/``v`` (D bf16 each) instead of the pools, and stored to the
+// pools at ``k_dst``/``v_dst`` (the row of its slot for this KV head) when
+// its tile is staged.  pos < 0: nothing to do.
+struct NewRow {
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* k_dst;
+  uint16_t* v_dst;
+  int pos;
+};
+
+template <int D, int NW, int PD = 1, int Q = kBf16, bool kStream = false, class Emit = NoEmit,
+          bool kAppend = false>
 __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, const uint16_t* q,
                                        bool row_ok, int p_row, int p_all, float scale_log2,
                                        uint16_t* k_lds, uint16_t* v_lds, RowAcc<D>& r,
                                        float* s_lds = nullptr, int seg = 0,
-                                       const Emit& emit = Emit()) {
+                                       const Emit& emit = Emit(), const NewRow& nr = NewRow()) {
+  static_assert(!kAppend || Q == kBf16, "the folded append takes bf16 pools");
   constexpr float kSlack = 8.0f;
   constexpr bool kLazy = NW == 1;
   constexpr int kEB = Q == kBf16 ? 2 : 1;   // bytes per element
@@ -275,7 +290,21 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
     const char* kb = static_cast<const char*>(h.k_cache) + off0;
     const char* vb = static_cast<const char*>(h.v_cache) + off0;
     const int64_t rstep = int64_t(h.row_elems) * kEB;
-    if (t0 + kKT <= L) {  // uniform: the whole tile is history
+    if (kAppend && nr.pos >= t0 && nr.pos < t0 + kKT) {  // uniform: the tile holds the new token
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const bool fresh = p0 + i == nr.pos;
+        nk[j][i] = make_uint4(0, 0, 0, 0);
+        nv[j][i] = make_uint4(0, 0, 0, 0);
+        if (fresh) {
+          nk[j][i] = kv_load(reinterpret_cast<const char*>(nr.k + cc * kEPC));
+          nv[j][i] = kv_load(reinterpret_cast<const char*>(nr.v + cc * kEPC));
+        } else if (p0 + i < L) {
+          nk[j][i] = kv_load(kb + i * rstep);
+          nv[j][i] = kv_load(vb + i * rstep);
+        }
+      }
+    } else if (t0 + kKT <= L) {  // uniform: the whole tile is history
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         nk[j][i] = kv_load(kb + i * rstep);
@@ -310,7 +339,7 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
   // Stage the tile of buffer j: K and V as [pos][d] bf16 (codes decoded).
   constexpr int kTileElems = kKT * kKStride;   // one LDS tile buffer of K
   constexpr int kVTileElems = kKT * kVStride;  // and of V
-  auto stage = [&](int j, int buf) {
+  auto stage = [&](int j, int buf, int t0) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int off = buf * kTileElems + (pg * kPer + i) * kKStride + cc * kEPC;
@@ -318,6 +347,14 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
       if constexpr (Q == kBf16) {
         *reinterpret_cast<uint4*>(k_lds + off) = nk[j][i];
         *reinterpret_cast<uint4*>(v_lds + voff) = nv[j][i];
+        if constexpr (kAppend) {
+          // the new token's chunk goes to its slot as well (the loads that
+          // read it have completed: its value was just staged)
+          if (t0 + pg * kPer + i == nr.pos) {
+            *reinterpret_cast<uint4*>(nr.k_dst + cc * kEPC) = nk[j][i];
+            *reinterpret_cast<uint4*>(nr.v_dst + cc * kEPC) = nv[j][i];
+          }
+        }
       } else if constexpr (Q == kFp8) {
         // code pairs straight to bf16 pairs (packed conversion)
         const uint32_t kw[4] = {nk[j][i].x, nk[j][i].y, nk[j][i].z, nk[j][i].w};
@@ -481,7 +518,7 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
     for (int j = 0; j < PD; ++j) {
       const int t = t0 + j * kKT;
       if (t >= t_hi) break;  // uniform
-      stage(j, buf);
+      stage(j, buf, t);
       lds_barrier();
       // the register buffer just staged takes the tile PD ahead, in flight
       // meanwhile

@@ -327,9 +327,10 @@ def test_fused_append_entry_point_validates_on_the_host():
 
 def test_append_fold_query(tuning):
     """pkv_attention_decode_append_folded: the append rides in the attention
-    kernel on the vector routes for waves of up to two query heads, not on
-    batches that share blocks or whose query groups span several waves (both
-    keep cacheable loads), not on the matrix route; one-byte pools give -1
+    kernel on the balanced split on the matrix cores, and on the vector routes
+    for waves of up to two query heads, not on vector batches that share
+    blocks or whose query groups span several waves (both keep cacheable
+    loads), not on the matrix route with partitions; one-byte pools give -1
     (the fused append refuses them)."""
     tuning("PKV_ATTN_APPEND", 0)
     tuning("PKV_ATTN_MODE", 0)
@@ -340,19 +341,22 @@ def test_append_fold_query(tuning):
         return lib.pkv_attention_decode_append_folded(
             N, Hq, maxlen, pt, shared, ctypes.byref(g(nb=8192, H=H, D=D, dt=dt)))
 
-    assert folded(64, 16, 8, 128, _lib.PKV_BF16) == 1          # 2 heads per wave
-    assert folded(64, 16, 8, 128, _lib.PKV_BF16, shared=1) == 0
-    assert folded(64, 16, 8, 128, _lib.PKV_BF16, pt=256) == 1  # fixed partitions
+    assert folded(64, 16, 8, 128, _lib.PKV_BF16) == 1          # matrix-core balanced split
+    assert folded(64, 16, 8, 128, _lib.PKV_BF16, shared=1) == 1
+    assert folded(64, 32, 8, 128, _lib.PKV_BF16) == 1
+    assert folded(64, 16, 8, 128, _lib.PKV_BF16, pt=256) == 1  # fixed partitions, 2 heads per wave
+    assert folded(64, 32, 8, 128, _lib.PKV_BF16, pt=256) == 0  # 4 heads per wave
+    assert folded(64, 16, 8, 64, _lib.PKV_BF16, shared=1) == 0  # vector kernels, cacheable loads
     assert folded(64, 8, 8, 128, _lib.PKV_F32) == 1            # 1 head per wave
     assert folded(64, 16, 8, 128, _lib.PKV_F32) == 0           # group split over 2 waves
-    assert folded(64, 32, 8, 128, _lib.PKV_BF16) == 0          # 4 heads per wave
     assert folded(4, 64, 8, 128, _lib.PKV_BF16) == 0           # matrix route
     assert folded(4, 64, 8, 128, _lib.PKV_FP8_E4M3) == -1
     assert folded(4, 63, 8, 128, _lib.PKV_BF16) == -1
     tuning("PKV_ATTN_APPEND", 2)
-    assert folded(64, 32, 8, 128, _lib.PKV_BF16) == 1
+    assert folded(64, 32, 8, 128, _lib.PKV_BF16, pt=256) == 1
     tuning("PKV_ATTN_APPEND", 1)
     assert folded(64, 16, 8, 128, _lib.PKV_BF16) == 0
+    assert folded(64, 16, 8, 128, _lib.PKV_BF16, pt=256) == 0
 
 
 def test_decode_route_query():
@@ -372,8 +376,9 @@ def test_decode_route_query():
     assert route(4, 64, 8, 128, _lib.PKV_FP8_E4M3) == M
     assert route(4, 64, 8, 128, _lib.PKV_INT8) == M
     assert route(4, 64, 8, 128, _lib.PKV_BF16, pt=16) == P
-    assert route(64, 16, 8, 128, _lib.PKV_BF16) == B
-    assert route(64, 32, 8, 128, _lib.PKV_BF16) == B
+    assert route(64, 16, 8, 128, _lib.PKV_BF16) == _lib.PKV_ROUTE_MATRIX_BALANCED
+    assert route(64, 32, 8, 128, _lib.PKV_BF16) == _lib.PKV_ROUTE_MATRIX_BALANCED
+    assert route(64, 16, 8, 128, _lib.PKV_BF16, pt=256) == P
     assert route(4, 64, 8, 64, _lib.PKV_BF16) == B
     assert route(4, 64, 8, 128, _lib.PKV_F32) == B
     assert route(4, 63, 8, 128, _lib.PKV_BF16) == -1
@@ -384,6 +389,7 @@ def test_decode_route_query():
     assert route(64, 16, 8, 128, _lib.PKV_INT8) == MB
     assert route(64, 16, 8, 128, _lib.PKV_INT8, pt=256) == P
     assert route(64, 8, 8, 128, _lib.PKV_FP8_E4M3) == B     # one head per group
+    assert route(64, 16, 8, 64, _lib.PKV_BF16) == B         # head_dim 64: vector kernels
     # the workspace of the matrix route: N * Hq * runs rows of D + 2 floats.
     # 256 partitions of 512 over 32 (sequence, KV head) histories are more
     # than the GPU holds at once: 96 equal shares of 1376 positions each
@@ -417,7 +423,7 @@ def test_tuning_knobs_read_once_and_set_through_the_abi(tuning):
     changes do nothing, pkv_set_tuning does (and refuses unknown names and
     values out of range)."""
     lib = pkv.lib()
-    geo = ctypes.byref(g(nb=8192, H=8, D=128, dt=_lib.PKV_BF16))
+    geo = ctypes.byref(g(nb=8192, H=8, D=64, dt=_lib.PKV_BF16))
     tuning("PKV_ATTN_MODE", 0)
     assert lib.pkv_attention_decode_route(64, 16, 4096, 0, geo) == _lib.PKV_ROUTE_BALANCED
     os.environ["PKV_ATTN_MODE"] = "1"
