@@ -70,7 +70,8 @@ typedef int32_t pkv_status;
 typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2, PKV_INT8 = 3 } pkv_dtype;
 
 /* Geometry of one cache pool pair.  block_size must be a power of two;
- * num_blocks * block_size < 2^31. */
+ * num_blocks * block_size < 2^31, and one block of a pool
+ * (block_size * num_kv_heads * head_dim * element size) under 2 GiB. */
 typedef struct pkv_geom {
   int32_t num_blocks;
   int32_t block_size;

@@ -66,8 +66,11 @@ struct MultiArgs {
   const float* v_scales;
 };
 
+// Register budgets that keep workgroups resident: eight-wave ones two per CU
+// (<= 128 registers a lane), four-wave ones three.
 template <int D, int NW, int Q, bool kStream>
 __global__ void __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(NW == 8 ? 4 : (NW == 4 ? 3 : 1))))
 attn_multi_kernel(MultiArgs a) {
   __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D, NW>()];
   __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D, NW>()];

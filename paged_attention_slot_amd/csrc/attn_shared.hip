@@ -103,8 +103,10 @@ __device__ __forceinline__ int seq_prefix(const SharedArgs& a, int s, int L) {
 }
 
 // grid = (row blocks * pre_parts, H_kv, num_groups).
+// (four-wave workgroups: a register budget that keeps three resident per CU)
 template <int D, int NW, int Q>
 __global__ void __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(NW == 4 ? 3 : 1)))
 attn_prefix_kernel(SharedArgs a) {
   __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D, NW>()];
   __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D, NW>()];
@@ -165,6 +167,7 @@ attn_prefix_kernel(SharedArgs a) {
 // grid = (suf_parts, H_kv, num_seqs).
 template <int D, int NW, int Q>
 __global__ void __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(NW == 4 ? 3 : 1)))
 attn_suffix_kernel(SharedArgs a) {
   __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D, NW>()];
   __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D, NW>()];

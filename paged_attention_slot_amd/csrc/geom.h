@@ -29,7 +29,8 @@ inline int log2_exact(int32_t v) {
 }
 
 // Common geometry validation: dtype known, block size a power of two, sizes
-// positive, pool index space below 2^31 slots, token row a multiple of 16 B.
+// positive, pool index space below 2^31 slots, token row a multiple of 16 B,
+// one block under 2 GiB (kernels take byte offsets inside a block in 32 bits).
 inline pkv_status check_geom(const pkv_geom* g, const char* who) {
   if (!g) return fail(PKV_ERR_INVALID_ARG, "%s: null geometry", who);
   if (elem_size(g->dtype) == 0) return fail(PKV_ERR_INVALID_ARG, "%s: unknown dtype %d", who, g->dtype);
@@ -43,6 +44,9 @@ inline pkv_status check_geom(const pkv_geom* g, const char* who) {
   if (row % 16 != 0)
     return fail(PKV_ERR_INVALID_ARG, "%s: token row of %lld bytes is not a multiple of 16", who,
                 (long long)row);
+  if (row * g->block_size >= (int64_t(1) << 31))
+    return fail(PKV_ERR_INVALID_ARG, "%s: one block of %lld bytes must be under 2 GiB", who,
+                (long long)(row * g->block_size));
   return PKV_OK;
 }
 

@@ -8,21 +8,22 @@
 //    workgroup as [position][d] rows, read back as MFMA operands: K with
 //    plain 16-byte reads, V through gfx950's transposing LDS read
 //    (ds_read_b64_tr_b16), which hands each lane the 4 positions of one d
-//    that the V^T operand needs.  With several waves two LDS tile buffers are
-//    used in turn, so one barrier per tile separates a tile's staging from
-//    its reading (a wave stages tile i + 1 only after the barrier of tile i,
-//    which every wave passes only once done with tile i - 1 in the same
-//    buffer); a single wave's LDS accesses run in order, so it uses one.  The next
-//    tile's global loads are issued before the current tile's matrix work,
-//    and the barrier waits only for LDS, so they stay in flight.
+//    that the V^T operand needs.  With several waves two LDS buffers each of
+//    K and V are used in turn and the walk is software-pipelined (a tile's
+//    scores are computed one step ahead of its weights, K staged two tiles
+//    ahead and V one), with one barrier per tile; a single wave's LDS
+//    accesses run in order, so it uses one buffer.  Tiles' global loads are
+//    issued two tiles ahead of their staging, and the barrier waits only for
+//    LDS, so they stay in flight.
 //  * Scores as S^T = K Q^T with v_mfma_f32_16x16x32_bf16: a lane's result
 //    fragment holds 8 positions of one query row (its lane & 15), so the
 //    online softmax (log2 units) needs only the ^16 and ^32 lane exchanges,
 //    and the weights P land directly in the operand layout of O^T += V^T P^T
 //    (positions ordered 16(j/4) + 4q + j%4 in both operands).  P enters as
 //    two bf16 terms (hi + lo), so the product keeps fp32-like weights.
-//  * A row sees positions t <= p_row inside [t_lo, t_hi); tiles are loaded
-//    with zeros past the history.
+//  * A row sees positions t <= p_row inside [t_lo, t_hi), which callers keep
+//    below the history's length; past it tiles load zeros for V (finite
+//    products) and leave K as it was (its scores are masked by selection).
 //  * One-byte caches ([KVM §19.2.4] precision table; [PFX] "KV Cache 量化"):
 //    FP8 e4m3 and INT8 codes are decoded exactly to bf16 pairs when a tile is
 //    staged, so the matrix work is the bf16 one.  The FP8 K scale is folded
@@ -47,10 +48,10 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kKT = 32;             // positions per K/V tile
 constexpr float kRefInit = -1e30f;  // reference of a row with no position yet
 
-// LDS of one workgroup of NW waves: K/V tile buffers (two for several
-// waves: the next tile is staged into one while the other is read; one
+// LDS of one workgroup of NW waves: K/V tile buffers (two each for several
+// waves: tiles ahead are staged into one while the other is read; one
 // wave's LDS accesses run in order, so it needs one), and for INT8 the
-// tiles' position scales.
+// tiles' position scales (three slots for several waves).
 // Row strides in LDS (bf16 elements): V rows padded by 32 bytes, so the
 // transposing reads (4 rows x 4 eight-byte columns per 16 lanes) fall in
 // different banks.  K rows by 32 bytes too with several waves: a 16-byte
@@ -95,7 +96,7 @@ __device__ __forceinline__ void lds_barrier() {
 // Element kinds of the cache pools.
 enum Kind : int { kBf16 = 0, kFp8 = 1, kInt8 = 2 };
 template <int Q, int NW> constexpr int s_lds_elems() {
-  return Q == kInt8 ? lds_tiles<NW>() * 2 * kKT : 1;
+  return Q == kInt8 ? (NW == 1 ? 1 : 3) * 2 * kKT : 1;
 }
 
 // The K/V history a workgroup reads: one KV head through one table row.
@@ -169,16 +170,17 @@ __device__ __forceinline__ void start(RowAcc<D>& r) {
 // the pools' element kind; INT8 needs ``s_lds`` (s_lds_elems<Q, NW>() floats
 // of LDS) for the tiles' scales.  p_all (the same in every lane) is a position every live
 // row of the workgroup sees: tiles entirely at or before it, and inside
-// [t_lo, t_hi), skip the per-score mask.  t_lo must be a multiple of 8 (a
+// [t_lo, t_hi), skip the per-score mask (p_all < h.len or t_hi <= h.len,
+// so tiles reaching past the history are masked).  t_lo must be a multiple of 8 (a
 // lane's positions of a tile then lie in one block).  PD tiles are in flight
 // ahead of the one being computed (PD register buffers of K/V per thread).
 //
-// With one wave (latency-bound, few rows) the reference m of a row moves
-// lazily: only when some row of the wave sees a score more than kSlack (log2
-// units) above its reference is the state rescaled, so weights stay <=
-// 2^kSlack and most tiles skip the rescale.  With more waves (matrix-bound)
-// every tile rescales: the branch would keep the compiler from interleaving
-// the tile's matrix work with its softmax (measured 20 % slower).
+// The reference m of a row moves lazily: only when some lane of the wave
+// holds a score more than kSlack (log2 units) above its row's reference is
+// the state rescaled (to the rows' maxima), so weights stay <= 2^kSlack and
+// most tiles skip both the rescale and the cross-lane maximum.  The sum of
+// weights is kept per lane (each lane's positions of its row) and reduced
+// over the row's four lanes only where a state is handed out.
 //
 // Segments: with an ``emit`` functor, [t_lo, t_hi) is cut at the multiples
 // of ``seg`` (t_lo and seg multiples of the tile): after a segment's last
@@ -211,8 +213,9 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
                                        float* s_lds = nullptr, int seg = 0,
                                        const Emit& emit = Emit(), const NewRow& nr = NewRow()) {
   static_assert(!kAppend || Q == kBf16, "the folded append takes bf16 pools");
+  static_assert(!kAppend || NW == 1, "the folded append runs in single-wave passes");
+  static_assert(NW == 1 || PD == 2, "several waves keep two tiles of registers in flight");
   constexpr float kSlack = 8.0f;
-  constexpr bool kLazy = NW == 1;
   constexpr int kEB = Q == kBf16 ? 2 : 1;   // bytes per element
   constexpr int kKS = D / 32;            // k-steps of the score product
   constexpr int kDT = D / 16;            // 16-wide d tiles of the output
@@ -247,79 +250,73 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
   static_assert(kChunks % (64 * NW) == 0, "tile chunks must split evenly");
   const int cc = tid % kChunksPerRow;
   const int pg = tid / kChunksPerRow;
+  // Register sets of tiles in flight: K/V chunks, and INT8's position scales
+  // (lanes < 32), which travel with K.
   uint4 nk[PD][kPer], nv[PD][kPer];
-  float nks[PD], nvs[PD];  // INT8: this lane's position scales (lanes < 32)
-  // Issue the global loads of the tile at t0 into buffer j (zeros past the
-  // history: never unmasked, and they keep the products finite).
+  float nks[PD], nvs[PD];
   // The tile's (at most 4, block_size >= 8) block ids come from a window of
   // 64 table entries held one per lane (tcache: entry tcache_base + lane) and
   // read with v_readlane, so a tile's loads do not wait for a table read:
   // the window is reloaded only when a tile reaches past it.
   const int last_idx = L > 0 ? (L - 1) >> h.block_shift : -1;
+  // Window of 64 entries from table index base: entries past the history, or
+  // naming no block of the pool, read as block 0 (only zero-filled or masked
+  // positions use them).  The asm waits for the window where it is loaded;
+  // otherwise the first v_readlane would wait for every load in flight, since
+  // the compiler cannot tell which path wrote it.
+  const auto window = [&](int base) {
+    int b = base + lane <= last_idx ? h.trow[base + lane] : 0;
+    b = (b >= 0 && b < h.num_blocks) ? b : 0;
+    asm volatile("" ::"v"(b));
+    return b;
+  };
   int tcache_base = t_lo >> h.block_shift;
-  int tcache = tcache_base + lane <= last_idx ? h.trow[tcache_base + lane] : 0;
-  // Wait for the window here; otherwise the first v_readlane would wait for
-  // every load in flight, since the compiler cannot tell which path wrote it.
-  asm volatile("" ::"v"(tcache));
+  int tcache = window(tcache_base);
+  // Byte offsets: this lane's d slice of KV head g, a position's row in its
+  // block, a block.
+  const int lane_pos = pg * kPer;
+  const int lane_off = (h.g * D + cc * kEPC) * kEB;
+  const int row_bytes = h.row_elems * kEB;
+  const uint32_t block_bytes = static_cast<uint32_t>(h.block_elems * kEB);  // < 2^31
   // K/V tile loads: non-temporal when the caller reads each byte once
   const auto kv_load = [](const char* p) {
     if constexpr (kStream) return load_stream(p);
     else return *reinterpret_cast<const uint4*>(p);
   };
-  auto fetch = [&](int j, int t0) {
+  // Issue the K loads (and INT8 scales) of the tile at t0 into register set j;
+  // returns the tile's byte offset in the pools for its V loads.  Past the
+  // history K is left as it was (its scores are masked by selection).
+  auto fetch_k = [&](int j, int t0) -> uint64_t {
     const int b0 = t0 >> h.block_shift;
     if (b0 + 3 - tcache_base >= 64) {  // uniform, rare: move the window to b0
       tcache_base = b0;
-      tcache = b0 + lane <= last_idx ? h.trow[b0 + lane] : 0;
-      asm volatile("" ::"v"(tcache));
+      tcache = window(b0);
     }
     int ids[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int idx = b0 + k;
-      const int b = idx <= last_idx ? __builtin_amdgcn_readlane(tcache, idx - tcache_base) : 0;
-      ids[k] = (b >= 0 && b < h.num_blocks) ? b : 0;
-    }
+    for (int k = 0; k < 4; ++k) ids[k] = __builtin_amdgcn_readlane(tcache, b0 + k - tcache_base);
     // This lane's kPer positions p0 .. p0 + kPer - 1 lie in one block (t0 is
     // a multiple of 8, kPer divides 8 and the block size).
-    const int p0 = t0 + pg * kPer;
+    const int p0 = t0 + lane_pos;
     const int k = (p0 >> h.block_shift) - b0;
     const int blk = k == 0 ? ids[0] : (k == 1 ? ids[1] : (k == 2 ? ids[2] : ids[3]));
-    const int64_t off0 = (int64_t(blk) * h.block_elems + int64_t(p0 & bmask) * h.row_elems +
-                          int64_t(h.g) * D + cc * kEPC) * kEB;
-    const char* kb = static_cast<const char*>(h.k_cache) + off0;
-    const char* vb = static_cast<const char*>(h.v_cache) + off0;
-    const int64_t rstep = int64_t(h.row_elems) * kEB;
+    const uint64_t off = uint64_t(static_cast<uint32_t>(blk)) * block_bytes +
+                         static_cast<uint32_t>((p0 & bmask) * row_bytes + lane_off);
+    const char* kb = static_cast<const char*>(h.k_cache) + off;
     if (kAppend && nr.pos >= t0 && nr.pos < t0 + kKT) {  // uniform: the tile holds the new token
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
-        const bool fresh = p0 + i == nr.pos;
         nk[j][i] = make_uint4(0, 0, 0, 0);
-        nv[j][i] = make_uint4(0, 0, 0, 0);
-        if (fresh) {
-          nk[j][i] = kv_load(reinterpret_cast<const char*>(nr.k + cc * kEPC));
-          nv[j][i] = kv_load(reinterpret_cast<const char*>(nr.v + cc * kEPC));
-        } else if (p0 + i < L) {
-          nk[j][i] = kv_load(kb + i * rstep);
-          nv[j][i] = kv_load(vb + i * rstep);
-        }
+        if (p0 + i == nr.pos) nk[j][i] = kv_load(reinterpret_cast<const char*>(nr.k + cc * kEPC));
+        else if (p0 + i < L) nk[j][i] = kv_load(kb + i * row_bytes);
       }
     } else if (t0 + kKT <= L) {  // uniform: the whole tile is history
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        nk[j][i] = kv_load(kb + i * rstep);
-        nv[j][i] = kv_load(vb + i * rstep);
-      }
+      for (int i = 0; i < kPer; ++i) nk[j][i] = kv_load(kb + i * row_bytes);
     } else {
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        nk[j][i] = make_uint4(0, 0, 0, 0);
-        nv[j][i] = make_uint4(0, 0, 0, 0);
-        if (p0 + i < L) {
-          nk[j][i] = kv_load(kb + i * rstep);
-          nv[j][i] = kv_load(vb + i * rstep);
-        }
-      }
+      for (int i = 0; i < kPer; ++i)
+        if (p0 + i < L) nk[j][i] = kv_load(kb + i * row_bytes);
     }
     if constexpr (Q == kInt8) {
       // Lane t < 32 fetches the scales of position t0 + t (0 past the
@@ -335,65 +332,84 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
         nvs[j] = h.v_scales[si];
       }
     }
+    return off;
   };
-  // Stage the tile of buffer j: K and V as [pos][d] bf16 (codes decoded).
+  // Issue the V loads of the tile at t0 (pool offset ``off`` from fetch_k)
+  // into register set j: zeros past the history, which keep the products
+  // finite.
+  auto fetch_v = [&](int j, int t0, uint64_t off) {
+    const char* vb = static_cast<const char*>(h.v_cache) + off;
+    const int p0 = t0 + lane_pos;
+    if (kAppend && nr.pos >= t0 && nr.pos < t0 + kKT) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        nv[j][i] = make_uint4(0, 0, 0, 0);
+        if (p0 + i == nr.pos) nv[j][i] = kv_load(reinterpret_cast<const char*>(nr.v + cc * kEPC));
+        else if (p0 + i < L) nv[j][i] = kv_load(vb + i * row_bytes);
+      }
+    } else if (t0 + kKT <= L) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) nv[j][i] = kv_load(vb + i * row_bytes);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        nv[j][i] = make_uint4(0, 0, 0, 0);
+        if (p0 + i < L) nv[j][i] = kv_load(vb + i * row_bytes);
+      }
+    }
+  };
+  // Stage a tile's K (register set j) into LDS tile buffer kbuf as [pos][d]
+  // bf16 (codes decoded), and INT8's scales into scale slot ss; its V into
+  // buffer vbuf.  With kAppend the new token's chunks go to its slot as well
+  // (the loads that read them have completed: their values are staged).
   constexpr int kTileElems = kKT * kKStride;   // one LDS tile buffer of K
   constexpr int kVTileElems = kKT * kVStride;  // and of V
-  auto stage = [&](int j, int buf, int t0) {
+  auto stage_rows = [&](const uint4& x, uint16_t* dst) {
+    if constexpr (Q == kBf16) {
+      *reinterpret_cast<uint4*>(dst) = x;
+    } else if constexpr (Q == kFp8) {
+      // code pairs straight to bf16 pairs (packed conversion)
+      const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+      uint32_t w[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w[2 * e] = fp8x2_to_bf16x2(xw[e], false);
+        w[2 * e + 1] = fp8x2_to_bf16x2(xw[e], true);
+      }
+      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(dst + 8) = make_uint4(w[4], w[5], w[6], w[7]);
+    } else {
+      float f[16];
+      uint32_t w[8];
+      decode_codes<Q>(x, f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = bf16_pair_exact(f[2 * e], f[2 * e + 1]);
+      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(dst + 8) = make_uint4(w[4], w[5], w[6], w[7]);
+    }
+  };
+  auto stage_k = [&](int j, int kbuf, int ss, int t0) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int off = buf * kTileElems + (pg * kPer + i) * kKStride + cc * kEPC;
-      const int voff = buf * kVTileElems + (pg * kPer + i) * kVStride + cc * kEPC;
-      if constexpr (Q == kBf16) {
-        *reinterpret_cast<uint4*>(k_lds + off) = nk[j][i];
-        *reinterpret_cast<uint4*>(v_lds + voff) = nv[j][i];
-        if constexpr (kAppend) {
-          // the new token's chunk goes to its slot as well (the loads that
-          // read it have completed: its value was just staged)
-          if (t0 + pg * kPer + i == nr.pos) {
-            *reinterpret_cast<uint4*>(nr.k_dst + cc * kEPC) = nk[j][i];
-            *reinterpret_cast<uint4*>(nr.v_dst + cc * kEPC) = nv[j][i];
-          }
-        }
-      } else if constexpr (Q == kFp8) {
-        // code pairs straight to bf16 pairs (packed conversion)
-        const uint32_t kw[4] = {nk[j][i].x, nk[j][i].y, nk[j][i].z, nk[j][i].w};
-        const uint32_t vw[4] = {nv[j][i].x, nv[j][i].y, nv[j][i].z, nv[j][i].w};
-        uint32_t w[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w[2 * e] = fp8x2_to_bf16x2(kw[e], false);
-          w[2 * e + 1] = fp8x2_to_bf16x2(kw[e], true);
-        }
-        *reinterpret_cast<uint4*>(k_lds + off) = make_uint4(w[0], w[1], w[2], w[3]);
-        *reinterpret_cast<uint4*>(k_lds + off + 8) = make_uint4(w[4], w[5], w[6], w[7]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w[2 * e] = fp8x2_to_bf16x2(vw[e], false);
-          w[2 * e + 1] = fp8x2_to_bf16x2(vw[e], true);
-        }
-        *reinterpret_cast<uint4*>(v_lds + voff) = make_uint4(w[0], w[1], w[2], w[3]);
-        *reinterpret_cast<uint4*>(v_lds + voff + 8) = make_uint4(w[4], w[5], w[6], w[7]);
-      } else {
-        float f[16];
-        uint32_t w[8];
-        decode_codes<Q>(nk[j][i], f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = bf16_pair_exact(f[2 * e], f[2 * e + 1]);
-        *reinterpret_cast<uint4*>(k_lds + off) = make_uint4(w[0], w[1], w[2], w[3]);
-        *reinterpret_cast<uint4*>(k_lds + off + 8) = make_uint4(w[4], w[5], w[6], w[7]);
-        decode_codes<Q>(nv[j][i], f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = bf16_pair_exact(f[2 * e], f[2 * e + 1]);
-        *reinterpret_cast<uint4*>(v_lds + voff) = make_uint4(w[0], w[1], w[2], w[3]);
-        *reinterpret_cast<uint4*>(v_lds + voff + 8) = make_uint4(w[4], w[5], w[6], w[7]);
-      }
+      stage_rows(nk[j][i], k_lds + kbuf * kTileElems + (pg * kPer + i) * kKStride + cc * kEPC);
+      if constexpr (kAppend)
+        if (t0 + pg * kPer + i == nr.pos)
+          *reinterpret_cast<uint4*>(nr.k_dst + cc * kEPC) = nk[j][i];
     }
     if constexpr (Q == kInt8) {
       if (tid < kKT) {
-        s_lds[2 * kKT * buf + tid] = nks[j];
-        s_lds[2 * kKT * buf + kKT + tid] = nvs[j];
+        s_lds[2 * kKT * ss + tid] = nks[j];
+        s_lds[2 * kKT * ss + kKT + tid] = nvs[j];
       }
+    }
+  };
+  auto stage_v = [&](int j, int vbuf, int t0) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      stage_rows(nv[j][i], v_lds + vbuf * kVTileElems + (pg * kPer + i) * kVStride + cc * kEPC);
+      if constexpr (kAppend)
+        if (t0 + pg * kPer + i == nr.pos)
+          *reinterpret_cast<uint4*>(nr.v_dst + cc * kEPC) = nv[j][i];
     }
   };
   // This lane's V^T reads: row 4 (lane >> 4) + (lane & 15) / 4 (+ 16 for the
@@ -403,11 +419,14 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
   // Last position this lane's row sees (-1: none): the mask of a tile that
   // not every live row sees whole is one compare per score against it.
   const int row_lim = row_ok ? (p_row < t_hi - 1 ? p_row : t_hi - 1) : -1;
+  // This lane's part of its row's sum of weights (the state's sum enters
+  // through the row's first lane).
+  float lpart = quad == 0 ? r.lsum : 0.f;
 
-  // A staged tile's scores S^T = K Q^T (LDS tile buffer buf): s[pt][i] is
+  // A staged tile's scores S^T = K Q^T (LDS tile buffer kbuf): s[pt][i] is
   // position 16 pt + 4 quad + i of the tile for row (lane & 15).
-  auto qk = [&](int buf, f32x4_t (&s)[2]) {
-    const uint16_t* kt = k_lds + buf * kTileElems;
+  auto qk = [&](int kbuf, f32x4_t (&s)[2]) {
+    const uint16_t* kt = k_lds + kbuf * kTileElems;
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -421,46 +440,56 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
       s[pt] = acc;
     }
   };
-  // The rest of a tile's work from its scores: mask, online softmax, P V.
-  auto softmax_pv = [&](int t0, int buf, const f32x4_t (&s)[2]) {
-    const uint16_t* vt = v_rd + buf * kVTileElems;
-    const float* st = s_lds + 2 * kKT * buf;
-    // Uniform: every live row sees every position of the tile.
-    const bool full = t0 + kKT - 1 <= p_all && t0 + kKT <= t_hi;
-    // Score e = 4 pt + i sits at position t0 + 16 pt + 4 quad + i, visible
-    // to this lane's row iff 16 pt + i <= vis.
-    const int vis = row_lim - t0 - 4 * quad;
-    float sc[8];
-    float tmax = -INFINITY;
+  // A tile's scores, ready for the exponent: masked (-inf) where the lane's
+  // row does not see the position, INT8 scaled with the key scales (scale
+  // slot ss); and the state's reference moved if some lane's score exceeds
+  // its row's reference by more than kSlack.
+  auto prepare = [&](int t0, int ss, const f32x4_t (&s)[2], float (&sc)[8]) {
+    const float* st = s_lds + 2 * kKT * ss;
 #pragma unroll
-    for (int pt = 0; pt < 2; ++pt) {
+    for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         // bf16 and FP8: unscaled here; INT8: scaled with its key scale
         float v = s[pt][i];
         if constexpr (Q == kInt8) v *= scale_log2 * st[16 * pt + 4 * quad + i];
-        if (!full) v = 16 * pt + i <= vis ? v : -INFINITY;
         sc[4 * pt + i] = v;
-        tmax = fmaxf(tmax, v);
       }
+    // Uniform: some live row does not see every position of the tile.  Score
+    // e = 4 pt + i sits at position t0 + 16 pt + 4 quad + i, visible to this
+    // lane's row iff 16 pt + i <= vis.
+    if (t0 + kKT - 1 > p_all || t0 + kKT > t_hi) {
+      const int vis = row_lim - t0 - 4 * quad;
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sc[4 * pt + i] = 16 * pt + i <= vis ? sc[4 * pt + i] : -INFINITY;
     }
-    tmax = max_across_rows16(tmax);
+    float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                       fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
     if constexpr (Q != kInt8) tmax *= scale_log2;
-    if (!kLazy || __builtin_amdgcn_ballot_w64(tmax > r.m + kSlack) != 0) {  // uniform
-      const float mn = fmaxf(r.m, tmax);
+    if (__builtin_amdgcn_ballot_w64(tmax > r.m + kSlack) != 0) {  // uniform
+      const float mn = fmaxf(r.m, max_across_rows16(tmax));
       const float alpha = fast_exp2(r.m - mn);
       r.m = mn;
-      r.lsum *= alpha;
+      lpart *= alpha;
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) r.o[dt][i] *= alpha;
     }
+  };
+  // The weights of prepared scores and their P V (LDS tile buffer vbuf,
+  // INT8's V scales in slot ss).
+  auto weigh = [&](int vbuf, int ss, const float (&sc)[8]) {
+    const uint16_t* vt = v_rd + vbuf * kVTileElems;
+    const float* st = s_lds + 2 * kKT * ss;
     const float mref = r.m;
     // Weights as two bf16 terms, p = hi + lo (hi = bf16(p), lo = bf16(p - hi)):
     // P V then carries p to about 2^-17 relative, like the fp32 sum.
     uint32_t ph[4], pl[4];
-    float psum = 0.f;
+    float psum;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       float p0, p1;
@@ -471,7 +500,7 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
         p0 = fast_exp2(fmaf(sc[2 * k], scale_log2, -mref));
         p1 = fast_exp2(fmaf(sc[2 * k + 1], scale_log2, -mref));
       }
-      psum += p0 + p1;
+      psum = k == 0 ? p0 + p1 : psum + (p0 + p1);
       // score element e = 2k (+1) sits at tile position 16 (e / 4) + 4 quad + e % 4
       if constexpr (Q == kFp8) {
         p0 *= h.v_scale;
@@ -484,8 +513,7 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
       ph[k] = hw;
       pl[k] = cvt_pk_bf16(p0 - __uint_as_float(hw << 16), p1 - __uint_as_float(hw & 0xFFFF0000u));
     }
-    psum = sum_across_rows16(psum);
-    r.lsum += psum;
+    lpart += psum;
     const bf16x8_t pfh = as_bf16x8(make_uint4(ph[0], ph[1], ph[2], ph[3]));
     const bf16x8_t pfl = as_bf16x8(make_uint4(pl[0], pl[1], pl[2], pl[3]));
 #pragma unroll
@@ -503,33 +531,91 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
     if constexpr (!std::is_same<Emit, NoEmit>::value) {
       const int te = t + kKT;
       if (te >= t_hi || te % seg == 0) {  // uniform: a segment is complete
+        r.lsum = sum_across_rows16(lpart);
         emit(t, r);
         start(r);
+        lpart = 0.f;
       }
     }
   };
 
 #pragma unroll
   for (int j = 0; j < PD; ++j)
-    if (t_lo + j * kKT < t_hi) fetch(j, t_lo + j * kKT);
-  int buf = 0;
-  for (int t0 = t_lo; t0 < t_hi; t0 += PD * kKT) {
 #pragma unroll
-    for (int j = 0; j < PD; ++j) {
-      const int t = t0 + j * kKT;
-      if (t >= t_hi) break;  // uniform
-      stage(j, buf, t);
-      lds_barrier();
-      // the register buffer just staged takes the tile PD ahead, in flight
-      // meanwhile
-      if (t + PD * kKT < t_hi) fetch(j, t + PD * kKT);
-      f32x4_t sv[2];
-      qk(buf, sv);
-      softmax_pv(t, buf, sv);
-      if constexpr (lds_tiles<NW>() == 2) buf ^= 1;
-      segment_end(t);
+    for (int i = 0; i < kPer; ++i) nk[j][i] = make_uint4(0, 0, 0, 0);
+  if constexpr (NW == 1) {
+    // One wave: tile t is staged, its scores and P V computed, in turn; the
+    // tile PD ahead is loaded meanwhile.
+#pragma unroll
+    for (int j = 0; j < PD; ++j)
+      if (t_lo + j * kKT < t_hi) fetch_v(j, t_lo + j * kKT, fetch_k(j, t_lo + j * kKT));
+    for (int t0 = t_lo; t0 < t_hi; t0 += PD * kKT) {
+#pragma unroll
+      for (int j = 0; j < PD; ++j) {
+        const int t = t0 + j * kKT;
+        if (t >= t_hi) break;  // uniform
+        stage_k(j, 0, 0, t);
+        stage_v(j, 0, t);
+        lds_barrier();
+        // the register set just staged takes the tile PD ahead, in flight
+        // meanwhile
+        if (t + PD * kKT < t_hi) fetch_v(j, t + PD * kKT, fetch_k(j, t + PD * kKT));
+        f32x4_t sv[2];
+        float sc[8];
+        qk(0, sv);
+        prepare(t, 0, sv, sc);
+        weigh(0, 0, sc);
+        segment_end(t);
+      }
+    }
+  } else {
+    // Several waves, software-pipelined: while tile i's weights and P V are
+    // computed, tile i + 1's scores are already on the matrix cores.  K is
+    // staged two tiles ahead, V one: iteration i, after one barrier, reads K
+    // buffer (i + 1) & 1 and V buffer i & 1, then stages K(i + 2) into K
+    // buffer i & 1 and V(i + 1) into V buffer (i + 1) & 1, whose readers
+    // (tile i's scores, tile i - 1's P V) every wave finished before that
+    // barrier.  INT8 scales staged with K(u) sit in slot u % 3 until tile u's
+    // P V.  Register sets: K(u) and V(u) in set u & 1; V loads trail K's by
+    // one tile, so each V load reuses the pool offset its K load computed.
+    const int n = (t_hi - t_lo + kKT - 1) / kKT;
+    const auto tile = [&](int u) { return t_lo + u * kKT; };
+    uint64_t voff = 0;
+    if (n > 0) fetch_v(0, tile(0), fetch_k(0, tile(0)));
+    if (n > 1) fetch_v(1, tile(1), fetch_k(1, tile(1)));
+    if (n > 0) {
+      stage_k(0, 0, 0, tile(0));
+      stage_v(0, 0, tile(0));
+    }
+    if (n > 1) stage_k(1, 1, 1, tile(1));
+    if (n > 2) fetch_v(0, tile(2), fetch_k(0, tile(2)));
+    if (n > 3) voff = fetch_k(1, tile(3));
+    lds_barrier();
+    f32x4_t s_nx[2];
+    float sc[8];
+    qk(0, s_nx);
+    if (n > 0) prepare(tile(0), 0, s_nx, sc);
+    int ss = 0;  // scale slot of tile i
+    for (int i0 = 0; i0 < n; i0 += 2) {
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        const int i = i0 + par;
+        if (i >= n) break;  // uniform
+        lds_barrier();
+        const int ss1 = ss == 2 ? 0 : ss + 1, ss2 = ss1 == 2 ? 0 : ss1 + 1;
+        qk(par ^ 1, s_nx);      // tile i + 1's scores (unused past the last tile)
+        weigh(par, ss, sc);     // tile i's weights and P V
+        if (i + 2 < n) stage_k(par, par, ss2, tile(i + 2));
+        if (i + 1 < n) stage_v(par ^ 1, par ^ 1, tile(i + 1));
+        if (i + 3 < n) fetch_v(par ^ 1, tile(i + 3), voff);
+        if (i + 4 < n) voff = fetch_k(par, tile(i + 4));
+        segment_end(tile(i));
+        if (i + 1 < n) prepare(tile(i + 1), ss1, s_nx, sc);
+        ss = ss1;
+      }
     }
   }
+  r.lsum = sum_across_rows16(lpart);
   // the caller may reuse the LDS (another pass) right after
   lds_barrier();
 }
