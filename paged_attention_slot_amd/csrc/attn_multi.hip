@@ -72,8 +72,8 @@ template <int D, int NW, int Q, bool kStream>
 __global__ void __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(NW == 8 ? 4 : (NW == 4 ? 3 : 1))))
 attn_multi_kernel(MultiArgs a) {
-  __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D, NW>()];
-  __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D, NW>()];
+  __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D, NW, Q>()];
+  __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D, NW, Q>()];
   __shared__ float s_lds[pkv::mfma::s_lds_elems<Q, NW>()];
 
   const int tid = threadIdx.x, lane = tid & 63;

@@ -108,8 +108,8 @@ template <int D, int NW, int Q>
 __global__ void __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(NW == 4 ? 3 : 1)))
 attn_prefix_kernel(SharedArgs a) {
-  __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D, NW>()];
-  __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D, NW>()];
+  __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D, NW, Q>()];
+  __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D, NW, Q>()];
   __shared__ float s_lds[pkv::mfma::s_lds_elems<Q, NW>()];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -169,8 +169,8 @@ template <int D, int NW, int Q>
 __global__ void __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(NW == 4 ? 3 : 1)))
 attn_suffix_kernel(SharedArgs a) {
-  __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D, NW>()];
-  __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D, NW>()];
+  __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D, NW, Q>()];
+  __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D, NW, Q>()];
   __shared__ float s_lds[pkv::mfma::s_lds_elems<Q, NW>()];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));

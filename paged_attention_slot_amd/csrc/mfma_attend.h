@@ -62,8 +62,46 @@ constexpr float kRefInit = -1e30f;  // reference of a row with no position yet
 template <int D, int NW> constexpr int k_stride() { return NW == 1 ? D + 8 : D + 16; }
 template <int D> constexpr int v_stride() { return D + 16; }
 template <int NW> constexpr int lds_tiles() { return NW == 1 ? 1 : 2; }
-template <int D, int NW> constexpr int k_lds_elems() { return lds_tiles<NW>() * kKT * k_stride<D, NW>(); }
-template <int D, int NW> constexpr int v_lds_elems() { return lds_tiles<NW>() * kKT * v_stride<D>(); }
+
+// Element kinds of the cache pools.
+enum Kind : int { kBf16 = 0, kFp8 = 1, kInt8 = 2 };
+
+// Eight-wave passes over bf16 pools with head_dim 128 load tiles straight
+// into LDS (gfx950's global_load_lds_dwordx4: each lane's 16 bytes land at
+// the wave's LDS base + 16 * lane, no registers and no LDS stores), into
+// four buffers each of K and V in the padded row layout.
+template <int D, int NW, int Q> constexpr bool direct_lds() {
+  return Q == kBf16 && NW == 8 && D == 128;
+}
+constexpr int kDirectBufs = 4;
+
+// One direct-to-LDS load: this lane's 16 bytes at base + off (base the same
+// in every lane) go to LDS byte lds_base + 16 * lane (lds_base the same in
+// every lane).  Written in asm so the compiler's wait insertion, which
+// cannot tell the tile buffers apart, adds no wait for it before the LDS
+// reads; the walk waits for these loads itself (vmcnt).  M0 (the LDS base)
+// is saved and restored around it, with the wait state an M0 write needs
+// before an LDS DMA.  No VGPR is written.
+__device__ __forceinline__ void load_to_lds16(const char* base, int off, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory");
+}
+
+template <int D, int NW, int Q = kBf16> constexpr int k_lds_elems() {
+  return (direct_lds<D, NW, Q>() ? kDirectBufs : lds_tiles<NW>()) * kKT * k_stride<D, NW>();
+}
+template <int D, int NW, int Q = kBf16> constexpr int v_lds_elems() {
+  return (direct_lds<D, NW, Q>() ? kDirectBufs : lds_tiles<NW>()) * kKT * v_stride<D>();
+}
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -93,8 +131,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Element kinds of the cache pools.
-enum Kind : int { kBf16 = 0, kFp8 = 1, kInt8 = 2 };
 template <int Q, int NW> constexpr int s_lds_elems() {
   return Q == kInt8 ? (NW == 1 ? 1 : 3) * 2 * kKT : 1;
 }
@@ -215,6 +251,7 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
   static_assert(!kAppend || Q == kBf16, "the folded append takes bf16 pools");
   static_assert(!kAppend || NW == 1, "the folded append runs in single-wave passes");
   static_assert(NW == 1 || PD == 2, "several waves keep two tiles of registers in flight");
+  constexpr bool kDirect = direct_lds<D, NW, Q>();
   constexpr float kSlack = 8.0f;
   constexpr int kEB = Q == kBf16 ? 2 : 1;   // bytes per element
   constexpr int kKS = D / 32;            // k-steps of the score product
@@ -480,10 +517,10 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
         for (int i = 0; i < 4; ++i) r.o[dt][i] *= alpha;
     }
   };
-  // The weights of prepared scores and their P V (LDS tile buffer vbuf,
-  // INT8's V scales in slot ss).
-  auto weigh = [&](int vbuf, int ss, const float (&sc)[8]) {
-    const uint16_t* vt = v_rd + vbuf * kVTileElems;
+  // The weights of prepared scores and their P V: vfrag(dt) reads this
+  // lane's V^T operand of d tile dt (V^T[16 dt + (lane & 15)][positions
+  // 4 quad .. + 3 and 16 + 4 quad .. + 3]); INT8's V scales in slot ss.
+  auto weigh = [&](const auto& vfrag, int ss, const float (&sc)[8]) {
     const float* st = s_lds + 2 * kKT * ss;
     const float mref = r.m;
     // Weights as two bf16 terms, p = hi + lo (hi = bf16(p), lo = bf16(p - hi)):
@@ -518,13 +555,19 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
     const bf16x8_t pfl = as_bf16x8(make_uint4(pl[0], pl[1], pl[2], pl[3]));
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt) {
-      // V^T[16 dt + (lane & 15)][positions 4 quad .. + 3 and 16 + 4 quad .. + 3]
-      const uint2 lo = lds_read_tr16(vt + 16 * dt);
-      const uint2 hi = lds_read_tr16(vt + 16 * kVStride + 16 * dt);
-      const bf16x8_t va = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+      const bf16x8_t va = vfrag(dt);
       f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfh, r.o[dt], 0, 0, 0);
       r.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfl, acc, 0, 0, 0);
     }
+  };
+  // V^T fragments from the padded layout's buffer vbuf
+  auto vfrag_padded = [&](int vbuf) {
+    const uint16_t* vt = v_rd + vbuf * kVTileElems;
+    return [vt](int dt) {
+      const uint2 lo = lds_read_tr16(vt + 16 * dt);
+      const uint2 hi = lds_read_tr16(vt + 16 * kVStride + 16 * dt);
+      return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+    };
   };
   // Segment end after the tile at t (see above).
   auto segment_end = [&](int t) {
@@ -564,8 +607,131 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
         float sc[8];
         qk(0, sv);
         prepare(t, 0, sv, sc);
-        weigh(0, 0, sc);
+        weigh(vfrag_padded(0), 0, sc);
         segment_end(t);
+      }
+    }
+  } else if constexpr (kDirect) {
+    // Eight waves, tiles loaded straight into LDS (see direct_lds), the same
+    // software pipeline as below: iteration i, after one barrier, computes
+    // tile i + 1's scores (K buffer (i + 1) % 4) and tile i's weights and
+    // P V (V buffer i % 4), and issues tile i + 3's loads into buffers
+    // (i + 3) % 4, whose previous tile (i - 1) every wave finished before
+    // that barrier.  Before the barrier of iteration i a wave waits for its
+    // loads of K(i + 1) and V(i) (every load issued later may stay in
+    // flight: loads complete in order).  The history's last tile, if
+    // partial, goes through registers with zeros past the history.
+    //
+    // The buffers keep the padded row layout of the register-staged walk
+    // (rows of 18 chunks of 16 bytes, the last two padding).  Wave w loads
+    // rows 4w .. 4w + 3, 72 chunk slots from LDS byte 1152 w of the buffer:
+    // one instruction for slots 0 .. 63 and one (8 lanes) for 64 .. 71;
+    // padding slots are not loaded.  The four rows lie in one block (t0 is a
+    // multiple of 8, blocks hold at least 8), so a tile's block and row
+    // offsets are the same in every lane: each lane adds only its slot's
+    // fixed offset.
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = (t_hi - t_lo + kKT - 1) / kKT;
+    const auto tile = [&](int u) { return t_lo + u * kKT; };
+    constexpr int kSlotsPerRow = kKStride * 2 / 16;
+    static_assert(kKStride == kVStride && kSlotsPerRow == 18, "rows of 18 chunks");
+    int srow[2], soff[2];
+    bool sval[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int z = 64 * e + lane;  // slot of the wave's 72
+      srow[e] = z / kSlotsPerRow;
+      const int x = z - kSlotsPerRow * srow[e];
+      sval[e] = z < 4 * kSlotsPerRow && x < 16;
+      soff[e] = srow[e] * row_bytes + (h.g * D + 8 * x) * 2;
+    }
+    typedef __attribute__((address_space(3))) u32x4_native_t lds_u32x4;
+    const auto lds_addr = [](uint16_t* q) {  // LDS byte address, in an SGPR
+      return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(
+          reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint16_t*)(q)))));
+    };
+    const uint32_t k_lds_a = lds_addr(k_lds), v_lds_a = lds_addr(v_lds);
+    const auto uniform_ptr = [](const char* q) {
+      const uint64_t v = reinterpret_cast<uint64_t>(q);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+      const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+      return reinterpret_cast<const char*>((uint64_t(hi) << 32) | lo);
+    };
+    auto issue = [&](int t0, int buf) {
+      const int b0 = t0 >> h.block_shift;
+      if (b0 + 3 - tcache_base >= 64) {  // uniform, rare: move the window to b0
+        tcache_base = b0;
+        tcache = window(b0);
+      }
+      const int p0 = t0 + 4 * w;  // the wave's first row
+      const int blk = __builtin_amdgcn_readlane(tcache, (p0 >> h.block_shift) - tcache_base);
+      const uint64_t ub = uint64_t(static_cast<uint32_t>(blk)) * block_bytes +
+                          static_cast<uint32_t>((p0 & bmask) * row_bytes);
+      const char* const kg = uniform_ptr(static_cast<const char*>(h.k_cache) + ub);
+      const char* const vg = uniform_ptr(static_cast<const char*>(h.v_cache) + ub);
+      const uint32_t kd = k_lds_a + buf * (kTileElems * 2) + w * (4 * kSlotsPerRow * 16);
+      const uint32_t vd = v_lds_a + buf * (kVTileElems * 2) + w * (4 * kSlotsPerRow * 16);
+      if (t0 + kKT <= L) {  // uniform: the whole tile is history
+        // K's two instructions, then V's (the waits count them in this order)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          if (sval[e]) load_to_lds16(kg, soff[e], kd + 1024 * e);
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          if (sval[e]) load_to_lds16(vg, soff[e], vd + 1024 * e);
+      } else {
+        // the history's last tile: through registers (waited for here, so
+        // the counts of direct loads stay as the waits assume), zeros past
+        // the history
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
+          if (sval[e] && p0 + srow[e] < L) {
+            kx = *reinterpret_cast<const uint4*>(kg + soff[e]);
+            vx = *reinterpret_cast<const uint4*>(vg + soff[e]);
+          }
+          if (sval[e]) {
+            *(lds_u32x4*)(uintptr_t)(kd + 1024 * e + 16 * lane) = u32x4_native_t{kx.x, kx.y, kx.z, kx.w};
+            *(lds_u32x4*)(uintptr_t)(vd + 1024 * e + 16 * lane) = u32x4_native_t{vx.x, vx.y, vx.z, vx.w};
+          }
+        }
+      }
+    };
+    // Tiles loaded directly (whole tiles of history): their loads (two per
+    // pool and wave) are the ones the waits count.
+    const auto direct = [&](int u) { return u < n && tile(u) + kKT <= L; };
+    const auto wait_loads = [](int later) {  // this wave's loads but the last ``later``
+      switch (later) {
+        case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+        case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+        case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+      if (u < n) issue(tile(u), u);
+    // K(0) is needed: after it come V(0) and both pools' loads of tiles 1, 2
+    wait_loads(direct(0) ? 2 * (1 + 2 * direct(1) + 2 * direct(2)) : 0);
+    lds_barrier();
+    f32x4_t s_nx[2];
+    float sc[8];
+    qk(0, s_nx);
+    if (n > 0) prepare(tile(0), 0, s_nx, sc);
+    for (int i0 = 0; i0 < n; i0 += kDirectBufs) {
+#pragma unroll
+      for (int b = 0; b < kDirectBufs; ++b) {
+        const int i = i0 + b;
+        if (i >= n) break;  // uniform
+        // K(i + 1) and V(i): after K(i + 1) come V(i + 1), then tile i + 2's
+        // (a tile through registers is complete once issued)
+        wait_loads(direct(i + 2) ? 6 : (direct(i + 1) ? 2 : 0));
+        lds_barrier();
+        qk((b + 1) % kDirectBufs, s_nx);      // tile i + 1's scores (unused past the last)
+        weigh(vfrag_padded(b), 0, sc);        // tile i's weights and P V
+        if (i + 3 < n) issue(tile(i + 3), (b + 3) % kDirectBufs);
+        segment_end(tile(i));
+        if (i + 1 < n) prepare(tile(i + 1), 0, s_nx, sc);
       }
     }
   } else {
@@ -604,7 +770,7 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
         lds_barrier();
         const int ss1 = ss == 2 ? 0 : ss + 1, ss2 = ss1 == 2 ? 0 : ss1 + 1;
         qk(par ^ 1, s_nx);      // tile i + 1's scores (unused past the last tile)
-        weigh(par, ss, sc);     // tile i's weights and P V
+        weigh(vfrag_padded(par), ss, sc);  // tile i's weights and P V
         if (i + 2 < n) stage_k(par, par, ss2, tile(i + 2));
         if (i + 1 < n) stage_v(par ^ 1, par ^ 1, tile(i + 1));
         if (i + 3 < n) fetch_v(par ^ 1, tile(i + 3), voff);
