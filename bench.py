@@ -399,8 +399,8 @@ def bench_shared(args) -> int:
             "traffic": None,
             "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
             "algorithmic_bytes_per_launch": alg_logical, "avg_launch_us": t_sh * 1e6,
-            "note": "attn_shared = attn_prefix_kernel + attn_suffix_kernel + "
-                    "attn_shared_merge_kernel (event time and traffic cover the three); "
+            "note": "attn_shared = attn_suffix_kernel + attn_prefix_kernel (which also "
+                    "combines each member's pieces; event time and traffic cover both); "
                     "achieved counts logical bytes (each sequence's whole history), which "
                     "exceed the HBM peak because each group's prefix is read once per block "
                     "of member rows; detail.unique_gbps counts every distinct cached "

@@ -162,9 +162,10 @@ pkv_status pkv_copy_blocks_quant(const int32_t* src_dst_pairs, int32_t num_pairs
  *
  * pkv_attention_decode_shared computes exactly what pkv_attention_decode
  * computes (bf16 pools) but reads each group's shared prefix once per block of
- * up to 64 (member, query head) rows instead of once per sequence: prefix
- * positions of all members on the matrix cores, then every sequence's own
- * positions, then a log-sum-exp merge of the fp32 partial states.
+ * 16 (member, query head) rows instead of once per sequence: first every
+ * sequence's own positions (fp32 partial states in the workspace), then the
+ * prefix positions of all members on the matrix cores, each block's result
+ * combined with its members' partial states by log-sum-exp.
  *   group_starts  device int32 [num_groups + 1]: group g is sequences
  *                 group_starts[g] .. group_starts[g+1]-1 (non-decreasing,
  *                 from 0 to num_seqs);

@@ -11,19 +11,19 @@
 // read reuse depends on the kernel).  Here the caller names groups of
 // consecutive sequences and the length of the prefix they share, and
 //
-//  * attn_prefix_kernel reads the prefix of a group once per (block of
-//    members, KV head, partition): its rows are (member, query head of the
-//    KV head's group) pairs, up to 64 per workgroup, all attending the shared
-//    positions (a member shorter than the prefix only its own), on the matrix
-//    cores (pkv::mfma::attend);
-//  * attn_suffix_kernel reads every sequence's remaining positions, one
-//    (sequence, KV head, partition) per workgroup, the G query heads as rows;
-//  * attn_shared_merge_kernel combines each (sequence, head)'s pieces by
-//    log-sum-exp: the partial states of the online softmax of the positions
-//    split between the two ([KVM §19.2.3] block-wise online softmax).
+//  * attn_suffix_kernel (first) reads every sequence's positions after its
+//    prefix, one (sequence, KV head, partition) per workgroup, the G query
+//    heads as rows, and leaves one fp32 piece (weighted sum, reference,
+//    sum) per partition; a sequence without a shared prefix is attended
+//    whole by its first partition's workgroup, which writes its result;
+//  * attn_prefix_kernel (second) reads the prefix of a group once per (KV
+//    head, block of 16 (member, query head) rows): its four waves walk a
+//    quarter of the prefix each on the matrix cores (pkv::mfma::attend),
+//    combine their states through LDS and with the member's suffix pieces
+//    by log-sum-exp ([KVM §19.2.3] block-wise online softmax), and write
+//    the result.  Only the suffix pieces travel through memory.
 //
-// The pieces are fp32 (weighted sum, reference, sum), so only the final
-// result is rounded to bf16.
+// Only the final result is rounded to bf16.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -45,8 +45,8 @@ struct SharedArgs {
   const int32_t* group_starts;   // [num_groups + 1]
   const int32_t* prefix_lens;    // [num_groups]
   uint16_t* out;
-  float* ws_acc;                 // [(s * H_q + h) * slots + slot][D]
-  float2* ws_ml;                 // [(s * H_q + h) * slots + slot]
+  float* ws_acc;                 // suffix pieces: [(s * H_q + h) * suf_parts + part][D]
+  float2* ws_ml;                 // [(s * H_q + h) * suf_parts + part]
   int64_t block_elems;
   int32_t row_elems;
   int32_t max_blocks;
@@ -59,9 +59,9 @@ struct SharedArgs {
   int32_t len_cap;
   int32_t max_prefix;            // prefix lengths are clamped to this
   int32_t max_group;             // larger groups share nothing (the grid has no rows for them)
-  int32_t members_per_block;     // prefix kernel: members per workgroup
-  int32_t pre_parts, pre_tokens; // prefix partitions: count and length
   int32_t suf_parts, suf_tokens; // suffix partitions
+  int32_t row_blocks;            // prefix workgroups per (group, KV head): 16 rows each
+  int32_t pre_blocks;            // prefix workgroups in all
   int32_t num_kv_heads;
   float scale_log2;              // FP8: the K tensor scale folded in
   float v_scale;                 // FP8
@@ -102,41 +102,57 @@ __device__ __forceinline__ int seq_prefix(const SharedArgs& a, int s, int L) {
   return p < L ? p : L;
 }
 
-// grid = (row blocks * pre_parts, H_kv, num_groups).
-// (four-wave workgroups: a register budget that keeps three resident per CU)
-template <int D, int NW, int Q>
-__global__ void __launch_bounds__(64 * NW)
-__attribute__((amdgpu_waves_per_eu(NW == 4 ? 3 : 1)))
-attn_prefix_kernel(SharedArgs a) {
-  __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D, NW, Q>()];
-  __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D, NW, Q>()];
-  __shared__ float s_lds[pkv::mfma::s_lds_elems<Q, NW>()];
+// attn_suffix_kernel (one wave per workgroup) runs first; attn_prefix_kernel
+// (four waves, each with its own LDS tile area) second, finishing every
+// member's result.
+constexpr int kSharedWaves = 4;
+
+template <int D, int Q, int W>
+struct SharedLds {
+  uint16_t k[W][pkv::mfma::k_lds_elems<D, 1, Q>()];
+  uint16_t v[W][pkv::mfma::v_lds_elems<D, 1, Q>()];
+  float s[W][pkv::mfma::s_lds_elems<Q, 1>()];
+};
+
+// One bf16 tile of registers in flight for the single-wave walks, two for
+// one-byte codes (as in the single-wave decode walk).
+template <int Q> constexpr int shared_pd() { return Q == pkv::mfma::kBf16 ? 1 : 2; }
+
+// Prefix role, workgroup x of pre_blocks = H_kv * row_blocks * num_groups
+// (KV head fastest: with 8 KV heads all the row blocks of one head go to one
+// XCD, as workgroups are dealt to the XCDs round robin, and share its L2
+// copy of that head's prefix).  Rows: 16 (member, query head) pairs of the
+// group's members; the four waves walk a quarter of the prefix each, then
+// combine their states through LDS into one piece per row.
+template <int D, int Q>
+__device__ void prefix_role(const SharedArgs& a, int x, SharedLds<D, Q, kSharedWaves>& lds) {
+  constexpr int kW = kSharedWaves;
+  static_assert(16 * D * 4 + 16 * 8 <= int(sizeof(lds.k[0])), "a wave's state fits its K area");
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int gi = blockIdx.z, g = blockIdx.y;
-  const int rb = blockIdx.x / a.pre_parts, part = blockIdx.x - rb * a.pre_parts;
+  const int g = x % a.num_kv_heads;
+  const int rb = (x / a.num_kv_heads) % a.row_blocks;
+  const int gi = x / (a.num_kv_heads * a.row_blocks);
   int first, count;
   const int P = group_prefix(a, gi, &first, &count);
-  const int j0 = rb * a.members_per_block;
-  if (P == 0 || j0 >= count) return;  // uniform over the workgroup
-  const int jn = min(a.members_per_block, count - j0);
-  const int t_lo = part * a.pre_tokens;
-  const int t_hi = min(t_lo + a.pre_tokens, P);
-  if (t_lo >= t_hi) return;
-
   const int G = a.group;
-  const int row = 16 * w + (lane & 15);
-  const int jl = row / G, hh = row - jl * G;
-  const bool row_ok = jl < jn;
-  const int s = first + j0 + (row_ok ? jl : 0);
+  const int nrows = count * G;  // (member, query head) rows of the group
+  const int r0 = 16 * rb;
+  if (P == 0 || r0 >= nrows) return;  // uniform over the workgroup
+
+  // This lane's row (lane & 15): member j, query head hh of KV head g.
+  const int rg = r0 + (lane & 15);
+  const bool row_ok = rg < nrows;
+  const int j = row_ok ? rg / G : 0, hh = row_ok ? rg - j * G : 0;
+  const int s = first + j;
   const int L = clamp_len(a.seq_lens[s], a.len_cap);
   const int64_t qh = int64_t(s) * a.num_q_heads + g * G + hh;
   // Positions every member of the block sees: up to the shortest one's last;
-  // positions some member sees: up to the longest one's last (members'
-  // lengths strided over the lanes, then a wave minimum and maximum).
+  // positions some member sees: up to the longest one's last.
+  const int j_lo = r0 / G, j_hi = min(count, (r0 + 15) / G + 1);
   int lmin = a.len_cap, lmax = 0;
-  for (int m = lane; m < jn; m += 64) {
-    const int lm = clamp_len(a.seq_lens[first + j0 + m], a.len_cap);
+  for (int m = j_lo + lane; m < j_hi; m += 64) {
+    const int lm = clamp_len(a.seq_lens[first + m], a.len_cap);
     lmin = min(lmin, lm);
     lmax = max(lmax, lm);
   }
@@ -150,37 +166,101 @@ attn_prefix_kernel(SharedArgs a) {
   // the fork: the History stops at the longest member, so slots past it load
   // as zeros instead of whatever bits they hold (a masked score with a NaN or
   // infinite V row would still put 0 * NaN into the products).
+  const int len = min(P, lmax);
   const pkv::mfma::History hist{a.k_cache,      a.v_cache,     a.block_tables + int64_t(first) * a.max_blocks,
-                                min(P, lmax),   g,             a.block_elems,
+                                len,            g,             a.block_elems,
                                 a.row_elems,    a.num_blocks,  a.block_shift,
                                 a.num_kv_heads, a.v_scale,     a.k_scales,
                                 a.v_scales};
+  // Wave w walks tiles [w * per, (w + 1) * per) of the prefix, alone (no
+  // workgroup barrier inside: the quarters may differ in length).
+  const int tiles = (len + kKT - 1) / kKT;
+  const int per = (tiles + kW - 1) / kW;
+  const int t_lo = min(w * per * kKT, len), t_hi = min((w + 1) * per * kKT, len);
   pkv::mfma::RowAcc<D> r;
   pkv::mfma::start(r);
-  pkv::mfma::attend<D, NW, (NW >= 2 ? 2 : 1), Q>(hist, t_lo, t_hi, a.q + qh * D, row_ok, L - 1,
-                                                lmin - 1, a.scale_log2, k_lds, v_lds, r, s_lds);
-  if (!row_ok) return;
-  const int64_t slot = qh * (a.pre_parts + a.suf_parts) + part;
-  pkv::mfma::store_piece<D>(r, a.ws_acc + slot * D, a.ws_ml + slot);
+  pkv::mfma::attend<D, 1, 2, Q, false, pkv::mfma::NoEmit, false, true>(
+      hist, t_lo, t_hi, a.q + qh * D, row_ok, L - 1, lmin - 1, a.scale_log2, lds.k[w], lds.v[w],
+      r, lds.s[w]);
+  // The wave's states to its K area: [row][D] weighted sums, then
+  // (reference, sum) per row.
+  float* st = reinterpret_cast<float*>(lds.k[w]);
+  pkv::mfma::store_piece<D>(r, st + (lane & 15) * D, reinterpret_cast<float2*>(st + 16 * D) + (lane & 15));
+  __syncthreads();
+  // Thread t combines row t / 16, elements (t % 16) * D / 16 .. + D / 16 - 1:
+  // the four waves' states and the member's suffix pieces (the suffix kernel
+  // ran before), by log-sum-exp, into the result.
+  constexpr int kE = D / 16;
+  const int t = threadIdx.x;
+  const int crow = t >> 4, d0 = (t & 15) * kE;
+  const int crg = r0 + crow;
+  if (crg >= nrows) return;
+  const int cj = crg / G, ch = crg - cj * G;
+  const int cs = first + cj;
+  const int cL = clamp_len(a.seq_lens[cs], a.len_cap);
+  const int cP = P < cL ? P : cL;
+  // (a member with nothing to attend, cL = 0, was written whole by the
+  // suffix kernel)
+  if (cP == 0) return;
+  const int np_suf = cL > cP ? min(a.suf_parts, (cL - cP + a.suf_tokens - 1) / a.suf_tokens) : 0;
+  const int64_t cqh = int64_t(cs) * a.num_q_heads + g * G + ch;
+  const int64_t base = cqh * a.suf_parts;
+  float M = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < kW; ++v)
+    M = fmaxf(M, reinterpret_cast<const float2*>(reinterpret_cast<const float*>(lds.k[v]) + 16 * D)[crow].x);
+  for (int p = 0; p < np_suf; ++p) M = fmaxf(M, a.ws_ml[base + p].x);
+  float lsum = 0.f, acc[kE];
+#pragma unroll
+  for (int e = 0; e < kE; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int v = 0; v < kW; ++v) {
+    const float* sv = reinterpret_cast<const float*>(lds.k[v]);
+    const float2 ml = reinterpret_cast<const float2*>(sv + 16 * D)[crow];
+    const float wgt = pkv::fast_exp2(ml.x - M);
+    lsum = fmaf(wgt, ml.y, lsum);
+#pragma unroll
+    for (int e = 0; e < kE; ++e) acc[e] = fmaf(wgt, sv[crow * D + d0 + e], acc[e]);
+  }
+  for (int p = 0; p < np_suf; ++p) {
+    const float2 ml = a.ws_ml[base + p];
+    const float wgt = pkv::fast_exp2(ml.x - M);
+    lsum = fmaf(wgt, ml.y, lsum);
+    const float* src = a.ws_acc + (base + p) * D + d0;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) acc[e] = fmaf(wgt, src[e], acc[e]);
+  }
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  uint16_t* dst = a.out + cqh * D + d0;
+#pragma unroll
+  for (int e = 0; e < kE; e += 2)
+    *reinterpret_cast<uint32_t*>(dst + e) = pkv::pack_bf16x2(acc[e] * inv, acc[e + 1] * inv);
 }
 
-// grid = (suf_parts, H_kv, num_seqs).
-template <int D, int NW, int Q>
-__global__ void __launch_bounds__(64 * NW)
-__attribute__((amdgpu_waves_per_eu(NW == 4 ? 3 : 1)))
-attn_suffix_kernel(SharedArgs a) {
-  __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D, NW, Q>()];
-  __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D, NW, Q>()];
-  __shared__ float s_lds[pkv::mfma::s_lds_elems<Q, NW>()];
+// Suffix role: wave item i = (row group, part, KV head, sequence), row group
+// fastest: query heads 16 rg .. 16 rg + 15 of the KV head's group, positions
+// P + part * suf_tokens .. of the sequence's own (part, part + suf_parts, ...:
+// a suffix longer than the grid was sized for is folded into the same
+// piece).  A sequence without a shared prefix is attended whole by its part
+// 0 items, which write the result.
+template <int D, int Q>
+__device__ void suffix_role(const SharedArgs& a, int64_t item, SharedLds<D, Q, 1>& lds) {
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int s = blockIdx.z, g = blockIdx.y, part = blockIdx.x;
+  constexpr int w = 0;
+  const int rgs = (a.group + 15) / 16;
+  const int rgi = static_cast<int>(item % rgs);
+  const int part = static_cast<int>((item / rgs) % a.suf_parts);
+  const int g = static_cast<int>((item / (int64_t(rgs) * a.suf_parts)) % a.num_kv_heads);
+  const int64_t s64 = item / (int64_t(rgs) * a.suf_parts * a.num_kv_heads);
+  if (s64 >= a.num_seqs) return;
+  const int s = static_cast<int>(s64);
   const int L = clamp_len(a.seq_lens[s], a.len_cap);
   const int P = seq_prefix(a, s, L);
-  if (P + part * a.suf_tokens >= L) return;  // the merge counts only parts holding positions
+  const bool whole = P == 0;
+  if (whole ? part > 0 : P + part * a.suf_tokens >= L) return;
 
   const int G = a.group;
-  const int hh = 16 * w + (lane & 15);
+  const int hh = 16 * rgi + (lane & 15);
   const bool row_ok = hh < G;
   const int64_t qh = int64_t(s) * a.num_q_heads + g * G + (row_ok ? hh : 0);
   const pkv::mfma::History hist{a.k_cache,      a.v_cache,     a.block_tables + int64_t(s) * a.max_blocks,
@@ -190,70 +270,46 @@ attn_suffix_kernel(SharedArgs a) {
                                 a.v_scales};
   pkv::mfma::RowAcc<D> r;
   pkv::mfma::start(r);
-  // Partitions part, part + suf_parts, ...: a suffix longer than the grid was
-  // sized for is folded into the same piece.
+  constexpr int kPD = shared_pd<Q>();
+  if (whole) {
+    pkv::mfma::attend<D, 1, kPD, Q, false, pkv::mfma::NoEmit, false, true>(
+        hist, 0, L, a.q + qh * D, row_ok, L - 1, L - 1, a.scale_log2, lds.k[w], lds.v[w], r,
+        lds.s[w]);
+    if (row_ok) pkv::mfma::store_row_bf16<D>(r, a.out + qh * D);
+    return;
+  }
   for (int t_lo = P + part * a.suf_tokens; t_lo < L; t_lo += a.suf_parts * a.suf_tokens)
-    pkv::mfma::attend<D, NW, (NW >= 2 ? 2 : 1), Q>(hist, t_lo, min(t_lo + a.suf_tokens, L),
-                                                  a.q + qh * D, row_ok, L - 1, L - 1,
-                                                  a.scale_log2, k_lds, v_lds, r, s_lds);
+    pkv::mfma::attend<D, 1, kPD, Q, false, pkv::mfma::NoEmit, false, true>(
+        hist, t_lo, min(t_lo + a.suf_tokens, L), a.q + qh * D, row_ok, L - 1, L - 1,
+        a.scale_log2, lds.k[w], lds.v[w], r, lds.s[w]);
   if (!row_ok) return;
-  const int64_t slot = qh * (a.pre_parts + a.suf_parts) + a.pre_parts + part;
+  const int64_t slot = qh * a.suf_parts + part;
   pkv::mfma::store_piece<D>(r, a.ws_acc + slot * D, a.ws_ml + slot);
 }
 
-// One wave per (head, sequence): log-sum-exp over the prefix pieces and the
-// suffix pieces that hold positions of this sequence.
-template <int D>
+// grid = pre_blocks, four waves.
+template <int D, int Q>
+__global__ void __launch_bounds__(64 * kSharedWaves)
+__attribute__((amdgpu_waves_per_eu(2)))
+attn_prefix_kernel(SharedArgs a) {
+  __shared__ __align__(16) SharedLds<D, Q, kSharedWaves> lds;
+  prefix_role<D, Q>(a, static_cast<int>(blockIdx.x), lds);
+}
+
+// grid = suffix items, one wave each.
+template <int D, int Q>
 __global__ void __launch_bounds__(64)
-attn_shared_merge_kernel(SharedArgs a) {
-  constexpr int kE = D / 64;
-  const int h = blockIdx.x, s = blockIdx.y;
-  const int lane = threadIdx.x;
-  const int L = clamp_len(a.seq_lens[s], a.len_cap);
-  const int P = seq_prefix(a, s, L);
-  const int np_pre = (P + a.pre_tokens - 1) / a.pre_tokens;
-  const int np_suf = min(a.suf_parts, (L - P + a.suf_tokens - 1) / a.suf_tokens);
-  const int64_t qh = int64_t(s) * a.num_q_heads + h;
-  const int64_t base = qh * (a.pre_parts + a.suf_parts);
-  float M = -INFINITY;
-  for (int p = lane; p < np_pre + np_suf; p += 64) {
-    const int slot = p < np_pre ? p : a.pre_parts + (p - np_pre);
-    M = fmaxf(M, a.ws_ml[base + slot].x);
-  }
-  M = pkv::wave_max(M);
-  float lsum = 0.f, acc[kE];
-#pragma unroll
-  for (int e = 0; e < kE; ++e) acc[e] = 0.f;
-  for (int p = 0; p < np_pre + np_suf; ++p) {
-    const int slot = p < np_pre ? p : a.pre_parts + (p - np_pre);
-    const float2 ml = a.ws_ml[base + slot];
-    const float wgt = pkv::fast_exp2(ml.x - M);
-    lsum = fmaf(wgt, ml.y, lsum);
-    const float* src = a.ws_acc + (base + slot) * D;
-#pragma unroll
-    for (int e = 0; e < kE; ++e) acc[e] = fmaf(wgt, src[lane * kE + e], acc[e]);
-  }
-  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-  uint16_t* dst = a.out + qh * D + lane * kE;
-#pragma unroll
-  for (int e = 0; e < kE; ++e) dst[e] = static_cast<uint16_t>(pkv::f32_to_bf16_bits(acc[e] * inv));
+attn_suffix_kernel(SharedArgs a) {
+  __shared__ __align__(16) SharedLds<D, Q, 1> lds;
+  suffix_role<D, Q>(a, int64_t(blockIdx.x), lds);
 }
 
 int64_t round_up_to(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
-// Partition length for `items` work items over histories up to `len`: split
-// until about 2048 workgroups exist, never below 256 positions.
-int part_tokens_for(int64_t items, int len) {
-  const int64_t parts = items >= 2048 ? 1 : (2048 + items - 1) / (items > 0 ? items : 1);
-  int64_t pt = round_up_to((int64_t(len) + parts - 1) / parts, kKT);
-  if (pt < 256) pt = 256;
-  const int64_t full = round_up_to(len > 0 ? len : 1, kKT);
-  return static_cast<int>(pt < full ? pt : full);
-}
-
 struct SharedPlan {
-  int nw_pre, nw_suf, members_per_block, row_blocks;
-  int pre_parts, pre_tokens, suf_parts, suf_tokens;
+  int row_blocks, pre_blocks;
+  int suf_parts, suf_tokens;
+  int64_t suf_blocks;
   size_t ws_bytes, ws_ml_off;
 };
 
@@ -288,18 +344,9 @@ pkv_status shared_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_groups
   if (num_seqs > 65535 || num_groups > 65535 || g->num_kv_heads > 65535)
     return pkv::fail(PKV_ERR_INVALID_ARG, "%s: more than 65535 sequences, groups or KV heads", who);
   const int mg = max_group_size > 0 ? max_group_size : 1;
-  // 16 (member, head) rows per wave, up to 4 waves (eight measured no faster
-  // on the shared-prefix configuration)
-  const int per64 = 64 / G;
-  const int rows = (mg < per64 ? mg : per64) * G;
-  pl->nw_pre = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
-  pl->members_per_block = 16 * pl->nw_pre / G;
-  pl->row_blocks = (mg + pl->members_per_block - 1) / pl->members_per_block;
-  pl->nw_suf = G <= 16 ? 1 : (G <= 32 ? 2 : 4);
-  const int pre_len = max_prefix_len > 0 ? max_prefix_len : 1;
+  // 16 (member, query head) rows per prefix workgroup
+  pl->row_blocks = static_cast<int>((int64_t(mg) * G + 15) / 16);
   const int seq_len = max_seq_len > 0 ? max_seq_len : 1;
-  pl->pre_tokens =
-      part_tokens_for(int64_t(num_groups) * g->num_kv_heads * pl->row_blocks, pre_len);
   // Suffix partitions from the longest suffix (a hint: longer suffixes are
   // folded into the grid's pieces): short critical paths, about 4096 items.
   const int suf_len = max_suffix_len > 0 && max_suffix_len < seq_len ? max_suffix_len : seq_len;
@@ -308,34 +355,28 @@ pkv_status shared_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_groups
   int64_t spt = round_up_to((suf_len + want - 1) / want, kKT);
   if (spt < 64) spt = 64;
   pl->suf_tokens = static_cast<int>(spt);
-  pl->pre_parts = (pre_len + pl->pre_tokens - 1) / pl->pre_tokens;
   pl->suf_parts = static_cast<int>((suf_len + spt - 1) / spt);
-  if (int64_t(pl->row_blocks) * pl->pre_parts > 2147483647LL)
-    return pkv::fail(PKV_ERR_INVALID_ARG, "%s: too many prefix work items", who);
-  const size_t slots = size_t(num_seqs) * num_q_heads * (pl->pre_parts + pl->suf_parts);
+  const int64_t pre_blocks = int64_t(num_groups) * g->num_kv_heads * pl->row_blocks;
+  const int64_t wave_items = int64_t(num_seqs) * g->num_kv_heads * pl->suf_parts * ((G + 15) / 16);
+  pl->suf_blocks = wave_items;
+  if (pre_blocks + pl->suf_blocks > 2147483647LL)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "%s: too many work items", who);
+  pl->pre_blocks = static_cast<int>(pre_blocks);
+  const size_t slots = size_t(num_seqs) * num_q_heads * pl->suf_parts;
   pl->ws_ml_off = slots * g->head_dim * sizeof(float);
   pl->ws_bytes = pl->ws_ml_off + slots * sizeof(float2);
   return PKV_OK;
 }
 
 template <int D, int Q>
-void launch_shared(const SharedPlan& pl, const SharedArgs& a, int num_kv_heads, hipStream_t st) {
-  if (a.num_groups > 0 && a.max_prefix > 0) {
-    const dim3 grid(pl.row_blocks * pl.pre_parts, num_kv_heads, a.num_groups);
-    switch (pl.nw_pre) {
-      case 1: hipLaunchKernelGGL((attn_prefix_kernel<D, 1, Q>), grid, dim3(64), 0, st, a); break;
-      case 2: hipLaunchKernelGGL((attn_prefix_kernel<D, 2, Q>), grid, dim3(128), 0, st, a); break;
-      default: hipLaunchKernelGGL((attn_prefix_kernel<D, 4, Q>), grid, dim3(256), 0, st, a); break;
-    }
-  }
-  const dim3 grid(pl.suf_parts, num_kv_heads, a.num_seqs);
-  switch (pl.nw_suf) {
-    case 1: hipLaunchKernelGGL((attn_suffix_kernel<D, 1, Q>), grid, dim3(64), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((attn_suffix_kernel<D, 2, Q>), grid, dim3(128), 0, st, a); break;
-    default: hipLaunchKernelGGL((attn_suffix_kernel<D, 4, Q>), grid, dim3(256), 0, st, a); break;
-  }
-  hipLaunchKernelGGL((attn_shared_merge_kernel<D>), dim3(a.num_q_heads, a.num_seqs), dim3(64), 0,
-                     st, a);
+hipError_t launch_shared(const SharedPlan& pl, const SharedArgs& a, hipStream_t st) {
+  if (pl.suf_blocks > 0)
+    hipLaunchKernelGGL((attn_suffix_kernel<D, Q>), dim3(static_cast<uint32_t>(pl.suf_blocks)),
+                       dim3(64), 0, st, a);
+  if (a.pre_blocks > 0)
+    hipLaunchKernelGGL((attn_prefix_kernel<D, Q>), dim3(static_cast<uint32_t>(a.pre_blocks)),
+                       dim3(64 * kSharedWaves), 0, st, a);
+  return hipSuccess;
 }
 
 pkv_status shared_impl(const char* who, int types, const void* q, const void* k_cache,
@@ -409,10 +450,9 @@ pkv_status shared_impl(const char* who, int types, const void* q, const void* k_
   a.len_cap = static_cast<int32_t>(max_seq_len < cap ? max_seq_len : cap);
   a.max_prefix = max_prefix_len < a.len_cap ? max_prefix_len : a.len_cap;
   a.max_group = max_group_size;
-  a.members_per_block = pl.members_per_block;
-  a.pre_parts = pl.pre_parts;
-  a.pre_tokens = pl.pre_tokens;
   a.suf_parts = pl.suf_parts;
+  a.row_blocks = pl.row_blocks;
+  a.pre_blocks = a.max_prefix > 0 ? pl.pre_blocks : 0;
   a.suf_tokens = pl.suf_tokens;
   a.scale_log2 = static_cast<float>(double(scale) * 1.4426950408889634 *
                                     (kind == pkv::mfma::kFp8 ? double(scales->k_scale) : 1.0));
@@ -420,15 +460,17 @@ pkv_status shared_impl(const char* who, int types, const void* q, const void* k_
   a.k_scales = kind == pkv::mfma::kInt8 ? scales->k_scales : nullptr;
   a.v_scales = kind == pkv::mfma::kInt8 ? scales->v_scales : nullptr;
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
   if (kind == pkv::mfma::kFp8)
-    launch_shared<128, pkv::mfma::kFp8>(pl, a, geom->num_kv_heads, st);
+    e = launch_shared<128, pkv::mfma::kFp8>(pl, a, st);
   else if (kind == pkv::mfma::kInt8)
-    launch_shared<128, pkv::mfma::kInt8>(pl, a, geom->num_kv_heads, st);
+    e = launch_shared<128, pkv::mfma::kInt8>(pl, a, st);
   else if (geom->head_dim == 128)
-    launch_shared<128, pkv::mfma::kBf16>(pl, a, geom->num_kv_heads, st);
+    e = launch_shared<128, pkv::mfma::kBf16>(pl, a, st);
   else
-    launch_shared<64, pkv::mfma::kBf16>(pl, a, geom->num_kv_heads, st);
-  if (hipError_t e = hipGetLastError())
+    e = launch_shared<64, pkv::mfma::kBf16>(pl, a, st);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess)
     return pkv::fail(PKV_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return PKV_OK;
 }

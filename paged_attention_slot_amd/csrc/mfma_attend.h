@@ -242,7 +242,7 @@ struct NewRow {
 };
 
 template <int D, int NW, int PD = 1, int Q = kBf16, bool kStream = false, class Emit = NoEmit,
-          bool kAppend = false>
+          bool kAppend = false, bool kWaveOnly = false>
 __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, const uint16_t* q,
                                        bool row_ok, int p_row, int p_all, float scale_log2,
                                        uint16_t* k_lds, uint16_t* v_lds, RowAcc<D>& r,
@@ -251,6 +251,15 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
   static_assert(!kAppend || Q == kBf16, "the folded append takes bf16 pools");
   static_assert(!kAppend || NW == 1, "the folded append runs in single-wave passes");
   static_assert(NW == 1 || PD == 2, "several waves keep two tiles of registers in flight");
+  static_assert(!kWaveOnly || NW == 1, "a wave-only walk is a single wave's");
+  // A single wave's LDS accesses run in order: it waits for its own and
+  // needs the workgroup barrier only when its workgroup is one wave.  A
+  // wave-only walk (kWaveOnly: one of several independent walks in a
+  // workgroup, possibly of different lengths) never touches the barrier.
+  const auto sync_lds = [] {
+    if constexpr (kWaveOnly) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    else lds_barrier();
+  };
   constexpr bool kDirect = direct_lds<D, NW, Q>();
   constexpr float kSlack = 8.0f;
   constexpr int kEB = Q == kBf16 ? 2 : 1;   // bytes per element
@@ -261,7 +270,10 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
   constexpr int kEPC = 16 / kEB;         // elements per 16-byte chunk
   constexpr int kChunksPerRow = D / kEPC;  // 16-byte chunks per K/V row
   constexpr int kChunks = kKT * kChunksPerRow;
-  const int tid = threadIdx.x, lane = tid & 63;
+  // (a single-wave walk uses its lane only: it may be one of several walks
+  // in a workgroup)
+  const int tid = NW == 1 ? static_cast<int>(threadIdx.x & 63) : static_cast<int>(threadIdx.x);
+  const int lane = tid & 63;
   const int quad = lane >> 4;
 
   // Scores are scaled inside the exponent (one fma with the reference) and
@@ -599,7 +611,7 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
         if (t >= t_hi) break;  // uniform
         stage_k(j, 0, 0, t);
         stage_v(j, 0, t);
-        lds_barrier();
+        sync_lds();
         // the register set just staged takes the tile PD ahead, in flight
         // meanwhile
         if (t + PD * kKT < t_hi) fetch_v(j, t + PD * kKT, fetch_k(j, t + PD * kKT));
@@ -783,7 +795,7 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
   }
   r.lsum = sum_across_rows16(lpart);
   // the caller may reuse the LDS (another pass) right after
-  lds_barrier();
+  sync_lds();
 }
 
 // Store this lane's fragment of a row's state as a piece: D floats of
