@@ -285,29 +285,30 @@ int32_t pkv_attention_partition_tokens(int32_t num_seqs, int32_t num_q_heads,
  * partitions a piece is exactly one partition (the result is the log-sum-exp
  * merge of the partitions' states).  On the matrix-core route the partition
  * length is the finest split asked for: when there are more (sequence, KV
- * head, partition) items than the GPU holds at once, one workgroup walks an
- * equal share of a history, cut at whole 32-position tiles, and folds it into
- * one piece (the merge of its partitions' states up to fp32 rounding order),
- * so a piece can span several partitions: for 4 histories of 131,072
- * positions, 8 KV heads and 512-token partitions, 96 pieces of 1,376
+ * head, partition) items than the GPU holds at once, one workgroup walks a
+ * run of consecutive whole partitions (about 2048 runs in all) and folds it
+ * into one piece (the merge of its partitions' states up to fp32 rounding
+ * order), so a piece can span several partitions: for 4 histories of
+ * 131,072 positions, 8 KV heads and 512-token partitions, 64 pieces of 2,048
  * positions each.  Returns the history length rounded up to a whole tile
- * when nothing is split, 0 on the balanced split (its pieces are intervals of
- * the batch's global tile order, not of one history) or on invalid
- * arguments. */
+ * when nothing is split, 0 on the balanced splits (their pieces are
+ * intervals of the batch's global tile order, not of one history) or on
+ * invalid arguments. */
 int32_t pkv_attention_piece_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
                                    int32_t partition_tokens, const pkv_geom* geom);
 
 /* Which kernels pkv_attention_decode (and its _phase, _append and _quant
  * forms) runs for these sizes: PKV_ROUTE_PARTITIONS (vector kernels, fixed
  * partitions), PKV_ROUTE_BALANCED (vector kernels, the balanced split) or
- * PKV_ROUTE_MATRIX (groups of 8 or more query heads per KV head at head_dim
- * 128, bf16 or one-byte pools, partition_tokens 0 or a multiple of 32: the
- * matrix-core pass of pkv_attention_multi with one query per sequence, fixed
- * partitions merged by log-sum-exp) or PKV_ROUTE_MATRIX_BALANCED (2 to 7
- * query heads per KV head at head_dim 128, bf16 or one-byte pools,
- * partition_tokens 0: the balanced split's intervals walked by one-wave
- * workgroups on the matrix cores, the group's heads as the rows of the
- * products).  PKV_ATTN_MODE overrides.  -1 on invalid arguments. */
+ * PKV_ROUTE_MATRIX (head_dim 128, bf16 or one-byte pools: more than 16
+ * query heads per KV head with partition_tokens 0 or a multiple of 32, or 8
+ * to 16 with a given multiple of 32: the matrix-core pass of
+ * pkv_attention_multi with one query per sequence, fixed partitions merged by
+ * log-sum-exp) or PKV_ROUTE_MATRIX_BALANCED (2 to 16 query heads per KV head
+ * at head_dim 128, bf16 or one-byte pools, partition_tokens 0: the balanced
+ * split's intervals walked by one-wave workgroups on the matrix cores, the
+ * group's heads as the rows of the products).  PKV_ATTN_MODE overrides.  -1
+ * on invalid arguments. */
 enum { PKV_ROUTE_PARTITIONS = 0, PKV_ROUTE_BALANCED = 1, PKV_ROUTE_MATRIX = 2,
        PKV_ROUTE_MATRIX_BALANCED = 3 };
 int32_t pkv_attention_decode_route(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
@@ -354,24 +355,24 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *                 share of 85 % of all K/V tiles of the batch, and further
  *                 workgroups, dispatched as those retire, take small chunks of
  *                 the rest; a sequence's history that spans several of these
- *                 intervals is merged the same way.  With 2 to 7 query heads
- *                 per KV head at head_dim 128 (bf16 or one-byte pools) the
- *                 intervals (of 32-position tiles) are walked on the matrix
- *                 cores, the group's heads as the rows of the products; with
- *                 one head per group, head_dim 64 or fp32 pools, on the
- *                 vector units.  Groups of 8 or more
- *                 query heads per KV head (head_dim 128) run on the matrix
- *                 cores instead, with fixed partitions (a multiple of 32;
- *                 automatic: about 3072 (sequence, KV head, partition) items
- *                 of at least 256 positions); see
- *                 pkv_attention_decode_route.  There a workgroup folds the
- *                 positions it walks into one piece: single partitions when
- *                 they alone fill the GPU, else equal shares of each history
- *                 (about 3072 workgroups in all), which equals the merge of
- *                 the partition pieces up to fp32 rounding order.  So on that
- *                 route partition_tokens is the finest split asked for, not
- *                 the split that runs: pkv_attention_piece_tokens says what
- *                 one piece covers.
+ *                 intervals is merged the same way.  With 2 to 16 query
+ *                 heads per KV head at head_dim 128 (bf16 or one-byte pools)
+ *                 the intervals (of 32-position tiles) are walked on the
+ *                 matrix cores, the group's heads as the rows of the
+ *                 products; with one head per group, head_dim 64 or fp32
+ *                 pools, on the vector units.  Groups of more than 16 query
+ *                 heads per KV head, and groups of 8 to 16 with a given
+ *                 partition length (a multiple of 32), run on the matrix
+ *                 cores with fixed partitions (automatic: about 3072
+ *                 (sequence, KV head, partition) items of at least 256
+ *                 positions); see pkv_attention_decode_route.  There a
+ *                 workgroup folds the positions it walks into one piece:
+ *                 single partitions when they alone fill the GPU, else runs
+ *                 of consecutive whole partitions (about 2048 workgroups in
+ *                 all), which equals the merge of the partition pieces up to
+ *                 fp32 rounding order.  So on that route partition_tokens is
+ *                 the finest split asked for, not the split that runs:
+ *                 pkv_attention_piece_tokens says what one piece covers.
  *   workspace     device buffer of at least pkv_attention_workspace_bytes(...)
  *                 bytes (may be NULL when that is 0); contents on entry are
  *                 ignored.  Calls that may run at the same time need
@@ -554,7 +555,7 @@ pkv_status pkv_attention_multi_quant(const void* q, const int32_t* q_offsets, co
  *   PKV_ATTN_PARTS_PER_WG    1..65535  matrix-core passes: consecutive
  *                                  partitions one workgroup walks (the decode
  *                                  route folds them into one piece, instead
- *                                  of its equal shares)
+ *                                  of its automatic runs)
  *   PKV_ATTN_APPEND          pkv_attention_decode_append: 1 = copy kernel
  *                                  first, 2 = folded into the attention kernel
  *                                  (vector routes with non-temporal loads only)

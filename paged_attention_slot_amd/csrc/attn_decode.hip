@@ -68,6 +68,10 @@ constexpr int kMaxWaveGroups = 8192;    // the workspace is sized for this many 
 constexpr int kDynamicPerMille = 150;   // balanced split: tiles handed out dynamically
 constexpr int kMinChunkTiles = 4;       // smallest dynamic chunk
 constexpr int kMaxChunks = 8192;        // the workspace is sized for this many chunks
+// The matrix-core balanced split: at most this many static workgroups (one
+// wave each; about 2048 are resident on 256 CUs), and so at most as many
+// dynamic chunks (a chunk count never exceeds the static count).
+constexpr int kMaxMatrixGroups = 3072;
 
 enum Mode : int { kPartitionMode = 0, kBalancedMode = 1, kMatrixMode = 2, kMatrixBalancedMode = 3 };
 
@@ -975,7 +979,8 @@ attn_merge_balanced_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // Balanced split on the matrix cores: the balanced split's intervals over the
-// batch's global tile order (tiles of 32 positions here), each walked by a
+// batch's global order of cut units (32-position tiles, or partitions of
+// partition_tokens positions when the caller gives one), each walked by a
 // one-wave workgroup with the matrix-core pass of the multi-token kernel
 // (pkv::mfma::attend): the G <= 16 query heads of a KV head are the rows of
 // the 16-row products, so q.k and p.v run on the matrix cores and only the
@@ -986,10 +991,9 @@ attn_merge_balanced_kernel(AttnArgs a) {
 // records are the balanced split's, so attn_merge_balanced_kernel merges
 // them.
 // ---------------------------------------------------------------------------
-constexpr int kMT = pkv::mfma::kKT;  // positions per tile on the matrix cores
-
-__device__ __forceinline__ int stream_tiles32(const AttnArgs& a, int s) {
-  return (clamp_len(a.seq_lens[s], a.len_cap) + kMT - 1) / kMT;
+// Cut units of a stream (a.part_tokens positions each, a multiple of 32).
+__device__ __forceinline__ int stream_units(const AttnArgs& a, int s) {
+  return (clamp_len(a.seq_lens[s], a.len_cap) + a.part_tokens - 1) / a.part_tokens;
 }
 
 // grid = static workgroups (the resident ones) + dynamic chunks, 64 threads;
@@ -1014,14 +1018,14 @@ attn_mfma_balanced_kernel(AttnArgs a) {
   const int s0 = lane * per;
   int tsum = 0;
   for (int i = 0; i < per; ++i)
-    if (s0 + i < N) tsum += Hkv * stream_tiles32(a, s0 + i);
+    if (s0 + i < N) tsum += Hkv * stream_units(a, s0 + i);
   const int incl = wave_incl_scan(tsum);
   const int total = __shfl(incl, 63, 64);
   int run = incl - tsum;
   for (int i = 0; i < per; ++i) {
     if (s0 + i < N) {
       base[s0 + i] = run;
-      run += Hkv * stream_tiles32(a, s0 + i);
+      run += Hkv * stream_units(a, s0 + i);
     }
   }
   if (lane == 0) base[N] = total;
@@ -1087,8 +1091,9 @@ attn_mfma_balanced_kernel(AttnArgs a) {
     // one-byte tiles are half the registers: two in flight ahead of the one
     // being computed, at the same occupancy
     constexpr int kPD = Q == pkv::mfma::kBf16 ? 1 : 2;
+    const int U = a.part_tokens;
     pkv::mfma::attend<D, 1, kPD, Q, kStream, pkv::mfma::NoEmit, kAppend>(
-        hist, t0 * kMT, min((t0 + seg) * kMT, L), q + qh * D, row_ok, L - 1, L - 1, scale_log2,
+        hist, t0 * U, min((t0 + seg) * U, L), q + qh * D, row_ok, L - 1, L - 1, scale_log2,
         k_lds, v_lds, r, s_lds, 0, pkv::mfma::NoEmit(), nr);
     const int64_t k = int64_t(s) * Hkv + kvh;
     if (lane == 0) {  // the stream's first and last intervals, for the merge
@@ -1210,22 +1215,29 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
                            (wpg == 1 || wpg == 2 || wpg == 4 || wpg == 8) &&
                            int64_t(num_seqs) * g->num_kv_heads * stream_tiles_max < (int64_t(1) << 31);
   const int km = knob_mode();
-  // Groups of 8 or more query heads per KV head go to the matrix cores: the
-  // vector kernels are bound by instruction issue there (a wave carries at
-  // most 4 heads), while the matrix-core pass does the q.k and p.v products
-  // for 16 heads at once and keeps only the softmax on the vector units.
+  // Groups of 8 or more query heads per KV head belong on the matrix cores:
+  // the vector kernels are bound by instruction issue there (a wave carries
+  // at most 4 heads), while the matrix-core pass does the q.k and p.v
+  // products for 16 heads at once and keeps only the softmax on the vector
+  // units (the fixed-partition route below takes those the balanced split
+  // does not).
   const bool matrix_ok = g->head_dim == 128 && (g->dtype == PKV_BF16 || pkv::is_quant(g->dtype)) &&
                          partition_tokens % 32 == 0 && g->num_kv_heads <= 65535;
-  // 2 to 7 query heads per KV head (head_dim 128, bf16 or one-byte codes):
-  // the balanced split on the matrix cores.  For one-byte codes the vector
-  // kernels are issue-bound decoding the codes; for bf16 the matrix cores
-  // match them on unshared batches (the llama3-8b layer: 718 against 720 us,
-  // the qwen layer: 91.7 against 95.4 us) and beat them where blocks are
-  // shared (the shared-prefix config: 153.5 against 177.0 us).
-  const int64_t tiles32_max = (int64_t(pl->len_cap) + 31) / 32;
+  // 2 to 16 query heads per KV head (head_dim 128, bf16 or one-byte codes,
+  // automatic partitions): the balanced split on the matrix cores.  For
+  // one-byte codes the vector kernels are issue-bound decoding the codes; for
+  // bf16 the matrix cores match them on unshared batches (the llama3-8b
+  // layer: 718 against 720 us, the qwen layer: 91.7 against 95.4 us) and beat
+  // them where blocks are shared (the shared-prefix config: 153.5 against
+  // 177.0 us) and on long histories with 8 heads per group (the 70b layer:
+  // 334 against 360 us on the fixed-partition matrix route).  The cut unit
+  // stays one tile: partitions given by the caller take the fixed-partition
+  // routes.
+  const int unit = 32;
+  const int64_t units_max = (int64_t(pl->len_cap) + unit - 1) / unit;
   const bool mbal_ok = matrix_ok && partition_tokens == 0 && num_seqs <= kMaxBalancedSeqs &&
-                       G <= 16 && int64_t(num_seqs) * g->num_kv_heads * tiles32_max < (int64_t(1) << 31);
-  if (mbal_ok && (km == 4 || (km == 0 && G >= 2 && G < 8))) {
+                       G <= 16 && int64_t(num_seqs) * g->num_kv_heads * units_max < (int64_t(1) << 31);
+  if (mbal_ok && (km == 4 || (km == 0 && G >= 2))) {
     pl->mode = kMatrixBalancedMode;
     pl->gw = G;
     pl->waves_per_group = 1;
@@ -1234,15 +1246,15 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
     pl->waves_per_item = pl->blocks_per_item = 0;
     pl->groups_per_block = 1;
     pl->num_parts = 0;
-    pl->part_tokens = 0;
-    pl->rows = (int64_t(num_seqs) * g->num_kv_heads + kMaxWaveGroups + kMaxChunks) * G;
+    pl->part_tokens = unit;  // the cut unit
+    pl->rows = (int64_t(num_seqs) * g->num_kv_heads + 2 * kMaxMatrixGroups) * G;
     const size_t acc = size_t(pl->rows) * g->head_dim * sizeof(float);
     pl->ws_ml_off = acc;
     pl->ws_span_off = acc + size_t(pl->rows) * sizeof(float2);
     pl->ws_bytes = pl->ws_span_off + round_up(int64_t(num_seqs) * g->num_kv_heads * 8, 256);
-    const int64_t tmax = int64_t(num_seqs) * g->num_kv_heads * tiles32_max;
+    const int64_t tmax = int64_t(num_seqs) * g->num_kv_heads * units_max;
     const int64_t kb = (tmax * kDynamicPerMille / 1000 + kMinChunkTiles - 1) / kMinChunkTiles;
-    pl->max_chunks = static_cast<int>(kb < kMaxChunks ? kb : kMaxChunks);
+    pl->max_chunks = static_cast<int>(kb < kMaxMatrixGroups ? kb : kMaxMatrixGroups);
     return PKV_OK;
   }
   if (matrix_ok && (km == 3 || (km == 0 && G >= 8))) {
@@ -1267,7 +1279,7 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len,
     pl->part_tokens = static_cast<int>(pt);
     pl->num_parts = static_cast<int>(np);
     pl->runs = pkv::decode_runs(num_seqs, g->num_kv_heads, pl->len_cap, pl->part_tokens,
-                                pl->num_parts);
+                                pl->num_parts, 2048);
     if (pl->runs.runs > 1) {
       pl->rows = int64_t(num_seqs) * num_q_heads * pl->runs.runs;
       pl->ws_ml_off = size_t(pl->rows) * g->head_dim * sizeof(float);
@@ -1764,7 +1776,7 @@ pkv_status attention_impl(const char* who, int32_t phases, const void* q, const 
     int blocks = resident_blocks(kern, 64, lds);
     if (blocks <= 0)
       return pkv::fail(PKV_ERR_HIP, "%s: occupancy query failed", who);
-    if (blocks > kMaxWaveGroups) blocks = kMaxWaveGroups;
+    if (blocks > kMaxMatrixGroups) blocks = kMaxMatrixGroups;
     a.num_groups = blocks;
     a.static_blocks = blocks;
     if (phases & 1) {

@@ -257,11 +257,11 @@ pkv_status multi_plan(int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
     return pkv::fail(PKV_ERR_INVALID_ARG, "%s: too many partitions or query blocks", who);
   pl->num_parts = static_cast<int>(np);
   // Runs of positions per workgroup, each folded into one piece (as on the
-  // decode route): single partitions when they fill the GPU, else equal
-  // shares of about 3072 workgroups.
+  // decode route): single partitions up to 4096 workgroups, else runs of
+  // whole partitions, about 4096 of them.
   const pkv::DecodeRuns dr =
       pkv::decode_runs(static_cast<int32_t>(int64_t(num_seqs) * pl->qblocks), g->num_kv_heads,
-                       len, pl->part_tokens, pl->num_parts);
+                       len, pl->part_tokens, pl->num_parts, 4096);
   pl->run_tokens = dr.run_tokens;
   pl->runs = dr.runs;
   if (pl->runs > 1) {
@@ -415,7 +415,7 @@ pkv_status multi_impl(const char* who, int types, const void* q, const int32_t* 
 namespace pkv {
 
 DecodeRuns decode_runs(int32_t num_seqs, int32_t num_kv_heads, int32_t len_cap,
-                       int32_t part_tokens, int32_t num_parts) {
+                       int32_t part_tokens, int32_t num_parts, int64_t fill) {
   DecodeRuns d;
   const int64_t items = int64_t(num_seqs) * num_kv_heads;
   const int64_t wgs = items * num_parts;
@@ -424,14 +424,13 @@ DecodeRuns decode_runs(int32_t num_seqs, int32_t num_kv_heads, int32_t len_cap,
     const int64_t ppw = knob < num_parts ? knob : num_parts;
     d.run_tokens = static_cast<int32_t>(ppw * part_tokens);
     d.runs = static_cast<int32_t>((num_parts + ppw - 1) / ppw);
-  } else if (wgs > 4096) {
-    // equal shares: about 3072 / items runs per history, cut at tiles
-    const int64_t tiles = len_cap > 0 ? (int64_t(len_cap) + kKT - 1) / kKT : 1;
-    int64_t w = (3072 + items - 1) / (items > 0 ? items : 1);
-    if (w > tiles) w = tiles;
-    const int64_t r = (tiles + w - 1) / w;
-    d.run_tokens = static_cast<int32_t>(r * kKT);
-    d.runs = static_cast<int32_t>((tiles + r - 1) / r);
+  } else if (wgs > fill) {
+    // runs of whole partitions, about fill / items per history
+    int64_t w = (fill + items - 1) / (items > 0 ? items : 1);
+    if (w > num_parts) w = num_parts;
+    const int64_t ppw = (num_parts + w - 1) / w;
+    d.run_tokens = static_cast<int32_t>(ppw * part_tokens);
+    d.runs = static_cast<int32_t>((num_parts + ppw - 1) / ppw);
   } else {
     d.run_tokens = part_tokens;
     d.runs = num_parts;

@@ -17,18 +17,21 @@ namespace pkv {
 // (run_tokens a multiple of 32) and leaves one piece, the online-softmax
 // state of its positions, at piece index r.  Runs are single partitions when
 // those alone fill the GPU; with more partitions than that (or whole runs of
-// PKV_ATTN_PARTS_PER_WG partitions) a run folds consecutive positions into one
-// piece, which is what a merge of their partition pieces would give, up to
-// fp32 rounding order: equal shares of about 3072 workgroups per batch, cut
-// at tiles, so every resident slot walks about as many positions and no
-// piece is stored mid-stream (a store in flight makes the next tile's wait
-// wait for it as well).
+// PKV_ATTN_PARTS_PER_WG partitions) a run folds consecutive whole partitions
+// into one piece, which is what a merge of their partition pieces would
+// give, up to fp32 rounding order: on the decode route about 2048 runs per
+// batch, as many single-wave workgroups as are resident at once on 256 CUs
+// (8 per CU: their LDS tiles), so every resident slot walks about as many
+// positions in one round and no piece is stored mid-stream (a store in
+// flight makes the next tile's wait wait for it as well).
 struct DecodeRuns {
   int32_t run_tokens, runs;
 };
 
+// fill: the number of workgroups past which partitions are folded into runs,
+// and about the number of runs then.
 DecodeRuns decode_runs(int32_t num_seqs, int32_t num_kv_heads, int32_t len_cap,
-                       int32_t part_tokens, int32_t num_parts);
+                       int32_t part_tokens, int32_t num_parts, int64_t fill);
 
 // One query row per sequence (row s of q and out, [num_seqs][num_q_heads][D]
 // bf16) against its history through the block tables, with the matrix-core

@@ -120,11 +120,12 @@ def test_cacheable_and_streaming_loads_agree(name):
 @pytest.mark.parametrize("ppw", [None, "3"])
 @pytest.mark.parametrize("pt", [0, 32, 96, 512])
 def test_matrix_route_matches_oracle(pt, ppw, tuning):
-    """Groups of 8 query heads per KV head take the matrix-core route, with
-    automatic or given partitions, and with runs of 3 partitions per
+    """The matrix-core route with fixed partitions (PKV_ATTN_MODE=3; the
+    default for more than 16 query heads per KV head), 8 heads per group,
+    with automatic or given partitions, and with runs of 3 partitions per
     workgroup (PKV_ATTN_PARTS_PER_WG): outputs against the oracle's split (or
     unsplit) attention."""
-    tuning("PKV_ATTN_MODE", 0)  # the route under test is the default
+    tuning("PKV_ATTN_MODE", 3)
     tuning("PKV_ATTN_PARTS_PER_WG", int(ppw) if ppw else 0)
     wl = independent_workload([1, 15, 16, 17, 64, 200, 333, 1500], num_q_heads=64,
                               num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16",
@@ -145,12 +146,11 @@ def test_matrix_route_matches_oracle(pt, ppw, tuning):
 @pytest.mark.parametrize("pt", [32, 64, 96])
 def test_matrix_route_equal_shares(pt, tuning):
     """More short partitions than the GPU holds at once on the matrix-core
-    route: workgroups take equal shares of 160 positions (cutting the 96-token
-    partitions) and fold each share into one piece, so the workspace holds
-    fewer rows than partitions.  Outputs against the oracle's split
+    route: workgroups take runs of whole partitions and fold each run into one
+    piece, so the workspace holds fewer rows than partitions.  Outputs against the oracle's split
     attention; then again with one history emptied, which must give zeros."""
     from paged_attention_slot_amd import ops
-    tuning("PKV_ATTN_MODE", 0)
+    tuning("PKV_ATTN_MODE", 3)
     tuning("PKV_ATTN_PARTS_PER_WG", 0)
     wl = independent_workload([1, 2, 31, 33, 500, 2047, 6000, 7500], num_q_heads=64,
                               num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16",
@@ -179,17 +179,19 @@ def test_matrix_route_equal_shares(pt, tuning):
     assert_gate(o, ref, "bf16", f"equal shares, one empty history, pt={pt}")
 
 
-@pytest.mark.parametrize("Hq,pt,shared", [(16, None, False), (16, None, True), (32, 64, False),
-                                          (64, None, False), (64, 32, False)],
+@pytest.mark.parametrize("Hq,pt,shared,mode", [(16, None, False, 0), (16, None, True, 0),
+                                               (32, 64, False, 1), (64, None, False, 3),
+                                               (64, 32, False, 3), (64, None, False, 0),
+                                               (64, 96, False, 0)],
                          ids=["balanced", "balanced-cacheable", "partitions", "matrix",
-                              "matrix-shares"])
-def test_split_phases_match_one_call(Hq, pt, shared, tuning):
+                              "matrix-shares", "matrix-balanced", "matrix-given-partitions"])
+def test_split_phases_match_one_call(Hq, pt, shared, mode, tuning):
     """pkv_attention_decode_phase: the per-partition phase, then the merge
     phase in a call of its own (which reads what the first left in the
-    workspace: pieces, and on the balanced split each stream's first and last
+    workspace: pieces, and on the balanced splits each stream's first and last
     interval), gives the bits of one call with both phases; a second merge
     call gives them again."""
-    tuning("PKV_ATTN_MODE", 0)
+    tuning("PKV_ATTN_MODE", mode)
     tuning("PKV_ATTN_PARTS_PER_WG", 0)
     wl = independent_workload([1, 15, 16, 17, 64, 200, 333, 1500, 2047, 3000], num_q_heads=Hq,
                               num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16",
@@ -360,17 +362,17 @@ def test_modes_match_oracle(mode_env, mode, dtype, B, D, Hq, Hkv):
 
 
 MBAL = [  # B, Hq, Hkv
-    (16, 16, 8), (16, 32, 8), (32, 64, 8), (8, 32, 2), (16, 128, 8), (64, 24, 4),
+    (16, 16, 8), (16, 32, 8), (32, 64, 8), (8, 32, 2), (16, 128, 8), (64, 24, 4), (32, 128, 16),
 ]
 
 
 @pytest.mark.parametrize("B,Hq,Hkv", MBAL, ids=lambda v: str(v))
 def test_matrix_balanced_route_matches_oracle(mode_env, B, Hq, Hkv):
     """The balanced split on the matrix cores (PKV_ATTN_MODE=4; the default
-    for one-byte pools with 2-7 heads per group) on bf16 pools: ragged
-    lengths from 1 to a few thousand (streams cut by many intervals, streams
-    inside one), every element against the oracle; then the two phases in
-    separate calls give the same bits."""
+    for 2 to 16 heads per group at head_dim 128 with automatic partitions)
+    on bf16 pools: ragged lengths from 1 to a few thousand (streams cut by
+    many intervals, streams inside one), every element against the oracle;
+    then the two phases in separate calls give the same bits."""
     mode_env(4)
     lens = [1, 2, 31, 32, 33, 100, 257, 600, 1000, 2500, 4100, 17]
     wl = independent_workload(lens, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128,

@@ -345,57 +345,70 @@ def test_append_fold_query(tuning):
     assert folded(64, 16, 8, 128, _lib.PKV_BF16, shared=1) == 1
     assert folded(64, 32, 8, 128, _lib.PKV_BF16) == 1
     assert folded(64, 16, 8, 128, _lib.PKV_BF16, pt=256) == 1  # fixed partitions, 2 heads per wave
-    assert folded(64, 32, 8, 128, _lib.PKV_BF16, pt=256) == 0  # 4 heads per wave
+    assert folded(4, 64, 8, 128, _lib.PKV_BF16) == 1           # 8 heads per group: the same
+    assert folded(4, 64, 8, 128, _lib.PKV_BF16, pt=512) == 0   # matrix route (partitions given)
     assert folded(64, 16, 8, 64, _lib.PKV_BF16, shared=1) == 0  # vector kernels, cacheable loads
     assert folded(64, 8, 8, 128, _lib.PKV_F32) == 1            # 1 head per wave
     assert folded(64, 16, 8, 128, _lib.PKV_F32) == 0           # group split over 2 waves
-    assert folded(4, 64, 8, 128, _lib.PKV_BF16) == 0           # matrix route
+    assert folded(4, 256, 8, 128, _lib.PKV_BF16) == 0          # matrix route
     assert folded(4, 64, 8, 128, _lib.PKV_FP8_E4M3) == -1
     assert folded(4, 63, 8, 128, _lib.PKV_BF16) == -1
+    tuning("PKV_ATTN_MODE", 1)                                 # vector kernels, partitions
+    assert folded(64, 16, 8, 128, _lib.PKV_BF16, pt=256) == 1  # 2 heads per wave
+    assert folded(64, 32, 8, 128, _lib.PKV_BF16, pt=256) == 0  # 4 heads per wave
     tuning("PKV_ATTN_APPEND", 2)
     assert folded(64, 32, 8, 128, _lib.PKV_BF16, pt=256) == 1
     tuning("PKV_ATTN_APPEND", 1)
-    assert folded(64, 16, 8, 128, _lib.PKV_BF16) == 0
     assert folded(64, 16, 8, 128, _lib.PKV_BF16, pt=256) == 0
+    tuning("PKV_ATTN_MODE", 0)
+    assert folded(64, 16, 8, 128, _lib.PKV_BF16) == 0
 
 
-def test_decode_route_query():
-    """pkv_attention_decode_route: 8+ query heads per KV head at head_dim 128
-    (bf16 or one-byte pools, partitions a multiple of 32) take the matrix
-    cores; narrower groups, fp32 pools, 64-wide heads and 16-token partitions
-    stay on the vector kernels; bad arguments give -1."""
+def test_decode_route_query(tuning):
+    """pkv_attention_decode_route: 2 to 16 query heads per KV head at head_dim
+    128 (bf16 or one-byte pools, automatic partitions) take the balanced
+    split on the matrix cores; wider groups, or 8 or more heads with given
+    partitions (a multiple of 32), the matrix-core route with fixed
+    partitions; one head per group, fp32 pools, 64-wide heads, 16-token
+    partitions and narrower groups with given partitions stay on the vector
+    kernels; bad arguments give -1."""
     lib = pkv.lib()
+    tuning("PKV_ATTN_MODE", 0)
 
     def route(N, Hq, H, D, dt, pt=0, maxlen=4096):
         return lib.pkv_attention_decode_route(N, Hq, maxlen, pt,
                                               ctypes.byref(g(nb=8192, H=H, D=D, dt=dt)))
 
     M, B, P = _lib.PKV_ROUTE_MATRIX, _lib.PKV_ROUTE_BALANCED, _lib.PKV_ROUTE_PARTITIONS
-    assert route(4, 64, 8, 128, _lib.PKV_BF16) == M
-    assert route(4, 64, 8, 128, _lib.PKV_BF16, pt=512) == M
-    assert route(4, 64, 8, 128, _lib.PKV_FP8_E4M3) == M
-    assert route(4, 64, 8, 128, _lib.PKV_INT8) == M
+    MB = _lib.PKV_ROUTE_MATRIX_BALANCED
+    assert route(4, 64, 8, 128, _lib.PKV_BF16) == MB
+    assert route(4, 64, 8, 128, _lib.PKV_BF16, pt=512) == M      # partitions given
+    assert route(4, 64, 8, 128, _lib.PKV_FP8_E4M3) == MB
+    assert route(4, 64, 8, 128, _lib.PKV_INT8) == MB
+    assert route(4, 128, 8, 128, _lib.PKV_BF16) == MB          # 16 heads per group
+    assert route(4, 256, 8, 128, _lib.PKV_BF16) == M           # 32 heads per group
+    assert route(4, 256, 8, 128, _lib.PKV_INT8, pt=512) == M
     assert route(4, 64, 8, 128, _lib.PKV_BF16, pt=16) == P
-    assert route(64, 16, 8, 128, _lib.PKV_BF16) == _lib.PKV_ROUTE_MATRIX_BALANCED
-    assert route(64, 32, 8, 128, _lib.PKV_BF16) == _lib.PKV_ROUTE_MATRIX_BALANCED
+    assert route(64, 16, 8, 128, _lib.PKV_BF16) == MB
+    assert route(64, 32, 8, 128, _lib.PKV_BF16) == MB
     assert route(64, 16, 8, 128, _lib.PKV_BF16, pt=256) == P
     assert route(4, 64, 8, 64, _lib.PKV_BF16) == B
     assert route(4, 64, 8, 128, _lib.PKV_F32) == B
     assert route(4, 63, 8, 128, _lib.PKV_BF16) == -1
-    # one-byte pools with 2-7 heads per group: the balanced split on the
-    # matrix cores (automatic partitions only)
-    MB = _lib.PKV_ROUTE_MATRIX_BALANCED
     assert route(256, 32, 8, 128, _lib.PKV_FP8_E4M3) == MB
     assert route(64, 16, 8, 128, _lib.PKV_INT8) == MB
     assert route(64, 16, 8, 128, _lib.PKV_INT8, pt=256) == P
     assert route(64, 8, 8, 128, _lib.PKV_FP8_E4M3) == B     # one head per group
     assert route(64, 16, 8, 64, _lib.PKV_BF16) == B         # head_dim 64: vector kernels
-    # the workspace of the matrix route: N * Hq * runs rows of D + 2 floats.
-    # 256 partitions of 512 over 32 (sequence, KV head) histories are more
-    # than the GPU holds at once: 96 equal shares of 1376 positions each
+    # the workspace of the matrix route (PKV_ATTN_MODE=3): N * Hq * runs rows
+    # of D + 2 floats.  256 partitions of 512 over 32 (sequence, KV head)
+    # histories are more than the GPU holds at once: 64 runs of 4 whole
+    # partitions each (about 2048 workgroups in all)
+    tuning("PKV_ATTN_MODE", 3)
+    assert route(4, 64, 8, 128, _lib.PKV_BF16, pt=512) == M
     n = lib.pkv_attention_workspace_bytes(4, 64, 131072, 512,
                                           ctypes.byref(g(nb=8192, H=8, D=128, dt=1)))
-    assert n == 4 * 64 * 96 * (128 + 2) * 4
+    assert n == 4 * 64 * 64 * (128 + 2) * 4
     # few partitions fill the GPU as whole partitions: one piece each
     n = lib.pkv_attention_workspace_bytes(4, 64, 4096, 512,
                                           ctypes.byref(g(nb=8192, H=8, D=128, dt=1)))
@@ -441,21 +454,26 @@ def test_tuning_knobs_read_once_and_set_through_the_abi(tuning):
     assert lib.pkv_get_tuning(b"PKV_ATTN_MODE") == 1
 
 
-def test_piece_tokens_query():
+def test_piece_tokens_query(tuning):
     """pkv_attention_piece_tokens: what one split-KV piece covers.  Fixed
     partitions on the vector kernels: one partition.  The matrix-core route
-    with more partitions than the GPU holds at once: equal shares that fold
-    several partitions (the long-context shape: 96 pieces of 1,376 positions
-    for 512-token partitions); with few partitions, one partition each.  The
-    balanced split: 0."""
+    with more partitions than the GPU holds at once: runs of whole
+    partitions (the long-context shape: 64 pieces of 2,048 positions for
+    512-token partitions); with few partitions, one partition each.  The
+    balanced splits: 0."""
     lib = pkv.lib()
 
     def piece(N, Hq, maxlen, pt, H=8, D=128, B=16, dt=_lib.PKV_BF16, nb=8192):
         return lib.pkv_attention_piece_tokens(N, Hq, maxlen, pt,
                                               ctypes.byref(g(nb=nb, B=B, H=H, D=D, dt=dt)))
 
-    assert piece(4, 64, 131072, 512, B=32, nb=18022) == 1376
-    assert piece(4, 64, 4096, 512) == 512
-    assert piece(64, 16, 4096, 256) == 256
+    tuning("PKV_ATTN_MODE", 0)
+    assert piece(4, 64, 131072, 512, B=32, nb=18022) == 2048  # partitions given: matrix route
+    assert piece(4, 64, 131072, 0, B=32, nb=18022) == 0       # matrix-core balanced split
     assert piece(64, 16, 4096, 0) == 0            # balanced split
     assert piece(4, 63, 4096, 0) == 0             # invalid: 63 heads over 8
+    tuning("PKV_ATTN_MODE", 3)                    # the matrix-core route
+    assert piece(4, 64, 131072, 512, B=32, nb=18022) == 2048
+    assert piece(4, 64, 4096, 512) == 512
+    tuning("PKV_ATTN_MODE", 1)                    # vector kernels, fixed partitions
+    assert piece(64, 16, 4096, 256) == 256

@@ -2,8 +2,9 @@
 workspace, nothing allocated) through the C ABI, against pkv_attention_decode
 with a caller's workspace: two calls in a row, the second with a smaller batch
 (the scratch still holds the first call's pieces), give the bits of the
-workspace entry point; both are also within the gate of the oracle.  Then a
-batch on the matrix-core route.  Every case prints its shape first."""
+workspace entry point; both are also within the gate of the oracle.  Then
+batches of eight heads per group on both matrix-core routes and an fp32
+batch.  Every case prints its shape first."""
 import numpy as np
 import pytest
 
@@ -73,10 +74,15 @@ def test_noalloc_twice_matches_the_workspace_entry_point():
         say("  gate", assert_gate(to_f64(bits(o)), ref, "bf16", wl.name))
 
 
-def test_noalloc_matrix_route_and_f32():
+@pytest.mark.parametrize("mode", [0, 3], ids=["default", "matrix-route"])
+def test_noalloc_eight_heads_per_group_and_f32(mode, tuning):
+    """Eight query heads per KV head on the default route (the balanced
+    split on the matrix cores) and on the matrix-core route with fixed
+    partitions (PKV_ATTN_MODE=3), then an fp32 batch."""
+    tuning("PKV_ATTN_MODE", mode)
     cases = [independent_workload([1, 15, 200, 1500, 64], num_q_heads=64, num_kv_heads=8,
                                   head_dim=128, block_size=16, dtype="bf16", seed=72,
-                                  name="matrix-route"),
+                                  name="eight-heads-per-group"),
              independent_workload([3, 40, 257], num_q_heads=8, num_kv_heads=2, head_dim=64,
                                   block_size=16, dtype="f32", seed=73, name="f32")]
     for wl in cases:
