@@ -55,6 +55,7 @@ struct MultiArgs {
   int32_t q_per_block;
   int32_t num_qblocks;
   int32_t num_kv_heads;
+  int32_t num_sg;           // (sequence, KV head) pairs (set at launch)
   int32_t num_parts;
   int32_t part_tokens;
   int32_t run_tokens;       // positions one workgroup walks (a multiple of 32)
@@ -66,28 +67,40 @@ struct MultiArgs {
   const float* v_scales;
 };
 
-// Register budgets that keep workgroups resident: eight-wave ones two per CU
-// (<= 128 registers a lane), four-wave ones three.
-template <int D, int NW, int Q, bool kStream>
+// RG row groups of 16 per wave (16 NW RG rows per workgroup).  Register
+// budgets that keep workgroups resident: eight-wave ones two per CU (<= 128
+// registers a lane), four-wave ones three, or two with two row groups a wave.
+template <int D, int NW, int Q, bool kStream, int RG = 1>
 __global__ void __launch_bounds__(64 * NW)
-__attribute__((amdgpu_waves_per_eu(NW == 8 ? 4 : (NW == 4 ? 3 : 1))))
+__attribute__((amdgpu_waves_per_eu(NW == 8 ? 4 : (NW == 4 ? (RG == 2 ? 2 : 3) : 1))))
 attn_multi_kernel(MultiArgs a) {
-  __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D, NW, Q>()];
-  __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D, NW, Q>()];
+  __shared__ __align__(16) uint16_t k_lds[pkv::mfma::k_lds_elems<D, NW, Q, RG>()];
+  __shared__ __align__(16) uint16_t v_lds[pkv::mfma::v_lds_elems<D, NW, Q, RG>()];
   __shared__ float s_lds[pkv::mfma::s_lds_elems<Q, NW>()];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(tid >> 6));
-  // grid = (query blocks * H_kv * sequences, runs of run_tokens
-  // positions).  Workgroups go to the XCDs round robin in launch order, so
-  // the XCD of (x, run) follows x.  Rotating the item by the run (item = x +
-  // run) spreads both every run over all XCDs and the runs of one item (one
-  // long history) over different XCDs; run-fastest order put all of run p on
-  // one XCD whenever the run count divides 8.
+  // grid = (query blocks * (sequence, KV head) pairs, runs of run_tokens
+  // positions).  Workgroups go to the XCDs round robin in launch order.
+  // One query block per pair (decode): rotating the item by the run (item =
+  // x + run) spreads both every run over all XCDs and the runs of one item
+  // (one long history) over different XCDs; run-fastest order put all of
+  // run p on one XCD whenever the run count divides 8.  Several query blocks
+  // (prefill chunks) all read their pair's history: they go to one XCD, in
+  // consecutive dispatch slots there, so that XCD's L2 fetches the history
+  // once for all of them (x = 8 k + c: XCD c, slot k; gridDim.x is a
+  // multiple of 8, padded with idle workgroups).
   const int qbs = a.num_qblocks;
-  const int items = qbs * a.num_kv_heads * static_cast<int>(gridDim.x / (qbs * a.num_kv_heads));
   const int run = blockIdx.y;
-  const int item = static_cast<int>((blockIdx.x + uint32_t(run)) % uint32_t(items));
+  int item;
+  if (qbs == 1) {
+    item = static_cast<int>((blockIdx.x + uint32_t(run)) % uint32_t(a.num_sg));
+  } else {
+    const int c = static_cast<int>(blockIdx.x & 7u), k = static_cast<int>(blockIdx.x >> 3);
+    const int sg = 8 * (k / qbs) + c;
+    if (sg >= a.num_sg) return;  // padding
+    item = sg * qbs + k % qbs;
+  }
   const int qb = item % qbs;
   const int g = (item / qbs) % a.num_kv_heads;
   const int s = item / (qbs * a.num_kv_heads);
@@ -104,45 +117,59 @@ attn_multi_kernel(MultiArgs a) {
   const int t_hi = min(min(t_lo + a.run_tokens, a.num_parts * a.part_tokens), p_last + 1);
   if (run > 0 && t_lo >= t_hi) return;     // no row of this block reaches these parts
 
-  // This lane's row: (query token jl of the block, head hh of the group).
+  // This lane's rows, one per row group: (query token jl of the block, head
+  // hh of the group).
   const int G = a.group;
-  const int row = 16 * w + (lane & 15);
-  const int jl = row / G, hh = row - jl * G;
-  const bool row_ok = jl < jn && q0 + j0 + jl < a.total_q;  // rows outside q: never touched
-  const int p_row = p_first + jl;
-  const int64_t qh = (int64_t(q0 + j0 + jl) * a.num_q_heads + g * G + hh);  // (row, head) index
+  bool row_ok[RG];
+  int p_row[RG];
+  int64_t qh[RG];  // (row, head) index
+  const uint16_t* qrow[RG];
+#pragma unroll
+  for (int gi = 0; gi < RG; ++gi) {
+    const int row = 16 * (RG * w + gi) + (lane & 15);
+    const int jl = row / G, hh = row - jl * G;
+    row_ok[gi] = jl < jn && q0 + j0 + jl < a.total_q;  // rows outside q: never touched
+    p_row[gi] = p_first + jl;
+    qh[gi] = int64_t(q0 + j0 + jl) * a.num_q_heads + g * G + hh;
+    qrow[gi] = a.q + qh[gi] * D;
+  }
 
   const pkv::mfma::History hist{a.k_cache,    a.v_cache,      a.block_tables + int64_t(s) * a.max_blocks,
                                 L,            g,              a.block_elems,
                                 a.row_elems,  a.num_blocks,   a.block_shift,
                                 a.num_kv_heads, a.v_scale,    a.k_scales,
                                 a.v_scales};
-  pkv::mfma::RowAcc<D> r;
-  pkv::mfma::start(r);
+  pkv::mfma::RowAcc<D> r[RG];
+#pragma unroll
+  for (int gi = 0; gi < RG; ++gi) pkv::mfma::start(r[gi]);
   constexpr int kPD = NW >= 2 ? 2 : 1;
   if (a.piece_stride == 1) {
     // one run covers the history: every row of the block sees the positions
     // up to its first query's
-    pkv::mfma::attend<D, NW, kPD, Q, kStream>(hist, t_lo, t_hi, a.q + qh * D, row_ok, p_row,
-                                              p_first, a.scale_log2, k_lds, v_lds, r, s_lds);
-    if (row_ok) pkv::mfma::store_row_bf16<D>(r, a.out + qh * D);
+    pkv::mfma::attend_rows<D, NW, kPD, Q, kStream, pkv::mfma::NoEmit, false, false, RG>(
+        hist, t_lo, t_hi, qrow, row_ok, p_row, p_first, a.scale_log2, k_lds, v_lds, r, s_lds);
+#pragma unroll
+    for (int gi = 0; gi < RG; ++gi)
+      if (row_ok[gi]) pkv::mfma::store_row_bf16<D>(r[gi], a.out + qh[gi] * D);
     return;
   }
   // one piece per piece_tokens positions (a partition, or the whole run on
   // the decode route), at [row, head][piece]; t_lo is a multiple of
   // piece_tokens
-  const auto emit = [&](int t, pkv::mfma::RowAcc<D>& rr) {
-    if (!row_ok) return;
-    const int64_t prow = qh * a.piece_stride + t / a.piece_tokens;
+  const auto emit = [&](int t, pkv::mfma::RowAcc<D>& rr, int gi) {
+    if (!row_ok[gi]) return;
+    const int64_t prow = qh[gi] * a.piece_stride + t / a.piece_tokens;
     pkv::mfma::store_piece<D>(rr, a.ws_acc + prow * D, a.ws_ml + prow);
   };
-  pkv::mfma::attend<D, NW, kPD, Q, kStream>(hist, t_lo, t_hi, a.q + qh * D, row_ok, p_row,
-                                            p_first, a.scale_log2, k_lds, v_lds, r, s_lds,
-                                            a.piece_tokens, emit);
-  if (row_ok && a.ws_np && (lane >> 4) == 0 && run == 0) {
-    const int np = p_row < 0 ? 0 : min(a.piece_stride, p_row / a.piece_tokens + 1);
-    a.ws_np[qh] = np;
-  }
+  pkv::mfma::attend_rows<D, NW, kPD, Q, kStream, decltype(emit), false, false, RG>(
+      hist, t_lo, t_hi, qrow, row_ok, p_row, p_first, a.scale_log2, k_lds, v_lds, r, s_lds,
+      a.piece_tokens, emit);
+#pragma unroll
+  for (int gi = 0; gi < RG; ++gi)
+    if (row_ok[gi] && a.ws_np && (lane >> 4) == 0 && run == 0) {
+      const int np = p_row[gi] < 0 ? 0 : min(a.piece_stride, p_row[gi] / a.piece_tokens + 1);
+      a.ws_np[qh[gi]] = np;
+    }
 }
 
 // Log-sum-exp merge of the partitions of one (query row, head): one wave,
@@ -253,7 +280,8 @@ pkv_status multi_plan(int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
     pl->part_tokens = static_cast<int>(pt < round_up_to(len, kKT) ? pt : round_up_to(len, kKT));
   }
   const int64_t np = (int64_t(len) + pl->part_tokens - 1) / pl->part_tokens;
-  if (np > 65535 || int64_t(pl->qblocks) * g->num_kv_heads * num_seqs > 2147483647LL)
+  if (np > 65535 ||
+      int64_t(pl->qblocks) * ((int64_t(g->num_kv_heads) * num_seqs + 7) / 8 * 8) > 2147483647LL)
     return pkv::fail(PKV_ERR_INVALID_ARG, "%s: too many partitions or query blocks", who);
   pl->num_parts = static_cast<int>(np);
   // Runs of positions per workgroup, each folded into one piece (as on the
@@ -293,16 +321,19 @@ void launch_multi_main(const MultiPlan& pl, const MultiArgs& a, int num_seqs, in
 }
 
 template <int D, int Q, bool kStream>
-void launch_multi_variant(const MultiPlan& pl, const MultiArgs& a, int num_seqs,
+void launch_multi_variant(const MultiPlan& pl, const MultiArgs& args, int num_seqs,
                           int num_kv_heads, hipStream_t st) {
-  const dim3 grid(pl.qblocks * num_kv_heads * num_seqs, pl.runs);
+  MultiArgs a = args;
+  a.num_sg = num_kv_heads * num_seqs;
+  const int sgs = pl.qblocks == 1 ? a.num_sg : (a.num_sg + 7) / 8 * 8;  // see the kernel
+  const dim3 grid(pl.qblocks * sgs, pl.runs);
   switch (pl.nw) {
     case 1: hipLaunchKernelGGL((attn_multi_kernel<D, 1, Q, kStream>), grid, dim3(64), 0, st, a); break;
     case 2: hipLaunchKernelGGL((attn_multi_kernel<D, 2, Q, kStream>), grid, dim3(128), 0, st, a); break;
     case 4: hipLaunchKernelGGL((attn_multi_kernel<D, 4, Q, kStream>), grid, dim3(256), 0, st, a); break;
     default:
-      if constexpr (D == 128 && Q == pkv::mfma::kBf16)  // the plan's condition for 8 waves
-        hipLaunchKernelGGL((attn_multi_kernel<D, 8, Q, kStream>), grid, dim3(512), 0, st, a);
+      if constexpr (D == 128 && Q == pkv::mfma::kBf16)  // the plan's condition for 128 rows
+        hipLaunchKernelGGL((attn_multi_kernel<D, 4, Q, kStream, 2>), grid, dim3(256), 0, st, a);
       break;
   }
 }

@@ -70,8 +70,8 @@ enum Kind : int { kBf16 = 0, kFp8 = 1, kInt8 = 2 };
 // into LDS (gfx950's global_load_lds_dwordx4: each lane's 16 bytes land at
 // the wave's LDS base + 16 * lane, no registers and no LDS stores), into
 // four buffers each of K and V in the padded row layout.
-template <int D, int NW, int Q> constexpr bool direct_lds() {
-  return Q == kBf16 && NW == 8 && D == 128;
+template <int D, int NW, int Q, int RG = 1> constexpr bool direct_lds() {
+  return Q == kBf16 && D == 128 && (NW == 8 || (NW == 4 && RG == 2));
 }
 constexpr int kDirectBufs = 4;
 
@@ -96,11 +96,11 @@ __device__ __forceinline__ void load_to_lds16(const char* base, int off, uint32_
       : "memory");
 }
 
-template <int D, int NW, int Q = kBf16> constexpr int k_lds_elems() {
-  return (direct_lds<D, NW, Q>() ? kDirectBufs : lds_tiles<NW>()) * kKT * k_stride<D, NW>();
+template <int D, int NW, int Q = kBf16, int RG = 1> constexpr int k_lds_elems() {
+  return (direct_lds<D, NW, Q, RG>() ? kDirectBufs : lds_tiles<NW>()) * kKT * k_stride<D, NW>();
 }
-template <int D, int NW, int Q = kBf16> constexpr int v_lds_elems() {
-  return (direct_lds<D, NW, Q>() ? kDirectBufs : lds_tiles<NW>()) * kKT * v_stride<D>();
+template <int D, int NW, int Q = kBf16, int RG = 1> constexpr int v_lds_elems() {
+  return (direct_lds<D, NW, Q, RG>() ? kDirectBufs : lds_tiles<NW>()) * kKT * v_stride<D>();
 }
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -225,7 +225,7 @@ __device__ __forceinline__ void start(RowAcc<D>& r) {
 // in flight, LDS buffers) runs on across the boundary.  One workgroup can so
 // produce the pieces of several split-KV partitions in one pass.
 struct NoEmit {
-  template <class R> __device__ void operator()(int, R&) const {}
+  template <class R> __device__ void operator()(int, R&, int) const {}
 };
 
 // The step's append folded into the pass (bf16 pools; kAppend): position
@@ -242,16 +242,20 @@ struct NewRow {
 };
 
 template <int D, int NW, int PD = 1, int Q = kBf16, bool kStream = false, class Emit = NoEmit,
-          bool kAppend = false, bool kWaveOnly = false>
-__device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, const uint16_t* q,
-                                       bool row_ok, int p_row, int p_all, float scale_log2,
-                                       uint16_t* k_lds, uint16_t* v_lds, RowAcc<D>& r,
-                                       float* s_lds = nullptr, int seg = 0,
-                                       const Emit& emit = Emit(), const NewRow& nr = NewRow()) {
+          bool kAppend = false, bool kWaveOnly = false, int RG = 1>
+__device__ __forceinline__ void attend_rows(const History& h, int t_lo, int t_hi,
+                                            const uint16_t* const (&q)[RG],
+                                            const bool (&row_ok)[RG], const int (&p_row)[RG],
+                                            int p_all, float scale_log2, uint16_t* k_lds,
+                                            uint16_t* v_lds, RowAcc<D> (&r)[RG],
+                                            float* s_lds = nullptr, int seg = 0,
+                                            const Emit& emit = Emit(),
+                                            const NewRow& nr = NewRow()) {
   static_assert(!kAppend || Q == kBf16, "the folded append takes bf16 pools");
   static_assert(!kAppend || NW == 1, "the folded append runs in single-wave passes");
   static_assert(NW == 1 || PD == 2, "several waves keep two tiles of registers in flight");
   static_assert(!kWaveOnly || NW == 1, "a wave-only walk is a single wave's");
+  static_assert(RG == 1 || NW >= 2, "row groups per wave take the multi-wave walks");
   // A single wave's LDS accesses run in order: it waits for its own and
   // needs the workgroup barrier only when its workgroup is one wave.  A
   // wave-only walk (kWaveOnly: one of several independent walks in a
@@ -260,7 +264,7 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
     if constexpr (kWaveOnly) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     else lds_barrier();
   };
-  constexpr bool kDirect = direct_lds<D, NW, Q>();
+  constexpr bool kDirect = direct_lds<D, NW, Q, RG>();
   constexpr float kSlack = 8.0f;
   constexpr int kEB = Q == kBf16 ? 2 : 1;   // bytes per element
   constexpr int kKS = D / 32;            // k-steps of the score product
@@ -282,13 +286,15 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
   // is kept off zero so a masked score never meets 0 * -inf.
   const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
   scale_log2 = fmaxf(fabsf(scale_log2), 1e-30f);
-  uint4 qf[kKS];
+  uint4 qf[RG][kKS];
 #pragma unroll
-  for (int ks = 0; ks < kKS; ++ks) {
-    qf[ks] = row_ok ? *reinterpret_cast<const uint4*>(q + 32 * ks + 8 * quad)
-                    : make_uint4(0, 0, 0, 0);
-    qf[ks] = make_uint4(qf[ks].x ^ qsign, qf[ks].y ^ qsign, qf[ks].z ^ qsign, qf[ks].w ^ qsign);
-  }
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      uint4 x = row_ok[g] ? *reinterpret_cast<const uint4*>(q[g] + 32 * ks + 8 * quad)
+                          : make_uint4(0, 0, 0, 0);
+      qf[g][ks] = make_uint4(x.x ^ qsign, x.y ^ qsign, x.z ^ qsign, x.w ^ qsign);
+    }
 
   const int L = h.len;
   const int bmask = (1 << h.block_shift) - 1;
@@ -467,109 +473,138 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
   const uint16_t* v_rd = v_lds + (4 * quad + ((lane & 15) >> 2)) * kVStride + 4 * (lane & 3);
   // Last position this lane's row sees (-1: none): the mask of a tile that
   // not every live row sees whole is one compare per score against it.
-  const int row_lim = row_ok ? (p_row < t_hi - 1 ? p_row : t_hi - 1) : -1;
+  int row_lim[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g)
+    row_lim[g] = row_ok[g] ? (p_row[g] < t_hi - 1 ? p_row[g] : t_hi - 1) : -1;
   // This lane's part of its row's sum of weights (the state's sum enters
   // through the row's first lane).
-  float lpart = quad == 0 ? r.lsum : 0.f;
+  float lpart[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) lpart[g] = quad == 0 ? r[g].lsum : 0.f;
 
   // A staged tile's scores S^T = K Q^T (LDS tile buffer kbuf): s[pt][i] is
   // position 16 pt + 4 quad + i of the tile for row (lane & 15).
-  auto qk = [&](int kbuf, f32x4_t (&s)[2]) {
+  // Each K operand read serves the RG row groups of the wave.
+  auto qk = [&](int kbuf, f32x4_t (&s)[RG][2]) {
     const uint16_t* kt = k_lds + kbuf * kTileElems;
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4_t acc[RG];
+#pragma unroll
+      for (int g = 0; g < RG; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks) {
         const uint4 ka = *reinterpret_cast<const uint4*>(
             kt + (16 * pt + (lane & 15)) * kKStride + 32 * ks + 8 * quad);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(qf[ks]), acc, 0,
-                                                      0, 0);
+#pragma unroll
+        for (int g = 0; g < RG; ++g)
+          acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(qf[g][ks]),
+                                                           acc[g], 0, 0, 0);
       }
-      s[pt] = acc;
+#pragma unroll
+      for (int g = 0; g < RG; ++g) s[g][pt] = acc[g];
     }
   };
   // A tile's scores, ready for the exponent: masked (-inf) where the lane's
   // row does not see the position, INT8 scaled with the key scales (scale
   // slot ss); and the state's reference moved if some lane's score exceeds
   // its row's reference by more than kSlack.
-  auto prepare = [&](int t0, int ss, const f32x4_t (&s)[2], float (&sc)[8]) {
+  auto prepare = [&](int t0, int ss, const f32x4_t (&s)[RG][2], float (&sc)[RG][8]) {
     const float* st = s_lds + 2 * kKT * ss;
 #pragma unroll
-    for (int pt = 0; pt < 2; ++pt)
+    for (int g = 0; g < RG; ++g)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // bf16 and FP8: unscaled here; INT8: scaled with its key scale
-        float v = s[pt][i];
-        if constexpr (Q == kInt8) v *= scale_log2 * st[16 * pt + 4 * quad + i];
-        sc[4 * pt + i] = v;
-      }
+      for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // bf16 and FP8: unscaled here; INT8: scaled with its key scale
+          float v = s[g][pt][i];
+          if constexpr (Q == kInt8) v *= scale_log2 * st[16 * pt + 4 * quad + i];
+          sc[g][4 * pt + i] = v;
+        }
     // Uniform: some live row does not see every position of the tile.  Score
     // e = 4 pt + i sits at position t0 + 16 pt + 4 quad + i, visible to this
     // lane's row iff 16 pt + i <= vis.
     if (t0 + kKT - 1 > p_all || t0 + kKT > t_hi) {
-      const int vis = row_lim - t0 - 4 * quad;
 #pragma unroll
-      for (int pt = 0; pt < 2; ++pt)
+      for (int g = 0; g < RG; ++g) {
+        const int vis = row_lim[g] - t0 - 4 * quad;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sc[4 * pt + i] = 16 * pt + i <= vis ? sc[4 * pt + i] : -INFINITY;
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sc[g][4 * pt + i] = 16 * pt + i <= vis ? sc[g][4 * pt + i] : -INFINITY;
+      }
     }
-    float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                       fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-    if constexpr (Q != kInt8) tmax *= scale_log2;
-    if (__builtin_amdgcn_ballot_w64(tmax > r.m + kSlack) != 0) {  // uniform
-      const float mn = fmaxf(r.m, max_across_rows16(tmax));
-      const float alpha = fast_exp2(r.m - mn);
-      r.m = mn;
-      lpart *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < kDT; ++dt)
+    for (int g = 0; g < RG; ++g) {
+      float tmax = fmaxf(fmaxf(fmaxf(sc[g][0], sc[g][1]), fmaxf(sc[g][2], sc[g][3])),
+                         fmaxf(fmaxf(sc[g][4], sc[g][5]), fmaxf(sc[g][6], sc[g][7])));
+      if constexpr (Q != kInt8) tmax *= scale_log2;
+      if (__builtin_amdgcn_ballot_w64(tmax > r[g].m + kSlack) != 0) {  // uniform
+        const float mn = fmaxf(r[g].m, max_across_rows16(tmax));
+        const float alpha = fast_exp2(r[g].m - mn);
+        r[g].m = mn;
+        lpart[g] *= alpha;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r.o[dt][i] *= alpha;
+        for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r[g].o[dt][i] *= alpha;
+      }
     }
   };
   // The weights of prepared scores and their P V: vfrag(dt) reads this
   // lane's V^T operand of d tile dt (V^T[16 dt + (lane & 15)][positions
   // 4 quad .. + 3 and 16 + 4 quad .. + 3]); INT8's V scales in slot ss.
-  auto weigh = [&](const auto& vfrag, int ss, const float (&sc)[8]) {
+  // Each V operand read serves the RG row groups of the wave.
+  auto weigh = [&](const auto& vfrag, int ss, const float (&sc)[RG][8]) {
     const float* st = s_lds + 2 * kKT * ss;
-    const float mref = r.m;
     // Weights as two bf16 terms, p = hi + lo (hi = bf16(p), lo = bf16(p - hi)):
     // P V then carries p to about 2^-17 relative, like the fp32 sum.
-    uint32_t ph[4], pl[4];
-    float psum;
+    bf16x8_t pfh[RG], pfl[RG];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float p0, p1;
-      if constexpr (Q == kInt8) {
-        p0 = fast_exp2(sc[2 * k] - mref);
-        p1 = fast_exp2(sc[2 * k + 1] - mref);
-      } else {
-        p0 = fast_exp2(fmaf(sc[2 * k], scale_log2, -mref));
-        p1 = fast_exp2(fmaf(sc[2 * k + 1], scale_log2, -mref));
+    for (int g = 0; g < RG; ++g) {
+      const float mref = r[g].m;
+      uint32_t ph[4], pl[4];
+      float psum;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float p0, p1;
+        if constexpr (Q == kInt8) {
+          p0 = fast_exp2(sc[g][2 * k] - mref);
+          p1 = fast_exp2(sc[g][2 * k + 1] - mref);
+        } else {
+          p0 = fast_exp2(fmaf(sc[g][2 * k], scale_log2, -mref));
+          p1 = fast_exp2(fmaf(sc[g][2 * k + 1], scale_log2, -mref));
+        }
+        psum = k == 0 ? p0 + p1 : psum + (p0 + p1);
+        // score element e = 2k (+1) sits at tile position 16 (e / 4) + 4 quad + e % 4
+        if constexpr (Q == kFp8) {
+          p0 *= h.v_scale;
+          p1 *= h.v_scale;
+        } else if constexpr (Q == kInt8) {
+          p0 *= st[kKT + 16 * ((2 * k) >> 2) + 4 * quad + ((2 * k) & 3)];
+          p1 *= st[kKT + 16 * ((2 * k + 1) >> 2) + 4 * quad + ((2 * k + 1) & 3)];
+        }
+        const uint32_t hw = cvt_pk_bf16(p0, p1);
+        ph[k] = hw;
+        pl[k] = cvt_pk_bf16(p0 - __uint_as_float(hw << 16), p1 - __uint_as_float(hw & 0xFFFF0000u));
       }
-      psum = k == 0 ? p0 + p1 : psum + (p0 + p1);
-      // score element e = 2k (+1) sits at tile position 16 (e / 4) + 4 quad + e % 4
-      if constexpr (Q == kFp8) {
-        p0 *= h.v_scale;
-        p1 *= h.v_scale;
-      } else if constexpr (Q == kInt8) {
-        p0 *= st[kKT + 16 * ((2 * k) >> 2) + 4 * quad + ((2 * k) & 3)];
-        p1 *= st[kKT + 16 * ((2 * k + 1) >> 2) + 4 * quad + ((2 * k + 1) & 3)];
-      }
-      const uint32_t hw = cvt_pk_bf16(p0, p1);
-      ph[k] = hw;
-      pl[k] = cvt_pk_bf16(p0 - __uint_as_float(hw << 16), p1 - __uint_as_float(hw & 0xFFFF0000u));
+      lpart[g] += psum;
+      pfh[g] = as_bf16x8(make_uint4(ph[0], ph[1], ph[2], ph[3]));
+      pfl[g] = as_bf16x8(make_uint4(pl[0], pl[1], pl[2], pl[3]));
     }
-    lpart += psum;
-    const bf16x8_t pfh = as_bf16x8(make_uint4(ph[0], ph[1], ph[2], ph[3]));
-    const bf16x8_t pfl = as_bf16x8(make_uint4(pl[0], pl[1], pl[2], pl[3]));
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt) {
       const bf16x8_t va = vfrag(dt);
-      f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfh, r.o[dt], 0, 0, 0);
-      r.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfl, acc, 0, 0, 0);
+      f32x4_t acc[RG];
+#pragma unroll
+      for (int g = 0; g < RG; ++g)
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfh[g], r[g].o[dt], 0, 0, 0);
+#pragma unroll
+      for (int g = 0; g < RG; ++g)
+        r[g].o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfl[g], acc[g], 0, 0, 0);
     }
   };
   // V^T fragments from the padded layout's buffer vbuf
@@ -586,10 +621,13 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
     if constexpr (!std::is_same<Emit, NoEmit>::value) {
       const int te = t + kKT;
       if (te >= t_hi || te % seg == 0) {  // uniform: a segment is complete
-        r.lsum = sum_across_rows16(lpart);
-        emit(t, r);
-        start(r);
-        lpart = 0.f;
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+          r[g].lsum = sum_across_rows16(lpart[g]);
+          emit(t, r[g], g);
+          start(r[g]);
+          lpart[g] = 0.f;
+        }
       }
     }
   };
@@ -615,8 +653,8 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
         // the register set just staged takes the tile PD ahead, in flight
         // meanwhile
         if (t + PD * kKT < t_hi) fetch_v(j, t + PD * kKT, fetch_k(j, t + PD * kKT));
-        f32x4_t sv[2];
-        float sc[8];
+        f32x4_t sv[RG][2];
+        float sc[RG][8];
         qk(0, sv);
         prepare(t, 0, sv, sc);
         weigh(vfrag_padded(0), 0, sc);
@@ -624,7 +662,7 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
       }
     }
   } else if constexpr (kDirect) {
-    // Eight waves, tiles loaded straight into LDS (see direct_lds), the same
+    // Tiles loaded straight into LDS (see direct_lds), the same
     // software pipeline as below: iteration i, after one barrier, computes
     // tile i + 1's scores (K buffer (i + 1) % 4) and tile i's weights and
     // P V (V buffer i % 4), and issues tile i + 3's loads into buffers
@@ -636,10 +674,11 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
     //
     // The buffers keep the padded row layout of the register-staged walk
     // (rows of 18 chunks of 16 bytes, the last two padding).  Wave w loads
-    // rows 4w .. 4w + 3, 72 chunk slots from LDS byte 1152 w of the buffer:
-    // one instruction for slots 0 .. 63 and one (8 lanes) for 64 .. 71;
-    // padding slots are not loaded.  The four rows lie in one block (t0 is a
-    // multiple of 8, blocks hold at least 8), so a tile's block and row
+    // rows kRW w .. kRW w + kRW - 1 (kRW = 32 / NW: 4 or 8), 18 kRW chunk
+    // slots from LDS byte 288 kRW w of the buffer, 64 slots per instruction
+    // (the last one partly masked: 72 slots take 2, 144 take 3); padding
+    // slots are not loaded.  The kRW rows lie in one block (t0 is a multiple
+    // of 8, blocks hold a power of two >= 8), so a tile's block and row
     // offsets are the same in every lane: each lane adds only its slot's
     // fixed offset.
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -647,14 +686,16 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
     const auto tile = [&](int u) { return t_lo + u * kKT; };
     constexpr int kSlotsPerRow = kKStride * 2 / 16;
     static_assert(kKStride == kVStride && kSlotsPerRow == 18, "rows of 18 chunks");
-    int srow[2], soff[2];
-    bool sval[2];
+    constexpr int kRW = kKT / NW;                            // rows per wave
+    constexpr int kLI = (kRW * kSlotsPerRow + 63) / 64;     // load instructions per pool
+    int srow[kLI], soff[kLI];
+    bool sval[kLI];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int z = 64 * e + lane;  // slot of the wave's 72
+    for (int e = 0; e < kLI; ++e) {
+      const int z = 64 * e + lane;  // slot of the wave's 18 kRW
       srow[e] = z / kSlotsPerRow;
       const int x = z - kSlotsPerRow * srow[e];
-      sval[e] = z < 4 * kSlotsPerRow && x < 16;
+      sval[e] = z < kRW * kSlotsPerRow && x < 16;
       soff[e] = srow[e] * row_bytes + (h.g * D + 8 * x) * 2;
     }
     typedef __attribute__((address_space(3))) u32x4_native_t lds_u32x4;
@@ -675,28 +716,28 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
         tcache_base = b0;
         tcache = window(b0);
       }
-      const int p0 = t0 + 4 * w;  // the wave's first row
+      const int p0 = t0 + kRW * w;  // the wave's first row
       const int blk = __builtin_amdgcn_readlane(tcache, (p0 >> h.block_shift) - tcache_base);
       const uint64_t ub = uint64_t(static_cast<uint32_t>(blk)) * block_bytes +
                           static_cast<uint32_t>((p0 & bmask) * row_bytes);
       const char* const kg = uniform_ptr(static_cast<const char*>(h.k_cache) + ub);
       const char* const vg = uniform_ptr(static_cast<const char*>(h.v_cache) + ub);
-      const uint32_t kd = k_lds_a + buf * (kTileElems * 2) + w * (4 * kSlotsPerRow * 16);
-      const uint32_t vd = v_lds_a + buf * (kVTileElems * 2) + w * (4 * kSlotsPerRow * 16);
+      const uint32_t kd = k_lds_a + buf * (kTileElems * 2) + w * (kRW * kSlotsPerRow * 16);
+      const uint32_t vd = v_lds_a + buf * (kVTileElems * 2) + w * (kRW * kSlotsPerRow * 16);
       if (t0 + kKT <= L) {  // uniform: the whole tile is history
-        // K's two instructions, then V's (the waits count them in this order)
+        // K's instructions, then V's (the waits count them in this order)
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
+        for (int e = 0; e < kLI; ++e)
           if (sval[e]) load_to_lds16(kg, soff[e], kd + 1024 * e);
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
+        for (int e = 0; e < kLI; ++e)
           if (sval[e]) load_to_lds16(vg, soff[e], vd + 1024 * e);
       } else {
         // the history's last tile: through registers (waited for here, so
         // the counts of direct loads stay as the waits assume), zeros past
         // the history
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
+        for (int e = 0; e < kLI; ++e) {
           uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
           if (sval[e] && p0 + srow[e] < L) {
             kx = *reinterpret_cast<const uint4*>(kg + soff[e]);
@@ -709,25 +750,36 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
         }
       }
     };
-    // Tiles loaded directly (whole tiles of history): their loads (two per
+    // Tiles loaded directly (whole tiles of history): their loads (kLI per
     // pool and wave) are the ones the waits count.
     const auto direct = [&](int u) { return u < n && tile(u) + kKT <= L; };
-    const auto wait_loads = [](int later) {  // this wave's loads but the last ``later``
-      switch (later) {
-        case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-        case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
-        case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-        default: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+    // This wave's loads but the last kLI * ``later`` (later: 0, 1, 3 or 5).
+    const auto wait_loads = [](int later) {
+      if constexpr (kLI == 2) {
+        switch (later) {
+          case 1: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+          case 3: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+          case 5: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+          default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+        }
+      } else {
+        static_assert(kLI == 3, "two or three load instructions per pool");
+        switch (later) {
+          case 1: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+          case 3: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+          case 5: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
+          default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+        }
       }
     };
 #pragma unroll
     for (int u = 0; u < 3; ++u)
       if (u < n) issue(tile(u), u);
     // K(0) is needed: after it come V(0) and both pools' loads of tiles 1, 2
-    wait_loads(direct(0) ? 2 * (1 + 2 * direct(1) + 2 * direct(2)) : 0);
+    wait_loads(direct(0) ? 1 + 2 * direct(1) + 2 * direct(2) : 0);
     lds_barrier();
-    f32x4_t s_nx[2];
-    float sc[8];
+    f32x4_t s_nx[RG][2];
+    float sc[RG][8];
     qk(0, s_nx);
     if (n > 0) prepare(tile(0), 0, s_nx, sc);
     for (int i0 = 0; i0 < n; i0 += kDirectBufs) {
@@ -737,7 +789,7 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
         if (i >= n) break;  // uniform
         // K(i + 1) and V(i): after K(i + 1) come V(i + 1), then tile i + 2's
         // (a tile through registers is complete once issued)
-        wait_loads(direct(i + 2) ? 6 : (direct(i + 1) ? 2 : 0));
+        wait_loads(direct(i + 2) ? 3 : (direct(i + 1) ? 1 : 0));
         lds_barrier();
         qk((b + 1) % kDirectBufs, s_nx);      // tile i + 1's scores (unused past the last)
         weigh(vfrag_padded(b), 0, sc);        // tile i's weights and P V
@@ -769,8 +821,8 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
     if (n > 2) fetch_v(0, tile(2), fetch_k(0, tile(2)));
     if (n > 3) voff = fetch_k(1, tile(3));
     lds_barrier();
-    f32x4_t s_nx[2];
-    float sc[8];
+    f32x4_t s_nx[RG][2];
+    float sc[RG][8];
     qk(0, s_nx);
     if (n > 0) prepare(tile(0), 0, s_nx, sc);
     int ss = 0;  // scale slot of tile i
@@ -793,9 +845,27 @@ __device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, con
       }
     }
   }
-  r.lsum = sum_across_rows16(lpart);
+#pragma unroll
+  for (int g = 0; g < RG; ++g) r[g].lsum = sum_across_rows16(lpart[g]);
   // the caller may reuse the LDS (another pass) right after
   sync_lds();
+}
+
+
+// One row group per wave (the form most walks take).
+template <int D, int NW, int PD = 1, int Q = kBf16, bool kStream = false, class Emit = NoEmit,
+          bool kAppend = false, bool kWaveOnly = false>
+__device__ __forceinline__ void attend(const History& h, int t_lo, int t_hi, const uint16_t* q,
+                                       bool row_ok, int p_row, int p_all, float scale_log2,
+                                       uint16_t* k_lds, uint16_t* v_lds, RowAcc<D>& r,
+                                       float* s_lds = nullptr, int seg = 0,
+                                       const Emit& emit = Emit(), const NewRow& nr = NewRow()) {
+  const uint16_t* const qs[1] = {q};
+  const bool oks[1] = {row_ok};
+  const int ps[1] = {p_row};
+  attend_rows<D, NW, PD, Q, kStream, Emit, kAppend, kWaveOnly, 1>(
+      h, t_lo, t_hi, qs, oks, ps, p_all, scale_log2, k_lds, v_lds,
+      *reinterpret_cast<RowAcc<D>(*)[1]>(&r), s_lds, seg, emit, nr);
 }
 
 // Store this lane's fragment of a row's state as a piece: D floats of
