@@ -47,15 +47,17 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 encoding / 8 bits
 PCIE_PEAK_GBPS = 32.0 * 16 * 128 / 130 / 8
 METRIC = "paged decode attention KV-read GB/s (% of MI355X HBM peak); tokens/s"
+# Sources of each kernel, under paged_attention_slot_amd/csrc/ (the build
+# script's flags shape the code too).
 KERNEL_SOURCES = {
-    "attn_balanced_kernel": ("attn_decode.hip", "lse_merge.h", "pkv_device.h"),
-    "attn_partition_kernel": ("attn_decode.hip", "lse_merge.h", "pkv_device.h"),
+    "attn_balanced_kernel": ("attn_decode.hip", "lse_merge.h", "pkv_device.h", "../build.py"),
+    "attn_partition_kernel": ("attn_decode.hip", "lse_merge.h", "pkv_device.h", "../build.py"),
     "attn_multi_kernel": ("attn_multi.hip", "mfma_attend.h", "mfma_route.h", "lse_merge.h",
-                          "pkv_device.h"),
-    "attn_shared": ("attn_shared.hip", "mfma_attend.h", "pkv_device.h"),
+                          "pkv_device.h", "../build.py"),
+    "attn_shared": ("attn_shared.hip", "mfma_attend.h", "pkv_device.h", "../build.py"),
     "attn_mfma_balanced_kernel": ("attn_decode.hip", "mfma_attend.h", "lse_merge.h",
-                                  "pkv_device.h"),
-    "swap_blocks_kernel": ("swap.hip",),
+                                  "pkv_device.h", "../build.py"),
+    "swap_blocks_kernel": ("swap.hip", "../build.py"),
 }
 
 
