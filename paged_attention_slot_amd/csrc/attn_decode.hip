@@ -1034,7 +1034,14 @@ attn_mfma_balanced_kernel(AttnArgs a) {
   const Intervals ivs(total, a.num_groups);
   int iv;
   if (static_cast<int>(blockIdx.x) < a.static_blocks) {
-    iv = blockIdx.x;
+    // Workgroups go to the 8 XCDs round robin (workgroup b to XCD b % 8);
+    // each XCD takes a contiguous eighth of the static intervals, so the
+    // KV heads of one sequence (consecutive streams) run side by side on one
+    // XCD: the INT8 scales, [slot][KV head] with one 32-byte sector per slot,
+    // then reach HBM once per slot instead of once per head.
+    const int B = a.static_blocks, b = blockIdx.x;
+    const int c = b & 7, q8 = B >> 3, r8 = B & 7;
+    iv = c * q8 + min(c, r8) + (b >> 3);
     if (iv >= ivs.Ws) return;
   } else {
     const int j = blockIdx.x - a.static_blocks;
