@@ -162,7 +162,7 @@ pkv_status pkv_copy_blocks_quant(const int32_t* src_dst_pairs, int32_t num_pairs
  *
  * pkv_attention_decode_shared computes exactly what pkv_attention_decode
  * computes (bf16 pools) but reads each group's shared prefix once per block of
- * 16 (member, query head) rows instead of once per sequence: first every
+ * 32 (member, query head) rows instead of once per sequence: first every
  * sequence's own positions (fp32 partial states in the workspace), then the
  * prefix positions of all members on the matrix cores, each block's result
  * combined with its members' partial states by log-sum-exp.

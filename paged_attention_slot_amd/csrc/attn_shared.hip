@@ -17,11 +17,12 @@
 //    sum) per partition; a sequence without a shared prefix is attended
 //    whole by its first partition's workgroup, which writes its result;
 //  * attn_prefix_kernel (second) reads the prefix of a group once per (KV
-//    head, block of 16 (member, query head) rows): its four waves walk a
-//    quarter of the prefix each on the matrix cores (pkv::mfma::attend),
-//    combine their states through LDS and with the member's suffix pieces
-//    by log-sum-exp ([KVM §19.2.3] block-wise online softmax), and write
-//    the result.  Only the suffix pieces travel through memory.
+//    head, block of 32 (member, query head) rows): its eight waves walk an
+//    eighth of the prefix each on the matrix cores (pkv::mfma::attend_rows,
+//    two row groups of 16 per wave), combine their states through LDS and
+//    with the member's suffix pieces by log-sum-exp ([KVM §19.2.3]
+//    block-wise online softmax), and write the result.  Only the suffix
+//    pieces travel through memory.
 //
 // Only the final result is rounded to bf16.
 #include <hip/hip_runtime.h>
@@ -60,7 +61,7 @@ struct SharedArgs {
   int32_t max_prefix;            // prefix lengths are clamped to this
   int32_t max_group;             // larger groups share nothing (the grid has no rows for them)
   int32_t suf_parts, suf_tokens; // suffix partitions
-  int32_t row_blocks;            // prefix workgroups per (group, KV head): 16 rows each
+  int32_t row_blocks;            // prefix workgroups per (group, KV head): 32 rows each
   int32_t pre_blocks;            // prefix workgroups in all
   int32_t num_kv_heads;
   float scale_log2;              // FP8: the K tensor scale folded in
@@ -103,9 +104,11 @@ __device__ __forceinline__ int seq_prefix(const SharedArgs& a, int s, int L) {
 }
 
 // attn_suffix_kernel (one wave per workgroup) runs first; attn_prefix_kernel
-// (four waves, each with its own LDS tile area) second, finishing every
-// member's result.
-constexpr int kSharedWaves = 4;
+// (eight waves, each with its own LDS tile area, two row groups of 16 each)
+// second, finishing every member's result.
+constexpr int kSharedWaves = 8;
+constexpr int kPrefixRG = 2;                // row groups of 16 per prefix workgroup
+constexpr int kPrefixRows = 16 * kPrefixRG;
 
 template <int D, int Q, int W>
 struct SharedLds {
@@ -115,19 +118,25 @@ struct SharedLds {
 };
 
 // One bf16 tile of registers in flight for the single-wave walks, two for
-// one-byte codes (as in the single-wave decode walk).
+// one-byte codes (as in the single-wave decode walk): with two row groups a
+// wave this keeps the prefix walk within 256 registers.
 template <int Q> constexpr int shared_pd() { return Q == pkv::mfma::kBf16 ? 1 : 2; }
 
 // Prefix role, workgroup x of pre_blocks = H_kv * row_blocks * num_groups
 // (KV head fastest: with 8 KV heads all the row blocks of one head go to one
 // XCD, as workgroups are dealt to the XCDs round robin, and share its L2
-// copy of that head's prefix).  Rows: 16 (member, query head) pairs of the
-// group's members; the four waves walk a quarter of the prefix each, then
+// copy of that head's prefix).  Rows: 32 (member, query head) pairs of the
+// group's members, two row groups of 16 in every wave; the eight waves walk
+// an eighth of the prefix each (one workgroup per CU by LDS, 2 waves per
+// SIMD: more walks of half the length than four waves of quarters), then
 // combine their states through LDS into one piece per row.
 template <int D, int Q>
 __device__ void prefix_role(const SharedArgs& a, int x, SharedLds<D, Q, kSharedWaves>& lds) {
   constexpr int kW = kSharedWaves;
-  static_assert(16 * D * 4 + 16 * 8 <= int(sizeof(lds.k[0])), "a wave's state fits its K area");
+  static_assert(16 * D * 4 + 16 * 8 <= int(sizeof(lds.k[0])) &&
+                16 * D * 4 + 16 * 8 <= int(sizeof(lds.v[0])),
+                "a row group's state fits a wave's K (group 0) or V (group 1) area");
+  static_assert(kPrefixRG == 2, "the states of two row groups per wave");
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int g = x % a.num_kv_heads;
@@ -137,19 +146,26 @@ __device__ void prefix_role(const SharedArgs& a, int x, SharedLds<D, Q, kSharedW
   const int P = group_prefix(a, gi, &first, &count);
   const int G = a.group;
   const int nrows = count * G;  // (member, query head) rows of the group
-  const int r0 = 16 * rb;
+  const int r0 = kPrefixRows * rb;
   if (P == 0 || r0 >= nrows) return;  // uniform over the workgroup
 
-  // This lane's row (lane & 15): member j, query head hh of KV head g.
-  const int rg = r0 + (lane & 15);
-  const bool row_ok = rg < nrows;
-  const int j = row_ok ? rg / G : 0, hh = row_ok ? rg - j * G : 0;
-  const int s = first + j;
-  const int L = clamp_len(a.seq_lens[s], a.len_cap);
-  const int64_t qh = int64_t(s) * a.num_q_heads + g * G + hh;
+  // This lane's rows (lane & 15 of each row group): member j, query head hh
+  // of KV head g.
+  bool row_ok[kPrefixRG];
+  int p_row[kPrefixRG];
+  const uint16_t* qrow[kPrefixRG];
+#pragma unroll
+  for (int rg = 0; rg < kPrefixRG; ++rg) {
+    const int rr = r0 + 16 * rg + (lane & 15);
+    row_ok[rg] = rr < nrows;
+    const int j = row_ok[rg] ? rr / G : 0, hh = row_ok[rg] ? rr - j * G : 0;
+    const int s = first + j;
+    p_row[rg] = clamp_len(a.seq_lens[s], a.len_cap) - 1;
+    qrow[rg] = a.q + (int64_t(s) * a.num_q_heads + g * G + hh) * D;
+  }
   // Positions every member of the block sees: up to the shortest one's last;
   // positions some member sees: up to the longest one's last.
-  const int j_lo = r0 / G, j_hi = min(count, (r0 + 15) / G + 1);
+  const int j_lo = r0 / G, j_hi = min(count, (r0 + kPrefixRows - 1) / G + 1);
   int lmin = a.len_cap, lmax = 0;
   for (int m = j_lo + lane; m < j_hi; m += 64) {
     const int lm = clamp_len(a.seq_lens[first + m], a.len_cap);
@@ -173,24 +189,33 @@ __device__ void prefix_role(const SharedArgs& a, int x, SharedLds<D, Q, kSharedW
                                 a.num_kv_heads, a.v_scale,     a.k_scales,
                                 a.v_scales};
   // Wave w walks tiles [w * per, (w + 1) * per) of the prefix, alone (no
-  // workgroup barrier inside: the quarters may differ in length).
+  // workgroup barrier inside: the eighths may differ in length).
   const int tiles = (len + kKT - 1) / kKT;
   const int per = (tiles + kW - 1) / kW;
   const int t_lo = min(w * per * kKT, len), t_hi = min((w + 1) * per * kKT, len);
-  pkv::mfma::RowAcc<D> r;
-  pkv::mfma::start(r);
-  pkv::mfma::attend<D, 1, 2, Q, false, pkv::mfma::NoEmit, false, true>(
-      hist, t_lo, t_hi, a.q + qh * D, row_ok, L - 1, lmin - 1, a.scale_log2, lds.k[w], lds.v[w],
-      r, lds.s[w]);
-  // The wave's states to its K area: [row][D] weighted sums, then
+  pkv::mfma::RowAcc<D> r[kPrefixRG];
+#pragma unroll
+  for (int rg = 0; rg < kPrefixRG; ++rg) pkv::mfma::start(r[rg]);
+  // one tile of registers in flight for every kind: two row groups fill the
+  // register budget
+  pkv::mfma::attend_rows<D, 1, 1, Q, false, pkv::mfma::NoEmit, false, true, kPrefixRG>(
+      hist, t_lo, t_hi, qrow, row_ok, p_row, lmin - 1, a.scale_log2, lds.k[w], lds.v[w], r,
+      lds.s[w]);
+  // The wave's states to its own areas (its walk is over): row group 0 in
+  // its K area, 1 in its V area, each [row][D] weighted sums, then
   // (reference, sum) per row.
-  float* st = reinterpret_cast<float*>(lds.k[w]);
-  pkv::mfma::store_piece<D>(r, st + (lane & 15) * D, reinterpret_cast<float2*>(st + 16 * D) + (lane & 15));
+#pragma unroll
+  for (int rg = 0; rg < kPrefixRG; ++rg) {
+    float* st = reinterpret_cast<float*>(rg == 0 ? lds.k[w] : lds.v[w]);
+    pkv::mfma::store_piece<D>(r[rg], st + (lane & 15) * D,
+                              reinterpret_cast<float2*>(st + 16 * D) + (lane & 15));
+  }
   __syncthreads();
   // Thread t combines row t / 16, elements (t % 16) * D / 16 .. + D / 16 - 1:
-  // the four waves' states and the member's suffix pieces (the suffix kernel
-  // ran before), by log-sum-exp, into the result.
+  // the eight waves' states and the member's suffix pieces (the suffix
+  // kernel ran before), by log-sum-exp, into the result.
   constexpr int kE = D / 16;
+  static_assert(64 * kW == 16 * kPrefixRows, "one thread per (row, sixteenth of a row)");
   const int t = threadIdx.x;
   const int crow = t >> 4, d0 = (t & 15) * kE;
   const int crg = r0 + crow;
@@ -205,22 +230,26 @@ __device__ void prefix_role(const SharedArgs& a, int x, SharedLds<D, Q, kSharedW
   const int np_suf = cL > cP ? min(a.suf_parts, (cL - cP + a.suf_tokens - 1) / a.suf_tokens) : 0;
   const int64_t cqh = int64_t(cs) * a.num_q_heads + g * G + ch;
   const int64_t base = cqh * a.suf_parts;
+  const int cgrp = crow >> 4, crl = crow & 15;
+  const auto state = [&](int v) {
+    return reinterpret_cast<const float*>(cgrp == 0 ? lds.k[v] : lds.v[v]);
+  };
   float M = -INFINITY;
 #pragma unroll
   for (int v = 0; v < kW; ++v)
-    M = fmaxf(M, reinterpret_cast<const float2*>(reinterpret_cast<const float*>(lds.k[v]) + 16 * D)[crow].x);
+    M = fmaxf(M, reinterpret_cast<const float2*>(state(v) + 16 * D)[crl].x);
   for (int p = 0; p < np_suf; ++p) M = fmaxf(M, a.ws_ml[base + p].x);
   float lsum = 0.f, acc[kE];
 #pragma unroll
   for (int e = 0; e < kE; ++e) acc[e] = 0.f;
 #pragma unroll
   for (int v = 0; v < kW; ++v) {
-    const float* sv = reinterpret_cast<const float*>(lds.k[v]);
-    const float2 ml = reinterpret_cast<const float2*>(sv + 16 * D)[crow];
+    const float* sv = state(v);
+    const float2 ml = reinterpret_cast<const float2*>(sv + 16 * D)[crl];
     const float wgt = pkv::fast_exp2(ml.x - M);
     lsum = fmaf(wgt, ml.y, lsum);
 #pragma unroll
-    for (int e = 0; e < kE; ++e) acc[e] = fmaf(wgt, sv[crow * D + d0 + e], acc[e]);
+    for (int e = 0; e < kE; ++e) acc[e] = fmaf(wgt, sv[crl * D + d0 + e], acc[e]);
   }
   for (int p = 0; p < np_suf; ++p) {
     const float2 ml = a.ws_ml[base + p];
@@ -287,7 +316,7 @@ __device__ void suffix_role(const SharedArgs& a, int64_t item, SharedLds<D, Q, 1
   pkv::mfma::store_piece<D>(r, a.ws_acc + slot * D, a.ws_ml + slot);
 }
 
-// grid = pre_blocks, four waves.
+// grid = pre_blocks, eight waves (one workgroup per CU by LDS).
 template <int D, int Q>
 __global__ void __launch_bounds__(64 * kSharedWaves)
 __attribute__((amdgpu_waves_per_eu(2)))
@@ -344,8 +373,8 @@ pkv_status shared_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_groups
   if (num_seqs > 65535 || num_groups > 65535 || g->num_kv_heads > 65535)
     return pkv::fail(PKV_ERR_INVALID_ARG, "%s: more than 65535 sequences, groups or KV heads", who);
   const int mg = max_group_size > 0 ? max_group_size : 1;
-  // 16 (member, query head) rows per prefix workgroup
-  pl->row_blocks = static_cast<int>((int64_t(mg) * G + 15) / 16);
+  // 32 (member, query head) rows per prefix workgroup
+  pl->row_blocks = static_cast<int>((int64_t(mg) * G + kPrefixRows - 1) / kPrefixRows);
   const int seq_len = max_seq_len > 0 ? max_seq_len : 1;
   // Suffix partitions from the longest suffix (a hint: longer suffixes are
   // folded into the grid's pieces): short critical paths, about 4096 items.

@@ -255,7 +255,6 @@ __device__ __forceinline__ void attend_rows(const History& h, int t_lo, int t_hi
   static_assert(!kAppend || NW == 1, "the folded append runs in single-wave passes");
   static_assert(NW == 1 || PD == 2, "several waves keep two tiles of registers in flight");
   static_assert(!kWaveOnly || NW == 1, "a wave-only walk is a single wave's");
-  static_assert(RG == 1 || NW >= 2, "row groups per wave take the multi-wave walks");
   // A single wave's LDS accesses run in order: it waits for its own and
   // needs the workgroup barrier only when its workgroup is one wave.  A
   // wave-only walk (kWaveOnly: one of several independent walks in a
