@@ -69,7 +69,8 @@ struct MultiArgs {
 
 // RG row groups of 16 per wave (16 NW RG rows per workgroup).  Register
 // budgets that keep workgroups resident: eight-wave ones two per CU (<= 128
-// registers a lane), four-wave ones three, or two with two row groups a wave.
+// registers a lane), four-wave ones three, or two with two row groups a wave
+// (the 128-row instance).
 template <int D, int NW, int Q, bool kStream, int RG = 1>
 __global__ void __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(NW == 8 ? 4 : (NW == 4 ? (RG == 2 ? 2 : 3) : 1))))
@@ -257,9 +258,10 @@ pkv_status multi_plan(int32_t num_seqs, int32_t num_q_heads, int32_t total_q,
     return pkv::fail(PKV_ERR_INVALID_ARG, "%s: partition_tokens %d must be a multiple of %d",
                      who, partition_tokens, kKT);
   const int mq = max_q_per_seq > 0 ? max_q_per_seq : 1;
-  // 16 rows per wave, up to 4 waves; 8 (128 rows) for longer chunks of
-  // bf16 rows of 128, whose K/V tiles then serve twice the rows per staging
-  // (one-byte and 64-wide tiles have 256 chunks, too few for 8 waves)
+  // 16 rows per wave, up to 4 waves; 128 rows (nw = 8 here: four waves of
+  // two 16-row groups, launched as such) for longer chunks of bf16 rows of
+  // 128, whose K/V tiles then serve twice the rows per staging (one-byte and
+  // 64-wide tiles keep 64 rows)
   const bool wide = g->head_dim == 128 && !quant;
   const int cap = (wide ? 128 : 64) / G;
   const int rows = (mq < cap ? mq : cap) * G;

@@ -14,7 +14,10 @@
 //    ahead and V one), with one barrier per tile; a single wave's LDS
 //    accesses run in order, so it uses one buffer.  Tiles' global loads are
 //    issued two tiles ahead of their staging, and the barrier waits only for
-//    LDS, so they stay in flight.
+//    LDS, so they stay in flight; bf16 rows of 128 on eight waves (or four
+//    of two row groups) load straight into four LDS buffers instead.
+//  * A wave carries RG groups of 16 query rows (attend_rows): each K/V
+//    operand read from LDS feeds RG matrix instructions.
 //  * Scores as S^T = K Q^T with v_mfma_f32_16x16x32_bf16: a lane's result
 //    fragment holds 8 positions of one query row (its lane & 15), so the
 //    online softmax (log2 units) needs only the ^16 and ^32 lane exchanges,
@@ -66,10 +69,11 @@ template <int NW> constexpr int lds_tiles() { return NW == 1 ? 1 : 2; }
 // Element kinds of the cache pools.
 enum Kind : int { kBf16 = 0, kFp8 = 1, kInt8 = 2 };
 
-// Eight-wave passes over bf16 pools with head_dim 128 load tiles straight
-// into LDS (gfx950's global_load_lds_dwordx4: each lane's 16 bytes land at
-// the wave's LDS base + 16 * lane, no registers and no LDS stores), into
-// four buffers each of K and V in the padded row layout.
+// Passes over bf16 pools with head_dim 128 on eight waves, or on four waves
+// of two row groups, load tiles straight into LDS (gfx950's
+// global_load_lds_dwordx4: each lane's 16 bytes land at the wave's LDS base
+// + 16 * lane, no registers and no LDS stores), into four buffers each of K
+// and V in the padded row layout.
 template <int D, int NW, int Q, int RG = 1> constexpr bool direct_lds() {
   return Q == kBf16 && D == 128 && (NW == 8 || (NW == 4 && RG == 2));
 }
