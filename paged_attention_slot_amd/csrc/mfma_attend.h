@@ -283,21 +283,15 @@ __device__ __forceinline__ void attend_rows(const History& h, int t_lo, int t_hi
   const int lane = tid & 63;
   const int quad = lane >> 4;
 
-  // Scores are scaled inside the exponent (one fma with the reference) and
-  // their max is taken unscaled, which needs a positive scale: a negative
-  // one flips the query's signs instead (exact in bf16), and the magnitude
-  // is kept off zero so a masked score never meets 0 * -inf.
-  const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
-  scale_log2 = fmaxf(fabsf(scale_log2), 1e-30f);
+  // The query rows as the score product's B operand (zeros for rows not
+  // live); the scale enters with the exponent's fma.
   uint4 qf[RG][kKS];
 #pragma unroll
   for (int g = 0; g < RG; ++g)
 #pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) {
-      uint4 x = row_ok[g] ? *reinterpret_cast<const uint4*>(q[g] + 32 * ks + 8 * quad)
-                          : make_uint4(0, 0, 0, 0);
-      qf[g][ks] = make_uint4(x.x ^ qsign, x.y ^ qsign, x.z ^ qsign, x.w ^ qsign);
-    }
+    for (int ks = 0; ks < kKS; ++ks)
+      qf[g][ks] = row_ok[g] ? *reinterpret_cast<const uint4*>(q[g] + 32 * ks + 8 * quad)
+                            : make_uint4(0, 0, 0, 0);
 
   const int L = h.len;
   const int bmask = (1 << h.block_shift) - 1;
@@ -509,44 +503,47 @@ __device__ __forceinline__ void attend_rows(const History& h, int t_lo, int t_hi
       for (int g = 0; g < RG; ++g) s[g][pt] = acc[g];
     }
   };
-  // A tile's scores, ready for the exponent: masked (-inf) where the lane's
-  // row does not see the position, INT8 scaled with the key scales (scale
-  // slot ss); and the state's reference moved if some lane's score exceeds
-  // its row's reference by more than kSlack.
-  auto prepare = [&](int t0, int ss, const f32x4_t (&s)[RG][2], float (&sc)[RG][8]) {
-    const float* st = s_lds + 2 * kKT * ss;
+  // A tile's exponents x = scale * score - m (log2 units, m the row's
+  // reference), -inf where the lane's row does not see the position; INT8
+  // scores carry their key scales (scale slot ss).  If some lane's x exceeds
+  // kSlack, the references move to the rows' maxima (the state rescaled) and
+  // the exponents are formed again against them.  The exponents are fresh
+  // registers, so the scores' registers are free for the next tile's product.
+  auto exps = [&](int t0, const float* st, const f32x4_t (&s)[RG][2], int g, float mref,
+                  float (&x)[RG][8]) {
 #pragma unroll
-    for (int g = 0; g < RG; ++g)
+    for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
-      for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // bf16 and FP8: unscaled here; INT8: scaled with its key scale
-          float v = s[g][pt][i];
-          if constexpr (Q == kInt8) v *= scale_log2 * st[16 * pt + 4 * quad + i];
-          sc[g][4 * pt + i] = v;
-        }
+      for (int i = 0; i < 4; ++i) {
+        float c = scale_log2;
+        if constexpr (Q == kInt8) c *= st[16 * pt + 4 * quad + i];
+        x[g][4 * pt + i] = fmaf(s[g][pt][i], c, -mref);
+      }
     // Uniform: some live row does not see every position of the tile.  Score
     // e = 4 pt + i sits at position t0 + 16 pt + 4 quad + i, visible to this
     // lane's row iff 16 pt + i <= vis.
     if (t0 + kKT - 1 > p_all || t0 + kKT > t_hi) {
+      const int vis = row_lim[g] - t0 - 4 * quad;
 #pragma unroll
-      for (int g = 0; g < RG; ++g) {
-        const int vis = row_lim[g] - t0 - 4 * quad;
+      for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
-        for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sc[g][4 * pt + i] = 16 * pt + i <= vis ? sc[g][4 * pt + i] : -INFINITY;
-      }
+        for (int i = 0; i < 4; ++i)
+          x[g][4 * pt + i] = 16 * pt + i <= vis ? x[g][4 * pt + i] : -INFINITY;
     }
+  };
+  // (the NaN-propagating maximum: its operands need no quieting first)
+  const auto max8 = [](const float (&v)[8]) {
+    const auto mx = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
+    return mx(mx(mx(mx(v[0], v[1]), v[2]), mx(mx(v[3], v[4]), v[5])), mx(v[6], v[7]));
+  };
+  auto prepare = [&](int t0, int ss, const f32x4_t (&s)[RG][2], float (&x)[RG][8]) {
+    const float* st = s_lds + 2 * kKT * ss;
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
-      float tmax = fmaxf(fmaxf(fmaxf(sc[g][0], sc[g][1]), fmaxf(sc[g][2], sc[g][3])),
-                         fmaxf(fmaxf(sc[g][4], sc[g][5]), fmaxf(sc[g][6], sc[g][7])));
-      if constexpr (Q != kInt8) tmax *= scale_log2;
-      if (__builtin_amdgcn_ballot_w64(tmax > r[g].m + kSlack) != 0) {  // uniform
-        const float mn = fmaxf(r[g].m, max_across_rows16(tmax));
+      exps(t0, st, s, g, r[g].m, x);
+      if (__builtin_amdgcn_ballot_w64(max8(x[g]) > kSlack) != 0) {  // uniform
+        exps(t0, st, s, g, 0.f, x);  // the scaled scores themselves
+        const float mn = fmaxf(r[g].m, max_across_rows16(max8(x[g])));
         const float alpha = fast_exp2(r[g].m - mn);
         r[g].m = mn;
         lpart[g] *= alpha;
@@ -554,33 +551,27 @@ __device__ __forceinline__ void attend_rows(const History& h, int t_lo, int t_hi
         for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) r[g].o[dt][i] *= alpha;
+        exps(t0, st, s, g, mn, x);
       }
     }
   };
-  // The weights of prepared scores and their P V: vfrag(dt) reads this
+  // The weights of prepared exponents and their P V: vfrag(dt) reads this
   // lane's V^T operand of d tile dt (V^T[16 dt + (lane & 15)][positions
   // 4 quad .. + 3 and 16 + 4 quad .. + 3]); INT8's V scales in slot ss.
   // Each V operand read serves the RG row groups of the wave.
-  auto weigh = [&](const auto& vfrag, int ss, const float (&sc)[RG][8]) {
+  auto weigh = [&](const auto& vfrag, int ss, const float (&x)[RG][8]) {
     const float* st = s_lds + 2 * kKT * ss;
     // Weights as two bf16 terms, p = hi + lo (hi = bf16(p), lo = bf16(p - hi)):
     // P V then carries p to about 2^-17 relative, like the fp32 sum.
     bf16x8_t pfh[RG], pfl[RG];
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
-      const float mref = r[g].m;
       uint32_t ph[4], pl[4];
       float psum;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        float p0, p1;
-        if constexpr (Q == kInt8) {
-          p0 = fast_exp2(sc[g][2 * k] - mref);
-          p1 = fast_exp2(sc[g][2 * k + 1] - mref);
-        } else {
-          p0 = fast_exp2(fmaf(sc[g][2 * k], scale_log2, -mref));
-          p1 = fast_exp2(fmaf(sc[g][2 * k + 1], scale_log2, -mref));
-        }
+        float p0 = fast_exp2(x[g][2 * k]);
+        float p1 = fast_exp2(x[g][2 * k + 1]);
         psum = k == 0 ? p0 + p1 : psum + (p0 + p1);
         // score element e = 2k (+1) sits at tile position 16 (e / 4) + 4 quad + e % 4
         if constexpr (Q == kFp8) {
