@@ -361,6 +361,24 @@ def test_modes_match_oracle(mode_env, mode, dtype, B, D, Hq, Hkv):
     assert_gate(gpu_out(step), ref, dtype, f"mode {mode}")
 
 
+@pytest.mark.parametrize("mode", [2, 3, 4], ids=["balanced", "matrix", "matrix-balanced"])
+@pytest.mark.parametrize("scale", [-0.0884, 0.0, 0.75], ids=["negative", "zero", "sharp"])
+def test_routes_with_unusual_scales(mode_env, mode, scale):
+    """Softmax scales taken as they come ([KVM] §19.2.3 applies the caller's
+    scale to q.k): negative (the weights favour the least similar keys), zero
+    (uniform weights over the history) and large (a sharp softmax whose
+    running reference moves often), on the vector balanced split and both
+    matrix-core routes, every element against the oracle."""
+    mode_env(mode)
+    lens = [1, 17, 32, 33, 300, 1000, 2047]
+    wl = independent_workload(lens, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                              dtype="bf16", seed=140 + mode, scale=scale)
+    step, ost = run_both(wl)
+    ref = oracle_attention(wl.q, ost.k_pool, ost.v_pool, ost.block_tables, ost.seq_lens,
+                           wl.scale)
+    say("  gate", assert_gate(gpu_out(step), ref, "bf16", f"mode {mode} scale {scale}"))
+
+
 MBAL = [  # B, Hq, Hkv
     (16, 16, 8), (16, 32, 8), (32, 64, 8), (8, 32, 2), (16, 128, 8), (64, 24, 4), (32, 128, 16),
 ]
