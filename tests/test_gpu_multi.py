@@ -59,7 +59,7 @@ def run_case(seed, lens, nq, Hq, Hkv, D, B, pt=0, scale=None):
     say(f"  case seed={seed} N={len(lens)} Hq={Hq} Hkv={Hkv} D={D} B={B} pt={pt} "
         f"lens={lens[:6]} nq={nq[:6]}")
     q, offs, kp, vp, tables, lens_a = case(seed, lens, nq, Hq, Hkv, D, B)
-    scale = scale or 1.0 / np.sqrt(D)
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
     out = ops.attention_multi(dev_bf16(q), torch.from_numpy(offs).cuda(), dev_bf16(kp),
                               dev_bf16(vp), torch.from_numpy(tables).cuda(),
                               torch.from_numpy(lens_a).cuda(), scale, max(nq),
@@ -95,6 +95,20 @@ def test_long_prefill_chunks(Hq, Hkv, D, B):
     nq = [512, 200, 301, 13]
     got, ref, _ = run_case(700 + Hq + D, lens, nq, Hq, Hkv, D, B)
     say("  gate", assert_gate(got, ref, "bf16", "prefill chunks"))
+
+
+@pytest.mark.parametrize("scale", [-0.0884, 0.0, 0.75], ids=["negative", "zero", "sharp"])
+@pytest.mark.parametrize("Hq,Hkv,D,B", [(32, 8, 128, 16), (12, 4, 64, 32), (16, 16, 128, 8)],
+                         ids=lambda v: str(v))
+def test_chunks_with_unusual_scales(Hq, Hkv, D, B, scale):
+    """The caller's scale as it comes (negative, zero, large enough that the
+    running references move often) on prefill-shaped chunks and single
+    queries: the four-wave direct-load walk, the register-staged walks and the
+    one-wave walk, against the oracle."""
+    lens = [512, 700, 301, 64, 9]
+    nq = [512, 200, 301, 13, 1]
+    got, ref, _ = run_case(800 + Hq + D, lens, nq, Hq, Hkv, D, B, scale=scale)
+    say("  gate", assert_gate(got, ref, "bf16", f"chunks scale {scale}"))
 
 
 @pytest.mark.parametrize("pt", [32, 64, 256])
