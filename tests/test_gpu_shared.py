@@ -85,6 +85,22 @@ def test_families(prefix, suffix, fp, spf, Hq, Hkv, D, B):
     assert_gate(got, ref, "bf16", wl.name)
 
 
+@pytest.mark.parametrize("scale", [-0.0884, 0.0, 0.75], ids=["negative", "zero", "sharp"])
+def test_family_with_unusual_scales(scale):
+    """The caller's scale as it comes on both kernels of the read-once path
+    (the prefix walk's two row groups, the suffix walks, the combine of their
+    states): negative, zero and large enough that the references move."""
+    wl = shared_prefix_workload(prefix_tokens=512, suffix_lens=[100, 1, 37, 250, 64, 3],
+                                forking_parents=2, samples_per_fork=3, num_q_heads=32,
+                                num_kv_heads=8, head_dim=128, block_size=32, dtype="bf16", seed=91,
+                                name="family-scale")
+    wl.scale = scale
+    wl.num_blocks += 16
+    wl.free_order = np.random.default_rng(91).permutation(wl.num_blocks).astype(np.int32)
+    got, ref, _ = run_wl(wl)
+    say("  gate", assert_gate(got, ref, "bf16", f"scale {scale}"))
+
+
 def hand_case(tables, lens, Hq, Hkv, D, B, nb, seed):
     from paged_attention_slot_amd import ops
     rng = np.random.default_rng(seed)
