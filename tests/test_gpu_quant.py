@@ -95,6 +95,21 @@ def test_modes_and_splits(kind, mode, tuning):
     assert_gate(gpu_out(step), ost.attention(), "bf16", f"{kind} mode {mode}")
 
 
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("mode", [2, 3, 4], ids=["balanced", "matrix", "matrix-balanced"])
+@pytest.mark.parametrize("scale", [-0.0884, 0.75], ids=["negative", "sharp"])
+def test_unusual_softmax_scales(kind, mode, scale, tuning):
+    """A negative softmax scale and one large enough that the running
+    references move often, over one-byte caches (the FP8 tensor scale and the
+    INT8 per-slot key scales folded into the exponents) on the vector and both
+    matrix-core routes."""
+    tuning("PKV_ATTN_MODE", mode)
+    wl = independent_workload([1, 17, 33, 300, 1000, 2047], num_q_heads=32, num_kv_heads=8,
+                              head_dim=128, block_size=16, dtype="bf16", seed=47, scale=scale)
+    step, ost = run_both(wl, kind, k_scale=0.5 if kind == "fp8_e4m3" else 1.0)
+    say("  gate", assert_gate(gpu_out(step), ost.attention(), "bf16", f"{kind} mode {mode}"))
+
+
 def test_fp8_scales_other_than_one():
     wl = independent_workload([5, 40, 129], num_q_heads=16, num_kv_heads=4, head_dim=128,
                               block_size=16, dtype="bf16", seed=43)
