@@ -162,10 +162,14 @@ pkv_status pkv_copy_blocks_quant(const int32_t* src_dst_pairs, int32_t num_pairs
  *
  * pkv_attention_decode_shared computes exactly what pkv_attention_decode
  * computes (bf16 pools) but reads each group's shared prefix once per block of
- * 32 (member, query head) rows instead of once per sequence: first every
- * sequence's own positions (fp32 partial states in the workspace), then the
- * prefix positions of all members on the matrix cores, each block's result
- * combined with its members' partial states by log-sum-exp.
+ * 32 (member, query head) rows instead of once per sequence.  With a suffix
+ * hint of at most 1024 positions one launch does the step: each block's
+ * workgroup walks its members' own positions and the prefix on the matrix
+ * cores and combines the states in LDS by log-sum-exp, and further workgroups
+ * attend the sequences that share nothing.  Otherwise every sequence's own
+ * positions go first (fp32 partial states in the workspace), then the prefix
+ * positions of all members, each block's result combined with its members'
+ * partial states.
  *   group_starts  device int32 [num_groups + 1]: group g is sequences
  *                 group_starts[g] .. group_starts[g+1]-1 (non-decreasing,
  *                 from 0 to num_seqs);
@@ -178,8 +182,9 @@ pkv_status pkv_copy_blocks_quant(const int32_t* src_dst_pairs, int32_t num_pairs
  *                 larger than max_group_size shares nothing).
  *   max_suffix_len  host hint: the longest run of positions after a
  *                 sequence's shared prefix (pkv_prefix_groups reports it);
- *                 it only sizes the suffix partitions (0 = max_seq_len; a
- *                 longer suffix is still attended in full).
+ *                 it chooses the form above and sizes the suffix partitions
+ *                 (0 = max_seq_len; a longer suffix is still attended in
+ *                 full).
  * Other arguments as pkv_attention_decode (q, out [num_seqs][H_q][D] bf16).
  * The workspace is required (pkv_attention_shared_workspace_bytes).  Groups
  * that break the contract give unspecified values, never out-of-pool reads.

@@ -11,18 +11,25 @@
 // read reuse depends on the kernel).  Here the caller names groups of
 // consecutive sequences and the length of the prefix they share, and
 //
-//  * attn_suffix_kernel (first) reads every sequence's positions after its
-//    prefix, one (sequence, KV head, partition) per workgroup, the G query
-//    heads as rows, and leaves one fp32 piece (weighted sum, reference,
-//    sum) per partition; a sequence without a shared prefix is attended
-//    whole by its first partition's workgroup, which writes its result;
-//  * attn_prefix_kernel (second) reads the prefix of a group once per (KV
-//    head, block of 32 (member, query head) rows): its eight waves walk an
-//    eighth of the prefix each on the matrix cores (pkv::mfma::attend_rows,
-//    two row groups of 16 per wave), combine their states through LDS and
-//    with the member's suffix pieces by log-sum-exp ([KVM §19.2.3]
-//    block-wise online softmax), and write the result.  Only the suffix
-//    pieces travel through memory.
+//  * attn_prefix_fused_kernel (suffix hints up to kFusedSuffix positions,
+//    one launch): the workgroup of a (KV head, block of 32 (member, query
+//    head) rows) first walks its members' own positions after the prefix
+//    (items of one member and up to 16 of its rows, its query heads, dealt
+//    to the waves in turn), then the prefix, cut among its eight waves so
+//    that their walks even out, on the matrix cores (pkv::mfma::attend_rows,
+//    two row groups of 16 per wave for the prefix), and combines all the
+//    states through LDS by
+//    log-sum-exp ([KVM §19.2.3] block-wise online softmax): nothing travels
+//    through memory but the result.  The workgroups past the prefix ones
+//    attend the sequences that share nothing, whole.
+//  * Otherwise, attn_suffix_kernel (first) reads every sequence's positions
+//    after its prefix, one (sequence, KV head, partition) per workgroup, and
+//    leaves one fp32 piece (weighted sum, reference, sum) per partition (a
+//    sequence without a shared prefix is attended whole by its first
+//    partition's workgroup, which writes its result); attn_prefix_kernel
+//    (second) reads the prefix of a group once per (KV head, block of 32
+//    rows), its eight waves an eighth each, and combines their states with
+//    the members' suffix pieces.
 //
 // Only the final result is rounded to bf16.
 #include <hip/hip_runtime.h>
@@ -64,6 +71,7 @@ struct SharedArgs {
   int32_t row_blocks;            // prefix workgroups per (group, KV head): 32 rows each
   int32_t pre_blocks;            // prefix workgroups in all
   int32_t num_kv_heads;
+  int32_t fused;                // the prefix kernel walks its members' suffixes too
   float scale_log2;              // FP8: the K tensor scale folded in
   float v_scale;                 // FP8
   const float* k_scales;         // INT8
@@ -109,12 +117,21 @@ __device__ __forceinline__ int seq_prefix(const SharedArgs& a, int s, int L) {
 constexpr int kSharedWaves = 8;
 constexpr int kPrefixRG = 2;                // row groups of 16 per prefix workgroup
 constexpr int kPrefixRows = 16 * kPrefixRG;
+constexpr int kFusedSuffix = 1024;         // longest suffix hint the prefix kernel walks itself
 
 template <int D, int Q, int W>
 struct SharedLds {
   uint16_t k[W][pkv::mfma::k_lds_elems<D, 1, Q>()];
   uint16_t v[W][pkv::mfma::v_lds_elems<D, 1, Q>()];
   float s[W][pkv::mfma::s_lds_elems<Q, 1>()];
+};
+
+// The suffix states of a prefix workgroup's rows when it walks its members'
+// suffixes itself: [row][D] weighted sums, then (reference, sum) per row.
+template <int D>
+struct SuffixStates {
+  float acc[32][D];
+  float2 ml[32];
 };
 
 // One bf16 tile of registers in flight for the single-wave walks, two for
@@ -130,8 +147,16 @@ template <int Q> constexpr int shared_pd() { return Q == pkv::mfma::kBf16 ? 1 : 
 // an eighth of the prefix each (one workgroup per CU by LDS, 2 waves per
 // SIMD: more walks of half the length than four waves of quarters), then
 // combine their states through LDS into one piece per row.
-template <int D, int Q>
-__device__ void prefix_role(const SharedArgs& a, int x, SharedLds<D, Q, kSharedWaves>& lds) {
+//
+// kFused: the workgroup also walks its members' own positions after the
+// prefix (so the suffix kernel leaves the group's members alone): work items
+// (member, up to 16 of its rows in the block) go to the waves round robin,
+// each a single-wave walk of that member's suffix with its query heads as
+// rows, before the prefix eighths; the states wait in ``suf`` for the
+// combine, and no piece travels through memory.
+template <int D, int Q, bool kFused>
+__device__ void prefix_role(const SharedArgs& a, int x, SharedLds<D, Q, kSharedWaves>& lds,
+                            SuffixStates<D>* suf) {
   constexpr int kW = kSharedWaves;
   static_assert(16 * D * 4 + 16 * 8 <= int(sizeof(lds.k[0])) &&
                 16 * D * 4 + 16 * 8 <= int(sizeof(lds.v[0])),
@@ -188,11 +213,81 @@ __device__ void prefix_role(const SharedArgs& a, int x, SharedLds<D, Q, kSharedW
                                 a.row_elems,    a.num_blocks,  a.block_shift,
                                 a.num_kv_heads, a.v_scale,     a.k_scales,
                                 a.v_scales};
+  if constexpr (kFused) {
+    // Suffix items, in member order: member j's rows of the block are
+    // [max(j G - r0, 0), min((j + 1) G - r0, 32, nrows - r0)), in chunks of 16.
+    int item = 0;
+    for (int j = j_lo; j < j_hi; ++j) {
+      const int ra = max(j * G - r0, 0);
+      const int rb = min(min((j + 1) * G - r0, kPrefixRows), nrows - r0);
+      for (int c0 = ra; c0 < rb; c0 += 16, ++item) {
+        if (item % kW != w) continue;  // uniform
+        const int i = c0 + (lane & 15);  // this lane's row of the block
+        const bool ok = i < min(c0 + 16, rb);
+        const int sj = first + j;
+        const int Lj = clamp_len(a.seq_lens[sj], a.len_cap);
+        const int hh = ok ? r0 + i - j * G : 0;
+        const uint16_t* const sq[1] = {a.q + (int64_t(sj) * a.num_q_heads + g * G + hh) * D};
+        const bool sok[1] = {ok};
+        const int sp[1] = {Lj - 1};
+        const pkv::mfma::History sh{a.k_cache,      a.v_cache,     a.block_tables + int64_t(sj) * a.max_blocks,
+                                    Lj,             g,             a.block_elems,
+                                    a.row_elems,    a.num_blocks,  a.block_shift,
+                                    a.num_kv_heads, a.v_scale,     a.k_scales,
+                                    a.v_scales};
+        pkv::mfma::RowAcc<D> rs[1];
+        pkv::mfma::start(rs[0]);
+        pkv::mfma::attend_rows<D, 1, shared_pd<Q>(), Q, false, pkv::mfma::NoEmit, false, true, 1>(
+            sh, min(P, Lj), Lj, sq, sok, sp, Lj - 1, a.scale_log2, lds.k[w], lds.v[w], rs,
+            lds.s[w]);
+        if (ok) pkv::mfma::store_piece<D>(rs[0], suf->acc[i], &suf->ml[i]);
+      }
+    }
+  }
   // Wave w walks tiles [w * per, (w + 1) * per) of the prefix, alone (no
-  // workgroup barrier inside: the eighths may differ in length).
+  // workgroup barrier inside: the eighths may differ in length).  kFused:
+  // the prefix is cut so that the waves' walks even out, a prefix tile (two
+  // row groups) counting twice a suffix tile (one): wave w takes prefix
+  // tiles in proportion to max(0, C - S_w), S_w its suffix tiles and C the
+  // workgroup's total over the waves.
   const int tiles = (len + kKT - 1) / kKT;
   const int per = (tiles + kW - 1) / kW;
-  const int t_lo = min(w * per * kKT, len), t_hi = min((w + 1) * per * kKT, len);
+  int t_lo = min(w * per * kKT, len), t_hi = min((w + 1) * per * kKT, len);
+  if constexpr (kFused) {
+    int sw[kW];
+#pragma unroll
+    for (int u = 0; u < kW; ++u) sw[u] = 0;
+    int item = 0;
+    for (int j = j_lo; j < j_hi; ++j) {
+      const int Lj = clamp_len(a.seq_lens[first + j], a.len_cap);
+      const int st = (Lj - min(P, Lj) + kKT - 1) / kKT;
+      const int ra = max(j * G - r0, 0);
+      const int rb = min(min((j + 1) * G - r0, kPrefixRows), nrows - r0);
+      for (int c0 = ra; c0 < rb; c0 += 16, ++item) {
+        const int v = item % kW;
+#pragma unroll
+        for (int u = 0; u < kW; ++u) sw[u] += u == v ? st : 0;
+      }
+    }
+    int tot = 0;
+#pragma unroll
+    for (int u = 0; u < kW; ++u) tot += sw[u];
+    const int C = (2 * tiles + tot + kW - 1) / kW;
+    int dsum = 0, before = 0, mine = 0;
+#pragma unroll
+    for (int u = 0; u < kW; ++u) {
+      const int d = max(0, C - sw[u]);
+      before += u < w ? d : 0;
+      mine = u == w ? d : mine;
+      dsum += d;
+    }
+    if (dsum > 0) {
+      const int b0 = static_cast<int>(int64_t(tiles) * before / dsum);
+      const int b1 = static_cast<int>(int64_t(tiles) * (before + mine) / dsum);
+      t_lo = min(b0 * kKT, len);
+      t_hi = min(b1 * kKT, len);
+    }
+  }
   pkv::mfma::RowAcc<D> r[kPrefixRG];
 #pragma unroll
   for (int rg = 0; rg < kPrefixRG; ++rg) pkv::mfma::start(r[rg]);
@@ -227,7 +322,8 @@ __device__ void prefix_role(const SharedArgs& a, int x, SharedLds<D, Q, kSharedW
   // (a member with nothing to attend, cL = 0, was written whole by the
   // suffix kernel)
   if (cP == 0) return;
-  const int np_suf = cL > cP ? min(a.suf_parts, (cL - cP + a.suf_tokens - 1) / a.suf_tokens) : 0;
+  const int np_suf =
+      kFused || cL <= cP ? 0 : min(a.suf_parts, (cL - cP + a.suf_tokens - 1) / a.suf_tokens);
   const int64_t cqh = int64_t(cs) * a.num_q_heads + g * G + ch;
   const int64_t base = cqh * a.suf_parts;
   const int cgrp = crow >> 4, crl = crow & 15;
@@ -239,9 +335,17 @@ __device__ void prefix_role(const SharedArgs& a, int x, SharedLds<D, Q, kSharedW
   for (int v = 0; v < kW; ++v)
     M = fmaxf(M, reinterpret_cast<const float2*>(state(v) + 16 * D)[crl].x);
   for (int p = 0; p < np_suf; ++p) M = fmaxf(M, a.ws_ml[base + p].x);
+  if constexpr (kFused) M = fmaxf(M, suf->ml[crow].x);
   float lsum = 0.f, acc[kE];
 #pragma unroll
   for (int e = 0; e < kE; ++e) acc[e] = 0.f;
+  if constexpr (kFused) {
+    const float2 ml = suf->ml[crow];
+    const float wgt = pkv::fast_exp2(ml.x - M);
+    lsum = ml.y * wgt;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) acc[e] = wgt * suf->acc[crow][d0 + e];
+  }
 #pragma unroll
   for (int v = 0; v < kW; ++v) {
     const float* sv = state(v);
@@ -273,9 +377,9 @@ __device__ void prefix_role(const SharedArgs& a, int x, SharedLds<D, Q, kSharedW
 // piece).  A sequence without a shared prefix is attended whole by its part
 // 0 items, which write the result.
 template <int D, int Q>
-__device__ void suffix_role(const SharedArgs& a, int64_t item, SharedLds<D, Q, 1>& lds) {
+__device__ void suffix_role(const SharedArgs& a, int64_t item, uint16_t* k_lds, uint16_t* v_lds,
+                            float* s_lds) {
   const int lane = threadIdx.x & 63;
-  constexpr int w = 0;
   const int rgs = (a.group + 15) / 16;
   const int rgi = static_cast<int>(item % rgs);
   const int part = static_cast<int>((item / rgs) % a.suf_parts);
@@ -286,6 +390,7 @@ __device__ void suffix_role(const SharedArgs& a, int64_t item, SharedLds<D, Q, 1
   const int L = clamp_len(a.seq_lens[s], a.len_cap);
   const int P = seq_prefix(a, s, L);
   const bool whole = P == 0;
+  if (!whole && a.fused) return;  // the prefix kernel walks this member's positions
   if (whole ? part > 0 : P + part * a.suf_tokens >= L) return;
 
   const int G = a.group;
@@ -302,15 +407,14 @@ __device__ void suffix_role(const SharedArgs& a, int64_t item, SharedLds<D, Q, 1
   constexpr int kPD = shared_pd<Q>();
   if (whole) {
     pkv::mfma::attend<D, 1, kPD, Q, false, pkv::mfma::NoEmit, false, true>(
-        hist, 0, L, a.q + qh * D, row_ok, L - 1, L - 1, a.scale_log2, lds.k[w], lds.v[w], r,
-        lds.s[w]);
+        hist, 0, L, a.q + qh * D, row_ok, L - 1, L - 1, a.scale_log2, k_lds, v_lds, r, s_lds);
     if (row_ok) pkv::mfma::store_row_bf16<D>(r, a.out + qh * D);
     return;
   }
   for (int t_lo = P + part * a.suf_tokens; t_lo < L; t_lo += a.suf_parts * a.suf_tokens)
     pkv::mfma::attend<D, 1, kPD, Q, false, pkv::mfma::NoEmit, false, true>(
         hist, t_lo, min(t_lo + a.suf_tokens, L), a.q + qh * D, row_ok, L - 1, L - 1,
-        a.scale_log2, lds.k[w], lds.v[w], r, lds.s[w]);
+        a.scale_log2, k_lds, v_lds, r, s_lds);
   if (!row_ok) return;
   const int64_t slot = qh * a.suf_parts + part;
   pkv::mfma::store_piece<D>(r, a.ws_acc + slot * D, a.ws_ml + slot);
@@ -322,7 +426,29 @@ __global__ void __launch_bounds__(64 * kSharedWaves)
 __attribute__((amdgpu_waves_per_eu(2)))
 attn_prefix_kernel(SharedArgs a) {
   __shared__ __align__(16) SharedLds<D, Q, kSharedWaves> lds;
-  prefix_role<D, Q>(a, static_cast<int>(blockIdx.x), lds);
+  prefix_role<D, Q, false>(a, static_cast<int>(blockIdx.x), lds, nullptr);
+}
+
+// The same with the members' suffixes walked in the workgroup (kFused).
+// grid = pre_blocks + whole_blocks: the workgroups past the prefix ones take
+// the sequences that share nothing (suffix items of part 0, round robin over
+// their waves; the others return at once), so one launch does the step.
+template <int D, int Q>
+__global__ void __launch_bounds__(64 * kSharedWaves)
+__attribute__((amdgpu_waves_per_eu(2)))
+attn_prefix_fused_kernel(SharedArgs a) {
+  __shared__ __align__(16) SharedLds<D, Q, kSharedWaves> lds;
+  __shared__ __align__(16) SuffixStates<D> suf;
+  const int x = static_cast<int>(blockIdx.x);
+  if (x < a.pre_blocks) {
+    prefix_role<D, Q, true>(a, x, lds, &suf);
+    return;
+  }
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int64_t items = int64_t(a.num_seqs) * a.num_kv_heads * ((a.group + 15) / 16);
+  const int64_t stride = int64_t(gridDim.x - a.pre_blocks) * kSharedWaves;
+  for (int64_t it = int64_t(x - a.pre_blocks) * kSharedWaves + w; it < items; it += stride)
+    suffix_role<D, Q>(a, it, lds.k[w], lds.v[w], lds.s[w]);
 }
 
 // grid = suffix items, one wave each.
@@ -330,13 +456,14 @@ template <int D, int Q>
 __global__ void __launch_bounds__(64)
 attn_suffix_kernel(SharedArgs a) {
   __shared__ __align__(16) SharedLds<D, Q, 1> lds;
-  suffix_role<D, Q>(a, int64_t(blockIdx.x), lds);
+  suffix_role<D, Q>(a, int64_t(blockIdx.x), lds.k[0], lds.v[0], lds.s[0]);
 }
 
 int64_t round_up_to(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 struct SharedPlan {
   int row_blocks, pre_blocks;
+  int fused;
   int suf_parts, suf_tokens;
   int64_t suf_blocks;
   size_t ws_bytes, ws_ml_off;
@@ -385,6 +512,15 @@ pkv_status shared_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_groups
   if (spt < 64) spt = 64;
   pl->suf_tokens = static_cast<int>(spt);
   pl->suf_parts = static_cast<int>((suf_len + spt - 1) / spt);
+  // Suffixes no longer than kFusedSuffix (by the hint): the prefix kernel
+  // walks its members' suffixes itself, and the suffix kernel only the
+  // sequences that share nothing (whole, in part 0).
+  pl->fused = max_suffix_len > 0 && max_suffix_len <= kFusedSuffix && max_group_size >= 2 &&
+              max_prefix_len > 0;
+  if (pl->fused) {
+    pl->suf_parts = 1;
+    pl->suf_tokens = static_cast<int>(round_up_to(seq_len, kKT));
+  }
   const int64_t pre_blocks = int64_t(num_groups) * g->num_kv_heads * pl->row_blocks;
   const int64_t wave_items = int64_t(num_seqs) * g->num_kv_heads * pl->suf_parts * ((G + 15) / 16);
   pl->suf_blocks = wave_items;
@@ -399,6 +535,14 @@ pkv_status shared_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_groups
 
 template <int D, int Q>
 hipError_t launch_shared(const SharedPlan& pl, const SharedArgs& a, hipStream_t st) {
+  if (a.fused) {
+    // whole sequences: about 8 (sequence, KV head) items per wave
+    const int64_t whole = (pl.suf_blocks + 8 * kSharedWaves - 1) / (8 * kSharedWaves);
+    hipLaunchKernelGGL((attn_prefix_fused_kernel<D, Q>),
+                       dim3(static_cast<uint32_t>(a.pre_blocks + whole)), dim3(64 * kSharedWaves), 0,
+                       st, a);
+    return hipSuccess;
+  }
   if (pl.suf_blocks > 0)
     hipLaunchKernelGGL((attn_suffix_kernel<D, Q>), dim3(static_cast<uint32_t>(pl.suf_blocks)),
                        dim3(64), 0, st, a);
@@ -483,6 +627,7 @@ pkv_status shared_impl(const char* who, int types, const void* q, const void* k_
   a.row_blocks = pl.row_blocks;
   a.pre_blocks = a.max_prefix > 0 ? pl.pre_blocks : 0;
   a.suf_tokens = pl.suf_tokens;
+  a.fused = pl.fused && a.pre_blocks > 0;
   a.scale_log2 = static_cast<float>(double(scale) * 1.4426950408889634 *
                                     (kind == pkv::mfma::kFp8 ? double(scales->k_scale) : 1.0));
   a.v_scale = kind == pkv::mfma::kFp8 ? scales->v_scale : 1.f;

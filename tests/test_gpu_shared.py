@@ -60,6 +60,30 @@ def test_shared_prefix_config_full():
     say("  gate", assert_gate(got, ref, "bf16", "shared-prefix-cow"))
 
 
+@pytest.mark.parametrize("hint", [0, 2000], ids=["no-hint", "long-hint"])
+def test_two_kernel_form_on_the_config(hint):
+    """Without a suffix hint, or with one past what the prefix workgroups walk
+    themselves, the step takes the two-kernel form (suffix pieces through the
+    workspace, then the prefix kernel's combine): every element against the
+    oracle, as the one-launch form."""
+    from paged_attention_slot_amd import ops
+    from paged_attention_slot_amd.runtime import to_host_bits
+    wl = config_workload("shared-prefix-cow")
+    got, ref, step = run_wl(wl, ([0, 176], [2048]))
+    gs, pl, mg, mp, _ = step.shared_groups()
+    n = ops.shared_workspace_bytes(wl.num_seqs, wl.num_q_heads, pl.numel(), mg, mp, hint,
+                                   step.max_seq_len, step.k_caches[0])
+    ws = torch.empty(max(n, 16), dtype=torch.uint8, device=step.q.device)
+    out = torch.empty_like(step.q)
+    ops.attention_decode_shared(step.q, step.k_caches[0], step.v_caches[0], step.block_tables,
+                                step.seq_lens, wl.scale, gs, pl, mg, mp, hint, out=out,
+                                max_seq_len=step.max_seq_len, workspace=ws)
+    torch.cuda.synchronize()
+    two = to_f64(to_host_bits(out))
+    say("  gate", assert_gate(two, ref, "bf16", f"two-kernel form, hint {hint}"))
+    assert_gate(got, ref, "bf16", "one-launch form")
+
+
 FAMILIES = [  # prefix, suffix lens, forking parents, samples, Hq, Hkv, D, B
     (64, [3, 16, 7, 1, 12, 30, 9], 4, 4, 16, 4, 128, 16),
     (40, [3, 9, 1, 20, 33], 2, 3, 8, 8, 128, 16),      # prefix ends inside a block
