@@ -337,6 +337,58 @@ def test_long_context_config_partitions_against_oracle_split():
     say("  gate", assert_gate(gpu_out(step), ref, "bf16", "long context, 512-token partitions"))
 
 
+@pytest.mark.parametrize("zeros", [(), (0,), (4,), (9,), (0, 4, 9), tuple(range(10))],
+                         ids=["none", "first", "middle", "last", "several", "all"])
+def test_matrix_balanced_empty_histories_and_used_workspaces(zeros, tuning):
+    """The matrix-core balanced split with its merge: empty histories anywhere
+    in the batch (or all of it) give zero rows; a workspace of arbitrary bytes
+    gives the bits of a zeroed one; the two phases in calls of their own give
+    the same bits; a smaller batch right after, on the same workspace, gives
+    the bits of its own call on a fresh one."""
+    from paged_attention_slot_amd import ops
+    tuning("PKV_ATTN_MODE", 4)
+    lens_all = [1, 15, 16, 17, 64, 200, 333, 1500, 2047, 3000]
+    wl = independent_workload(lens_all, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                              block_size=16, dtype="bf16", seed=91)
+    step, ost = run_both(wl, attention=False)
+    say(f"  split {step.split} zeros={zeros}")
+    lens = step.seq_lens.clone()
+    for z in zeros:
+        lens[z] = 0
+    N, Hq = wl.num_seqs, wl.num_q_heads
+    need = ops.workspace_bytes(N, Hq, wl.max_seq_len, step.k_cache, 0)
+    dev = step.q.device
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    dirty_h = torch.randint(0, 256, (need,), dtype=torch.uint8, generator=gen)
+
+    def call(n, ws, phases=3):
+        out = torch.full_like(step.q[:n], 7.0)
+        for ph in ((1, 2) if phases == 12 else (3,)):
+            ops.attention_decode(step.q[:n], step.k_cache, step.v_cache, step.block_tables[:n],
+                                 lens[:n], wl.scale, out=out, max_seq_len=wl.max_seq_len,
+                                 workspace=ws, phases=ph)
+        torch.cuda.synchronize()
+        return host_bits(out)
+
+    clean = call(N, torch.zeros(need, dtype=torch.uint8, device=dev))
+    dirty_ws = dirty_h.to(dev)
+    dirty = call(N, dirty_ws)
+    assert np.array_equal(clean, dirty), "a workspace of arbitrary bytes changes the result"
+    split = call(N, dirty_ws, phases=12)
+    assert np.array_equal(clean, split), "phase 1 then phase 2 differs from one call"
+    o = to_f64(clean)
+    for z in zeros:
+        assert not o[z].any(), f"empty history {z} not zero"
+    ref = oracle_attention(wl.q, ost.k_pool, ost.v_pool, ost.block_tables, lens.cpu().numpy(),
+                           wl.scale)
+    say("  gate", assert_gate(o, ref, "bf16", f"matrix-balanced zeros={zeros}"))
+    n2 = 6
+    again = call(n2, dirty_ws)
+    fresh = call(n2, torch.zeros(ops.workspace_bytes(n2, Hq, wl.max_seq_len, step.k_cache, 0),
+                                 dtype=torch.uint8, device=dev))
+    assert np.array_equal(again, fresh), "a smaller batch on a used workspace differs"
+
+
 # -- the two work distributions ------------------------------------------------
 
 @pytest.fixture
